@@ -1,0 +1,438 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Each test checks the oracle against something other than itself: a library routine
+(PyTorch / NumPy in float64), a closed form, an invariant the method must satisfy, a
+figure the pages print, or brute force on tiny inputs.  Each is chosen so that a
+plausible mistake (a dropped term, a wrong sign or index, a transposed operand, the
+other RoPE pairing, a wrong GQA map) fails at least one of them.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle
+from decoder_only_transformer_decode_amd import synth
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _gold(name):
+    with open(os.path.join(GOLD, name)) as f:
+        return json.load(f)
+
+
+def _expr(v):
+    if isinstance(v, str):
+        return eval(v, {"cos": math.cos, "sin": math.sin})
+    return float(v)
+
+
+# ------------------------------------------------------------------------------------
+# scalar encodings: against NumPy's float16 and PyTorch's bfloat16 conversions
+# ------------------------------------------------------------------------------------
+
+def test_bf16_decode_all_patterns_vs_torch():
+    bits = np.arange(65536, dtype=np.uint32)
+    ref = torch.from_numpy((bits << 16).astype(np.uint32).view(np.int32)).view(torch.float32).double().numpy()
+    got = np.array([oracle.bf16_to_double(int(b)) for b in bits])
+    finite = np.isfinite(ref)
+    assert np.array_equal(got[finite], ref[finite])
+    assert np.all(np.isnan(got[np.isnan(ref)]))
+
+
+def test_bf16_round_vs_torch_on_fp32_values():
+    rng = np.random.default_rng(0)
+    vals = np.concatenate([
+        rng.standard_normal(4000).astype(np.float32),
+        (rng.standard_normal(1000) * 1e-38).astype(np.float32),   # bf16 subnormal range
+        (rng.standard_normal(1000) * 1e30).astype(np.float32),
+    ])
+    # exact ties: bf16 grid points plus half a bf16 ulp (odd and even neighbours)
+    base = torch.tensor([1.0, 1.0078125, 3.0, -5.0, 1e-3], dtype=torch.bfloat16).float().numpy()
+    ulp = np.abs(base) * 2.0 ** -7
+    ties = (base + np.sign(base) * ulp / 2).astype(np.float32)
+    vals = np.concatenate([vals, ties])
+    ref = torch.from_numpy(vals).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = np.array([oracle.double_to_bf16(float(v)) for v in vals], dtype=np.uint16)
+    assert np.array_equal(got, ref)
+
+
+def test_fp16_round_and_decode_vs_numpy():
+    rng = np.random.default_rng(1)
+    vals = np.concatenate([rng.standard_normal(3000), rng.standard_normal(500) * 1e-6,
+                           rng.standard_normal(500) * 3e4, [65504.0, 65519.99, 65520.0, 1e6,
+                                                           2.0 ** -24, 2.0 ** -25, 3 * 2.0 ** -26]])
+    with np.errstate(over="ignore"):
+        ref = vals.astype(np.float16).view(np.uint16)
+    got = np.array([oracle.double_to_fp16(float(v)) for v in vals], dtype=np.uint16)
+    assert np.array_equal(got, ref)
+    bits = np.arange(65536, dtype=np.uint16)
+    refd = bits.view(np.float16).astype(np.float64)
+    gotd = np.array([oracle.fp16_to_double(int(b)) for b in bits])
+    fin = np.isfinite(refd)
+    assert np.array_equal(gotd[fin], refd[fin])
+    assert np.array_equal(np.isinf(gotd), np.isinf(refd))
+
+
+def test_round_act_f32_is_binary32():
+    rng = np.random.default_rng(2)
+    x = rng.standard_normal(1000)
+    got = np.array([oracle.round_act(v, oracle.ACT_F32) for v in x])
+    assert np.array_equal(got, x.astype(np.float32).astype(np.float64))
+
+
+# ------------------------------------------------------------------------------------
+# weight formats and dequantization
+# ------------------------------------------------------------------------------------
+
+def test_int8_row_worked_example_page_rule():
+    g = _gold("page_figures.json")["int8_row_rule"]
+    w = np.array([g["worked_row"]], dtype=np.float32)
+    q, s = synth.encode_int8_row(w)
+    assert q.tolist()[0] == g["expected_codes"]
+    assert abs(float(s[0]) - g["expected_scale"]) < 1e-8
+    deq = oracle.dequant_row(oracle.W_INT8_ROW, q, s, 0)
+    assert np.allclose(deq, w[0], atol=float(s[0]) / 2 + 1e-7)
+
+
+def test_int8_row_dequant_is_one_fp32_product():
+    rng = np.random.default_rng(3)
+    w = (rng.standard_normal((7, 96)) * 0.02).astype(np.float32)
+    q, s = synth.encode_int8_row(w)
+    for r in range(7):
+        got = oracle.dequant_row(oracle.W_INT8_ROW, q, s, r)
+        # exact product in float64 (8 x 24 significant bits), then one rounding to binary32
+        exact = (q[r].astype(np.float64) * np.float64(s[r])).astype(np.float32)
+        assert np.array_equal(got.view(np.uint32), exact.view(np.uint32))
+        # the code reconstructs the original row to half a step
+        assert np.all(np.abs(got.astype(np.float64) - w[r]) <= s[r] / 2 * (1 + 1e-6) + 1e-12)
+        assert np.max(np.abs(q[r])) == 127
+
+
+def test_q8_0_dequant_exact_and_blockwise():
+    rng = np.random.default_rng(4)
+    w = (rng.standard_normal((5, 128)) * 0.02).astype(np.float32)
+    w[2, 32:64] = 0.0                         # an all-zero block
+    q, d = synth.encode_q8_0(w)
+    assert d.shape == (5, 4) and d.dtype == np.float16
+    for r in range(5):
+        got = oracle.dequant_row(oracle.W_Q8_0, q, d, r)
+        # fp32(q) * fp32(d16) is exact: 8 + 11 significant bits < 24
+        exact = q[r].astype(np.float64) * np.repeat(d[r].astype(np.float64), 32)
+        assert np.array_equal(got.astype(np.float64), exact)
+        bound = np.repeat(d[r].astype(np.float64), 32) / 2 + np.abs(w[r]) * 2.0 ** -10
+        assert np.all(np.abs(got - w[r]) <= bound + 1e-12)
+    assert np.all(q[2, 32:64] == 0) and d[2, 1] == 0
+
+
+def test_quant_bytes_page_figures():
+    g = _gold("page_figures.json")
+    qb = g["quant_bytes"]
+    per_w = (qb["q8_0_block_weights"] + 2) / qb["q8_0_block_weights"]
+    assert round(per_w, 2) == qb["q8_0_bytes_per_weight_approx"]
+    assert 16 + 2 == qb["q4_0_block_bytes"] and 18 * 8 / 32 == qb["q4_0_bits_per_weight"]
+    # the Llama-3.2-1B shape in Q8_0: matrices come in just under the 1.32 GB file
+    s = synth.LLAMA32_1B.shape
+    n = sum(r * c for r, c in synth.matrix_shapes(s).values())
+    total = n * per_w
+    file_bytes = g["llama32_1b_q8_0_file"]["file_bytes_approx"]
+    assert 0.97 * file_bytes < total < file_bytes
+
+
+def test_gemv_matches_float64_matmul_all_formats():
+    rng = np.random.default_rng(5)
+    w = (rng.standard_normal((33, 160)) * 0.02).astype(np.float32)
+    x = rng.standard_normal(160)
+    for fmt in (oracle.W_INT8_ROW, oracle.W_Q8_0, oracle.W_BF16):
+        parts = synth.encode_matrix(w, fmt)
+        if fmt == oracle.W_INT8_ROW:
+            W = parts["q"].astype(np.float64) * parts["s"].astype(np.float64)[:, None]
+            got = oracle.gemv(fmt, parts["q"], parts["s"], x)
+        elif fmt == oracle.W_Q8_0:
+            W = parts["q"].astype(np.float64) * np.repeat(parts["s"].astype(np.float64), 32, axis=1)
+            got = oracle.gemv(fmt, parts["q"], parts["s"], x)
+        else:
+            W = synth.bf16_bits_to_f32(parts["w"]).astype(np.float64)
+            got = oracle.gemv(fmt, parts["w"], None, x)
+        ref = torch.from_numpy(W) @ torch.from_numpy(x)
+        assert np.allclose(got, ref.numpy(), rtol=1e-12, atol=1e-14)
+
+
+def test_row_major_layout_page_example():
+    g = _gold("page_figures.json")["row_major_example"]
+    rows, cols = g["shape"]
+    # a bf16 [2,3] matrix holding the flat values 1..6 in storage order
+    flat = np.arange(1, rows * cols + 1, dtype=np.float32)
+    W = synth.f32_to_bf16_bits(flat).reshape(rows, cols)
+    for key, off in g["element_offsets"].items():
+        i, j = map(int, key.split(","))
+        e = np.zeros(cols); e[j] = 1.0
+        assert oracle.gemv(oracle.W_BF16, W, None, e)[i] == flat[off]
+
+
+# ------------------------------------------------------------------------------------
+# RMSNorm, SiLU
+# ------------------------------------------------------------------------------------
+
+def test_rmsnorm_vs_torch():
+    rng = np.random.default_rng(6)
+    for n in (8, 256, 4096):
+        x = rng.standard_normal(n) * 3
+        g = (1 + 0.02 * rng.standard_normal(n)).astype(np.float32)
+        ref = F.rms_norm(torch.from_numpy(x), (n,), weight=torch.from_numpy(g.astype(np.float64)), eps=1e-5)
+        assert np.allclose(oracle.rmsnorm(x, g, 1e-5), ref.numpy(), rtol=1e-13, atol=1e-15)
+
+
+def test_rmsnorm_constant_vector_closed_form():
+    c = _gold("closed_forms.json")["rmsnorm_constant_vector"]
+    n = c["n"]
+    g = np.linspace(0.5, 1.5, n).astype(np.float32)
+    got = oracle.rmsnorm(np.full(n, c["c"]), g, c["eps"])
+    exp = c["c"] / math.sqrt(c["c"] ** 2 + c["eps"]) * g.astype(np.float64)
+    assert np.allclose(got, exp, rtol=1e-15)
+
+
+def test_silu_vs_torch():
+    z = np.linspace(-30, 30, 601)
+    ref = F.silu(torch.from_numpy(z)).numpy()
+    got = np.array([oracle.silu(v) for v in z])
+    assert np.allclose(got, ref, rtol=1e-14, atol=1e-300)
+    assert oracle.silu(0.0) == 0.0
+
+
+# ------------------------------------------------------------------------------------
+# RoPE
+# ------------------------------------------------------------------------------------
+
+def test_rope_closed_forms_half_split():
+    c = _gold("closed_forms.json")["rope_half_split_d4"]
+    for case in c["cases"]:
+        got = oracle.rope(np.array(case["v"], dtype=np.float64), case["pos"], c["theta"])
+        exp = np.array([_expr(e) for e in case["expected"]])
+        assert np.allclose(got, exp, atol=1e-15), case
+    inter = np.array([_expr(e) for e in c["interleaved_would_give_for_case0"]])
+    got0 = oracle.rope(np.array([1.0, 0, 0, 0]), 1, c["theta"])
+    assert not np.allclose(got0, inter)
+
+
+def test_rope_is_complex_rotation():
+    rng = np.random.default_rng(7)
+    d, theta = 128, 10000.0
+    for pos in (0, 1, 17, 4095, 16383):
+        v = rng.standard_normal(d)
+        z = v[: d // 2] + 1j * v[d // 2:]
+        ang = pos * theta ** (-2.0 * np.arange(d // 2) / d)
+        rz = z * np.exp(1j * ang)
+        exp = np.concatenate([rz.real, rz.imag])
+        got = oracle.rope(v, pos, theta)
+        # the angle pos*f carries ~pos ulps of rounding in either formulation
+        assert np.allclose(got, exp, rtol=0, atol=1e-15 * max(pos, 1) * np.abs(v).max() * 8)
+        assert abs(np.linalg.norm(got) - np.linalg.norm(v)) <= 1e-13 * np.linalg.norm(v)
+
+
+def test_rope_relative_position_property():
+    rng = np.random.default_rng(8)
+    d, theta = 64, 10000.0
+    q, k = rng.standard_normal(d), rng.standard_normal(d)
+    ref = oracle.rope(q, 10, theta) @ oracle.rope(k, 3, theta)
+    for m in (7, 100, 2000):
+        got = oracle.rope(q, m + 7, theta) @ oracle.rope(k, m, theta)
+        assert abs(got - ref) < 1e-10
+
+
+# ------------------------------------------------------------------------------------
+# attention and GQA
+# ------------------------------------------------------------------------------------
+
+def test_attention_vs_torch_sdpa_gqa():
+    rng = np.random.default_rng(9)
+    hq, hkv, d = 8, 2, 32
+    for n in (1, 2, 15, 64):
+        q = rng.standard_normal((hq, d))
+        K = rng.standard_normal((n, hkv, d))
+        V = rng.standard_normal((n, hkv, d))
+        ref = F.scaled_dot_product_attention(
+            torch.from_numpy(q)[None, :, None, :],                      # [1, hq, 1, d]
+            torch.from_numpy(K).permute(1, 0, 2)[None].contiguous(),     # [1, hkv, n, d]
+            torch.from_numpy(V).permute(1, 0, 2)[None].contiguous(),
+            enable_gqa=True)[0, :, 0, :]
+        assert np.allclose(oracle.attention(q, K, V), ref.numpy(), rtol=1e-12, atol=1e-13)
+
+
+def test_gqa_equals_mha_with_repeated_kv_heads():
+    rng = np.random.default_rng(10)
+    hq, hkv, d, n = 8, 2, 16, 9
+    q = rng.standard_normal((hq, d))
+    K = rng.standard_normal((n, hkv, d)); V = rng.standard_normal((n, hkv, d))
+    Kr = np.repeat(K, hq // hkv, axis=1); Vr = np.repeat(V, hq // hkv, axis=1)
+    assert np.allclose(oracle.attention(q, K, V), oracle.attention(q, Kr, Vr), rtol=0, atol=1e-15)
+
+
+def test_gqa_head_map_page_figures():
+    g = _gold("page_figures.json")["gqa_head_map"]
+    hq, hkv, d, n = g["n_q_heads"], g["n_kv_heads"], 4, 3
+    q = np.zeros((hq, d))
+    K = np.zeros((n, hkv, d))
+    V = np.zeros((n, hkv, d))
+    for j in range(hkv):
+        V[:, j, :] = j                        # each kv head carries its own index
+    out = oracle.attention(q, K, V)
+    assert out[:, 0].round().astype(int).tolist() == g["kv_head_of_q_head"]
+
+
+def test_attention_special_cases():
+    rng = np.random.default_rng(11)
+    hq, hkv, d = 4, 4, 8
+    q = rng.standard_normal((hq, d))
+    K = rng.standard_normal((1, hkv, d)); V = rng.standard_normal((1, hkv, d))
+    assert np.array_equal(oracle.attention(q, K, V), V[0])          # one position: o = v0
+    K5 = np.repeat(K, 5, axis=0); V5 = rng.standard_normal((5, hkv, d))
+    assert np.allclose(oracle.attention(q, K5, V5), V5.mean(axis=0), atol=1e-14)  # equal keys
+    ones = np.ones((5, hkv, d))
+    assert np.allclose(oracle.attention(q, rng.standard_normal((5, hkv, d)), ones), 1.0,
+                       atol=1e-14)   # softmax weights sum to 1
+
+
+def test_argmax_ties_and_nan():
+    assert oracle.argmax_f32([1.0, 3.0, 3.0, 2.0]) == 1
+    assert oracle.argmax_f32([-5.0, -5.0]) == 0
+    assert oracle.argmax_f32([1.0, float("nan")]) == -2
+    rng = np.random.default_rng(12)
+    v = rng.standard_normal(4096).astype(np.float32)
+    assert oracle.argmax_f32(v) == int(np.argmax(v))
+
+
+def test_kv_int8_quantization_bounds():
+    rng = np.random.default_rng(13)
+    for scale in (1e-3, 1.0, 50.0):
+        x = rng.standard_normal(128) * scale
+        q, s16 = oracle.kv_quant_i8(x)
+        s = float(np.array([s16], dtype=np.uint16).view(np.float16)[0])
+        assert s16 == int(np.array([np.max(np.abs(x)) / 127.0]).astype(np.float16).view(np.uint16)[0])
+        assert np.all(np.abs(q.astype(np.float64) * s - x) <= s / 2 * (1 + 1e-12) + 1e-300)
+        assert np.max(np.abs(q)) in (126, 127)
+    q, s16 = oracle.kv_quant_i8(np.zeros(16))
+    assert s16 == 0 and not q.any()
+
+
+# ------------------------------------------------------------------------------------
+# whole model: cache invariants and an independent brute-force forward
+# ------------------------------------------------------------------------------------
+
+def _model(shape, seed=99, max_ctx=16, max_seqs=2):
+    w = synth.gen_weights(shape, seed, threads=2)
+    return oracle.Model(shape, w, max_ctx=max_ctx, max_seqs=max_seqs), w
+
+
+@pytest.mark.parametrize("kw", [
+    dict(),
+    dict(act=synth.ACT_BF16, kvfmt=synth.KV_BF16),
+    dict(wfmt=synth.W_Q8_0, act=synth.ACT_BF16, kvfmt=synth.KV_I8, tied=True),
+    dict(wfmt=synth.W_BF16, act=synth.ACT_BF16, kvfmt=synth.KV_BF16),
+])
+def test_cached_decode_equals_full_recompute(kw):
+    shape = synth.tiny_shape(**kw)
+    m, _ = _model(shape)
+    toks = synth.prompt_tokens(shape.vocab, 9, seed=5)
+    for t in range(len(toks)):
+        nxt, logits, hid = m.step(0, toks[t], t, want_hidden=True)
+        fn, flog, fhid = m.full_forward(toks[: t + 1], want_hidden=True)
+        assert nxt == fn
+        assert np.allclose(logits, flog, rtol=0, atol=1e-6 * np.abs(flog).max())
+        assert np.allclose(hid, fhid, rtol=1e-12, atol=1e-12)
+
+
+def test_sequences_are_independent():
+    shape = synth.tiny_shape()
+    m, _ = _model(shape)
+    a = synth.prompt_tokens(shape.vocab, 6, seed=1)
+    b = synth.prompt_tokens(shape.vocab, 6, seed=2)
+    outs_a = []
+    for t in range(6):
+        outs_a.append(m.step(0, a[t], t)[1])
+        m.step(1, b[t], t)
+    m2, _ = _model(shape)
+    for t in range(6):
+        assert np.array_equal(m2.step(0, a[t], t)[1], outs_a[t])
+
+
+def test_gqa_model_with_equal_heads_is_mha_and_kv_roundtrip():
+    shape = synth.tiny_shape(n_kv_heads=4)     # Hkv = Hq
+    m, _ = _model(shape)
+    toks = synth.prompt_tokens(shape.vocab, 4, seed=3)
+    for t in range(4):
+        m.step(0, toks[t], t)
+    k, v = m.kv_read(0, 1, 0, 4)
+    kr, vr, _, _ = m.kv_read_raw(0, 1, 0, 4)
+    assert np.array_equal(k, kr.astype(np.float64)) and np.array_equal(v, vr.astype(np.float64))
+
+
+def _torch_forward(shape, weights, tokens):
+    """Independent brute-force forward of a whole prefix in float64 torch, built from
+    library routines (rms_norm, causal scaled_dot_product_attention with GQA, silu) and
+    complex-number RoPE.  Activation and KV rounding to binary32 at the same points."""
+    D, hd = shape.dim, shape.head_dim
+    n = len(tokens)
+
+    def deq(name):
+        p = weights[name]
+        if "s" in p and p["s"].dtype == np.float32:
+            return torch.from_numpy(p["q"].astype(np.float64) * p["s"].astype(np.float64)[:, None])
+        if "s" in p:
+            return torch.from_numpy(p["q"].astype(np.float64) *
+                                    np.repeat(p["s"].astype(np.float64), 32, axis=1))
+        return torch.from_numpy(synth.bf16_bits_to_f32(p["w"]).astype(np.float64))
+
+    def r32(t):
+        return t.float().double()
+
+    def rope(t):                       # t [n, heads, hd]
+        half = hd // 2
+        z = torch.complex(t[..., :half], t[..., half:])
+        ang = torch.arange(n, dtype=torch.float64)[:, None] * \
+            shape.rope_theta ** (-2.0 * torch.arange(half, dtype=torch.float64) / hd)
+        z = z * torch.polar(torch.ones_like(ang), ang)[:, None, :]
+        return torch.cat([z.real, z.imag], dim=-1)
+
+    emb = deq("tok_emb")
+    x = r32(emb[torch.as_tensor(tokens, dtype=torch.long)])     # fp32 dequant of the rows
+    for i in range(shape.n_layers):
+        g = lambda nm: torch.from_numpy(weights[f"L{i}.{nm}"]["g"].astype(np.float64))
+        xn = r32(F.rms_norm(x, (D,), weight=g("attn_norm"), eps=shape.rms_eps))
+        q = (xn @ deq(f"L{i}.wq").T).view(n, shape.n_q_heads, hd)
+        k = (xn @ deq(f"L{i}.wk").T).view(n, shape.n_kv_heads, hd)
+        v = (xn @ deq(f"L{i}.wv").T).view(n, shape.n_kv_heads, hd)
+        q, k = rope(q), r32(rope(k))
+        v = r32(v)
+        o = F.scaled_dot_product_attention(q.transpose(0, 1)[None], k.transpose(0, 1)[None].contiguous(),
+                                           v.transpose(0, 1)[None].contiguous(),
+                                           is_causal=True, enable_gqa=True)[0].transpose(0, 1)
+        o = r32(o.reshape(n, -1))
+        x = x + o @ deq(f"L{i}.wo").T
+        xn = r32(F.rms_norm(x, (D,), weight=g("ffn_norm"), eps=shape.rms_eps))
+        h = r32(F.silu(xn @ deq(f"L{i}.w_gate").T) * (xn @ deq(f"L{i}.w_up").T))
+        x = x + h @ deq(f"L{i}.w_down").T
+    fin = torch.from_numpy(weights["final_norm"]["g"].astype(np.float64))
+    xn = r32(F.rms_norm(x[-1], (D,), weight=fin, eps=shape.rms_eps))
+    head = emb if shape.tied else deq("lm_head")
+    return (xn @ head.T).float().numpy(), x[-1].numpy()
+
+
+@pytest.mark.parametrize("kw", [dict(), dict(wfmt=synth.W_Q8_0, tied=True), dict(wfmt=synth.W_BF16)])
+def test_oracle_matches_brute_force_torch_forward(kw):
+    shape = synth.tiny_shape(**kw)
+    m, w = _model(shape, max_ctx=12)
+    toks = synth.prompt_tokens(shape.vocab, 12, seed=4)
+    for t in range(12):
+        nxt, logits, hid = m.step(0, toks[t], t, want_hidden=True)
+    ref_logits, ref_x = _torch_forward(shape, w, toks)
+    scale = np.abs(ref_logits).max()
+    assert np.max(np.abs(logits - ref_logits)) <= 1e-5 * scale
+    assert np.allclose(hid[-1], ref_x, rtol=1e-5, atol=1e-6 * np.abs(ref_x).max())
+    if np.sort(ref_logits)[-1] - np.sort(ref_logits)[-2] > 1e-4 * scale:
+        assert nxt == int(np.argmax(ref_logits))
