@@ -1,0 +1,202 @@
+"""Decode-step benchmark: tokens/s and achieved HBM bandwidth of the MI355X decode step.
+
+Workload (default): the SmolLM3-3B-shaped decoder with random weights (dim 2048, 36 layers,
+16 q / 4 kv heads, head_dim 128, ffn 11008, vocab 128256; int8 weight-only with per-row
+fp32 scales, bf16 activations and KV cache), batch 1: prefill 512 random tokens, then
+greedy decode toward context 2048.  One step = one pass of the whole decode step (embed,
+36 x [RMSNorm, QKV+RoPE, KV append + GQA attention, O + residual, RMSNorm, gate/up +
+SwiGLU, down + residual], final RMSNorm, LM head, argmax) for one token.
+
+Prints one JSON line (rank 0).  Runs on one GPU only.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from decoder_only_transformer_decode_amd import dtd, synth  # noqa: E402
+
+PEAK_HBM_GBS = 8000.0   # MI355X HBM3E, 8 TB/s
+
+
+def weight_bytes(s: synth.ModelShape) -> dict:
+    """Stored bytes of every matrix read by one decode step (the embedding row gather and
+    the norm gains are left out), by projection."""
+    def mat(r, c):
+        if s.wfmt == synth.W_BF16:
+            return r * c * 2
+        if s.wfmt == synth.W_INT8_ROW:
+            return r * c + r * 4
+        return r * c + r * (c // 32) * 2
+    per_layer = {
+        "qkv": mat(s.q_dim + 2 * s.kv_dim, s.dim),
+        "o": mat(s.dim, s.q_dim),
+        "gate_up": mat(2 * s.ffn_dim, s.dim),
+        "down": mat(s.dim, s.ffn_dim),
+    }
+    out = {k: v * s.n_layers for k, v in per_layer.items()}
+    out["lm_head"] = mat(s.vocab, s.dim)
+    out["per_layer"] = per_layer
+    return out
+
+
+def kv_bytes_per_position(s: synth.ModelShape) -> int:
+    """Stored K and V bytes of one position across all layers (+ fp16 scales for int8)."""
+    el = {synth.KV_F32: 4, synth.KV_BF16: 2, synth.KV_I8: 1}[s.kvfmt]
+    per = 2 * s.n_layers * s.n_kv_heads * s.head_dim * el
+    if s.kvfmt == synth.KV_I8:
+        per += 2 * s.n_layers * s.n_kv_heads * 2
+    return per
+
+
+def cpu_baseline(w: synth.Workload, weights, ctx_mid: int, n_steps: int) -> dict:
+    """The oracle, as it stands, on this host: n_steps decode steps at contexts around the
+    middle of the decoded range, from synthetic stored KV."""
+    import oracle
+    s = w.shape
+    m = oracle.Model(s, weights, max_ctx=w.context, max_seqs=1)
+    for layer in range(s.n_layers):
+        k, v, ks, vs = synth.synthetic_kv(s, ctx_mid, seed=5, layer=layer)
+        m.kv_write(0, layer, 0, k, v, ks, vs)
+    tok = 17
+    t0 = time.perf_counter()
+    for i in range(n_steps):
+        tok, _, _ = m.step(0, tok, ctx_mid + i)
+    dt = time.perf_counter() - t0
+    return {"value": n_steps / dt, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{n_steps} batch-1 decode steps at attended context {ctx_mid + 1}..{ctx_mid + n_steps} "
+                      f"(synthetic stored KV), fp64 oracle, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1536)
+    ap.add_argument("--warmup", type=int, default=16)
+    ap.add_argument("--workload", default=synth.SMOLLM3_3B.shape.name, choices=sorted(synth.BY_NAME))
+    ap.add_argument("--cpu-steps", type=int, default=8)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-kernel-timing", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this decode step runs on a single MI355X and has no "
+              "multi-GPU path; run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    w = synth.BY_NAME[args.workload]
+    s = w.shape
+    if w.batch != 1:
+        print("only the batch-1 workloads are benchmarked here", file=sys.stderr)
+        sys.exit(2)
+    K, W = args.steps, args.warmup
+    if w.prompt_len + K > w.context:
+        print(f"--steps {K} would run past context {w.context}", file=sys.stderr)
+        sys.exit(2)
+
+    t0 = time.perf_counter()
+    weights = synth.gen_weights(s, synth.weights_seed(w))
+    t_gen = time.perf_counter() - t0
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda", 0)
+    eng = dtd.Engine(s, max_ctx=w.context, max_seqs=2, max_batch=1)
+    eng.load_weights(synth.flat_tensors(weights))
+    print(f"[bench] weights generated in {t_gen:.1f} s and loaded", file=sys.stderr, flush=True)
+
+    prompt = torch.as_tensor(synth.prompt_tokens(s.vocab, w.prompt_len)).to(dev)
+    tok = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    def decode(n):
+        for _ in range(n):
+            dtd.dtd_decode_step(eng.h, [0], tok.data_ptr(), tok.data_ptr())
+
+    def fresh_sequence():
+        if eng.seq_len(0) >= 0:
+            eng.reset_seq(0)
+        nxt, _ = eng.prefill(0, prompt)
+        tok.copy_(nxt)
+        torch.cuda.synchronize()
+
+    # warmup: W steps on a throwaway sequence
+    fresh_sequence()
+    decode(W)
+    torch.cuda.synchronize()
+
+    # timed region: K greedy steps from position 512, the token fed back on the device
+    fresh_sequence()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    decode(K)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    assert eng.seq_len(0) == w.prompt_len + K
+
+    wb = weight_bytes(s)
+    wtot = sum(v for k, v in wb.items() if k != "per_layer")
+    kvpp = kv_bytes_per_position(s)
+    attended = np.arange(w.prompt_len + 1, w.prompt_len + K + 1, dtype=np.float64)
+    kv_total = float(kvpp * attended.sum())
+    bytes_total = wtot * K + kv_total
+    gbs = bytes_total / dt / 1e9
+
+    roofline = None
+    if not args.no_kernel_timing:
+        # same workload again with HIP events around every gate/up projection launch (the
+        # kernel moving the most bytes), on the engine's stream
+        fresh_sequence()
+        dtd.dtd_debug_kernel_timing(eng.h, dtd.KERNEL_GATE_UP, True)
+        decode(K)
+        ms, cnt = dtd.dtd_debug_kernel_timing(eng.h, dtd.KERNEL_GATE_UP, False)
+        per_launch = wb["per_layer"]["gate_up"]
+        avg_s = ms / 1e3 / max(cnt, 1)
+        ach = per_launch / avg_s / 1e9
+        roofline = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                    "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None,
+                    "kernel": "k_gemv (gate/up projection, int8-row, SwiGLU epilogue)",
+                    "bytes_per_launch": per_launch, "avg_launch_us": round(avg_s * 1e6, 2),
+                    "launches": cnt}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        ctx_mid = (w.prompt_len + w.context) // 2
+        cpu = cpu_baseline(w, weights, ctx_mid, args.cpu_steps)
+
+    rec = {
+        "metric": "decode tokens/s and achieved HBM GB/s (% of peak) per decode step, 1 GPU",
+        "value": round(K / dt, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(dt / K * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{s.name} batch-1 greedy decode, prefill {w.prompt_len} random tokens "
+                               f"then {K} steps (attended context {w.prompt_len + 1}..{w.prompt_len + K})",
+                   "dim": s.dim, "layers": s.n_layers, "q_heads": s.n_q_heads, "kv_heads": s.n_kv_heads,
+                   "head_dim": s.head_dim, "ffn": s.ffn_dim, "vocab": s.vocab,
+                   "weights": synth.WFMT_NAMES[s.wfmt], "activations": synth.ACT_NAMES[s.act],
+                   "kv_cache": synth.KV_NAMES[s.kvfmt], "batch": 1},
+        "hbm_gbs": round(gbs, 1),
+        "hbm_frac_of_peak": round(gbs / PEAK_HBM_GBS, 4),
+        "bytes_per_step": round(bytes_total / K),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    eng.close()
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,1067 @@
+// dtd_engine.cpp -- host side of libdtd.so: the C ABI of include/dtd.h, configuration and
+// weight validation (fail-closed, in the spirit of the hardened loader of the nxmr.cn C17
+// engine article, 4.1), weight repacking, the paged KV block pool with per-sequence block
+// tables (Qwen3-8B engine article, 4.3.1: fixed-size blocks, O(1) allocation from a free
+// pool, one block list per sequence id), and the per-step launch sequence.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <unordered_map>
+#include <vector>
+
+#include "../../include/dtd.h"
+#include "dtd_internal.h"
+
+using namespace dtd;
+
+namespace {
+
+constexpr int kRing = 64;   // pinned step-descriptor slots in flight
+
+struct LayerW {
+  MatDev qkv, o, gu, down;
+  float* attn_norm = nullptr;
+  float* ffn_norm = nullptr;
+};
+
+struct Seq {
+  int slot = -1;
+  int len = 0;
+  std::vector<int32_t> blocks;
+};
+
+struct TimerPair {
+  hipEvent_t a, b;
+};
+
+}  // namespace
+
+struct dtd_engine {
+  dtd_config cfg{};
+  Dims d{};
+  hipStream_t stream = nullptr;
+  int device = 0;
+  bool broken = false;
+  bool loaded = false;
+  std::string err;
+
+  std::vector<LayerW> layers;
+  MatDev emb{}, head{};
+  float* final_norm = nullptr;
+  std::vector<void*> weight_allocs;
+
+  float* rope_cos = nullptr;
+  float* rope_sin = nullptr;
+
+  void* kpool = nullptr;
+  void* vpool = nullptr;
+  uint16_t* kspool = nullptr;
+  uint16_t* vspool = nullptr;
+  size_t kv_layer_elems = 0;    // elements of K (or V) per layer
+  size_t kv_layer_scales = 0;   // fp16 scales of K (or V) per layer
+  int32_t* bt_dev = nullptr;
+
+  float* x = nullptr;
+  void* xn = nullptr;
+  float* q = nullptr;
+  float* knew = nullptr;
+  float* vnew = nullptr;
+  float* partials = nullptr;
+  void* o = nullptr;
+  void* h = nullptr;
+  float* logits = nullptr;
+  int32_t* err_dev = nullptr;
+  StepDesc* desc_dev = nullptr;
+  int32_t* rows_dev = nullptr;  // scratch for debug row lists
+  int rows_cap = 0;
+
+  StepDesc* desc_host = nullptr;  // pinned [kRing]
+  hipEvent_t desc_ev[kRing];
+  bool desc_ev_used[kRing];
+  int ring = 0;
+  int32_t* err_host = nullptr;    // pinned
+
+  std::unordered_map<int64_t, Seq> seqs;
+  std::vector<int> free_slots;
+  std::vector<int32_t> free_blocks;
+
+  float* capture = nullptr;
+
+  int timing_kind = -1;
+  std::vector<TimerPair> timers;
+  size_t timers_used = 0;
+};
+
+// ---------------------------------------------------------------------------------------
+// helpers
+// ---------------------------------------------------------------------------------------
+
+static dtd_status fail(dtd_engine* e, dtd_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  if (e) e->err = buf;
+  return st;
+}
+
+#define HIP_OK(e, call)                                                               \
+  do {                                                                                \
+    hipError_t _r = (call);                                                           \
+    if (_r != hipSuccess) {                                                           \
+      (e)->broken = true;                                                             \
+      return fail((e), DTD_E_HIP, "%s failed: %s", #call, hipGetErrorString(_r));     \
+    }                                                                                 \
+  } while (0)
+
+static int vec_elems(int wfmt) { return wfmt == DTD_W_BF16 ? 8 : 16; }
+
+static dtd_status check_config(const dtd_config* c, char* msg, int32_t msg_len) {
+  auto bad = [&](dtd_status st, const char* fmt, auto... args) {
+    if (msg && msg_len > 0) snprintf(msg, (size_t)msg_len, fmt, args...);
+    return st;
+  };
+  if (!c) return bad(DTD_E_ARG, "%s", "null config");
+  if (c->abi_version != DTD_ABI_VERSION) return bad(DTD_E_ARG, "abi_version %d, library has %d", c->abi_version, DTD_ABI_VERSION);
+  if (c->dim <= 0 || c->n_layers <= 0 || c->n_q_heads <= 0 || c->n_kv_heads <= 0 ||
+      c->head_dim <= 0 || c->ffn_dim <= 0 || c->vocab <= 0)
+    return bad(DTD_E_ARG, "%s", "dimensions must be positive");
+  if (c->n_q_heads % c->n_kv_heads) return bad(DTD_E_ARG, "n_kv_heads %d does not divide n_q_heads %d", c->n_kv_heads, c->n_q_heads);
+  if (c->wfmt < 0 || c->wfmt > 2 || c->act < 0 || c->act > 1 || c->kvfmt < 0 || c->kvfmt > 2)
+    return bad(DTD_E_ARG, "%s", "unknown weight, activation or KV format");
+  if (!(c->rms_eps >= 0.f) || !(c->rope_theta > 0.f)) return bad(DTD_E_ARG, "%s", "rms_eps must be >= 0 and rope_theta > 0");
+  if (c->kv_block_size <= 0 || c->kv_block_size > 4096 || c->kv_num_blocks <= 0 || c->max_seqs <= 0 ||
+      c->max_ctx <= 0 || c->max_batch <= 0)
+    return bad(DTD_E_ARG, "%s", "KV pool, sequence and batch limits must be positive");
+  if (c->max_batch > kMaxBatch) return bad(DTD_E_UNSUPPORTED, "max_batch %d > %d", c->max_batch, kMaxBatch);
+  if (c->head_dim % 4 || c->head_dim < 8 || c->head_dim > 128)
+    return bad(DTD_E_UNSUPPORTED, "head_dim %d (a multiple of 4 in [8, 128] supported)", c->head_dim);
+  const int G = c->n_q_heads / c->n_kv_heads;
+  if (G * c->head_dim > 2048) return bad(DTD_E_UNSUPPORTED, "query group size x head_dim = %d > 2048", G * c->head_dim);
+  const int qd = c->n_q_heads * c->head_dim;
+  const int v = vec_elems(c->wfmt);
+  if (c->dim % v || c->ffn_dim % v || qd % v)
+    return bad(DTD_E_UNSUPPORTED, "dim, ffn_dim and n_q_heads*head_dim must be multiples of %d", v);
+  if (c->wfmt == DTD_W_Q8_0 && (c->dim % 32 || c->ffn_dim % 32 || qd % 32))
+    return bad(DTD_E_ARG, "%s", "Q8_0 needs every matrix width to be a multiple of 32");
+  if ((int64_t)c->max_ctx * c->kv_block_size > (int64_t)1 << 40) return bad(DTD_E_ARG, "%s", "max_ctx too large");
+  if (msg && msg_len > 0) msg[0] = 0;
+  return DTD_OK;
+}
+
+// expected weight parts, in a fixed order
+static std::vector<dtd_tensor_spec> expected_parts(const dtd_config* c) {
+  std::vector<dtd_tensor_spec> out;
+  const int D = c->dim, F = c->ffn_dim, V = c->vocab;
+  const int qd = c->n_q_heads * c->head_dim, kvd = c->n_kv_heads * c->head_dim;
+  auto add = [&](const std::string& name, int rows, int cols, int elem, int64_t nbytes) {
+    dtd_tensor_spec s{};
+    snprintf(s.name, sizeof(s.name), "%s", name.c_str());
+    s.rows = rows; s.cols = cols; s.elem = elem; s.nbytes = nbytes;
+    out.push_back(s);
+  };
+  auto mat = [&](const std::string& base, int rows, int cols) {
+    if (c->wfmt == DTD_W_BF16) {
+      add(base + ".w", rows, cols, 2, (int64_t)rows * cols * 2);
+    } else {
+      add(base + ".q", rows, cols, 1, (int64_t)rows * cols);
+      if (c->wfmt == DTD_W_INT8_ROW) add(base + ".s", rows, 1, 4, (int64_t)rows * 4);
+      else add(base + ".s", rows, cols / 32, 2, (int64_t)rows * (cols / 32) * 2);
+    }
+  };
+  auto gain = [&](const std::string& base) { add(base + ".g", 1, D, 4, (int64_t)D * 4); };
+  mat("tok_emb", V, D);
+  for (int i = 0; i < c->n_layers; i++) {
+    const std::string L = "L" + std::to_string(i);
+    gain(L + ".attn_norm");
+    mat(L + ".wq", qd, D);
+    mat(L + ".wk", kvd, D);
+    mat(L + ".wv", kvd, D);
+    mat(L + ".wo", D, qd);
+    gain(L + ".ffn_norm");
+    mat(L + ".w_gate", F, D);
+    mat(L + ".w_up", F, D);
+    mat(L + ".w_down", D, F);
+  }
+  gain("final_norm");
+  if (!c->tied_embeddings) mat("lm_head", V, D);
+  return out;
+}
+
+static Dims make_dims(const dtd_config* c) {
+  Dims d{};
+  d.D = c->dim; d.L = c->n_layers; d.Hq = c->n_q_heads; d.Hkv = c->n_kv_heads; d.hd = c->head_dim;
+  d.F = c->ffn_dim; d.V = c->vocab;
+  d.G = d.Hq / d.Hkv;
+  d.q_dim = d.Hq * d.hd; d.kv_dim = d.Hkv * d.hd; d.qkv_rows = d.q_dim + 2 * d.kv_dim;
+  d.bs = c->kv_block_size;
+  d.max_blocks = (c->max_ctx + d.bs - 1) / d.bs;
+  d.max_ctx = c->max_ctx;
+  // Split the context so that a full batch at full context gives ~2048 work items.
+  const int64_t work = (int64_t)c->max_batch * d.Hkv * c->max_ctx;
+  int ct = kAttnTile;
+  while (ct < 2048 && (int64_t)ct * 2048 < work) ct <<= 1;
+  d.ct = ct;
+  d.nch = (c->max_ctx + ct - 1) / ct;
+  d.eps = c->rms_eps;
+  d.wfmt = c->wfmt; d.act = c->act; d.kvfmt = c->kvfmt;
+  return d;
+}
+
+static size_t act_bytes(int act) { return act == DTD_ACT_BF16 ? 2 : 4; }
+static size_t kv_elem_bytes(int kvfmt) { return kvfmt == DTD_KV_F32 ? 4 : (kvfmt == DTD_KV_BF16 ? 2 : 1); }
+
+// stored row of logical row r within the fused QKV matrix (q/k heads pair rows (i, i+hd/2))
+static int qkv_stored_row(const Dims& d, int part, int r) {
+  if (part == 2) return d.q_dim + d.kv_dim + r;
+  const int h = r / d.hd, i = r % d.hd, half = d.hd / 2;
+  const int p = i < half ? 2 * i : 2 * (i - half) + 1;
+  return (part == 0 ? 0 : d.q_dim) + h * d.hd + p;
+}
+
+static void release_weights(dtd_engine* e) {
+  for (void* p : e->weight_allocs) (void)hipFree(p);
+  e->weight_allocs.clear();
+  e->layers.clear();
+  e->loaded = false;
+}
+
+// ---------------------------------------------------------------------------------------
+// host-only queries
+// ---------------------------------------------------------------------------------------
+
+extern "C" dtd_status dtd_validate_config(const dtd_config* cfg, char* msg, int32_t msg_len) {
+  return check_config(cfg, msg, msg_len);
+}
+
+extern "C" int32_t dtd_expected_tensors(const dtd_config* cfg, dtd_tensor_spec* out, int32_t cap) {
+  const dtd_status st = check_config(cfg, nullptr, 0);
+  if (st != DTD_OK) return st;
+  const auto v = expected_parts(cfg);
+  if (out)
+    for (int32_t i = 0; i < cap && i < (int32_t)v.size(); i++) out[i] = v[(size_t)i];
+  return (int32_t)v.size();
+}
+
+// ---------------------------------------------------------------------------------------
+// lifecycle
+// ---------------------------------------------------------------------------------------
+
+template <typename T>
+static dtd_status dev_alloc(dtd_engine* e, T** p, size_t bytes) {
+  void* q = nullptr;
+  if (bytes == 0) bytes = 16;
+  hipError_t r = hipMalloc(&q, bytes);
+  if (r != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(e, DTD_E_OOM, "hipMalloc(%zu) failed: %s", bytes, hipGetErrorString(r));
+  }
+  *p = (T*)q;
+  return DTD_OK;
+}
+
+static void free_all(dtd_engine* e) {
+  release_weights(e);
+  void* ps[] = {e->rope_cos, e->rope_sin, e->kpool, e->vpool, e->kspool, e->vspool, e->bt_dev,
+                e->x, e->xn, e->q, e->knew, e->vnew, e->partials, e->o, e->h, e->logits,
+                e->err_dev, e->desc_dev, e->rows_dev};
+  for (void* p : ps)
+    if (p) (void)hipFree(p);
+  if (e->desc_host) (void)hipHostFree(e->desc_host);
+  if (e->err_host) (void)hipHostFree(e->err_host);
+  for (int i = 0; i < kRing; i++)
+    if (e->desc_ev[i]) (void)hipEventDestroy(e->desc_ev[i]);
+  for (auto& t : e->timers) { (void)hipEventDestroy(t.a); (void)hipEventDestroy(t.b); }
+}
+
+extern "C" dtd_status dtd_create(const dtd_config* cfg, void* hip_stream, dtd_engine** out) {
+  if (!out) return DTD_E_ARG;
+  *out = nullptr;
+  const dtd_status vs = check_config(cfg, nullptr, 0);
+  if (vs != DTD_OK) return vs;
+  dtd_engine* e = new dtd_engine();
+  for (int i = 0; i < kRing; i++) { e->desc_ev[i] = nullptr; e->desc_ev_used[i] = false; }
+  e->cfg = *cfg;
+  e->d = make_dims(cfg);
+  e->stream = (hipStream_t)hip_stream;
+  const Dims& d = e->d;
+  auto cleanup = [&](dtd_status st) { free_all(e); delete e; return st; };
+  if (hipGetDevice(&e->device) != hipSuccess) return cleanup(DTD_E_HIP);
+
+  // RoPE tables: angle pos * theta^(-2i/d) in double, cos/sin stored as fp32
+  const int half = d.hd / 2;
+  std::vector<float> cs((size_t)cfg->max_ctx * half), sn((size_t)cfg->max_ctx * half);
+  for (int p = 0; p < cfg->max_ctx; p++)
+    for (int i = 0; i < half; i++) {
+      const double f = std::pow((double)cfg->rope_theta, -2.0 * i / d.hd);
+      const double a = (double)p * f;
+      cs[(size_t)p * half + i] = (float)std::cos(a);
+      sn[(size_t)p * half + i] = (float)std::sin(a);
+    }
+  dtd_status st;
+  if ((st = dev_alloc(e, &e->rope_cos, cs.size() * 4)) || (st = dev_alloc(e, &e->rope_sin, sn.size() * 4)))
+    return cleanup(st);
+  if (hipMemcpy(e->rope_cos, cs.data(), cs.size() * 4, hipMemcpyHostToDevice) != hipSuccess ||
+      hipMemcpy(e->rope_sin, sn.data(), sn.size() * 4, hipMemcpyHostToDevice) != hipSuccess)
+    return cleanup(DTD_E_HIP);
+
+  // KV pool: per layer K, V [n_blocks][Hkv][bs][hd] (+ fp16 scales [n_blocks][Hkv][bs])
+  e->kv_layer_elems = (size_t)cfg->kv_num_blocks * d.Hkv * d.bs * d.hd;
+  e->kv_layer_scales = (size_t)cfg->kv_num_blocks * d.Hkv * d.bs;
+  const size_t kvb = e->kv_layer_elems * kv_elem_bytes(cfg->kvfmt) * d.L;
+  if ((st = dev_alloc(e, &e->kpool, kvb)) || (st = dev_alloc(e, &e->vpool, kvb))) return cleanup(st);
+  if (cfg->kvfmt == DTD_KV_I8) {
+    if ((st = dev_alloc(e, &e->kspool, e->kv_layer_scales * 2 * d.L)) ||
+        (st = dev_alloc(e, &e->vspool, e->kv_layer_scales * 2 * d.L)))
+      return cleanup(st);
+  }
+  const size_t bt_bytes = (size_t)cfg->max_seqs * d.max_blocks * 4;
+  if ((st = dev_alloc(e, &e->bt_dev, bt_bytes))) return cleanup(st);
+  if (hipMemset(e->bt_dev, 0, bt_bytes) != hipSuccess) return cleanup(DTD_E_HIP);
+
+  const int MB = cfg->max_batch;
+  const size_t ab = act_bytes(cfg->act);
+  if ((st = dev_alloc(e, &e->x, (size_t)MB * d.D * 4)) ||
+      (st = dev_alloc(e, &e->xn, (size_t)MB * d.D * ab)) ||
+      (st = dev_alloc(e, &e->q, (size_t)MB * d.q_dim * 4)) ||
+      (st = dev_alloc(e, &e->knew, (size_t)MB * d.kv_dim * 4)) ||
+      (st = dev_alloc(e, &e->vnew, (size_t)MB * d.kv_dim * 4)) ||
+      (st = dev_alloc(e, &e->partials, (size_t)MB * d.Hq * d.nch * (d.hd + 2) * 4)) ||
+      (st = dev_alloc(e, &e->o, (size_t)MB * d.q_dim * ab)) ||
+      (st = dev_alloc(e, &e->h, (size_t)MB * d.F * ab)) ||
+      (st = dev_alloc(e, &e->logits, (size_t)MB * d.V * 4)) ||
+      (st = dev_alloc(e, &e->err_dev, 16)) || (st = dev_alloc(e, &e->desc_dev, sizeof(StepDesc))))
+    return cleanup(st);
+  if (hipMemset(e->err_dev, 0, 16) != hipSuccess) return cleanup(DTD_E_HIP);
+  if (hipHostMalloc((void**)&e->desc_host, sizeof(StepDesc) * kRing, 0) != hipSuccess ||
+      hipHostMalloc((void**)&e->err_host, 16, 0) != hipSuccess)
+    return cleanup(DTD_E_OOM);
+  memset(e->err_host, 0, 16);
+  for (int i = 0; i < kRing; i++)
+    if (hipEventCreateWithFlags(&e->desc_ev[i], hipEventDisableTiming) != hipSuccess) return cleanup(DTD_E_HIP);
+
+  // free lists: slots in order; blocks in a fixed shuffled order so that block tables are
+  // never the identity (the paged path is exercised even for one sequence)
+  for (int s = cfg->max_seqs - 1; s >= 0; s--) e->free_slots.push_back(s);
+  e->free_blocks.resize((size_t)cfg->kv_num_blocks);
+  for (int i = 0; i < cfg->kv_num_blocks; i++) e->free_blocks[(size_t)i] = i;
+  uint64_t lcg = 0x9E3779B97F4A7C15ull;
+  for (int i = cfg->kv_num_blocks - 1; i > 0; i--) {
+    lcg = lcg * 6364136223846793005ull + 1442695040888963407ull;
+    const int j = (int)((lcg >> 33) % (uint64_t)(i + 1));
+    std::swap(e->free_blocks[(size_t)i], e->free_blocks[(size_t)j]);
+  }
+  *out = e;
+  return DTD_OK;
+}
+
+extern "C" void dtd_destroy(dtd_engine* e) {
+  if (!e) return;
+  (void)hipSetDevice(e->device);
+  (void)hipStreamSynchronize(e->stream);
+  free_all(e);
+  delete e;
+}
+
+extern "C" const char* dtd_last_error(const dtd_engine* e) {
+  return e ? e->err.c_str() : "null engine";
+}
+
+// ---------------------------------------------------------------------------------------
+// weights
+// ---------------------------------------------------------------------------------------
+
+namespace {
+
+struct SrcPart {
+  const uint8_t* host = nullptr;  // host copy of the caller's part
+  std::vector<uint8_t> own;       // staging if the caller's part lives on the device
+  int64_t nbytes = 0;
+};
+
+// one logical matrix: codes/bits (part "q" or "w") and scales (part "s")
+struct SrcMat {
+  const SrcPart* w = nullptr;
+  const SrcPart* s = nullptr;
+  int rows = 0, cols = 0;
+};
+
+}  // namespace
+
+// Packs several logical matrices stacked (or interleaved) by a row map into one device
+// matrix: stored row `r` takes row srcrow[r] of matrix srcmat[r].
+static dtd_status upload_packed(dtd_engine* e, const std::vector<SrcMat>& mats,
+                                const std::vector<std::pair<int, int>>& rowmap, int cols, MatDev* out) {
+  const int wfmt = e->cfg.wfmt;
+  const int rows = (int)rowmap.size();
+  const size_t eb = wfmt == DTD_W_BF16 ? 2 : 1;
+  const size_t wrow = (size_t)cols * eb;
+  const size_t srow = wfmt == DTD_W_INT8_ROW ? 4 : (wfmt == DTD_W_Q8_0 ? (size_t)(cols / 32) * 2 : 0);
+  std::vector<uint8_t> wbuf((size_t)rows * wrow), sbuf((size_t)rows * srow);
+  for (int r = 0; r < rows; r++) {
+    const SrcMat& m = mats[(size_t)rowmap[(size_t)r].first];
+    const int sr = rowmap[(size_t)r].second;
+    memcpy(wbuf.data() + (size_t)r * wrow, m.w->host + (size_t)sr * wrow, wrow);
+    if (srow) memcpy(sbuf.data() + (size_t)r * srow, m.s->host + (size_t)sr * srow, srow);
+  }
+  void* wd = nullptr;
+  void* sd = nullptr;
+  dtd_status st;
+  if ((st = dev_alloc(e, &wd, wbuf.size()))) return st;
+  e->weight_allocs.push_back(wd);
+  HIP_OK(e, hipMemcpy(wd, wbuf.data(), wbuf.size(), hipMemcpyHostToDevice));
+  if (srow) {
+    if ((st = dev_alloc(e, &sd, sbuf.size()))) return st;
+    e->weight_allocs.push_back(sd);
+    HIP_OK(e, hipMemcpy(sd, sbuf.data(), sbuf.size(), hipMemcpyHostToDevice));
+  }
+  out->w = wd;
+  out->s = sd;
+  out->rows = rows;
+  out->cols = cols;
+  return DTD_OK;
+}
+
+extern "C" dtd_status dtd_load_weights(dtd_engine* e, const dtd_tensor* t, int32_t n) {
+  if (!e) return DTD_E_ARG;
+  if (e->broken) return fail(e, DTD_E_STATE, "engine unusable after a HIP error");
+  if (!t || n <= 0) return fail(e, DTD_E_ARG, "no tensors");
+  HIP_OK(e, hipSetDevice(e->device));
+  const auto spec = expected_parts(&e->cfg);
+  std::unordered_map<std::string, size_t> idx;
+  for (size_t i = 0; i < spec.size(); i++) idx[spec[i].name] = i;
+  std::vector<SrcPart> parts(spec.size());
+  std::vector<bool> seen(spec.size(), false);
+  for (int32_t i = 0; i < n; i++) {
+    if (!t[i].name || !t[i].data) return fail(e, DTD_E_ARG, "tensor %d: null name or data", i);
+    auto it = idx.find(t[i].name);
+    if (it == idx.end()) return fail(e, DTD_E_ARG, "unknown tensor '%s'", t[i].name);
+    if (seen[it->second]) return fail(e, DTD_E_ARG, "duplicate tensor '%s'", t[i].name);
+    if (t[i].nbytes != spec[it->second].nbytes)
+      return fail(e, DTD_E_ARG, "tensor '%s': %lld bytes, expected %lld", t[i].name,
+                  (long long)t[i].nbytes, (long long)spec[it->second].nbytes);
+    seen[it->second] = true;
+  }
+  for (size_t i = 0; i < spec.size(); i++)
+    if (!seen[i]) return fail(e, DTD_E_ARG, "missing tensor '%s'", spec[i].name);
+  // all parts validated: only now touch engine state
+  for (int32_t i = 0; i < n; i++) {
+    SrcPart& p = parts[idx[t[i].name]];
+    p.nbytes = t[i].nbytes;
+    if (t[i].on_device) {
+      p.own.resize((size_t)t[i].nbytes);
+      HIP_OK(e, hipMemcpy(p.own.data(), t[i].data, (size_t)t[i].nbytes, hipMemcpyDeviceToHost));
+      p.host = p.own.data();
+    } else {
+      p.host = (const uint8_t*)t[i].data;
+    }
+  }
+  auto part = [&](const std::string& name) -> const SrcPart* { return &parts[idx[name]]; };
+  const bool bf = e->cfg.wfmt == DTD_W_BF16;
+  auto srcmat = [&](const std::string& base, int rows, int cols) {
+    SrcMat m;
+    m.w = part(base + (bf ? ".w" : ".q"));
+    m.s = bf ? nullptr : part(base + ".s");
+    m.rows = rows; m.cols = cols;
+    return m;
+  };
+  auto gain = [&](const std::string& name, float** dst) -> dtd_status {
+    dtd_status st = dev_alloc(e, dst, (size_t)e->d.D * 4);
+    if (st) return st;
+    e->weight_allocs.push_back(*dst);
+    HIP_OK(e, hipMemcpy(*dst, part(name + ".g")->host, (size_t)e->d.D * 4, hipMemcpyHostToDevice));
+    return DTD_OK;
+  };
+
+  release_weights(e);
+  const Dims& d = e->d;
+  dtd_status st;
+  auto identity = [](int src, int rows) {
+    std::vector<std::pair<int, int>> m((size_t)rows);
+    for (int r = 0; r < rows; r++) m[(size_t)r] = {src, r};
+    return m;
+  };
+  if ((st = upload_packed(e, {srcmat("tok_emb", d.V, d.D)}, identity(0, d.V), d.D, &e->emb))) goto bad;
+  e->layers.resize((size_t)d.L);
+  for (int l = 0; l < d.L; l++) {
+    const std::string L = "L" + std::to_string(l);
+    LayerW& W = e->layers[(size_t)l];
+    if ((st = gain(L + ".attn_norm", &W.attn_norm)) || (st = gain(L + ".ffn_norm", &W.ffn_norm))) goto bad;
+    {
+      std::vector<SrcMat> m = {srcmat(L + ".wq", d.q_dim, d.D), srcmat(L + ".wk", d.kv_dim, d.D),
+                               srcmat(L + ".wv", d.kv_dim, d.D)};
+      std::vector<std::pair<int, int>> map((size_t)d.qkv_rows);
+      for (int part_i = 0; part_i < 3; part_i++) {
+        const int rows = part_i == 0 ? d.q_dim : d.kv_dim;
+        for (int r = 0; r < rows; r++) map[(size_t)qkv_stored_row(d, part_i, r)] = {part_i, r};
+      }
+      if ((st = upload_packed(e, m, map, d.D, &W.qkv))) goto bad;
+    }
+    if ((st = upload_packed(e, {srcmat(L + ".wo", d.D, d.q_dim)}, identity(0, d.D), d.q_dim, &W.o))) goto bad;
+    {
+      std::vector<SrcMat> m = {srcmat(L + ".w_gate", d.F, d.D), srcmat(L + ".w_up", d.F, d.D)};
+      std::vector<std::pair<int, int>> map((size_t)2 * d.F);
+      for (int f = 0; f < d.F; f++) { map[(size_t)2 * f] = {0, f}; map[(size_t)2 * f + 1] = {1, f}; }
+      if ((st = upload_packed(e, m, map, d.D, &W.gu))) goto bad;
+    }
+    if ((st = upload_packed(e, {srcmat(L + ".w_down", d.D, d.F)}, identity(0, d.D), d.F, &W.down))) goto bad;
+  }
+  if ((st = gain("final_norm", &e->final_norm))) goto bad;
+  if (e->cfg.tied_embeddings) e->head = e->emb;
+  else if ((st = upload_packed(e, {srcmat("lm_head", d.V, d.D)}, identity(0, d.V), d.D, &e->head))) goto bad;
+  e->loaded = true;
+  return DTD_OK;
+bad:
+  release_weights(e);
+  return st;
+}
+
+// ---------------------------------------------------------------------------------------
+// the step
+// ---------------------------------------------------------------------------------------
+
+static hipError_t timed_begin(dtd_engine* e, int kind, TimerPair** tp) {
+  *tp = nullptr;
+  if (e->timing_kind != kind) return hipSuccess;
+  if (e->timers_used == e->timers.size()) {
+    TimerPair p;
+    hipError_t r = hipEventCreate(&p.a);
+    if (r != hipSuccess) return r;
+    r = hipEventCreate(&p.b);
+    if (r != hipSuccess) return r;
+    e->timers.push_back(p);
+  }
+  *tp = &e->timers[e->timers_used++];
+  return hipEventRecord((*tp)->a, e->stream);
+}
+
+static hipError_t timed_end(dtd_engine* e, TimerPair* tp) {
+  return tp ? hipEventRecord(tp->b, e->stream) : hipSuccess;
+}
+
+#define TIMED(kind, call)                                   \
+  do {                                                      \
+    TimerPair* _tp;                                         \
+    HIP_OK(e, timed_begin(e, (kind), &_tp));                \
+    HIP_OK(e, (call));                                      \
+    HIP_OK(e, timed_end(e, _tp));                           \
+  } while (0)
+
+struct Update { int slot, lblock, pblock; };
+
+// Probe records of dtd_debug_decode_probe: per layer, fields [B][n] in this order.
+struct ProbeLayout {
+  size_t x_in, xn, q, k, v, o, x_mid, xn2, h, x_out, record;
+};
+
+static ProbeLayout probe_layout(const Dims& d, int B, size_t ab) {
+  ProbeLayout p{};
+  size_t off = 0;
+  auto field = [&](size_t n, size_t eb) { const size_t o = off; off += (size_t)B * n * eb; return o; };
+  p.x_in = field(d.D, 4);
+  p.xn = field(d.D, ab);
+  p.q = field(d.q_dim, 4);
+  p.k = field(d.kv_dim, 4);
+  p.v = field(d.kv_dim, 4);
+  p.o = field(d.q_dim, ab);
+  p.x_mid = field(d.D, 4);
+  p.xn2 = field(d.D, ab);
+  p.h = field(d.F, ab);
+  p.x_out = field(d.D, 4);
+  p.record = off;
+  return p;
+}
+
+// With inject/capture (debug probe): every kernel of every layer reads its input from the
+// inject record and its output is copied to the capture record, so each kernel can be
+// compared with the reference operation on identical inputs.
+static dtd_status run_step(dtd_engine* e, int B, const int* slots, const int* poss,
+                           const int32_t* tokens, int32_t* next, float* logits_out, bool do_head,
+                           const std::vector<Update>& upd, const uint8_t* inject = nullptr,
+                           uint8_t* capture = nullptr) {
+  const Dims& d = e->d;
+  hipStream_t st = e->stream;
+  // descriptor into the next pinned ring slot, then one host->device copy
+  StepDesc* hd = &e->desc_host[e->ring];
+  if (e->desc_ev_used[e->ring]) HIP_OK(e, hipEventSynchronize(e->desc_ev[e->ring]));
+  memset(hd, 0, sizeof(StepDesc));
+  hd->batch = B;
+  hd->do_head = do_head ? 1 : 0;
+  hd->n_updates = (int32_t)upd.size();
+  hd->tokens = tokens;
+  hd->next_tokens = next;
+  hd->logits_out = logits_out;
+  for (int b = 0; b < B; b++) { hd->pos[b] = poss[b]; hd->slot[b] = slots[b]; }
+  for (size_t u = 0; u < upd.size(); u++) {
+    hd->upd[u][0] = upd[u].slot; hd->upd[u][1] = upd[u].lblock; hd->upd[u][2] = upd[u].pblock;
+  }
+  HIP_OK(e, hipMemcpyAsync(e->desc_dev, hd, sizeof(StepDesc), hipMemcpyHostToDevice, st));
+  HIP_OK(e, hipEventRecord(e->desc_ev[e->ring], st));
+  e->desc_ev_used[e->ring] = true;
+  e->ring = (e->ring + 1) % kRing;
+
+  HIP_OK(e, launch_embed(d, e->emb, e->desc_dev, B, e->bt_dev, e->x, e->err_dev, st));
+  const size_t ab = act_bytes(e->cfg.act);
+  const ProbeLayout pl = probe_layout(d, B, ab);
+  const bool probe = inject && capture;
+  auto cp = [&](void* dst, const void* src, size_t n) {
+    return hipMemcpyAsync(dst, src, n, hipMemcpyDeviceToDevice, st);
+  };
+  if (e->capture)
+    HIP_OK(e, hipMemcpyAsync(e->capture, e->x, (size_t)B * d.D * 4, hipMemcpyDeviceToDevice, st));
+  const size_t kvb = kv_elem_bytes(e->cfg.kvfmt);
+  EpiArgs ea{};
+  ea.desc = e->desc_dev;
+  ea.q = e->q; ea.knew = e->knew; ea.vnew = e->vnew;
+  ea.rope_cos = e->rope_cos; ea.rope_sin = e->rope_sin;
+  ea.x = e->x; ea.h = e->h; ea.logits = e->logits;
+  const size_t fx = (size_t)B * d.D * 4, fxn = (size_t)B * d.D * ab, fq = (size_t)B * d.q_dim * 4;
+  const size_t fkv = (size_t)B * d.kv_dim * 4, fo = (size_t)B * d.q_dim * ab, fh = (size_t)B * d.F * ab;
+  for (int l = 0; l < d.L; l++) {
+    const LayerW& W = e->layers[(size_t)l];
+    KvLayer kv;
+    kv.k = (uint8_t*)e->kpool + (size_t)l * e->kv_layer_elems * kvb;
+    kv.v = (uint8_t*)e->vpool + (size_t)l * e->kv_layer_elems * kvb;
+    kv.ks = e->kspool ? e->kspool + (size_t)l * e->kv_layer_scales : nullptr;
+    kv.vs = e->vspool ? e->vspool + (size_t)l * e->kv_layer_scales : nullptr;
+    const uint8_t* in = probe ? inject + (size_t)l * pl.record : nullptr;
+    uint8_t* out = probe ? capture + (size_t)l * pl.record : nullptr;
+    if (probe) {
+      HIP_OK(e, cp(e->x, in + pl.x_in, fx));
+      HIP_OK(e, cp(out + pl.x_in, in + pl.x_in, fx));
+    }
+    HIP_OK(e, launch_rmsnorm(d, e->x, W.attn_norm, e->xn, B, st));
+    if (probe) {
+      HIP_OK(e, cp(out + pl.xn, e->xn, fxn));
+      HIP_OK(e, cp(e->xn, in + pl.xn, fxn));
+    }
+    TIMED(2, launch_gemv(d, W.qkv, e->xn, B, EPI_QKV, ea, st));
+    if (probe) {
+      HIP_OK(e, cp(out + pl.q, e->q, fq));
+      HIP_OK(e, cp(out + pl.k, e->knew, fkv));
+      HIP_OK(e, cp(out + pl.v, e->vnew, fkv));
+      HIP_OK(e, cp(e->q, in + pl.q, fq));
+      HIP_OK(e, cp(e->knew, in + pl.k, fkv));
+      HIP_OK(e, cp(e->vnew, in + pl.v, fkv));
+    }
+    TIMED(4, launch_attention(d, e->desc_dev, B, e->q, e->knew, e->vnew, kv, e->bt_dev, e->partials, st));
+    HIP_OK(e, launch_combine(d, e->desc_dev, B, e->partials, e->o, st));
+    if (probe) {
+      HIP_OK(e, cp(out + pl.o, e->o, fo));
+      HIP_OK(e, cp(e->o, in + pl.o, fo));
+      HIP_OK(e, cp(e->x, in + pl.x_in, fx));
+    }
+    TIMED(3, launch_gemv(d, W.o, e->o, B, EPI_RESID, ea, st));
+    if (probe) {
+      HIP_OK(e, cp(out + pl.x_mid, e->x, fx));
+      HIP_OK(e, cp(e->x, in + pl.x_mid, fx));
+    }
+    HIP_OK(e, launch_rmsnorm(d, e->x, W.ffn_norm, e->xn, B, st));
+    if (probe) {
+      HIP_OK(e, cp(out + pl.xn2, e->xn, fxn));
+      HIP_OK(e, cp(e->xn, in + pl.xn2, fxn));
+    }
+    TIMED(0, launch_gemv(d, W.gu, e->xn, B, EPI_SWIGLU, ea, st));
+    if (probe) {
+      HIP_OK(e, cp(out + pl.h, e->h, fh));
+      HIP_OK(e, cp(e->h, in + pl.h, fh));
+    }
+    TIMED(1, launch_gemv(d, W.down, e->h, B, EPI_RESID, ea, st));
+    if (probe) HIP_OK(e, cp(out + pl.x_out, e->x, fx));
+    if (e->capture)
+      HIP_OK(e, hipMemcpyAsync(e->capture + (size_t)(l + 1) * B * d.D, e->x, (size_t)B * d.D * 4,
+                               hipMemcpyDeviceToDevice, st));
+  }
+  if (probe) HIP_OK(e, cp(e->x, inject + (size_t)(d.L - 1) * pl.record + pl.x_out, fx));
+  if (do_head) {
+    HIP_OK(e, launch_rmsnorm(d, e->x, e->final_norm, e->xn, B, st));
+    TIMED(5, launch_gemv(d, e->head, e->xn, B, EPI_LOGITS, ea, st));
+    HIP_OK(e, launch_argmax(d, e->desc_dev, B, e->logits, st));
+  }
+  HIP_OK(e, hipMemcpyAsync(e->err_host, e->err_dev, 4, hipMemcpyDeviceToHost, st));
+  return DTD_OK;
+}
+
+static dtd_status ready(dtd_engine* e) {
+  if (!e) return DTD_E_ARG;
+  if (e->broken) return fail(e, DTD_E_STATE, "engine unusable after a HIP error");
+  if (!e->loaded) return fail(e, DTD_E_STATE, "weights not loaded");
+  HIP_OK(e, hipSetDevice(e->device));
+  return DTD_OK;
+}
+
+static int blocks_needed(const dtd_engine* e, int len) { return (len + e->d.bs - 1) / e->d.bs; }
+
+extern "C" dtd_status dtd_prefill(dtd_engine* e, int64_t seq_id, const int32_t* tokens_dev, int32_t n,
+                                  int32_t* next_token_dev, float* logits_dev) {
+  dtd_status st = ready(e);
+  if (st) return st;
+  if (!tokens_dev || !next_token_dev || n <= 0) return fail(e, DTD_E_ARG, "prefill: null pointer or n <= 0");
+  auto it = e->seqs.find(seq_id);
+  const bool is_new = it == e->seqs.end();
+  const int len0 = is_new ? 0 : it->second.len;
+  if ((int64_t)len0 + n > e->cfg.max_ctx)
+    return fail(e, DTD_E_CTX, "prefill: %d + %d positions exceed max_ctx %d", len0, n, e->cfg.max_ctx);
+  if (is_new && e->free_slots.empty()) return fail(e, DTD_E_KVFULL, "prefill: no free sequence slot");
+  const int have = is_new ? 0 : (int)it->second.blocks.size();
+  const int need = blocks_needed(e, len0 + n) - have;
+  if (need > (int)e->free_blocks.size())
+    return fail(e, DTD_E_KVFULL, "prefill: needs %d KV blocks, %zu free", need, e->free_blocks.size());
+  if (is_new) {
+    Seq s;
+    s.slot = e->free_slots.back();
+    e->free_slots.pop_back();
+    it = e->seqs.emplace(seq_id, s).first;
+  }
+  Seq& s = it->second;
+  for (int i = 0; i < n; i++) {
+    const int pos = s.len;
+    std::vector<Update> upd;
+    if (pos / e->d.bs >= (int)s.blocks.size()) {
+      const int32_t b = e->free_blocks.back();
+      e->free_blocks.pop_back();
+      s.blocks.push_back(b);
+      upd.push_back({s.slot, (int)s.blocks.size() - 1, b});
+    }
+    const bool last = i == n - 1;
+    st = run_step(e, 1, &s.slot, &pos, tokens_dev + i, next_token_dev, last ? logits_dev : nullptr, last, upd);
+    if (st) return st;
+    s.len++;
+  }
+  return DTD_OK;
+}
+
+static dtd_status decode_impl(dtd_engine* e, int32_t batch, const int64_t* seq_ids_host,
+                              const int32_t* tokens_dev, int32_t* next_tokens_dev, float* logits_dev,
+                              const uint8_t* inject, uint8_t* capture, bool create_missing) {
+  dtd_status st = ready(e);
+  if (st) return st;
+  if (batch <= 0 || batch > e->cfg.max_batch)
+    return fail(e, DTD_E_ARG, "decode_step: batch %d outside [1, %d]", batch, e->cfg.max_batch);
+  if (!seq_ids_host || !tokens_dev || !next_tokens_dev) return fail(e, DTD_E_ARG, "decode_step: null pointer");
+  int need = 0;
+  std::vector<Seq*> ss((size_t)batch);
+  int missing = 0;
+  for (int b = 0; b < batch; b++) {
+    for (int c = 0; c < b; c++)
+      if (seq_ids_host[c] == seq_ids_host[b])
+        return fail(e, DTD_E_ARG, "decode_step: seq_id %lld repeated in the batch", (long long)seq_ids_host[b]);
+    if (create_missing && e->seqs.find(seq_ids_host[b]) == e->seqs.end()) missing++;
+  }
+  if (missing > (int)e->free_slots.size()) return fail(e, DTD_E_KVFULL, "decode_step: no free sequence slot");
+  if (missing > (int)e->free_blocks.size()) return fail(e, DTD_E_KVFULL, "decode_step: no free KV block");
+  for (int b = 0; b < batch && missing; b++)
+    if (e->seqs.find(seq_ids_host[b]) == e->seqs.end()) {
+      Seq s;
+      s.slot = e->free_slots.back();
+      e->free_slots.pop_back();
+      e->seqs.emplace(seq_ids_host[b], s);
+    }
+  for (int b = 0; b < batch; b++) {
+    auto it = e->seqs.find(seq_ids_host[b]);
+    if (it == e->seqs.end()) return fail(e, DTD_E_NOSEQ, "decode_step: unknown seq_id %lld", (long long)seq_ids_host[b]);
+    Seq& s = it->second;
+    if (s.len + 1 > e->cfg.max_ctx)
+      return fail(e, DTD_E_CTX, "decode_step: seq_id %lld is at max_ctx %d", (long long)seq_ids_host[b], e->cfg.max_ctx);
+    if (s.len / e->d.bs >= (int)s.blocks.size()) need++;
+    ss[(size_t)b] = &s;
+  }
+  if (need > (int)e->free_blocks.size())
+    return fail(e, DTD_E_KVFULL, "decode_step: needs %d KV blocks, %zu free", need, e->free_blocks.size());
+  std::vector<int> slots((size_t)batch), poss((size_t)batch);
+  std::vector<Update> upd;
+  for (int b = 0; b < batch; b++) {
+    Seq& s = *ss[(size_t)b];
+    if (s.len / e->d.bs >= (int)s.blocks.size()) {
+      const int32_t blk = e->free_blocks.back();
+      e->free_blocks.pop_back();
+      s.blocks.push_back(blk);
+      upd.push_back({s.slot, (int)s.blocks.size() - 1, blk});
+    }
+    slots[(size_t)b] = s.slot;
+    poss[(size_t)b] = s.len;
+  }
+  st = run_step(e, batch, slots.data(), poss.data(), tokens_dev, next_tokens_dev, logits_dev, true, upd,
+                inject, capture);
+  if (st) return st;
+  for (int b = 0; b < batch; b++) ss[(size_t)b]->len++;
+  return DTD_OK;
+}
+
+extern "C" dtd_status dtd_decode_step(dtd_engine* e, int32_t batch, const int64_t* seq_ids_host,
+                                      const int32_t* tokens_dev, int32_t* next_tokens_dev,
+                                      float* logits_dev) {
+  return decode_impl(e, batch, seq_ids_host, tokens_dev, next_tokens_dev, logits_dev, nullptr, nullptr, false);
+}
+
+extern "C" dtd_status dtd_debug_decode_probe(dtd_engine* e, int32_t batch, const int64_t* seq_ids_host,
+                                             const int32_t* tokens_dev, const void* inject_dev,
+                                             void* capture_dev, int32_t* next_tokens_dev,
+                                             float* logits_dev) {
+  if (e && (!inject_dev || !capture_dev)) return fail(e, DTD_E_ARG, "decode_probe: null buffer");
+  return decode_impl(e, batch, seq_ids_host, tokens_dev, next_tokens_dev, logits_dev,
+                     (const uint8_t*)inject_dev, (uint8_t*)capture_dev, true);
+}
+
+extern "C" int64_t dtd_debug_probe_record_bytes(const dtd_config* cfg, int32_t batch) {
+  const dtd_status st = check_config(cfg, nullptr, 0);
+  if (st != DTD_OK) return st;
+  if (batch <= 0) return DTD_E_ARG;
+  const Dims d = make_dims(cfg);
+  return (int64_t)probe_layout(d, batch, act_bytes(cfg->act)).record;
+}
+
+extern "C" dtd_status dtd_reset_seq(dtd_engine* e, int64_t seq_id) {
+  if (!e) return DTD_E_ARG;
+  auto it = e->seqs.find(seq_id);
+  if (it == e->seqs.end()) return fail(e, DTD_E_NOSEQ, "reset_seq: unknown seq_id %lld", (long long)seq_id);
+  for (auto b = it->second.blocks.rbegin(); b != it->second.blocks.rend(); ++b) e->free_blocks.push_back(*b);
+  e->free_slots.push_back(it->second.slot);
+  e->seqs.erase(it);
+  return DTD_OK;
+}
+
+extern "C" int32_t dtd_seq_len(const dtd_engine* e, int64_t seq_id) {
+  if (!e) return DTD_E_ARG;
+  auto it = e->seqs.find(seq_id);
+  return it == e->seqs.end() ? DTD_E_NOSEQ : it->second.len;
+}
+
+extern "C" dtd_status dtd_check_device_errors(dtd_engine* e) {
+  if (!e) return DTD_E_ARG;
+  if (e->broken) return fail(e, DTD_E_STATE, "engine unusable after a HIP error");
+  HIP_OK(e, hipSetDevice(e->device));
+  HIP_OK(e, hipStreamSynchronize(e->stream));
+  if (*e->err_host) {
+    *e->err_host = 0;
+    HIP_OK(e, hipMemsetAsync(e->err_dev, 0, 4, e->stream));
+    HIP_OK(e, hipStreamSynchronize(e->stream));
+    return fail(e, DTD_E_ARG, "a token id outside [0, %d) was read on the device (used as id 0)", e->d.V);
+  }
+  return DTD_OK;
+}
+
+// ---------------------------------------------------------------------------------------
+// debug / measurement
+// ---------------------------------------------------------------------------------------
+
+extern "C" dtd_status dtd_debug_dequant_rows(dtd_engine* e, const char* matrix, int32_t r0, int32_t nrows,
+                                             float* out_dev) {
+  dtd_status st = ready(e);
+  if (st) return st;
+  if (!matrix || !out_dev || nrows <= 0 || r0 < 0) return fail(e, DTD_E_ARG, "dequant_rows: bad arguments");
+  const Dims& d = e->d;
+  const std::string name = matrix;
+  const MatDev* m = nullptr;
+  int rows = 0;
+  std::vector<int32_t> map;
+  int li = -1;
+  char field[32] = {0};
+  if (name == "tok_emb" || (name == "lm_head" && !e->cfg.tied_embeddings)) {
+    m = name == "tok_emb" ? &e->emb : &e->head;
+    rows = d.V;
+    for (int r = r0; r < r0 + nrows && r < rows; r++) map.push_back(r);
+  } else if (sscanf(name.c_str(), "L%d.%31s", &li, field) == 2 && li >= 0 && li < d.L) {
+    const LayerW& W = e->layers[(size_t)li];
+    const std::string f = field;
+    if (f == "wq" || f == "wk" || f == "wv") {
+      const int part = f == "wq" ? 0 : (f == "wk" ? 1 : 2);
+      rows = part == 0 ? d.q_dim : d.kv_dim;
+      m = &W.qkv;
+      for (int r = r0; r < r0 + nrows && r < rows; r++) map.push_back(qkv_stored_row(d, part, r));
+    } else if (f == "w_gate" || f == "w_up") {
+      rows = d.F;
+      m = &W.gu;
+      for (int r = r0; r < r0 + nrows && r < rows; r++) map.push_back(2 * r + (f == "w_up"));
+    } else if (f == "wo" || f == "w_down") {
+      rows = d.D;
+      m = f == "wo" ? &W.o : &W.down;
+      for (int r = r0; r < r0 + nrows && r < rows; r++) map.push_back(r);
+    }
+  }
+  if (!m) return fail(e, DTD_E_ARG, "dequant_rows: unknown matrix '%s'", matrix);
+  if ((int)map.size() != nrows) return fail(e, DTD_E_ARG, "dequant_rows: rows [%d, %d) outside [0, %d)", r0, r0 + nrows, rows);
+  if (e->rows_cap < nrows) {
+    if (e->rows_dev) HIP_OK(e, hipFree(e->rows_dev));
+    e->rows_dev = nullptr;
+    e->rows_cap = 0;
+    if ((st = dev_alloc(e, &e->rows_dev, (size_t)nrows * 4))) return st;
+    e->rows_cap = nrows;
+  }
+  HIP_OK(e, hipStreamSynchronize(e->stream));
+  HIP_OK(e, hipMemcpy(e->rows_dev, map.data(), (size_t)nrows * 4, hipMemcpyHostToDevice));
+  HIP_OK(e, launch_dequant_rows(d, *m, e->rows_dev, nrows, out_dev, e->stream));
+  HIP_OK(e, hipStreamSynchronize(e->stream));
+  return DTD_OK;
+}
+
+extern "C" dtd_status dtd_debug_capture_hidden(dtd_engine* e, int32_t enable, float* out_dev) {
+  if (!e) return DTD_E_ARG;
+  if (enable && !out_dev) return fail(e, DTD_E_ARG, "capture_hidden: null buffer");
+  e->capture = enable ? out_dev : nullptr;
+  return DTD_OK;
+}
+
+// make sure a sequence exists with blocks for [0, len); new block-table entries are written
+// synchronously (the debug entry points are synchronous)
+static dtd_status ensure_seq_blocks(dtd_engine* e, int64_t seq_id, int len, Seq** out) {
+  auto it = e->seqs.find(seq_id);
+  if (it == e->seqs.end()) {
+    if (e->free_slots.empty()) return fail(e, DTD_E_KVFULL, "no free sequence slot");
+    Seq s;
+    s.slot = e->free_slots.back();
+    e->free_slots.pop_back();
+    it = e->seqs.emplace(seq_id, s).first;
+  }
+  Seq& s = it->second;
+  const int need = blocks_needed(e, len) - (int)s.blocks.size();
+  if (need > (int)e->free_blocks.size()) return fail(e, DTD_E_KVFULL, "needs %d KV blocks, %zu free", need, e->free_blocks.size());
+  if (need > 0) {
+    for (int i = 0; i < need; i++) {
+      s.blocks.push_back(e->free_blocks.back());
+      e->free_blocks.pop_back();
+    }
+    HIP_OK(e, hipStreamSynchronize(e->stream));
+    HIP_OK(e, hipMemcpy(e->bt_dev + (size_t)s.slot * e->d.max_blocks, s.blocks.data(), s.blocks.size() * 4,
+                        hipMemcpyHostToDevice));
+  }
+  *out = &s;
+  return DTD_OK;
+}
+
+static dtd_status kv_copy(dtd_engine* e, int64_t seq_id, int32_t layer, int32_t pos0, int32_t n,
+                          void* k, void* v, void* ks, void* vs, bool write) {
+  dtd_status st = ready(e);
+  if (st) return st;
+  const Dims& d = e->d;
+  if (layer < 0 || layer >= d.L || pos0 < 0 || n <= 0 || (int64_t)pos0 + n > e->cfg.max_ctx || !k || !v)
+    return fail(e, DTD_E_ARG, "kv copy: bad layer/range/pointer");
+  const bool i8 = e->cfg.kvfmt == DTD_KV_I8;
+  if (i8 && (!ks || !vs)) return fail(e, DTD_E_ARG, "kv copy: int8 KV needs scale buffers");
+  Seq* s = nullptr;
+  if (write) {
+    if ((st = ensure_seq_blocks(e, seq_id, pos0 + n, &s))) return st;
+  } else {
+    auto it = e->seqs.find(seq_id);
+    if (it == e->seqs.end()) return fail(e, DTD_E_NOSEQ, "kv read: unknown seq_id");
+    s = &it->second;
+    if (pos0 + n > (int)s->blocks.size() * d.bs) return fail(e, DTD_E_ARG, "kv read: positions not allocated");
+  }
+  HIP_OK(e, hipStreamSynchronize(e->stream));
+  // one block of one layer is [Hkv][bs][hd] (+ scales [Hkv][bs]): copy it whole, patch the
+  // touched positions on the host, copy it back
+  const size_t eb = kv_elem_bytes(e->cfg.kvfmt);
+  const size_t rowb = (size_t)d.hd * eb;
+  const size_t blkb = (size_t)d.Hkv * d.bs * rowb;
+  const size_t blks = (size_t)d.Hkv * d.bs;
+  uint8_t* kb = (uint8_t*)e->kpool + (size_t)layer * e->kv_layer_elems * eb;
+  uint8_t* vb = (uint8_t*)e->vpool + (size_t)layer * e->kv_layer_elems * eb;
+  uint16_t* ksb = i8 ? e->kspool + (size_t)layer * e->kv_layer_scales : nullptr;
+  uint16_t* vsb = i8 ? e->vspool + (size_t)layer * e->kv_layer_scales : nullptr;
+  std::vector<uint8_t> img(blkb);
+  std::vector<uint16_t> simg(blks);
+  for (int which = 0; which < 2; which++) {
+    uint8_t* pool = which ? vb : kb;
+    uint16_t* spool = which ? vsb : ksb;
+    uint8_t* host = (uint8_t*)(which ? v : k);
+    uint16_t* hsc = (uint16_t*)(which ? vs : ks);
+    for (int lb = pos0 / d.bs; lb <= (pos0 + n - 1) / d.bs; lb++) {
+      const size_t blk = (size_t)s->blocks[(size_t)lb];
+      const int t_lo = std::max(pos0, lb * d.bs), t_hi = std::min(pos0 + n, (lb + 1) * d.bs);
+      HIP_OK(e, hipMemcpy(img.data(), pool + blk * blkb, blkb, hipMemcpyDeviceToHost));
+      if (i8) HIP_OK(e, hipMemcpy(simg.data(), spool + blk * blks, blks * 2, hipMemcpyDeviceToHost));
+      for (int pos = t_lo; pos < t_hi; pos++) {
+        const int off = pos - lb * d.bs, t = pos - pos0;
+        for (int j = 0; j < d.Hkv; j++) {
+          uint8_t* dev_row = img.data() + ((size_t)j * d.bs + off) * rowb;
+          uint8_t* host_row = host + ((size_t)t * d.Hkv + j) * rowb;
+          uint16_t* dev_s = simg.data() + (size_t)j * d.bs + off;
+          uint16_t* host_s = i8 ? hsc + (size_t)t * d.Hkv + j : nullptr;
+          if (write) {
+            memcpy(dev_row, host_row, rowb);
+            if (i8) *dev_s = *host_s;
+          } else {
+            memcpy(host_row, dev_row, rowb);
+            if (i8) *host_s = *dev_s;
+          }
+        }
+      }
+      if (write) {
+        HIP_OK(e, hipMemcpy(pool + blk * blkb, img.data(), blkb, hipMemcpyHostToDevice));
+        if (i8) HIP_OK(e, hipMemcpy(spool + blk * blks, simg.data(), blks * 2, hipMemcpyHostToDevice));
+      }
+    }
+  }
+  if (write && pos0 + n > s->len) s->len = pos0 + n;
+  return DTD_OK;
+}
+
+extern "C" dtd_status dtd_debug_kv_write(dtd_engine* e, int64_t seq_id, int32_t layer, int32_t pos0,
+                                         int32_t n, const void* k, const void* v, const void* k_scale,
+                                         const void* v_scale) {
+  return kv_copy(e, seq_id, layer, pos0, n, (void*)k, (void*)v, (void*)k_scale, (void*)v_scale, true);
+}
+
+extern "C" dtd_status dtd_debug_kv_read(dtd_engine* e, int64_t seq_id, int32_t layer, int32_t pos0,
+                                        int32_t n, void* k, void* v, void* k_scale, void* v_scale) {
+  return kv_copy(e, seq_id, layer, pos0, n, k, v, k_scale, v_scale, false);
+}
+
+extern "C" dtd_status dtd_debug_kv_fill(dtd_engine* e, int64_t seq_id, int32_t len, uint64_t seed) {
+  dtd_status st = ready(e);
+  if (st) return st;
+  if (len <= 0 || len > e->cfg.max_ctx) return fail(e, DTD_E_ARG, "kv_fill: len %d outside [1, max_ctx]", len);
+  Seq* s = nullptr;
+  if ((st = ensure_seq_blocks(e, seq_id, len, &s))) return st;
+  const Dims& d = e->d;
+  const int nblk = blocks_needed(e, len);
+  int32_t* blocks_dev = nullptr;
+  if ((st = dev_alloc(e, &blocks_dev, (size_t)nblk * 4))) return st;
+  hipError_t r = hipMemcpy(blocks_dev, s->blocks.data(), (size_t)nblk * 4, hipMemcpyHostToDevice);
+  const size_t eb = kv_elem_bytes(e->cfg.kvfmt);
+  for (int l = 0; l < d.L && r == hipSuccess; l++) {
+    KvLayer kv;
+    kv.k = (uint8_t*)e->kpool + (size_t)l * e->kv_layer_elems * eb;
+    kv.v = (uint8_t*)e->vpool + (size_t)l * e->kv_layer_elems * eb;
+    kv.ks = e->kspool ? e->kspool + (size_t)l * e->kv_layer_scales : nullptr;
+    kv.vs = e->vspool ? e->vspool + (size_t)l * e->kv_layer_scales : nullptr;
+    r = launch_kv_fill(d, kv, blocks_dev, nblk, len, l, seed, e->stream);
+  }
+  if (r == hipSuccess) r = hipStreamSynchronize(e->stream);
+  (void)hipFree(blocks_dev);
+  if (r != hipSuccess) {
+    e->broken = true;
+    return fail(e, DTD_E_HIP, "kv_fill: %s", hipGetErrorString(r));
+  }
+  if (len > s->len) s->len = len;
+  return DTD_OK;
+}
+
+extern "C" dtd_status dtd_debug_kernel_timing(dtd_engine* e, int32_t kind, int32_t enable, double* total_ms,
+                                              int64_t* count) {
+  if (!e) return DTD_E_ARG;
+  if (kind < 0 || kind > 5) return fail(e, DTD_E_ARG, "kernel_timing: kind %d outside [0, 5]", kind);
+  HIP_OK(e, hipSetDevice(e->device));
+  double total = 0.0;
+  int64_t cnt = 0;
+  if (e->timing_kind == kind && e->timers_used) {
+    HIP_OK(e, hipStreamSynchronize(e->stream));
+    for (size_t i = 0; i < e->timers_used; i++) {
+      float ms = 0.f;
+      HIP_OK(e, hipEventElapsedTime(&ms, e->timers[i].a, e->timers[i].b));
+      total += ms;
+      cnt++;
+    }
+  }
+  e->timers_used = 0;
+  e->timing_kind = enable ? kind : (e->timing_kind == kind ? -1 : e->timing_kind);
+  if (total_ms) *total_ms = total;
+  if (count) *count = cnt;
+  return DTD_OK;
+}

@@ -1,0 +1,713 @@
+// dtd_kernels.hip -- gfx950 (MI355X, CDNA4) kernels of the Llama-family decode step.
+//
+// Decode at small batch is bound by HBM traffic: every weight byte is read once per
+// step and used for B multiply-adds ("从 smollm3.go 看 LLM inference", int8 weight-only
+// quantization section: the int8 path exists to cut weight-memory traffic).  The kernels
+// are therefore shaped around streaming weights with 16-byte coalesced loads per lane,
+// dequantising in registers, keeping activations in LDS, and reducing across the 64-wide
+// wavefront with cross-lane shuffles.  Everything that does not move weight or KV bytes
+// (RMSNorm scaling, RoPE, KV append, SwiGLU, residual adds, argmax) rides in the
+// prologues and epilogues of those kernels.
+#include <math.h>
+#include <stdint.h>
+#include <limits.h>
+
+#include "dtd_internal.h"
+
+namespace dtd {
+namespace {
+
+// ---------------------------------------------------------------------------------------
+// scalar helpers
+// ---------------------------------------------------------------------------------------
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t b16) { return __uint_as_float(b16 << 16); }
+
+// float -> bf16, round to nearest even (NaN kept quiet)
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ float round_act(float v, int act) {
+  return act == ACT_BF16 ? bf16_to_f32(f32_to_bf16(v)) : v;
+}
+
+__device__ __forceinline__ float f16_to_f32(uint16_t h) {
+  return (float)__builtin_bit_cast(_Float16, h);
+}
+
+__device__ __forceinline__ uint16_t f32_to_f16(float f) {  // hardware convert, RNE
+  return __builtin_bit_cast(uint16_t, (_Float16)f);
+}
+
+__device__ __forceinline__ float sext8(uint32_t u, int byte) {
+  return (float)((int32_t)(u << (24 - 8 * byte)) >> 24);
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
+  return v;
+}
+
+// sum over a 256-thread block; every thread gets the result
+__device__ __forceinline__ float block_sum256(float v, float* red) {
+  v = wave_sum(v);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __syncthreads();
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  return red[0] + red[1] + red[2] + red[3];
+}
+
+__device__ __forceinline__ float block_max256(float v, float* red) {
+  v = wave_max(v);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __syncthreads();
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+
+// one stored weight element as fp32: int8-row q*s, Q8_0 q*d (one fp32 product), bf16 widen
+__device__ __forceinline__ float deq_elem(const MatDev& m, int wfmt, int r, int c) {
+  const size_t e = (size_t)r * m.cols + c;
+  if (wfmt == W_INT8_ROW) return (float)((const int8_t*)m.w)[e] * ((const float*)m.s)[r];
+  if (wfmt == W_Q8_0)
+    return (float)((const int8_t*)m.w)[e] *
+           f16_to_f32(((const uint16_t*)m.s)[(size_t)r * (m.cols / 32) + c / 32]);
+  return bf16_to_f32(((const uint16_t*)m.w)[e]);
+}
+
+// ---------------------------------------------------------------------------------------
+// S0 embedding (+ block-table updates of this step)
+// ---------------------------------------------------------------------------------------
+
+__global__ __launch_bounds__(256) void k_embed(Dims d, MatDev emb, const StepDesc* desc,
+                                               int32_t* bt, float* x, int32_t* err) {
+  const int b = blockIdx.x;
+  if (b == 0) {
+    for (int u = threadIdx.x; u < desc->n_updates; u += blockDim.x)
+      bt[(size_t)desc->upd[u][0] * d.max_blocks + desc->upd[u][1]] = desc->upd[u][2];
+  }
+  int t = desc->tokens[b];
+  if (t < 0 || t >= d.V) {
+    if (threadIdx.x == 0) atomicOr(err, 1);
+    t = 0;
+  }
+  float* xb = x + (size_t)b * d.D;
+  for (int i = threadIdx.x; i < d.D; i += blockDim.x) xb[i] = deq_elem(emb, d.wfmt, t, i);
+}
+
+// ---------------------------------------------------------------------------------------
+// S1 / S7 / S10 RMSNorm: xn = round_act(x / sqrt(mean(x^2) + eps) * g)
+// ---------------------------------------------------------------------------------------
+
+__global__ __launch_bounds__(256) void k_rmsnorm(const float* x, const float* g, void* xn, int D,
+                                                 float eps, int act) {
+  __shared__ float red[4];
+  const int b = blockIdx.x;
+  const float* xb = x + (size_t)b * D;
+  float ss = 0.f;
+  for (int i = threadIdx.x; i < D; i += 256) ss += xb[i] * xb[i];
+  ss = block_sum256(ss, red);
+  const float r = 1.0f / sqrtf(ss / (float)D + eps);
+  if (act == ACT_BF16) {
+    uint16_t* o = (uint16_t*)xn + (size_t)b * D;
+    for (int i = threadIdx.x; i < D; i += 256) o[i] = f32_to_bf16(xb[i] * r * g[i]);
+  } else {
+    float* o = (float*)xn + (size_t)b * D;
+    for (int i = threadIdx.x; i < D; i += 256) o[i] = xb[i] * r * g[i];
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// S2 / S6 / S8 / S9 / S10 weight-streaming GEMV with fused epilogues
+//
+// A 256-thread block = 4 waves; each wave owns ROWS consecutive stored rows and all NB
+// batch columns of its grid.y slice.  Per K step each lane loads one 16-byte vector of
+// each row (16 int8 codes or 8 bf16), reads the matching activations from LDS, and
+// accumulates in fp32.  The activation chunk is staged into LDS in a swizzled order so
+// that lane l's j-th float4 of a K step sits at float4 index (j*64 + l): the wave's
+// ds_read_b128 then covers consecutive addresses and is free of bank conflicts.
+// ---------------------------------------------------------------------------------------
+
+struct GemvArgs {
+  Dims d;
+  MatDev m;
+  const void* xin;   // [B][K] activations (fp32 or bf16)
+  int B;
+  int act_in;
+  int kc;            // activation chunk length staged in LDS (multiple of the K step)
+  EpiArgs ea;
+};
+
+template <int WFMT> struct WVec { static constexpr int VEC = 16; static constexpr int EB = 1; };
+template <> struct WVec<W_BF16> { static constexpr int VEC = 8; static constexpr int EB = 2; };
+
+template <int EPI, int ROWS>
+__device__ __forceinline__ void gemv_epilogue(const GemvArgs& a, int b, int row0, const float* v) {
+  const int N = a.m.rows;
+  const Dims& d = a.d;
+  if constexpr (EPI == EPI_QKV) {
+    // Stored QKV rows: q and k heads hold the RoPE pairs (i, i + hd/2) as adjacent rows
+    // (2i, 2i+1); v rows are in natural order.
+    const int pos = a.ea.desc->pos[b];
+    const int half = d.hd >> 1;
+#pragma unroll
+    for (int i = 0; i < ROWS; i += 2) {
+      const int n = row0 + i;
+      if (n >= N) break;
+      const float u = v[i], w = v[i + 1];
+      if (n < d.q_dim + d.kv_dim) {
+        const bool isq = n < d.q_dim;
+        const int nn = isq ? n : n - d.q_dim;
+        const int h = nn / d.hd, p = (nn - h * d.hd) >> 1;
+        const float c = a.ea.rope_cos[(size_t)pos * half + p];
+        const float s = a.ea.rope_sin[(size_t)pos * half + p];
+        float* dst = isq ? a.ea.q + (size_t)b * d.q_dim : a.ea.knew + (size_t)b * d.kv_dim;
+        dst[h * d.hd + p] = u * c - w * s;
+        dst[h * d.hd + p + half] = u * s + w * c;
+      } else {
+        const int nn = n - d.q_dim - d.kv_dim;
+        a.ea.vnew[(size_t)b * d.kv_dim + nn] = u;
+        a.ea.vnew[(size_t)b * d.kv_dim + nn + 1] = w;
+      }
+    }
+  } else if constexpr (EPI == EPI_RESID) {
+#pragma unroll
+    for (int i = 0; i < ROWS; i++)
+      if (row0 + i < N) a.ea.x[(size_t)b * N + row0 + i] += v[i];
+  } else if constexpr (EPI == EPI_SWIGLU) {
+    // stored rows (2f, 2f+1) = (gate f, up f)
+#pragma unroll
+    for (int i = 0; i < ROWS; i += 2) {
+      const int n = row0 + i;
+      if (n >= N) break;
+      const int f = n >> 1;
+      const float gt = v[i], up = v[i + 1];
+      const float hv = gt / (1.0f + expf(-gt)) * up;
+      if (d.act == ACT_BF16)
+        ((uint16_t*)a.ea.h)[(size_t)b * d.F + f] = f32_to_bf16(hv);
+      else
+        ((float*)a.ea.h)[(size_t)b * d.F + f] = hv;
+    }
+  } else {  // EPI_LOGITS
+    float* out = a.ea.desc->logits_out;
+#pragma unroll
+    for (int i = 0; i < ROWS; i++) {
+      const int r = row0 + i;
+      if (r < N) {
+        a.ea.logits[(size_t)b * N + r] = v[i];
+        if (out) out[(size_t)b * N + r] = v[i];
+      }
+    }
+  }
+}
+
+template <int WFMT, int EPI, int NB, int ROWS>
+__global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
+  constexpr int VEC = WVec<WFMT>::VEC;
+  constexpr int EB = WVec<WFMT>::EB;
+  constexpr int KSTEP = 64 * VEC;
+  extern __shared__ float xs[];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int N = a.m.rows, K = a.m.cols;
+  const int row0 = (blockIdx.x * 4 + wave) * ROWS;
+  const int b0 = blockIdx.y * NB;
+  const int nb = min(NB, a.B - b0);
+  const int KCP = a.kc;
+  const uint8_t* wbase = (const uint8_t*)a.m.w;
+  const size_t row_bytes = (size_t)K * EB;
+
+  float acc[ROWS][NB];
+#pragma unroll
+  for (int i = 0; i < ROWS; i++)
+#pragma unroll
+    for (int bb = 0; bb < NB; bb++) acc[i][bb] = 0.f;
+
+  for (int kc0 = 0; kc0 < K; kc0 += KCP) {
+    const int kcn = min(KCP, K - kc0);
+    const int kcpad = (kcn + KSTEP - 1) / KSTEP * KSTEP;
+    if (kc0) __syncthreads();
+    for (int idx = threadIdx.x; idx < NB * kcpad; idx += 256) {
+      const int bb = idx / kcpad, kk = idx - bb * kcpad;
+      float v = 0.f;
+      if (bb < nb && kk < kcn) {
+        const size_t gi = (size_t)(b0 + bb) * K + kc0 + kk;
+        v = a.act_in == ACT_BF16 ? bf16_to_f32(((const uint16_t*)a.xin)[gi])
+                                 : ((const float*)a.xin)[gi];
+      }
+      const int st = kk / KSTEP, r = kk - st * KSTEP, ln = r / VEC, j = r - ln * VEC;
+      xs[bb * KCP + st * KSTEP + (j >> 2) * 256 + ln * 4 + (j & 3)] = v;
+    }
+    __syncthreads();
+
+    for (int ks = 0; ks < kcn; ks += KSTEP) {
+      const int kl = ks + lane * VEC;
+      const bool kvalid = kl < kcn;
+      const int k = kc0 + kl;
+      uint4 wv[ROWS];
+      float qs[ROWS];
+#pragma unroll
+      for (int i = 0; i < ROWS; i++) {
+        const int r = row0 + i;
+        const bool ok = kvalid && r < N;
+        wv[i] = ok ? *(const uint4*)(wbase + (size_t)r * row_bytes + (size_t)k * EB)
+                   : make_uint4(0u, 0u, 0u, 0u);
+        if constexpr (WFMT == W_Q8_0)
+          qs[i] = ok ? f16_to_f32(((const uint16_t*)a.m.s)[(size_t)r * (K / 32) + (k >> 5)]) : 0.f;
+      }
+#pragma unroll
+      for (int bb = 0; bb < NB; bb++) {
+        float xv[VEC];
+        const float4* xp = (const float4*)(xs + bb * KCP + ks) + lane;
+#pragma unroll
+        for (int jj = 0; jj < VEC / 4; jj++) {
+          const float4 t = xp[jj * 64];
+          xv[4 * jj + 0] = t.x; xv[4 * jj + 1] = t.y; xv[4 * jj + 2] = t.z; xv[4 * jj + 3] = t.w;
+        }
+#pragma unroll
+        for (int i = 0; i < ROWS; i++) {
+          const uint32_t u[4] = {wv[i].x, wv[i].y, wv[i].z, wv[i].w};
+          if constexpr (WFMT == W_BF16) {
+            float s = acc[i][bb];
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+              s += __uint_as_float(u[q] << 16) * xv[2 * q];
+              s += __uint_as_float(u[q] & 0xffff0000u) * xv[2 * q + 1];
+            }
+            acc[i][bb] = s;
+          } else {
+            float s = 0.f;
+#pragma unroll
+            for (int q = 0; q < 4; q++)
+#pragma unroll
+              for (int by = 0; by < 4; by++) s += sext8(u[q], by) * xv[4 * q + by];
+            if constexpr (WFMT == W_Q8_0) acc[i][bb] += qs[i] * s;
+            else acc[i][bb] += s;
+          }
+        }
+      }
+    }
+  }
+
+#pragma unroll
+  for (int i = 0; i < ROWS; i++)
+#pragma unroll
+    for (int bb = 0; bb < NB; bb++) acc[i][bb] = wave_sum(acc[i][bb]);
+
+  if (lane == 0) {
+    for (int bb = 0; bb < nb; bb++) {
+      float v[ROWS];
+#pragma unroll
+      for (int i = 0; i < ROWS; i++) {
+        v[i] = acc[i][bb];
+        if constexpr (WFMT == W_INT8_ROW)
+          if (row0 + i < N) v[i] *= ((const float*)a.m.s)[row0 + i];  // scale after the dot
+      }
+      gemv_epilogue<EPI, ROWS>(a, b0 + bb, row0, v);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// S4 + S5 split-K GQA decode attention with the KV append of the new token
+//
+// Work item = (chunk c, kv head j, sequence b).  The item streams positions
+// [c*ct, min((c+1)*ct, pos+1)) of head j through LDS in 64-position tiles; the G query
+// heads that share kv head j all use each staged K/V row, so K/V is read once per query
+// group (the GQA decode rule of the Qwen3-8B engine article, 4.4.2).  Softmax is online
+// across tiles (running max, running sum, rescaled accumulators); each item leaves an
+// unnormalised partial (acc, m, l) per head that k_combine merges.  The item whose chunk
+// holds the new position rounds the new k/v to the KV encoding, writes it through the
+// block table and uses the stored value.
+// ---------------------------------------------------------------------------------------
+
+struct AttnArgs {
+  Dims d;
+  const StepDesc* desc;
+  const float* q;
+  const float* knew;
+  const float* vnew;
+  KvLayer kv;
+  const int32_t* bt;
+  float* partials;   // [B][Hq][nch][hd+2]
+};
+
+constexpr int kMaxOutPerThread = 8;   // G*hd <= 2048
+
+template <int KVFMT>
+__device__ __forceinline__ void stage_tile(const AttnArgs& a, const void* pool, const uint16_t* spool,
+                                           const int32_t* btrow, int j, int t0, int n, int pos,
+                                           const float* newv, float* t_s, int ldk) {
+  const Dims& d = a.d;
+  const int hd = d.hd, per = hd >> 2;
+  for (int e = threadIdx.x; e < n * per; e += 256) {
+    const int tl = e / per, i = (e - tl * per) * 4, t = t0 + tl;
+    float v0, v1, v2, v3;
+    if (t == pos) {
+      v0 = newv[i]; v1 = newv[i + 1]; v2 = newv[i + 2]; v3 = newv[i + 3];
+    } else {
+      const int blk = btrow[t / d.bs], off = t - (t / d.bs) * d.bs;
+      const size_t row = ((size_t)blk * d.Hkv + j) * d.bs + off;
+      const size_t base = row * hd + i;
+      if constexpr (KVFMT == KV_F32) {
+        const float4 f = *(const float4*)((const float*)pool + base);
+        v0 = f.x; v1 = f.y; v2 = f.z; v3 = f.w;
+      } else if constexpr (KVFMT == KV_BF16) {
+        const uint2 u = *(const uint2*)((const uint16_t*)pool + base);
+        v0 = __uint_as_float(u.x << 16); v1 = __uint_as_float(u.x & 0xffff0000u);
+        v2 = __uint_as_float(u.y << 16); v3 = __uint_as_float(u.y & 0xffff0000u);
+      } else {
+        const uint32_t u = *(const uint32_t*)((const int8_t*)pool + base);
+        const float s = f16_to_f32(spool[row]);
+        v0 = sext8(u, 0) * s; v1 = sext8(u, 1) * s; v2 = sext8(u, 2) * s; v3 = sext8(u, 3) * s;
+      }
+    }
+    float* dst = t_s + tl * ldk + i;
+    dst[0] = v0; dst[1] = v1; dst[2] = v2; dst[3] = v3;
+  }
+}
+
+template <int KVFMT>
+__global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
+  const Dims& d = a.d;
+  const int c = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
+  const int pos = a.desc->pos[b];
+  const int len = pos + 1;
+  const int t_begin = c * d.ct;
+  if (t_begin >= len) return;
+  const int t_end = min(len, t_begin + d.ct);
+  const int slot = a.desc->slot[b];
+  const int hd = d.hd, G = d.G, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int ldk = hd + 1;
+  const int32_t* btrow = a.bt + (size_t)slot * d.max_blocks;
+
+  extern __shared__ float sm[];
+  float* q_s = sm;                          // [G][hd], pre-scaled by 1/sqrt(hd)
+  float* t_s = q_s + G * hd;                // [64][hd+1]: K tile, then V tile
+  float* p_s = t_s + kAttnTile * ldk;       // [G][64]: scores, then probabilities
+  float* st_s = p_s + G * kAttnTile;        // [G][4]: running max, running sum, rescale
+  float* new_s = st_s + G * 4;              // [2][hd]: stored (decoded) new k, v
+  float* red = new_s + 2 * hd;              // [4] reduction scratch
+
+  const float scale = 1.0f / sqrtf((float)hd);
+  for (int e = tid; e < G * hd; e += 256)
+    q_s[e] = a.q[(size_t)b * d.q_dim + (size_t)j * G * hd + e] * scale;
+  for (int g = tid; g < G; g += 256) { st_s[g * 4] = -INFINITY; st_s[g * 4 + 1] = 0.f; }
+
+  if (pos >= t_begin && pos < t_end) {  // this item appends the new token of head j
+    const int blk = btrow[pos / d.bs], off = pos - (pos / d.bs) * d.bs;
+    const size_t row = ((size_t)blk * d.Hkv + j) * d.bs + off;
+    for (int which = 0; which < 2; which++) {
+      const float* src = (which ? a.vnew : a.knew) + (size_t)b * d.kv_dim + (size_t)j * hd;
+      void* pool = which ? a.kv.v : a.kv.k;
+      const float xv = tid < hd ? src[tid] : 0.f;
+      if constexpr (KVFMT == KV_F32) {
+        if (tid < hd) { ((float*)pool)[row * hd + tid] = xv; new_s[which * hd + tid] = xv; }
+      } else if constexpr (KVFMT == KV_BF16) {
+        if (tid < hd) {
+          const uint16_t bits = f32_to_bf16(xv);
+          ((uint16_t*)pool)[row * hd + tid] = bits;
+          new_s[which * hd + tid] = bf16_to_f32(bits);
+        }
+      } else {
+        const float amax = block_max256(fabsf(xv), red);
+        const uint16_t s16 = f32_to_f16(amax / 127.0f);
+        const float s = f16_to_f32(s16);
+        float qv = 0.f;
+        if (s != 0.f) qv = fminf(fmaxf(rintf(xv / s), -127.f), 127.f);
+        if (tid < hd) {
+          ((int8_t*)pool)[row * hd + tid] = (int8_t)qv;
+          new_s[which * hd + tid] = qv * s;
+        }
+        if (tid == 0) (which ? a.kv.vs : a.kv.ks)[row] = s16;
+      }
+    }
+  }
+  __syncthreads();
+
+  float acc[kMaxOutPerThread];
+#pragma unroll
+  for (int k = 0; k < kMaxOutPerThread; k++) acc[k] = 0.f;
+
+  for (int t0 = t_begin; t0 < t_end; t0 += kAttnTile) {
+    const int n = min(kAttnTile, t_end - t0);
+    stage_tile<KVFMT>(a, a.kv.k, a.kv.ks, btrow, j, t0, n, pos, new_s, t_s, ldk);
+    __syncthreads();
+    for (int sidx = tid; sidx < G * kAttnTile; sidx += 256) {
+      const int g = sidx / kAttnTile, tl = sidx - g * kAttnTile;
+      float s = -INFINITY;
+      if (tl < n) {
+        s = 0.f;
+        const float* qg = q_s + g * hd;
+        const float* kr = t_s + tl * ldk;
+        for (int i = 0; i < hd; i++) s += qg[i] * kr[i];
+      }
+      p_s[sidx] = s;
+    }
+    __syncthreads();
+    for (int g = wave; g < G; g += 4) {
+      const float s = p_s[g * kAttnTile + lane];
+      const float mt = wave_max(s);
+      const float mo = st_s[g * 4], lo = st_s[g * 4 + 1];
+      const float mn = fmaxf(mo, mt);
+      const float p = lane < n ? expf(s - mn) : 0.f;
+      const float ps = wave_sum(p);
+      p_s[g * kAttnTile + lane] = p;
+      if (lane == 0) {
+        const float al = expf(mo - mn);
+        st_s[g * 4] = mn;
+        st_s[g * 4 + 1] = lo * al + ps;
+        st_s[g * 4 + 2] = al;
+      }
+    }
+    __syncthreads();
+    stage_tile<KVFMT>(a, a.kv.v, a.kv.vs, btrow, j, t0, n, pos, new_s + hd, t_s, ldk);
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < kMaxOutPerThread; k++) {
+      const int oi = tid + k * 256;
+      if (oi < G * hd) {
+        const int g = oi / hd, i = oi - g * hd;
+        const float* pg = p_s + g * kAttnTile;
+        float sum = 0.f;
+        for (int tl = 0; tl < n; tl++) sum += pg[tl] * t_s[tl * ldk + i];
+        acc[k] = acc[k] * st_s[g * 4 + 2] + sum;
+      }
+    }
+    __syncthreads();
+  }
+
+  const int c_stride = hd + 2;
+#pragma unroll
+  for (int k = 0; k < kMaxOutPerThread; k++) {
+    const int oi = tid + k * 256;
+    if (oi < G * hd) {
+      const int g = oi / hd, i = oi - g * hd, h = j * G + g;
+      a.partials[(((size_t)b * d.Hq + h) * d.nch + c) * c_stride + i] = acc[k];
+    }
+  }
+  for (int g = tid; g < G; g += 256) {
+    const int h = j * G + g;
+    float* P = a.partials + (((size_t)b * d.Hq + h) * d.nch + c) * c_stride;
+    P[hd] = st_s[g * 4];
+    P[hd + 1] = st_s[g * 4 + 1];
+  }
+}
+
+// merge the chunk partials of one (head, sequence): o = sum_c e^(m_c-M) acc_c / sum_c e^(m_c-M) l_c
+__global__ __launch_bounds__(256) void k_combine(Dims d, const StepDesc* desc, const float* partials,
+                                                 void* o) {
+  const int h = blockIdx.x, b = blockIdx.y, i = threadIdx.x;
+  const int len = desc->pos[b] + 1;
+  const int nv = (len + d.ct - 1) / d.ct;
+  const int cs = d.hd + 2;
+  const float* P = partials + ((size_t)b * d.Hq + h) * d.nch * cs;
+  float M = -INFINITY;
+  for (int c = 0; c < nv; c++) M = fmaxf(M, P[c * cs + d.hd]);
+  float L = 0.f, acc = 0.f;
+  for (int c = 0; c < nv; c++) {
+    const float w = expf(P[c * cs + d.hd] - M);
+    L += w * P[c * cs + d.hd + 1];
+    if (i < d.hd) acc += w * P[c * cs + i];
+  }
+  if (i < d.hd) {
+    const float v = acc / L;
+    const size_t oi = (size_t)b * d.q_dim + (size_t)h * d.hd + i;
+    if (d.act == ACT_BF16) ((uint16_t*)o)[oi] = f32_to_bf16(v);
+    else ((float*)o)[oi] = v;
+  }
+}
+
+// S11 greedy argmax over the fp32 logits, lowest index among equal maxima
+__global__ __launch_bounds__(1024) void k_argmax(const float* logits, int V, const StepDesc* desc) {
+  __shared__ float bv[16];
+  __shared__ int bi[16];
+  const int b = blockIdx.x;
+  const float* L = logits + (size_t)b * V;
+  float best = -INFINITY;
+  int idx = INT_MAX;
+  for (int v = threadIdx.x; v < V; v += 1024) {
+    const float x = L[v];
+    if (x > best || (idx == INT_MAX && !isnan(x))) { best = x; idx = v; }
+  }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    const float ob = __shfl_xor(best, m, 64);
+    const int oi = __shfl_xor(idx, m, 64);
+    if (ob > best || (ob == best && oi < idx)) { best = ob; idx = oi; }
+  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) { bv[wave] = best; bi[wave] = idx; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < 16; w++)
+      if (bv[w] > best || (bv[w] == best && bi[w] < idx)) { best = bv[w]; idx = bi[w]; }
+    desc->next_tokens[b] = idx == INT_MAX ? 0 : idx;
+  }
+}
+
+__global__ __launch_bounds__(256) void k_dequant_rows(Dims d, MatDev m, const int32_t* rows,
+                                                      float* out) {
+  const int r = blockIdx.x, sr = rows[r];
+  for (int c = threadIdx.x; c < m.cols; c += 256)
+    out[(size_t)r * m.cols + c] = deq_elem(m, d.wfmt, sr, c);
+}
+
+// counter-based hash (splitmix64 finaliser) for synthetic KV contents
+__device__ __forceinline__ uint64_t mix64(uint64_t z) {
+  z = (z ^ (z >> 30)) * 0xbf58476d1ce4e5b9ull;
+  z = (z ^ (z >> 27)) * 0x94d049bb133111ebull;
+  return z ^ (z >> 31);
+}
+
+__global__ __launch_bounds__(256) void k_kv_fill(Dims d, KvLayer kv, const int32_t* blocks, int len,
+                                                 int layer, uint64_t seed) {
+  const int bi = blockIdx.x, j = blockIdx.y;
+  const int blk = blocks[bi];
+  const float amp = 0.02f * sqrtf((float)d.D) * 1.7320508f;  // uniform(-amp, amp) has sd 0.02*sqrt(D)
+  for (int e = threadIdx.x; e < d.bs * d.hd; e += 256) {
+    const int off = e / d.hd, i = e - off * d.hd, t = bi * d.bs + off;
+    if (t >= len) continue;
+    const size_t row = ((size_t)blk * d.Hkv + j) * d.bs + off;
+    for (int which = 0; which < 2; which++) {
+      const uint64_t h = mix64(seed ^ mix64(((uint64_t)layer << 40) ^ ((uint64_t)t << 20) ^
+                                            ((uint64_t)j << 12) ^ ((uint64_t)i << 1) ^ (uint64_t)which));
+      const float u = (float)(h >> 40) * (1.0f / 16777216.0f) * 2.f - 1.f;
+      void* pool = which ? kv.v : kv.k;
+      if (d.kvfmt == KV_F32) ((float*)pool)[row * d.hd + i] = u * amp;
+      else if (d.kvfmt == KV_BF16) ((uint16_t*)pool)[row * d.hd + i] = f32_to_bf16(u * amp);
+      else {
+        ((int8_t*)pool)[row * d.hd + i] = (int8_t)rintf(u * 127.f);
+        if (i == 0) (which ? kv.vs : kv.ks)[row] = f32_to_f16(amp / 127.f);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// launch helpers
+// ---------------------------------------------------------------------------------------
+
+template <int WFMT, int EPI>
+hipError_t gemv_dispatch(const GemvArgs& a, int NB, int ROWS, dim3 grid, size_t smem, hipStream_t st) {
+  if (NB == 1 && ROWS == 2) hipLaunchKernelGGL((k_gemv<WFMT, EPI, 1, 2>), grid, dim3(256), smem, st, a);
+  else if (NB == 1 && ROWS == 4) hipLaunchKernelGGL((k_gemv<WFMT, EPI, 1, 4>), grid, dim3(256), smem, st, a);
+  else if (NB == 4 && ROWS == 2) hipLaunchKernelGGL((k_gemv<WFMT, EPI, 4, 2>), grid, dim3(256), smem, st, a);
+  else hipLaunchKernelGGL((k_gemv<WFMT, EPI, 4, 4>), grid, dim3(256), smem, st, a);
+  return hipGetLastError();
+}
+
+template <int WFMT>
+hipError_t gemv_epi(const GemvArgs& a, int epi, int NB, int ROWS, dim3 grid, size_t smem, hipStream_t st) {
+  switch (epi) {
+    case EPI_QKV: return gemv_dispatch<WFMT, EPI_QKV>(a, NB, ROWS, grid, smem, st);
+    case EPI_RESID: return gemv_dispatch<WFMT, EPI_RESID>(a, NB, ROWS, grid, smem, st);
+    case EPI_SWIGLU: return gemv_dispatch<WFMT, EPI_SWIGLU>(a, NB, ROWS, grid, smem, st);
+    default: return gemv_dispatch<WFMT, EPI_LOGITS>(a, NB, ROWS, grid, smem, st);
+  }
+}
+
+size_t attn_smem_bytes(const Dims& d) {
+  return sizeof(float) * ((size_t)d.G * d.hd + (size_t)kAttnTile * (d.hd + 1) +
+                          (size_t)d.G * kAttnTile + (size_t)d.G * 4 + 2 * (size_t)d.hd + 4);
+}
+
+}  // namespace
+
+hipError_t launch_embed(const Dims& d, const MatDev& emb, const StepDesc* desc, int B,
+                        int32_t* block_table, float* x, int32_t* err, hipStream_t st) {
+  hipLaunchKernelGGL(k_embed, dim3(B), dim3(256), 0, st, d, emb, desc, block_table, x, err);
+  return hipGetLastError();
+}
+
+hipError_t launch_rmsnorm(const Dims& d, const float* x, const float* g, void* xn, int B,
+                          hipStream_t st) {
+  hipLaunchKernelGGL(k_rmsnorm, dim3(B), dim3(256), 0, st, x, g, xn, d.D, d.eps, d.act);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemv(const Dims& d, const MatDev& m, const void* xin, int B, int epi,
+                       const EpiArgs& ea, hipStream_t st) {
+  GemvArgs a;
+  a.d = d;
+  a.m = m;
+  a.xin = xin;
+  a.B = B;
+  a.act_in = d.act;
+  a.ea = ea;
+  const int NB = B == 1 ? 1 : 4;
+  const int ROWS = m.rows >= 4 * 16 * 256 ? 4 : 2;
+  const int VEC = d.wfmt == W_BF16 ? 8 : 16, KSTEP = 64 * VEC;
+  const int budget_floats = 16384;  // 64 KiB of LDS
+  int kc = (budget_floats / NB) / KSTEP * KSTEP;
+  const int kpad = (m.cols + KSTEP - 1) / KSTEP * KSTEP;
+  if (kc > kpad) kc = kpad;
+  a.kc = kc;
+  const dim3 grid((m.rows + 4 * ROWS - 1) / (4 * ROWS), (B + NB - 1) / NB);
+  const size_t smem = sizeof(float) * (size_t)NB * kc;
+  switch (d.wfmt) {
+    case W_INT8_ROW: return gemv_epi<W_INT8_ROW>(a, epi, NB, ROWS, grid, smem, st);
+    case W_Q8_0: return gemv_epi<W_Q8_0>(a, epi, NB, ROWS, grid, smem, st);
+    default: return gemv_epi<W_BF16>(a, epi, NB, ROWS, grid, smem, st);
+  }
+}
+
+hipError_t launch_attention(const Dims& d, const StepDesc* desc, int B, const float* q,
+                            const float* knew, const float* vnew, const KvLayer& kv,
+                            const int32_t* block_table, float* partials, hipStream_t st) {
+  AttnArgs a;
+  a.d = d;
+  a.desc = desc;
+  a.q = q;
+  a.knew = knew;
+  a.vnew = vnew;
+  a.kv = kv;
+  a.bt = block_table;
+  a.partials = partials;
+  const dim3 grid(d.nch, d.Hkv, B);
+  const size_t smem = attn_smem_bytes(d);
+  if (d.kvfmt == KV_F32) hipLaunchKernelGGL(k_attn<KV_F32>, grid, dim3(256), smem, st, a);
+  else if (d.kvfmt == KV_BF16) hipLaunchKernelGGL(k_attn<KV_BF16>, grid, dim3(256), smem, st, a);
+  else hipLaunchKernelGGL(k_attn<KV_I8>, grid, dim3(256), smem, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(const Dims& d, const StepDesc* desc, int B, const float* partials,
+                          void* o, hipStream_t st) {
+  hipLaunchKernelGGL(k_combine, dim3(d.Hq, B), dim3(d.hd), 0, st, d, desc, partials, o);
+  return hipGetLastError();
+}
+
+hipError_t launch_argmax(const Dims& d, const StepDesc* desc, int B, const float* logits,
+                         hipStream_t st) {
+  hipLaunchKernelGGL(k_argmax, dim3(B), dim3(1024), 0, st, logits, d.V, desc);
+  return hipGetLastError();
+}
+
+hipError_t launch_dequant_rows(const Dims& d, const MatDev& m, const int32_t* rows, int nrows,
+                               float* out, hipStream_t st) {
+  hipLaunchKernelGGL(k_dequant_rows, dim3(nrows), dim3(256), 0, st, d, m, rows, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_kv_fill(const Dims& d, const KvLayer& kv, const int32_t* blocks, int nblk_used,
+                          int len, int layer, uint64_t seed, hipStream_t st) {
+  hipLaunchKernelGGL(k_kv_fill, dim3(nblk_used, d.Hkv), dim3(256), 0, st, d, kv, blocks, len, layer,
+                     seed);
+  return hipGetLastError();
+}
+
+}  // namespace dtd

@@ -1,0 +1,226 @@
+/* dtd.h -- C ABI of libdtd.so, the MI355X (gfx950) decode step of a Llama-family
+ * decoder-only transformer.
+ *
+ * What one decode step computes, per sequence (the pre-norm block described by
+ * "从 smollm3.go 看 LLM inference", Transformer block and self-attention sections, and by
+ * the Qwen3-8B engine article, 4.2.2):
+ *   x = embed(token); for every layer: x += Wo . attn(rope(Wq . rmsnorm(x)), K, V);
+ *   x += Wdown . (silu(Wgate . rmsnorm(x)) * (Wup . rmsnorm(x)));
+ *   logits = Whead . rmsnorm(x); next = argmax(logits)  (greedy, lowest index on ties).
+ * The interface mirrors the Qwen3-8B engine article's inner service (4.1.2: Prefill,
+ * DecodeStep, ResetSeq, token ids only, the engine owns each seq_id's KV) and
+ * smollm3.go's Forward(token, pos) / Prefill(tokens, startPos) (Prefill and Decode).
+ *
+ * Conventions for every entry point:
+ *   - Returns dtd_status: 0 on success, < 0 on error.  Never throws, never aborts.
+ *   - Everything is validated on the host before any work is enqueued; on error nothing
+ *     changes and dtd_last_error() describes the problem.
+ *   - `*_dev` pointers are device memory owned by the caller; they must stay valid until
+ *     the enqueued work completes, which the caller observes by synchronising the stream
+ *     given to dtd_create (the ownership rule of cgo-style boundaries, "Go 语言原本" 20.2.3:
+ *     memory handed across may only be kept while the caller keeps it alive).
+ *   - Host pointers are read during the call only.
+ *   - The engine owns its copies of the weights, the KV block pool, block tables and
+ *     work buffers.  One engine is driven from one host thread and one stream.
+ *   - A HIP runtime failure returns DTD_E_HIP and leaves the engine unusable (destroy it).
+ */
+#ifndef DTD_H
+#define DTD_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DTD_ABI_VERSION 1
+
+typedef enum {
+  DTD_OK = 0,
+  DTD_E_ARG = -1,          /* bad argument, shape, size, name or token id */
+  DTD_E_STATE = -2,        /* call not valid in this state (e.g. no weights loaded) */
+  DTD_E_NOSEQ = -3,        /* unknown seq_id */
+  DTD_E_CTX = -4,          /* sequence would exceed max_ctx */
+  DTD_E_KVFULL = -5,       /* no free KV block or sequence slot */
+  DTD_E_OOM = -6,          /* device allocation failed */
+  DTD_E_HIP = -7,          /* HIP runtime error; engine unusable */
+  DTD_E_UNSUPPORTED = -8   /* configuration outside what the kernels implement */
+} dtd_status;
+
+/* weight storage (the offline export formats):
+ *   INT8_ROW: int8 codes [rows][cols] + one fp32 scale per row; W[r][c] = q[r][c]*s[r]
+ *             ("从 smollm3.go 看 LLM inference", int8 weight-only quantization);
+ *   Q8_0:     int8 codes [rows][cols] + one fp16 scale per run of 32 columns
+ *             [rows][cols/32] ("Go 语言原本" 20.2.4);
+ *   BF16:     bf16 bit patterns [rows][cols]. */
+enum { DTD_W_INT8_ROW = 0, DTD_W_Q8_0 = 1, DTD_W_BF16 = 2 };
+/* activation storage type at the rounding points: each RMSNorm output, the attention
+ * output and the SwiGLU output.  The residual stream, queries, scores, softmax,
+ * accumulators and logits are fp32 in every configuration. */
+enum { DTD_ACT_F32 = 0, DTD_ACT_BF16 = 1 };
+/* KV cache storage: fp32, bf16, or int8 codes with one fp16 scale per (token, KV head),
+ * s = fp16(max|x|/127), q = clamp(rint(x/s), -127, 127). */
+enum { DTD_KV_F32 = 0, DTD_KV_BF16 = 1, DTD_KV_I8 = 2 };
+
+typedef struct {
+  int32_t abi_version;        /* DTD_ABI_VERSION */
+  int32_t dim;                /* model width D */
+  int32_t n_layers;
+  int32_t n_q_heads;          /* Hq; q_dim = Hq * head_dim */
+  int32_t n_kv_heads;         /* Hkv, divides Hq; q head h reads kv head h / (Hq/Hkv) */
+  int32_t head_dim;           /* d: a multiple of 4 in [8, 128] */
+  int32_t ffn_dim;            /* F */
+  int32_t vocab;              /* V */
+  float   rms_eps;            /* added inside the square root */
+  float   rope_theta;         /* half-split RoPE base: pair (i, i+d/2) turns by pos*theta^(-2i/d) */
+  int32_t tied_embeddings;    /* 1: the LM head reuses tok_emb */
+  int32_t wfmt;               /* DTD_W_* */
+  int32_t act;                /* DTD_ACT_* */
+  int32_t kvfmt;              /* DTD_KV_* */
+  int32_t kv_block_size;      /* tokens per KV block (paged KV, Qwen3-8B engine article 4.3.1) */
+  int32_t kv_num_blocks;      /* blocks in the pool, shared by all sequences and layers */
+  int32_t max_seqs;           /* live sequences at once */
+  int32_t max_ctx;            /* positions per sequence */
+  int32_t max_batch;          /* sequences per decode_step call, <= 64 */
+} dtd_config;
+
+/* One named weight part for dtd_load_weights.  Names: "tok_emb", "lm_head" (absent when
+ * tied), "final_norm", and per layer i "L{i}.attn_norm", "L{i}.wq", "L{i}.wk", "L{i}.wv",
+ * "L{i}.wo", "L{i}.ffn_norm", "L{i}.w_gate", "L{i}.w_up", "L{i}.w_down", each followed by
+ * a part suffix: ".q" int8 codes and ".s" scales (INT8_ROW, Q8_0), ".w" bf16 bits (BF16),
+ * ".g" fp32 gains (norms).  Matrices are row-major [out][in]: wq [Hq*d][D],
+ * wk/wv [Hkv*d][D], wo [D][Hq*d], w_gate/w_up [F][D], w_down [D][F], tok_emb/lm_head
+ * [V][D].  nbytes must equal the exact size of the part. */
+typedef struct {
+  const char* name;
+  const void* data;
+  int64_t     nbytes;
+  int32_t     on_device;      /* 0: host memory, 1: device memory */
+} dtd_tensor;
+
+/* Expected weight part, as reported by dtd_expected_tensors. */
+typedef struct {
+  char    name[48];
+  int64_t nbytes;
+  int32_t rows, cols;         /* matrix shape, or [1][D] for gains */
+  int32_t elem;               /* bytes per element of this part: 1, 2 or 4 */
+} dtd_tensor_spec;
+
+typedef struct dtd_engine dtd_engine;
+
+/* ---- host-only queries (no GPU needed) ------------------------------------------- */
+
+/* Checks a configuration against what the kernels implement.  msg (may be NULL) gets a
+ * NUL-terminated reason of at most msg_len bytes. */
+dtd_status dtd_validate_config(const dtd_config* cfg, char* msg, int32_t msg_len);
+
+/* Lists the weight parts dtd_load_weights expects for cfg.  Returns the count (and fills
+ * at most cap entries of out, which may be NULL), or a dtd_status < 0 if cfg is invalid. */
+int32_t dtd_expected_tensors(const dtd_config* cfg, dtd_tensor_spec* out, int32_t cap);
+
+/* ---- lifecycle ---------------------------------------------------------------------- */
+
+/* Creates an engine on the current HIP device.  hip_stream is a hipStream_t (NULL = the
+ * null stream); all work is enqueued on it.  Allocates the KV pool and work buffers. */
+dtd_status dtd_create(const dtd_config* cfg, void* hip_stream, dtd_engine** out);
+
+/* Copies every weight part into engine-owned device memory (repacked for the kernels).
+ * All parts must be given in one call; fail-closed: a missing, unknown, duplicate or
+ * wrongly sized part is rejected before anything is copied.  Synchronous: the caller may
+ * free its buffers when it returns. */
+dtd_status dtd_load_weights(dtd_engine* e, const dtd_tensor* t, int32_t n);
+
+/* Appends n tokens (device int32 [n], each in [0, V)) to sequence seq_id, creating the
+ * sequence if it is new, by running them through the decode step one position after
+ * the other.  Writes the greedy next token after the last one to next_token_dev
+ * (int32 [1]) and, if logits_dev is not NULL, its fp32 logits [V]. */
+dtd_status dtd_prefill(dtd_engine* e, int64_t seq_id, const int32_t* tokens_dev, int32_t n,
+                       int32_t* next_token_dev, float* logits_dev);
+
+/* One decode step for `batch` distinct existing sequences: token b (tokens_dev[b], device
+ * int32) goes at position len(seq_ids_host[b]) of its sequence, whose KV grows by one.
+ * Writes next_tokens_dev[b] (int32 [batch]) and, if logits_dev is not NULL, fp32 logits
+ * [batch][V].  next_tokens_dev may equal tokens_dev (greedy loop without a host round
+ * trip). */
+dtd_status dtd_decode_step(dtd_engine* e, int32_t batch, const int64_t* seq_ids_host,
+                           const int32_t* tokens_dev, int32_t* next_tokens_dev,
+                           float* logits_dev);
+
+/* Forgets a sequence: its KV blocks and slot return to the free lists.  Host only. */
+dtd_status dtd_reset_seq(dtd_engine* e, int64_t seq_id);
+
+/* Current length (positions written) of a sequence, or a dtd_status < 0. */
+int32_t dtd_seq_len(const dtd_engine* e, int64_t seq_id);
+
+/* Reports a token id outside [0, V) seen on the device by an earlier prefill or decode
+ * step (such tokens are read as id 0).  Synchronises the stream.  DTD_E_ARG if one was
+ * seen since the last check, else DTD_OK. */
+dtd_status dtd_check_device_errors(dtd_engine* e);
+
+void        dtd_destroy(dtd_engine* e);
+const char* dtd_last_error(const dtd_engine* e);
+
+/* ---- debug and measurement entry points (tests and benchmarks) -------------------- */
+
+/* Dequantises stored rows [r0, r0+nrows) of one matrix (name as in load_weights without
+ * the part suffix, e.g. "L3.w_down") to fp32 out_dev [nrows][cols], with the same
+ * per-element product the kernels use (q * s in fp32, or bf16 widened). */
+dtd_status dtd_debug_dequant_rows(dtd_engine* e, const char* matrix, int32_t r0, int32_t nrows,
+                                  float* out_dev);
+
+/* While enabled, each later prefill token or decode step copies the fp32 residual stream
+ * after the embedding and after every layer to out_dev [(L+1)][batch][D] (the buffer is
+ * overwritten by every step).  enable = 0 turns it off. */
+dtd_status dtd_debug_capture_hidden(dtd_engine* e, int32_t enable, float* out_dev);
+
+/* A decode step like dtd_decode_step in which every kernel reads its input from an inject
+ * record and its output is copied to a capture record, so that each kernel can be checked
+ * against the reference operation on identical inputs.  Both buffers hold one record per
+ * layer; a record is these fields in order, each [batch][n] (f32 = fp32, act = the
+ * activation type), of dtd_debug_probe_record_bytes() bytes in total:
+ *   x_in f32 [D] | xn act [D] | q f32 [q_dim] | k f32 [kv_dim] | v f32 [kv_dim] |
+ *   o act [q_dim] | x_mid f32 [D] | xn2 act [D] | h act [F] | x_out f32 [D]
+ * Per layer: xn = RMSNorm(inject.x_in); (q, k, v) = QKV+RoPE(inject.xn);
+ * o = attention(inject.q, cache + inject k/v appended at the new position);
+ * x_mid = inject.x_in + Wo.inject.o; xn2 = RMSNorm(inject.x_mid);
+ * h = SwiGLU(inject.xn2); x_out = inject.x_mid + Wdown.inject.h.  The final norm and LM
+ * head read the last layer's inject.x_out.  Unlike dtd_decode_step, a seq_id not seen
+ * before starts a new sequence at position 0. */
+dtd_status dtd_debug_decode_probe(dtd_engine* e, int32_t batch, const int64_t* seq_ids_host,
+                                  const int32_t* tokens_dev, const void* inject_dev,
+                                  void* capture_dev, int32_t* next_tokens_dev, float* logits_dev);
+
+/* Bytes of one probe record for cfg and batch (host only), or a dtd_status < 0. */
+int64_t dtd_debug_probe_record_bytes(const dtd_config* cfg, int32_t batch);
+
+/* Writes stored KV of positions [pos0, pos0+n) of one layer from host memory, native
+ * encoding [n][Hkv][d] (fp32 / bf16 bits / int8 codes) plus fp16 scales [n][Hkv] for
+ * int8 (k_scale, v_scale NULL otherwise).  Creates the sequence if new, allocates its
+ * blocks and extends its length to at least pos0+n (positions must be written before
+ * they are attended).  Synchronous. */
+dtd_status dtd_debug_kv_write(dtd_engine* e, int64_t seq_id, int32_t layer, int32_t pos0,
+                              int32_t n, const void* k, const void* v, const void* k_scale,
+                              const void* v_scale);
+
+/* Reads stored KV of positions [pos0, pos0+n) through the block table into host memory
+ * in the layout dtd_debug_kv_write takes.  Synchronous. */
+dtd_status dtd_debug_kv_read(dtd_engine* e, int64_t seq_id, int32_t layer, int32_t pos0,
+                             int32_t n, void* k, void* v, void* k_scale, void* v_scale);
+
+/* Sets a sequence's length to len (creating it if new) with synthetic KV in every layer:
+ * values from a counter-based hash of (seed, layer, position, head, i), spread like
+ * N(0, (0.02*sqrt(D))^2) but not Gaussian.  For timing long contexts only. */
+dtd_status dtd_debug_kv_fill(dtd_engine* e, int64_t seq_id, int32_t len, uint64_t seed);
+
+/* Kernel timing.  kind: 0 = the gate/up projection, 1 = the down projection, 2 = the
+ * QKV projection, 3 = the output projection, 4 = attention, 5 = LM head.  While enabled,
+ * HIP events bracket every launch of that kernel on the engine's stream; *total_ms
+ * and *count return the summed duration and number of launches since enabling and
+ * reset them.  Synchronises the stream when reading. */
+dtd_status dtd_debug_kernel_timing(dtd_engine* e, int32_t kind, int32_t enable,
+                                   double* total_ms, int64_t* count);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DTD_H */

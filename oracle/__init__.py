@@ -55,6 +55,7 @@ def lib():
         L.orc_fp16_to_double.argtypes, L.orc_fp16_to_double.restype = [U16], D
         L.orc_double_to_fp16.argtypes, L.orc_double_to_fp16.restype = [D], U16
         L.orc_round_act.argtypes, L.orc_round_act.restype = [D, I32], D
+        L.orc_round_act_n.argtypes, L.orc_round_act_n.restype = [P, I32, I32, P], None
         L.orc_rmsnorm.argtypes, L.orc_rmsnorm.restype = [P, P, I32, D, P], None
         L.orc_dequant_row.argtypes, L.orc_dequant_row.restype = [I32, P, P, I32, I32, P], None
         L.orc_gemv.argtypes, L.orc_gemv.restype = [I32, P, P, I32, I32, P, P], None
@@ -67,7 +68,8 @@ def lib():
         L.orc_destroy.argtypes, L.orc_destroy.restype = [P], None
         L.orc_set_tensor.argtypes, L.orc_set_tensor.restype = [P, C.c_char_p, P, P], I32
         L.orc_ready.argtypes, L.orc_ready.restype = [P], I32
-        L.orc_step.argtypes, L.orc_step.restype = [P, I32, I32, I32, P, P], I32
+        L.orc_step.argtypes, L.orc_step.restype = [P, I32, I32, I32, P, P, P], I32
+        L.orc_trace_len.argtypes, L.orc_trace_len.restype = [P], I32
         L.orc_kv_write.argtypes, L.orc_kv_write.restype = [P, I32, I32, I32, I32, P, P, P, P], I32
         L.orc_kv_read.argtypes, L.orc_kv_read.restype = [P, I32, I32, I32, I32, P, P], I32
         L.orc_kv_read_raw.argtypes, L.orc_kv_read_raw.restype = [P, I32, I32, I32, I32, P, P, P, P], I32
@@ -105,6 +107,13 @@ def double_to_fp16(x: float) -> int:
 
 def round_act(x: float, act: int) -> float:
     return lib().orc_round_act(float(x), int(act))
+
+
+def round_act_n(x, act: int):
+    x = _c(x, np.float64)
+    out = np.empty_like(x)
+    lib().orc_round_act_n(_p(x), x.size, int(act), _p(out))
+    return out
 
 
 def rmsnorm(x, g, eps):
@@ -205,14 +214,33 @@ class Model:
             lib().orc_destroy(h)
             self._h = None
 
-    def step(self, seq: int, token: int, pos: int, want_logits=True, want_hidden=False):
+    def step(self, seq: int, token: int, pos: int, want_logits=True, want_hidden=False,
+             want_trace=False):
+        """Returns (next token, logits, hidden) or, with want_trace, (next, logits, hidden,
+        trace [L][record]) -- see trace_fields for the record layout."""
         s = self.shape
         logits = np.empty(s.vocab, dtype=np.float32) if want_logits else None
-        hidden = np.empty((s.n_layers + 1, s.dim), dtype=np.float64) if want_hidden else None
-        nxt = lib().orc_step(self._h, int(seq), int(token), int(pos), _p(logits), _p(hidden))
+        hidden = np.empty((s.n_layers + 1, s.dim), dtype=np.float64) if (want_hidden or want_trace) else None
+        trace = None
+        if want_trace:
+            trace = np.empty((s.n_layers, lib().orc_trace_len(self._h)), dtype=np.float64)
+        nxt = lib().orc_step(self._h, int(seq), int(token), int(pos), _p(logits), _p(hidden), _p(trace))
         if nxt < 0:
             raise RuntimeError(f"orc_step failed: {nxt}")
+        if want_trace:
+            return nxt, logits, hidden, trace
         return nxt, logits, hidden
+
+    def trace_fields(self):
+        """(name, offset, length) of each field of a trace record."""
+        s = self.shape
+        out, off = [], 0
+        for name, n in (("x_in", s.dim), ("xn", s.dim), ("q", s.q_dim), ("k", s.kv_dim),
+                        ("v", s.kv_dim), ("o", s.q_dim), ("x_mid", s.dim), ("xn2", s.dim),
+                        ("h", s.ffn_dim), ("x_out", s.dim)):
+            out.append((name, off, n))
+            off += n
+        return out
 
     def kv_write(self, seq, layer, pos0, k, v, ks=None, vs=None):
         k = np.ascontiguousarray(k); v = np.ascontiguousarray(v)

@@ -81,6 +81,10 @@ double orc_round_act(double x, int32_t act) {
   return (double)(float)x; /* binary32, round to nearest even */
 }
 
+void orc_round_act_n(const double* x, int32_t n, int32_t act, double* out) {
+  for (int32_t i = 0; i < n; i++) out[i] = orc_round_act(x[i], act);
+}
+
 /* ------------------------------------------------------------------------------------ */
 /* single operations                                                                    */
 /* ------------------------------------------------------------------------------------ */
@@ -417,16 +421,29 @@ static int32_t head_logits(const orc_model* m, const double* x, scratch_t* s, fl
   return next;
 }
 
-/* the feed-forward half of a layer: x += W_down (silu(W_gate xn) * (W_up xn)) */
-static void ffn_half(const orc_model* m, const layer_t* L, double* x, scratch_t* s) {
+/* the feed-forward half of a layer: x += W_down (silu(W_gate xn) * (W_up xn));
+ * xn2_pre / h_pre (may be NULL) receive the values before activation rounding */
+static void ffn_half(const orc_model* m, const layer_t* L, double* x, scratch_t* s,
+                     double* xn2_pre, double* h_pre) {
   const orc_cfg* c = &m->c;
   orc_rmsnorm(x, L->ffn_norm, c->dim, c->rms_eps, s->xn);
+  if (xn2_pre) memcpy(xn2_pre, s->xn, sizeof(double) * (size_t)c->dim);
   round_vec(s->xn, c->dim, c->act);
   gemv_mat(m, &L->w_gate, s->xn, s->a);
   gemv_mat(m, &L->w_up, s->xn, s->b);
-  for (int32_t i = 0; i < c->ffn_dim; i++) s->h[i] = orc_round_act(orc_silu(s->a[i]) * s->b[i], c->act);
+  for (int32_t i = 0; i < c->ffn_dim; i++) {
+    const double hv = orc_silu(s->a[i]) * s->b[i];
+    if (h_pre) h_pre[i] = hv;
+    s->h[i] = orc_round_act(hv, c->act);
+  }
   gemv_mat(m, &L->w_down, s->h, s->tmp);
   for (int32_t i = 0; i < c->dim; i++) x[i] += s->tmp[i];
+}
+
+int32_t orc_trace_len(const orc_model* m) {
+  const orc_cfg* c = &m->c;
+  const int32_t qd = c->n_q_heads * c->head_dim, kvd = c->n_kv_heads * c->head_dim;
+  return 5 * c->dim + 2 * qd + 2 * kvd + c->ffn_dim;
 }
 
 /* xn -> q, k, v with RoPE applied to every q and k head at position pos */
@@ -440,7 +457,7 @@ static void qkv_rope(const orc_model* m, const layer_t* L, int32_t pos, scratch_
 }
 
 int32_t orc_step(orc_model* m, int32_t seq, int32_t token, int32_t pos, float* logits,
-                 double* hidden) {
+                 double* hidden, double* trace) {
   const orc_cfg* c = &m->c;
   if (!orc_ready(m)) return -10;
   if (seq < 0 || seq >= c->max_seqs) return -11;
@@ -457,20 +474,43 @@ int32_t orc_step(orc_model* m, int32_t seq, int32_t token, int32_t pos, float* l
 
   embed_row(m, token, x);
   if (hidden) memcpy(hidden, x, sizeof(double) * (size_t)c->dim);
+  const int32_t D = c->dim;
+  const size_t dsz = sizeof(double);
   for (int32_t l = 0; l < c->n_layers; l++) {
     const layer_t* L = &m->layers[l];
+    /* trace record fields of this layer (NULL when not tracing) */
+    double* t_x_in = trace ? trace + (size_t)l * orc_trace_len(m) : NULL;
+    double* t_xn = trace ? t_x_in + D : NULL;
+    double* t_q = trace ? t_xn + D : NULL;
+    double* t_k = trace ? t_q + qd : NULL;
+    double* t_v = trace ? t_k + kvd : NULL;
+    double* t_o = trace ? t_v + kvd : NULL;
+    double* t_xmid = trace ? t_o + qd : NULL;
+    double* t_xn2 = trace ? t_xmid + D : NULL;
+    double* t_h = trace ? t_xn2 + D : NULL;
+    double* t_xout = trace ? t_h + c->ffn_dim : NULL;
+    if (trace) memcpy(t_x_in, x, dsz * D);
     orc_rmsnorm(x, L->attn_norm, c->dim, c->rms_eps, s.xn);
+    if (trace) memcpy(t_xn, s.xn, dsz * D);
     round_vec(s.xn, c->dim, c->act);
     qkv_rope(m, L, pos, &s);
+    if (trace) {
+      memcpy(t_q, s.q, dsz * qd);
+      memcpy(t_k, s.k, dsz * kvd);
+      memcpy(t_v, s.v, dsz * kvd);
+    }
     kv_store(c, kv->k, kv->ks, l, pos, s.k);
     kv_store(c, kv->v, kv->vs, l, pos, s.v);
     kv_load(c, kv->k, kv->ks, l, 0, pos + 1, Kd);
     kv_load(c, kv->v, kv->vs, l, 0, pos + 1, Vd);
     orc_attention(s.q, c->n_q_heads, c->n_kv_heads, c->head_dim, pos + 1, Kd, Vd, s.o);
+    if (trace) memcpy(t_o, s.o, dsz * qd);
     round_vec(s.o, qd, c->act);
     gemv_mat(m, &L->wo, s.o, s.tmp);
     for (int32_t i = 0; i < c->dim; i++) x[i] += s.tmp[i];
-    ffn_half(m, L, x, &s);
+    if (trace) memcpy(t_xmid, x, dsz * D);
+    ffn_half(m, L, x, &s, t_xn2, t_h);
+    if (trace) memcpy(t_xout, x, dsz * D);
     if (hidden) memcpy(hidden + (size_t)(l + 1) * c->dim, x, sizeof(double) * (size_t)c->dim);
   }
   int32_t next = head_logits(m, x, &s, logits);
@@ -587,7 +627,7 @@ int32_t orc_full_forward(orc_model* m, const int32_t* tokens, int32_t n, float* 
       round_vec(s.o, qd, c->act);
       gemv_mat(m, &L->wo, s.o, s.tmp);
       for (int32_t i = 0; i < D; i++) x[i] += s.tmp[i];
-      ffn_half(m, L, x, &s);
+      ffn_half(m, L, x, &s, NULL, NULL);
     }
     if (hidden) memcpy(hidden + (size_t)(l + 1) * D, X + (size_t)(n - 1) * D, sizeof(double) * (size_t)D);
   }

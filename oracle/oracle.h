@@ -58,6 +58,7 @@ uint16_t orc_double_to_bf16(double x);      /* round to nearest even */
 double   orc_fp16_to_double(uint16_t h);
 uint16_t orc_double_to_fp16(double x);      /* round to nearest even */
 double   orc_round_act(double x, int32_t act);
+void     orc_round_act_n(const double* x, int32_t n, int32_t act, double* out);
 
 /* ---- single operations on plain arrays ---- */
 /* out[i] = x[i] / sqrt(mean(x^2) + eps) * g[i] */
@@ -93,9 +94,15 @@ int32_t    orc_ready(const orc_model* m);
 /* One decode step of sequence `seq` for `token` at position `pos`: writes K/V at pos,
  * attends over [0, pos].  logits (fp32 [vocab]) and hidden (double [(L+1)*dim]: the
  * residual stream after the embedding and after each layer) may be NULL.
+ * trace (may be NULL) receives, per layer, the record
+ *   x_in [D] | xn [D] | q [q_dim] | k [kv_dim] | v [kv_dim] | o [q_dim] | x_mid [D] |
+ *   xn2 [D] | h [F] | x_out [D]
+ * where xn, o, xn2 and h are the values before their activation rounding, q and k are
+ * after RoPE, and k, v are before the KV rounding (orc_trace_len() doubles per layer).
  * Returns the greedy next token, or < 0 on error. */
 int32_t    orc_step(orc_model* m, int32_t seq, int32_t token, int32_t pos,
-                    float* logits, double* hidden);
+                    float* logits, double* hidden, double* trace);
+int32_t    orc_trace_len(const orc_model* m);
 /* Writes n positions of stored K/V (native encoding, [n][hkv][d]; scales [n][hkv] fp16
  * for int8) at pos0..pos0+n-1 of (seq, layer). */
 int32_t    orc_kv_write(orc_model* m, int32_t seq, int32_t layer, int32_t pos0, int32_t n,

@@ -1,0 +1,239 @@
+"""Runs the HIP engine (through the C ABI) and the CPU oracle on the same seeded inputs."""
+from __future__ import annotations
+
+import numpy as np
+
+import oracle
+from decoder_only_transformer_decode_amd import dtd, synth
+
+TOL = 2e-3   # max |gpu - oracle| / max |oracle| per tensor (fp32 accumulation)
+ENV_EPS = 1e-6     # relative noise used to measure the oracle's own sensitivity
+ENV_FACTOR = 4.0   # free-running bound: max(TOL, ENV_FACTOR x the oracle's sensitivity)
+
+
+def normwise(g, r) -> float:
+    g = np.asarray(g, dtype=np.float64)
+    r = np.asarray(r, dtype=np.float64)
+    den = np.abs(r).max()
+    return float(np.abs(g - r).max() / (den if den > 0 else 1.0))
+
+
+def top2_margin(logits) -> float:
+    s = np.sort(np.asarray(logits, dtype=np.float64))
+    return float(s[-1] - s[-2])
+
+
+def need_gpu():
+    import pytest
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need an MI355X; none is visible")
+    dtd.load()   # raises if libdtd.so was not built: no fallback
+
+
+class Pair:
+    """An engine and an oracle model holding the same weights."""
+
+    def __init__(self, shape, *, max_ctx, max_seqs=1, max_batch=1, seed=11, weights=None,
+                 kv_block_size=16, kv_num_blocks=None):
+        import torch
+        self.torch = torch
+        self.shape = shape
+        self.w = weights if weights is not None else synth.gen_weights(shape, seed)
+        self.eng = dtd.Engine(shape, max_ctx=max_ctx, max_seqs=max_seqs, max_batch=max_batch,
+                              kv_block_size=kv_block_size, kv_num_blocks=kv_num_blocks)
+        self.eng.load_weights(synth.flat_tensors(self.w))
+        self.orc = oracle.Model(shape, self.w, max_ctx=max_ctx, max_seqs=max_seqs)
+        self.dev = self.eng.device
+        self.slot_of = {}
+
+    def close(self):
+        self.eng.close()
+
+    def oslot(self, seq_id):
+        if seq_id not in self.slot_of:
+            self.slot_of[seq_id] = len(self.slot_of)
+        return self.slot_of[seq_id]
+
+    # ---- GPU side ----
+    def gpu_prefill(self, seq_id, tokens):
+        nxt, logits = self.eng.prefill(seq_id, tokens, want_logits=True)
+        self.torch.cuda.synchronize()
+        return int(nxt.item()), logits.cpu().numpy()
+
+    def gpu_step(self, seq_ids, tokens, capture=False):
+        t = self.torch
+        B = len(seq_ids)
+        hid = None
+        if capture:
+            hid = t.empty((self.shape.n_layers + 1, B, self.shape.dim), dtype=t.float32, device=self.dev)
+            dtd.dtd_debug_capture_hidden(self.eng.h, True, hid.data_ptr())
+        nxt, logits = self.eng.decode_step(seq_ids, tokens, want_logits=True)
+        t.cuda.synchronize()
+        if capture:
+            dtd.dtd_debug_capture_hidden(self.eng.h, False)
+        return (nxt.cpu().numpy().astype(np.int64), logits.cpu().numpy(),
+                None if hid is None else hid.cpu().numpy())
+
+    # ---- oracle side ----
+    def orc_prefill(self, seq_id, tokens, start=0):
+        s = self.oslot(seq_id)
+        out = None
+        for i, tok in enumerate(tokens):
+            out = self.orc.step(s, int(tok), start + i)
+        return out[0], out[1]
+
+    def orc_step(self, seq_id, token, pos, hidden=False):
+        return self.orc.step(self.oslot(seq_id), int(token), pos, want_hidden=hidden)
+
+    def perturbed_oracle(self, seed, max_ctx, max_seqs=1):
+        """An oracle whose norm gains are scaled by (1 + ENV_EPS * N(0,1)): its distance from
+        the plain oracle measures how far rounding-sized noise moves the method's outputs."""
+        rng = np.random.default_rng(seed)
+        w2 = {}
+        for n, parts in self.w.items():
+            if "g" in parts:
+                g = parts["g"].astype(np.float64)
+                w2[n] = {"g": (g * (1 + ENV_EPS * rng.standard_normal(g.shape))).astype(np.float32)}
+            else:
+                w2[n] = parts
+        return oracle.Model(self.shape, w2, max_ctx=max_ctx, max_seqs=max_seqs)
+
+    def write_kv_both(self, seq_id, n_pos, seed, extra=()):
+        """Identical synthetic stored KV for positions [0, n_pos) of every layer."""
+        for layer in range(self.shape.n_layers):
+            k, v, ks, vs = synth.synthetic_kv(self.shape, n_pos, seed, layer)
+            dtd.dtd_debug_kv_write(self.eng.h, seq_id, layer, 0, k, v,
+                                   None if ks is None else ks.view(np.uint16),
+                                   None if vs is None else vs.view(np.uint16))
+            self.orc.kv_write(self.oslot(seq_id), layer, 0, k, v, ks, vs)
+            for om, slot in extra:
+                om.kv_write(slot, layer, 0, k, v, ks, vs)
+
+
+# ---------------------------------------------------------------------------------------
+# per-kernel probe: the GPU's kernels fed the oracle's own intermediate values
+# ---------------------------------------------------------------------------------------
+
+BAND = 2e-5   # half-width of the "near a rounding midpoint" band, x rms of the vector
+
+
+def check_rounded(tag, g, r, act):
+    """g: GPU values after the activation rounding (float64 array); r: the oracle's values
+    before it.  Rounding is monotone, so g is a correct rounding of some value within `band`
+    of r exactly when round(r - band) <= g <= round(r + band), band = BAND * rms(r).  Where
+    that interval holds one bf16 value (r is not near a rounding midpoint) this demands g
+    == round(r) bit for bit."""
+    r = np.asarray(r, dtype=np.float64)
+    if act == synth.ACT_F32:
+        e = normwise(g, r)
+        assert e <= TOL, f"{tag}: {e:.3e}"
+        return 0
+    band = BAND * np.sqrt(np.mean(r * r))
+    lo = oracle.round_act_n(r - band, act)
+    hi = oracle.round_act_n(r + band, act)
+    ok = (g >= lo) & (g <= hi)
+    if not ok.all():
+        i = int(np.flatnonzero(~ok)[0])
+        raise AssertionError(f"{tag}: {int((~ok).sum())} of {r.size} roundings outside "
+                             f"[round(r-band), round(r+band)]; first at {i}: gpu {g[i]!r}, "
+                             f"oracle unrounded {r[i]!r}, band {band:.3e}")
+    return int((g != oracle.round_act_n(r, act)).sum())
+
+
+def _to_act(x, act):
+    if act == synth.ACT_BF16:
+        return synth.f32_to_bf16_bits(x.astype(np.float32))   # x already holds bf16 values
+    return x.astype(np.float32)
+
+
+def _from_act(raw, act):
+    if act == synth.ACT_BF16:
+        return synth.bf16_bits_to_f32(raw.view(np.uint16)).astype(np.float64)
+    return raw.view(np.float32).astype(np.float64)
+
+
+def probe_step(P, gpu_ids, orc_ids, toks, poss, tag, check=True):
+    """Oracle step (with its per-layer trace) for each sequence, then one GPU probe step in
+    which every kernel reads the oracle's own inputs; every kernel's output is compared
+    with the oracle's.  Returns the oracle outputs [(next, logits, hidden, trace)]."""
+    t = P.torch
+    s = P.shape
+    B = len(gpu_ids)
+    act = s.act
+    outs = [P.orc.step(P.oslot(o), int(toks[b]), int(poss[b]), want_trace=True)
+            for b, o in enumerate(orc_ids)]
+    fields = {name: (off, n) for name, off, n in P.orc.trace_fields()}
+    layout, rec = dtd.probe_fields(s, B)
+    inj = np.zeros((s.n_layers, rec), dtype=np.uint8)
+    # k and v are injected as the oracle's stored (already rounded) cache entries: the GPU
+    # stores round_kv of what it is given, which reproduces them exactly in every KV format
+    stored = [[P.orc.kv_read(P.oslot(o), l, int(poss[b]), 1) for l in range(s.n_layers)]
+              for b, o in enumerate(orc_ids)]
+    for l in range(s.n_layers):
+        for name, off, n, is_act in layout:
+            o0, _ = fields[name]
+            if name in ("k", "v"):
+                vals = np.stack([stored[b][l][0 if name == "k" else 1].reshape(-1) for b in range(B)])
+            else:
+                vals = np.stack([outs[b][3][l, o0:o0 + n] for b in range(B)])   # [B][n] float64
+            if is_act:
+                vals = oracle.round_act_n(vals, act).reshape(B, n)
+                raw = _to_act(vals, act)
+            else:
+                raw = vals.astype(np.float32)
+            inj[l, off:off + raw.nbytes] = raw.view(np.uint8).reshape(-1)
+    inj_d = t.as_tensor(inj).to(P.dev)
+    cap_d = t.zeros_like(inj_d)
+    tok = t.as_tensor(np.asarray(toks, dtype=np.int32)).to(P.dev)
+    nxt = t.empty(B, dtype=t.int32, device=P.dev)
+    logits = t.empty((B, s.vocab), dtype=t.float32, device=P.dev)
+    dtd.dtd_debug_decode_probe(P.eng.h, list(gpu_ids), tok.data_ptr(), inj_d.data_ptr(), cap_d.data_ptr(),
+                               nxt.data_ptr(), logits.data_ptr())
+    t.cuda.synchronize()
+    if not check:
+        return outs
+    cap = cap_d.cpu().numpy()
+    lg = logits.cpu().numpy()
+    ng = nxt.cpu().numpy()
+    flips = 0
+    worst = 0.0
+    for l in range(s.n_layers):
+        for name, off, n, is_act in layout:
+            if name == "x_in":
+                continue
+            o0, _ = fields[name]
+            for b in range(B):
+                raw = cap[l, off + b * n * (2 if (is_act and act == synth.ACT_BF16) else 4):][
+                    : n * (2 if (is_act and act == synth.ACT_BF16) else 4)]
+                r = outs[b][3][l, o0:o0 + n]
+                where = f"{tag} seq {gpu_ids[b]} layer {l} {name}"
+                if is_act:
+                    flips += check_rounded(where, _from_act(raw.copy(), act), r, act)
+                else:
+                    e = normwise(raw.copy().view(np.float32), r)
+                    worst = max(worst, e)
+                    assert e <= TOL, f"{where}: {e:.3e}"
+    # the KV the GPU appended at the new position equals the oracle's, bit for bit
+    for b, o in enumerate(orc_ids):
+        for l in range(s.n_layers):
+            kr, vr, ksr, vsr = P.orc.kv_read_raw(P.oslot(o), l, int(poss[b]), 1)
+            kg, vg = np.empty_like(kr), np.empty_like(vr)
+            ksg = vsg = None
+            if ksr is not None:
+                ksg, vsg = np.empty_like(ksr), np.empty_like(vsr)
+            dtd.dtd_debug_kv_read(P.eng.h, gpu_ids[b], l, int(poss[b]), 1, kg, vg, ksg, vsg)
+            assert np.array_equal(kg, kr) and np.array_equal(vg, vr), f"{tag} seq {gpu_ids[b]} layer {l} KV"
+            if ksr is not None:
+                assert np.array_equal(ksg, ksr) and np.array_equal(vsg, vsr), f"{tag} KV scales"
+    for b in range(B):
+        no, lo = outs[b][0], outs[b][1]
+        e = normwise(lg[b], lo)
+        delta = np.abs(lg[b].astype(np.float64) - lo).max()
+        assert e <= TOL, f"{tag} seq {gpu_ids[b]} logits {e:.3e}"
+        if top2_margin(lo) > 2 * delta:
+            assert int(ng[b]) == no, f"{tag} seq {gpu_ids[b]}: token {int(ng[b])} vs {no}"
+    P.probe_stats = getattr(P, "probe_stats", [0, 0.0])
+    P.probe_stats[0] += flips
+    P.probe_stats[1] = max(P.probe_stats[1], worst)
+    return outs

@@ -1,0 +1,91 @@
+"""The C-ABI library: loads without a GPU, exports every declared symbol, and its host-only
+entry points (configuration checks, weight manifest) agree with the input recipe."""
+import ctypes as C
+
+import numpy as np
+import pytest
+
+from decoder_only_transformer_decode_amd import dtd, synth
+
+
+def test_library_exports_every_declared_function():
+    lib = dtd.load()
+    names = dtd.declared_functions()
+    assert len(names) >= 17
+    for n in names:
+        assert hasattr(lib, n), n
+        assert n in dtd._SIGS, f"binding lacks {n}"
+
+
+@pytest.mark.parametrize("w", synth.WORKLOADS, ids=lambda w: w.shape.name)
+def test_expected_tensors_match_input_recipe(w):
+    s = w.shape.replace(n_layers=2)
+    cfg = dtd.config_from_shape(s, max_ctx=256, max_batch=min(w.batch, 64))
+    st, msg = dtd.dtd_validate_config(cfg)
+    assert st == dtd.DTD_OK, msg
+    specs = {sp.name.decode(): sp for sp in dtd.dtd_expected_tensors(cfg)}
+    shapes = synth.matrix_shapes(s)
+    # sizes implied by the recipe's encodings, without generating the weights
+    want = {}
+    for name, (r, c) in shapes.items():
+        if s.wfmt == synth.W_BF16:
+            want[name + ".w"] = r * c * 2
+        else:
+            want[name + ".q"] = r * c
+            want[name + ".s"] = r * 4 if s.wfmt == synth.W_INT8_ROW else r * (c // 32) * 2
+    for n in synth.norm_names(s):
+        want[n + ".g"] = s.dim * 4
+    assert {k: v.nbytes for k, v in specs.items()} == want
+
+
+def test_expected_tensors_match_generated_bytes():
+    s = synth.tiny_shape(wfmt=synth.W_Q8_0, tied=True)
+    flat = synth.flat_tensors(synth.gen_weights(s, 3))
+    cfg = dtd.config_from_shape(s, max_ctx=64)
+    specs = {sp.name.decode(): sp.nbytes for sp in dtd.dtd_expected_tensors(cfg)}
+    assert specs == {k: v.nbytes for k, v in flat.items()}
+
+
+def _cfg(**kw):
+    c = dtd.config_from_shape(synth.TINY.shape, max_ctx=64)
+    for k, v in kw.items():
+        setattr(c, k, v)
+    return c
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(), dtd.DTD_OK),
+    (dict(abi_version=2), dtd.DTD_E_ARG),
+    (dict(n_kv_heads=3), dtd.DTD_E_ARG),
+    (dict(head_dim=50), dtd.DTD_E_UNSUPPORTED),
+    (dict(head_dim=256, dim=512), dtd.DTD_E_UNSUPPORTED),
+    (dict(dim=0), dtd.DTD_E_ARG),
+    (dict(wfmt=7), dtd.DTD_E_ARG),
+    (dict(max_batch=65), dtd.DTD_E_UNSUPPORTED),
+    (dict(max_batch=0), dtd.DTD_E_ARG),
+    (dict(kv_block_size=0), dtd.DTD_E_ARG),
+    (dict(dim=264), dtd.DTD_E_UNSUPPORTED),            # not a multiple of 16
+    (dict(wfmt=1, dim=272), dtd.DTD_E_ARG),            # Q8_0 needs multiples of 32
+    (dict(rope_theta=0.0), dtd.DTD_E_ARG),
+    (dict(n_q_heads=128, n_kv_heads=1, head_dim=32, dim=4096), dtd.DTD_E_UNSUPPORTED),  # G*hd > 2048
+])
+def test_validate_config(kw, status):
+    st, msg = dtd.dtd_validate_config(_cfg(**kw))
+    assert st == status, msg
+    if status != dtd.DTD_OK:
+        assert msg
+
+
+def test_expected_tensors_rejects_bad_config():
+    lib = dtd.load()
+    bad = _cfg(n_kv_heads=3)
+    assert lib.dtd_expected_tensors(C.byref(bad), None, 0) == dtd.DTD_E_ARG
+
+
+def test_null_engine_calls_are_errors_not_crashes():
+    lib = dtd.load()
+    assert lib.dtd_reset_seq(None, 1) == dtd.DTD_E_ARG
+    assert lib.dtd_seq_len(None, 1) == dtd.DTD_E_ARG
+    assert lib.dtd_decode_step(None, 1, None, None, None, None) == dtd.DTD_E_ARG
+    assert lib.dtd_last_error(None) == b"null engine"
+    lib.dtd_destroy(None)

@@ -1,0 +1,105 @@
+"""Parity at the measured shapes.
+
+The SmolLM3-3B-shaped model runs at full size in the launch configuration the benchmark
+times (batch 1, max context 2048): identical stored KV is written to the engine and the
+oracle for 2046 positions and two decode steps are compared in full (all 128256 logits,
+every layer's output).  The other shapes run at full width with two layers (the oracle's
+cost at 32-36 layers of 8B-class width and 64-sequence batches is out of reach of a
+test), with their real batch structure, KV format and long contexts.
+
+Each step is compared twice: kernel by kernel, with every GPU kernel reading the oracle's
+own inputs (fp32 outputs within 2e-3, bf16-rounded outputs equal to the oracle's rounding
+wherever it is unique), and free-running against max(2e-3, 4 x the oracle's own
+sensitivity to 1e-6 relative noise in its norm gains), because bf16 rounding points make
+the method itself that sensitive.
+"""
+import numpy as np
+import pytest
+
+from decoder_only_transformer_decode_amd import dtd, synth
+from _pair import ENV_FACTOR, TOL, Pair, need_gpu, normwise, probe_step, top2_margin
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    need_gpu()
+
+
+def _write_kv(P, O2, sid, gpu_ids, n, seed):
+    s = P.shape
+    for layer in range(s.n_layers):
+        k, v, ks, vs = synth.synthetic_kv(s, n, seed=seed, layer=layer)
+        ks16 = None if ks is None else ks.view(np.uint16)
+        vs16 = None if vs is None else vs.view(np.uint16)
+        for g in gpu_ids:
+            dtd.dtd_debug_kv_write(P.eng.h, g, layer, 0, k, v, ks16, vs16)
+        P.orc.kv_write(P.oslot(sid), layer, 0, k, v, ks, vs)
+        O2.kv_write(P.oslot(sid), layer, 0, k, v, ks, vs)
+
+
+def _run(P, O2, seq_ids, n_pos, steps=2, tok0=17):
+    """seq_ids: oracle/free-running GPU ids; probed GPU copies use id + 100."""
+    s = P.shape
+    toks = {sid: tok0 + 3 * i for i, sid in enumerate(seq_ids)}
+    pos = dict(n_pos)
+    worst_free, worst_env = 0.0, 0.0
+    for step in range(steps):
+        ng, lg, _ = P.gpu_step(seq_ids, [toks[i] for i in seq_ids])
+        outs = probe_step(P, [i + 100 for i in seq_ids], seq_ids, [toks[i] for i in seq_ids],
+                          [pos[i] for i in seq_ids], f"{s.name} step {step}")
+        for b, sid in enumerate(seq_ids):
+            no, lo = outs[b][0], outs[b][1]
+            fe = normwise(lg[b], lo)
+            pe = normwise(O2.step(P.oslot(sid), toks[sid], pos[sid])[1], lo)
+            print(f"{s.name} step {step} seq {sid} T={pos[sid] + 1}: probe ok (bf16 flips so far "
+                  f"{P.probe_stats[0]}, worst fp32 field err {P.probe_stats[1]:.2e}), margin "
+                  f"{top2_margin(lo):.3e}; free-running {fe:.2e} (token {int(ng[b])}/{no}), "
+                  f"oracle sensitivity {pe:.2e}", flush=True)
+            worst_free, worst_env = max(worst_free, fe), max(worst_env, pe)
+            toks[sid] = no
+            pos[sid] += 1
+    assert worst_free <= max(TOL, ENV_FACTOR * worst_env), (worst_free, worst_env)
+
+
+def _pair(w, shape, **kw):
+    P = Pair(shape, max_ctx=w.context, weights=synth.gen_weights(shape, synth.weights_seed(w)), **kw)
+    O2 = P.perturbed_oracle(9, max_ctx=w.context, max_seqs=kw.get("max_seqs", 1))
+    return P, O2
+
+
+def test_smollm3_shape_full_size_at_context_2048():
+    w = synth.SMOLLM3_3B
+    P, O2 = _pair(w, w.shape, max_seqs=2)
+    _write_kv(P, O2, 0, [0, 100], w.context - 2, seed=5)
+    _run(P, O2, [0], {0: w.context - 2})
+    P.close()
+
+
+def test_llama32_1b_shape_full_width_q8_0_tied_at_context_4096():
+    w = synth.LLAMA32_1B
+    P, O2 = _pair(w, w.shape.replace(n_layers=2), max_seqs=2)
+    _write_kv(P, O2, 0, [0, 100], w.context - 2, seed=6)
+    _run(P, O2, [0], {0: w.context - 2})
+    P.close()
+
+
+def test_qwen3_8b_shape_full_width_bf16_paged_batch():
+    w = synth.QWEN3_8B
+    ctx = [int(c) for c in synth.context_lengths(w.batch)[:3]]
+    P, O2 = _pair(w, w.shape.replace(n_layers=2), max_seqs=6, max_batch=3)
+    for sid, n in enumerate(ctx):
+        _write_kv(P, O2, sid, [sid, sid + 100], n, seed=30 + sid)
+    _run(P, O2, [0, 1, 2], dict(enumerate(ctx)))
+    P.close()
+
+
+def test_llama3_8b_shape_full_width_int8_kv_at_context_16384():
+    w = synth.LLAMA3_8B
+    n = w.context - 2
+    P, O2 = _pair(w, w.shape.replace(n_layers=2), max_seqs=4, max_batch=2)
+    for sid in (0, 1):
+        _write_kv(P, O2, sid, [sid, sid + 100], n, seed=40 + sid)
+    _run(P, O2, [1, 0], {0: n, 1: n})
+    P.close()

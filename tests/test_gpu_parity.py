@@ -1,0 +1,349 @@
+"""Parity of the HIP decode step (through the C ABI) with the CPU oracle.
+
+Bar: bit-exact for dequantisation, block-table indexing and greedy tokens on the tiny
+config; logits and hidden states within max|gpu - oracle| / max|oracle| <= 2e-3.  Where a
+test is teacher-forced, the GPU's greedy token must equal the oracle's whenever the
+oracle's top-1/top-2 margin exceeds twice the observed logit error (then no rounding
+difference of that size can reorder them).
+"""
+import numpy as np
+import pytest
+
+from decoder_only_transformer_decode_amd import dtd, synth
+from _pair import ENV_FACTOR, TOL, Pair, need_gpu, normwise, probe_step, top2_margin
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    need_gpu()
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def _check_logits(tag, g_log, o_log, g_tok, o_tok):
+    err = normwise(g_log, o_log)
+    delta = np.abs(np.asarray(g_log, np.float64) - np.asarray(o_log, np.float64)).max()
+    margin = top2_margin(o_log)
+    _say(f"{tag}: logits err {err:.2e} margin {margin:.3e} tok gpu {g_tok} oracle {o_tok}")
+    assert err <= TOL, f"{tag}: logits normwise error {err:.3e}"
+    if margin > 2 * delta:
+        assert g_tok == o_tok, f"{tag}: greedy token differs with margin {margin} > 2*{delta}"
+
+
+# ---------------------------------------------------------------------------------------
+# the tiny configuration, end to end, free-running greedy
+# ---------------------------------------------------------------------------------------
+
+def test_tiny_config_end_to_end_identical_greedy_tokens():
+    w = synth.TINY
+    s = w.shape
+    P = Pair(s, max_ctx=w.context, seed=synth.weights_seed(w))
+    prompt = synth.prompt_tokens(s.vocab, w.prompt_len)
+    g_tok, g_log = P.gpu_prefill(0, prompt)
+    o_tok, o_log = P.orc_prefill(0, prompt)
+    _check_logits("prefill", g_log, o_log, g_tok, o_tok)
+    toks_g, toks_o = [g_tok], [o_tok]
+    worst_h = 0.0
+    for step in range(w.context - w.prompt_len):
+        pos = w.prompt_len + step
+        ng, lg, hid = P.gpu_step([0], [toks_g[-1]], capture=True)
+        no, lo, ho = P.orc_step(0, toks_o[-1], pos, hidden=True)
+        for layer in range(s.n_layers + 1):
+            e = normwise(hid[layer, 0], ho[layer])
+            worst_h = max(worst_h, e)
+            assert e <= TOL, f"step {step} layer {layer} hidden error {e:.3e}"
+        _check_logits(f"step {step}", lg[0], lo, int(ng[0]), no)
+        toks_g.append(int(ng[0]))
+        toks_o.append(no)
+    _say(f"tiny: tokens {toks_g}, worst hidden err {worst_h:.2e}")
+    assert toks_g == toks_o
+    assert len(toks_g) == 33
+    P.close()
+
+
+# ---------------------------------------------------------------------------------------
+# every storage format, multi-tile and ragged shapes
+#
+# Two comparisons per step.  (1) Kernel by kernel (dtd_debug_decode_probe): every GPU
+# kernel of every layer reads the oracle's own input for it.  fp32 outputs (q, k, v, the
+# residual stream, logits) must be within 2e-3; outputs rounded to bf16 (the norm outputs,
+# attention output, SwiGLU output) must equal the oracle's rounding of its unrounded value
+# wherever that rounding is unique, i.e. outside a band of 2e-5 x rms around a rounding
+# midpoint, and be one of the two neighbours inside it.  (2) Free-running: the GPU's own
+# trajectory against the oracle's.  With bf16 rounding points the method itself is
+# ill-conditioned: fp32-rounding-sized noise flips a few roundings, each moving the outputs
+# by up to ~1e-3.  The free-running bound is max(2e-3, 4 x the distance between the oracle
+# and an oracle whose norm gains carry 1e-6 relative noise), on the same tokens.
+# ---------------------------------------------------------------------------------------
+
+_GRID = synth.ModelShape("grid", 320, 2, 10, 2, 32, 608, 1000, synth.W_INT8_ROW, synth.ACT_F32, synth.KV_F32)
+_FORMATS = [
+    dict(),
+    dict(act=synth.ACT_BF16, kvfmt=synth.KV_BF16),
+    dict(wfmt=synth.W_Q8_0, act=synth.ACT_BF16, kvfmt=synth.KV_BF16, tied=True),
+    dict(wfmt=synth.W_BF16, act=synth.ACT_BF16, kvfmt=synth.KV_BF16),
+    dict(act=synth.ACT_BF16, kvfmt=synth.KV_I8),
+    dict(wfmt=synth.W_Q8_0, kvfmt=synth.KV_I8),
+    dict(n_q_heads=8, n_kv_heads=4, head_dim=64, act=synth.ACT_BF16, kvfmt=synth.KV_BF16),
+    dict(n_q_heads=4, n_kv_heads=4, head_dim=16, wfmt=synth.W_BF16),   # MHA, q_dim != D
+]
+
+
+class Tracker:
+    """Free-running errors and the oracle's own sensitivity over a whole run."""
+
+    def __init__(self):
+        self.gpu = 0.0
+        self.env = 0.0
+
+    def add(self, g, r, rp):
+        self.gpu = max(self.gpu, normwise(g, r))
+        self.env = max(self.env, normwise(rp, r))
+
+    def check(self, tag):
+        bound = max(TOL, ENV_FACTOR * self.env)
+        _say(f"{tag}: free-running max err {self.gpu:.2e}, oracle sensitivity {self.env:.2e}, bound {bound:.2e}")
+        assert self.gpu <= bound, f"{tag}: free-running error {self.gpu:.3e} > {bound:.3e}"
+
+
+def teacher_forced(P, gpu_ids, orc_ids, toks, poss, tag):
+    """One probed step: every GPU kernel fed the oracle's inputs and compared with it."""
+    return probe_step(P, gpu_ids, orc_ids, toks, poss, tag)
+
+
+@pytest.mark.parametrize("kw", _FORMATS, ids=lambda kw: "-".join(f"{k}={v}" for k, v in kw.items()) or "base")
+def test_formats(kw):
+    s = _GRID.replace(**kw)
+    P = Pair(s, max_ctx=96, max_seqs=2, seed=21)
+    O2 = P.perturbed_oracle(1, max_ctx=96)
+    prompt = synth.prompt_tokens(s.vocab, 70, seed=3)
+    tr = Tracker()
+    # sequence 0 (GPU) is teacher-forced position by position; sequence 1 (GPU) runs free
+    for i, t in enumerate(prompt[:-1]):
+        teacher_forced(P, [0], [0], [int(t)], [i], f"prefill {i}")
+        O2.step(0, int(t), i)
+    _, g_log = P.gpu_prefill(1, prompt)
+    outs = teacher_forced(P, [0], [0], [int(prompt[-1])], [69], "prefill 69")
+    tr.add(g_log, outs[0][1], O2.step(0, int(prompt[-1]), 69)[1])
+    tok = outs[0][0]
+    for step in range(8):
+        ng, lg, hid = P.gpu_step([1], [tok], capture=True)
+        outs = teacher_forced(P, [0], [0], [tok], [70 + step], f"step {step}")
+        o2 = O2.step(0, tok, 70 + step)
+        tr.add(lg[0], outs[0][1], o2[1])
+        tok = outs[0][0]
+    tr.check("formats " + s.name)
+    P.close()
+
+
+def test_dequant_rows_bit_exact_all_formats():
+    for kw in _FORMATS[:4]:
+        s = _GRID.replace(**kw)
+        P = Pair(s, max_ctx=32, seed=5)
+        t = P.torch
+        for name, (rows, cols) in synth.matrix_shapes(s).items():
+            out = t.empty((rows, cols), dtype=t.float32, device=P.dev)
+            dtd.dtd_debug_dequant_rows(P.eng.h, name, 0, rows, out.data_ptr())
+            got = out.cpu().numpy()
+            parts = P.w[name]
+            import oracle
+            w = parts.get("w", parts.get("q"))
+            sc = parts.get("s")
+            for r in range(rows):
+                ref = oracle.dequant_row(s.wfmt, w, sc, r)
+                assert np.array_equal(got[r].view(np.uint32), ref.view(np.uint32)), (name, r)
+        P.close()
+
+
+# ---------------------------------------------------------------------------------------
+# batched decode over paged KV: sequences of different lengths in one step
+# ---------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("kw", [dict(), dict(wfmt=synth.W_BF16, act=synth.ACT_BF16, kvfmt=synth.KV_BF16),
+                                dict(act=synth.ACT_BF16, kvfmt=synth.KV_I8)], ids=["f32", "bf16", "i8kv"])
+def test_batched_decode_mixed_lengths(kw):
+    s = _GRID.replace(**kw)
+    lens = [3, 17, 40, 64, 65]
+    ids = [7, 3, 11, 5, 9]
+    P = Pair(s, max_ctx=80, max_seqs=12, max_batch=6, seed=8)
+    O2 = P.perturbed_oracle(2, max_ctx=80, max_seqs=6)
+    toks = {}
+    tr = Tracker()
+    # free-running sequences use the ids; teacher-forced copies use id + 100
+    for sid, n in zip(ids, lens):
+        prompt = synth.prompt_tokens(s.vocab, n, seed=sid)
+        P.gpu_prefill(sid, prompt)
+        for i, t in enumerate(prompt):
+            outs = teacher_forced(P, [sid + 100], [sid], [int(t)], [i], f"prefill seq {sid} pos {i}")
+            O2.step(P.oslot(sid), int(t), i)
+        toks[sid] = outs[0][0]
+    order = [9, 7, 5, 11, 3]          # batch order differs from creation order
+    pos = {sid: n for sid, n in zip(ids, lens)}
+    for step in range(4):
+        ng, lg, hid = P.gpu_step(order, [toks[i] for i in order])
+        outs = teacher_forced(P, [i + 100 for i in order], order, [toks[i] for i in order],
+                              [pos[i] for i in order], f"step {step}")
+        for b, sid in enumerate(order):
+            tr.add(lg[b], outs[b][1], O2.step(P.oslot(sid), toks[sid], pos[sid])[1])
+            toks[sid] = outs[b][0]
+            pos[sid] += 1
+    for sid in ids:
+        assert P.eng.seq_len(sid) == pos[sid] == P.eng.seq_len(sid + 100)
+    tr.check("batched " + s.name)
+    P.close()
+
+
+# ---------------------------------------------------------------------------------------
+# KV cache: block-table indexing, long contexts from identical stored KV
+# ---------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("kvfmt", [synth.KV_F32, synth.KV_BF16, synth.KV_I8])
+def test_kv_block_table_roundtrip_bit_exact(kvfmt):
+    s = _GRID.replace(kvfmt=kvfmt)
+    P = Pair(s, max_ctx=200, max_seqs=2, seed=1)
+    n, hk, hd = 150, s.n_kv_heads, s.head_dim
+    t, j, i = np.meshgrid(np.arange(n), np.arange(hk), np.arange(hd), indexing="ij")
+    code = (t * 7 + j * 3 + i) % 251 - 125            # exactly representable in every format
+    if kvfmt == synth.KV_F32:
+        k = code.astype(np.float32); v = (-code).astype(np.float32)
+    elif kvfmt == synth.KV_BF16:
+        k = synth.f32_to_bf16_bits(code.astype(np.float32)); v = synth.f32_to_bf16_bits((-code).astype(np.float32))
+    else:
+        k = code.clip(-127, 127).astype(np.int8); v = (-code).clip(-127, 127).astype(np.int8)
+    ks = vs = None
+    if kvfmt == synth.KV_I8:
+        ks = (np.arange(n * hk).reshape(n, hk) % 97 + 1).astype(np.float16).view(np.uint16)
+        vs = (np.arange(n * hk).reshape(n, hk) % 89 + 2).astype(np.float16).view(np.uint16)
+    for layer in range(s.n_layers):
+        dtd.dtd_debug_kv_write(P.eng.h, 4, layer, 0, k, v, ks, vs)
+        # a second sequence interleaves its blocks with the first one's
+        dtd.dtd_debug_kv_write(P.eng.h, 6, layer, 0, v, k, vs, ks)
+    for layer in range(s.n_layers):
+        for sid, (ek, ev, eks, evs) in ((4, (k, v, ks, vs)), (6, (v, k, vs, ks))):
+            ko, vo = np.empty_like(k), np.empty_like(v)
+            kso = vso = None
+            if kvfmt == synth.KV_I8:
+                kso, vso = np.empty_like(ks), np.empty_like(vs)
+            dtd.dtd_debug_kv_read(P.eng.h, sid, layer, 0, n, ko, vo, kso, vso)
+            assert np.array_equal(ko, ek) and np.array_equal(vo, ev)
+            if kvfmt == synth.KV_I8:
+                assert np.array_equal(kso, eks) and np.array_equal(vso, evs)
+    P.close()
+
+
+@pytest.mark.parametrize("kw,n_pos", [(dict(act=synth.ACT_BF16, kvfmt=synth.KV_BF16), 700),
+                                      (dict(act=synth.ACT_BF16, kvfmt=synth.KV_I8), 1000),
+                                      (dict(), 333)], ids=["bf16-700", "i8-1000", "f32-333"])
+def test_long_context_from_identical_stored_kv(kw, n_pos):
+    s = _GRID.replace(**kw)
+    P = Pair(s, max_ctx=n_pos + 4, max_seqs=2, seed=2)
+    O2 = P.perturbed_oracle(3, max_ctx=n_pos + 4)
+    P.write_kv_both(0, n_pos, seed=77, extra=[(O2, 0)])
+    for layer in range(s.n_layers):          # the free-running GPU copy gets the same KV
+        k, v, ks, vs = synth.synthetic_kv(s, n_pos, 77, layer)
+        dtd.dtd_debug_kv_write(P.eng.h, 1, layer, 0, k, v, None if ks is None else ks.view(np.uint16),
+                               None if vs is None else vs.view(np.uint16))
+    tr = Tracker()
+    tok = 5
+    for step in range(3):
+        ng, lg, _ = P.gpu_step([1], [tok])
+        outs = teacher_forced(P, [0], [0], [tok], [n_pos + step], f"T={n_pos + step + 1}")
+        tr.add(lg[0], outs[0][1], O2.step(0, tok, n_pos + step)[1])
+        tok = outs[0][0]
+    tr.check(f"long context {n_pos}")
+    # the KV the GPU appended (teacher-forced copy) matches the oracle's stored KV
+    for layer in range(s.n_layers):
+        kr, vr, ksr, vsr = P.orc.kv_read_raw(0, layer, n_pos, 3)
+        ko, vo = np.empty_like(kr), np.empty_like(vr)
+        kso = vso = None
+        if ksr is not None:
+            kso, vso = np.empty_like(ksr), np.empty_like(vsr)
+        dtd.dtd_debug_kv_read(P.eng.h, 0, layer, n_pos, 3, ko, vo, kso, vso)
+        kd, vd = P.orc.kv_read(0, layer, n_pos, 3)
+        if s.kvfmt == synth.KV_F32:
+            gk, gv = ko.astype(np.float64), vo.astype(np.float64)
+        elif s.kvfmt == synth.KV_BF16:
+            gk, gv = synth.bf16_bits_to_f32(ko).astype(np.float64), synth.bf16_bits_to_f32(vo).astype(np.float64)
+        else:
+            gk = ko.astype(np.float64) * kso.view(np.float16).astype(np.float64)[..., None]
+            gv = vo.astype(np.float64) * vso.view(np.float16).astype(np.float64)[..., None]
+        assert normwise(gk, kd) <= TOL and normwise(gv, vd) <= TOL
+    P.close()
+
+
+# ---------------------------------------------------------------------------------------
+# engine semantics
+# ---------------------------------------------------------------------------------------
+
+def test_prefill_equals_sequential_steps_and_is_deterministic():
+    s = _GRID.replace(act=synth.ACT_BF16, kvfmt=synth.KV_BF16)
+    P = Pair(s, max_ctx=64, max_seqs=3, seed=4)
+    prompt = synth.prompt_tokens(s.vocab, 20, seed=9)
+    _, lp = P.gpu_prefill(1, prompt)
+    P.gpu_prefill(2, prompt[:1])
+    for t in prompt[1:]:
+        _, ls, _ = P.gpu_step([2], [t])
+    assert np.array_equal(lp, ls[0])
+    P.eng.reset_seq(1)
+    _, lp2 = P.gpu_prefill(1, prompt)
+    assert np.array_equal(lp, lp2)
+    P.close()
+
+
+def test_error_paths_leave_state_unchanged():
+    t = pytest.importorskip("torch")
+    s = _GRID
+    P = Pair(s, max_ctx=40, max_seqs=2, max_batch=2, kv_num_blocks=3, seed=4)
+    h = P.eng.h
+    dev = P.dev
+    tok = t.zeros(4, dtype=t.int32, device=dev)
+    out = t.zeros(4, dtype=t.int32, device=dev)
+    lib = dtd.load()
+    ids = (dtd.C.c_int64 * 2)(1, 2)
+    assert lib.dtd_decode_step(h, 1, ids, tok.data_ptr(), out.data_ptr(), None) == dtd.DTD_E_NOSEQ
+    P.gpu_prefill(1, [1, 2, 3])
+    same = (dtd.C.c_int64 * 2)(1, 1)
+    assert lib.dtd_decode_step(h, 2, same, tok.data_ptr(), out.data_ptr(), None) == dtd.DTD_E_ARG
+    assert lib.dtd_decode_step(h, 3, ids, tok.data_ptr(), out.data_ptr(), None) == dtd.DTD_E_ARG
+    big = t.zeros(60, dtype=t.int32, device=dev)
+    assert lib.dtd_prefill(h, 1, big.data_ptr(), 60, out.data_ptr(), None) == dtd.DTD_E_CTX
+    # 3 blocks of 16: seq 1 holds one; 40 positions of a new sequence need 3 -> KV full
+    assert lib.dtd_prefill(h, 2, big.data_ptr(), 40, out.data_ptr(), None) == dtd.DTD_E_KVFULL
+    assert P.eng.seq_len(1) == 3 and P.eng.seq_len(2) == dtd.DTD_E_NOSEQ
+    assert lib.dtd_reset_seq(h, 99) == dtd.DTD_E_NOSEQ
+    bad = t.tensor([5, s.vocab + 3], dtype=t.int32, device=dev)
+    assert lib.dtd_prefill(h, 2, bad.data_ptr(), 2, out.data_ptr(), None) == dtd.DTD_OK
+    assert lib.dtd_check_device_errors(h) == dtd.DTD_E_ARG
+    assert lib.dtd_check_device_errors(h) == dtd.DTD_OK
+    P.close()
+
+
+def test_load_weights_fail_closed():
+    s = _GRID
+    w = synth.flat_tensors(synth.gen_weights(s, 1))
+    eng = dtd.Engine(s, max_ctx=16)
+    missing = dict(w)
+    missing.pop("L1.w_down.q")
+    with pytest.raises(dtd.DtdError) as ei:
+        eng.load_weights(missing)
+    assert ei.value.status == dtd.DTD_E_ARG and "missing" in str(ei.value)
+    wrong = dict(w)
+    wrong["L0.wq.s"] = wrong["L0.wq.s"][:-1]
+    with pytest.raises(dtd.DtdError):
+        eng.load_weights(wrong)
+    extra = dict(w)
+    extra["L9.wq.q"] = w["L0.wq.q"]
+    with pytest.raises(dtd.DtdError):
+        eng.load_weights(extra)
+    t = eng.torch
+    tok = t.zeros(1, dtype=t.int32, device=eng.device)
+    with pytest.raises(dtd.DtdError) as ei:
+        eng.prefill(0, tok)
+    assert ei.value.status == dtd.DTD_E_STATE
+    eng.load_weights(w)
+    eng.prefill(0, tok)
+    eng.close()
