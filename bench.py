@@ -82,7 +82,7 @@ def main():
     ap.add_argument("--steps", type=int, default=1536)
     ap.add_argument("--warmup", type=int, default=16)
     ap.add_argument("--workload", default=synth.SMOLLM3_3B.shape.name, choices=sorted(synth.BY_NAME))
-    ap.add_argument("--cpu-steps", type=int, default=8)
+    ap.add_argument("--cpu-steps", type=int, default=40)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true")
     args = ap.parse_args()
