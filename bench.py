@@ -85,6 +85,8 @@ def main():
     ap.add_argument("--cpu-steps", type=int, default=40)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true")
+    ap.add_argument("--path", choices=["auto", "per-kernel", "persistent"], default="auto",
+                    help="schedule: auto (persistent step kernel at batch 1), or force one")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this decode step runs on a single MI355X and has no "
@@ -109,7 +111,11 @@ def main():
     dev = torch.device("cuda", 0)
     eng = dtd.Engine(s, max_ctx=w.context, max_seqs=2, max_batch=1)
     eng.load_weights(synth.flat_tensors(weights))
-    print(f"[bench] weights generated in {t_gen:.1f} s and loaded", file=sys.stderr, flush=True)
+    dtd.dtd_debug_set_path(eng.h, {"auto": dtd.PATH_AUTO, "per-kernel": dtd.PATH_PER_KERNEL,
+                                   "persistent": dtd.PATH_PERSISTENT}[args.path])
+    persistent = dtd.dtd_debug_uses_persistent(eng.h, 1)
+    print(f"[bench] weights generated in {t_gen:.1f} s and loaded; "
+          f"{'persistent step kernel' if persistent else 'one kernel per sub-step'}", file=sys.stderr, flush=True)
 
     prompt = torch.as_tensor(synth.prompt_tokens(s.vocab, w.prompt_len)).to(dev)
     tok = torch.zeros(1, dtype=torch.int32, device=dev)
@@ -149,19 +155,25 @@ def main():
 
     roofline = None
     if not args.no_kernel_timing:
-        # same workload again with HIP events around every gate/up projection launch (the
-        # kernel moving the most bytes), on the engine's stream
+        # the same workload again with HIP events around every launch of the kernel that
+        # moves the most bytes, on the engine's stream: the persistent step kernel (weights
+        # + KV of one step per launch) or, per sub-step, the gate/up projection
         fresh_sequence()
-        dtd.dtd_debug_kernel_timing(eng.h, dtd.KERNEL_GATE_UP, True)
+        kind = dtd.KERNEL_STEP if persistent else dtd.KERNEL_GATE_UP
+        dtd.dtd_debug_kernel_timing(eng.h, kind, True)
         decode(K)
-        ms, cnt = dtd.dtd_debug_kernel_timing(eng.h, dtd.KERNEL_GATE_UP, False)
-        per_launch = wb["per_layer"]["gate_up"]
+        ms, cnt = dtd.dtd_debug_kernel_timing(eng.h, kind, False)
+        if persistent:
+            per_launch = wtot + kv_total / K
+            name = "k_step (persistent batch-1 decode step, int8-row weights, bf16 KV)"
+        else:
+            per_launch = wb["per_layer"]["gate_up"]
+            name = "k_gemv (gate/up projection, int8-row, SwiGLU epilogue)"
         avg_s = ms / 1e3 / max(cnt, 1)
-        ach = per_launch / avg_s / 1e9
+        ach = per_launch / avg_s / 1e9 if cnt else 0.0
         roofline = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                    "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None,
-                    "kernel": "k_gemv (gate/up projection, int8-row, SwiGLU epilogue)",
-                    "bytes_per_launch": per_launch, "avg_launch_us": round(avg_s * 1e6, 2),
+                    "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None, "kernel": name,
+                    "bytes_per_launch": round(per_launch), "avg_launch_us": round(avg_s * 1e6, 2),
                     "launches": cnt}
 
     cpu = None

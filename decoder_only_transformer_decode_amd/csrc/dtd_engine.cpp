@@ -92,10 +92,23 @@ struct dtd_engine {
 
   float* capture = nullptr;
 
+  // persistent batch-1 step kernel
+  bool persist_ok = false;
+  int nwg = 0;                   // workgroups (one per compute unit)
+  size_t p_smem = 0;
+  int p_nch = 0;                 // chunk stride of partials for the persistent path
+  PLayer* players = nullptr;     // [L] device table
+  uint64_t* tags = nullptr;      // tagged hand-off buffers of the step kernel (one allocation)
+  size_t tags_words = 0;
+  uint32_t epoch = 1;            // tag of the next launch's first phase (0 never used)
+  int path = 0;                  // 0 auto, 1 per-kernel, 2 persistent
+
   int timing_kind = -1;
   std::vector<TimerPair> timers;
   size_t timers_used = 0;
 };
+
+static thread_local std::string g_create_err;   // message of this thread's last failed dtd_create
 
 // ---------------------------------------------------------------------------------------
 // helpers
@@ -270,7 +283,7 @@ static void free_all(dtd_engine* e) {
   release_weights(e);
   void* ps[] = {e->rope_cos, e->rope_sin, e->kpool, e->vpool, e->kspool, e->vspool, e->bt_dev,
                 e->x, e->xn, e->q, e->knew, e->vnew, e->partials, e->o, e->h, e->logits,
-                e->err_dev, e->desc_dev, e->rows_dev};
+                e->err_dev, e->desc_dev, e->rows_dev, e->players, e->tags};
   for (void* p : ps)
     if (p) (void)hipFree(p);
   if (e->desc_host) (void)hipHostFree(e->desc_host);
@@ -281,18 +294,30 @@ static void free_all(dtd_engine* e) {
 }
 
 extern "C" dtd_status dtd_create(const dtd_config* cfg, void* hip_stream, dtd_engine** out) {
-  if (!out) return DTD_E_ARG;
+  g_create_err.clear();
+  if (!out) { g_create_err = "dtd_create: out is null"; return DTD_E_ARG; }
   *out = nullptr;
-  const dtd_status vs = check_config(cfg, nullptr, 0);
-  if (vs != DTD_OK) return vs;
+  char vmsg[256] = {0};
+  const dtd_status vs = check_config(cfg, vmsg, (int32_t)sizeof(vmsg));
+  if (vs != DTD_OK) {
+    g_create_err = std::string("dtd_create: ") + vmsg;
+    return vs;
+  }
   dtd_engine* e = new dtd_engine();
   for (int i = 0; i < kRing; i++) { e->desc_ev[i] = nullptr; e->desc_ev_used[i] = false; }
   e->cfg = *cfg;
   e->d = make_dims(cfg);
   e->stream = (hipStream_t)hip_stream;
   const Dims& d = e->d;
-  auto cleanup = [&](dtd_status st) { free_all(e); delete e; return st; };
-  if (hipGetDevice(&e->device) != hipSuccess) return cleanup(DTD_E_HIP);
+  // a failed create leaves its message for dtd_last_error(NULL) on this thread
+  auto cleanup = [&](dtd_status st) {
+    g_create_err = e->err.empty() ? "dtd_create: a HIP call failed: " + std::string(hipGetErrorString(hipGetLastError()))
+                                  : "dtd_create: " + e->err;
+    free_all(e);
+    delete e;
+    return st;
+  };
+  if (hipGetDevice(&e->device) != hipSuccess) { e->err = "hipGetDevice failed"; return cleanup(DTD_E_HIP); }
 
   // RoPE tables: angle pos * theta^(-2i/d) in double, cos/sin stored as fp32
   const int half = d.hd / 2;
@@ -332,13 +357,37 @@ extern "C" dtd_status dtd_create(const dtd_config* cfg, void* hip_stream, dtd_en
       (st = dev_alloc(e, &e->q, (size_t)MB * d.q_dim * 4)) ||
       (st = dev_alloc(e, &e->knew, (size_t)MB * d.kv_dim * 4)) ||
       (st = dev_alloc(e, &e->vnew, (size_t)MB * d.kv_dim * 4)) ||
-      (st = dev_alloc(e, &e->partials, (size_t)MB * d.Hq * d.nch * (d.hd + 2) * 4)) ||
+      (st = dev_alloc(e, &e->partials, std::max((size_t)MB * d.nch, (size_t)(cfg->max_ctx + kAttnTile - 1) / kAttnTile) *
+                                              d.Hq * (d.hd + 2) * 4)) ||
       (st = dev_alloc(e, &e->o, (size_t)MB * d.q_dim * ab)) ||
       (st = dev_alloc(e, &e->h, (size_t)MB * d.F * ab)) ||
       (st = dev_alloc(e, &e->logits, (size_t)MB * d.V * 4)) ||
       (st = dev_alloc(e, &e->err_dev, 16)) || (st = dev_alloc(e, &e->desc_dev, sizeof(StepDesc))))
     return cleanup(st);
   if (hipMemset(e->err_dev, 0, 16) != hipSuccess) return cleanup(DTD_E_HIP);
+
+  // persistent batch-1 step kernel: one workgroup per compute unit, all resident
+  {
+    int cus = 0, coop = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, e->device) != hipSuccess ||
+        hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, e->device) != hipSuccess)
+      return cleanup(DTD_E_HIP);
+    e->p_nch = (cfg->max_ctx + kAttnTile - 1) / kAttnTile;
+    e->p_smem = persistent_smem_bytes(d, e->p_nch);
+    if (coop && cus > 0 && persistent_prepare(d, e->p_smem, &per_cu) == hipSuccess && per_cu >= 1) {
+      e->persist_ok = true;
+      e->nwg = cus;
+    }
+    (void)hipGetLastError();
+    const int nw = e->nwg > 0 ? e->nwg : 1;
+    // tagged buffers: q, k, v, o, x_mid, h, x_out, chunk partials, per-workgroup argmax
+    e->tags_words = (size_t)2 * d.q_dim + 2 * (size_t)d.kv_dim + 2 * (size_t)d.D + (size_t)d.F +
+                    (size_t)d.Hq * e->p_nch * (d.hd + 2) + 2 * (size_t)nw;
+    if ((st = dev_alloc(e, &e->players, sizeof(PLayer) * (size_t)d.L)) ||
+        (st = dev_alloc(e, &e->tags, sizeof(uint64_t) * e->tags_words)))
+      return cleanup(st);
+    if (hipMemset(e->tags, 0, sizeof(uint64_t) * e->tags_words) != hipSuccess) return cleanup(DTD_E_HIP);
+  }
   if (hipHostMalloc((void**)&e->desc_host, sizeof(StepDesc) * kRing, 0) != hipSuccess ||
       hipHostMalloc((void**)&e->err_host, 16, 0) != hipSuccess)
     return cleanup(DTD_E_OOM);
@@ -370,7 +419,8 @@ extern "C" void dtd_destroy(dtd_engine* e) {
 }
 
 extern "C" const char* dtd_last_error(const dtd_engine* e) {
-  return e ? e->err.c_str() : "null engine";
+  if (e) return e->err.c_str();
+  return g_create_err.empty() ? "null engine" : g_create_err.c_str();
 }
 
 // ---------------------------------------------------------------------------------------
@@ -515,6 +565,21 @@ extern "C" dtd_status dtd_load_weights(dtd_engine* e, const dtd_tensor* t, int32
   if ((st = gain("final_norm", &e->final_norm))) goto bad;
   if (e->cfg.tied_embeddings) e->head = e->emb;
   else if ((st = upload_packed(e, {srcmat("lm_head", d.V, d.D)}, identity(0, d.V), d.D, &e->head))) goto bad;
+  {
+    std::vector<PLayer> tab((size_t)d.L);
+    const size_t kvb = kv_elem_bytes(e->cfg.kvfmt);
+    for (int l = 0; l < d.L; l++) {
+      const LayerW& W = e->layers[(size_t)l];
+      PLayer& P = tab[(size_t)l];
+      P.qkv = W.qkv; P.o = W.o; P.gu = W.gu; P.down = W.down;
+      P.attn_norm = W.attn_norm; P.ffn_norm = W.ffn_norm;
+      P.kv.k = (uint8_t*)e->kpool + (size_t)l * e->kv_layer_elems * kvb;
+      P.kv.v = (uint8_t*)e->vpool + (size_t)l * e->kv_layer_elems * kvb;
+      P.kv.ks = e->kspool ? e->kspool + (size_t)l * e->kv_layer_scales : nullptr;
+      P.kv.vs = e->vspool ? e->vspool + (size_t)l * e->kv_layer_scales : nullptr;
+    }
+    HIP_OK(e, hipMemcpy(e->players, tab.data(), sizeof(PLayer) * tab.size(), hipMemcpyHostToDevice));
+  }
   e->loaded = true;
   return DTD_OK;
 bad:
@@ -556,10 +621,6 @@ static hipError_t timed_end(dtd_engine* e, TimerPair* tp) {
 struct Update { int slot, lblock, pblock; };
 
 // Probe records of dtd_debug_decode_probe: per layer, fields [B][n] in this order.
-struct ProbeLayout {
-  size_t x_in, xn, q, k, v, o, x_mid, xn2, h, x_out, record;
-};
-
 static ProbeLayout probe_layout(const Dims& d, int B, size_t ab) {
   ProbeLayout p{};
   size_t off = 0;
@@ -581,7 +642,7 @@ static ProbeLayout probe_layout(const Dims& d, int B, size_t ab) {
 // With inject/capture (debug probe): every kernel of every layer reads its input from the
 // inject record and its output is copied to the capture record, so each kernel can be
 // compared with the reference operation on identical inputs.
-static dtd_status run_step(dtd_engine* e, int B, const int* slots, const int* poss,
+static dtd_status run_step(dtd_engine* e, int B, const int* slots, const int* poss, const int* pblks,
                            const int32_t* tokens, int32_t* next, float* logits_out, bool do_head,
                            const std::vector<Update>& upd, const uint8_t* inject = nullptr,
                            uint8_t* capture = nullptr) {
@@ -597,7 +658,7 @@ static dtd_status run_step(dtd_engine* e, int B, const int* slots, const int* po
   hd->tokens = tokens;
   hd->next_tokens = next;
   hd->logits_out = logits_out;
-  for (int b = 0; b < B; b++) { hd->pos[b] = poss[b]; hd->slot[b] = slots[b]; }
+  for (int b = 0; b < B; b++) { hd->pos[b] = poss[b]; hd->slot[b] = slots[b]; hd->pos_block[b] = pblks[b]; }
   for (size_t u = 0; u < upd.size(); u++) {
     hd->upd[u][0] = upd[u].slot; hd->upd[u][1] = upd[u].lblock; hd->upd[u][2] = upd[u].pblock;
   }
@@ -605,6 +666,55 @@ static dtd_status run_step(dtd_engine* e, int B, const int* slots, const int* po
   HIP_OK(e, hipEventRecord(e->desc_ev[e->ring], st));
   e->desc_ev_used[e->ring] = true;
   e->ring = (e->ring + 1) % kRing;
+
+  if (e->persist_ok && B == 1 && !e->capture && e->path != 1) {
+    PersistArgs a{};
+    a.d = d;
+    a.layers = e->players;
+    a.emb = e->emb;
+    a.head = e->head;
+    a.final_norm = e->final_norm;
+    a.desc = e->desc_dev;
+    a.bt = e->bt_dev;
+    a.rope_cos = e->rope_cos;
+    a.rope_sin = e->rope_sin;
+    {
+      uint64_t* t = e->tags;
+      a.t_q = t; t += d.q_dim;
+      a.t_k = t; t += d.kv_dim;
+      a.t_v = t; t += d.kv_dim;
+      a.t_o = t; t += d.q_dim;
+      a.t_xm = t; t += d.D;
+      a.t_h = t; t += d.F;
+      a.t_xo = t; t += d.D;
+      a.t_part = t; t += (size_t)d.Hq * e->p_nch * (d.hd + 2);
+      a.t_am = t;
+    }
+    // tags are 32-bit: before they would wrap, clear the buffers and start again at 1
+    const uint32_t ntag = (uint32_t)persistent_tags_per_step(d);
+    if (e->epoch > 0xffffffffu - ntag) {
+      HIP_OK(e, hipMemsetAsync(e->tags, 0, sizeof(uint64_t) * e->tags_words, st));
+      e->epoch = 1;
+    }
+    a.epoch = e->epoch;
+    a.logits = e->logits;
+    a.err = e->err_dev;
+    // attention split: about one (kv head, chunk) item per workgroup, chunks of >= 64
+    const int64_t T = poss[0] + 1;
+    int ct = (int)((T * d.Hkv + e->nwg - 1) / e->nwg);
+    ct = std::max(kAttnTile, (ct + kAttnTile - 1) / kAttnTile * kAttnTile);
+    a.ct = ct;
+    a.nch = e->p_nch;
+    a.xs_floats = (int)persistent_xs_floats(d, e->p_nch);
+    a.inject = inject;
+    a.capture = capture;
+    a.po = probe_layout(d, 1, act_bytes(e->cfg.act));
+    TIMED(6, launch_persistent(a, e->nwg, e->p_smem, st));
+    e->epoch += ntag;
+    HIP_OK(e, hipMemcpyAsync(e->err_host, e->err_dev, 4, hipMemcpyDeviceToHost, st));
+    return DTD_OK;
+  }
+  if (e->path == 2) return fail(e, DTD_E_UNSUPPORTED, "persistent step kernel unavailable for this call");
 
   HIP_OK(e, launch_embed(d, e->emb, e->desc_dev, B, e->bt_dev, e->x, e->err_dev, st));
   const size_t ab = act_bytes(e->cfg.act);
@@ -730,7 +840,9 @@ extern "C" dtd_status dtd_prefill(dtd_engine* e, int64_t seq_id, const int32_t* 
       upd.push_back({s.slot, (int)s.blocks.size() - 1, b});
     }
     const bool last = i == n - 1;
-    st = run_step(e, 1, &s.slot, &pos, tokens_dev + i, next_token_dev, last ? logits_dev : nullptr, last, upd);
+    const int pblk = s.blocks[(size_t)(pos / e->d.bs)];
+    st = run_step(e, 1, &s.slot, &pos, &pblk, tokens_dev + i, next_token_dev, last ? logits_dev : nullptr, last,
+                  upd);
     if (st) return st;
     s.len++;
   }
@@ -774,7 +886,7 @@ static dtd_status decode_impl(dtd_engine* e, int32_t batch, const int64_t* seq_i
   }
   if (need > (int)e->free_blocks.size())
     return fail(e, DTD_E_KVFULL, "decode_step: needs %d KV blocks, %zu free", need, e->free_blocks.size());
-  std::vector<int> slots((size_t)batch), poss((size_t)batch);
+  std::vector<int> slots((size_t)batch), poss((size_t)batch), pblks((size_t)batch);
   std::vector<Update> upd;
   for (int b = 0; b < batch; b++) {
     Seq& s = *ss[(size_t)b];
@@ -786,8 +898,9 @@ static dtd_status decode_impl(dtd_engine* e, int32_t batch, const int64_t* seq_i
     }
     slots[(size_t)b] = s.slot;
     poss[(size_t)b] = s.len;
+    pblks[(size_t)b] = s.blocks[(size_t)(s.len / e->d.bs)];
   }
-  st = run_step(e, batch, slots.data(), poss.data(), tokens_dev, next_tokens_dev, logits_dev, true, upd,
+  st = run_step(e, batch, slots.data(), poss.data(), pblks.data(), tokens_dev, next_tokens_dev, logits_dev, true, upd,
                 inject, capture);
   if (st) return st;
   for (int b = 0; b < batch; b++) ss[(size_t)b]->len++;
@@ -838,7 +951,12 @@ extern "C" dtd_status dtd_check_device_errors(dtd_engine* e) {
   if (e->broken) return fail(e, DTD_E_STATE, "engine unusable after a HIP error");
   HIP_OK(e, hipSetDevice(e->device));
   HIP_OK(e, hipStreamSynchronize(e->stream));
-  if (*e->err_host) {
+  const int32_t flags = *e->err_host;
+  if (flags & kErrBarrier) {
+    e->broken = true;
+    return fail(e, DTD_E_HIP, "persistent step kernel: a wait for another workgroup timed out; engine unusable");
+  }
+  if (flags) {
     *e->err_host = 0;
     HIP_OK(e, hipMemsetAsync(e->err_dev, 0, 4, e->stream));
     HIP_OK(e, hipStreamSynchronize(e->stream));
@@ -1046,7 +1164,7 @@ extern "C" dtd_status dtd_debug_kv_fill(dtd_engine* e, int64_t seq_id, int32_t l
 extern "C" dtd_status dtd_debug_kernel_timing(dtd_engine* e, int32_t kind, int32_t enable, double* total_ms,
                                               int64_t* count) {
   if (!e) return DTD_E_ARG;
-  if (kind < 0 || kind > 5) return fail(e, DTD_E_ARG, "kernel_timing: kind %d outside [0, 5]", kind);
+  if (kind < 0 || kind > 6) return fail(e, DTD_E_ARG, "kernel_timing: kind %d outside [0, 6]", kind);
   HIP_OK(e, hipSetDevice(e->device));
   double total = 0.0;
   int64_t cnt = 0;
@@ -1064,4 +1182,17 @@ extern "C" dtd_status dtd_debug_kernel_timing(dtd_engine* e, int32_t kind, int32
   if (total_ms) *total_ms = total;
   if (count) *count = cnt;
   return DTD_OK;
+}
+
+extern "C" dtd_status dtd_debug_set_path(dtd_engine* e, int32_t path) {
+  if (!e) return DTD_E_ARG;
+  if (path < 0 || path > 2) return fail(e, DTD_E_ARG, "set_path: path %d outside [0, 2]", path);
+  if (path == 2 && !e->persist_ok) return fail(e, DTD_E_UNSUPPORTED, "persistent step kernel unavailable on this device");
+  e->path = path;
+  return DTD_OK;
+}
+
+extern "C" int32_t dtd_debug_uses_persistent(const dtd_engine* e, int32_t batch) {
+  if (!e) return DTD_E_ARG;
+  return e->persist_ok && batch == 1 && !e->capture && e->path != 1 ? 1 : 0;
 }

@@ -10,6 +10,9 @@ namespace dtd {
 constexpr int kMaxBatch = 64;
 constexpr int kMaxUpdates = 64;
 constexpr int kAttnTile = 64;      // positions per LDS tile in decode attention (one per lane)
+constexpr int kPersistWaves = 8;   // waves per workgroup of the persistent step kernel
+constexpr int kErrToken = 1;       // device error bits: token id out of range
+constexpr int kErrBarrier = 2;     //                    a cross-workgroup wait timed out
 
 enum WFmt { W_INT8_ROW = 0, W_Q8_0 = 1, W_BF16 = 2 };
 enum Act { ACT_F32 = 0, ACT_BF16 = 1 };
@@ -28,6 +31,7 @@ struct StepDesc {
   float* logits_out;                 // [batch][V] or null (caller memory)
   int32_t pos[kMaxBatch];            // position the new token takes
   int32_t slot[kMaxBatch];           // sequence slot (block-table row)
+  int32_t pos_block[kMaxBatch];      // physical KV block of the new position
   int32_t upd[kMaxUpdates][3];       // (slot, logical block, physical block)
 };
 
@@ -77,7 +81,58 @@ struct EpiArgs {
   float* logits;       // [B][V] engine buffer
 };
 
-// ---- launchers (dtd_kernels.hip) ----
+// Byte offsets of the fields of one layer's probe record (see dtd_debug_decode_probe).
+struct ProbeLayout {
+  size_t x_in, xn, q, k, v, o, x_mid, xn2, h, x_out, record;
+};
+
+// One layer's weights and KV pool, as the persistent kernel reads them (device table).
+struct PLayer {
+  MatDev qkv, o, gu, down;
+  const float* attn_norm;
+  const float* ffn_norm;
+  KvLayer kv;
+};
+
+// Arguments of the persistent batch-1 step kernel (dtd_persistent.hip).  Vectors that
+// pass between workgroups live in "tagged" buffers: 64-bit words (epoch << 32 | fp32 bits)
+// written with device-scope stores; a reader polls a word until it carries the epoch of
+// the phase it wants, so the data and its readiness arrive in one memory round trip.
+struct PersistArgs {
+  Dims d;
+  const PLayer* layers;     // [L] in device memory
+  MatDev emb, head;
+  const float* final_norm;
+  const StepDesc* desc;
+  int32_t* bt;
+  const float* rope_cos;
+  const float* rope_sin;
+  uint64_t* t_q;            // tagged [q_dim] post-RoPE queries
+  uint64_t* t_k;            // tagged [kv_dim] post-RoPE new key
+  uint64_t* t_v;            // tagged [kv_dim] new value
+  uint64_t* t_o;            // tagged [q_dim] attention output (rounded to the activation type)
+  uint64_t* t_xm;           // tagged [D] residual stream after attention
+  uint64_t* t_h;            // tagged [F] SwiGLU output (rounded)
+  uint64_t* t_xo;           // tagged [D] residual stream after the feed-forward block
+  uint64_t* t_part;         // tagged [Hq][nch][hd+2] attention chunk partials (acc, m, l)
+  uint64_t* t_am;           // tagged [nwg][2] per-workgroup argmax (value, index)
+  uint32_t epoch;           // tag of this launch's first phase (6 per layer, 1 for the head)
+  float* logits;            // [V]
+  int32_t* err;
+  int ct;                   // attention chunk length of this step
+  int nch;                  // chunk stride of partials
+  int xs_floats;            // LDS floats before the residual-stream copy
+  const uint8_t* inject;    // probe records (null: normal step)
+  uint8_t* capture;
+  ProbeLayout po;
+};
+
+// ---- launchers (dtd_kernels.hip, dtd_persistent.hip) ----
+size_t persistent_smem_bytes(const Dims& d, int nch);
+size_t persistent_xs_floats(const Dims& d, int nch);
+int persistent_tags_per_step(const Dims& d);
+hipError_t persistent_prepare(const Dims& d, size_t smem, int* blocks_per_cu);
+hipError_t launch_persistent(const PersistArgs& a, int nwg, size_t smem, hipStream_t st);
 hipError_t launch_embed(const Dims& d, const MatDev& emb, const StepDesc* desc, int B,
                         int32_t* block_table, float* x, int32_t* err, hipStream_t st);
 hipError_t launch_rmsnorm(const Dims& d, const float* x, const float* g, void* xn, int B,

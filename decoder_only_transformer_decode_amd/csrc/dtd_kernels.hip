@@ -12,81 +12,13 @@
 #include <stdint.h>
 #include <limits.h>
 
+#include "dtd_device.h"
 #include "dtd_internal.h"
 
 namespace dtd {
 namespace {
 
-// ---------------------------------------------------------------------------------------
-// scalar helpers
-// ---------------------------------------------------------------------------------------
-
-__device__ __forceinline__ float bf16_to_f32(uint32_t b16) { return __uint_as_float(b16 << 16); }
-
-// float -> bf16, round to nearest even (NaN kept quiet)
-__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
-}
-
-__device__ __forceinline__ float round_act(float v, int act) {
-  return act == ACT_BF16 ? bf16_to_f32(f32_to_bf16(v)) : v;
-}
-
-__device__ __forceinline__ float f16_to_f32(uint16_t h) {
-  return (float)__builtin_bit_cast(_Float16, h);
-}
-
-__device__ __forceinline__ uint16_t f32_to_f16(float f) {  // hardware convert, RNE
-  return __builtin_bit_cast(uint16_t, (_Float16)f);
-}
-
-__device__ __forceinline__ float sext8(uint32_t u, int byte) {
-  return (float)((int32_t)(u << (24 - 8 * byte)) >> 24);
-}
-
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
-  return v;
-}
-
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
-  return v;
-}
-
-// sum over a 256-thread block; every thread gets the result
-__device__ __forceinline__ float block_sum256(float v, float* red) {
-  v = wave_sum(v);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  __syncthreads();
-  if (lane == 0) red[wave] = v;
-  __syncthreads();
-  return red[0] + red[1] + red[2] + red[3];
-}
-
-__device__ __forceinline__ float block_max256(float v, float* red) {
-  v = wave_max(v);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  __syncthreads();
-  if (lane == 0) red[wave] = v;
-  __syncthreads();
-  return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-}
-
-// one stored weight element as fp32: int8-row q*s, Q8_0 q*d (one fp32 product), bf16 widen
-__device__ __forceinline__ float deq_elem(const MatDev& m, int wfmt, int r, int c) {
-  const size_t e = (size_t)r * m.cols + c;
-  if (wfmt == W_INT8_ROW) return (float)((const int8_t*)m.w)[e] * ((const float*)m.s)[r];
-  if (wfmt == W_Q8_0)
-    return (float)((const int8_t*)m.w)[e] *
-           f16_to_f32(((const uint16_t*)m.s)[(size_t)r * (m.cols / 32) + c / 32]);
-  return bf16_to_f32(((const uint16_t*)m.w)[e]);
-}
+using namespace dev;
 
 // ---------------------------------------------------------------------------------------
 // S0 embedding (+ block-table updates of this step)
@@ -119,7 +51,7 @@ __global__ __launch_bounds__(256) void k_rmsnorm(const float* x, const float* g,
   const float* xb = x + (size_t)b * D;
   float ss = 0.f;
   for (int i = threadIdx.x; i < D; i += 256) ss += xb[i] * xb[i];
-  ss = block_sum256(ss, red);
+  ss = block_sum(ss, red);
   const float r = 1.0f / sqrtf(ss / (float)D + eps);
   if (act == ACT_BF16) {
     uint16_t* o = (uint16_t*)xn + (size_t)b * D;
@@ -322,213 +254,30 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
 }
 
 // ---------------------------------------------------------------------------------------
-// S4 + S5 split-K GQA decode attention with the KV append of the new token
-//
-// Work item = (chunk c, kv head j, sequence b).  The item streams positions
-// [c*ct, min((c+1)*ct, pos+1)) of head j through LDS in 64-position tiles; the G query
-// heads that share kv head j all use each staged K/V row, so K/V is read once per query
-// group (the GQA decode rule of the Qwen3-8B engine article, 4.4.2).  Softmax is online
-// across tiles (running max, running sum, rescaled accumulators); each item leaves an
-// unnormalised partial (acc, m, l) per head that k_combine merges.  The item whose chunk
-// holds the new position rounds the new k/v to the KV encoding, writes it through the
-// block table and uses the stored value.
+// S4 + S5 split-K GQA decode attention (work item in dtd_device.h) and the chunk merge
 // ---------------------------------------------------------------------------------------
 
-struct AttnArgs {
-  Dims d;
-  const StepDesc* desc;
-  const float* q;
-  const float* knew;
-  const float* vnew;
-  KvLayer kv;
-  const int32_t* bt;
-  float* partials;   // [B][Hq][nch][hd+2]
-};
-
-constexpr int kMaxOutPerThread = 8;   // G*hd <= 2048
-
 template <int KVFMT>
-__device__ __forceinline__ void stage_tile(const AttnArgs& a, const void* pool, const uint16_t* spool,
-                                           const int32_t* btrow, int j, int t0, int n, int pos,
-                                           const float* newv, float* t_s, int ldk) {
-  const Dims& d = a.d;
-  const int hd = d.hd, per = hd >> 2;
-  for (int e = threadIdx.x; e < n * per; e += 256) {
-    const int tl = e / per, i = (e - tl * per) * 4, t = t0 + tl;
-    float v0, v1, v2, v3;
-    if (t == pos) {
-      v0 = newv[i]; v1 = newv[i + 1]; v2 = newv[i + 2]; v3 = newv[i + 3];
-    } else {
-      const int blk = btrow[t / d.bs], off = t - (t / d.bs) * d.bs;
-      const size_t row = ((size_t)blk * d.Hkv + j) * d.bs + off;
-      const size_t base = row * hd + i;
-      if constexpr (KVFMT == KV_F32) {
-        const float4 f = *(const float4*)((const float*)pool + base);
-        v0 = f.x; v1 = f.y; v2 = f.z; v3 = f.w;
-      } else if constexpr (KVFMT == KV_BF16) {
-        const uint2 u = *(const uint2*)((const uint16_t*)pool + base);
-        v0 = __uint_as_float(u.x << 16); v1 = __uint_as_float(u.x & 0xffff0000u);
-        v2 = __uint_as_float(u.y << 16); v3 = __uint_as_float(u.y & 0xffff0000u);
-      } else {
-        const uint32_t u = *(const uint32_t*)((const int8_t*)pool + base);
-        const float s = f16_to_f32(spool[row]);
-        v0 = sext8(u, 0) * s; v1 = sext8(u, 1) * s; v2 = sext8(u, 2) * s; v3 = sext8(u, 3) * s;
-      }
-    }
-    float* dst = t_s + tl * ldk + i;
-    dst[0] = v0; dst[1] = v1; dst[2] = v2; dst[3] = v3;
-  }
-}
-
-template <int KVFMT>
-__global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
-  const Dims& d = a.d;
-  const int c = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
-  const int pos = a.desc->pos[b];
-  const int len = pos + 1;
-  const int t_begin = c * d.ct;
-  if (t_begin >= len) return;
-  const int t_end = min(len, t_begin + d.ct);
-  const int slot = a.desc->slot[b];
-  const int hd = d.hd, G = d.G, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int ldk = hd + 1;
-  const int32_t* btrow = a.bt + (size_t)slot * d.max_blocks;
-
+__global__ __launch_bounds__(256) void k_attn(AttnCtx a, const StepDesc* desc, float* partials) {
   extern __shared__ float sm[];
-  float* q_s = sm;                          // [G][hd], pre-scaled by 1/sqrt(hd)
-  float* t_s = q_s + G * hd;                // [64][hd+1]: K tile, then V tile
-  float* p_s = t_s + kAttnTile * ldk;       // [G][64]: scores, then probabilities
-  float* st_s = p_s + G * kAttnTile;        // [G][4]: running max, running sum, rescale
-  float* new_s = st_s + G * 4;              // [2][hd]: stored (decoded) new k, v
-  float* red = new_s + 2 * hd;              // [4] reduction scratch
-
-  const float scale = 1.0f / sqrtf((float)hd);
-  for (int e = tid; e < G * hd; e += 256)
-    q_s[e] = a.q[(size_t)b * d.q_dim + (size_t)j * G * hd + e] * scale;
-  for (int g = tid; g < G; g += 256) { st_s[g * 4] = -INFINITY; st_s[g * 4 + 1] = 0.f; }
-
-  if (pos >= t_begin && pos < t_end) {  // this item appends the new token of head j
-    const int blk = btrow[pos / d.bs], off = pos - (pos / d.bs) * d.bs;
-    const size_t row = ((size_t)blk * d.Hkv + j) * d.bs + off;
-    for (int which = 0; which < 2; which++) {
-      const float* src = (which ? a.vnew : a.knew) + (size_t)b * d.kv_dim + (size_t)j * hd;
-      void* pool = which ? a.kv.v : a.kv.k;
-      const float xv = tid < hd ? src[tid] : 0.f;
-      if constexpr (KVFMT == KV_F32) {
-        if (tid < hd) { ((float*)pool)[row * hd + tid] = xv; new_s[which * hd + tid] = xv; }
-      } else if constexpr (KVFMT == KV_BF16) {
-        if (tid < hd) {
-          const uint16_t bits = f32_to_bf16(xv);
-          ((uint16_t*)pool)[row * hd + tid] = bits;
-          new_s[which * hd + tid] = bf16_to_f32(bits);
-        }
-      } else {
-        const float amax = block_max256(fabsf(xv), red);
-        const uint16_t s16 = f32_to_f16(amax / 127.0f);
-        const float s = f16_to_f32(s16);
-        float qv = 0.f;
-        if (s != 0.f) qv = fminf(fmaxf(rintf(xv / s), -127.f), 127.f);
-        if (tid < hd) {
-          ((int8_t*)pool)[row * hd + tid] = (int8_t)qv;
-          new_s[which * hd + tid] = qv * s;
-        }
-        if (tid == 0) (which ? a.kv.vs : a.kv.ks)[row] = s16;
-      }
-    }
-  }
-  __syncthreads();
-
-  float acc[kMaxOutPerThread];
-#pragma unroll
-  for (int k = 0; k < kMaxOutPerThread; k++) acc[k] = 0.f;
-
-  for (int t0 = t_begin; t0 < t_end; t0 += kAttnTile) {
-    const int n = min(kAttnTile, t_end - t0);
-    stage_tile<KVFMT>(a, a.kv.k, a.kv.ks, btrow, j, t0, n, pos, new_s, t_s, ldk);
-    __syncthreads();
-    for (int sidx = tid; sidx < G * kAttnTile; sidx += 256) {
-      const int g = sidx / kAttnTile, tl = sidx - g * kAttnTile;
-      float s = -INFINITY;
-      if (tl < n) {
-        s = 0.f;
-        const float* qg = q_s + g * hd;
-        const float* kr = t_s + tl * ldk;
-        for (int i = 0; i < hd; i++) s += qg[i] * kr[i];
-      }
-      p_s[sidx] = s;
-    }
-    __syncthreads();
-    for (int g = wave; g < G; g += 4) {
-      const float s = p_s[g * kAttnTile + lane];
-      const float mt = wave_max(s);
-      const float mo = st_s[g * 4], lo = st_s[g * 4 + 1];
-      const float mn = fmaxf(mo, mt);
-      const float p = lane < n ? expf(s - mn) : 0.f;
-      const float ps = wave_sum(p);
-      p_s[g * kAttnTile + lane] = p;
-      if (lane == 0) {
-        const float al = expf(mo - mn);
-        st_s[g * 4] = mn;
-        st_s[g * 4 + 1] = lo * al + ps;
-        st_s[g * 4 + 2] = al;
-      }
-    }
-    __syncthreads();
-    stage_tile<KVFMT>(a, a.kv.v, a.kv.vs, btrow, j, t0, n, pos, new_s + hd, t_s, ldk);
-    __syncthreads();
-#pragma unroll
-    for (int k = 0; k < kMaxOutPerThread; k++) {
-      const int oi = tid + k * 256;
-      if (oi < G * hd) {
-        const int g = oi / hd, i = oi - g * hd;
-        const float* pg = p_s + g * kAttnTile;
-        float sum = 0.f;
-        for (int tl = 0; tl < n; tl++) sum += pg[tl] * t_s[tl * ldk + i];
-        acc[k] = acc[k] * st_s[g * 4 + 2] + sum;
-      }
-    }
-    __syncthreads();
-  }
-
-  const int c_stride = hd + 2;
-#pragma unroll
-  for (int k = 0; k < kMaxOutPerThread; k++) {
-    const int oi = tid + k * 256;
-    if (oi < G * hd) {
-      const int g = oi / hd, i = oi - g * hd, h = j * G + g;
-      a.partials[(((size_t)b * d.Hq + h) * d.nch + c) * c_stride + i] = acc[k];
-    }
-  }
-  for (int g = tid; g < G; g += 256) {
-    const int h = j * G + g;
-    float* P = a.partials + (((size_t)b * d.Hq + h) * d.nch + c) * c_stride;
-    P[hd] = st_s[g * 4];
-    P[hd + 1] = st_s[g * 4 + 1];
-  }
+  const int c = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
+  const int pos = desc->pos[b];
+  if (c * a.ct > pos) return;               // chunk beyond this sequence's length
+  const int G = a.d.G, hd = a.d.hd;
+  attn_item<KVFMT>(a, b, j, c, pos, desc->slot[b], desc->pos_block[b],
+                   a.q + (size_t)b * a.d.q_dim + (size_t)j * G * hd,
+                   a.knew + (size_t)b * a.d.kv_dim + (size_t)j * hd,
+                   a.vnew + (size_t)b * a.d.kv_dim + (size_t)j * hd, sm,
+                   [partials](size_t i, float v) { partials[i] = v; });
 }
 
-// merge the chunk partials of one (head, sequence): o = sum_c e^(m_c-M) acc_c / sum_c e^(m_c-M) l_c
+// one (head, sequence): o = merge of its chunk partials, rounded to the activation type
 __global__ __launch_bounds__(256) void k_combine(Dims d, const StepDesc* desc, const float* partials,
                                                  void* o) {
   const int h = blockIdx.x, b = blockIdx.y, i = threadIdx.x;
-  const int len = desc->pos[b] + 1;
-  const int nv = (len + d.ct - 1) / d.ct;
-  const int cs = d.hd + 2;
-  const float* P = partials + ((size_t)b * d.Hq + h) * d.nch * cs;
-  float M = -INFINITY;
-  for (int c = 0; c < nv; c++) M = fmaxf(M, P[c * cs + d.hd]);
-  float L = 0.f, acc = 0.f;
-  for (int c = 0; c < nv; c++) {
-    const float w = expf(P[c * cs + d.hd] - M);
-    L += w * P[c * cs + d.hd + 1];
-    if (i < d.hd) acc += w * P[c * cs + i];
-  }
-  if (i < d.hd) {
-    const float v = acc / L;
-    const size_t oi = (size_t)b * d.q_dim + (size_t)h * d.hd + i;
-    if (d.act == ACT_BF16) ((uint16_t*)o)[oi] = f32_to_bf16(v);
-    else ((float*)o)[oi] = v;
-  }
+  const int nv = (desc->pos[b] + d.ct) / d.ct;
+  const float* P = partials + ((size_t)b * d.Hq + h) * d.nch * (d.hd + 2);
+  if (i < d.hd) store_act(o, (size_t)b * d.q_dim + (size_t)h * d.hd + i, combine_one(P, nv, d.hd, i), d.act);
 }
 
 // S11 greedy argmax over the fp32 logits, lowest index among equal maxima
@@ -620,10 +369,6 @@ hipError_t gemv_epi(const GemvArgs& a, int epi, int NB, int ROWS, dim3 grid, siz
   }
 }
 
-size_t attn_smem_bytes(const Dims& d) {
-  return sizeof(float) * ((size_t)d.G * d.hd + (size_t)kAttnTile * (d.hd + 1) +
-                          (size_t)d.G * kAttnTile + (size_t)d.G * 4 + 2 * (size_t)d.hd + 4);
-}
 
 }  // namespace
 
@@ -668,20 +413,20 @@ hipError_t launch_gemv(const Dims& d, const MatDev& m, const void* xin, int B, i
 hipError_t launch_attention(const Dims& d, const StepDesc* desc, int B, const float* q,
                             const float* knew, const float* vnew, const KvLayer& kv,
                             const int32_t* block_table, float* partials, hipStream_t st) {
-  AttnArgs a;
+  AttnCtx a;
   a.d = d;
-  a.desc = desc;
   a.q = q;
   a.knew = knew;
   a.vnew = vnew;
   a.kv = kv;
   a.bt = block_table;
-  a.partials = partials;
+  a.ct = d.ct;
+  a.nch = d.nch;
   const dim3 grid(d.nch, d.Hkv, B);
-  const size_t smem = attn_smem_bytes(d);
-  if (d.kvfmt == KV_F32) hipLaunchKernelGGL(k_attn<KV_F32>, grid, dim3(256), smem, st, a);
-  else if (d.kvfmt == KV_BF16) hipLaunchKernelGGL(k_attn<KV_BF16>, grid, dim3(256), smem, st, a);
-  else hipLaunchKernelGGL(k_attn<KV_I8>, grid, dim3(256), smem, st, a);
+  const size_t smem = sizeof(float) * attn_smem_floats(d.G, d.hd);
+  if (d.kvfmt == KV_F32) hipLaunchKernelGGL(k_attn<KV_F32>, grid, dim3(256), smem, st, a, desc, partials);
+  else if (d.kvfmt == KV_BF16) hipLaunchKernelGGL(k_attn<KV_BF16>, grid, dim3(256), smem, st, a, desc, partials);
+  else hipLaunchKernelGGL(k_attn<KV_I8>, grid, dim3(256), smem, st, a, desc, partials);
   return hipGetLastError();
 }
 

@@ -23,7 +23,8 @@ DTD_OK, DTD_E_ARG, DTD_E_STATE, DTD_E_NOSEQ, DTD_E_CTX, DTD_E_KVFULL, DTD_E_OOM,
     DTD_E_UNSUPPORTED = 0, -1, -2, -3, -4, -5, -6, -7, -8
 STATUS_NAMES = {0: "DTD_OK", -1: "DTD_E_ARG", -2: "DTD_E_STATE", -3: "DTD_E_NOSEQ", -4: "DTD_E_CTX",
                 -5: "DTD_E_KVFULL", -6: "DTD_E_OOM", -7: "DTD_E_HIP", -8: "DTD_E_UNSUPPORTED"}
-KERNEL_GATE_UP, KERNEL_DOWN, KERNEL_QKV, KERNEL_O, KERNEL_ATTN, KERNEL_HEAD = range(6)
+KERNEL_GATE_UP, KERNEL_DOWN, KERNEL_QKV, KERNEL_O, KERNEL_ATTN, KERNEL_HEAD, KERNEL_STEP = range(7)
+PATH_AUTO, PATH_PER_KERNEL, PATH_PERSISTENT = 0, 1, 2
 
 
 class dtd_config(C.Structure):
@@ -75,6 +76,8 @@ _SIGS = {
     "dtd_debug_kernel_timing": ([_P, _I32, _I32, C.POINTER(C.c_double), C.POINTER(_I64)], _I32),
     "dtd_debug_decode_probe": ([_P, _I32, C.POINTER(_I64), _P, _P, _P, _P, _P], _I32),
     "dtd_debug_probe_record_bytes": ([C.POINTER(dtd_config), _I32], _I64),
+    "dtd_debug_set_path": ([_P, _I32], _I32),
+    "dtd_debug_uses_persistent": ([_P, _I32], _I32),
 }
 
 
@@ -82,6 +85,10 @@ def load(path: str = LIB_PATH):
     """Opens libdtd.so.  Raises FileNotFoundError if it has not been built."""
     global _lib
     if _lib is None:
+        # torch ships its own HIP runtime under the same soname; it has to be in the process
+        # first, so that the library binds to that one runtime (two runtimes in one process
+        # do not share devices or streams)
+        import torch  # noqa: F401
         if not os.path.exists(path):
             raise FileNotFoundError(f"{path} is missing: build it with __graft_entry__.build()")
         L = C.CDLL(path)
@@ -138,7 +145,7 @@ def dtd_create(cfg: dtd_config, stream: int):
     h = C.c_void_p()
     st = load().dtd_create(C.byref(cfg), C.c_void_p(stream), C.byref(h))
     if st != DTD_OK:
-        raise DtdError(st, "dtd_create failed")
+        raise DtdError(st, load().dtd_last_error(None).decode() or "dtd_create failed")
     return h
 
 
@@ -239,6 +246,14 @@ def dtd_debug_decode_probe(eng, seq_ids: Sequence[int], tokens_dev: int, inject_
     _check(eng, load().dtd_debug_decode_probe(
         eng, len(seq_ids), ids, C.c_void_p(tokens_dev), C.c_void_p(inject_dev),
         C.c_void_p(capture_dev), C.c_void_p(next_tokens_dev), C.c_void_p(logits_dev or None)))
+
+
+def dtd_debug_set_path(eng, path: int):
+    _check(eng, load().dtd_debug_set_path(eng, path))
+
+
+def dtd_debug_uses_persistent(eng, batch: int) -> bool:
+    return bool(load().dtd_debug_uses_persistent(eng, batch))
 
 
 def dtd_debug_kv_fill(eng, seq_id: int, length: int, seed: int):

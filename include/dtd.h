@@ -158,6 +158,9 @@ int32_t dtd_seq_len(const dtd_engine* e, int64_t seq_id);
 dtd_status dtd_check_device_errors(dtd_engine* e);
 
 void        dtd_destroy(dtd_engine* e);
+/* Message of the engine's last failed call.  With e == NULL: the message of this thread's
+ * last dtd_create if it failed, else "null engine".  The string is owned by the library
+ * and valid until the next call on the same engine (or thread, for e == NULL). */
 const char* dtd_last_error(const dtd_engine* e);
 
 /* ---- debug and measurement entry points (tests and benchmarks) -------------------- */
@@ -213,12 +216,22 @@ dtd_status dtd_debug_kv_read(dtd_engine* e, int64_t seq_id, int32_t layer, int32
 dtd_status dtd_debug_kv_fill(dtd_engine* e, int64_t seq_id, int32_t len, uint64_t seed);
 
 /* Kernel timing.  kind: 0 = the gate/up projection, 1 = the down projection, 2 = the
- * QKV projection, 3 = the output projection, 4 = attention, 5 = LM head.  While enabled,
+ * QKV projection, 3 = the output projection, 4 = attention, 5 = LM head (per-kernel
+ * schedule), 6 = the persistent step kernel (whole batch-1 step).  While enabled,
  * HIP events bracket every launch of that kernel on the engine's stream; *total_ms
  * and *count return the summed duration and number of launches since enabling and
  * reset them.  Synchronises the stream when reading. */
 dtd_status dtd_debug_kernel_timing(dtd_engine* e, int32_t kind, int32_t enable,
                                    double* total_ms, int64_t* count);
+
+/* Schedule selection.  path 0 (default): batch-1 steps run as one persistent kernel per
+ * step (every phase in one cooperative launch) when the device allows it, other batches
+ * and hidden-state capture as one kernel per sub-step; 1: always one kernel per sub-step;
+ * 2: persistent only (calls it cannot serve fail with DTD_E_UNSUPPORTED). */
+dtd_status dtd_debug_set_path(dtd_engine* e, int32_t path);
+
+/* 1 if a decode step of this batch size would run the persistent kernel now, else 0. */
+int32_t dtd_debug_uses_persistent(const dtd_engine* e, int32_t batch);
 
 #ifdef __cplusplus
 }

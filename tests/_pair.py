@@ -35,7 +35,7 @@ class Pair:
     """An engine and an oracle model holding the same weights."""
 
     def __init__(self, shape, *, max_ctx, max_seqs=1, max_batch=1, seed=11, weights=None,
-                 kv_block_size=16, kv_num_blocks=None):
+                 kv_block_size=16, kv_num_blocks=None, path=dtd.PATH_AUTO):
         import torch
         self.torch = torch
         self.shape = shape
@@ -43,6 +43,7 @@ class Pair:
         self.eng = dtd.Engine(shape, max_ctx=max_ctx, max_seqs=max_seqs, max_batch=max_batch,
                               kv_block_size=kv_block_size, kv_num_blocks=kv_num_blocks)
         self.eng.load_weights(synth.flat_tensors(self.w))
+        dtd.dtd_debug_set_path(self.eng.h, path)
         self.orc = oracle.Model(shape, self.w, max_ctx=max_ctx, max_seqs=max_seqs)
         self.dev = self.eng.device
         self.slot_of = {}

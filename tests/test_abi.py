@@ -89,3 +89,15 @@ def test_null_engine_calls_are_errors_not_crashes():
     assert lib.dtd_decode_step(None, 1, None, None, None, None) == dtd.DTD_E_ARG
     assert lib.dtd_last_error(None) == b"null engine"
     lib.dtd_destroy(None)
+
+
+def test_rejected_create_leaves_its_reason_for_last_error():
+    # the config is checked before any device call, so this runs without a GPU
+    lib = dtd.load()
+    bad = _cfg(n_kv_heads=3)
+    h = C.c_void_p(1)
+    assert lib.dtd_create(C.byref(bad), None, C.byref(h)) == dtd.DTD_E_ARG
+    assert not h.value
+    assert b"n_kv_heads 3" in lib.dtd_last_error(None)
+    with pytest.raises(dtd.DtdError, match="n_kv_heads 3"):
+        dtd.dtd_create(bad, 0)

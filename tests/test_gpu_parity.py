@@ -38,31 +38,52 @@ def _check_logits(tag, g_log, o_log, g_tok, o_tok):
 # the tiny configuration, end to end, free-running greedy
 # ---------------------------------------------------------------------------------------
 
-def test_tiny_config_end_to_end_identical_greedy_tokens():
+PATHS = [dtd.PATH_PERSISTENT, dtd.PATH_PER_KERNEL]
+PATH_IDS = ["persistent", "per-kernel"]
+
+
+@pytest.mark.parametrize("path", PATHS, ids=PATH_IDS)
+def test_tiny_config_end_to_end_identical_greedy_tokens(path):
     w = synth.TINY
     s = w.shape
-    P = Pair(s, max_ctx=w.context, seed=synth.weights_seed(w))
+    P = Pair(s, max_ctx=w.context, seed=synth.weights_seed(w), path=path)
+    assert dtd.dtd_debug_uses_persistent(P.eng.h, 1) == (path == dtd.PATH_PERSISTENT)
     prompt = synth.prompt_tokens(s.vocab, w.prompt_len)
     g_tok, g_log = P.gpu_prefill(0, prompt)
     o_tok, o_log = P.orc_prefill(0, prompt)
     _check_logits("prefill", g_log, o_log, g_tok, o_tok)
     toks_g, toks_o = [g_tok], [o_tok]
     worst_h = 0.0
+    capture = path == dtd.PATH_PER_KERNEL      # hidden-state capture runs the per-kernel schedule
     for step in range(w.context - w.prompt_len):
         pos = w.prompt_len + step
-        ng, lg, hid = P.gpu_step([0], [toks_g[-1]], capture=True)
+        ng, lg, hid = P.gpu_step([0], [toks_g[-1]], capture=capture)
         no, lo, ho = P.orc_step(0, toks_o[-1], pos, hidden=True)
-        for layer in range(s.n_layers + 1):
-            e = normwise(hid[layer, 0], ho[layer])
-            worst_h = max(worst_h, e)
-            assert e <= TOL, f"step {step} layer {layer} hidden error {e:.3e}"
+        if capture:
+            for layer in range(s.n_layers + 1):
+                e = normwise(hid[layer, 0], ho[layer])
+                worst_h = max(worst_h, e)
+                assert e <= TOL, f"step {step} layer {layer} hidden error {e:.3e}"
         _check_logits(f"step {step}", lg[0], lo, int(ng[0]), no)
         toks_g.append(int(ng[0]))
         toks_o.append(no)
-    _say(f"tiny: tokens {toks_g}, worst hidden err {worst_h:.2e}")
+    _say(f"tiny ({PATH_IDS[PATHS.index(path)]}): tokens {toks_g}, worst hidden err {worst_h:.2e}")
     assert toks_g == toks_o
     assert len(toks_g) == 33
     P.close()
+
+
+def test_persistent_and_per_kernel_schedules_agree():
+    s = _GRID.replace(act=synth.ACT_BF16, kvfmt=synth.KV_BF16)
+    A = Pair(s, max_ctx=64, seed=6, path=dtd.PATH_PERSISTENT)
+    B = Pair(s, max_ctx=64, seed=6, weights=A.w, path=dtd.PATH_PER_KERNEL)
+    prompt = synth.prompt_tokens(s.vocab, 24, seed=2)
+    _, la = A.gpu_prefill(0, prompt)
+    _, lb = B.gpu_prefill(0, prompt)
+    assert normwise(la, lb) <= TOL
+    assert dtd.dtd_debug_uses_persistent(A.eng.h, 1) and not dtd.dtd_debug_uses_persistent(A.eng.h, 2)
+    A.close()
+    B.close()
 
 
 # ---------------------------------------------------------------------------------------
@@ -115,10 +136,11 @@ def teacher_forced(P, gpu_ids, orc_ids, toks, poss, tag):
     return probe_step(P, gpu_ids, orc_ids, toks, poss, tag)
 
 
+@pytest.mark.parametrize("path", PATHS, ids=PATH_IDS)
 @pytest.mark.parametrize("kw", _FORMATS, ids=lambda kw: "-".join(f"{k}={v}" for k, v in kw.items()) or "base")
-def test_formats(kw):
+def test_formats(kw, path):
     s = _GRID.replace(**kw)
-    P = Pair(s, max_ctx=96, max_seqs=2, seed=21)
+    P = Pair(s, max_ctx=96, max_seqs=2, seed=21, path=path)
     O2 = P.perturbed_oracle(1, max_ctx=96)
     prompt = synth.prompt_tokens(s.vocab, 70, seed=3)
     tr = Tracker()
@@ -131,7 +153,7 @@ def test_formats(kw):
     tr.add(g_log, outs[0][1], O2.step(0, int(prompt[-1]), 69)[1])
     tok = outs[0][0]
     for step in range(8):
-        ng, lg, hid = P.gpu_step([1], [tok], capture=True)
+        ng, lg, _ = P.gpu_step([1], [tok])
         outs = teacher_forced(P, [0], [0], [tok], [70 + step], f"step {step}")
         o2 = O2.step(0, tok, 70 + step)
         tr.add(lg[0], outs[0][1], o2[1])
