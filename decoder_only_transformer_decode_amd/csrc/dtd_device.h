@@ -12,6 +12,36 @@ namespace dtd {
 namespace dev {
 
 // ---------------------------------------------------------------------------------------
+// global-memory access through pointers the compiler cannot prove global (read from a table
+// or a struct): without the address-space cast it emits FLAT instructions, which count
+// against the LDS counter too, so every later LDS access would wait for them, in-flight
+// weight prefetches included
+// ---------------------------------------------------------------------------------------
+
+typedef unsigned int gv4u __attribute__((ext_vector_type(4)));
+typedef unsigned int gv2u __attribute__((ext_vector_type(2)));
+
+// 8- and 16-byte types load through native vectors: a copy of HIP's vector structs is
+// split into 32-bit pieces that lose the address space
+template <typename T>
+__device__ __forceinline__ T gload(const void* p) {
+  if constexpr (sizeof(T) == 16) {
+    const gv4u v = *(const __attribute__((address_space(1))) gv4u*)p;
+    return __builtin_bit_cast(T, v);
+  } else if constexpr (sizeof(T) == 8) {
+    const gv2u v = *(const __attribute__((address_space(1))) gv2u*)p;
+    return __builtin_bit_cast(T, v);
+  } else {
+    return *(const __attribute__((address_space(1))) T*)p;
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ void gstore(void* p, T v) {
+  *(__attribute__((address_space(1))) T*)p = v;
+}
+
+// ---------------------------------------------------------------------------------------
 // number formats
 // ---------------------------------------------------------------------------------------
 
@@ -143,24 +173,59 @@ __device__ __forceinline__ void stage_tile(const Dims& d, const void* pool, cons
     if (t == pos) {
       v0 = newv[i]; v1 = newv[i + 1]; v2 = newv[i + 2]; v3 = newv[i + 3];
     } else {
-      const int blk = btrow[t / d.bs], off = t - (t / d.bs) * d.bs;
+      const int blk = gload<int32_t>(btrow + t / d.bs), off = t - (t / d.bs) * d.bs;
       const size_t row = ((size_t)blk * d.Hkv + j) * d.bs + off;
       const size_t base = row * hd + i;
       if constexpr (KVFMT == KV_F32) {
-        const float4 f = *(const float4*)((const float*)pool + base);
+        const float4 f = gload<float4>((const float*)pool + base);
         v0 = f.x; v1 = f.y; v2 = f.z; v3 = f.w;
       } else if constexpr (KVFMT == KV_BF16) {
-        const uint2 u = *(const uint2*)((const uint16_t*)pool + base);
+        const uint2 u = gload<uint2>((const uint16_t*)pool + base);
         v0 = __uint_as_float(u.x << 16); v1 = __uint_as_float(u.x & 0xffff0000u);
         v2 = __uint_as_float(u.y << 16); v3 = __uint_as_float(u.y & 0xffff0000u);
       } else {
-        const uint32_t u = *(const uint32_t*)((const int8_t*)pool + base);
-        const float s = f16_to_f32(spool[row]);
+        const uint32_t u = gload<uint32_t>((const int8_t*)pool + base);
+        const float s = f16_to_f32(gload<uint16_t>(spool + row));
         v0 = sext8(u, 0) * s; v1 = sext8(u, 1) * s; v2 = sext8(u, 2) * s; v3 = sext8(u, 3) * s;
       }
     }
     float* dst = t_s + tl * ldk + i;
     dst[0] = v0; dst[1] = v1; dst[2] = v2; dst[3] = v3;
+  }
+}
+
+// Rounds the new position's key and value (kn, vn: hd fp32 each) to the KV encoding,
+// writes them to pool row `row` of kv head j's layout, and leaves the stored (decoded)
+// values in new_s [2][hd].  All threads of the block must call this: the int8 scale is a
+// block-wide max.  red: reduction scratch (>= one float per wave).
+template <int KVFMT>
+__device__ __forceinline__ void kv_append(const KvLayer& kv, size_t row, int hd, const float* kn, const float* vn,
+                                          float* new_s, float* red) {
+  const int tid = threadIdx.x;
+  for (int which = 0; which < 2; which++) {
+    const float* src = which ? vn : kn;
+    void* pool = which ? kv.v : kv.k;
+    const float xv = tid < hd ? src[tid] : 0.f;
+    if constexpr (KVFMT == KV_F32) {
+      if (tid < hd) { gstore<float>((float*)pool + row * hd + tid, xv); new_s[which * hd + tid] = xv; }
+    } else if constexpr (KVFMT == KV_BF16) {
+      if (tid < hd) {
+        const uint16_t bits = f32_to_bf16(xv);
+        gstore<uint16_t>((uint16_t*)pool + row * hd + tid, bits);
+        new_s[which * hd + tid] = bf16_to_f32(bits);
+      }
+    } else {
+      const float amax = block_max(fabsf(xv), red);
+      const uint16_t s16 = f32_to_f16(amax / 127.0f);
+      const float s = f16_to_f32(s16);
+      float qv = 0.f;
+      if (s != 0.f) qv = fminf(fmaxf(rintf(xv / s), -127.f), 127.f);
+      if (tid < hd) {
+        gstore<int8_t>((int8_t*)pool + row * hd + tid, (int8_t)qv);
+        new_s[which * hd + tid] = qv * s;
+      }
+      if (tid == 0) gstore<uint16_t>((which ? kv.vs : kv.ks) + row, s16);
+    }
   }
 }
 
@@ -195,32 +260,7 @@ __device__ __forceinline__ void attn_item(const AttnCtx& a, int b, int j, int c,
 
   if (pos >= t_begin && pos < t_end) {  // this item appends the new token of head j
     const int off = pos - (pos / d.bs) * d.bs;
-    const size_t row = ((size_t)pos_blk * d.Hkv + j) * d.bs + off;
-    for (int which = 0; which < 2; which++) {
-      const float* src = which ? vn : kn;
-      void* pool = which ? a.kv.v : a.kv.k;
-      const float xv = tid < hd ? src[tid] : 0.f;
-      if constexpr (KVFMT == KV_F32) {
-        if (tid < hd) { ((float*)pool)[row * hd + tid] = xv; new_s[which * hd + tid] = xv; }
-      } else if constexpr (KVFMT == KV_BF16) {
-        if (tid < hd) {
-          const uint16_t bits = f32_to_bf16(xv);
-          ((uint16_t*)pool)[row * hd + tid] = bits;
-          new_s[which * hd + tid] = bf16_to_f32(bits);
-        }
-      } else {
-        const float amax = block_max(fabsf(xv), red);
-        const uint16_t s16 = f32_to_f16(amax / 127.0f);
-        const float s = f16_to_f32(s16);
-        float qv = 0.f;
-        if (s != 0.f) qv = fminf(fmaxf(rintf(xv / s), -127.f), 127.f);
-        if (tid < hd) {
-          ((int8_t*)pool)[row * hd + tid] = (int8_t)qv;
-          new_s[which * hd + tid] = qv * s;
-        }
-        if (tid == 0) (which ? a.kv.vs : a.kv.ks)[row] = s16;
-      }
-    }
+    kv_append<KVFMT>(a.kv, ((size_t)pos_blk * d.Hkv + j) * d.bs + off, hd, kn, vn, new_s, red);
   }
   __syncthreads();
 

@@ -373,8 +373,9 @@ extern "C" dtd_status dtd_create(const dtd_config* cfg, void* hip_stream, dtd_en
         hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, e->device) != hipSuccess)
       return cleanup(DTD_E_HIP);
     e->p_nch = (cfg->max_ctx + kAttnTile - 1) / kAttnTile;
-    e->p_smem = persistent_smem_bytes(d, e->p_nch);
-    if (coop && cus > 0 && persistent_prepare(d, e->p_smem, &per_cu) == hipSuccess && per_cu >= 1) {
+    e->p_smem = persistent_smem_bytes(d, e->p_nch, cus > 0 ? cus : 1);
+    if (coop && cus > 0 && persistent_supports(d) && persistent_prepare(d, e->p_smem, &per_cu) == hipSuccess &&
+        per_cu >= 1) {
       e->persist_ok = true;
       e->nwg = cus;
     }

@@ -128,9 +128,10 @@ struct PersistArgs {
 };
 
 // ---- launchers (dtd_kernels.hip, dtd_persistent.hip) ----
-size_t persistent_smem_bytes(const Dims& d, int nch);
+size_t persistent_smem_bytes(const Dims& d, int nch, int nwg);
 size_t persistent_xs_floats(const Dims& d, int nch);
 int persistent_tags_per_step(const Dims& d);
+bool persistent_supports(const Dims& d);   // shapes the persistent step kernel handles
 hipError_t persistent_prepare(const Dims& d, size_t smem, int* blocks_per_cu);
 hipError_t launch_persistent(const PersistArgs& a, int nwg, size_t smem, hipStream_t st);
 hipError_t launch_embed(const Dims& d, const MatDev& emb, const StepDesc* desc, int B,

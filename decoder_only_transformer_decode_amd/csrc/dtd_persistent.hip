@@ -40,7 +40,7 @@ using namespace dev;
 
 constexpr int PW = kPersistWaves;   // waves per workgroup
 constexpr int PT = PW * 64;         // threads per workgroup
-constexpr int GRP = 8;              // lines per lane in one prefetch group
+constexpr int GRP = 4;              // lines per lane in one prefetch group
 constexpr unsigned kSpinLimit = 1u << 20;
 
 // tags of one layer's hand-offs: tag = epoch + layer * kTagsPerLayer + kind; the head's
@@ -57,9 +57,19 @@ __device__ uint64_t g_phase_trace[kTraceWG * kTraceEv];
     if (threadIdx.x == 0 && blockIdx.x < kTraceWG && (ev) < kTraceEv)                       \
       g_phase_trace[blockIdx.x * kTraceEv + (ev)] = __builtin_amdgcn_s_memrealtime();       \
   } while (0)
+// timestamps inside a streaming loop go to LDS first (a global store there would make the
+// compiler drain all loads in flight at every later wait)
+__shared__ unsigned long long g_trace_lds[16];
+#define PTRACE_LDS(k)                                                                      \
+  do {                                                                                     \
+    if (threadIdx.x == 0 && (k) < 16) g_trace_lds[(k)] = __builtin_amdgcn_s_memrealtime();   \
+  } while (0)
 #else
 #define PTRACE(ev) \
   do {             \
+  } while (0)
+#define PTRACE_LDS(k) \
+  do {                \
   } while (0)
 #endif
 
@@ -70,19 +80,21 @@ template <> struct PVec<W_BF16> { static constexpr int VEC = 8; };
 // tagged words
 // ---------------------------------------------------------------------------------------
 
+typedef __attribute__((address_space(1))) uint64_t gword;
+
 __device__ __forceinline__ void put_tag(uint64_t* p, uint32_t tag, float v) {
-  __hip_atomic_store(p, ((uint64_t)tag << 32) | __float_as_uint(v), __ATOMIC_RELAXED,
+  __hip_atomic_store((gword*)p, ((uint64_t)tag << 32) | __float_as_uint(v), __ATOMIC_RELAXED,
                      __HIP_MEMORY_SCOPE_AGENT);
 }
 
 __device__ __forceinline__ uint64_t get_word(const uint64_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return __hip_atomic_load((gword*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Re-polls p until it carries tag.  Gives up (raising kErrBarrier and the workgroup's LDS
 // fail flag) after kSpinLimit polls, or as soon as another thread or workgroup has given up,
 // so every wait ends.
-__device__ __noinline__ float wait_slow(const uint64_t* p, uint32_t tag, int32_t* err, int* fail) {
+__device__ __forceinline__ float wait_slow(const uint64_t* p, uint32_t tag, int32_t* err, int* fail) {
   unsigned spins = 0;
   for (;;) {
     if (*(volatile int*)fail) return 0.f;
@@ -149,6 +161,7 @@ struct PPhase {
   int K;     // elements per row
   int cpr;   // 1 KB lines per row
   int p0;    // first row pair owned by this workgroup
+  int ps;    // stride between the row pairs it owns
   int np;    // row pairs owned by this workgroup
 };
 
@@ -161,52 +174,81 @@ __device__ __forceinline__ PPhase make_phase(const MatDev& m, int g, int nwg) {
   p.K = m.cols;
   p.Kb = m.cols * (WFMT == W_BF16 ? 2 : 1);
   p.cpr = (p.Kb + 1023) >> 10;
+  // Row pairs are dealt out round-robin (workgroup g owns pairs g, g + nwg, ...), not in one
+  // contiguous slice per workgroup: every hand-off lines all workgroups up at the start of a
+  // projection, and with contiguous slices they would then all read the same offset of
+  // slices a fixed stride apart, which piles the requests onto a few HBM channels; dealt
+  // out, they read neighbouring rows of one region.
   const int pairs = (m.rows + 1) >> 1;
-  p.p0 = (int)((long long)pairs * g / nwg);
-  p.np = (int)((long long)pairs * (g + 1) / nwg) - p.p0;
+  p.p0 = g;
+  p.ps = nwg;
+  p.np = g < pairs ? (pairs - 1 - g) / nwg + 1 : 0;
   return p;
 }
 
-__device__ __forceinline__ PPhase empty_phase() {
+// a phase with no rows; its (unused) loads read `any`, a readable global address
+__device__ __forceinline__ PPhase empty_phase(const void* any) {
   PPhase p{};
   p.cpr = 1;
+  p.ps = 1;
+  p.w = p.s = (const uint8_t*)any;
   return p;
 }
+
+// this thread's wave, as a value the compiler knows is wave-uniform (branches on it become
+// scalar branches, and both arms of an if/else are never laid out as one masked sequence)
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
 // pairs of this wave in the phase
 __device__ __forceinline__ int wave_pairs(const PPhase& p, int wave) {
   return p.np > wave ? (p.np - wave + PW - 1) / PW : 0;
 }
 
-// Issues the loads of lines [c0, c0 + GRP) of this wave's stream in phase p.
+// The weight stream's loads are issued so that the compiler's wait insertion can count
+// them exactly: every group issues the same loads unconditionally, each buffer has one
+// issue site per loop, and branches depend only on wave-uniform values.  Otherwise it
+// falls back to a full drain (vmcnt(0)) before each group, leaving one group in flight
+// per wave instead of two.
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+
+template <int WFMT> struct Grp {
+  static constexpr int SC = WFMT == W_BF16 ? 0 : GRP;   // scale loads per group
+};
+
+struct WBuf {
+  v4u w[GRP];
+  uint32_t sc[GRP];   // Q8_0: fp16 block scale bits; int8-row: fp32 row scale bits
+};
+
+// Issues the loads of lines [c0, c0 + GRP) of this wave's stream in phase p, with their
+// scales (Q8_0: the line's block scale; int8-row: the row scale).  Every call issues the
+// same loads whatever the phase: a line (or a lane's part of one) outside the matrix reads
+// offset 0 of the matrix instead, and its value is never used (whole lines are skipped by
+// the consumer; a lane's part past the row end meets the input vector's zero padding).
+// Addresses are a uniform base plus a 32-bit offset (a matrix is below 4 GiB).
 template <int WFMT>
-__device__ __forceinline__ void issue_group(const PPhase& p, int c0, uint4 (&buf)[GRP], float (&sc)[GRP]) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+__device__ __forceinline__ void issue_group(const PPhase& p, int c0, WBuf& b) {
+  const int wave = wave_id(), lane = threadIdx.x & 63;
   const int total = wave_pairs(p, wave) * 2 * p.cpr;
-  int k = 0, rs = 0, j = 0;
-  if (c0 < total) {
-    const int per = 2 * p.cpr;
-    k = c0 / per;
-    const int rem = c0 - k * per;
-    rs = rem >= p.cpr;
-    j = rem - rs * p.cpr;
-  }
+  const int per = 2 * p.cpr;
+  int k = c0 / per;
+  const int rem = c0 - k * per;
+  int rs = rem >= p.cpr;
+  int j = rem - rs * p.cpr;
 #pragma unroll
   for (int s = 0; s < GRP; s++) {
-    buf[s] = make_uint4(0u, 0u, 0u, 0u);
-    sc[s] = 0.f;
-    if (c0 + s < total) {
-      const int row = 2 * (p.p0 + wave + PW * k) + rs;
-      const int cb = (j * 64 + lane) * 16;
-      if (row < p.N && cb < p.Kb) {
-        buf[s] = *(const uint4*)(p.w + (size_t)row * p.Kb + cb);
-        if constexpr (WFMT == W_Q8_0)
-          sc[s] = f16_to_f32(*(const uint16_t*)(p.s + ((size_t)row * (p.K >> 5) + (cb >> 5)) * 2));
-      }
-      if (++j == p.cpr) {
-        j = 0;
-        if (++rs == 2) { rs = 0; ++k; }
-      }
+    const int row = 2 * (p.p0 + p.ps * (wave + PW * k)) + rs;
+    const int cb = (j * 64 + lane) * 16;
+    const bool rok = c0 + s < total && row < p.N;
+    const bool ok = rok && cb < p.Kb;
+    b.w[s] = gload<v4u>(p.w + (ok ? (uint32_t)row * (uint32_t)p.Kb + (uint32_t)cb : 0u));
+    if constexpr (WFMT == W_Q8_0)
+      b.sc[s] = gload<uint16_t>(p.s + (ok ? ((uint32_t)row * (uint32_t)(p.K >> 5) + (uint32_t)(cb >> 5)) * 2u : 0u));
+    else if constexpr (WFMT == W_INT8_ROW)
+      b.sc[s] = gload<uint32_t>(p.s + (rok ? (uint32_t)row * 4u : 0u));
+    if (++j == p.cpr) {
+      j = 0;
+      if (++rs == 2) { rs = 0; ++k; }
     }
   }
 }
@@ -222,9 +264,7 @@ struct PEpi {
   float* cq;
   float* ck;
   float* cv;
-  int pos;
-  const float* rope_cos;
-  const float* rope_sin;
+  const float* rope;   // LDS: cos | sin of this step's position, hd/2 each
   // residual: out[r] = xf[r] + value
   const float* xf;
   uint64_t* tout;
@@ -235,7 +275,7 @@ struct PEpi {
   // logits
   float* logits;
   float* logits_out;
-  float best;     // running argmax (lane 0)
+  float best;     // this thread's argmax over its rows
   int best_idx;
 };
 
@@ -244,109 +284,172 @@ __device__ __forceinline__ void emit(uint64_t* t, float* c, uint32_t tag, int i,
   put_tag(t + i, tag, v);
 }
 
-template <int WFMT, int EPI>
-__device__ __forceinline__ void pair_epilogue(const Dims& d, const PPhase& p, int pair, float v0, float v1,
-                                              PEpi& e) {
-  const int r0 = 2 * pair, r1 = r0 + 1;
-  if constexpr (WFMT == W_INT8_ROW) {  // per-row scale after the dot
-    v0 *= ((const float*)p.s)[r0];
-    if (r1 < p.N) v1 *= ((const float*)p.s)[r1];
-  }
+// The epilogue of one projection, run by the whole workgroup after its rows are done: the
+// finished dot products of its row pairs are in ores (LDS; local pair t, i.e. global pair
+// p.p0 + p.ps*t, at ores[2t], ores[2t+1]).
+// Stores happen only here, never inside the streaming loop: gfx950 counts loads and stores
+// on one counter, so a store pending there would make every wait for a weight group also
+// wait for the store's acknowledgement and for the group issued after it.
+template <int EPI>
+__device__ __forceinline__ void phase_epilogue(const Dims& d, const PPhase& p, const float* ores, PEpi& e) {
   if constexpr (EPI == EPI_QKV) {
     // stored QKV rows: q and k heads hold the RoPE pairs (i, i + hd/2) as rows (2i, 2i+1)
     const int half = d.hd >> 1;
-    if (r0 < d.q_dim + d.kv_dim) {
-      const bool isq = r0 < d.q_dim;
-      const int nn = isq ? r0 : r0 - d.q_dim;
-      const int h = nn / d.hd, i = (nn - h * d.hd) >> 1;
-      const float c = e.rope_cos[(size_t)e.pos * half + i];
-      const float s = e.rope_sin[(size_t)e.pos * half + i];
-      uint64_t* t = isq ? e.tq : e.tk;
-      float* cp = isq ? e.cq : e.ck;
-      emit(t, cp, e.tag, h * d.hd + i, v0 * c - v1 * s);
-      emit(t, cp, e.tag, h * d.hd + i + half, v0 * s + v1 * c);
-    } else {
-      const int nn = r0 - d.q_dim - d.kv_dim;
-      emit(e.tv, e.cv, e.tag, nn, v0);
-      emit(e.tv, e.cv, e.tag, nn + 1, v1);
+    for (int t = threadIdx.x; t < p.np; t += PT) {
+      const int r = 2 * (p.p0 + p.ps * t);
+      const float v0 = ores[2 * t], v1 = ores[2 * t + 1];
+      if (r < d.q_dim + d.kv_dim) {
+        const bool isq = r < d.q_dim;
+        const int nn = isq ? r : r - d.q_dim;
+        const int h = nn / d.hd, i = (nn - h * d.hd) >> 1;
+        const float c = e.rope[i], sn = e.rope[half + i];
+        uint64_t* tt = isq ? e.tq : e.tk;
+        float* cp = isq ? e.cq : e.ck;
+        emit(tt, cp, e.tag, h * d.hd + i, v0 * c - v1 * sn);
+        emit(tt, cp, e.tag, h * d.hd + i + half, v0 * sn + v1 * c);
+      } else {
+        const int nn = r - d.q_dim - d.kv_dim;
+        emit(e.tv, e.cv, e.tag, nn, v0);
+        emit(e.tv, e.cv, e.tag, nn + 1, v1);
+      }
     }
   } else if constexpr (EPI == EPI_RESID) {
-    emit(e.tout, e.cout, e.tag, r0, e.xf[r0] + v0);
-    if (r1 < p.N) emit(e.tout, e.cout, e.tag, r1, e.xf[r1] + v1);
+    for (int u = threadIdx.x; u < 2 * p.np; u += PT) {
+      const int r = 2 * (p.p0 + p.ps * (u >> 1)) + (u & 1);
+      if (r < p.N) emit(e.tout, e.cout, e.tag, r, e.xf[r] + ores[u]);
+    }
   } else if constexpr (EPI == EPI_SWIGLU) {
-    const float hv = v0 / (1.0f + expf(-v0)) * v1;   // rows (2f, 2f+1) = (gate f, up f)
-    if (e.ch) store_act(e.ch, pair, hv, d.act);
-    put_tag(e.th + pair, e.tag, round_act(hv, d.act));
+    for (int t = threadIdx.x; t < p.np; t += PT) {   // rows (2f, 2f+1) = (gate f, up f)
+      const int f = p.p0 + p.ps * t;
+      const float v0 = ores[2 * t], v1 = ores[2 * t + 1];
+      const float hv = v0 / (1.0f + expf(-v0)) * v1;
+      if (e.ch) store_act(e.ch, f, hv, d.act);
+      put_tag(e.th + f, e.tag, round_act(hv, d.act));
+    }
   } else {
-    e.logits[r0] = v0;
-    if (e.logits_out) e.logits_out[r0] = v0;
-    if (v0 > e.best || (e.best_idx == INT_MAX && !isnan(v0))) { e.best = v0; e.best_idx = r0; }
-    if (r1 < p.N) {
-      e.logits[r1] = v1;
-      if (e.logits_out) e.logits_out[r1] = v1;
-      if (v1 > e.best) { e.best = v1; e.best_idx = r1; }
+    for (int u = threadIdx.x; u < 2 * p.np; u += PT) {   // rows visited in increasing order
+      const int r = 2 * (p.p0 + p.ps * (u >> 1)) + (u & 1);
+      if (r >= p.N) continue;
+      const float v = ores[u];
+      gstore<float>(e.logits + r, v);
+      if (e.logits_out) gstore<float>(e.logits_out + r, v);
+      if (v > e.best || (e.best_idx == INT_MAX && !isnan(v))) { e.best = v; e.best_idx = r; }
     }
   }
 }
 
-// Streams this wave's rows of phase p against the input vector in LDS (xs).  On entry pre
-// holds this phase's first group (already issued); on exit it holds the first group of
-// phase nx, issued before returning and still in flight.
-template <int WFMT, int EPI>
-__device__ __forceinline__ void gemv_phase(const Dims& d, const PPhase& p, const PPhase& nx, uint4 (&pre)[GRP],
-                                           float (&psc)[GRP], const float* xs, PEpi& e) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int total = wave_pairs(p, wave) * 2 * p.cpr;
-  const float4* x4 = (const float4*)xs;
-  uint4 cur[GRP];
-  float csc[GRP];
+// consume cursor of one wave's stream: position (pair k of the wave, row rs of the pair,
+// line j of the row) and the running dot products of the pair's two rows
+struct Cursor {
+  int k, rs, j;
+  float acc0, acc1;
+  float rsc0, rsc1;   // int8-row: scales of the pair's rows
+  float rsc_line;     // int8-row: scale carried by the last real line
+};
+
+// Multiplies lines [c0, c0 + GRP) of buffer b against the input vector; a finished pair's
+// dot products go to ores (LDS, local pair index).  Every line's registers are read
+// whether or not the line is real (a pad line's product is discarded by a select): a load
+// whose value is never read is still pending when its register is reissued, and the
+// compiler then waits for every load in flight, not just that one.
+template <int WFMT>
+__device__ __forceinline__ void consume_group(const PPhase& p, int c0, int total, const WBuf& b, const float4* x4,
+                                              Cursor& cu, float* ores) {
+  const int wave = wave_id(), lane = threadIdx.x & 63;
 #pragma unroll
-  for (int s = 0; s < GRP; s++) { cur[s] = pre[s]; csc[s] = psc[s]; }
-  float acc0 = 0.f, acc1 = 0.f;
-  int k = 0, rs = 0, j = 0;   // consume cursor
-  for (int c0 = 0; c0 < total || c0 == 0; c0 += GRP) {
-    if (c0 + GRP < total) issue_group<WFMT>(p, c0 + GRP, pre, psc);
-    else issue_group<WFMT>(nx, 0, pre, psc);   // first group of the next phase
+  for (int s = 0; s < GRP; s++) {
+    const bool valid = c0 + s < total;   // wave-uniform
+    const v4u v = b.w[s];
+    const int j = cu.j;
+    float part = 0.f;
+    if constexpr (WFMT == W_BF16) {
+      const float4 xa = x4[(j * 2 + 0) * 64 + lane], xb = x4[(j * 2 + 1) * 64 + lane];
+      part = __uint_as_float(v.x << 16) * xa.x + __uint_as_float(v.x & 0xffff0000u) * xa.y +
+             __uint_as_float(v.y << 16) * xa.z + __uint_as_float(v.y & 0xffff0000u) * xa.w +
+             __uint_as_float(v.z << 16) * xb.x + __uint_as_float(v.z & 0xffff0000u) * xb.y +
+             __uint_as_float(v.w << 16) * xb.z + __uint_as_float(v.w & 0xffff0000u) * xb.w;
+    } else {
+      const uint32_t u[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-    for (int s = 0; s < GRP; s++) {
-      if (c0 + s < total) {
-        const uint4 w = cur[s];
-        float part = 0.f;
-        if constexpr (WFMT == W_BF16) {
-          const float4 xa = x4[(j * 2 + 0) * 64 + lane], xb = x4[(j * 2 + 1) * 64 + lane];
-          part = __uint_as_float(w.x << 16) * xa.x + __uint_as_float(w.x & 0xffff0000u) * xa.y +
-                 __uint_as_float(w.y << 16) * xa.z + __uint_as_float(w.y & 0xffff0000u) * xa.w +
-                 __uint_as_float(w.z << 16) * xb.x + __uint_as_float(w.z & 0xffff0000u) * xb.y +
-                 __uint_as_float(w.w << 16) * xb.z + __uint_as_float(w.w & 0xffff0000u) * xb.w;
-        } else {
-          const uint32_t u[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-          for (int q = 0; q < 4; q++) {
-            const float4 xv = x4[(j * 4 + q) * 64 + lane];
-            part += sext8(u[q], 0) * xv.x + sext8(u[q], 1) * xv.y + sext8(u[q], 2) * xv.z +
-                    sext8(u[q], 3) * xv.w;
-          }
-          if constexpr (WFMT == W_Q8_0) part *= csc[s];
+      for (int q = 0; q < 4; q++) {
+        const float4 xv = x4[(j * 4 + q) * 64 + lane];
+        part += sext8(u[q], 0) * xv.x + sext8(u[q], 1) * xv.y + sext8(u[q], 2) * xv.z + sext8(u[q], 3) * xv.w;
+      }
+      if constexpr (WFMT == W_Q8_0) part *= f16_to_f32((uint16_t)b.sc[s]);
+    }
+    if constexpr (WFMT == W_INT8_ROW) {   // every line of a row carries the row's scale
+      const float scl = __uint_as_float(b.sc[s]);
+      cu.rsc_line = valid ? scl : cu.rsc_line;
+    }
+    part = valid ? part : 0.f;
+    if (cu.rs) cu.acc1 += part;
+    else cu.acc0 += part;
+    if (valid && ++cu.j == p.cpr) {
+      if constexpr (WFMT == W_INT8_ROW) {
+        if (cu.rs) cu.rsc1 = cu.rsc_line;
+        else cu.rsc0 = cu.rsc_line;
+      }
+      cu.j = 0;
+      if (++cu.rs == 2) {
+        cu.rs = 0;
+        // int8-row: per-row scale after the dot
+        const float v0 = wave_sum(cu.acc0) * cu.rsc0, v1 = wave_sum(cu.acc1) * cu.rsc1;
+        cu.acc0 = cu.acc1 = 0.f;
+        if (lane == 0) {
+          const int lp = wave + PW * cu.k;   // pair index within this workgroup's range
+          ores[2 * lp] = v0;
+          ores[2 * lp + 1] = v1;
         }
-        if (rs) acc1 += part;
-        else acc0 += part;
-        if (++j == p.cpr) {
-          j = 0;
-          if (++rs == 2) {
-            rs = 0;
-            const float v0 = wave_sum(acc0), v1 = wave_sum(acc1);
-            acc0 = acc1 = 0.f;
-            if (lane == 0) pair_epilogue<WFMT, EPI>(d, p, p.p0 + wave + PW * k, v0, v1, e);
-            ++k;
-          }
-        }
+        ++cu.k;
       }
     }
-    // after the last group, pre holds the next phase's loads still in flight: copying them
-    // here would wait for them, so they are left for the next phase to pick up
-    if (c0 + GRP >= total) break;
-#pragma unroll
-    for (int s = 0; s < GRP; s++) { cur[s] = pre[s]; csc[s] = psc[s]; }
+  }
+}
+
+// Issues group gidx of the sequence "groups 0..ng2-1 of p, then groups of nx": the phase is
+// picked by uniform selects, so each buffer has exactly one issue site in the loop below
+// (two sites would be free to use different registers for the same in-flight group, and a
+// copy at the join would read registers that a load has yet to write).
+template <int WFMT>
+__device__ __forceinline__ void issue_seq(const PPhase& p, const PPhase& nx, int ng2, int gidx, WBuf& b) {
+  const bool in_nx = gidx >= ng2;
+  PPhase q;
+  q.w = in_nx ? nx.w : p.w;
+  q.s = in_nx ? nx.s : p.s;
+  q.N = in_nx ? nx.N : p.N;
+  q.Kb = in_nx ? nx.Kb : p.Kb;
+  q.K = in_nx ? nx.K : p.K;
+  q.cpr = in_nx ? nx.cpr : p.cpr;
+  q.p0 = in_nx ? nx.p0 : p.p0;
+  q.ps = in_nx ? nx.ps : p.ps;
+  q.np = in_nx ? nx.np : p.np;
+  issue_group<WFMT>(q, (in_nx ? gidx - ng2 : gidx) * GRP, b);
+}
+
+// Streams this wave's rows of phase p against the input vector in LDS (xs), leaving each
+// finished dot product in ores.  Two register buffers alternate, A with the even groups and
+// B with the odd ones (no copies between them, so nothing waits on a load in flight), and
+// both stay loaded across phase boundaries: on entry A and B hold groups 0 and 1 of this
+// phase (issued during an earlier phase), on exit they hold groups 0 and 1 of nx.  The
+// group count is padded to an even number >= 2 so the roles line up at the boundary; pad
+// groups issue loads whose values are not used.  A wave's share of one projection is only
+// a few groups, so without loads in flight across the wait between phases every phase
+// would cost whole round trips to HBM.  With nx empty, A and B end holding loads whose
+// values are not used.
+template <int WFMT>
+__device__ __forceinline__ void gemv_phase(const PPhase& p, const PPhase& nx, WBuf& A, WBuf& B, const float* xs,
+                                           float* ores) {
+  const int wave = wave_id();
+  const int total = wave_pairs(p, wave) * 2 * p.cpr;
+  int ng2 = ((total + GRP - 1) / GRP + 1) & ~1;
+  if (ng2 < 2) ng2 = 2;
+  const float4* x4 = (const float4*)xs;
+  Cursor cu{0, 0, 0, 0.f, 0.f, 1.f, 1.f, 1.f};
+  for (int gi = 0; gi < ng2; gi += 2) {
+    consume_group<WFMT>(p, gi * GRP, total, A, x4, cu, ores);       // B stays in flight
+    issue_seq<WFMT>(p, nx, ng2, gi + 2, A);
+    consume_group<WFMT>(p, (gi + 1) * GRP, total, B, x4, cu, ores); // A stays in flight
+    issue_seq<WFMT>(p, nx, ng2, gi + 3, B);
   }
 }
 
@@ -376,20 +479,39 @@ __device__ __forceinline__ void stage_tagged(const uint64_t* src, uint32_t tag, 
   gather(K, tag, err, fail, [&](int i) { return src + i; }, [&](int i, float v) { xs[swz<VEC>(i)] = v; });
 }
 
+// RMSNorm gains of this thread's elements (i = tid + k*PT), loaded ahead of the wait for
+// the vector they scale
+constexpr int kNormPer = 8;    // model width up to 8 * PT
+__device__ __forceinline__ void gain_issue(const float* gain, int D, float (&gn)[kNormPer]) {
+#pragma unroll
+  for (int k = 0; k < kNormPer; k++) {
+    const int i = (int)threadIdx.x + k * PT;
+    gn[k] = i < D ? gload<float>(gain + i) : 0.f;
+  }
+}
+
 // xs = round_act(xf / sqrt(mean(xf^2) + eps) * gain), xf in LDS (complete: the caller has
 // synchronised); cap: optional copy in activation storage
 template <int VEC>
-__device__ __forceinline__ void norm_lds(const float* xf, const float* gain, int D, float eps, int act, float* xs,
-                                         void* cap, float* red) {
+__device__ __forceinline__ void norm_lds(const float* xf, const float (&gn)[kNormPer], int D, float eps, int act,
+                                         float* xs, void* cap, float* red) {
   float ss = 0.f;
-  for (int i = threadIdx.x; i < D; i += PT) ss += xf[i] * xf[i];
+#pragma unroll
+  for (int k = 0; k < kNormPer; k++) {
+    const int i = (int)threadIdx.x + k * PT;
+    if (i < D) ss += xf[i] * xf[i];
+  }
   ss = block_sum(ss, red);
   const float r = 1.0f / sqrtf(ss / (float)D + eps);
   zero_tail<VEC>(D, xs);
-  for (int i = threadIdx.x; i < D; i += PT) {
-    const float v = round_act(xf[i] * r * gain[i], act);
-    if (cap) store_act(cap, i, v, act);
-    xs[swz<VEC>(i)] = v;
+#pragma unroll
+  for (int k = 0; k < kNormPer; k++) {
+    const int i = (int)threadIdx.x + k * PT;
+    if (i < D) {
+      const float v = round_act(xf[i] * r * gn[k], act);
+      if (cap) store_act(cap, i, v, act);
+      xs[swz<VEC>(i)] = v;
+    }
   }
 }
 
@@ -398,9 +520,220 @@ __device__ __forceinline__ void load_plain_f32(const void* src, int n, float* ds
 }
 
 // ---------------------------------------------------------------------------------------
+// split-K GQA attention items
+//
+// An item (kv head j, chunk c) attends the G query heads that share kv head j to
+// positions [c*ct, min((c+1)*ct, pos+1)) in 64-position tiles, with an online softmax
+// across tiles, and leaves an unnormalised partial (acc, running max m, running sum l) per
+// head (the GQA decode rule of the Qwen3-8B engine article, 4.4.2: each K/V row is read
+// once for the whole query group).  A tile's K and V rows are loaded into registers ahead
+// of use, 16-byte vectors spread over the workgroup: an item's first tile before the wait
+// for its q, each later tile while the previous one is computed.  The block-table row sits
+// in LDS, so no KV load waits on another load.
+// ---------------------------------------------------------------------------------------
+
+template <int KVFMT> struct KvEB { static constexpr int EB = KVFMT == KV_F32 ? 4 : (KVFMT == KV_BF16 ? 2 : 1); };
+constexpr int kAttnOut = 4;    // outputs per thread: G*hd <= 2048 over PT threads
+
+// One tile (64 rows x hd*EB bytes, hd <= 128) of K and of V in registers: EB 16-byte
+// vectors per thread and matrix.
+template <int KVFMT>
+struct KvRegs {
+  static constexpr int NV = KvEB<KVFMT>::EB * 64 * 128 / 16 / PT;
+  uint4 k[NV];
+  uint4 v[NV];
+  float ks, vs;   // int8: scales of tile row threadIdx.x
+};
+
+__device__ __forceinline__ size_t kv_row(const Dims& d, const int* bt_s, int j, int t) {
+  const int lb = t / d.bs;
+  return ((size_t)bt_s[lb] * d.Hkv + j) * d.bs + (t - lb * d.bs);
+}
+
+// issues the loads of tile rows [t0, t0 + n) of kv head j
+template <int KVFMT>
+__device__ __forceinline__ void kv_issue(const Dims& d, const KvLayer& kv, const int* bt_s, int j, int t0, int n,
+                                         KvRegs<KVFMT>& r) {
+  constexpr int EB = KvEB<KVFMT>::EB;
+  const int vpr = d.hd * EB / 16;
+#pragma unroll
+  for (int k = 0; k < KvRegs<KVFMT>::NV; k++) {
+    const int v = (int)threadIdx.x + k * PT;
+    r.k[k] = r.v[k] = make_uint4(0u, 0u, 0u, 0u);
+    if (v < n * vpr) {
+      const int tl = v / vpr, cc = v - tl * vpr;
+      const size_t off = kv_row(d, bt_s, j, t0 + tl) * d.hd * EB + (size_t)cc * 16;
+      r.k[k] = gload<uint4>((const uint8_t*)kv.k + off);
+      r.v[k] = gload<uint4>((const uint8_t*)kv.v + off);
+    }
+  }
+  if constexpr (KVFMT == KV_I8) {
+    r.ks = r.vs = 0.f;
+    if ((int)threadIdx.x < n) {
+      const size_t row = kv_row(d, bt_s, j, t0 + threadIdx.x);
+      r.ks = f16_to_f32(gload<uint16_t>(kv.ks + row));
+      r.vs = f16_to_f32(gload<uint16_t>(kv.vs + row));
+    }
+  }
+}
+
+// decodes the registers of tile rows [t0, t0 + n) into LDS tiles tk, tv [64][hd+1]; row
+// pos (the new position) comes from new_s [2][hd] instead.  int8: row scales in ks_s, vs_s.
+template <int KVFMT>
+__device__ __forceinline__ void kv_store(const Dims& d, const KvRegs<KVFMT>& r, int t0, int n, int pos,
+                                         const float* new_s, const float* ks_s, const float* vs_s, float* tk,
+                                         float* tv) {
+  constexpr int EB = KvEB<KVFMT>::EB;
+  constexpr int PER = 16 / EB;   // elements per vector
+  const int hd = d.hd, ldk = hd + 1, vpr = hd * EB / 16;
+#pragma unroll
+  for (int k = 0; k < KvRegs<KVFMT>::NV; k++) {
+    const int v = (int)threadIdx.x + k * PT;
+    if (v < n * vpr) {
+      const int tl = v / vpr, e0 = (v - tl * vpr) * PER;
+      float* dk = tk + tl * ldk + e0;
+      float* dv = tv + tl * ldk + e0;
+      if (t0 + tl == pos) {
+#pragma unroll
+        for (int e = 0; e < PER; e++) { dk[e] = new_s[e0 + e]; dv[e] = new_s[hd + e0 + e]; }
+        continue;
+      }
+      const uint32_t uk[4] = {r.k[k].x, r.k[k].y, r.k[k].z, r.k[k].w};
+      const uint32_t uv[4] = {r.v[k].x, r.v[k].y, r.v[k].z, r.v[k].w};
+#pragma unroll
+      for (int q = 0; q < 4; q++) {
+        if constexpr (KVFMT == KV_F32) {
+          dk[q] = __uint_as_float(uk[q]);
+          dv[q] = __uint_as_float(uv[q]);
+        } else if constexpr (KVFMT == KV_BF16) {
+          dk[2 * q] = __uint_as_float(uk[q] << 16);
+          dk[2 * q + 1] = __uint_as_float(uk[q] & 0xffff0000u);
+          dv[2 * q] = __uint_as_float(uv[q] << 16);
+          dv[2 * q + 1] = __uint_as_float(uv[q] & 0xffff0000u);
+        } else {
+          const float sk = ks_s[tl], sv = vs_s[tl];
+#pragma unroll
+          for (int b = 0; b < 4; b++) {
+            dk[4 * q + b] = sext8(uk[q], b) * sk;
+            dv[4 * q + b] = sext8(uv[q], b) * sv;
+          }
+        }
+      }
+    }
+  }
+}
+
+__host__ __device__ inline size_t attn_p_floats(int G, int hd) {
+  return (size_t)G * hd + 2 * (size_t)kAttnTile * (hd + 1) + (size_t)G * kAttnTile + (size_t)G * 4 +
+         2 * (size_t)hd + 2 * (size_t)kAttnTile + PW;
+}
+
+// One item; all threads call it.  kr holds the item's first tile (issued by the caller).
+// qg, kn, vn: the group's queries and head j's new key/value (LDS); sm: attn_p_floats of LDS.
+template <int KVFMT, typename Put>
+__device__ __forceinline__ void attn_item_p(const Dims& d, const KvLayer& kv, const int* bt_s, int j, int c,
+                                            int ct, int nch, int pos, int pos_blk, const float* qg, const float* kn,
+                                            const float* vn, float* sm, KvRegs<KVFMT>& kr, Put put) {
+  const int hd = d.hd, G = d.G, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int t_begin = c * ct, t_end = min(pos + 1, t_begin + ct), ldk = hd + 1;
+  float* q_s = sm;                          // [G][hd], pre-scaled by 1/sqrt(hd)
+  float* tk = q_s + G * hd;                 // [64][hd+1]
+  float* tv = tk + kAttnTile * ldk;         // [64][hd+1]
+  float* p_s = tv + kAttnTile * ldk;        // [G][64]: scores, then probabilities
+  float* st_s = p_s + G * kAttnTile;        // [G][4]: running max, running sum, rescale
+  float* new_s = st_s + G * 4;              // [2][hd]: stored (decoded) new k, v
+  float* ks_s = new_s + 2 * hd;             // [64] int8 row scales of K
+  float* vs_s = ks_s + kAttnTile;           // [64] and of V
+  float* red = vs_s + kAttnTile;            // [PW]
+
+  const float scale = 1.0f / sqrtf((float)hd);
+  for (int e = tid; e < G * hd; e += PT) q_s[e] = qg[e] * scale;
+  for (int g = tid; g < G; g += PT) { st_s[g * 4] = -INFINITY; st_s[g * 4 + 1] = 0.f; }
+  if (pos >= t_begin && pos < t_end) {   // this item appends the new token of head j
+    const int off = pos - (pos / d.bs) * d.bs;
+    kv_append<KVFMT>(kv, ((size_t)pos_blk * d.Hkv + j) * d.bs + off, hd, kn, vn, new_s, red);
+  }
+  float acc[kAttnOut];
+#pragma unroll
+  for (int k = 0; k < kAttnOut; k++) acc[k] = 0.f;
+
+  for (int t0 = t_begin; t0 < t_end; t0 += kAttnTile) {
+    const int n = min(kAttnTile, t_end - t0);
+    if constexpr (KVFMT == KV_I8) {
+      if (tid < n) { ks_s[tid] = kr.ks; vs_s[tid] = kr.vs; }
+    }
+    __syncthreads();   // new_s, q_s, scales; the previous tile's readers are done
+    kv_store<KVFMT>(d, kr, t0, n, pos, new_s, ks_s, vs_s, tk, tv);
+    if (t0 + kAttnTile < t_end) kv_issue<KVFMT>(d, kv, bt_s, j, t0 + kAttnTile, min(kAttnTile, t_end - t0 - kAttnTile), kr);
+    __syncthreads();
+    for (int sidx = tid; sidx < G * kAttnTile; sidx += PT) {
+      const int g = sidx / kAttnTile, tl = sidx - g * kAttnTile;
+      float sc = -INFINITY;
+      if (tl < n) {
+        sc = 0.f;
+        const float* qq = q_s + g * hd;
+        const float* kr_ = tk + tl * ldk;
+        for (int i = 0; i < hd; i++) sc += qq[i] * kr_[i];
+      }
+      p_s[sidx] = sc;
+    }
+    __syncthreads();
+    for (int g = wave; g < G; g += PW) {
+      const float sc = p_s[g * kAttnTile + lane];
+      const float mt = wave_max(sc);
+      const float mo = st_s[g * 4], lo = st_s[g * 4 + 1];
+      const float mn = fmaxf(mo, mt);
+      const float pr = lane < n ? expf(sc - mn) : 0.f;
+      const float ps = wave_sum(pr);
+      p_s[g * kAttnTile + lane] = pr;
+      if (lane == 0) {
+        const float al = expf(mo - mn);
+        st_s[g * 4] = mn;
+        st_s[g * 4 + 1] = lo * al + ps;
+        st_s[g * 4 + 2] = al;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < kAttnOut; k++) {
+      const int oi = tid + k * PT;
+      if (oi < G * hd) {
+        const int g = oi / hd, i = oi - g * hd;
+        const float* pg = p_s + g * kAttnTile;
+        float sum = 0.f;
+        for (int tl = 0; tl < n; tl++) sum += pg[tl] * tv[tl * ldk + i];
+        acc[k] = acc[k] * st_s[g * 4 + 2] + sum;
+      }
+    }
+  }
+  __syncthreads();
+  const int cs = hd + 2;
+#pragma unroll
+  for (int k = 0; k < kAttnOut; k++) {
+    const int oi = tid + k * PT;
+    if (oi < G * hd) {
+      const int g = oi / hd, i = oi - g * hd;
+      put(((size_t)(j * G + g) * nch + c) * cs + i, acc[k]);   // partial layout [Hq][nch][hd+2]
+    }
+  }
+  for (int g = tid; g < G; g += PT) {
+    const size_t P = ((size_t)(j * G + g) * nch + c) * cs;
+    put(P + hd, st_s[g * 4]);
+    put(P + hd + 1, st_s[g * 4 + 1]);
+  }
+}
+
+// ---------------------------------------------------------------------------------------
 // the step kernel
 // ---------------------------------------------------------------------------------------
 
+// Phases of the flat loop: four per layer, then the LM head.
+enum { PH_QKV = 0, PH_O = 1, PH_GU = 2, PH_DOWN = 3, PH_HEAD = 4 };
+
+// The step as one flat loop over phases, so that the weight streaming, the input staging,
+// the epilogues and the attention each exist once in the binary: the loop body is executed
+// every layer, and a body larger than the instruction cache (64 KB) is refetched from L2
+// every layer, which stalls the weight stream far more than the fetch itself costs.
 template <int WFMT, int KVFMT>
 __global__ __launch_bounds__(PT) void k_step(PersistArgs a) {
   constexpr int VEC = PVec<WFMT>::VEC;
@@ -409,6 +742,7 @@ __global__ __launch_bounds__(PT) void k_step(PersistArgs a) {
   __shared__ int sfail;
   __shared__ float wbest[PW];
   __shared__ int widx[PW];
+  __shared__ float rope_s[128];       // cos | sin of this step's position (hd <= 128)
   const Dims& d = a.d;
   const int g = blockIdx.x, nwg = gridDim.x, tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
@@ -417,6 +751,8 @@ __global__ __launch_bounds__(PT) void k_step(PersistArgs a) {
   int32_t* err = a.err;
   float* xs = smem;                   // swizzled input vector of the current projection
   float* xf = smem + a.xs_floats;     // residual stream [D], plain order
+  int* bt_s = (int*)(xf + d.D);       // the sequence's block-table row [max_blocks]
+  float* ores = (float*)(bt_s + d.max_blocks);   // finished dot products of this workgroup's rows
   const int G = d.G, hd = d.hd, cs = hd + 2;
   auto T = [&](int l, int kind) { return a.epoch + (uint32_t)(l * kTagsPerLayer + kind); };
   auto inj = [&](int l, size_t off) { return (const void*)(a.inject + (size_t)l * a.po.record + off); };
@@ -424,83 +760,149 @@ __global__ __launch_bounds__(PT) void k_step(PersistArgs a) {
 
   PTRACE(0);
   if (tid == 0) sfail = 0;
-  // this step's block-table entries: every workgroup writes them (identical values), so its
-  // own attention reads see them without a hand-off
-  for (int u = tid; u < desc->n_updates; u += PT)
-    a.bt[(size_t)desc->upd[u][0] * d.max_blocks + desc->upd[u][1]] = desc->upd[u][2];
   int tok = desc->tokens[0];
   if (tok < 0 || tok >= d.V) {
     if (tid == 0) __hip_atomic_fetch_or(err, kErrToken, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     tok = 0;
   }
   const int pos = desc->pos[0], slot = desc->slot[0], pos_blk = desc->pos_block[0];
+  const bool do_head = desc->do_head != 0;
 
-  uint4 pre[GRP];
-  float psc[GRP];
+  WBuf pre, preb;   // weight groups in flight (A, B of gemv_phase)
+  float gn[kNormPer];
+  const void* dummy = a.layers[0].qkv.w;
   PPhase ph = make_phase<WFMT>(a.layers[0].qkv, g, nwg);
-  issue_group<WFMT>(ph, 0, pre, psc);
+  issue_group<WFMT>(ph, 0, pre);
+  issue_group<WFMT>(ph, GRP, preb);
+  // the sequence's block-table row in LDS with this step's entries applied; workgroup 0
+  // also stores those entries in the table for later steps
+  {
+    const int32_t* btrow = a.bt + (size_t)slot * d.max_blocks;
+    for (int b = tid; b < d.max_blocks; b += PT) {
+      int v = btrow[b];
+      for (int u = 0; u < desc->n_updates; u++)
+        if (desc->upd[u][0] == slot && desc->upd[u][1] == b) v = desc->upd[u][2];
+      bt_s[b] = v;
+    }
+    if (g == 0)
+      for (int u = tid; u < desc->n_updates; u += PT)
+        a.bt[(size_t)desc->upd[u][0] * d.max_blocks + desc->upd[u][1]] = desc->upd[u][2];
+  }
+  for (int i = tid; i < (hd >> 1); i += PT) {
+    rope_s[i] = gload<float>(a.rope_cos + (size_t)pos * (hd >> 1) + i);
+    rope_s[(hd >> 1) + i] = gload<float>(a.rope_sin + (size_t)pos * (hd >> 1) + i);
+  }
   // layer-0 input: the token's embedding row, dequantised by every workgroup
   if (!probe)
     for (int i = tid; i < d.D; i += PT) xf[i] = deq_elem(a.emb, d.wfmt, tok, i);
   __syncthreads();
 
   PEpi e{};
-  e.pos = pos;
-  e.rope_cos = a.rope_cos;
-  e.rope_sin = a.rope_sin;
+  e.rope = rope_s;
   e.xf = xf;
-  for (int l = 0; l < d.L; l++) {
-    const PLayer& Ly = a.layers[l];
+  e.logits = a.logits;
+  e.logits_out = desc->logits_out;
+  e.best = -INFINITY;
+  e.best_idx = INT_MAX;
+  const int nph = 4 * d.L + (do_head ? 1 : 0);
+#pragma clang loop unroll(disable)
+  for (int q = 0; q < nph; q++) {
+    const int l = q >> 2;                        // layer (d.L for the head)
+    const int k = q == 4 * d.L ? PH_HEAD : (q & 3);
+    const PLayer& Ly = a.layers[l < d.L ? l : d.L - 1];
     const int tb = 1 + l * 11;
-    PTRACE(tb);
-    // ---- RMSNorm -> QKV GEMV + RoPE ----
+    PTRACE(k == PH_HEAD ? tb : tb + (k == PH_QKV ? 0 : 2 * k + 2));
+
+    // ---- input of the projection ----
     // A probe step takes every wait of a normal step (the waits are what order the reuse of
     // the hand-off buffers), then replaces the input it received with the injected one.
-    if (l > 0) {
-      gather(d.D, T(l - 1, TG_XO), err, &sfail, [&](int i) { return a.t_xo + i; },
-             [&](int i, float v) { xf[i] = v; });
+    if (k == PH_QKV || k == PH_GU || k == PH_HEAD) {
+      // RMSNorm of the residual stream: layer 0's QKV input is the embedding row (in xf)
+      gain_issue(k == PH_QKV ? Ly.attn_norm : (k == PH_GU ? Ly.ffn_norm : a.final_norm), d.D, gn);
+      if (q > 0) {
+        const uint64_t* src = k == PH_GU ? a.t_xm : a.t_xo;
+        gather(d.D, k == PH_GU ? T(l, TG_XM) : T(l - 1, TG_XO), err, &sfail, [&](int i) { return src + i; },
+               [&](int i, float v) { xf[i] = v; });
+        __syncthreads();
+        if (sfail) return;
+      }
+      if (probe) {
+        const int lp = k == PH_HEAD ? d.L - 1 : l;
+        load_plain_f32(inj(lp, k == PH_QKV ? a.po.x_in : (k == PH_GU ? a.po.x_mid : a.po.x_out)), d.D, xf);
+        __syncthreads();
+        if (k != PH_HEAD) {
+          if (g == 0) {
+            norm_lds<VEC>(xf, gn, d.D, d.eps, d.act, xs, cap(l, k == PH_QKV ? a.po.xn : a.po.xn2), red);
+            __syncthreads();
+          }
+          stage_plain<VEC>(inj(l, k == PH_QKV ? a.po.xn : a.po.xn2), d.act, d.D, xs);
+        } else {
+          norm_lds<VEC>(xf, gn, d.D, d.eps, d.act, xs, nullptr, red);
+        }
+      } else {
+        norm_lds<VEC>(xf, gn, d.D, d.eps, d.act, xs, nullptr, red);
+      }
+    } else {
+      // the attention output (O) or the SwiGLU output (down), as produced
+      const bool is_o = k == PH_O;
+      stage_tagged<VEC>(is_o ? a.t_o : a.t_h, T(l, is_o ? TG_O : TG_H), is_o ? d.q_dim : d.F, xs, err, &sfail);
       __syncthreads();
       if (sfail) return;
-    }
-    if (probe) {
-      load_plain_f32(inj(l, a.po.x_in), d.D, xf);
-      __syncthreads();
-      if (g == 0) {
-        norm_lds<VEC>(xf, Ly.attn_norm, d.D, d.eps, d.act, xs, cap(l, a.po.xn), red);
-        __syncthreads();
-      }
-      stage_plain<VEC>(inj(l, a.po.xn), d.act, d.D, xs);
-    } else {
-      norm_lds<VEC>(xf, Ly.attn_norm, d.D, d.eps, d.act, xs, nullptr, red);
+      if (probe) stage_plain<VEC>(inj(l, is_o ? a.po.o : a.po.h), d.act, is_o ? d.q_dim : d.F, xs);
     }
     __syncthreads();
-    e.tag = T(l, TG_QKV);
-    e.tq = a.t_q;
-    e.tk = a.t_k;
-    e.tv = a.t_v;
-    e.cq = probe ? (float*)cap(l, a.po.q) : nullptr;
-    e.ck = probe ? (float*)cap(l, a.po.k) : nullptr;
-    e.cv = probe ? (float*)cap(l, a.po.v) : nullptr;
-    PPhase nx = make_phase<WFMT>(Ly.o, g, nwg);   // the prefetch skips attention
-    PTRACE(tb + 1);
-    gemv_phase<WFMT, EPI_QKV>(d, ph, nx, pre, psc, xs, e);
-    PTRACE(tb + 2);
 
-    // ---- KV append + split-K attention ----
-    const int nv = (pos + a.ct) / a.ct;
-    const int items = d.Hkv * nv;
-    const uint32_t tpart = T(l, TG_PART);
-    {
-      AttnCtx ac{};
-      ac.d = d;
-      ac.kv = Ly.kv;
-      ac.bt = a.bt;
-      ac.ct = a.ct;
-      ac.nch = a.nch;
-      float* ain = smem + attn_smem_floats(G, hd);   // [G*hd] q group | [hd] k | [hd] v
+    // ---- the projection; the next one's first weight groups are issued at its end (after
+    // QKV none: the O projection's weights are issued after attention, since otherwise their
+    // registers would stay live across the attention items) ----
+    PPhase nx;
+    if (k == PH_O) nx = make_phase<WFMT>(Ly.gu, g, nwg);
+    else if (k == PH_GU) nx = make_phase<WFMT>(Ly.down, g, nwg);
+    else if (k == PH_DOWN && l + 1 < d.L) nx = make_phase<WFMT>(a.layers[l + 1].qkv, g, nwg);
+    else if (k == PH_DOWN && do_head) nx = make_phase<WFMT>(a.head, g, nwg);
+    else nx = empty_phase(dummy);
+    PTRACE(k == PH_HEAD ? tb + 1 : tb + (k == PH_QKV ? 1 : 2 * k + 3));
+    gemv_phase<WFMT>(ph, nx, pre, preb, xs, ores);
+    __syncthreads();
+
+    // ---- epilogue ----
+    if (k == PH_QKV) {
+      e.tag = T(l, TG_QKV);
+      e.tq = a.t_q;
+      e.tk = a.t_k;
+      e.tv = a.t_v;
+      e.cq = probe ? (float*)cap(l, a.po.q) : nullptr;
+      e.ck = probe ? (float*)cap(l, a.po.k) : nullptr;
+      e.cv = probe ? (float*)cap(l, a.po.v) : nullptr;
+      phase_epilogue<EPI_QKV>(d, ph, ores, e);
+    } else if (k == PH_O || k == PH_DOWN) {
+      const bool is_o = k == PH_O;
+      e.tag = T(l, is_o ? TG_XM : TG_XO);
+      e.tout = is_o ? a.t_xm : a.t_xo;
+      e.cout = probe ? (float*)cap(l, is_o ? a.po.x_mid : a.po.x_out) : nullptr;
+      phase_epilogue<EPI_RESID>(d, ph, ores, e);
+    } else if (k == PH_GU) {
+      e.tag = T(l, TG_H);
+      e.th = a.t_h;
+      e.ch = probe ? cap(l, a.po.h) : nullptr;
+      phase_epilogue<EPI_SWIGLU>(d, ph, ores, e);
+    } else {
+      phase_epilogue<EPI_LOGITS>(d, ph, ores, e);
+    }
+    PTRACE(k == PH_HEAD ? tb + 2 : tb + (k == PH_QKV ? 2 : 2 * k + 4));
+
+    if (k == PH_QKV) {
+      // ---- KV append + split-K attention ----
+      const int nv = (pos + a.ct) / a.ct;
+      const int items = d.Hkv * nv;
+      const uint32_t tpart = T(l, TG_PART);
+      float* ain = smem + attn_p_floats(G, hd);   // [G*hd] q group | [hd] k | [hd] v
       const int nin = G * hd + 2 * hd;
+      KvRegs<KVFMT> kr;
       for (int it = g; it < items; it += nwg) {
-        const int j = it / nv, c = it - j * nv;
+        const int j = it / nv, c = it - j * nv, t0 = c * a.ct;
+        // the item's first KV tile is on its way while q, k, v are awaited
+        kv_issue<KVFMT>(d, Ly.kv, bt_s, j, t0, min(kAttnTile, min(pos + 1, t0 + a.ct) - t0), kr);
         __syncthreads();
         gather(nin, T(l, TG_QKV), err, &sfail,
                [&](int t) {
@@ -520,8 +922,8 @@ __global__ __launch_bounds__(PT) void k_step(PersistArgs a) {
         __syncthreads();
         if (sfail) return;
         uint64_t* tp = a.t_part;
-        attn_item<KVFMT>(ac, 0, j, c, pos, slot, pos_blk, ain, ain + G * hd, ain + G * hd + hd, smem,
-                         [tp, tpart](size_t i, float v) { put_tag(tp + i, tpart, v); });
+        attn_item_p<KVFMT>(d, Ly.kv, bt_s, j, c, a.ct, a.nch, pos, pos_blk, ain, ain + G * hd, ain + G * hd + hd,
+                           smem, kr, [tp, tpart](size_t i, float v) { put_tag(tp + i, tpart, v); });
       }
       PTRACE(tb + 3);
       // Merge: the workgroup that ran a head group's last chunk combines its chunks, after all
@@ -561,11 +963,11 @@ __global__ __launch_bounds__(PT) void k_step(PersistArgs a) {
           for (int c0 = 0; c0 < nv; c0 += 8) {
             uint64_t w[8];
 #pragma unroll
-            for (int k = 0; k < 8; k++) w[k] = c0 + k < nv ? get_word(P + (size_t)(c0 + k) * cs) : 0;
+            for (int u = 0; u < 8; u++) w[u] = c0 + u < nv ? get_word(P + (size_t)(c0 + u) * cs) : 0;
 #pragma unroll
-            for (int k = 0; k < 8; k++)
-              if (c0 + k < nv)
-                acc += ml[(gg * nv + c0 + k) * 2] * tag_value(P + (size_t)(c0 + k) * cs, w[k], tpart, err, &sfail);
+            for (int u = 0; u < 8; u++)
+              if (c0 + u < nv)
+                acc += ml[(gg * nv + c0 + u) * 2] * tag_value(P + (size_t)(c0 + u) * cs, w[u], tpart, err, &sfail);
           }
           const float o = acc / Ls[gg];
           if (probe) store_act(cap(l, a.po.o), (size_t)h * hd + i, o, d.act);
@@ -574,95 +976,28 @@ __global__ __launch_bounds__(PT) void k_step(PersistArgs a) {
         __syncthreads();
         if (sfail) return;
       }
-    }
-
-    PTRACE(tb + 4);
-    // ---- O GEMV + residual ----
-    __syncthreads();
-    stage_tagged<VEC>(a.t_o, T(l, TG_O), d.q_dim, xs, err, &sfail);
-    __syncthreads();
-    if (sfail) return;
-    if (probe) {
-      stage_plain<VEC>(inj(l, a.po.o), d.act, d.q_dim, xs);
+      // the O projection's first weight groups
+      nx = make_phase<WFMT>(Ly.o, g, nwg);
+      issue_group<WFMT>(nx, 0, pre);
+      issue_group<WFMT>(nx, GRP, preb);
       __syncthreads();
     }
-    e.tag = T(l, TG_XM);
-    e.tout = a.t_xm;
-    e.cout = probe ? (float*)cap(l, a.po.x_mid) : nullptr;
     ph = nx;
-    nx = make_phase<WFMT>(Ly.gu, g, nwg);
-    PTRACE(tb + 5);
-    gemv_phase<WFMT, EPI_RESID>(d, ph, nx, pre, psc, xs, e);
-    PTRACE(tb + 6);
-
-    // ---- RMSNorm -> gate/up GEMV + SwiGLU ----
-    __syncthreads();
-    gather(d.D, T(l, TG_XM), err, &sfail, [&](int i) { return a.t_xm + i; }, [&](int i, float v) { xf[i] = v; });
-    __syncthreads();
-    if (sfail) return;
-    if (probe) {
-      load_plain_f32(inj(l, a.po.x_mid), d.D, xf);
-      __syncthreads();
-      if (g == 0) {
-        norm_lds<VEC>(xf, Ly.ffn_norm, d.D, d.eps, d.act, xs, cap(l, a.po.xn2), red);
-        __syncthreads();
-      }
-      stage_plain<VEC>(inj(l, a.po.xn2), d.act, d.D, xs);
-    } else {
-      norm_lds<VEC>(xf, Ly.ffn_norm, d.D, d.eps, d.act, xs, nullptr, red);
-    }
-    __syncthreads();
-    e.tag = T(l, TG_H);
-    e.th = a.t_h;
-    e.ch = probe ? cap(l, a.po.h) : nullptr;
-    ph = nx;
-    nx = make_phase<WFMT>(Ly.down, g, nwg);
-    PTRACE(tb + 7);
-    gemv_phase<WFMT, EPI_SWIGLU>(d, ph, nx, pre, psc, xs, e);
-    PTRACE(tb + 8);
-
-    // ---- down GEMV + residual ----
-    __syncthreads();
-    stage_tagged<VEC>(a.t_h, T(l, TG_H), d.F, xs, err, &sfail);
-    __syncthreads();
-    if (sfail) return;
-    if (probe) {
-      stage_plain<VEC>(inj(l, a.po.h), d.act, d.F, xs);
-      __syncthreads();
-    }
-    e.tag = T(l, TG_XO);
-    e.tout = a.t_xo;
-    e.cout = probe ? (float*)cap(l, a.po.x_out) : nullptr;
-    ph = nx;
-    nx = l + 1 < d.L ? make_phase<WFMT>(a.layers[l + 1].qkv, g, nwg)
-                     : (desc->do_head ? make_phase<WFMT>(a.head, g, nwg) : empty_phase());
-    PTRACE(tb + 9);
-    gemv_phase<WFMT, EPI_RESID>(d, ph, nx, pre, psc, xs, e);
-    PTRACE(tb + 10);
-    ph = nx;
-    __syncthreads();
   }
-  if (!desc->do_head) return;
+  if (!do_head) return;
 
-  // ---- final RMSNorm -> LM head + greedy argmax ----
-  gather(d.D, T(d.L - 1, TG_XO), err, &sfail, [&](int i) { return a.t_xo + i; },
-         [&](int i, float v) { xf[i] = v; });
-  __syncthreads();
-  if (sfail) return;
-  if (probe) {
-    load_plain_f32(inj(d.L - 1, a.po.x_out), d.D, xf);
-    __syncthreads();
+  // ---- greedy argmax over the logits: this workgroup's winner, then workgroup 0 reduces ----
+  {   // first index among equal maxima
+    float b = e.best;
+    int bi = e.best_idx;
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) {
+      const float ov = __shfl_xor(b, m, 64);
+      const int oi = __shfl_xor(bi, m, 64);
+      if (ov > b || (ov == b && oi < bi)) { b = ov; bi = oi; }
+    }
+    if (lane == 0) { wbest[wave] = b; widx[wave] = bi; }
   }
-  norm_lds<VEC>(xf, a.final_norm, d.D, d.eps, d.act, xs, nullptr, red);
-  __syncthreads();
-  e.logits = a.logits;
-  e.logits_out = desc->logits_out;
-  e.best = -INFINITY;
-  e.best_idx = INT_MAX;
-  PTRACE(1 + d.L * 11);
-  gemv_phase<WFMT, EPI_LOGITS>(d, ph, empty_phase(), pre, psc, xs, e);
-  PTRACE(2 + d.L * 11);
-  if (lane == 0) { wbest[wave] = e.best; widx[wave] = e.best_idx; }
   __syncthreads();
   const uint32_t thead = T(d.L, 0);
   if (tid == 0) {
@@ -674,7 +1009,6 @@ __global__ __launch_bounds__(PT) void k_step(PersistArgs a) {
     put_tag(a.t_am + 2 * g + 1, thead, __int_as_float(bi));
   }
   if (g != 0) return;
-  // workgroup 0 reduces the per-workgroup winners (first index among equal maxima)
   gather(2 * nwg, thead, err, &sfail, [&](int t) { return a.t_am + t; }, [&](int t, float v) { xs[t] = v; });
   __syncthreads();
   if (sfail || wave != 0) return;
@@ -723,15 +1057,32 @@ size_t persistent_xs_floats(const Dims& d, int nch) {
   int kmax = d.D > d.F ? d.D : d.F;
   if (d.q_dim > kmax) kmax = d.q_dim;
   size_t need = (size_t)(kmax + kstep - 1) / kstep * kstep;                             // projection input
-  const size_t at = dev::attn_smem_floats(d.G, d.hd) + (size_t)d.G * d.hd + 2 * (size_t)d.hd;  // attention
+  const size_t at = attn_p_floats(d.G, d.hd) + (size_t)d.G * d.hd + 2 * (size_t)d.hd;  // attention
   const size_t mg = 2 * (size_t)d.G * nch + (size_t)d.G;                                // chunk merge
   if (at > need) need = at;
   if (mg > need) need = mg;
   return (need + 3) / 4 * 4;
 }
 
-size_t persistent_smem_bytes(const Dims& d, int nch) {
-  return (persistent_xs_floats(d, nch) + (size_t)d.D) * sizeof(float);
+// rows one workgroup owns in the largest projection
+static size_t rows_per_wg(const Dims& d, int nwg) {
+  int nmax = d.qkv_rows;
+  if (d.D > nmax) nmax = d.D;
+  if (2 * d.F > nmax) nmax = 2 * d.F;
+  if (d.V > nmax) nmax = d.V;
+  const size_t pairs = ((size_t)nmax + 1) / 2;
+  return 2 * ((pairs + nwg - 1) / nwg);
+}
+
+size_t persistent_smem_bytes(const Dims& d, int nch, int nwg) {
+  return (persistent_xs_floats(d, nch) + (size_t)d.D + (size_t)d.max_blocks + rows_per_wg(d, nwg)) *
+         sizeof(float);
+}
+
+bool persistent_supports(const Dims& d) {
+  const int eb = d.kvfmt == KV_F32 ? 4 : (d.kvfmt == KV_BF16 ? 2 : 1);
+  return d.D <= kNormPer * PT && d.hd <= 128 && (d.hd * eb) % 16 == 0 &&
+         (size_t)d.G * d.hd <= (size_t)kAttnOut * PT;
 }
 
 int persistent_tags_per_step(const Dims& d) { return d.L * kTagsPerLayer + 1; }

@@ -111,6 +111,8 @@ _FORMATS = [
     dict(wfmt=synth.W_Q8_0, kvfmt=synth.KV_I8),
     dict(n_q_heads=8, n_kv_heads=4, head_dim=64, act=synth.ACT_BF16, kvfmt=synth.KV_BF16),
     dict(n_q_heads=4, n_kv_heads=4, head_dim=16, wfmt=synth.W_BF16),   # MHA, q_dim != D
+    dict(wfmt=synth.W_Q8_0),                                            # Q8_0 with fp32 KV
+    dict(wfmt=synth.W_BF16, act=synth.ACT_BF16, kvfmt=synth.KV_I8),
 ]
 
 
