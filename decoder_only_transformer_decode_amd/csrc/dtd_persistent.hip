@@ -82,6 +82,15 @@ template <> struct PVec<W_BF16> { static constexpr int VEC = 8; };
 
 typedef __attribute__((address_space(1))) uint64_t gword;
 
+// Reads a register that a load may have written, unconditionally.  The compiler tracks loads
+// in flight per register; a load whose register is read only under a branch some wave can
+// skip counts as possibly pending after that branch, and the next wait for a weight group
+// then drains every load in flight instead of waiting for that group alone.
+template <typename T>
+__device__ __forceinline__ void settle(const T& v) {
+  asm volatile("" ::"v"(v));
+}
+
 __device__ __forceinline__ void put_tag(uint64_t* p, uint32_t tag, float v) {
   __hip_atomic_store((gword*)p, ((uint64_t)tag << 32) | __float_as_uint(v), __ATOMIC_RELAXED,
                      __HIP_MEMORY_SCOPE_AGENT);
@@ -136,6 +145,8 @@ __device__ __forceinline__ void gather(int n, uint32_t tag, int32_t* err, int* f
       const int i = i0 + k * PT + (int)threadIdx.x;
       if (i < n) put(i, tag_value(src(i), w[k], tag, err, fail));
     }
+#pragma unroll
+    for (int k = 0; k < B; k++) settle(w[k]);
   }
 }
 
@@ -220,37 +231,43 @@ struct WBuf {
   uint32_t sc[GRP];   // Q8_0: fp16 block scale bits; int8-row: fp32 row scale bits
 };
 
-// Issues the loads of lines [c0, c0 + GRP) of this wave's stream in phase p, with their
-// scales (Q8_0: the line's block scale; int8-row: the row scale).  Every call issues the
-// same loads whatever the phase: a line (or a lane's part of one) outside the matrix reads
-// offset 0 of the matrix instead, and its value is never used (whole lines are skipped by
-// the consumer; a lane's part past the row end meets the input vector's zero padding).
-// Addresses are a uniform base plus a 32-bit offset (a matrix is below 4 GiB).
+// A wave's stream in one phase: its row pairs in turn, each pair as 2*cpr lines that
+// interleave the two rows, (row 0, line 0), (row 1, line 0), (row 0, line 1), ... so a line's
+// row is the parity of its index, and both rows of a line step share one input chunk.  A
+// pair's line count is even and GRP is even, so every group starts on row 0.
+//
+// Position of the next line step a wave issues: line count c, pair k (of the wave) and line j
+// of the rows.  Kept across calls so that no division is needed per group.
+struct ICur {
+  int c, k, j;
+};
+
+// Issues the next GRP lines of this wave's stream in phase p, with their scales (Q8_0: the
+// line's block scale; int8-row: the row scale), and advances the cursor.  Every call issues
+// the same loads whatever the phase: a line (or a lane's part of one) outside the matrix reads
+// offset 0 of the matrix instead, and its value is never used (whole lines are skipped by the
+// consumer; a lane's part past the row end meets the input vector's zero padding).  Addresses
+// are a uniform base plus a 32-bit offset (a matrix is below 4 GiB).
 template <int WFMT>
-__device__ __forceinline__ void issue_group(const PPhase& p, int c0, WBuf& b) {
+__device__ __forceinline__ void issue_group(const PPhase& p, ICur& ic, WBuf& b) {
   const int wave = wave_id(), lane = threadIdx.x & 63;
   const int total = wave_pairs(p, wave) * 2 * p.cpr;
-  const int per = 2 * p.cpr;
-  int k = c0 / per;
-  const int rem = c0 - k * per;
-  int rs = rem >= p.cpr;
-  int j = rem - rs * p.cpr;
 #pragma unroll
   for (int s = 0; s < GRP; s++) {
-    const int row = 2 * (p.p0 + p.ps * (wave + PW * k)) + rs;
-    const int cb = (j * 64 + lane) * 16;
-    const bool rok = c0 + s < total && row < p.N;
+    const int row = 2 * (p.p0 + p.ps * (wave + PW * ic.k)) + (s & 1);
+    const int cb = (ic.j * 64 + lane) * 16;
+    const bool rok = ic.c + s < total && row < p.N;
     const bool ok = rok && cb < p.Kb;
     b.w[s] = gload<v4u>(p.w + (ok ? (uint32_t)row * (uint32_t)p.Kb + (uint32_t)cb : 0u));
     if constexpr (WFMT == W_Q8_0)
       b.sc[s] = gload<uint16_t>(p.s + (ok ? ((uint32_t)row * (uint32_t)(p.K >> 5) + (uint32_t)(cb >> 5)) * 2u : 0u));
     else if constexpr (WFMT == W_INT8_ROW)
       b.sc[s] = gload<uint32_t>(p.s + (rok ? (uint32_t)row * 4u : 0u));
-    if (++j == p.cpr) {
-      j = 0;
-      if (++rs == 2) { rs = 0; ++k; }
+    if (s & 1) {
+      if (++ic.j == p.cpr) { ic.j = 0; ++ic.k; }
     }
   }
+  ic.c += GRP;
 }
 
 // Epilogue destinations of one phase: tagged words, and in a probe step (the c* pointers
@@ -338,70 +355,108 @@ __device__ __forceinline__ void phase_epilogue(const Dims& d, const PPhase& p, c
   }
 }
 
-// consume cursor of one wave's stream: position (pair k of the wave, row rs of the pair,
-// line j of the row) and the running dot products of the pair's two rows
+// Sum over the 64 lanes of a wave with DPP moves only (no LDS round trips): quad swaps,
+// then half-row and row mirrors give every lane its 16-lane row sum, two row broadcasts
+// fold rows 0+1 into row 1 / rows 2+3 into row 3 and then row 1 into row 3; lane 63 holds
+// the total, returned as a wave-uniform value.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_add(float v) {
+  return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xf, false));
+}
+
+__device__ __forceinline__ float wave_total(float v) {
+  v = dpp_add<0xb1, 0xf>(v);    // quad_perm [1,0,3,2]
+  v = dpp_add<0x4e, 0xf>(v);    // quad_perm [2,3,0,1]
+  v = dpp_add<0x141, 0xf>(v);   // row_half_mirror
+  v = dpp_add<0x140, 0xf>(v);   // row_mirror
+  v = dpp_add<0x142, 0xa>(v);   // row_bcast:15 into rows 1 and 3
+  v = dpp_add<0x143, 0xc>(v);   // row_bcast:31 into rows 2 and 3
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
+// consume cursor of one wave's stream: line step j of pair k, and the running dot products
+// of the pair's two rows
 struct Cursor {
-  int k, rs, j;
+  int k, j;
   float acc0, acc1;
   float rsc0, rsc1;   // int8-row: scales of the pair's rows
-  float rsc_line;     // int8-row: scale carried by the last real line
 };
 
-// Multiplies lines [c0, c0 + GRP) of buffer b against the input vector; a finished pair's
-// dot products go to ores (LDS, local pair index).  Every line's registers are read
-// whether or not the line is real (a pad line's product is discarded by a select): a load
-// whose value is never read is still pending when its register is reissued, and the
-// compiler then waits for every load in flight, not just that one.
+// dot product of one line (16 bytes per lane) with this lane's input chunk
+template <int WFMT>
+__device__ __forceinline__ float line_dot(const v4u& v, const float4 (&x)[WFMT == W_BF16 ? 2 : 4]) {
+  float part = 0.f;
+  if constexpr (WFMT == W_BF16) {
+    const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+      const float4 xq = x[q >> 1];
+      const float x0 = q & 1 ? xq.z : xq.x, x1 = q & 1 ? xq.w : xq.y;
+      part = fmaf(__uint_as_float(u[q] << 16), x0, part);
+      part = fmaf(__uint_as_float(u[q] & 0xffff0000u), x1, part);
+    }
+  } else {
+    const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+      part = fmaf(sext8(u[q], 0), x[q].x, part);
+      part = fmaf(sext8(u[q], 1), x[q].y, part);
+      part = fmaf(sext8(u[q], 2), x[q].z, part);
+      part = fmaf(sext8(u[q], 3), x[q].w, part);
+    }
+  }
+  return part;
+}
+
+// Multiplies lines [c0, c0 + GRP) of buffer b against the input vector: two line steps, each
+// one line of row 0 and one of row 1 of a pair at the same input chunk.  A finished pair's
+// dot products go to ores (LDS, local pair index).  Every line's registers are read whether
+// or not the line is real (a pad step's products are dropped by a select): a load whose value
+// is never read is still pending when its register is reissued, and the compiler then waits
+// for every load in flight, not just that one.
 template <int WFMT>
 __device__ __forceinline__ void consume_group(const PPhase& p, int c0, int total, const WBuf& b, const float4* x4,
                                               Cursor& cu, float* ores) {
   const int wave = wave_id(), lane = threadIdx.x & 63;
+  constexpr int XQ = WFMT == W_BF16 ? 2 : 4;   // float4 of input per lane and line
+  // both steps' input chunks first, so their LDS round trips overlap (a pad step reads some
+  // chunk below cpr)
+  const int j0 = cu.j, j1 = cu.j + 1 == p.cpr ? 0 : cu.j + 1;
+  float4 xa[XQ], xb[XQ];
 #pragma unroll
-  for (int s = 0; s < GRP; s++) {
-    const bool valid = c0 + s < total;   // wave-uniform
-    const v4u v = b.w[s];
-    const int j = cu.j;
-    float part = 0.f;
-    if constexpr (WFMT == W_BF16) {
-      const float4 xa = x4[(j * 2 + 0) * 64 + lane], xb = x4[(j * 2 + 1) * 64 + lane];
-      part = __uint_as_float(v.x << 16) * xa.x + __uint_as_float(v.x & 0xffff0000u) * xa.y +
-             __uint_as_float(v.y << 16) * xa.z + __uint_as_float(v.y & 0xffff0000u) * xa.w +
-             __uint_as_float(v.z << 16) * xb.x + __uint_as_float(v.z & 0xffff0000u) * xb.y +
-             __uint_as_float(v.w << 16) * xb.z + __uint_as_float(v.w & 0xffff0000u) * xb.w;
-    } else {
-      const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+  for (int q = 0; q < XQ; q++) {
+    xa[q] = x4[(j0 * XQ + q) * 64 + lane];
+    xb[q] = x4[(j1 * XQ + q) * 64 + lane];
+  }
+  float part[GRP];
+  part[0] = line_dot<WFMT>(b.w[0], xa);
+  part[1] = line_dot<WFMT>(b.w[1], xa);
+  part[2] = line_dot<WFMT>(b.w[2], xb);
+  part[3] = line_dot<WFMT>(b.w[3], xb);
+  if constexpr (WFMT == W_Q8_0) {
 #pragma unroll
-      for (int q = 0; q < 4; q++) {
-        const float4 xv = x4[(j * 4 + q) * 64 + lane];
-        part += sext8(u[q], 0) * xv.x + sext8(u[q], 1) * xv.y + sext8(u[q], 2) * xv.z + sext8(u[q], 3) * xv.w;
-      }
-      if constexpr (WFMT == W_Q8_0) part *= f16_to_f32((uint16_t)b.sc[s]);
-    }
+    for (int s = 0; s < GRP; s++) part[s] *= f16_to_f32((uint16_t)b.sc[s]);
+  }
+#pragma unroll
+  for (int st = 0; st < GRP / 2; st++) {
+    const bool valid = c0 + 2 * st < total;   // wave-uniform; both lines of a step together
+    cu.acc0 += valid ? part[2 * st] : 0.f;
+    cu.acc1 += valid ? part[2 * st + 1] : 0.f;
     if constexpr (WFMT == W_INT8_ROW) {   // every line of a row carries the row's scale
-      const float scl = __uint_as_float(b.sc[s]);
-      cu.rsc_line = valid ? scl : cu.rsc_line;
+      cu.rsc0 = valid ? __uint_as_float(b.sc[2 * st]) : cu.rsc0;
+      cu.rsc1 = valid ? __uint_as_float(b.sc[2 * st + 1]) : cu.rsc1;
     }
-    part = valid ? part : 0.f;
-    if (cu.rs) cu.acc1 += part;
-    else cu.acc0 += part;
     if (valid && ++cu.j == p.cpr) {
-      if constexpr (WFMT == W_INT8_ROW) {
-        if (cu.rs) cu.rsc1 = cu.rsc_line;
-        else cu.rsc0 = cu.rsc_line;
-      }
       cu.j = 0;
-      if (++cu.rs == 2) {
-        cu.rs = 0;
-        // int8-row: per-row scale after the dot
-        const float v0 = wave_sum(cu.acc0) * cu.rsc0, v1 = wave_sum(cu.acc1) * cu.rsc1;
-        cu.acc0 = cu.acc1 = 0.f;
-        if (lane == 0) {
-          const int lp = wave + PW * cu.k;   // pair index within this workgroup's range
-          ores[2 * lp] = v0;
-          ores[2 * lp + 1] = v1;
-        }
-        ++cu.k;
+      // int8-row: per-row scale after the dot
+      const float v0 = wave_total(cu.acc0) * cu.rsc0, v1 = wave_total(cu.acc1) * cu.rsc1;
+      cu.acc0 = cu.acc1 = 0.f;
+      if (lane == 0) {
+        const int lp = wave + PW * cu.k;   // pair index within this workgroup's range
+        ores[2 * lp] = v0;
+        ores[2 * lp + 1] = v1;
       }
+      ++cu.k;
     }
   }
 }
@@ -409,10 +464,12 @@ __device__ __forceinline__ void consume_group(const PPhase& p, int c0, int total
 // Issues group gidx of the sequence "groups 0..ng2-1 of p, then groups of nx": the phase is
 // picked by uniform selects, so each buffer has exactly one issue site in the loop below
 // (two sites would be free to use different registers for the same in-flight group, and a
-// copy at the join would read registers that a load has yet to write).
+// copy at the join would read registers that a load has yet to write).  The cursor restarts
+// at the first group of nx.
 template <int WFMT>
-__device__ __forceinline__ void issue_seq(const PPhase& p, const PPhase& nx, int ng2, int gidx, WBuf& b) {
+__device__ __forceinline__ void issue_seq(const PPhase& p, const PPhase& nx, int ng2, int gidx, WBuf& b, ICur& ic) {
   const bool in_nx = gidx >= ng2;
+  if (gidx == ng2) ic = ICur{0, 0, 0};
   PPhase q;
   q.w = in_nx ? nx.w : p.w;
   q.s = in_nx ? nx.s : p.s;
@@ -423,7 +480,10 @@ __device__ __forceinline__ void issue_seq(const PPhase& p, const PPhase& nx, int
   q.p0 = in_nx ? nx.p0 : p.p0;
   q.ps = in_nx ? nx.ps : p.ps;
   q.np = in_nx ? nx.np : p.np;
-  issue_group<WFMT>(q, (in_nx ? gidx - ng2 : gidx) * GRP, b);
+  issue_group<WFMT>(q, ic, b);
+  // nothing of the following consume may be scheduled above these loads: a product of the
+  // group issued just before would then wait for that group before this one is on its way
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 // Streams this wave's rows of phase p against the input vector in LDS (xs), leaving each
@@ -438,18 +498,18 @@ __device__ __forceinline__ void issue_seq(const PPhase& p, const PPhase& nx, int
 // values are not used.
 template <int WFMT>
 __device__ __forceinline__ void gemv_phase(const PPhase& p, const PPhase& nx, WBuf& A, WBuf& B, const float* xs,
-                                           float* ores) {
+                                           float* ores, ICur& ic) {
   const int wave = wave_id();
   const int total = wave_pairs(p, wave) * 2 * p.cpr;
   int ng2 = ((total + GRP - 1) / GRP + 1) & ~1;
   if (ng2 < 2) ng2 = 2;
   const float4* x4 = (const float4*)xs;
-  Cursor cu{0, 0, 0, 0.f, 0.f, 1.f, 1.f, 1.f};
+  Cursor cu{0, 0, 0.f, 0.f, 1.f, 1.f};
   for (int gi = 0; gi < ng2; gi += 2) {
     consume_group<WFMT>(p, gi * GRP, total, A, x4, cu, ores);       // B stays in flight
-    issue_seq<WFMT>(p, nx, ng2, gi + 2, A);
+    issue_seq<WFMT>(p, nx, ng2, gi + 2, A, ic);
     consume_group<WFMT>(p, (gi + 1) * GRP, total, B, x4, cu, ores); // A stays in flight
-    issue_seq<WFMT>(p, nx, ng2, gi + 3, B);
+    issue_seq<WFMT>(p, nx, ng2, gi + 3, B, ic);
   }
 }
 
@@ -513,6 +573,10 @@ __device__ __forceinline__ void norm_lds(const float* xf, const float (&gn)[kNor
       xs[swz<VEC>(i)] = v;
     }
   }
+  // the gains were read above only where i < D; this unconditional read ends their loads on
+  // every path (see settle())
+#pragma unroll
+  for (int k = 0; k < kNormPer; k++) settle(gn[k]);
 }
 
 __device__ __forceinline__ void load_plain_f32(const void* src, int n, float* dst) {
@@ -727,6 +791,32 @@ __device__ __forceinline__ void attn_item_p(const Dims& d, const KvLayer& kv, co
 // the step kernel
 // ---------------------------------------------------------------------------------------
 
+// The layer table is read through the constant address space: the host writes it before the
+// launch and the kernel never does, so its (wave-uniform) fields come in by scalar loads,
+// which wait on their own counter.  Read by vector loads they would be the youngest loads in
+// flight when a projection starts, and waiting for them there would drain the weight groups
+// issued before them.
+typedef const __attribute__((address_space(4))) PLayer CPLayer;
+typedef const __attribute__((address_space(4))) MatDev CMatDev;
+
+__device__ __forceinline__ MatDev cmat(CMatDev* m) {
+  MatDev r;
+  r.w = m->w;
+  r.s = m->s;
+  r.rows = m->rows;
+  r.cols = m->cols;
+  return r;
+}
+
+__device__ __forceinline__ KvLayer ckv(CPLayer* t) {
+  KvLayer r;
+  r.k = t->kv.k;
+  r.v = t->kv.v;
+  r.ks = t->kv.ks;
+  r.vs = t->kv.vs;
+  return r;
+}
+
 // Phases of the flat loop: four per layer, then the LM head.
 enum { PH_QKV = 0, PH_O = 1, PH_GU = 2, PH_DOWN = 3, PH_HEAD = 4 };
 
@@ -770,10 +860,12 @@ __global__ __launch_bounds__(PT) void k_step(PersistArgs a) {
 
   WBuf pre, preb;   // weight groups in flight (A, B of gemv_phase)
   float gn[kNormPer];
-  const void* dummy = a.layers[0].qkv.w;
-  PPhase ph = make_phase<WFMT>(a.layers[0].qkv, g, nwg);
-  issue_group<WFMT>(ph, 0, pre);
-  issue_group<WFMT>(ph, GRP, preb);
+  CPLayer* layers = (CPLayer*)a.layers;
+  const void* dummy = layers[0].qkv.w;
+  PPhase ph = make_phase<WFMT>(cmat(&layers[0].qkv), g, nwg);
+  ICur ic{0, 0, 0};   // issue cursor of phase ph (then of the phase after it)
+  issue_group<WFMT>(ph, ic, pre);
+  issue_group<WFMT>(ph, ic, preb);
   // the sequence's block-table row in LDS with this step's entries applied; workgroup 0
   // also stores those entries in the table for later steps
   {
@@ -809,7 +901,7 @@ __global__ __launch_bounds__(PT) void k_step(PersistArgs a) {
   for (int q = 0; q < nph; q++) {
     const int l = q >> 2;                        // layer (d.L for the head)
     const int k = q == 4 * d.L ? PH_HEAD : (q & 3);
-    const PLayer& Ly = a.layers[l < d.L ? l : d.L - 1];
+    CPLayer* Ly = layers + (l < d.L ? l : d.L - 1);
     const int tb = 1 + l * 11;
     PTRACE(k == PH_HEAD ? tb : tb + (k == PH_QKV ? 0 : 2 * k + 2));
 
@@ -818,7 +910,7 @@ __global__ __launch_bounds__(PT) void k_step(PersistArgs a) {
     // the hand-off buffers), then replaces the input it received with the injected one.
     if (k == PH_QKV || k == PH_GU || k == PH_HEAD) {
       // RMSNorm of the residual stream: layer 0's QKV input is the embedding row (in xf)
-      gain_issue(k == PH_QKV ? Ly.attn_norm : (k == PH_GU ? Ly.ffn_norm : a.final_norm), d.D, gn);
+      gain_issue(k == PH_QKV ? Ly->attn_norm : (k == PH_GU ? Ly->ffn_norm : a.final_norm), d.D, gn);
       if (q > 0) {
         const uint64_t* src = k == PH_GU ? a.t_xm : a.t_xo;
         gather(d.D, k == PH_GU ? T(l, TG_XM) : T(l - 1, TG_XO), err, &sfail, [&](int i) { return src + i; },
@@ -826,18 +918,19 @@ __global__ __launch_bounds__(PT) void k_step(PersistArgs a) {
         __syncthreads();
         if (sfail) return;
       }
+      // Every path reads the gains (gn): a load whose register is never read stays pending
+      // into the projection below, and waiting for it there would also wait for the weight
+      // groups in flight.
       if (probe) {
         const int lp = k == PH_HEAD ? d.L - 1 : l;
         load_plain_f32(inj(lp, k == PH_QKV ? a.po.x_in : (k == PH_GU ? a.po.x_mid : a.po.x_out)), d.D, xf);
         __syncthreads();
+        const bool keep = k != PH_HEAD && g == 0;   // workgroup 0 records the normalised input
+        norm_lds<VEC>(xf, gn, d.D, d.eps, d.act, xs, keep ? cap(l, k == PH_QKV ? a.po.xn : a.po.xn2) : nullptr,
+                      red);
         if (k != PH_HEAD) {
-          if (g == 0) {
-            norm_lds<VEC>(xf, gn, d.D, d.eps, d.act, xs, cap(l, k == PH_QKV ? a.po.xn : a.po.xn2), red);
-            __syncthreads();
-          }
+          __syncthreads();
           stage_plain<VEC>(inj(l, k == PH_QKV ? a.po.xn : a.po.xn2), d.act, d.D, xs);
-        } else {
-          norm_lds<VEC>(xf, gn, d.D, d.eps, d.act, xs, nullptr, red);
         }
       } else {
         norm_lds<VEC>(xf, gn, d.D, d.eps, d.act, xs, nullptr, red);
@@ -856,13 +949,15 @@ __global__ __launch_bounds__(PT) void k_step(PersistArgs a) {
     // QKV none: the O projection's weights are issued after attention, since otherwise their
     // registers would stay live across the attention items) ----
     PPhase nx;
-    if (k == PH_O) nx = make_phase<WFMT>(Ly.gu, g, nwg);
-    else if (k == PH_GU) nx = make_phase<WFMT>(Ly.down, g, nwg);
-    else if (k == PH_DOWN && l + 1 < d.L) nx = make_phase<WFMT>(a.layers[l + 1].qkv, g, nwg);
+    if (k == PH_O) nx = make_phase<WFMT>(cmat(&Ly->gu), g, nwg);
+    else if (k == PH_GU) nx = make_phase<WFMT>(cmat(&Ly->down), g, nwg);
+    else if (k == PH_DOWN && l + 1 < d.L) nx = make_phase<WFMT>(cmat(&layers[l + 1].qkv), g, nwg);
     else if (k == PH_DOWN && do_head) nx = make_phase<WFMT>(a.head, g, nwg);
     else nx = empty_phase(dummy);
     PTRACE(k == PH_HEAD ? tb + 1 : tb + (k == PH_QKV ? 1 : 2 * k + 3));
-    gemv_phase<WFMT>(ph, nx, pre, preb, xs, ores);
+#pragma unroll
+    for (int i = 0; i < kNormPer; i++) settle(gn[i]);   // no gain load may reach the stream
+    gemv_phase<WFMT>(ph, nx, pre, preb, xs, ores, ic);
     __syncthreads();
 
     // ---- epilogue ----
@@ -899,10 +994,11 @@ __global__ __launch_bounds__(PT) void k_step(PersistArgs a) {
       float* ain = smem + attn_p_floats(G, hd);   // [G*hd] q group | [hd] k | [hd] v
       const int nin = G * hd + 2 * hd;
       KvRegs<KVFMT> kr;
+      const KvLayer lkv = ckv(Ly);
       for (int it = g; it < items; it += nwg) {
         const int j = it / nv, c = it - j * nv, t0 = c * a.ct;
         // the item's first KV tile is on its way while q, k, v are awaited
-        kv_issue<KVFMT>(d, Ly.kv, bt_s, j, t0, min(kAttnTile, min(pos + 1, t0 + a.ct) - t0), kr);
+        kv_issue<KVFMT>(d, lkv, bt_s, j, t0, min(kAttnTile, min(pos + 1, t0 + a.ct) - t0), kr);
         __syncthreads();
         gather(nin, T(l, TG_QKV), err, &sfail,
                [&](int t) {
@@ -922,7 +1018,7 @@ __global__ __launch_bounds__(PT) void k_step(PersistArgs a) {
         __syncthreads();
         if (sfail) return;
         uint64_t* tp = a.t_part;
-        attn_item_p<KVFMT>(d, Ly.kv, bt_s, j, c, a.ct, a.nch, pos, pos_blk, ain, ain + G * hd, ain + G * hd + hd,
+        attn_item_p<KVFMT>(d, lkv, bt_s, j, c, a.ct, a.nch, pos, pos_blk, ain, ain + G * hd, ain + G * hd + hd,
                            smem, kr, [tp, tpart](size_t i, float v) { put_tag(tp + i, tpart, v); });
       }
       PTRACE(tb + 3);
@@ -968,6 +1064,8 @@ __global__ __launch_bounds__(PT) void k_step(PersistArgs a) {
             for (int u = 0; u < 8; u++)
               if (c0 + u < nv)
                 acc += ml[(gg * nv + c0 + u) * 2] * tag_value(P + (size_t)(c0 + u) * cs, w[u], tpart, err, &sfail);
+#pragma unroll
+            for (int u = 0; u < 8; u++) settle(w[u]);
           }
           const float o = acc / Ls[gg];
           if (probe) store_act(cap(l, a.po.o), (size_t)h * hd + i, o, d.act);
@@ -977,9 +1075,10 @@ __global__ __launch_bounds__(PT) void k_step(PersistArgs a) {
         if (sfail) return;
       }
       // the O projection's first weight groups
-      nx = make_phase<WFMT>(Ly.o, g, nwg);
-      issue_group<WFMT>(nx, 0, pre);
-      issue_group<WFMT>(nx, GRP, preb);
+      nx = make_phase<WFMT>(cmat(&Ly->o), g, nwg);
+      ic = ICur{0, 0, 0};
+      issue_group<WFMT>(nx, ic, pre);
+      issue_group<WFMT>(nx, ic, preb);
       __syncthreads();
     }
     ph = nx;
