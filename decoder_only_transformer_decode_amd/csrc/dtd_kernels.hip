@@ -151,7 +151,7 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
   constexpr int VEC = WVec<WFMT>::VEC;
   constexpr int EB = WVec<WFMT>::EB;
   constexpr int KSTEP = 64 * VEC;
-  extern __shared__ float xs[];
+  extern __shared__ __attribute__((aligned(16))) float xs[];   // read as float4
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int N = a.m.rows, K = a.m.cols;
@@ -259,7 +259,7 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
 
 template <int KVFMT>
 __global__ __launch_bounds__(256) void k_attn(AttnCtx a, const StepDesc* desc, float* partials) {
-  extern __shared__ float sm[];
+  extern __shared__ __attribute__((aligned(16))) float sm[];   // read as float4
   const int c = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
   const int pos = desc->pos[b];
   if (c * a.ct > pos) return;               // chunk beyond this sequence's length

@@ -64,7 +64,15 @@ __shared__ unsigned long long g_trace_lds[16];
   do {                                                                                     \
     if (threadIdx.x == 0 && (k) < 16) g_trace_lds[(k)] = __builtin_amdgcn_s_memrealtime();   \
   } while (0)
+// inside an attention item: only when the caller set the item-trace flag
+#define ITRACE(ev) \
+  do {                 \
+    if (itrace) PTRACE(ev); \
+  } while (0)
 #else
+#define ITRACE(ev) \
+  do {              \
+  } while (0)
 #define PTRACE(ev) \
   do {             \
   } while (0)
@@ -89,6 +97,13 @@ typedef __attribute__((address_space(1))) uint64_t gword;
 template <typename T>
 __device__ __forceinline__ void settle(const T& v) {
   asm volatile("" ::"v"(v));
+}
+
+__device__ __forceinline__ void settle(const uint4& v) {
+  settle(v.x);
+  settle(v.y);
+  settle(v.z);
+  settle(v.w);
 }
 
 __device__ __forceinline__ void put_tag(uint64_t* p, uint32_t tag, float v) {
@@ -374,6 +389,23 @@ __device__ __forceinline__ float wave_total(float v) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
+// the same shape of reduction for the maximum (rows left out by a broadcast keep -inf)
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_max(float v) {
+  return fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp((int)0xff800000, __float_as_int(v), CTRL, ROW_MASK,
+                                                             0xf, false)));
+}
+
+__device__ __forceinline__ float wave_top(float v) {
+  v = dpp_max<0xb1, 0xf>(v);
+  v = dpp_max<0x4e, 0xf>(v);
+  v = dpp_max<0x141, 0xf>(v);
+  v = dpp_max<0x140, 0xf>(v);
+  v = dpp_max<0x142, 0xa>(v);
+  v = dpp_max<0x143, 0xc>(v);
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
 // consume cursor of one wave's stream: line step j of pair k, and the running dot products
 // of the pair's two rows
 struct Cursor {
@@ -641,54 +673,79 @@ __device__ __forceinline__ void kv_issue(const Dims& d, const KvLayer& kv, const
   }
 }
 
-// decodes the registers of tile rows [t0, t0 + n) into LDS tiles tk, tv [64][hd+1]; row
-// pos (the new position) comes from new_s [2][hd] instead.  int8: row scales in ks_s, vs_s.
+// KV tile rows in LDS are padded to hd + 4 floats: lane t reading row t as float4s then
+// touches every bank once per 16 lanes.
+__host__ __device__ inline int kv_ld(int hd) { return hd + 4; }
+
+// Decodes the registers of tile rows [t0, t0 + n) into LDS tiles tk, tv [64][hd+4]; row pos
+// (the new position) comes from new_s [2][hd] instead; rows [n, 64) of tv are zeroed (their
+// probabilities are 0, and 0 times a stale non-finite value would not be).  int8: row
+// scales in ks_s, vs_s.
 template <int KVFMT>
 __device__ __forceinline__ void kv_store(const Dims& d, const KvRegs<KVFMT>& r, int t0, int n, int pos,
                                          const float* new_s, const float* ks_s, const float* vs_s, float* tk,
                                          float* tv) {
   constexpr int EB = KvEB<KVFMT>::EB;
   constexpr int PER = 16 / EB;   // elements per vector
-  const int hd = d.hd, ldk = hd + 1, vpr = hd * EB / 16;
+  const int hd = d.hd, ldk = kv_ld(hd), vpr = hd * EB / 16;
 #pragma unroll
   for (int k = 0; k < KvRegs<KVFMT>::NV; k++) {
     const int v = (int)threadIdx.x + k * PT;
-    if (v < n * vpr) {
+    if (v < kAttnTile * vpr) {
       const int tl = v / vpr, e0 = (v - tl * vpr) * PER;
-      float* dk = tk + tl * ldk + e0;
-      float* dv = tv + tl * ldk + e0;
-      if (t0 + tl == pos) {
+      float4* dk = (float4*)(tk + tl * ldk + e0);
+      float4* dv = (float4*)(tv + tl * ldk + e0);
+      float fk[PER], fv[PER];
+      if (tl >= n) {
 #pragma unroll
-        for (int e = 0; e < PER; e++) { dk[e] = new_s[e0 + e]; dv[e] = new_s[hd + e0 + e]; }
-        continue;
-      }
-      const uint32_t uk[4] = {r.k[k].x, r.k[k].y, r.k[k].z, r.k[k].w};
-      const uint32_t uv[4] = {r.v[k].x, r.v[k].y, r.v[k].z, r.v[k].w};
+        for (int e = 0; e < PER; e++) fk[e] = fv[e] = 0.f;
+      } else if (t0 + tl == pos) {
 #pragma unroll
-      for (int q = 0; q < 4; q++) {
-        if constexpr (KVFMT == KV_F32) {
-          dk[q] = __uint_as_float(uk[q]);
-          dv[q] = __uint_as_float(uv[q]);
-        } else if constexpr (KVFMT == KV_BF16) {
-          dk[2 * q] = __uint_as_float(uk[q] << 16);
-          dk[2 * q + 1] = __uint_as_float(uk[q] & 0xffff0000u);
-          dv[2 * q] = __uint_as_float(uv[q] << 16);
-          dv[2 * q + 1] = __uint_as_float(uv[q] & 0xffff0000u);
-        } else {
-          const float sk = ks_s[tl], sv = vs_s[tl];
+        for (int e = 0; e < PER; e++) { fk[e] = new_s[e0 + e]; fv[e] = new_s[hd + e0 + e]; }
+      } else {
+        const uint32_t uk[4] = {r.k[k].x, r.k[k].y, r.k[k].z, r.k[k].w};
+        const uint32_t uv[4] = {r.v[k].x, r.v[k].y, r.v[k].z, r.v[k].w};
 #pragma unroll
-          for (int b = 0; b < 4; b++) {
-            dk[4 * q + b] = sext8(uk[q], b) * sk;
-            dv[4 * q + b] = sext8(uv[q], b) * sv;
+        for (int q = 0; q < 4; q++) {
+          if constexpr (KVFMT == KV_F32) {
+            fk[q] = __uint_as_float(uk[q]);
+            fv[q] = __uint_as_float(uv[q]);
+          } else if constexpr (KVFMT == KV_BF16) {
+            fk[2 * q] = __uint_as_float(uk[q] << 16);
+            fk[2 * q + 1] = __uint_as_float(uk[q] & 0xffff0000u);
+            fv[2 * q] = __uint_as_float(uv[q] << 16);
+            fv[2 * q + 1] = __uint_as_float(uv[q] & 0xffff0000u);
+          } else {
+            const float sk = ks_s[tl], sv = vs_s[tl];
+#pragma unroll
+            for (int b = 0; b < 4; b++) {
+              fk[4 * q + b] = sext8(uk[q], b) * sk;
+              fv[4 * q + b] = sext8(uv[q], b) * sv;
+            }
           }
         }
       }
+#pragma unroll
+      for (int e = 0; e < PER / 4; e++) {
+        dk[e] = make_float4(fk[4 * e], fk[4 * e + 1], fk[4 * e + 2], fk[4 * e + 3]);
+        dv[e] = make_float4(fv[4 * e], fv[4 * e + 1], fv[4 * e + 2], fv[4 * e + 3]);
+      }
     }
+  }
+  // the tile's loads were read above only for rows below n
+#pragma unroll
+  for (int k = 0; k < KvRegs<KVFMT>::NV; k++) {
+    settle(r.k[k]);
+    settle(r.v[k]);
+  }
+  if constexpr (KVFMT == KV_I8) {
+    settle(r.ks);
+    settle(r.vs);
   }
 }
 
 __host__ __device__ inline size_t attn_p_floats(int G, int hd) {
-  return (size_t)G * hd + 2 * (size_t)kAttnTile * (hd + 1) + (size_t)G * kAttnTile + (size_t)G * 4 +
+  return (size_t)G * hd + 2 * (size_t)kAttnTile * kv_ld(hd) + (size_t)G * kAttnTile + (size_t)G * 4 +
          2 * (size_t)hd + 2 * (size_t)kAttnTile + PW;
 }
 
@@ -697,12 +754,13 @@ __host__ __device__ inline size_t attn_p_floats(int G, int hd) {
 template <int KVFMT, typename Put>
 __device__ __forceinline__ void attn_item_p(const Dims& d, const KvLayer& kv, const int* bt_s, int j, int c,
                                             int ct, int nch, int pos, int pos_blk, const float* qg, const float* kn,
-                                            const float* vn, float* sm, KvRegs<KVFMT>& kr, Put put) {
+                                            const float* vn, float* sm, KvRegs<KVFMT>& kr, Put put,
+                                            bool itrace = false) {
   const int hd = d.hd, G = d.G, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int t_begin = c * ct, t_end = min(pos + 1, t_begin + ct), ldk = hd + 1;
+  const int t_begin = c * ct, t_end = min(pos + 1, t_begin + ct), ldk = kv_ld(hd);
   float* q_s = sm;                          // [G][hd], pre-scaled by 1/sqrt(hd)
-  float* tk = q_s + G * hd;                 // [64][hd+1]
-  float* tv = tk + kAttnTile * ldk;         // [64][hd+1]
+  float* tk = q_s + G * hd;                 // [64][hd+4]
+  float* tv = tk + kAttnTile * ldk;         // [64][hd+4]
   float* p_s = tv + kAttnTile * ldk;        // [G][64]: scores, then probabilities
   float* st_s = p_s + G * kAttnTile;        // [G][4]: running max, running sum, rescale
   float* new_s = st_s + G * 4;              // [2][hd]: stored (decoded) new k, v
@@ -720,6 +778,7 @@ __device__ __forceinline__ void attn_item_p(const Dims& d, const KvLayer& kv, co
   float acc[kAttnOut];
 #pragma unroll
   for (int k = 0; k < kAttnOut; k++) acc[k] = 0.f;
+  ITRACE(403);
 
   for (int t0 = t_begin; t0 < t_end; t0 += kAttnTile) {
     const int n = min(kAttnTile, t_end - t0);
@@ -730,25 +789,31 @@ __device__ __forceinline__ void attn_item_p(const Dims& d, const KvLayer& kv, co
     kv_store<KVFMT>(d, kr, t0, n, pos, new_s, ks_s, vs_s, tk, tv);
     if (t0 + kAttnTile < t_end) kv_issue<KVFMT>(d, kv, bt_s, j, t0 + kAttnTile, min(kAttnTile, t_end - t0 - kAttnTile), kr);
     __syncthreads();
-    for (int sidx = tid; sidx < G * kAttnTile; sidx += PT) {
-      const int g = sidx / kAttnTile, tl = sidx - g * kAttnTile;
-      float sc = -INFINITY;
-      if (tl < n) {
-        sc = 0.f;
-        const float* qq = q_s + g * hd;
-        const float* kr_ = tk + tl * ldk;
-        for (int i = 0; i < hd; i++) sc += qq[i] * kr_[i];
-      }
-      p_s[sidx] = sc;
-    }
-    __syncthreads();
+    ITRACE(404);
+    // scores and softmax: wave w takes heads w, w + PW, ...; lane t is tile row t, whose
+    // key it reads as float4s against the (broadcast) query; the wave then holds the head's
+    // 64 scores, one per lane, and reduces them with DPP
     for (int g = wave; g < G; g += PW) {
-      const float sc = p_s[g * kAttnTile + lane];
-      const float mt = wave_max(sc);
+      const float4* kq = (const float4*)(tk + lane * ldk);
+      const float4* qq = (const float4*)(q_s + g * hd);
+      const int hd4 = hd >> 2;
+      float s0 = 0.f, s1 = 0.f;
+      int c4 = 0;
+      for (; c4 + 1 < hd4; c4 += 2) {
+        const float4 ka = kq[c4], kb = kq[c4 + 1], qa = qq[c4], qb = qq[c4 + 1];
+        s0 = fmaf(ka.x, qa.x, s0); s0 = fmaf(ka.y, qa.y, s0); s0 = fmaf(ka.z, qa.z, s0); s0 = fmaf(ka.w, qa.w, s0);
+        s1 = fmaf(kb.x, qb.x, s1); s1 = fmaf(kb.y, qb.y, s1); s1 = fmaf(kb.z, qb.z, s1); s1 = fmaf(kb.w, qb.w, s1);
+      }
+      if (c4 < hd4) {
+        const float4 ka = kq[c4], qa = qq[c4];
+        s0 = fmaf(ka.x, qa.x, s0); s0 = fmaf(ka.y, qa.y, s0); s0 = fmaf(ka.z, qa.z, s0); s0 = fmaf(ka.w, qa.w, s0);
+      }
+      const float sc = lane < n ? s0 + s1 : -INFINITY;
+      const float mt = wave_top(sc);
       const float mo = st_s[g * 4], lo = st_s[g * 4 + 1];
       const float mn = fmaxf(mo, mt);
       const float pr = lane < n ? expf(sc - mn) : 0.f;
-      const float ps = wave_sum(pr);
+      const float ps = wave_total(pr);
       p_s[g * kAttnTile + lane] = pr;
       if (lane == 0) {
         const float al = expf(mo - mn);
@@ -758,19 +823,30 @@ __device__ __forceinline__ void attn_item_p(const Dims& d, const KvLayer& kv, co
       }
     }
     __syncthreads();
+    ITRACE(405);
+    // P V: output (g, i) over the 64 tile rows (rows past n have p = 0 and v = 0)
 #pragma unroll
     for (int k = 0; k < kAttnOut; k++) {
       const int oi = tid + k * PT;
       if (oi < G * hd) {
         const int g = oi / hd, i = oi - g * hd;
-        const float* pg = p_s + g * kAttnTile;
-        float sum = 0.f;
-        for (int tl = 0; tl < n; tl++) sum += pg[tl] * tv[tl * ldk + i];
-        acc[k] = acc[k] * st_s[g * 4 + 2] + sum;
+        const float4* pg = (const float4*)(p_s + g * kAttnTile);
+        float s0 = 0.f, s1 = 0.f;
+#pragma unroll 2
+        for (int t4 = 0; t4 < kAttnTile / 4; t4 += 2) {
+          const float4 pa = pg[t4], pb = pg[t4 + 1];
+          const float* vr = tv + (4 * t4) * ldk + i;
+          s0 = fmaf(pa.x, vr[0], s0); s0 = fmaf(pa.y, vr[ldk], s0);
+          s0 = fmaf(pa.z, vr[2 * ldk], s0); s0 = fmaf(pa.w, vr[3 * ldk], s0);
+          s1 = fmaf(pb.x, vr[4 * ldk], s1); s1 = fmaf(pb.y, vr[5 * ldk], s1);
+          s1 = fmaf(pb.z, vr[6 * ldk], s1); s1 = fmaf(pb.w, vr[7 * ldk], s1);
+        }
+        acc[k] = acc[k] * st_s[g * 4 + 2] + (s0 + s1);
       }
     }
   }
   __syncthreads();
+  ITRACE(406);
   const int cs = hd + 2;
 #pragma unroll
   for (int k = 0; k < kAttnOut; k++) {
@@ -827,7 +903,9 @@ enum { PH_QKV = 0, PH_O = 1, PH_GU = 2, PH_DOWN = 3, PH_HEAD = 4 };
 template <int WFMT, int KVFMT>
 __global__ __launch_bounds__(PT) void k_step(PersistArgs a) {
   constexpr int VEC = PVec<WFMT>::VEC;
-  extern __shared__ float smem[];
+  // Dynamic LDS is placed after the static variables below; without the alignment it would
+  // start at their (unaligned) end, and every float4 access to it would be split.
+  extern __shared__ __attribute__((aligned(16))) float smem[];
   __shared__ float red[PW];
   __shared__ int sfail;
   __shared__ float wbest[PW];
@@ -1017,18 +1095,30 @@ __global__ __launch_bounds__(PT) void k_step(PersistArgs a) {
         }
         __syncthreads();
         if (sfail) return;
+        if (l == 5) PTRACE(400);
         uint64_t* tp = a.t_part;
         attn_item_p<KVFMT>(d, lkv, bt_s, j, c, a.ct, a.nch, pos, pos_blk, ain, ain + G * hd, ain + G * hd + hd,
-                           smem, kr, [tp, tpart](size_t i, float v) { put_tag(tp + i, tpart, v); });
+                           smem, kr, [tp, tpart](size_t i, float v) { put_tag(tp + i, tpart, v); }, l == 5);
+        if (l == 5) PTRACE(401);
       }
       PTRACE(tb + 3);
       // Merge: the workgroup that ran a head group's last chunk combines its chunks, after all
-      // of its own items (so no workgroup waits on one that is itself waiting).
+      // of its own items (so no workgroup waits on one that is itself waiting).  The chunk
+      // vectors of a thread's first output are loaded before the (m, l) words are gathered, so
+      // the two round trips overlap.
       for (int it = g; it < items; it += nwg) {
         const int j = it / nv, c = it - j * nv;
         if (c != nv - 1) continue;
         float* ml = smem;                 // [G][nv][2]: (m, l), then (weight, l)
         float* Ls = smem + 2 * G * nv;    // [G] sum of weighted l
+        constexpr int MB = 16;            // chunk words per thread in flight
+        uint64_t w[MB];                   // first batch: chunks [0, MB) of output tid
+        {
+          const int oi0 = tid < G * hd ? tid : 0;
+          const uint64_t* P0 = a.t_part + (size_t)(j * G + oi0 / hd) * a.nch * cs + (oi0 - (oi0 / hd) * hd);
+#pragma unroll
+          for (int u = 0; u < MB; u++) w[u] = u < nv ? get_word(P0 + (size_t)u * cs) : 0;
+        }
         __syncthreads();
         gather(G * nv * 2, tpart, err, &sfail,
                [&](int t) {
@@ -1038,17 +1128,18 @@ __global__ __launch_bounds__(PT) void k_step(PersistArgs a) {
                [&](int t, float v) { ml[t] = v; });
         __syncthreads();
         if (sfail) return;
+        if (l == 5) PTRACE(402);
         for (int gg = wave; gg < G; gg += PW) {   // weights e^(m_c - M) and their l sum
           float M = -INFINITY;
           for (int cc = lane; cc < nv; cc += 64) M = fmaxf(M, ml[(gg * nv + cc) * 2]);
-          M = wave_max(M);
+          M = wave_top(M);
           float L = 0.f;
           for (int cc = lane; cc < nv; cc += 64) {
-            const float w = expf(ml[(gg * nv + cc) * 2] - M);
-            ml[(gg * nv + cc) * 2] = w;
-            L += w * ml[(gg * nv + cc) * 2 + 1];
+            const float wt = expf(ml[(gg * nv + cc) * 2] - M);
+            ml[(gg * nv + cc) * 2] = wt;
+            L += wt * ml[(gg * nv + cc) * 2 + 1];
           }
-          L = wave_sum(L);
+          L = wave_total(L);
           if (lane == 0) Ls[gg] = L;
         }
         __syncthreads();
@@ -1056,21 +1147,24 @@ __global__ __launch_bounds__(PT) void k_step(PersistArgs a) {
           const int gg = oi / hd, i = oi - gg * hd, h = j * G + gg;
           const uint64_t* P = a.t_part + (size_t)h * a.nch * cs + i;
           float acc = 0.f;
-          for (int c0 = 0; c0 < nv; c0 += 8) {
-            uint64_t w[8];
+          for (int c0 = 0; c0 < nv; c0 += MB) {
+            if (oi != tid || c0 != 0) {
 #pragma unroll
-            for (int u = 0; u < 8; u++) w[u] = c0 + u < nv ? get_word(P + (size_t)(c0 + u) * cs) : 0;
+              for (int u = 0; u < MB; u++) w[u] = c0 + u < nv ? get_word(P + (size_t)(c0 + u) * cs) : 0;
+            }
 #pragma unroll
-            for (int u = 0; u < 8; u++)
+            for (int u = 0; u < MB; u++)
               if (c0 + u < nv)
                 acc += ml[(gg * nv + c0 + u) * 2] * tag_value(P + (size_t)(c0 + u) * cs, w[u], tpart, err, &sfail);
 #pragma unroll
-            for (int u = 0; u < 8; u++) settle(w[u]);
+            for (int u = 0; u < MB; u++) settle(w[u]);
           }
           const float o = acc / Ls[gg];
           if (probe) store_act(cap(l, a.po.o), (size_t)h * hd + i, o, d.act);
           put_tag(a.t_o + h * hd + i, T(l, TG_O), round_act(o, d.act));
         }
+#pragma unroll
+        for (int u = 0; u < MB; u++) settle(w[u]);
         __syncthreads();
         if (sfail) return;
       }
