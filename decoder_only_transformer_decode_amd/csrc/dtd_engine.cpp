@@ -382,7 +382,7 @@ extern "C" dtd_status dtd_create(const dtd_config* cfg, void* hip_stream, dtd_en
     (void)hipGetLastError();
     const int nw = e->nwg > 0 ? e->nwg : 1;
     // tagged buffers: q, k, v, o, x_mid, h, x_out, chunk partials, per-workgroup argmax
-    e->tags_words = (size_t)2 * d.q_dim + 2 * (size_t)d.kv_dim + 2 * (size_t)d.D + (size_t)d.F +
+    e->tags_words = (size_t)2 * d.q_dim + 2 * (size_t)d.kv_dim + 2 * (size_t)d.D + h_buffer_words(d.F, nw) +
                     (size_t)d.Hq * e->p_nch * (d.hd + 2) + 2 * (size_t)nw;
     if ((st = dev_alloc(e, &e->players, sizeof(PLayer) * (size_t)d.L)) ||
         (st = dev_alloc(e, &e->tags, sizeof(uint64_t) * e->tags_words)))
@@ -686,7 +686,7 @@ static dtd_status run_step(dtd_engine* e, int B, const int* slots, const int* po
       a.t_v = t; t += d.kv_dim;
       a.t_o = t; t += d.q_dim;
       a.t_xm = t; t += d.D;
-      a.t_h = t; t += d.F;
+      a.t_h = t; t += h_buffer_words(d.F, e->nwg);
       a.t_xo = t; t += d.D;
       a.t_part = t; t += (size_t)d.Hq * e->p_nch * (d.hd + 2);
       a.t_am = t;

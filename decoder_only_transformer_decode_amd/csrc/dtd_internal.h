@@ -127,6 +127,15 @@ struct PersistArgs {
   ProbeLayout po;
 };
 
+// Packed hand-off of the SwiGLU output with bf16 activations: each workgroup of the step
+// kernel writes this many words (two values each) of its F-row share, pads included.
+__host__ __device__ inline int h_words_per_wg(int F, int nwg) { return ((F + nwg - 1) / nwg + 1) / 2; }
+// words of the SwiGLU output's hand-off buffer (either layout)
+inline size_t h_buffer_words(int F, int nwg) {
+  const size_t packed = (size_t)nwg * h_words_per_wg(F, nwg);
+  return packed > (size_t)F ? packed : (size_t)F;
+}
+
 // ---- launchers (dtd_kernels.hip, dtd_persistent.hip) ----
 size_t persistent_smem_bytes(const Dims& d, int nch, int nwg);
 size_t persistent_xs_floats(const Dims& d, int nch);

@@ -89,6 +89,7 @@ template <> struct PVec<W_BF16> { static constexpr int VEC = 8; };
 // ---------------------------------------------------------------------------------------
 
 typedef __attribute__((address_space(1))) uint64_t gword;
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 
 // Reads a register that a load may have written, unconditionally.  The compiler tracks loads
 // in flight per register; a load whose register is read only under a branch some wave can
@@ -97,6 +98,13 @@ typedef __attribute__((address_space(1))) uint64_t gword;
 template <typename T>
 __device__ __forceinline__ void settle(const T& v) {
   asm volatile("" ::"v"(v));
+}
+
+__device__ __forceinline__ void settle(const v4u& v) {
+  settle(v.x);
+  settle(v.y);
+  settle(v.z);
+  settle(v.w);
 }
 
 __device__ __forceinline__ void settle(const uint4& v) {
@@ -115,50 +123,52 @@ __device__ __forceinline__ uint64_t get_word(const uint64_t* p) {
   return __hip_atomic_load((gword*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Re-polls p until it carries tag.  Gives up (raising kErrBarrier and the workgroup's LDS
-// fail flag) after kSpinLimit polls, or as soon as another thread or workgroup has given up,
-// so every wait ends.
-__device__ __forceinline__ float wait_slow(const uint64_t* p, uint32_t tag, int32_t* err, int* fail) {
+// Waits until all B words w[k] carry tag, re-loading the stale ones together (load(k))
+// once per round, so that a batch costs one memory round trip per round rather than one per
+// stale word.  Words a thread does not hold start out carrying the tag.  Gives up (raising
+// kErrBarrier and the workgroup's LDS fail flag) after kSpinLimit rounds, or as soon as
+// another thread or workgroup has given up, so every wait ends; the caller synchronises the
+// workgroup and then tests the fail flag.
+template <int B, typename Load>
+__device__ __forceinline__ void await_tags(uint64_t (&w)[B], uint32_t tag, int32_t* err, int* fail, Load load) {
   unsigned spins = 0;
   for (;;) {
-    if (*(volatile int*)fail) return 0.f;
-    __builtin_amdgcn_s_sleep(2);
-    const uint64_t w = get_word(p);
-    if ((uint32_t)(w >> 32) == tag) return __uint_as_float((uint32_t)w);
+    bool all = true;
+#pragma unroll
+    for (int k = 0; k < B; k++) all = all && (uint32_t)(w[k] >> 32) == tag;
+    if (all || *(volatile int*)fail) return;
     ++spins;
     if (spins > kSpinLimit ||
         ((spins & 255) == 0 &&
          (__hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & kErrBarrier))) {
       __hip_atomic_fetch_or(err, kErrBarrier, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       *(volatile int*)fail = 1;
-      return 0.f;
+      return;
     }
+    __builtin_amdgcn_s_sleep(2);
+#pragma unroll
+    for (int k = 0; k < B; k++)
+      if ((uint32_t)(w[k] >> 32) != tag) w[k] = load(k);
   }
 }
 
-// value of word p (first loaded as w) once it carries tag
-__device__ __forceinline__ float tag_value(const uint64_t* p, uint64_t w, uint32_t tag, int32_t* err, int* fail) {
-  if ((uint32_t)(w >> 32) == tag) return __uint_as_float((uint32_t)w);
-  return wait_slow(p, tag, err, fail);
-}
-
 // Reads n tagged words, word i at src(i), handing each value to put(i, v).  Every thread
-// of the workgroup takes part with up to 8 loads in flight before it checks any tag.  The
-// caller synchronises the workgroup and then tests the fail flag.
-template <typename Src, typename Put>
+// of the workgroup takes part with up to B loads in flight.  The caller synchronises the
+// workgroup and then tests the fail flag.
+template <int B = 8, typename Src, typename Put>
 __device__ __forceinline__ void gather(int n, uint32_t tag, int32_t* err, int* fail, Src src, Put put) {
-  constexpr int B = 8;
   for (int i0 = 0; i0 < n; i0 += B * PT) {
     uint64_t w[B];
 #pragma unroll
     for (int k = 0; k < B; k++) {
       const int i = i0 + k * PT + (int)threadIdx.x;
-      w[k] = i < n ? get_word(src(i)) : 0;
+      w[k] = i < n ? get_word(src(i)) : (uint64_t)tag << 32;
     }
+    await_tags<B>(w, tag, err, fail, [&](int k) { return get_word(src(i0 + k * PT + (int)threadIdx.x)); });
 #pragma unroll
     for (int k = 0; k < B; k++) {
       const int i = i0 + k * PT + (int)threadIdx.x;
-      if (i < n) put(i, tag_value(src(i), w[k], tag, err, fail));
+      if (i < n) put(i, __uint_as_float((uint32_t)w[k]));
     }
 #pragma unroll
     for (int k = 0; k < B; k++) settle(w[k]);
@@ -235,7 +245,6 @@ __device__ __forceinline__ int wave_pairs(const PPhase& p, int wave) {
 // issue site per loop, and branches depend only on wave-uniform values.  Otherwise it
 // falls back to a full drain (vmcnt(0)) before each group, leaving one group in flight
 // per wave instead of two.
-typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 
 template <int WFMT> struct Grp {
   static constexpr int SC = WFMT == W_BF16 ? 0 : GRP;   // scale loads per group
@@ -304,6 +313,7 @@ struct PEpi {
   // SwiGLU
   uint64_t* th;
   void* ch;
+  int hs;         // bf16 activations: packed words of h per workgroup
   // logits
   float* logits;
   float* logits_out;
@@ -351,12 +361,32 @@ __device__ __forceinline__ void phase_epilogue(const Dims& d, const PPhase& p, c
       if (r < p.N) emit(e.tout, e.cout, e.tag, r, e.xf[r] + ores[u]);
     }
   } else if constexpr (EPI == EPI_SWIGLU) {
-    for (int t = threadIdx.x; t < p.np; t += PT) {   // rows (2f, 2f+1) = (gate f, up f)
-      const int f = p.p0 + p.ps * t;
-      const float v0 = ores[2 * t], v1 = ores[2 * t + 1];
-      const float hv = v0 / (1.0f + expf(-v0)) * v1;
-      if (e.ch) store_act(e.ch, f, hv, d.act);
-      put_tag(e.th + f, e.tag, round_act(hv, d.act));
+    if (d.act == ACT_BF16) {
+      // two outputs per word: word u of this workgroup carries its local pairs 2u, 2u + 1
+      // (low, high half); every one of its hs words is written, pads as zero
+      for (int u = threadIdx.x; u < e.hs; u += PT) {
+        uint32_t bits = 0;
+#pragma unroll
+        for (int hh = 0; hh < 2; hh++) {
+          const int t = 2 * u + hh;
+          if (t < p.np) {   // rows (2f, 2f+1) = (gate f, up f)
+            const int f = p.p0 + p.ps * t;
+            const float v0 = ores[2 * t], v1 = ores[2 * t + 1];
+            const float hv = v0 / (1.0f + expf(-v0)) * v1;
+            if (e.ch) store_act(e.ch, f, hv, d.act);
+            bits |= (uint32_t)f32_to_bf16(hv) << (16 * hh);
+          }
+        }
+        put_tag(e.th + (size_t)p.p0 * e.hs + u, e.tag, __uint_as_float(bits));
+      }
+    } else {
+      for (int t = threadIdx.x; t < p.np; t += PT) {   // rows (2f, 2f+1) = (gate f, up f)
+        const int f = p.p0 + p.ps * t;
+        const float v0 = ores[2 * t], v1 = ores[2 * t + 1];
+        const float hv = v0 / (1.0f + expf(-v0)) * v1;
+        if (e.ch) store_act(e.ch, f, hv, d.act);
+        put_tag(e.th + f, e.tag, hv);
+      }
     }
   } else {
     for (int u = threadIdx.x; u < 2 * p.np; u += PT) {   // rows visited in increasing order
@@ -450,6 +480,17 @@ template <int WFMT>
 __device__ __forceinline__ void consume_group(const PPhase& p, int c0, int total, const WBuf& b, const float4* x4,
                                               Cursor& cu, float* ores) {
   const int wave = wave_id(), lane = threadIdx.x & 63;
+  if (c0 >= total) {   // a pad group (wave-uniform): its registers are read, nothing else
+    // (the scales in the form the products use, so that no conversion of them is placed
+    // next to their loads)
+#pragma unroll
+    for (int s = 0; s < GRP; s++) {
+      settle(b.w[s]);
+      if constexpr (WFMT == W_Q8_0) settle(f16_to_f32((uint16_t)b.sc[s]));
+      else if constexpr (WFMT == W_INT8_ROW) settle(__uint_as_float(b.sc[s]));
+    }
+    return;
+  }
   constexpr int XQ = WFMT == W_BF16 ? 2 : 4;   // float4 of input per lane and line
   // both steps' input chunks first, so their LDS round trips overlap (a pad step reads some
   // chunk below cpr)
@@ -561,6 +602,21 @@ template <int VEC>
 __device__ __forceinline__ void stage_plain(const void* src, int act, int K, float* xs) {
   zero_tail<VEC>(K, xs);
   for (int i = threadIdx.x; i < K; i += PT) xs[swz<VEC>(i)] = load_act(src, i, act);
+}
+
+// tagged words carrying two bf16 values each (low half, high half) into LDS, swizzled;
+// pos(w, i0, i1) gives the two element indices of word w (-1: none)
+template <int VEC, int B = 8, typename Pos>
+__device__ __forceinline__ void stage_tagged_pairs(const uint64_t* src, uint32_t tag, int nwords, int K, float* xs,
+                                                   int32_t* err, int* fail, Pos pos) {
+  zero_tail<VEC>(K, xs);
+  gather<B>(nwords, tag, err, fail, [&](int w) { return src + w; }, [&](int w, float v) {
+    const uint32_t b = __float_as_uint(v);
+    int i0, i1;
+    pos(w, i0, i1);
+    if (i0 >= 0) xs[swz<VEC>(i0)] = __uint_as_float(b << 16);
+    if (i1 >= 0) xs[swz<VEC>(i1)] = __uint_as_float(b & 0xffff0000u);
+  });
 }
 
 // tagged vector into LDS, swizzled
@@ -1016,7 +1072,23 @@ __global__ __launch_bounds__(PT) void k_step(PersistArgs a) {
     } else {
       // the attention output (O) or the SwiGLU output (down), as produced
       const bool is_o = k == PH_O;
-      stage_tagged<VEC>(is_o ? a.t_o : a.t_h, T(l, is_o ? TG_O : TG_H), is_o ? d.q_dim : d.F, xs, err, &sfail);
+      if (d.act == ACT_BF16) {   // two values per word
+        if (is_o) {
+          stage_tagged_pairs<VEC>(a.t_o, T(l, TG_O), d.q_dim >> 1, d.q_dim, xs, err, &sfail,
+                                  [](int w, int& i0, int& i1) { i0 = 2 * w; i1 = 2 * w + 1; });
+        } else {
+          const int hs = h_words_per_wg(d.F, nwg);
+          stage_tagged_pairs<VEC>(a.t_h, T(l, TG_H), nwg * hs, d.F, xs, err, &sfail,
+                                  [&](int w, int& i0, int& i1) {
+                                    const int gp = w / hs, u = w - gp * hs;
+                                    const int np = gp < d.F ? (d.F - 1 - gp) / nwg + 1 : 0;
+                                    i0 = 2 * u < np ? gp + nwg * 2 * u : -1;
+                                    i1 = 2 * u + 1 < np ? gp + nwg * (2 * u + 1) : -1;
+                                  });
+        }
+      } else {
+        stage_tagged<VEC>(is_o ? a.t_o : a.t_h, T(l, is_o ? TG_O : TG_H), is_o ? d.q_dim : d.F, xs, err, &sfail);
+      }
       __syncthreads();
       if (sfail) return;
       if (probe) stage_plain<VEC>(inj(l, is_o ? a.po.o : a.po.h), d.act, is_o ? d.q_dim : d.F, xs);
@@ -1057,6 +1129,7 @@ __global__ __launch_bounds__(PT) void k_step(PersistArgs a) {
     } else if (k == PH_GU) {
       e.tag = T(l, TG_H);
       e.th = a.t_h;
+      e.hs = h_words_per_wg(d.F, nwg);
       e.ch = probe ? cap(l, a.po.h) : nullptr;
       phase_epilogue<EPI_SWIGLU>(d, ph, ores, e);
     } else {
@@ -1102,23 +1175,22 @@ __global__ __launch_bounds__(PT) void k_step(PersistArgs a) {
         if (l == 5) PTRACE(401);
       }
       PTRACE(tb + 3);
+      // the O projection's first weight groups, on their way during the merge (a merging
+      // workgroup would otherwise be the last to start O, and every workgroup waits for its rows)
+      nx = make_phase<WFMT>(cmat(&Ly->o), g, nwg);
+      ic = ICur{0, 0, 0};
+      issue_group<WFMT>(nx, ic, pre);
+      issue_group<WFMT>(nx, ic, preb);
       // Merge: the workgroup that ran a head group's last chunk combines its chunks, after all
-      // of its own items (so no workgroup waits on one that is itself waiting).  The chunk
-      // vectors of a thread's first output are loaded before the (m, l) words are gathered, so
-      // the two round trips overlap.
+      // of its own items (so no workgroup waits on one that is itself waiting).  Its chunk
+      // words are loaded only after the (m, l) words of every chunk have arrived: loaded
+      // earlier, words of chunks still running would be re-polled one by one.
       for (int it = g; it < items; it += nwg) {
         const int j = it / nv, c = it - j * nv;
         if (c != nv - 1) continue;
         float* ml = smem;                 // [G][nv][2]: (m, l), then (weight, l)
         float* Ls = smem + 2 * G * nv;    // [G] sum of weighted l
-        constexpr int MB = 16;            // chunk words per thread in flight
-        uint64_t w[MB];                   // first batch: chunks [0, MB) of output tid
-        {
-          const int oi0 = tid < G * hd ? tid : 0;
-          const uint64_t* P0 = a.t_part + (size_t)(j * G + oi0 / hd) * a.nch * cs + (oi0 - (oi0 / hd) * hd);
-#pragma unroll
-          for (int u = 0; u < MB; u++) w[u] = u < nv ? get_word(P0 + (size_t)u * cs) : 0;
-        }
+        constexpr int MB = 8;             // chunk words per thread in flight
         __syncthreads();
         gather(G * nv * 2, tpart, err, &sfail,
                [&](int t) {
@@ -1143,36 +1215,37 @@ __global__ __launch_bounds__(PT) void k_step(PersistArgs a) {
           if (lane == 0) Ls[gg] = L;
         }
         __syncthreads();
+        if (l == 5) PTRACE(409);
         for (int oi = tid; oi < G * hd; oi += PT) {
           const int gg = oi / hd, i = oi - gg * hd, h = j * G + gg;
           const uint64_t* P = a.t_part + (size_t)h * a.nch * cs + i;
           float acc = 0.f;
           for (int c0 = 0; c0 < nv; c0 += MB) {
-            if (oi != tid || c0 != 0) {
+            uint64_t w[MB];
 #pragma unroll
-              for (int u = 0; u < MB; u++) w[u] = c0 + u < nv ? get_word(P + (size_t)(c0 + u) * cs) : 0;
-            }
+            for (int u = 0; u < MB; u++) w[u] = c0 + u < nv ? get_word(P + (size_t)(c0 + u) * cs) : (uint64_t)tpart << 32;
+            await_tags<MB>(w, tpart, err, &sfail, [&](int u) { return get_word(P + (size_t)(c0 + u) * cs); });
 #pragma unroll
             for (int u = 0; u < MB; u++)
-              if (c0 + u < nv)
-                acc += ml[(gg * nv + c0 + u) * 2] * tag_value(P + (size_t)(c0 + u) * cs, w[u], tpart, err, &sfail);
+              if (c0 + u < nv) acc += ml[(gg * nv + c0 + u) * 2] * __uint_as_float((uint32_t)w[u]);
 #pragma unroll
             for (int u = 0; u < MB; u++) settle(w[u]);
           }
           const float o = acc / Ls[gg];
           if (probe) store_act(cap(l, a.po.o), (size_t)h * hd + i, o, d.act);
-          put_tag(a.t_o + h * hd + i, T(l, TG_O), round_act(o, d.act));
+          if (d.act == ACT_BF16) {   // outputs 2w, 2w + 1 share word w (G*hd is even: both lanes are here)
+            const uint32_t mine = f32_to_bf16(o);
+            const uint32_t other = (uint32_t)__shfl_xor((int)mine, 1, 64);
+            if ((oi & 1) == 0) put_tag(a.t_o + ((h * hd + i) >> 1), T(l, TG_O), __uint_as_float(mine | (other << 16)));
+          } else {
+            put_tag(a.t_o + h * hd + i, T(l, TG_O), o);
+          }
         }
-#pragma unroll
-        for (int u = 0; u < MB; u++) settle(w[u]);
+        if (l == 5) PTRACE(410);
         __syncthreads();
+        if (l == 5) PTRACE(411);
         if (sfail) return;
       }
-      // the O projection's first weight groups
-      nx = make_phase<WFMT>(cmat(&Ly->o), g, nwg);
-      ic = ICur{0, 0, 0};
-      issue_group<WFMT>(nx, ic, pre);
-      issue_group<WFMT>(nx, ic, preb);
       __syncthreads();
     }
     ph = nx;
