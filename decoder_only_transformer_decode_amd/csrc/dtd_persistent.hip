@@ -800,9 +800,13 @@ __device__ __forceinline__ void kv_store(const Dims& d, const KvRegs<KVFMT>& r, 
   }
 }
 
+// partial products of the MFMA tile, per group of 4 heads: scores [4 waves][64 lanes][4],
+// then P V [4 row quarters][2 halves][64][4]
+__host__ __device__ inline size_t attn_red_floats(int G) { return (size_t)(G + 3) / 4 * (4 * 2 * 64 * 4); }
+
 __host__ __device__ inline size_t attn_p_floats(int G, int hd) {
   return (size_t)G * hd + 2 * (size_t)kAttnTile * kv_ld(hd) + (size_t)G * kAttnTile + (size_t)G * 4 +
-         2 * (size_t)hd + 2 * (size_t)kAttnTile + PW;
+         2 * (size_t)hd + 2 * (size_t)kAttnTile + PW + attn_red_floats(G);
 }
 
 // One item; all threads call it.  kr holds the item's first tile (issued by the caller).
@@ -823,6 +827,7 @@ __device__ __forceinline__ void attn_item_p(const Dims& d, const KvLayer& kv, co
   float* ks_s = new_s + 2 * hd;             // [64] int8 row scales of K
   float* vs_s = ks_s + kAttnTile;           // [64] and of V
   float* red = vs_s + kAttnTile;            // [PW]
+  float* mred = red + PW;                   // [attn_red_floats(G)] MFMA partials
 
   const float scale = 1.0f / sqrtf((float)hd);
   for (int e = tid; e < G * hd; e += PT) q_s[e] = qg[e] * scale;
@@ -846,25 +851,41 @@ __device__ __forceinline__ void attn_item_p(const Dims& d, const KvLayer& kv, co
     if (t0 + kAttnTile < t_end) kv_issue<KVFMT>(d, kv, bt_s, j, t0 + kAttnTile, min(kAttnTile, t_end - t0 - kAttnTile), kr);
     __syncthreads();
     ITRACE(404);
-    // scores and softmax: wave w takes heads w, w + PW, ...; lane t is tile row t, whose
-    // key it reads as float4s against the (broadcast) query; the wave then holds the head's
-    // 64 scores, one per lane, and reduces them with DPP
+    // Scores on the matrix cores, heads in groups of 4: one v_mfma_f32_4x4x1f32 multiplies,
+    // for one head dimension d, the 64 tile rows (A: lane t holds k[t][d]) by 4 queries (B:
+    // lane t holds q[4 hg + t % 4][d], 0 past the last head); lane t then holds
+    // S[4(t/4) + r][4 hg + t % 4] in its r-th result.  Waves 0-3 each run a quarter of the
+    // head dimensions; their partial results meet in LDS.
+    typedef float f4v __attribute__((ext_vector_type(4)));
+    const int nhg = (G + 3) >> 2;
+    if (wave < 4) {
+      const int d0 = wave * (hd >> 2), d1 = d0 + (hd >> 2);
+      const float* kr_ = tk + lane * ldk;
+      for (int hg = 0; hg < nhg; hg++) {
+        const int gq = 4 * hg + (lane & 3);
+        const bool qok = gq < G;
+        const float* qr_ = q_s + (qok ? gq : 0) * hd;
+        f4v sacc = {0.f, 0.f, 0.f, 0.f};
+        for (int dd = d0; dd < d1; dd += 4) {
+          const float4 ka = *(const float4*)(kr_ + dd);
+          const float4 q4 = *(const float4*)(qr_ + dd);
+          const float4 qa = qok ? q4 : make_float4(0.f, 0.f, 0.f, 0.f);
+          sacc = __builtin_amdgcn_mfma_f32_4x4x1f32(ka.x, qa.x, sacc, 0, 0, 0);
+          sacc = __builtin_amdgcn_mfma_f32_4x4x1f32(ka.y, qa.y, sacc, 0, 0, 0);
+          sacc = __builtin_amdgcn_mfma_f32_4x4x1f32(ka.z, qa.z, sacc, 0, 0, 0);
+          sacc = __builtin_amdgcn_mfma_f32_4x4x1f32(ka.w, qa.w, sacc, 0, 0, 0);
+        }
+        *(float4*)(mred + ((hg * 4 + wave) * 64 + lane) * 4) = make_float4(sacc[0], sacc[1], sacc[2], sacc[3]);
+      }
+    }
+    __syncthreads();
+    // softmax: wave w takes heads w, w + PW, ...; lane t is tile row t, its score the sum of
+    // the 4 partials
     for (int g = wave; g < G; g += PW) {
-      const float4* kq = (const float4*)(tk + lane * ldk);
-      const float4* qq = (const float4*)(q_s + g * hd);
-      const int hd4 = hd >> 2;
-      float s0 = 0.f, s1 = 0.f;
-      int c4 = 0;
-      for (; c4 + 1 < hd4; c4 += 2) {
-        const float4 ka = kq[c4], kb = kq[c4 + 1], qa = qq[c4], qb = qq[c4 + 1];
-        s0 = fmaf(ka.x, qa.x, s0); s0 = fmaf(ka.y, qa.y, s0); s0 = fmaf(ka.z, qa.z, s0); s0 = fmaf(ka.w, qa.w, s0);
-        s1 = fmaf(kb.x, qb.x, s1); s1 = fmaf(kb.y, qb.y, s1); s1 = fmaf(kb.z, qb.z, s1); s1 = fmaf(kb.w, qb.w, s1);
-      }
-      if (c4 < hd4) {
-        const float4 ka = kq[c4], qa = qq[c4];
-        s0 = fmaf(ka.x, qa.x, s0); s0 = fmaf(ka.y, qa.y, s0); s0 = fmaf(ka.z, qa.z, s0); s0 = fmaf(ka.w, qa.w, s0);
-      }
-      const float sc = lane < n ? s0 + s1 : -INFINITY;
+      const float* mr = mred + (g >> 2) * 1024;
+      const int src = (4 * (lane >> 2) + (g & 3)) * 4 + (lane & 3);
+      const float raw = mr[src] + mr[256 + src] + mr[512 + src] + mr[768 + src];
+      const float sc = lane < n ? raw : -INFINITY;
       const float mt = wave_top(sc);
       const float mo = st_s[g * 4], lo = st_s[g * 4 + 1];
       const float mn = fmaxf(mo, mt);
@@ -880,24 +901,46 @@ __device__ __forceinline__ void attn_item_p(const Dims& d, const KvLayer& kv, co
     }
     __syncthreads();
     ITRACE(405);
-    // P V: output (g, i) over the 64 tile rows (rows past n have p = 0 and v = 0)
+    // P V on the matrix cores, per group of 4 heads: one MFMA per tile row t multiplies 64
+    // head dimensions (A: lane holds v[t][64 half + lane]) by 4 probabilities (B: lane holds
+    // p[4 hg + lane % 4][t]); lane l then holds O[64 half + 4(l/4) + r][4 hg + l % 4].  Wave w
+    // takes half w % 2 and rows 16 (w/2) .. +16; the 4 row quarters meet in LDS.
+    {
+      const int half = wave & 1, qt = wave >> 1;
+      const int col = 64 * half + lane;
+      const bool in = col < hd;
+      for (int hg = 0; hg < nhg; hg++) {
+        const int gp = 4 * hg + (lane & 3);
+        const bool pok = gp < G;
+        f4v oacc = {0.f, 0.f, 0.f, 0.f};
+        if (64 * half < hd) {
+          const float* pq = p_s + (pok ? gp : 0) * kAttnTile + 16 * qt;
+          for (int t4 = 0; t4 < 16; t4 += 4) {
+            const float4 p4 = *(const float4*)(pq + t4);
+            const float4 pp = pok ? p4 : make_float4(0.f, 0.f, 0.f, 0.f);
+            const float* vr = tv + (16 * qt + t4) * ldk + (in ? col : 0);
+            oacc = __builtin_amdgcn_mfma_f32_4x4x1f32(in ? vr[0] : 0.f, pp.x, oacc, 0, 0, 0);
+            oacc = __builtin_amdgcn_mfma_f32_4x4x1f32(in ? vr[ldk] : 0.f, pp.y, oacc, 0, 0, 0);
+            oacc = __builtin_amdgcn_mfma_f32_4x4x1f32(in ? vr[2 * ldk] : 0.f, pp.z, oacc, 0, 0, 0);
+            oacc = __builtin_amdgcn_mfma_f32_4x4x1f32(in ? vr[3 * ldk] : 0.f, pp.w, oacc, 0, 0, 0);
+          }
+        }
+        if (hg == 0) __syncthreads();   // the score partials are no longer read
+        *(float4*)(mred + (hg * 2048) + ((qt * 2 + half) * 64 + lane) * 4) =
+            make_float4(oacc[0], oacc[1], oacc[2], oacc[3]);
+      }
+    }
+    __syncthreads();
 #pragma unroll
     for (int k = 0; k < kAttnOut; k++) {
       const int oi = tid + k * PT;
       if (oi < G * hd) {
         const int g = oi / hd, i = oi - g * hd;
-        const float4* pg = (const float4*)(p_s + g * kAttnTile);
-        float s0 = 0.f, s1 = 0.f;
-#pragma unroll 2
-        for (int t4 = 0; t4 < kAttnTile / 4; t4 += 2) {
-          const float4 pa = pg[t4], pb = pg[t4 + 1];
-          const float* vr = tv + (4 * t4) * ldk + i;
-          s0 = fmaf(pa.x, vr[0], s0); s0 = fmaf(pa.y, vr[ldk], s0);
-          s0 = fmaf(pa.z, vr[2 * ldk], s0); s0 = fmaf(pa.w, vr[3 * ldk], s0);
-          s1 = fmaf(pb.x, vr[4 * ldk], s1); s1 = fmaf(pb.y, vr[5 * ldk], s1);
-          s1 = fmaf(pb.z, vr[6 * ldk], s1); s1 = fmaf(pb.w, vr[7 * ldk], s1);
-        }
-        acc[k] = acc[k] * st_s[g * 4 + 2] + (s0 + s1);
+        const int hf = i >> 6, ii = i & 63;
+        const float* mr = mred + (g >> 2) * 2048;
+        const int src = (hf * 64 + 4 * (ii >> 2) + (g & 3)) * 4 + (ii & 3);
+        const float sum = mr[src] + mr[512 + src] + mr[1024 + src] + mr[1536 + src];
+        acc[k] = acc[k] * st_s[g * 4 + 2] + sum;
       }
     }
   }
@@ -1347,7 +1390,7 @@ size_t persistent_smem_bytes(const Dims& d, int nch, int nwg) {
 
 bool persistent_supports(const Dims& d) {
   const int eb = d.kvfmt == KV_F32 ? 4 : (d.kvfmt == KV_BF16 ? 2 : 1);
-  return d.D <= kNormPer * PT && d.hd <= 128 && (d.hd * eb) % 16 == 0 &&
+  return d.D <= kNormPer * PT && d.hd <= 128 && (d.hd * eb) % 16 == 0 && d.hd % 16 == 0 &&
          (size_t)d.G * d.hd <= (size_t)kAttnOut * PT;
 }
 
