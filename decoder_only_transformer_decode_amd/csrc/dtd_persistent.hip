@@ -1194,7 +1194,7 @@ __global__ __launch_bounds__(PT) void k_step(PersistArgs a) {
         // the item's first KV tile is on its way while q, k, v are awaited
         kv_issue<KVFMT>(d, lkv, bt_s, j, t0, min(kAttnTile, min(pos + 1, t0 + a.ct) - t0), kr);
         __syncthreads();
-        gather(nin, T(l, TG_QKV), err, &sfail,
+        gather<2>(nin, T(l, TG_QKV), err, &sfail,
                [&](int t) {
                  return t < G * hd ? a.t_q + j * G * hd + t
                                    : t < G * hd + hd ? a.t_k + j * hd + (t - G * hd)
@@ -1224,70 +1224,79 @@ __global__ __launch_bounds__(PT) void k_step(PersistArgs a) {
       ic = ICur{0, 0, 0};
       issue_group<WFMT>(nx, ic, pre);
       issue_group<WFMT>(nx, ic, preb);
-      // Merge: the workgroup that ran a head group's last chunk combines its chunks, after all
-      // of its own items (so no workgroup waits on one that is itself waiting).  Its chunk
-      // words are loaded only after the (m, l) words of every chunk have arrived: loaded
-      // earlier, words of chunks still running would be re-polled one by one.
+      // Merge: q head h = j G + gh is combined by the workgroup that ran chunk
+      // nv - 1 - (gh mod nv) of head group j, after all of its own items (so no workgroup waits
+      // on one that is itself waiting), and the G heads of a group merge in parallel.  Output
+      // dimension i gets PT / hd threads, each over every (PT / hd)-th chunk.
       for (int it = g; it < items; it += nwg) {
         const int j = it / nv, c = it - j * nv;
-        if (c != nv - 1) continue;
-        float* ml = smem;                 // [G][nv][2]: (m, l), then (weight, l)
-        float* Ls = smem + 2 * G * nv;    // [G] sum of weighted l
-        constexpr int MB = 8;             // chunk words per thread in flight
-        __syncthreads();
-        gather(G * nv * 2, tpart, err, &sfail,
-               [&](int t) {
-                 const int gg = t / (2 * nv), r = t - gg * 2 * nv;
-                 return a.t_part + ((size_t)(j * G + gg) * a.nch + (r >> 1)) * cs + hd + (r & 1);
-               },
-               [&](int t, float v) { ml[t] = v; });
-        __syncthreads();
-        if (sfail) return;
-        if (l == 5) PTRACE(402);
-        for (int gg = wave; gg < G; gg += PW) {   // weights e^(m_c - M) and their l sum
-          float M = -INFINITY;
-          for (int cc = lane; cc < nv; cc += 64) M = fmaxf(M, ml[(gg * nv + cc) * 2]);
-          M = wave_top(M);
-          float L = 0.f;
-          for (int cc = lane; cc < nv; cc += 64) {
-            const float wt = expf(ml[(gg * nv + cc) * 2] - M);
-            ml[(gg * nv + cc) * 2] = wt;
-            L += wt * ml[(gg * nv + cc) * 2 + 1];
+        for (int gh = nv - 1 - c; gh < G; gh += nv) {
+          const int h = j * G + gh;
+          const uint64_t* PH = a.t_part + (size_t)h * a.nch * cs;   // chunk cc at PH + cc cs
+          const int NP = PT / hd, i = tid % hd, part = tid / hd;
+          float* ml = smem;                   // [nv][2]: (m, l), then (weight, l)
+          float* psum = smem + 2 * nv;        // [NP][hd] partial sums
+          float* Lsum = psum + NP * hd;       // [1]
+          constexpr int MB = 8;
+          __syncthreads();
+          gather<1>(2 * nv, tpart, err, &sfail, [&](int t) { return PH + (size_t)(t >> 1) * cs + hd + (t & 1); },
+                 [&](int t, float v) { ml[t] = v; });
+          __syncthreads();
+          if (sfail) return;
+          if (l == 5) PTRACE(402);
+          if (wave == 0) {   // weights e^(m_c - M) and their l sum
+            float M = -INFINITY;
+            for (int cc = lane; cc < nv; cc += 64) M = fmaxf(M, ml[cc * 2]);
+            M = wave_top(M);
+            float L = 0.f;
+            for (int cc = lane; cc < nv; cc += 64) {
+              const float wt = expf(ml[cc * 2] - M);
+              ml[cc * 2] = wt;
+              L += wt * ml[cc * 2 + 1];
+            }
+            L = wave_total(L);
+            if (lane == 0) Lsum[0] = L;
           }
-          L = wave_total(L);
-          if (lane == 0) Ls[gg] = L;
-        }
-        __syncthreads();
-        if (l == 5) PTRACE(409);
-        for (int oi = tid; oi < G * hd; oi += PT) {
-          const int gg = oi / hd, i = oi - gg * hd, h = j * G + gg;
-          const uint64_t* P = a.t_part + (size_t)h * a.nch * cs + i;
+          __syncthreads();
+          if (l == 5) PTRACE(409);
           float acc = 0.f;
-          for (int c0 = 0; c0 < nv; c0 += MB) {
+          for (int c0 = 0; c0 < nv; c0 += MB * NP) {
             uint64_t w[MB];
 #pragma unroll
-            for (int u = 0; u < MB; u++) w[u] = c0 + u < nv ? get_word(P + (size_t)(c0 + u) * cs) : (uint64_t)tpart << 32;
-            await_tags<MB>(w, tpart, err, &sfail, [&](int u) { return get_word(P + (size_t)(c0 + u) * cs); });
+            for (int u = 0; u < MB; u++) {
+              const int cc = c0 + part + u * NP;
+              w[u] = part < NP && cc < nv ? get_word(PH + (size_t)cc * cs + i) : (uint64_t)tpart << 32;
+            }
+            await_tags<MB>(w, tpart, err, &sfail,
+                           [&](int u) { return get_word(PH + (size_t)(c0 + part + u * NP) * cs + i); });
 #pragma unroll
-            for (int u = 0; u < MB; u++)
-              if (c0 + u < nv) acc += ml[(gg * nv + c0 + u) * 2] * __uint_as_float((uint32_t)w[u]);
+            for (int u = 0; u < MB; u++) {
+              const int cc = c0 + part + u * NP;
+              if (part < NP && cc < nv) acc += ml[cc * 2] * __uint_as_float((uint32_t)w[u]);
+            }
 #pragma unroll
             for (int u = 0; u < MB; u++) settle(w[u]);
           }
-          const float o = acc / Ls[gg];
-          if (probe) store_act(cap(l, a.po.o), (size_t)h * hd + i, o, d.act);
-          if (d.act == ACT_BF16) {   // outputs 2w, 2w + 1 share word w (G*hd is even: both lanes are here)
-            const uint32_t mine = f32_to_bf16(o);
-            const uint32_t other = (uint32_t)__shfl_xor((int)mine, 1, 64);
-            if ((oi & 1) == 0) put_tag(a.t_o + ((h * hd + i) >> 1), T(l, TG_O), __uint_as_float(mine | (other << 16)));
-          } else {
-            put_tag(a.t_o + h * hd + i, T(l, TG_O), o);
+          if (part < NP) psum[part * hd + i] = acc;
+          __syncthreads();
+          if (sfail) return;
+          if (tid < hd) {
+            float sum = 0.f;
+            for (int pp = 0; pp < NP; pp++) sum += psum[pp * hd + tid];
+            const float o = sum / Lsum[0];
+            if (probe) store_act(cap(l, a.po.o), (size_t)h * hd + tid, o, d.act);
+            if (d.act == ACT_BF16) {   // outputs 2w, 2w + 1 share word w (hd is even)
+              const uint32_t mine = f32_to_bf16(o);
+              const uint32_t other = (uint32_t)__shfl_xor((int)mine, 1, 64);
+              if ((tid & 1) == 0) put_tag(a.t_o + ((h * hd + tid) >> 1), T(l, TG_O), __uint_as_float(mine | (other << 16)));
+            } else {
+              put_tag(a.t_o + h * hd + tid, T(l, TG_O), o);
+            }
           }
+          if (l == 5) PTRACE(410);
+          __syncthreads();
+          if (l == 5) PTRACE(411);
         }
-        if (l == 5) PTRACE(410);
-        __syncthreads();
-        if (l == 5) PTRACE(411);
-        if (sfail) return;
       }
       __syncthreads();
     }
