@@ -128,8 +128,8 @@ struct PersistArgs {
 };
 
 // Packed hand-off of the SwiGLU output with bf16 activations: each workgroup of the step
-// kernel writes this many words (two values each) of its F-row share, pads included.
-__host__ __device__ inline int h_words_per_wg(int F, int nwg) { return ((F + nwg - 1) / nwg + 1) / 2; }
+// kernel writes this many words (three values each) of its F-row share, pads included.
+__host__ __device__ inline int h_words_per_wg(int F, int nwg) { return ((F + nwg - 1) / nwg + 2) / 3; }
 // words of the SwiGLU output's hand-off buffer (either layout)
 inline size_t h_buffer_words(int F, int nwg) {
   const size_t packed = (size_t)nwg * h_words_per_wg(F, nwg);

@@ -119,6 +119,10 @@ __device__ __forceinline__ void put_tag(uint64_t* p, uint32_t tag, float v) {
                      __HIP_MEMORY_SCOPE_AGENT);
 }
 
+__device__ __forceinline__ void put_word(uint64_t* p, uint64_t w) {
+  __hip_atomic_store((gword*)p, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 __device__ __forceinline__ uint64_t get_word(const uint64_t* p) {
   return __hip_atomic_load((gword*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -129,13 +133,16 @@ __device__ __forceinline__ uint64_t get_word(const uint64_t* p) {
 // kErrBarrier and the workgroup's LDS fail flag) after kSpinLimit rounds, or as soon as
 // another thread or workgroup has given up, so every wait ends; the caller synchronises the
 // workgroup and then tests the fail flag.
-template <int B, typename Load>
+//
+// SHIFT is the position of the tag in a word: 32 (value in the low half), or 48 for words
+// that carry three bf16 values under a 16-bit tag.
+template <int B, int SHIFT = 32, typename Load>
 __device__ __forceinline__ void await_tags(uint64_t (&w)[B], uint32_t tag, int32_t* err, int* fail, Load load) {
   unsigned spins = 0;
   for (;;) {
     bool all = true;
 #pragma unroll
-    for (int k = 0; k < B; k++) all = all && (uint32_t)(w[k] >> 32) == tag;
+    for (int k = 0; k < B; k++) all = all && (uint32_t)(w[k] >> SHIFT) == tag;
     if (all || *(volatile int*)fail) return;
     ++spins;
     if (spins > kSpinLimit ||
@@ -148,31 +155,40 @@ __device__ __forceinline__ void await_tags(uint64_t (&w)[B], uint32_t tag, int32
     __builtin_amdgcn_s_sleep(2);
 #pragma unroll
     for (int k = 0; k < B; k++)
-      if ((uint32_t)(w[k] >> 32) != tag) w[k] = load(k);
+      if ((uint32_t)(w[k] >> SHIFT) != tag) w[k] = load(k);
   }
 }
 
 // Reads n tagged words, word i at src(i), handing each value to put(i, v).  Every thread
 // of the workgroup takes part with up to B loads in flight.  The caller synchronises the
 // workgroup and then tests the fail flag.
-template <int B = 8, typename Src, typename Put>
-__device__ __forceinline__ void gather(int n, uint32_t tag, int32_t* err, int* fail, Src src, Put put) {
+// Reads n tagged words, word i at src(i), handing each whole word to put(i, w).  Every
+// thread of the workgroup takes part with up to B loads in flight.  The caller synchronises
+// the workgroup and then tests the fail flag.
+template <int B, int SHIFT, typename Src, typename Put>
+__device__ __forceinline__ void gather_words(int n, uint32_t tag, int32_t* err, int* fail, Src src, Put put) {
   for (int i0 = 0; i0 < n; i0 += B * PT) {
     uint64_t w[B];
 #pragma unroll
     for (int k = 0; k < B; k++) {
       const int i = i0 + k * PT + (int)threadIdx.x;
-      w[k] = i < n ? get_word(src(i)) : (uint64_t)tag << 32;
+      w[k] = i < n ? get_word(src(i)) : (uint64_t)tag << SHIFT;
     }
-    await_tags<B>(w, tag, err, fail, [&](int k) { return get_word(src(i0 + k * PT + (int)threadIdx.x)); });
+    await_tags<B, SHIFT>(w, tag, err, fail, [&](int k) { return get_word(src(i0 + k * PT + (int)threadIdx.x)); });
 #pragma unroll
     for (int k = 0; k < B; k++) {
       const int i = i0 + k * PT + (int)threadIdx.x;
-      if (i < n) put(i, __uint_as_float((uint32_t)w[k]));
+      if (i < n) put(i, w[k]);
     }
 #pragma unroll
     for (int k = 0; k < B; k++) settle(w[k]);
   }
+}
+
+// the same, handing each word's value (low 32 bits) as a float
+template <int B = 8, typename Src, typename Put>
+__device__ __forceinline__ void gather(int n, uint32_t tag, int32_t* err, int* fail, Src src, Put put) {
+  gather_words<B, 32>(n, tag, err, fail, src, [&](int i, uint64_t w) { put(i, __uint_as_float((uint32_t)w)); });
 }
 
 // ---------------------------------------------------------------------------------------
@@ -362,22 +378,24 @@ __device__ __forceinline__ void phase_epilogue(const Dims& d, const PPhase& p, c
     }
   } else if constexpr (EPI == EPI_SWIGLU) {
     if (d.act == ACT_BF16) {
-      // two outputs per word: word u of this workgroup carries its local pairs 2u, 2u + 1
-      // (low, high half); every one of its hs words is written, pads as zero
+      // three outputs per word under a 16-bit tag: word u of this workgroup carries its local
+      // pairs 3u, 3u + 1, 3u + 2 in bits 0-15, 16-31, 32-47.  Every one of its hs words is
+      // written in every layer, pads as zero, so a stale word is never more than one layer's
+      // tags behind and a 16-bit tag cannot be mistaken.
       for (int u = threadIdx.x; u < e.hs; u += PT) {
-        uint32_t bits = 0;
+        uint64_t bits = (uint64_t)(e.tag & 0xffffu) << 48;
 #pragma unroll
-        for (int hh = 0; hh < 2; hh++) {
-          const int t = 2 * u + hh;
+        for (int hh = 0; hh < 3; hh++) {
+          const int t = 3 * u + hh;
           if (t < p.np) {   // rows (2f, 2f+1) = (gate f, up f)
             const int f = p.p0 + p.ps * t;
             const float v0 = ores[2 * t], v1 = ores[2 * t + 1];
             const float hv = v0 / (1.0f + expf(-v0)) * v1;
             if (e.ch) store_act(e.ch, f, hv, d.act);
-            bits |= (uint32_t)f32_to_bf16(hv) << (16 * hh);
+            bits |= (uint64_t)f32_to_bf16(hv) << (16 * hh);
           }
         }
-        put_tag(e.th + (size_t)p.p0 * e.hs + u, e.tag, __uint_as_float(bits));
+        put_word(e.th + (size_t)p.p0 * e.hs + u, bits);
       }
     } else {
       for (int t = threadIdx.x; t < p.np; t += PT) {   // rows (2f, 2f+1) = (gate f, up f)
@@ -578,12 +596,21 @@ __device__ __forceinline__ void gemv_phase(const PPhase& p, const PPhase& nx, WB
   if (ng2 < 2) ng2 = 2;
   const float4* x4 = (const float4*)xs;
   Cursor cu{0, 0, 0.f, 0.f, 1.f, 1.f};
+  // The two waves sharing a SIMD (w and w + 4) take turns at the higher issue priority, one
+  // group each; otherwise the older wave wins every tie and the younger one finishes its
+  // share of the phase well after it.
+  const bool young = wave >= PW / 2;
   for (int gi = 0; gi < ng2; gi += 2) {
+    if (young) __builtin_amdgcn_s_setprio(1);
+    else __builtin_amdgcn_s_setprio(0);
     consume_group<WFMT>(p, gi * GRP, total, A, x4, cu, ores);       // B stays in flight
     issue_seq<WFMT>(p, nx, ng2, gi + 2, A, ic);
+    if (young) __builtin_amdgcn_s_setprio(0);
+    else __builtin_amdgcn_s_setprio(1);
     consume_group<WFMT>(p, (gi + 1) * GRP, total, B, x4, cu, ores); // A stays in flight
     issue_seq<WFMT>(p, nx, ng2, gi + 3, B, ic);
   }
+  __builtin_amdgcn_s_setprio(0);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -1119,15 +1146,20 @@ __global__ __launch_bounds__(PT) void k_step(PersistArgs a) {
         if (is_o) {
           stage_tagged_pairs<VEC>(a.t_o, T(l, TG_O), d.q_dim >> 1, d.q_dim, xs, err, &sfail,
                                   [](int w, int& i0, int& i1) { i0 = 2 * w; i1 = 2 * w + 1; });
-        } else {
+        } else {   // three values per word, 16-bit tag
           const int hs = h_words_per_wg(d.F, nwg);
-          stage_tagged_pairs<VEC>(a.t_h, T(l, TG_H), nwg * hs, d.F, xs, err, &sfail,
-                                  [&](int w, int& i0, int& i1) {
-                                    const int gp = w / hs, u = w - gp * hs;
-                                    const int np = gp < d.F ? (d.F - 1 - gp) / nwg + 1 : 0;
-                                    i0 = 2 * u < np ? gp + nwg * 2 * u : -1;
-                                    i1 = 2 * u + 1 < np ? gp + nwg * (2 * u + 1) : -1;
-                                  });
+          zero_tail<VEC>(d.F, xs);
+          gather_words<8, 48>(nwg * hs, T(l, TG_H) & 0xffffu, err, &sfail, [&](int w) { return a.t_h + w; },
+                              [&](int w, uint64_t word) {
+                                const int gp = w / hs, u = w - gp * hs;
+                                const int np = gp < d.F ? (d.F - 1 - gp) / nwg + 1 : 0;
+#pragma unroll
+                                for (int hh = 0; hh < 3; hh++) {
+                                  const int t = 3 * u + hh;
+                                  if (t < np)
+                                    xs[swz<VEC>(gp + nwg * t)] = __uint_as_float((uint32_t)(word >> (16 * hh)) << 16);
+                                }
+                              });
         }
       } else {
         stage_tagged<VEC>(is_o ? a.t_o : a.t_h, T(l, is_o ? TG_O : TG_H), is_o ? d.q_dim : d.F, xs, err, &sfail);
