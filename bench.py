@@ -57,6 +57,36 @@ def kv_bytes_per_position(s: synth.ModelShape) -> int:
     return per
 
 
+KERNEL_SOURCES = ["decoder_only_transformer_decode_amd/csrc/dtd_persistent.hip",
+                  "decoder_only_transformer_decode_amd/csrc/dtd_device.h",
+                  "decoder_only_transformer_decode_amd/csrc/dtd_internal.h"]
+
+
+def kernel_source_hash() -> str:
+    """sha256 over the step kernel's sources, to tell whether recorded counters still apply"""
+    import hashlib
+    h = hashlib.sha256()
+    root = os.path.dirname(os.path.abspath(__file__))
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(root, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(workload: str):
+    """HBM bytes per step-kernel launch from the committed FETCH_SIZE / WRITE_SIZE readings of
+    this workload (each scaled by what the counter reads for a plain copy of known size), or
+    None when there are none or the kernel's sources have changed since they were taken."""
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", f"k_step_traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        r = json.load(f)
+    if r.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    return (r["fetch_kib_per_launch"] * r["fetch_scale"] + r["write_kib_per_launch"] * r["write_scale"]) * 1024.0
+
+
 def cpu_baseline(w: synth.Workload, weights, ctx_mid: int, n_steps: int) -> dict:
     """The oracle, as it stands, on this host: n_steps decode steps at contexts around the
     middle of the decoded range, from synthetic stored KV."""
@@ -85,6 +115,9 @@ def main():
     ap.add_argument("--cpu-steps", type=int, default=40)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only copy MIB MiB device to device 3 times and exit: the plain copy whose "
+                         "FETCH_SIZE / WRITE_SIZE counter readings scale the step kernel's")
     ap.add_argument("--path", choices=["auto", "per-kernel", "persistent"], default="auto",
                     help="schedule: auto (persistent step kernel at batch 1), or force one")
     args = ap.parse_args()
@@ -94,6 +127,15 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.copy_probe:
+        n = args.copy_probe << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": n, "copies": 3}), flush=True)
+        return
     w = synth.BY_NAME[args.workload]
     s = w.shape
     if w.batch != 1:
@@ -171,8 +213,10 @@ def main():
             name = "k_gemv (gate/up projection, int8-row, SwiGLU epilogue)"
         avg_s = ms / 1e3 / max(cnt, 1)
         ach = per_launch / avg_s / 1e9 if cnt else 0.0
+        traffic = recorded_traffic(s.name) if persistent else None
         roofline = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                    "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None, "kernel": name,
+                    "frac": round(ach / PEAK_HBM_GBS, 4),
+                    "traffic": None if traffic is None else round(traffic), "kernel": name,
                     "bytes_per_launch": round(per_launch), "avg_launch_us": round(avg_s * 1e6, 2),
                     "launches": cnt}
 

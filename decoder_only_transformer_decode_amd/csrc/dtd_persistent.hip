@@ -1148,6 +1148,7 @@ __global__ __launch_bounds__(PT) void k_step(PersistArgs a) {
                                   [](int w, int& i0, int& i1) { i0 = 2 * w; i1 = 2 * w + 1; });
         } else {   // three values per word, 16-bit tag
           const int hs = h_words_per_wg(d.F, nwg);
+          if (l == 5) PTRACE(415);
           zero_tail<VEC>(d.F, xs);
           gather_words<8, 48>(nwg * hs, T(l, TG_H) & 0xffffu, err, &sfail, [&](int w) { return a.t_h + w; },
                               [&](int w, uint64_t word) {
@@ -1160,6 +1161,7 @@ __global__ __launch_bounds__(PT) void k_step(PersistArgs a) {
                                     xs[swz<VEC>(gp + nwg * t)] = __uint_as_float((uint32_t)(word >> (16 * hh)) << 16);
                                 }
                               });
+          if (l == 5) PTRACE(416);
         }
       } else {
         stage_tagged<VEC>(is_o ? a.t_o : a.t_h, T(l, is_o ? TG_O : TG_H), is_o ? d.q_dim : d.F, xs, err, &sfail);
