@@ -36,6 +36,18 @@ __device__ __forceinline__ T gload(const void* p) {
   }
 }
 
+// the same for data read once per step (weights): the nontemporal hint streams the lines
+// through the caches instead of keeping them, which sustains a higher HBM read rate
+template <typename T>
+__device__ __forceinline__ T gload_stream(const void* p) {
+  if constexpr (sizeof(T) == 16) {
+    const gv4u v = __builtin_nontemporal_load((const __attribute__((address_space(1))) gv4u*)p);
+    return __builtin_bit_cast(T, v);
+  } else {
+    return __builtin_nontemporal_load((const __attribute__((address_space(1))) T*)p);
+  }
+}
+
 template <typename T>
 __device__ __forceinline__ void gstore(void* p, T v) {
   *(__attribute__((address_space(1))) T*)p = v;

@@ -19,8 +19,9 @@
 // chain of such waits through every reader of its previous contents, so a reader never
 // meets a later phase's word in place of the one it waits for.
 //
-// Weight streaming: each projection's rows are split into contiguous row-pair ranges per
-// workgroup; within a workgroup, wave w owns pairs w, w+PW, ...  A wave walks its rows in
+// Weight streaming: each projection's row pairs are dealt out to the workgroups; within a
+// workgroup, wave w owns pairs w, w+PW, ... (with fewer pairs than waves, several waves share
+// a pair, each with part of its lines).  A wave walks its rows in
 // 1 KB lines (16 bytes per lane, coalesced) in groups of GRP lines, double buffered in
 // registers: while one group is multiplied against the input vector (held in LDS with a
 // bank-conflict-free swizzle), the next is in flight.  At the end of a projection each wave
@@ -40,7 +41,7 @@ using namespace dev;
 
 constexpr int PW = kPersistWaves;   // waves per workgroup
 constexpr int PT = PW * 64;         // threads per workgroup
-constexpr int GRP = 4;              // lines per lane in one prefetch group
+constexpr int GRP = 2;              // lines per lane in one prefetch group
 constexpr unsigned kSpinLimit = 1u << 20;
 
 // tags of one layer's hand-offs: tag = epoch + layer * kTagsPerLayer + kind; the head's
@@ -64,6 +65,12 @@ __shared__ unsigned long long g_trace_lds[16];
   do {                                                                                     \
     if (threadIdx.x == 0 && (k) < 16) g_trace_lds[(k)] = __builtin_amdgcn_s_memrealtime();   \
   } while (0)
+// a value instead of a time stamp
+#define PTRACE_SET(ev, val)                                                                 \
+  do {                                                                                      \
+    if (threadIdx.x == 0 && blockIdx.x < kTraceWG && (ev) < kTraceEv)                       \
+      g_phase_trace[blockIdx.x * kTraceEv + (ev)] = (val);                                  \
+  } while (0)
 // inside an attention item: only when the caller set the item-trace flag
 #define ITRACE(ev) \
   do {                 \
@@ -72,6 +79,9 @@ __shared__ unsigned long long g_trace_lds[16];
 #else
 #define ITRACE(ev) \
   do {              \
+  } while (0)
+#define PTRACE_SET(ev, val) \
+  do {                      \
   } while (0)
 #define PTRACE(ev) \
   do {             \
@@ -204,17 +214,24 @@ __device__ __forceinline__ int swz(int i) {
   return st * KSTEP + (e >> 2) * 256 + ln * 4 + (e & 3);
 }
 
-// one weight-streaming phase of this workgroup
+// this thread's wave, as a value the compiler knows is wave-uniform (branches on it become
+// scalar branches, and both arms of an if/else are never laid out as one masked sequence)
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
+// one weight-streaming phase of this workgroup, with the share of the calling wave
 struct PPhase {
   const uint8_t* w;
   const uint8_t* s;
-  int N;     // matrix rows
-  int Kb;    // bytes per row
-  int K;     // elements per row
-  int cpr;   // 1 KB lines per row
-  int p0;    // first row pair owned by this workgroup
-  int ps;    // stride between the row pairs it owns
-  int np;    // row pairs owned by this workgroup
+  int N;       // matrix rows
+  int Kb;      // bytes per row
+  int K;       // elements per row
+  int p0;      // first row pair owned by this workgroup
+  int ps;      // stride between the row pairs it owns
+  int np;      // row pairs owned by this workgroup
+  int sp;      // waves sharing each pair, each with a contiguous range of its lines
+  // this wave's share: pairs pb, pb + pst, ...; lines [jb, je) of each; 2 * pairs * (je - jb)
+  // lines in all; the results of its k-th pair go to LDS slots ob + ost * k (+1)
+  int pb, pst, jb, je, total, ob, ost;
 };
 
 template <int WFMT>
@@ -225,7 +242,7 @@ __device__ __forceinline__ PPhase make_phase(const MatDev& m, int g, int nwg) {
   p.N = m.rows;
   p.K = m.cols;
   p.Kb = m.cols * (WFMT == W_BF16 ? 2 : 1);
-  p.cpr = (p.Kb + 1023) >> 10;
+  const int cpr = (p.Kb + 1023) >> 10;   // 1 KB lines per row
   // Row pairs are dealt out round-robin (workgroup g owns pairs g, g + nwg, ...), not in one
   // contiguous slice per workgroup: every hand-off lines all workgroups up at the start of a
   // projection, and with contiguous slices they would then all read the same offset of
@@ -235,26 +252,38 @@ __device__ __forceinline__ PPhase make_phase(const MatDev& m, int g, int nwg) {
   p.p0 = g;
   p.ps = nwg;
   p.np = g < pairs ? (pairs - 1 - g) / nwg + 1 : 0;
+  // With fewer pairs than waves, sp waves share each pair, each taking a contiguous range of
+  // its lines, so that every wave keeps loads in flight; their partial results meet in the
+  // epilogue.
+  int sp = 1;
+  while (2 * sp <= PW && 2 * sp * p.np <= PW && 2 * sp <= cpr) sp *= 2;
+  p.sp = sp;
+  const int ws = PW / sp, wave = wave_id();
+  const int part = wave / ws, wl = wave - part * ws;
+  const int ch = (cpr + sp - 1) / sp;
+  p.jb = min(cpr, part * ch);
+  p.je = min(cpr, p.jb + ch);
+  const int npw = p.np > wl ? (p.np - wl + ws - 1) / ws : 0;
+  p.total = 2 * npw * (p.je - p.jb);
+  p.pb = g + nwg * wl;
+  p.pst = nwg * ws;
+  p.ob = 2 * (part * p.np + wl);
+  p.ost = 2 * ws;
   return p;
 }
 
 // a phase with no rows; its (unused) loads read `any`, a readable global address
 __device__ __forceinline__ PPhase empty_phase(const void* any) {
   PPhase p{};
-  p.cpr = 1;
   p.ps = 1;
+  p.sp = 1;
+  p.je = 1;
+  p.pst = 1;
+  p.ost = 2;
   p.w = p.s = (const uint8_t*)any;
   return p;
 }
 
-// this thread's wave, as a value the compiler knows is wave-uniform (branches on it become
-// scalar branches, and both arms of an if/else are never laid out as one masked sequence)
-__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
-
-// pairs of this wave in the phase
-__device__ __forceinline__ int wave_pairs(const PPhase& p, int wave) {
-  return p.np > wave ? (p.np - wave + PW - 1) / PW : 0;
-}
 
 // The weight stream's loads are issued so that the compiler's wait insertion can count
 // them exactly: every group issues the same loads unconditionally, each buffer has one
@@ -290,21 +319,20 @@ struct ICur {
 // are a uniform base plus a 32-bit offset (a matrix is below 4 GiB).
 template <int WFMT>
 __device__ __forceinline__ void issue_group(const PPhase& p, ICur& ic, WBuf& b) {
-  const int wave = wave_id(), lane = threadIdx.x & 63;
-  const int total = wave_pairs(p, wave) * 2 * p.cpr;
+  const int lane = threadIdx.x & 63;
 #pragma unroll
   for (int s = 0; s < GRP; s++) {
-    const int row = 2 * (p.p0 + p.ps * (wave + PW * ic.k)) + (s & 1);
+    const int row = 2 * (p.pb + p.pst * ic.k) + (s & 1);
     const int cb = (ic.j * 64 + lane) * 16;
-    const bool rok = ic.c + s < total && row < p.N;
+    const bool rok = ic.c + s < p.total && row < p.N;
     const bool ok = rok && cb < p.Kb;
-    b.w[s] = gload<v4u>(p.w + (ok ? (uint32_t)row * (uint32_t)p.Kb + (uint32_t)cb : 0u));
+    b.w[s] = gload_stream<v4u>(p.w + (ok ? (uint32_t)row * (uint32_t)p.Kb + (uint32_t)cb : 0u));
     if constexpr (WFMT == W_Q8_0)
       b.sc[s] = gload<uint16_t>(p.s + (ok ? ((uint32_t)row * (uint32_t)(p.K >> 5) + (uint32_t)(cb >> 5)) * 2u : 0u));
     else if constexpr (WFMT == W_INT8_ROW)
       b.sc[s] = gload<uint32_t>(p.s + (rok ? (uint32_t)row * 4u : 0u));
     if (s & 1) {
-      if (++ic.j == p.cpr) { ic.j = 0; ++ic.k; }
+      if (++ic.j == p.je) { ic.j = p.jb; ++ic.k; }
     }
   }
   ic.c += GRP;
@@ -342,9 +370,16 @@ __device__ __forceinline__ void emit(uint64_t* t, float* c, uint32_t tag, int i,
   put_tag(t + i, tag, v);
 }
 
-// The epilogue of one projection, run by the whole workgroup after its rows are done: the
-// finished dot products of its row pairs are in ores (LDS; local pair t, i.e. global pair
-// p.p0 + p.ps*t, at ores[2t], ores[2t+1]).
+// Result of row r (0 or 1) of local pair t (global pair p.p0 + p.ps*t) of a finished
+// projection: the parts of the waves that shared the pair, added in a fixed order.
+__device__ __forceinline__ float pair_result(const PPhase& p, const float* ores, int t, int r) {
+  float v = ores[2 * t + r];
+  for (int part = 1; part < p.sp; part++) v += ores[2 * (part * p.np + t) + r];
+  return v;
+}
+
+// The epilogue of one projection, run by the whole workgroup after its rows are done (their
+// results in ores, LDS, read through pair_result).
 // Stores happen only here, never inside the streaming loop: gfx950 counts loads and stores
 // on one counter, so a store pending there would make every wait for a weight group also
 // wait for the store's acknowledgement and for the group issued after it.
@@ -355,7 +390,7 @@ __device__ __forceinline__ void phase_epilogue(const Dims& d, const PPhase& p, c
     const int half = d.hd >> 1;
     for (int t = threadIdx.x; t < p.np; t += PT) {
       const int r = 2 * (p.p0 + p.ps * t);
-      const float v0 = ores[2 * t], v1 = ores[2 * t + 1];
+      const float v0 = pair_result(p, ores, t, 0), v1 = pair_result(p, ores, t, 1);
       if (r < d.q_dim + d.kv_dim) {
         const bool isq = r < d.q_dim;
         const int nn = isq ? r : r - d.q_dim;
@@ -374,7 +409,7 @@ __device__ __forceinline__ void phase_epilogue(const Dims& d, const PPhase& p, c
   } else if constexpr (EPI == EPI_RESID) {
     for (int u = threadIdx.x; u < 2 * p.np; u += PT) {
       const int r = 2 * (p.p0 + p.ps * (u >> 1)) + (u & 1);
-      if (r < p.N) emit(e.tout, e.cout, e.tag, r, e.xf[r] + ores[u]);
+      if (r < p.N) emit(e.tout, e.cout, e.tag, r, e.xf[r] + pair_result(p, ores, u >> 1, u & 1));
     }
   } else if constexpr (EPI == EPI_SWIGLU) {
     if (d.act == ACT_BF16) {
@@ -389,7 +424,7 @@ __device__ __forceinline__ void phase_epilogue(const Dims& d, const PPhase& p, c
           const int t = 3 * u + hh;
           if (t < p.np) {   // rows (2f, 2f+1) = (gate f, up f)
             const int f = p.p0 + p.ps * t;
-            const float v0 = ores[2 * t], v1 = ores[2 * t + 1];
+            const float v0 = pair_result(p, ores, t, 0), v1 = pair_result(p, ores, t, 1);
             const float hv = v0 / (1.0f + expf(-v0)) * v1;
             if (e.ch) store_act(e.ch, f, hv, d.act);
             bits |= (uint64_t)f32_to_bf16(hv) << (16 * hh);
@@ -400,7 +435,7 @@ __device__ __forceinline__ void phase_epilogue(const Dims& d, const PPhase& p, c
     } else {
       for (int t = threadIdx.x; t < p.np; t += PT) {   // rows (2f, 2f+1) = (gate f, up f)
         const int f = p.p0 + p.ps * t;
-        const float v0 = ores[2 * t], v1 = ores[2 * t + 1];
+        const float v0 = pair_result(p, ores, t, 0), v1 = pair_result(p, ores, t, 1);
         const float hv = v0 / (1.0f + expf(-v0)) * v1;
         if (e.ch) store_act(e.ch, f, hv, d.act);
         put_tag(e.th + f, e.tag, hv);
@@ -410,7 +445,7 @@ __device__ __forceinline__ void phase_epilogue(const Dims& d, const PPhase& p, c
     for (int u = threadIdx.x; u < 2 * p.np; u += PT) {   // rows visited in increasing order
       const int r = 2 * (p.p0 + p.ps * (u >> 1)) + (u & 1);
       if (r >= p.N) continue;
-      const float v = ores[u];
+      const float v = pair_result(p, ores, u >> 1, u & 1);
       gstore<float>(e.logits + r, v);
       if (e.logits_out) gstore<float>(e.logits_out + r, v);
       if (v > e.best || (e.best_idx == INT_MAX && !isnan(v))) { e.best = v; e.best_idx = r; }
@@ -510,20 +545,23 @@ __device__ __forceinline__ void consume_group(const PPhase& p, int c0, int total
     return;
   }
   constexpr int XQ = WFMT == W_BF16 ? 2 : 4;   // float4 of input per lane and line
-  // both steps' input chunks first, so their LDS round trips overlap (a pad step reads some
+  constexpr int NS = GRP / 2;                  // line steps in a group
+  // all steps' input chunks first, so their LDS round trips overlap (a pad step reads some
   // chunk below cpr)
-  const int j0 = cu.j, j1 = cu.j + 1 == p.cpr ? 0 : cu.j + 1;
-  float4 xa[XQ], xb[XQ];
+  float4 xc[NS][XQ];
+  int jj = cu.j;
 #pragma unroll
-  for (int q = 0; q < XQ; q++) {
-    xa[q] = x4[(j0 * XQ + q) * 64 + lane];
-    xb[q] = x4[(j1 * XQ + q) * 64 + lane];
+  for (int st = 0; st < NS; st++) {
+#pragma unroll
+    for (int q = 0; q < XQ; q++) xc[st][q] = x4[(jj * XQ + q) * 64 + lane];
+    jj = jj + 1 == p.je ? p.jb : jj + 1;
   }
   float part[GRP];
-  part[0] = line_dot<WFMT>(b.w[0], xa);
-  part[1] = line_dot<WFMT>(b.w[1], xa);
-  part[2] = line_dot<WFMT>(b.w[2], xb);
-  part[3] = line_dot<WFMT>(b.w[3], xb);
+#pragma unroll
+  for (int st = 0; st < NS; st++) {
+    part[2 * st] = line_dot<WFMT>(b.w[2 * st], xc[st]);
+    part[2 * st + 1] = line_dot<WFMT>(b.w[2 * st + 1], xc[st]);
+  }
   if constexpr (WFMT == W_Q8_0) {
 #pragma unroll
     for (int s = 0; s < GRP; s++) part[s] *= f16_to_f32((uint16_t)b.sc[s]);
@@ -537,15 +575,15 @@ __device__ __forceinline__ void consume_group(const PPhase& p, int c0, int total
       cu.rsc0 = valid ? __uint_as_float(b.sc[2 * st]) : cu.rsc0;
       cu.rsc1 = valid ? __uint_as_float(b.sc[2 * st + 1]) : cu.rsc1;
     }
-    if (valid && ++cu.j == p.cpr) {
-      cu.j = 0;
+    if (valid && ++cu.j == p.je) {
+      cu.j = p.jb;
       // int8-row: per-row scale after the dot
       const float v0 = wave_total(cu.acc0) * cu.rsc0, v1 = wave_total(cu.acc1) * cu.rsc1;
       cu.acc0 = cu.acc1 = 0.f;
       if (lane == 0) {
-        const int lp = wave + PW * cu.k;   // pair index within this workgroup's range
-        ores[2 * lp] = v0;
-        ores[2 * lp + 1] = v1;
+        const int o = p.ob + p.ost * cu.k;
+        ores[o] = v0;
+        ores[o + 1] = v1;
       }
       ++cu.k;
     }
@@ -560,17 +598,18 @@ __device__ __forceinline__ void consume_group(const PPhase& p, int c0, int total
 template <int WFMT>
 __device__ __forceinline__ void issue_seq(const PPhase& p, const PPhase& nx, int ng2, int gidx, WBuf& b, ICur& ic) {
   const bool in_nx = gidx >= ng2;
-  if (gidx == ng2) ic = ICur{0, 0, 0};
+  if (gidx == ng2) ic = ICur{0, 0, nx.jb};
   PPhase q;
   q.w = in_nx ? nx.w : p.w;
   q.s = in_nx ? nx.s : p.s;
   q.N = in_nx ? nx.N : p.N;
   q.Kb = in_nx ? nx.Kb : p.Kb;
   q.K = in_nx ? nx.K : p.K;
-  q.cpr = in_nx ? nx.cpr : p.cpr;
-  q.p0 = in_nx ? nx.p0 : p.p0;
-  q.ps = in_nx ? nx.ps : p.ps;
-  q.np = in_nx ? nx.np : p.np;
+  q.pb = in_nx ? nx.pb : p.pb;
+  q.pst = in_nx ? nx.pst : p.pst;
+  q.jb = in_nx ? nx.jb : p.jb;
+  q.je = in_nx ? nx.je : p.je;
+  q.total = in_nx ? nx.total : p.total;
   issue_group<WFMT>(q, ic, b);
   // nothing of the following consume may be scheduled above these loads: a product of the
   // group issued just before would then wait for that group before this one is on its way
@@ -591,11 +630,11 @@ template <int WFMT>
 __device__ __forceinline__ void gemv_phase(const PPhase& p, const PPhase& nx, WBuf& A, WBuf& B, const float* xs,
                                            float* ores, ICur& ic) {
   const int wave = wave_id();
-  const int total = wave_pairs(p, wave) * 2 * p.cpr;
+  const int total = p.total;
   int ng2 = ((total + GRP - 1) / GRP + 1) & ~1;
   if (ng2 < 2) ng2 = 2;
   const float4* x4 = (const float4*)xs;
-  Cursor cu{0, 0, 0.f, 0.f, 1.f, 1.f};
+  Cursor cu{0, p.jb, 0.f, 0.f, 1.f, 1.f};
   // The two waves sharing a SIMD (w and w + 4) take turns at the higher issue priority, one
   // group each; otherwise the older wave wins every tie and the younger one finishes its
   // share of the phase well after it.
@@ -1067,7 +1106,7 @@ __global__ __launch_bounds__(PT) void k_step(PersistArgs a) {
   CPLayer* layers = (CPLayer*)a.layers;
   const void* dummy = layers[0].qkv.w;
   PPhase ph = make_phase<WFMT>(cmat(&layers[0].qkv), g, nwg);
-  ICur ic{0, 0, 0};   // issue cursor of phase ph (then of the phase after it)
+  ICur ic{0, 0, ph.jb};   // issue cursor of phase ph (then of the phase after it)
   issue_group<WFMT>(ph, ic, pre);
   issue_group<WFMT>(ph, ic, preb);
   // the sequence's block-table row in LDS with this step's entries applied; workgroup 0
@@ -1185,7 +1224,13 @@ __global__ __launch_bounds__(PT) void k_step(PersistArgs a) {
 #pragma unroll
     for (int i = 0; i < kNormPer; i++) settle(gn[i]);   // no gain load may reach the stream
     gemv_phase<WFMT>(ph, nx, pre, preb, xs, ores, ic);
+#ifdef DTD_PHASE_TRACE
+    if (l == 5 && (k == PH_GU || k == PH_DOWN) && lane == 0)
+      g_phase_trace[g * kTraceEv + 430 + (k == PH_GU ? 0 : 10) + wave] = __builtin_amdgcn_s_memrealtime();
+#endif
     __syncthreads();
+    if (l == 5 && k == PH_GU) PTRACE(438);
+    if (l == 5 && k == PH_DOWN) PTRACE(448);
 
     // ---- epilogue ----
     if (k == PH_QKV) {
@@ -1209,6 +1254,7 @@ __global__ __launch_bounds__(PT) void k_step(PersistArgs a) {
       e.hs = h_words_per_wg(d.F, nwg);
       e.ch = probe ? cap(l, a.po.h) : nullptr;
       phase_epilogue<EPI_SWIGLU>(d, ph, ores, e);
+      if (l == 5) PTRACE(439);
     } else {
       phase_epilogue<EPI_LOGITS>(d, ph, ores, e);
     }
@@ -1255,7 +1301,7 @@ __global__ __launch_bounds__(PT) void k_step(PersistArgs a) {
       // the O projection's first weight groups, on their way during the merge (a merging
       // workgroup would otherwise be the last to start O, and every workgroup waits for its rows)
       nx = make_phase<WFMT>(cmat(&Ly->o), g, nwg);
-      ic = ICur{0, 0, 0};
+      ic = ICur{0, 0, nx.jb};
       issue_group<WFMT>(nx, ic, pre);
       issue_group<WFMT>(nx, ic, preb);
       // Merge: q head h = j G + gh is combined by the workgroup that ran chunk
@@ -1427,8 +1473,9 @@ static size_t rows_per_wg(const Dims& d, int nwg) {
 }
 
 size_t persistent_smem_bytes(const Dims& d, int nch, int nwg) {
-  return (persistent_xs_floats(d, nch) + (size_t)d.D + (size_t)d.max_blocks + rows_per_wg(d, nwg)) *
-         sizeof(float);
+  // result slots: a projection's rows, or 2 per wave when waves share pairs
+  const size_t res = rows_per_wg(d, nwg) > 2 * (size_t)PW ? rows_per_wg(d, nwg) : 2 * (size_t)PW;
+  return (persistent_xs_floats(d, nch) + (size_t)d.D + (size_t)d.max_blocks + res) * sizeof(float);
 }
 
 bool persistent_supports(const Dims& d) {
