@@ -417,20 +417,25 @@ __device__ __forceinline__ void phase_epilogue(const Dims& d, const PPhase& p, c
       // pairs 3u, 3u + 1, 3u + 2 in bits 0-15, 16-31, 32-47.  Every one of its hs words is
       // written in every layer, pads as zero, so a stale word is never more than one layer's
       // tags behind and a 16-bit tag cannot be mistaken.
-      for (int u = threadIdx.x; u < e.hs; u += PT) {
-        uint64_t bits = (uint64_t)(e.tag & 0xffffu) << 48;
-#pragma unroll
-        for (int hh = 0; hh < 3; hh++) {
-          const int t = 3 * u + hh;
-          if (t < p.np) {   // rows (2f, 2f+1) = (gate f, up f)
-            const int f = p.p0 + p.ps * t;
-            const float v0 = pair_result(p, ores, t, 0), v1 = pair_result(p, ores, t, 1);
-            const float hv = v0 / (1.0f + expf(-v0)) * v1;
-            if (e.ch) store_act(e.ch, f, hv, d.act);
-            bits |= (uint64_t)f32_to_bf16(hv) << (16 * hh);
-          }
+      // One output per lane, the three of word u in lanes 4u .. 4u+2 of a quad (16 words per
+      // wave and pass), so that a lane computes one SiLU, not three in a row; the quad's first
+      // lane collects the other two by DPP and stores the word.
+      const int lane = threadIdx.x & 63;
+      for (int u0 = 16 * wave_id(); u0 < e.hs; u0 += 16 * PW) {   // wave-uniform
+        const int u = u0 + (lane >> 2), hh = lane & 3, t = 3 * u + hh;
+        uint32_t b = 0;
+        if (hh < 3 && t < p.np) {   // rows (2f, 2f+1) = (gate f, up f)
+          const float v0 = pair_result(p, ores, t, 0), v1 = pair_result(p, ores, t, 1);
+          const float hv = v0 / (1.0f + expf(-v0)) * v1;
+          if (e.ch) store_act(e.ch, p.p0 + p.ps * t, hv, d.act);
+          b = f32_to_bf16(hv);
         }
-        put_word(e.th + (size_t)p.p0 * e.hs + u, bits);
+        // quad_perm [1,1,1,1] and [2,2,2,2]: every lane of the quad reads lane 1, lane 2
+        const uint32_t b1 = (uint32_t)__builtin_amdgcn_mov_dpp((int)b, 0x55, 0xf, 0xf, false);
+        const uint32_t b2 = (uint32_t)__builtin_amdgcn_mov_dpp((int)b, 0xaa, 0xf, 0xf, false);
+        if (hh == 0 && u < e.hs)
+          put_word(e.th + (size_t)p.p0 * e.hs + u,
+                   (uint64_t)(e.tag & 0xffffu) << 48 | (uint64_t)b2 << 32 | (uint64_t)b1 << 16 | b);
       }
     } else {
       for (int t = threadIdx.x; t < p.np; t += PT) {   // rows (2f, 2f+1) = (gate f, up f)
