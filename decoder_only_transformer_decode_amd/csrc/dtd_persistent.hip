@@ -53,10 +53,12 @@ enum { TG_QKV = 0, TG_PART = 1, TG_O = 2, TG_XM = 3, TG_H = 4, TG_XO = 5, kTagsP
 // real-time counter at every phase boundary (1 + 11 per layer + 3 events).
 constexpr int kTraceWG = 256, kTraceEv = 512;
 __device__ uint64_t g_phase_trace[kTraceWG * kTraceEv];
+// (the kernel keeps the buffer's address in trace_base: read through the GOT at every
+// stamp, a miss in the scalar cache would add a memory round trip to the stamp)
 #define PTRACE(ev)                                                                          \
   do {                                                                                      \
     if (threadIdx.x == 0 && blockIdx.x < kTraceWG && (ev) < kTraceEv)                       \
-      g_phase_trace[blockIdx.x * kTraceEv + (ev)] = __builtin_amdgcn_s_memrealtime();       \
+      trace_base[blockIdx.x * kTraceEv + (ev)] = __builtin_amdgcn_s_memrealtime();          \
   } while (0)
 // timestamps inside a streaming loop go to LDS first (a global store there would make the
 // compiler drain all loads in flight at every later wait)
@@ -69,7 +71,7 @@ __shared__ unsigned long long g_trace_lds[16];
 #define PTRACE_SET(ev, val)                                                                 \
   do {                                                                                      \
     if (threadIdx.x == 0 && blockIdx.x < kTraceWG && (ev) < kTraceEv)                       \
-      g_phase_trace[blockIdx.x * kTraceEv + (ev)] = (val);                                  \
+      trace_base[blockIdx.x * kTraceEv + (ev)] = (val);                                     \
   } while (0)
 // inside an attention item: only when the caller set the item-trace flag
 #define ITRACE(ev) \
@@ -477,6 +479,19 @@ __device__ __forceinline__ float wave_total(float v) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
+// Sum over the workgroup: DPP within each wave, then the PW wave totals through LDS (red,
+// 16-byte aligned) read back as two float4, added in a fixed order.  Uses the compile-time
+// wave count: reading blockDim would be a scalar memory load on the critical path.
+__device__ __forceinline__ float wg_sum(float v, float* red) {
+  static_assert(PW == 8, "two float4 of wave totals");
+  const float t = wave_total(v);
+  __syncthreads();   // earlier readers of red are done
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = t;
+  __syncthreads();
+  const float4 a = *(const float4*)red, b = *(const float4*)(red + 4);
+  return ((a.x + a.y) + (a.z + a.w)) + ((b.x + b.y) + (b.z + b.w));
+}
+
 // the same shape of reduction for the maximum (rows left out by a broadcast keep -inf)
 template <int CTRL, int ROW_MASK>
 __device__ __forceinline__ float dpp_max(float v) {
@@ -714,20 +729,25 @@ __device__ __forceinline__ void gain_issue(const float* gain, int D, float (&gn)
 template <int VEC>
 __device__ __forceinline__ void norm_lds(const float* xf, const float (&gn)[kNormPer], int D, float eps, int act,
                                          float* xs, void* cap, float* red) {
+  // all reads unconditional (a clamped index), so that they are issued together rather
+  // than one branch and one LDS round trip at a time
+  float xv[kNormPer];
   float ss = 0.f;
 #pragma unroll
   for (int k = 0; k < kNormPer; k++) {
     const int i = (int)threadIdx.x + k * PT;
-    if (i < D) ss += xf[i] * xf[i];
+    xv[k] = xf[i < D ? i : 0];
   }
-  ss = block_sum(ss, red);
+#pragma unroll
+  for (int k = 0; k < kNormPer; k++) ss += (int)threadIdx.x + k * PT < D ? xv[k] * xv[k] : 0.f;
+  ss = wg_sum(ss, red);
   const float r = 1.0f / sqrtf(ss / (float)D + eps);
   zero_tail<VEC>(D, xs);
 #pragma unroll
   for (int k = 0; k < kNormPer; k++) {
     const int i = (int)threadIdx.x + k * PT;
     if (i < D) {
-      const float v = round_act(xf[i] * r * gn[k], act);
+      const float v = round_act(xv[k] * r * gn[k], act);
       if (cap) store_act(cap, i, v, act);
       xs[swz<VEC>(i)] = v;
     }
@@ -889,6 +909,9 @@ __device__ __forceinline__ void attn_item_p(const Dims& d, const KvLayer& kv, co
                                             bool itrace = false) {
   const int hd = d.hd, G = d.G, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int t_begin = c * ct, t_end = min(pos + 1, t_begin + ct), ldk = kv_ld(hd);
+#ifdef DTD_PHASE_TRACE
+  uint64_t* trace_base = g_phase_trace;
+#endif
   float* q_s = sm;                          // [G][hd], pre-scaled by 1/sqrt(hd)
   float* tk = q_s + G * hd;                 // [64][hd+4]
   float* tv = tk + kAttnTile * ldk;         // [64][hd+4]
@@ -1076,7 +1099,7 @@ __global__ __launch_bounds__(PT) void k_step(PersistArgs a) {
   // Dynamic LDS is placed after the static variables below; without the alignment it would
   // start at their (unaligned) end, and every float4 access to it would be split.
   extern __shared__ __attribute__((aligned(16))) float smem[];
-  __shared__ float red[PW];
+  __shared__ __attribute__((aligned(16))) float red[PW];
   __shared__ int sfail;
   __shared__ float wbest[PW];
   __shared__ int widx[PW];
@@ -1096,6 +1119,10 @@ __global__ __launch_bounds__(PT) void k_step(PersistArgs a) {
   auto inj = [&](int l, size_t off) { return (const void*)(a.inject + (size_t)l * a.po.record + off); };
   auto cap = [&](int l, size_t off) { return (void*)(a.capture + (size_t)l * a.po.record + off); };
 
+#ifdef DTD_PHASE_TRACE
+  uint64_t* trace_base = g_phase_trace;
+  asm volatile("" : "+s"(trace_base));   // a value, not an address to rematerialise
+#endif
   PTRACE(0);
   if (tid == 0) sfail = 0;
   int tok = desc->tokens[0];
@@ -1163,7 +1190,9 @@ __global__ __launch_bounds__(PT) void k_step(PersistArgs a) {
         const uint64_t* src = k == PH_GU ? a.t_xm : a.t_xo;
         gather(d.D, k == PH_GU ? T(l, TG_XM) : T(l - 1, TG_XO), err, &sfail, [&](int i) { return src + i; },
                [&](int i, float v) { xf[i] = v; });
+        if (l == 5 && k == PH_GU) PTRACE(452);
         __syncthreads();
+        if (l == 5 && k == PH_GU) PTRACE(453);
         if (sfail) return;
       }
       // Every path reads the gains (gn): a load whose register is never read stays pending
@@ -1182,6 +1211,7 @@ __global__ __launch_bounds__(PT) void k_step(PersistArgs a) {
         }
       } else {
         norm_lds<VEC>(xf, gn, d.D, d.eps, d.act, xs, nullptr, red);
+        if (l == 5 && k == PH_GU) PTRACE(454);
       }
     } else {
       // the attention output (O) or the SwiGLU output (down), as produced
@@ -1231,7 +1261,7 @@ __global__ __launch_bounds__(PT) void k_step(PersistArgs a) {
     gemv_phase<WFMT>(ph, nx, pre, preb, xs, ores, ic);
 #ifdef DTD_PHASE_TRACE
     if (l == 5 && (k == PH_GU || k == PH_DOWN) && lane == 0)
-      g_phase_trace[g * kTraceEv + 430 + (k == PH_GU ? 0 : 10) + wave] = __builtin_amdgcn_s_memrealtime();
+      trace_base[g * kTraceEv + 430 + (k == PH_GU ? 0 : 10) + wave] = __builtin_amdgcn_s_memrealtime();
 #endif
     __syncthreads();
     if (l == 5 && k == PH_GU) PTRACE(438);
