@@ -59,12 +59,13 @@ __device__ __forceinline__ void gstore(void* p, T v) {
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t b16) { return __uint_as_float(b16 << 16); }
 
-// float -> bf16, round to nearest even (NaN kept quiet)
+// float -> bf16, round to nearest even (NaN kept quiet); written as a select rather than an
+// early return so that it compiles without a branch
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+  const uint32_t u = __float_as_uint(f);
+  const uint32_t rne = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+  const uint32_t nan = (u >> 16) | 0x40u;
+  return (uint16_t)((u & 0x7fffffffu) > 0x7f800000u ? nan : rne);
 }
 
 __device__ __forceinline__ float round_act(float v, int act) {

@@ -53,12 +53,10 @@ enum { TG_QKV = 0, TG_PART = 1, TG_O = 2, TG_XM = 3, TG_H = 4, TG_XO = 5, kTagsP
 // real-time counter at every phase boundary (1 + 11 per layer + 3 events).
 constexpr int kTraceWG = 256, kTraceEv = 512;
 __device__ uint64_t g_phase_trace[kTraceWG * kTraceEv];
-// (the kernel keeps the buffer's address in trace_base: read through the GOT at every
-// stamp, a miss in the scalar cache would add a memory round trip to the stamp)
 #define PTRACE(ev)                                                                          \
   do {                                                                                      \
     if (threadIdx.x == 0 && blockIdx.x < kTraceWG && (ev) < kTraceEv)                       \
-      trace_base[blockIdx.x * kTraceEv + (ev)] = __builtin_amdgcn_s_memrealtime();          \
+      g_phase_trace[blockIdx.x * kTraceEv + (ev)] = __builtin_amdgcn_s_memrealtime();       \
   } while (0)
 // timestamps inside a streaming loop go to LDS first (a global store there would make the
 // compiler drain all loads in flight at every later wait)
@@ -71,7 +69,7 @@ __shared__ unsigned long long g_trace_lds[16];
 #define PTRACE_SET(ev, val)                                                                 \
   do {                                                                                      \
     if (threadIdx.x == 0 && blockIdx.x < kTraceWG && (ev) < kTraceEv)                       \
-      trace_base[blockIdx.x * kTraceEv + (ev)] = (val);                                     \
+      g_phase_trace[blockIdx.x * kTraceEv + (ev)] = (val);                                  \
   } while (0)
 // inside an attention item: only when the caller set the item-trace flag
 #define ITRACE(ev) \
@@ -113,6 +111,13 @@ __device__ __forceinline__ void settle(const T& v) {
 }
 
 __device__ __forceinline__ void settle(const v4u& v) {
+  settle(v.x);
+  settle(v.y);
+  settle(v.z);
+  settle(v.w);
+}
+
+__device__ __forceinline__ void settle(const float4& v) {
   settle(v.x);
   settle(v.y);
   settle(v.z);
@@ -715,47 +720,61 @@ __device__ __forceinline__ void stage_tagged(const uint64_t* src, uint32_t tag, 
 
 // RMSNorm gains of this thread's elements (i = tid + k*PT), loaded ahead of the wait for
 // the vector they scale
-constexpr int kNormPer = 8;    // model width up to 8 * PT
-__device__ __forceinline__ void gain_issue(const float* gain, int D, float (&gn)[kNormPer]) {
+constexpr int kNormPer = 8;             // model width up to 8 * PT
+constexpr int kNormV = kNormPer / 4;    // passes of 4 consecutive elements per thread
+
+// this thread's gains: elements 4(tid + k PT) .. +4 of pass k (0 past D; D is a multiple of 4)
+__device__ __forceinline__ void gain_issue(const float* gain, int D, float4 (&gn)[kNormV]) {
 #pragma unroll
-  for (int k = 0; k < kNormPer; k++) {
-    const int i = (int)threadIdx.x + k * PT;
-    gn[k] = i < D ? gload<float>(gain + i) : 0.f;
+  for (int k = 0; k < kNormV; k++) {
+    const int i = 4 * ((int)threadIdx.x + k * PT);
+    gn[k] = i < D ? gload<float4>(gain + i) : make_float4(0.f, 0.f, 0.f, 0.f);
   }
 }
 
 // xs = round_act(xf / sqrt(mean(xf^2) + eps) * gain), xf in LDS (complete: the caller has
-// synchronised); cap: optional copy in activation storage
+// synchronised); cap: optional copy in activation storage.  A thread takes 4 consecutive
+// elements per pass, which are 4 consecutive floats of the swizzled input too, so the reads,
+// the gains and the writes are float4 and the serial chain stays short.
 template <int VEC>
-__device__ __forceinline__ void norm_lds(const float* xf, const float (&gn)[kNormPer], int D, float eps, int act,
+__device__ __forceinline__ void norm_lds(const float* xf, const float4 (&gn)[kNormV], int D, float eps, int act,
                                          float* xs, void* cap, float* red) {
-  // all reads unconditional (a clamped index), so that they are issued together rather
-  // than one branch and one LDS round trip at a time
-  float xv[kNormPer];
+  float4 xv[kNormV];
+#pragma unroll
+  for (int k = 0; k < kNormV; k++) {   // all reads first, unconditionally (a clamped index)
+    const int i = 4 * ((int)threadIdx.x + k * PT);
+    xv[k] = *(const float4*)(xf + (i < D ? i : 0));
+  }
   float ss = 0.f;
 #pragma unroll
-  for (int k = 0; k < kNormPer; k++) {
-    const int i = (int)threadIdx.x + k * PT;
-    xv[k] = xf[i < D ? i : 0];
+  for (int k = 0; k < kNormV; k++) {
+    const float4 v = xv[k];
+    const float q = v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+    ss += 4 * ((int)threadIdx.x + k * PT) < D ? q : 0.f;
   }
-#pragma unroll
-  for (int k = 0; k < kNormPer; k++) ss += (int)threadIdx.x + k * PT < D ? xv[k] * xv[k] : 0.f;
   ss = wg_sum(ss, red);
   const float r = 1.0f / sqrtf(ss / (float)D + eps);
   zero_tail<VEC>(D, xs);
 #pragma unroll
-  for (int k = 0; k < kNormPer; k++) {
-    const int i = (int)threadIdx.x + k * PT;
+  for (int k = 0; k < kNormV; k++) {
+    const int i = 4 * ((int)threadIdx.x + k * PT);
     if (i < D) {
-      const float v = round_act(xv[k] * r * gn[k], act);
-      if (cap) store_act(cap, i, v, act);
-      xs[swz<VEC>(i)] = v;
+      const float4 g = gn[k], x = xv[k];
+      const float4 v = make_float4(round_act(x.x * r * g.x, act), round_act(x.y * r * g.y, act),
+                                   round_act(x.z * r * g.z, act), round_act(x.w * r * g.w, act));
+      if (cap) {
+        store_act(cap, i, v.x, act);
+        store_act(cap, i + 1, v.y, act);
+        store_act(cap, i + 2, v.z, act);
+        store_act(cap, i + 3, v.w, act);
+      }
+      *(float4*)(xs + swz<VEC>(i)) = v;
     }
   }
   // the gains were read above only where i < D; this unconditional read ends their loads on
   // every path (see settle())
 #pragma unroll
-  for (int k = 0; k < kNormPer; k++) settle(gn[k]);
+  for (int k = 0; k < kNormV; k++) settle(gn[k]);
 }
 
 __device__ __forceinline__ void load_plain_f32(const void* src, int n, float* dst) {
@@ -909,9 +928,6 @@ __device__ __forceinline__ void attn_item_p(const Dims& d, const KvLayer& kv, co
                                             bool itrace = false) {
   const int hd = d.hd, G = d.G, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int t_begin = c * ct, t_end = min(pos + 1, t_begin + ct), ldk = kv_ld(hd);
-#ifdef DTD_PHASE_TRACE
-  uint64_t* trace_base = g_phase_trace;
-#endif
   float* q_s = sm;                          // [G][hd], pre-scaled by 1/sqrt(hd)
   float* tk = q_s + G * hd;                 // [64][hd+4]
   float* tv = tk + kAttnTile * ldk;         // [64][hd+4]
@@ -1119,10 +1135,6 @@ __global__ __launch_bounds__(PT) void k_step(PersistArgs a) {
   auto inj = [&](int l, size_t off) { return (const void*)(a.inject + (size_t)l * a.po.record + off); };
   auto cap = [&](int l, size_t off) { return (void*)(a.capture + (size_t)l * a.po.record + off); };
 
-#ifdef DTD_PHASE_TRACE
-  uint64_t* trace_base = g_phase_trace;
-  asm volatile("" : "+s"(trace_base));   // a value, not an address to rematerialise
-#endif
   PTRACE(0);
   if (tid == 0) sfail = 0;
   int tok = desc->tokens[0];
@@ -1134,7 +1146,7 @@ __global__ __launch_bounds__(PT) void k_step(PersistArgs a) {
   const bool do_head = desc->do_head != 0;
 
   WBuf pre, preb;   // weight groups in flight (A, B of gemv_phase)
-  float gn[kNormPer];
+  float4 gn[kNormV];
   CPLayer* layers = (CPLayer*)a.layers;
   const void* dummy = layers[0].qkv.w;
   PPhase ph = make_phase<WFMT>(cmat(&layers[0].qkv), g, nwg);
@@ -1179,6 +1191,18 @@ __global__ __launch_bounds__(PT) void k_step(PersistArgs a) {
     CPLayer* Ly = layers + (l < d.L ? l : d.L - 1);
     const int tb = 1 + l * 11;
     PTRACE(k == PH_HEAD ? tb : tb + (k == PH_QKV ? 0 : 2 * k + 2));
+
+    // The phase after this one (its first weight groups are issued at the end of this
+    // projection; after QKV none: the O projection's weights are issued after attention,
+    // since otherwise their registers would stay live across the attention items).  Worked
+    // out here, while the input below is still on its way, not between the input and the
+    // projection.
+    PPhase nx;
+    if (k == PH_O) nx = make_phase<WFMT>(cmat(&Ly->gu), g, nwg);
+    else if (k == PH_GU) nx = make_phase<WFMT>(cmat(&Ly->down), g, nwg);
+    else if (k == PH_DOWN && l + 1 < d.L) nx = make_phase<WFMT>(cmat(&layers[l + 1].qkv), g, nwg);
+    else if (k == PH_DOWN && do_head) nx = make_phase<WFMT>(a.head, g, nwg);
+    else nx = empty_phase(dummy);
 
     // ---- input of the projection ----
     // A probe step takes every wait of a normal step (the waits are what order the reuse of
@@ -1246,22 +1270,14 @@ __global__ __launch_bounds__(PT) void k_step(PersistArgs a) {
     }
     __syncthreads();
 
-    // ---- the projection; the next one's first weight groups are issued at its end (after
-    // QKV none: the O projection's weights are issued after attention, since otherwise their
-    // registers would stay live across the attention items) ----
-    PPhase nx;
-    if (k == PH_O) nx = make_phase<WFMT>(cmat(&Ly->gu), g, nwg);
-    else if (k == PH_GU) nx = make_phase<WFMT>(cmat(&Ly->down), g, nwg);
-    else if (k == PH_DOWN && l + 1 < d.L) nx = make_phase<WFMT>(cmat(&layers[l + 1].qkv), g, nwg);
-    else if (k == PH_DOWN && do_head) nx = make_phase<WFMT>(a.head, g, nwg);
-    else nx = empty_phase(dummy);
+    // ---- the projection; the next one's first weight groups are issued at its end ----
     PTRACE(k == PH_HEAD ? tb + 1 : tb + (k == PH_QKV ? 1 : 2 * k + 3));
 #pragma unroll
-    for (int i = 0; i < kNormPer; i++) settle(gn[i]);   // no gain load may reach the stream
+    for (int i = 0; i < kNormV; i++) settle(gn[i]);   // no gain load may reach the stream
     gemv_phase<WFMT>(ph, nx, pre, preb, xs, ores, ic);
 #ifdef DTD_PHASE_TRACE
     if (l == 5 && (k == PH_GU || k == PH_DOWN) && lane == 0)
-      trace_base[g * kTraceEv + 430 + (k == PH_GU ? 0 : 10) + wave] = __builtin_amdgcn_s_memrealtime();
+      g_phase_trace[g * kTraceEv + 430 + (k == PH_GU ? 0 : 10) + wave] = __builtin_amdgcn_s_memrealtime();
 #endif
     __syncthreads();
     if (l == 5 && k == PH_GU) PTRACE(438);
@@ -1515,7 +1531,7 @@ size_t persistent_smem_bytes(const Dims& d, int nch, int nwg) {
 
 bool persistent_supports(const Dims& d) {
   const int eb = d.kvfmt == KV_F32 ? 4 : (d.kvfmt == KV_BF16 ? 2 : 1);
-  return d.D <= kNormPer * PT && d.hd <= 128 && (d.hd * eb) % 16 == 0 && d.hd % 16 == 0 &&
+  return d.D <= kNormPer * PT && d.D % 4 == 0 && d.hd <= 128 && (d.hd * eb) % 16 == 0 && d.hd % 16 == 0 &&
          (size_t)d.G * d.hd <= (size_t)kAttnOut * PT;
 }
 
