@@ -1274,7 +1274,11 @@ __global__ __launch_bounds__(PT) void k_step(PersistArgs a) {
     PTRACE(k == PH_HEAD ? tb + 1 : tb + (k == PH_QKV ? 1 : 2 * k + 3));
 #pragma unroll
     for (int i = 0; i < kNormV; i++) settle(gn[i]);   // no gain load may reach the stream
-    gemv_phase<WFMT>(ph, nx, pre, preb, xs, ores, ic);
+    // The loop ends with loads of nothing (pad groups) in A and B; the next phase's first
+    // groups are issued after the epilogue below.  A CU's memory instructions issue in order,
+    // so issued before the epilogue they would hold up its stores, which publish what every
+    // other workgroup waits for, until their own data had come in.
+    gemv_phase<WFMT>(ph, empty_phase(dummy), pre, preb, xs, ores, ic);
 #ifdef DTD_PHASE_TRACE
     if (l == 5 && (k == PH_GU || k == PH_DOWN) && lane == 0)
       g_phase_trace[g * kTraceEv + 430 + (k == PH_GU ? 0 : 10) + wave] = __builtin_amdgcn_s_memrealtime();
@@ -1308,6 +1312,12 @@ __global__ __launch_bounds__(PT) void k_step(PersistArgs a) {
       if (l == 5) PTRACE(439);
     } else {
       phase_epilogue<EPI_LOGITS>(d, ph, ores, e);
+    }
+    // the next phase's first weight groups (none after QKV, see above)
+    if (k != PH_QKV && k != PH_HEAD) {
+      ic = ICur{0, 0, nx.jb};
+      issue_group<WFMT>(nx, ic, pre);
+      issue_group<WFMT>(nx, ic, preb);
     }
     PTRACE(k == PH_HEAD ? tb + 2 : tb + (k == PH_QKV ? 2 : 2 * k + 4));
 
