@@ -712,8 +712,7 @@ static dtd_status run_step(dtd_engine* e, int B, const int* slots, const int* po
     a.po = probe_layout(d, 1, act_bytes(e->cfg.act));
     TIMED(6, launch_persistent(a, e->nwg, e->p_smem, st));
     e->epoch += ntag;
-    HIP_OK(e, hipMemcpyAsync(e->err_host, e->err_dev, 4, hipMemcpyDeviceToHost, st));
-    return DTD_OK;
+      return DTD_OK;
   }
   if (e->path == 2) return fail(e, DTD_E_UNSUPPORTED, "persistent step kernel unavailable for this call");
 
@@ -795,7 +794,6 @@ static dtd_status run_step(dtd_engine* e, int B, const int* slots, const int* po
     TIMED(5, launch_gemv(d, e->head, e->xn, B, EPI_LOGITS, ea, st));
     HIP_OK(e, launch_argmax(d, e->desc_dev, B, e->logits, st));
   }
-  HIP_OK(e, hipMemcpyAsync(e->err_host, e->err_dev, 4, hipMemcpyDeviceToHost, st));
   return DTD_OK;
 }
 
@@ -952,6 +950,8 @@ extern "C" dtd_status dtd_check_device_errors(dtd_engine* e) {
   if (e->broken) return fail(e, DTD_E_STATE, "engine unusable after a HIP error");
   HIP_OK(e, hipSetDevice(e->device));
   HIP_OK(e, hipStreamSynchronize(e->stream));
+  // the device's error bits stay set until cleared here; read them now (not after every step)
+  HIP_OK(e, hipMemcpy(e->err_host, e->err_dev, 4, hipMemcpyDeviceToHost));
   const int32_t flags = *e->err_host;
   if (flags & kErrBarrier) {
     e->broken = true;
