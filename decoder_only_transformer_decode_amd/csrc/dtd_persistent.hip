@@ -1246,12 +1246,17 @@ __global__ __launch_bounds__(PT) void k_step(PersistArgs a) {
                                   [](int w, int& i0, int& i1) { i0 = 2 * w; i1 = 2 * w + 1; });
         } else {   // three values per word, 16-bit tag
           const int hs = h_words_per_wg(d.F, nwg);
+          // Word w comes from workgroup w / hs, found by a multiply with 2^32 / hs rounded up
+          // (64-bit: it is 2^32 for hs = 1; exact while w * hs < 2^32), and workgroup gp owns
+          // fq + (gp < fr) SwiGLU outputs: no integer division per word on the way in.
+          const uint64_t hs_inv = 0xffffffffull / (uint64_t)hs + 1ull;
+          const int fq = d.F / nwg, fr = d.F - fq * nwg;
           if (l == 5) PTRACE(415);
           zero_tail<VEC>(d.F, xs);
           gather_words<8, 48>(nwg * hs, T(l, TG_H) & 0xffffu, err, &sfail, [&](int w) { return a.t_h + w; },
                               [&](int w, uint64_t word) {
-                                const int gp = w / hs, u = w - gp * hs;
-                                const int np = gp < d.F ? (d.F - 1 - gp) / nwg + 1 : 0;
+                                const int gp = (int)(((uint64_t)(uint32_t)w * hs_inv) >> 32), u = w - gp * hs;
+                                const int np = fq + (gp < fr ? 1 : 0);
 #pragma unroll
                                 for (int hh = 0; hh < 3; hh++) {
                                   const int t = 3 * u + hh;
