@@ -615,45 +615,28 @@ __device__ __forceinline__ void consume_group(const PPhase& p, int c0, int total
   }
 }
 
-// Issues group gidx of the sequence "groups 0..ng2-1 of p, then groups of nx": the phase is
-// picked by uniform selects, so each buffer has exactly one issue site in the loop below
-// (two sites would be free to use different registers for the same in-flight group, and a
-// copy at the join would read registers that a load has yet to write).  The cursor restarts
-// at the first group of nx.
+// Issues the next group of phase p into b (past the wave's last line: pad loads, see
+// issue_group).  Nothing of the following consume may be scheduled above these loads: a
+// product of the group issued just before would then wait for that group before this one is
+// on its way.
 template <int WFMT>
-__device__ __forceinline__ void issue_seq(const PPhase& p, const PPhase& nx, int ng2, int gidx, WBuf& b, ICur& ic) {
-  const bool in_nx = gidx >= ng2;
-  if (gidx == ng2) ic = ICur{0, 0, nx.jb};
-  PPhase q;
-  q.w = in_nx ? nx.w : p.w;
-  q.s = in_nx ? nx.s : p.s;
-  q.N = in_nx ? nx.N : p.N;
-  q.Kb = in_nx ? nx.Kb : p.Kb;
-  q.K = in_nx ? nx.K : p.K;
-  q.pb = in_nx ? nx.pb : p.pb;
-  q.pst = in_nx ? nx.pst : p.pst;
-  q.jb = in_nx ? nx.jb : p.jb;
-  q.je = in_nx ? nx.je : p.je;
-  q.total = in_nx ? nx.total : p.total;
-  issue_group<WFMT>(q, ic, b);
-  // nothing of the following consume may be scheduled above these loads: a product of the
-  // group issued just before would then wait for that group before this one is on its way
+__device__ __forceinline__ void issue_next(const PPhase& p, WBuf& b, ICur& ic) {
+  issue_group<WFMT>(p, ic, b);
   __builtin_amdgcn_sched_barrier(0);
 }
 
 // Streams this wave's rows of phase p against the input vector in LDS (xs), leaving each
 // finished dot product in ores.  Two register buffers alternate, A with the even groups and
-// B with the odd ones (no copies between them, so nothing waits on a load in flight), and
-// both stay loaded across phase boundaries: on entry A and B hold groups 0 and 1 of this
-// phase (issued during an earlier phase), on exit they hold groups 0 and 1 of nx.  The
-// group count is padded to an even number >= 2 so the roles line up at the boundary; pad
-// groups issue loads whose values are not used.  A wave's share of one projection is only
-// a few groups, so without loads in flight across the wait between phases every phase
-// would cost whole round trips to HBM.  With nx empty, A and B end holding loads whose
-// values are not used.
+// B with the odd ones (no copies between them, so nothing waits on a load in flight): on
+// entry A and B hold groups 0 and 1 of this phase (issued before the wait for its input); on
+// exit they hold pad loads, whose values are not used (the caller issues the next phase's
+// first groups after its epilogue).  The group count is padded to an even number >= 2 so
+// the roles line up.  A wave's share of one projection is only a few groups, so without
+// loads in flight across the wait between phases every phase would cost whole round trips
+// to HBM.
 template <int WFMT>
-__device__ __forceinline__ void gemv_phase(const PPhase& p, const PPhase& nx, WBuf& A, WBuf& B, const float* xs,
-                                           float* ores, ICur& ic) {
+__device__ __forceinline__ void gemv_phase(const PPhase& p, WBuf& A, WBuf& B, const float* xs, float* ores,
+                                           ICur& ic) {
   const int wave = wave_id();
   const int total = p.total;
   int ng2 = ((total + GRP - 1) / GRP + 1) & ~1;
@@ -668,11 +651,11 @@ __device__ __forceinline__ void gemv_phase(const PPhase& p, const PPhase& nx, WB
     if (young) __builtin_amdgcn_s_setprio(1);
     else __builtin_amdgcn_s_setprio(0);
     consume_group<WFMT>(p, gi * GRP, total, A, x4, cu, ores);       // B stays in flight
-    issue_seq<WFMT>(p, nx, ng2, gi + 2, A, ic);
+    issue_next<WFMT>(p, A, ic);
     if (young) __builtin_amdgcn_s_setprio(0);
     else __builtin_amdgcn_s_setprio(1);
     consume_group<WFMT>(p, (gi + 1) * GRP, total, B, x4, cu, ores); // A stays in flight
-    issue_seq<WFMT>(p, nx, ng2, gi + 3, B, ic);
+    issue_next<WFMT>(p, B, ic);
   }
   __builtin_amdgcn_s_setprio(0);
 }
@@ -1283,7 +1266,7 @@ __global__ __launch_bounds__(PT) void k_step(PersistArgs a) {
     // groups are issued after the epilogue below.  A CU's memory instructions issue in order,
     // so issued before the epilogue they would hold up its stores, which publish what every
     // other workgroup waits for, until their own data had come in.
-    gemv_phase<WFMT>(ph, empty_phase(dummy), pre, preb, xs, ores, ic);
+    gemv_phase<WFMT>(ph, pre, preb, xs, ores, ic);
 #ifdef DTD_PHASE_TRACE
     if (l == 5 && (k == PH_GU || k == PH_DOWN) && lane == 0)
       g_phase_trace[g * kTraceEv + 430 + (k == PH_GU ? 0 : 10) + wave] = __builtin_amdgcn_s_memrealtime();
