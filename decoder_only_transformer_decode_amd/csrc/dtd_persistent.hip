@@ -893,7 +893,7 @@ __device__ __forceinline__ void kv_store(const Dims& d, const KvRegs<KVFMT>& r, 
   }
 }
 
-// partial products of the MFMA tile, per group of 4 heads: scores [4 waves][64 lanes][4],
+// partial products of the MFMA tile, per group of 4 heads: scores [8 waves][64 lanes][4],
 // then P V [4 row quarters][2 halves][64][4]
 __host__ __device__ inline size_t attn_red_floats(int G) { return (size_t)(G + 3) / 4 * (4 * 2 * 64 * 4); }
 
@@ -947,12 +947,15 @@ __device__ __forceinline__ void attn_item_p(const Dims& d, const KvLayer& kv, co
     // Scores on the matrix cores, heads in groups of 4: one v_mfma_f32_4x4x1f32 multiplies,
     // for one head dimension d, the 64 tile rows (A: lane t holds k[t][d]) by 4 queries (B:
     // lane t holds q[4 hg + t % 4][d], 0 past the last head); lane t then holds
-    // S[4(t/4) + r][4 hg + t % 4] in its r-th result.  Waves 0-3 each run a quarter of the
-    // head dimensions; their partial results meet in LDS.
+    // S[4(t/4) + r][4 hg + t % 4] in its r-th result.  The waves each run a share of the head
+    // dimensions; their partial results meet in LDS.
     typedef float f4v __attribute__((ext_vector_type(4)));
     const int nhg = (G + 3) >> 2;
-    if (wave < 4) {
-      const int d0 = wave * (hd >> 2), d1 = d0 + (hd >> 2);
+    // the head dimensions split over all 8 waves (4 when hd is not a multiple of 32), which
+    // halves each wave's chain of dependent products
+    const int sw = hd % 32 == 0 ? PW : 4;
+    if (wave < sw) {
+      const int d0 = wave * (hd / sw), d1 = d0 + hd / sw;
       const float* kr_ = tk + lane * ldk;
       for (int hg = 0; hg < nhg; hg++) {
         const int gq = 4 * hg + (lane & 3);
@@ -968,16 +971,17 @@ __device__ __forceinline__ void attn_item_p(const Dims& d, const KvLayer& kv, co
           sacc = __builtin_amdgcn_mfma_f32_4x4x1f32(ka.z, qa.z, sacc, 0, 0, 0);
           sacc = __builtin_amdgcn_mfma_f32_4x4x1f32(ka.w, qa.w, sacc, 0, 0, 0);
         }
-        *(float4*)(mred + ((hg * 4 + wave) * 64 + lane) * 4) = make_float4(sacc[0], sacc[1], sacc[2], sacc[3]);
+        *(float4*)(mred + ((hg * PW + wave) * 64 + lane) * 4) = make_float4(sacc[0], sacc[1], sacc[2], sacc[3]);
       }
     }
     __syncthreads();
     // softmax: wave w takes heads w, w + PW, ...; lane t is tile row t, its score the sum of
     // the 4 partials
     for (int g = wave; g < G; g += PW) {
-      const float* mr = mred + (g >> 2) * 1024;
+      const float* mr = mred + (g >> 2) * (PW * 256);
       const int src = (4 * (lane >> 2) + (g & 3)) * 4 + (lane & 3);
-      const float raw = mr[src] + mr[256 + src] + mr[512 + src] + mr[768 + src];
+      float raw = ((mr[src] + mr[256 + src]) + (mr[512 + src] + mr[768 + src]));
+      if (sw == PW) raw += (mr[1024 + src] + mr[1280 + src]) + (mr[1536 + src] + mr[1792 + src]);
       const float sc = lane < n ? raw : -INFINITY;
       const float mt = wave_top(sc);
       const float mo = st_s[g * 4], lo = st_s[g * 4 + 1];
