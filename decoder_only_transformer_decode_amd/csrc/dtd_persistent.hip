@@ -1096,7 +1096,10 @@ enum { PH_QKV = 0, PH_O = 1, PH_GU = 2, PH_DOWN = 3, PH_HEAD = 4 };
 // the epilogues and the attention each exist once in the binary: the loop body is executed
 // every layer, and a body larger than the instruction cache (64 KB) is refetched from L2
 // every layer, which stalls the weight stream far more than the fetch itself costs.
-template <int WFMT, int KVFMT>
+// PROBE: the debug-probe variant (every projection's input from the inject record, outputs
+// copied to the capture record).  A separate instantiation, so that the normal step kernel
+// carries none of that code.
+template <int WFMT, int KVFMT, bool PROBE>
 __global__ __launch_bounds__(PT) void k_step(PersistArgs a) {
   constexpr int VEC = PVec<WFMT>::VEC;
   // Dynamic LDS is placed after the static variables below; without the alignment it would
@@ -1110,7 +1113,7 @@ __global__ __launch_bounds__(PT) void k_step(PersistArgs a) {
   const Dims& d = a.d;
   const int g = blockIdx.x, nwg = gridDim.x, tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
-  const bool probe = a.inject != nullptr;
+  constexpr bool probe = PROBE;
   const StepDesc* desc = a.desc;
   int32_t* err = a.err;
   float* xs = smem;                   // swizzled input vector of the current projection
@@ -1481,24 +1484,24 @@ __global__ __launch_bounds__(PT) void k_step(PersistArgs a) {
 }
 
 template <int WFMT, int KVFMT>
-const void* step_kernel() {
-  return (const void*)k_step<WFMT, KVFMT>;
+const void* step_kernel(bool probe) {
+  return probe ? (const void*)k_step<WFMT, KVFMT, true> : (const void*)k_step<WFMT, KVFMT, false>;
 }
 
-const void* pick(int wfmt, int kvfmt) {
+const void* pick(int wfmt, int kvfmt, bool probe) {
   if (wfmt == W_INT8_ROW) {
-    if (kvfmt == KV_F32) return step_kernel<W_INT8_ROW, KV_F32>();
-    if (kvfmt == KV_BF16) return step_kernel<W_INT8_ROW, KV_BF16>();
-    return step_kernel<W_INT8_ROW, KV_I8>();
+    if (kvfmt == KV_F32) return step_kernel<W_INT8_ROW, KV_F32>(probe);
+    if (kvfmt == KV_BF16) return step_kernel<W_INT8_ROW, KV_BF16>(probe);
+    return step_kernel<W_INT8_ROW, KV_I8>(probe);
   }
   if (wfmt == W_Q8_0) {
-    if (kvfmt == KV_F32) return step_kernel<W_Q8_0, KV_F32>();
-    if (kvfmt == KV_BF16) return step_kernel<W_Q8_0, KV_BF16>();
-    return step_kernel<W_Q8_0, KV_I8>();
+    if (kvfmt == KV_F32) return step_kernel<W_Q8_0, KV_F32>(probe);
+    if (kvfmt == KV_BF16) return step_kernel<W_Q8_0, KV_BF16>(probe);
+    return step_kernel<W_Q8_0, KV_I8>(probe);
   }
-  if (kvfmt == KV_F32) return step_kernel<W_BF16, KV_F32>();
-  if (kvfmt == KV_BF16) return step_kernel<W_BF16, KV_BF16>();
-  return step_kernel<W_BF16, KV_I8>();
+  if (kvfmt == KV_F32) return step_kernel<W_BF16, KV_F32>(probe);
+  if (kvfmt == KV_BF16) return step_kernel<W_BF16, KV_BF16>(probe);
+  return step_kernel<W_BF16, KV_I8>(probe);
 }
 
 }  // namespace
@@ -1540,15 +1543,18 @@ bool persistent_supports(const Dims& d) {
 int persistent_tags_per_step(const Dims& d) { return d.L * kTagsPerLayer + 1; }
 
 hipError_t persistent_prepare(const Dims& d, size_t smem, int* blocks_per_cu) {
-  const void* f = pick(d.wfmt, d.kvfmt);
-  hipError_t r = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-  if (r != hipSuccess) return r;
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, f, PT, smem);
+  for (const bool probe : {true, false}) {
+    hipError_t r = hipFuncSetAttribute(pick(d.wfmt, d.kvfmt, probe), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)smem);
+    if (r != hipSuccess) return r;
+  }
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, pick(d.wfmt, d.kvfmt, false), PT, smem);
 }
 
 hipError_t launch_persistent(const PersistArgs& a, int nwg, size_t smem, hipStream_t st) {
   void* args[] = {(void*)&a};
-  return hipLaunchCooperativeKernel(pick(a.d.wfmt, a.d.kvfmt), dim3(nwg), dim3(PT), args, (unsigned)smem, st);
+  return hipLaunchCooperativeKernel(pick(a.d.wfmt, a.d.kvfmt, a.inject != nullptr), dim3(nwg), dim3(PT), args,
+                                    (unsigned)smem, st);
 }
 
 }  // namespace dtd
