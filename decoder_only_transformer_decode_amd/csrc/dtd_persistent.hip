@@ -349,6 +349,7 @@ __device__ __forceinline__ void issue_group(const PPhase& p, ICur& ic, WBuf& b) 
 // set) also plain values in the capture record.
 struct PEpi {
   uint32_t tag;
+  int act;        // activation type (a constant in the step kernels that fix it)
   // QKV
   uint64_t* tq;
   uint64_t* tk;
@@ -419,7 +420,7 @@ __device__ __forceinline__ void phase_epilogue(const Dims& d, const PPhase& p, c
       if (r < p.N) emit(e.tout, e.cout, e.tag, r, e.xf[r] + pair_result(p, ores, u >> 1, u & 1));
     }
   } else if constexpr (EPI == EPI_SWIGLU) {
-    if (d.act == ACT_BF16) {
+    if (e.act == ACT_BF16) {
       // three outputs per word under a 16-bit tag: word u of this workgroup carries its local
       // pairs 3u, 3u + 1, 3u + 2 in bits 0-15, 16-31, 32-47.  Every one of its hs words is
       // written in every layer, pads as zero, so a stale word is never more than one layer's
@@ -434,7 +435,7 @@ __device__ __forceinline__ void phase_epilogue(const Dims& d, const PPhase& p, c
         if (hh < 3 && t < p.np) {   // rows (2f, 2f+1) = (gate f, up f)
           const float v0 = pair_result(p, ores, t, 0), v1 = pair_result(p, ores, t, 1);
           const float hv = v0 / (1.0f + expf(-v0)) * v1;
-          if (e.ch) store_act(e.ch, p.p0 + p.ps * t, hv, d.act);
+          if (e.ch) store_act(e.ch, p.p0 + p.ps * t, hv, e.act);
           b = f32_to_bf16(hv);
         }
         // quad_perm [1,1,1,1] and [2,2,2,2]: every lane of the quad reads lane 1, lane 2
@@ -449,7 +450,7 @@ __device__ __forceinline__ void phase_epilogue(const Dims& d, const PPhase& p, c
         const int f = p.p0 + p.ps * t;
         const float v0 = pair_result(p, ores, t, 0), v1 = pair_result(p, ores, t, 1);
         const float hv = v0 / (1.0f + expf(-v0)) * v1;
-        if (e.ch) store_act(e.ch, f, hv, d.act);
+        if (e.ch) store_act(e.ch, f, hv, e.act);
         put_tag(e.th + f, e.tag, hv);
       }
     }
@@ -1099,7 +1100,9 @@ enum { PH_QKV = 0, PH_O = 1, PH_GU = 2, PH_DOWN = 3, PH_HEAD = 4 };
 // PROBE: the debug-probe variant (every projection's input from the inject record, outputs
 // copied to the capture record).  A separate instantiation, so that the normal step kernel
 // carries none of that code.
-template <int WFMT, int KVFMT, bool PROBE>
+// ACTT: the activation type as a constant (ACT_F32, ACT_BF16), or -1 to read it from the
+// dimensions (the probe variants).
+template <int WFMT, int KVFMT, bool PROBE, int ACTT>
 __global__ __launch_bounds__(PT) void k_step(PersistArgs a) {
   constexpr int VEC = PVec<WFMT>::VEC;
   // Dynamic LDS is placed after the static variables below; without the alignment it would
@@ -1114,6 +1117,7 @@ __global__ __launch_bounds__(PT) void k_step(PersistArgs a) {
   const int g = blockIdx.x, nwg = gridDim.x, tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   constexpr bool probe = PROBE;
+  const int act = ACTT >= 0 ? ACTT : a.d.act;
   const StepDesc* desc = a.desc;
   int32_t* err = a.err;
   float* xs = smem;                   // swizzled input vector of the current projection
@@ -1173,6 +1177,7 @@ __global__ __launch_bounds__(PT) void k_step(PersistArgs a) {
   e.logits_out = desc->logits_out;
   e.best = -INFINITY;
   e.best_idx = INT_MAX;
+  e.act = act;
   const int nph = 4 * d.L + (do_head ? 1 : 0);
 #pragma clang loop unroll(disable)
   for (int q = 0; q < nph; q++) {
@@ -1217,20 +1222,20 @@ __global__ __launch_bounds__(PT) void k_step(PersistArgs a) {
         load_plain_f32(inj(lp, k == PH_QKV ? a.po.x_in : (k == PH_GU ? a.po.x_mid : a.po.x_out)), d.D, xf);
         __syncthreads();
         const bool keep = k != PH_HEAD && g == 0;   // workgroup 0 records the normalised input
-        norm_lds<VEC>(xf, gn, d.D, d.eps, d.act, xs, keep ? cap(l, k == PH_QKV ? a.po.xn : a.po.xn2) : nullptr,
+        norm_lds<VEC>(xf, gn, d.D, d.eps, act, xs, keep ? cap(l, k == PH_QKV ? a.po.xn : a.po.xn2) : nullptr,
                       red);
         if (k != PH_HEAD) {
           __syncthreads();
-          stage_plain<VEC>(inj(l, k == PH_QKV ? a.po.xn : a.po.xn2), d.act, d.D, xs);
+          stage_plain<VEC>(inj(l, k == PH_QKV ? a.po.xn : a.po.xn2), act, d.D, xs);
         }
       } else {
-        norm_lds<VEC>(xf, gn, d.D, d.eps, d.act, xs, nullptr, red);
+        norm_lds<VEC>(xf, gn, d.D, d.eps, act, xs, nullptr, red);
         if (l == 5 && k == PH_GU) PTRACE(454);
       }
     } else {
       // the attention output (O) or the SwiGLU output (down), as produced
       const bool is_o = k == PH_O;
-      if (d.act == ACT_BF16) {   // two values per word
+      if (act == ACT_BF16) {   // two values per word
         if (is_o) {
           stage_tagged_pairs<VEC>(a.t_o, T(l, TG_O), d.q_dim >> 1, d.q_dim, xs, err, &sfail,
                                   [](int w, int& i0, int& i1) { i0 = 2 * w; i1 = 2 * w + 1; });
@@ -1261,7 +1266,7 @@ __global__ __launch_bounds__(PT) void k_step(PersistArgs a) {
       }
       __syncthreads();
       if (sfail) return;
-      if (probe) stage_plain<VEC>(inj(l, is_o ? a.po.o : a.po.h), d.act, is_o ? d.q_dim : d.F, xs);
+      if (probe) stage_plain<VEC>(inj(l, is_o ? a.po.o : a.po.h), act, is_o ? d.q_dim : d.F, xs);
     }
     __syncthreads();
 
@@ -1420,8 +1425,8 @@ __global__ __launch_bounds__(PT) void k_step(PersistArgs a) {
             float sum = 0.f;
             for (int pp = 0; pp < NP; pp++) sum += psum[pp * hd + tid];
             const float o = sum / Lsum[0];
-            if (probe) store_act(cap(l, a.po.o), (size_t)h * hd + tid, o, d.act);
-            if (d.act == ACT_BF16) {   // outputs 2w, 2w + 1 share word w (hd is even)
+            if (probe) store_act(cap(l, a.po.o), (size_t)h * hd + tid, o, act);
+            if (act == ACT_BF16) {   // outputs 2w, 2w + 1 share word w (hd is even)
               const uint32_t mine = f32_to_bf16(o);
               const uint32_t other = (uint32_t)__shfl_xor((int)mine, 1, 64);
               if ((tid & 1) == 0) put_tag(a.t_o + ((h * hd + tid) >> 1), T(l, TG_O), __uint_as_float(mine | (other << 16)));
@@ -1484,24 +1489,26 @@ __global__ __launch_bounds__(PT) void k_step(PersistArgs a) {
 }
 
 template <int WFMT, int KVFMT>
-const void* step_kernel(bool probe) {
-  return probe ? (const void*)k_step<WFMT, KVFMT, true> : (const void*)k_step<WFMT, KVFMT, false>;
+const void* step_kernel(bool probe, int act) {
+  if (probe) return (const void*)k_step<WFMT, KVFMT, true, -1>;
+  return act == ACT_BF16 ? (const void*)k_step<WFMT, KVFMT, false, ACT_BF16>
+                         : (const void*)k_step<WFMT, KVFMT, false, ACT_F32>;
 }
 
-const void* pick(int wfmt, int kvfmt, bool probe) {
+const void* pick(int wfmt, int kvfmt, bool probe, int act) {
   if (wfmt == W_INT8_ROW) {
-    if (kvfmt == KV_F32) return step_kernel<W_INT8_ROW, KV_F32>(probe);
-    if (kvfmt == KV_BF16) return step_kernel<W_INT8_ROW, KV_BF16>(probe);
-    return step_kernel<W_INT8_ROW, KV_I8>(probe);
+    if (kvfmt == KV_F32) return step_kernel<W_INT8_ROW, KV_F32>(probe, act);
+    if (kvfmt == KV_BF16) return step_kernel<W_INT8_ROW, KV_BF16>(probe, act);
+    return step_kernel<W_INT8_ROW, KV_I8>(probe, act);
   }
   if (wfmt == W_Q8_0) {
-    if (kvfmt == KV_F32) return step_kernel<W_Q8_0, KV_F32>(probe);
-    if (kvfmt == KV_BF16) return step_kernel<W_Q8_0, KV_BF16>(probe);
-    return step_kernel<W_Q8_0, KV_I8>(probe);
+    if (kvfmt == KV_F32) return step_kernel<W_Q8_0, KV_F32>(probe, act);
+    if (kvfmt == KV_BF16) return step_kernel<W_Q8_0, KV_BF16>(probe, act);
+    return step_kernel<W_Q8_0, KV_I8>(probe, act);
   }
-  if (kvfmt == KV_F32) return step_kernel<W_BF16, KV_F32>(probe);
-  if (kvfmt == KV_BF16) return step_kernel<W_BF16, KV_BF16>(probe);
-  return step_kernel<W_BF16, KV_I8>(probe);
+  if (kvfmt == KV_F32) return step_kernel<W_BF16, KV_F32>(probe, act);
+  if (kvfmt == KV_BF16) return step_kernel<W_BF16, KV_BF16>(probe, act);
+  return step_kernel<W_BF16, KV_I8>(probe, act);
 }
 
 }  // namespace
@@ -1544,17 +1551,17 @@ int persistent_tags_per_step(const Dims& d) { return d.L * kTagsPerLayer + 1; }
 
 hipError_t persistent_prepare(const Dims& d, size_t smem, int* blocks_per_cu) {
   for (const bool probe : {true, false}) {
-    hipError_t r = hipFuncSetAttribute(pick(d.wfmt, d.kvfmt, probe), hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)smem);
+    hipError_t r = hipFuncSetAttribute(pick(d.wfmt, d.kvfmt, probe, d.act),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
     if (r != hipSuccess) return r;
   }
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, pick(d.wfmt, d.kvfmt, false), PT, smem);
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, pick(d.wfmt, d.kvfmt, false, d.act), PT, smem);
 }
 
 hipError_t launch_persistent(const PersistArgs& a, int nwg, size_t smem, hipStream_t st) {
   void* args[] = {(void*)&a};
-  return hipLaunchCooperativeKernel(pick(a.d.wfmt, a.d.kvfmt, a.inject != nullptr), dim3(nwg), dim3(PT), args,
-                                    (unsigned)smem, st);
+  return hipLaunchCooperativeKernel(pick(a.d.wfmt, a.d.kvfmt, a.inject != nullptr, a.d.act), dim3(nwg), dim3(PT),
+                                    args, (unsigned)smem, st);
 }
 
 }  // namespace dtd
