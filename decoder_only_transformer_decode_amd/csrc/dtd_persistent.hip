@@ -40,6 +40,8 @@ namespace {
 using namespace dev;
 
 constexpr int PW = kPersistWaves;   // waves per workgroup
+constexpr int kLogPW = __builtin_ctz(PW);
+static_assert((PW & (PW - 1)) == 0, "waves per workgroup: a power of two");
 constexpr int PT = PW * 64;         // threads per workgroup
 constexpr int GRP = 2;              // lines per lane in one prefetch group
 constexpr unsigned kSpinLimit = 1u << 20;
@@ -262,15 +264,16 @@ __device__ __forceinline__ PPhase make_phase(const MatDev& m, int g, int nwg) {
   // With fewer pairs than waves, sp waves share each pair, each taking a contiguous range of
   // its lines, so that every wave keeps loads in flight; their partial results meet in the
   // epilogue.
-  int sp = 1;
-  while (2 * sp <= PW && 2 * sp * p.np <= PW && 2 * sp <= cpr) sp *= 2;
+  // (sp and ws are powers of two: their divisions are shifts)
+  int sp = 1, lsp = 0;
+  while (2 * sp <= PW && 2 * sp * p.np <= PW && 2 * sp <= cpr) sp *= 2, lsp++;
   p.sp = sp;
-  const int ws = PW / sp, wave = wave_id();
-  const int part = wave / ws, wl = wave - part * ws;
-  const int ch = (cpr + sp - 1) / sp;
+  const int lws = kLogPW - lsp, ws = PW >> lsp, wave = wave_id();
+  const int part = wave >> lws, wl = wave & (ws - 1);
+  const int ch = (cpr + sp - 1) >> lsp;
   p.jb = min(cpr, part * ch);
   p.je = min(cpr, p.jb + ch);
-  const int npw = p.np > wl ? (p.np - wl + ws - 1) / ws : 0;
+  const int npw = p.np > wl ? (p.np - wl + ws - 1) >> lws : 0;
   p.total = 2 * npw * (p.je - p.jb);
   p.pb = g + nwg * wl;
   p.pst = nwg * ws;
@@ -1193,11 +1196,17 @@ __global__ __launch_bounds__(PT) void k_step(PersistArgs a) {
     // out here, while the input below is still on its way, not between the input and the
     // projection.
     PPhase nx;
-    if (k == PH_O) nx = make_phase<WFMT>(cmat(&Ly->gu), g, nwg);
-    else if (k == PH_GU) nx = make_phase<WFMT>(cmat(&Ly->down), g, nwg);
-    else if (k == PH_DOWN && l + 1 < d.L) nx = make_phase<WFMT>(cmat(&layers[l + 1].qkv), g, nwg);
-    else if (k == PH_DOWN && do_head) nx = make_phase<WFMT>(a.head, g, nwg);
-    else nx = empty_phase(dummy);
+    {
+      // the matrix is picked first, so that the descriptor's arithmetic has one copy
+      MatDev nm;
+      bool has = true;
+      if (k == PH_O) nm = cmat(&Ly->gu);
+      else if (k == PH_GU) nm = cmat(&Ly->down);
+      else if (k == PH_DOWN && l + 1 < d.L) nm = cmat(&layers[l + 1].qkv);
+      else if (k == PH_DOWN && do_head) nm = a.head;
+      else has = false;
+      nx = has ? make_phase<WFMT>(nm, g, nwg) : empty_phase(dummy);
+    }
 
     // ---- input of the projection ----
     // A probe step takes every wait of a normal step (the waits are what order the reuse of
