@@ -216,11 +216,12 @@ __device__ __forceinline__ void gather(int n, uint32_t tag, int32_t* err, int* f
 
 // LDS position of input element i, for lines of 64 lanes x VEC elements: the q-th float4 of
 // lane l in line j sits at float4 index (j*VEC/4 + q)*64 + l.
+// (i >= 0; unsigned, the divisions are plain shifts)
 template <int VEC>
 __device__ __forceinline__ int swz(int i) {
-  constexpr int KSTEP = 64 * VEC;
-  const int st = i / KSTEP, r = i - st * KSTEP, ln = r / VEC, e = r - ln * VEC;
-  return st * KSTEP + (e >> 2) * 256 + ln * 4 + (e & 3);
+  constexpr unsigned KSTEP = 64 * VEC;
+  const unsigned u = (unsigned)i, st = u / KSTEP, r = u % KSTEP, ln = r / VEC, e = r % VEC;
+  return (int)(st * KSTEP + (e >> 2) * 256 + ln * 4 + (e & 3));
 }
 
 // this thread's wave, as a value the compiler knows is wave-uniform (branches on it become
@@ -1246,7 +1247,8 @@ __global__ __launch_bounds__(PT) void k_step(PersistArgs a) {
       const bool is_o = k == PH_O;
       if (act == ACT_BF16) {   // two values per word
         if (is_o) {
-          stage_tagged_pairs<VEC>(a.t_o, T(l, TG_O), d.q_dim >> 1, d.q_dim, xs, err, &sfail,
+          // (4 words per thread: one round up to q_dim 4096)
+          stage_tagged_pairs<VEC, 4>(a.t_o, T(l, TG_O), d.q_dim >> 1, d.q_dim, xs, err, &sfail,
                                   [](int w, int& i0, int& i1) { i0 = 2 * w; i1 = 2 * w + 1; });
         } else {   // three values per word, 16-bit tag
           const int hs = h_words_per_wg(d.F, nwg);
@@ -1477,7 +1479,7 @@ __global__ __launch_bounds__(PT) void k_step(PersistArgs a) {
     put_tag(a.t_am + 2 * g + 1, thead, __int_as_float(bi));
   }
   if (g != 0) return;
-  gather(2 * nwg, thead, err, &sfail, [&](int t) { return a.t_am + t; }, [&](int t, float v) { xs[t] = v; });
+  gather<1>(2 * nwg, thead, err, &sfail, [&](int t) { return a.t_am + t; }, [&](int t, float v) { xs[t] = v; });
   __syncthreads();
   if (sfail || wave != 0) return;
   float b = -INFINITY;
