@@ -1106,7 +1106,7 @@ enum { PH_QKV = 0, PH_O = 1, PH_GU = 2, PH_DOWN = 3, PH_HEAD = 4 };
 // carries none of that code.
 // ACTT: the activation type as a constant (ACT_F32, ACT_BF16), or -1 to read it from the
 // dimensions (the probe variants).
-template <int WFMT, int KVFMT, bool PROBE, int ACTT>
+template <int WFMT, int KVFMT, bool PROBE, int ACTT, int HD>
 __global__ __launch_bounds__(PT) void k_step(PersistArgs a) {
   constexpr int VEC = PVec<WFMT>::VEC;
   // Dynamic LDS is placed after the static variables below; without the alignment it would
@@ -1117,7 +1117,11 @@ __global__ __launch_bounds__(PT) void k_step(PersistArgs a) {
   __shared__ float wbest[PW];
   __shared__ int widx[PW];
   __shared__ float rope_s[128];       // cos | sin of this step's position (hd <= 128)
-  const Dims& d = a.d;
+  // The head size as a constant where the instantiation names one (HD > 0): the attention
+  // item's and the merge's divisions, strides and split counts by it then fold away.
+  Dims dv = a.d;
+  if constexpr (HD > 0) dv.hd = HD;
+  const Dims& d = dv;
   const int g = blockIdx.x, nwg = gridDim.x, tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   constexpr bool probe = PROBE;
@@ -1499,27 +1503,32 @@ __global__ __launch_bounds__(PT) void k_step(PersistArgs a) {
   PTRACE(3 + d.L * 11);
 }
 
+// the probe step, and the normal step per activation type, each with the head size of the
+// target models (128) fixed or read at run time
 template <int WFMT, int KVFMT>
-const void* step_kernel(bool probe, int act) {
-  if (probe) return (const void*)k_step<WFMT, KVFMT, true, -1>;
-  return act == ACT_BF16 ? (const void*)k_step<WFMT, KVFMT, false, ACT_BF16>
-                         : (const void*)k_step<WFMT, KVFMT, false, ACT_F32>;
+const void* step_kernel(bool probe, int act, int hd) {
+  if (probe) return (const void*)k_step<WFMT, KVFMT, true, -1, 0>;
+  if (hd == 128)
+    return act == ACT_BF16 ? (const void*)k_step<WFMT, KVFMT, false, ACT_BF16, 128>
+                           : (const void*)k_step<WFMT, KVFMT, false, ACT_F32, 128>;
+  return act == ACT_BF16 ? (const void*)k_step<WFMT, KVFMT, false, ACT_BF16, 0>
+                         : (const void*)k_step<WFMT, KVFMT, false, ACT_F32, 0>;
 }
 
-const void* pick(int wfmt, int kvfmt, bool probe, int act) {
+const void* pick(int wfmt, int kvfmt, bool probe, int act, int hd) {
   if (wfmt == W_INT8_ROW) {
-    if (kvfmt == KV_F32) return step_kernel<W_INT8_ROW, KV_F32>(probe, act);
-    if (kvfmt == KV_BF16) return step_kernel<W_INT8_ROW, KV_BF16>(probe, act);
-    return step_kernel<W_INT8_ROW, KV_I8>(probe, act);
+    if (kvfmt == KV_F32) return step_kernel<W_INT8_ROW, KV_F32>(probe, act, hd);
+    if (kvfmt == KV_BF16) return step_kernel<W_INT8_ROW, KV_BF16>(probe, act, hd);
+    return step_kernel<W_INT8_ROW, KV_I8>(probe, act, hd);
   }
   if (wfmt == W_Q8_0) {
-    if (kvfmt == KV_F32) return step_kernel<W_Q8_0, KV_F32>(probe, act);
-    if (kvfmt == KV_BF16) return step_kernel<W_Q8_0, KV_BF16>(probe, act);
-    return step_kernel<W_Q8_0, KV_I8>(probe, act);
+    if (kvfmt == KV_F32) return step_kernel<W_Q8_0, KV_F32>(probe, act, hd);
+    if (kvfmt == KV_BF16) return step_kernel<W_Q8_0, KV_BF16>(probe, act, hd);
+    return step_kernel<W_Q8_0, KV_I8>(probe, act, hd);
   }
-  if (kvfmt == KV_F32) return step_kernel<W_BF16, KV_F32>(probe, act);
-  if (kvfmt == KV_BF16) return step_kernel<W_BF16, KV_BF16>(probe, act);
-  return step_kernel<W_BF16, KV_I8>(probe, act);
+  if (kvfmt == KV_F32) return step_kernel<W_BF16, KV_F32>(probe, act, hd);
+  if (kvfmt == KV_BF16) return step_kernel<W_BF16, KV_BF16>(probe, act, hd);
+  return step_kernel<W_BF16, KV_I8>(probe, act, hd);
 }
 
 }  // namespace
@@ -1562,16 +1571,16 @@ int persistent_tags_per_step(const Dims& d) { return d.L * kTagsPerLayer + 1; }
 
 hipError_t persistent_prepare(const Dims& d, size_t smem, int* blocks_per_cu) {
   for (const bool probe : {true, false}) {
-    hipError_t r = hipFuncSetAttribute(pick(d.wfmt, d.kvfmt, probe, d.act),
+    hipError_t r = hipFuncSetAttribute(pick(d.wfmt, d.kvfmt, probe, d.act, d.hd),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
     if (r != hipSuccess) return r;
   }
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, pick(d.wfmt, d.kvfmt, false, d.act), PT, smem);
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, pick(d.wfmt, d.kvfmt, false, d.act, d.hd), PT, smem);
 }
 
 hipError_t launch_persistent(const PersistArgs& a, int nwg, size_t smem, hipStream_t st) {
   void* args[] = {(void*)&a};
-  return hipLaunchCooperativeKernel(pick(a.d.wfmt, a.d.kvfmt, a.inject != nullptr, a.d.act), dim3(nwg), dim3(PT),
+  return hipLaunchCooperativeKernel(pick(a.d.wfmt, a.d.kvfmt, a.inject != nullptr, a.d.act, a.d.hd), dim3(nwg), dim3(PT),
                                     args, (unsigned)smem, st);
 }
 
