@@ -41,6 +41,7 @@ using namespace dev;
 
 constexpr int PW = kPersistWaves;   // waves per workgroup
 constexpr int kLogPW = __builtin_ctz(PW);
+constexpr int kFixedG = 4, kFixedBs = 16;   // the common attention shape (with head size 128)
 static_assert((PW & (PW - 1)) == 0, "waves per workgroup: a power of two");
 constexpr int PT = PW * 64;         // threads per workgroup
 constexpr int GRP = 2;              // lines per lane in one prefetch group
@@ -1117,10 +1118,15 @@ __global__ __launch_bounds__(PT) void k_step(PersistArgs a) {
   __shared__ float wbest[PW];
   __shared__ int widx[PW];
   __shared__ float rope_s[128];       // cos | sin of this step's position (hd <= 128)
-  // The head size as a constant where the instantiation names one (HD > 0): the attention
-  // item's and the merge's divisions, strides and split counts by it then fold away.
+  // The common attention shape as constants where the instantiation names it (HD > 0: head
+  // size HD, 4 query heads per KV head, KV blocks of 16 positions): the attention item's and
+  // the merge's divisions, strides, loop and split counts by them then fold away.
   Dims dv = a.d;
-  if constexpr (HD > 0) dv.hd = HD;
+  if constexpr (HD > 0) {
+    dv.hd = HD;
+    dv.G = kFixedG;
+    dv.bs = kFixedBs;
+  }
   const Dims& d = dv;
   const int g = blockIdx.x, nwg = gridDim.x, tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
@@ -1503,32 +1509,35 @@ __global__ __launch_bounds__(PT) void k_step(PersistArgs a) {
   PTRACE(3 + d.L * 11);
 }
 
-// the probe step, and the normal step per activation type, each with the head size of the
-// target models (128) fixed or read at run time
+// the probe step, and the normal step per activation type, each with the attention shape of
+// the target models (head size 128, 4 query heads per KV head, KV blocks of 16) fixed or read
+// at run time
 template <int WFMT, int KVFMT>
-const void* step_kernel(bool probe, int act, int hd) {
+const void* step_kernel(bool probe, int act, bool fixed) {
   if (probe) return (const void*)k_step<WFMT, KVFMT, true, -1, 0>;
-  if (hd == 128)
+  if (fixed)
     return act == ACT_BF16 ? (const void*)k_step<WFMT, KVFMT, false, ACT_BF16, 128>
                            : (const void*)k_step<WFMT, KVFMT, false, ACT_F32, 128>;
   return act == ACT_BF16 ? (const void*)k_step<WFMT, KVFMT, false, ACT_BF16, 0>
                          : (const void*)k_step<WFMT, KVFMT, false, ACT_F32, 0>;
 }
 
-const void* pick(int wfmt, int kvfmt, bool probe, int act, int hd) {
+const void* pick(const Dims& d, bool probe) {
+  const int wfmt = d.wfmt, kvfmt = d.kvfmt, act = d.act;
+  const bool fixed = d.hd == 128 && d.G == kFixedG && d.bs == kFixedBs;
   if (wfmt == W_INT8_ROW) {
-    if (kvfmt == KV_F32) return step_kernel<W_INT8_ROW, KV_F32>(probe, act, hd);
-    if (kvfmt == KV_BF16) return step_kernel<W_INT8_ROW, KV_BF16>(probe, act, hd);
-    return step_kernel<W_INT8_ROW, KV_I8>(probe, act, hd);
+    if (kvfmt == KV_F32) return step_kernel<W_INT8_ROW, KV_F32>(probe, act, fixed);
+    if (kvfmt == KV_BF16) return step_kernel<W_INT8_ROW, KV_BF16>(probe, act, fixed);
+    return step_kernel<W_INT8_ROW, KV_I8>(probe, act, fixed);
   }
   if (wfmt == W_Q8_0) {
-    if (kvfmt == KV_F32) return step_kernel<W_Q8_0, KV_F32>(probe, act, hd);
-    if (kvfmt == KV_BF16) return step_kernel<W_Q8_0, KV_BF16>(probe, act, hd);
-    return step_kernel<W_Q8_0, KV_I8>(probe, act, hd);
+    if (kvfmt == KV_F32) return step_kernel<W_Q8_0, KV_F32>(probe, act, fixed);
+    if (kvfmt == KV_BF16) return step_kernel<W_Q8_0, KV_BF16>(probe, act, fixed);
+    return step_kernel<W_Q8_0, KV_I8>(probe, act, fixed);
   }
-  if (kvfmt == KV_F32) return step_kernel<W_BF16, KV_F32>(probe, act, hd);
-  if (kvfmt == KV_BF16) return step_kernel<W_BF16, KV_BF16>(probe, act, hd);
-  return step_kernel<W_BF16, KV_I8>(probe, act, hd);
+  if (kvfmt == KV_F32) return step_kernel<W_BF16, KV_F32>(probe, act, fixed);
+  if (kvfmt == KV_BF16) return step_kernel<W_BF16, KV_BF16>(probe, act, fixed);
+  return step_kernel<W_BF16, KV_I8>(probe, act, fixed);
 }
 
 }  // namespace
@@ -1571,16 +1580,16 @@ int persistent_tags_per_step(const Dims& d) { return d.L * kTagsPerLayer + 1; }
 
 hipError_t persistent_prepare(const Dims& d, size_t smem, int* blocks_per_cu) {
   for (const bool probe : {true, false}) {
-    hipError_t r = hipFuncSetAttribute(pick(d.wfmt, d.kvfmt, probe, d.act, d.hd),
+    hipError_t r = hipFuncSetAttribute(pick(d, probe),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
     if (r != hipSuccess) return r;
   }
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, pick(d.wfmt, d.kvfmt, false, d.act, d.hd), PT, smem);
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, pick(d, false), PT, smem);
 }
 
 hipError_t launch_persistent(const PersistArgs& a, int nwg, size_t smem, hipStream_t st) {
   void* args[] = {(void*)&a};
-  return hipLaunchCooperativeKernel(pick(a.d.wfmt, a.d.kvfmt, a.inject != nullptr, a.d.act, a.d.hd), dim3(nwg), dim3(PT),
+  return hipLaunchCooperativeKernel(pick(a.d, a.inject != nullptr), dim3(nwg), dim3(PT),
                                     args, (unsigned)smem, st);
 }
 

@@ -113,11 +113,12 @@ _FORMATS = [
     dict(n_q_heads=4, n_kv_heads=4, head_dim=16, wfmt=synth.W_BF16),   # MHA, q_dim != D
     dict(wfmt=synth.W_Q8_0),                                            # Q8_0 with fp32 KV
     dict(wfmt=synth.W_BF16, act=synth.ACT_BF16, kvfmt=synth.KV_I8),
-    # head size 128, which the batch-1 step kernel is also built for with the size fixed at
-    # compile time: each activation type and each weight and KV encoding at least once
-    dict(n_q_heads=4, n_kv_heads=2, head_dim=128),
-    dict(n_q_heads=4, n_kv_heads=2, head_dim=128, wfmt=synth.W_Q8_0, act=synth.ACT_BF16, kvfmt=synth.KV_I8),
-    dict(n_q_heads=4, n_kv_heads=2, head_dim=128, wfmt=synth.W_BF16, act=synth.ACT_BF16, kvfmt=synth.KV_BF16),
+    # head size 128 with 4 query heads per KV head (and the default 16-position KV blocks),
+    # the shape the batch-1 step kernel is also built for with those sizes fixed at compile
+    # time: each activation type and each weight and KV encoding at least once
+    dict(n_q_heads=8, n_kv_heads=2, head_dim=128),
+    dict(n_q_heads=8, n_kv_heads=2, head_dim=128, wfmt=synth.W_Q8_0, act=synth.ACT_BF16, kvfmt=synth.KV_I8),
+    dict(n_q_heads=8, n_kv_heads=2, head_dim=128, wfmt=synth.W_BF16, act=synth.ACT_BF16, kvfmt=synth.KV_BF16),
 ]
 
 
