@@ -372,10 +372,145 @@ def test_gqa_model_with_equal_heads_is_mha_and_kv_roundtrip():
     assert np.array_equal(k, kr.astype(np.float64)) and np.array_equal(v, vr.astype(np.float64))
 
 
+# ------------------------------------------------------------------------------------
+# independent roundings for the brute-force forward (not the oracle's C code)
+# ------------------------------------------------------------------------------------
+
+def bf16_rne(x) -> np.ndarray:
+    """float64 -> the nearest bf16 value (ties to even), as float64, with ONE rounding.
+
+    torch's float64 -> bfloat16 conversion goes through float32 and so rounds twice; here
+    torch's float64 -> float32 conversion (one correct rounding) is followed by its
+    float32 -> bfloat16 conversion, and where the float32 value is itself a bf16 midpoint
+    (its low 16 bits are 0x8000, so that second step decided a tie the exact value may not
+    have had) the exact value picks the neighbour on its own side."""
+    x = np.asarray(x, dtype=np.float64)
+    f = torch.from_numpy(np.ascontiguousarray(x)).float()
+    out = f.to(torch.bfloat16).float().numpy().astype(np.float64)
+    bits = f.numpy().view(np.uint32)
+    mid = (bits & np.uint32(0xFFFF)) == np.uint32(0x8000)
+    fx = f.numpy().astype(np.float64)
+    away = mid & (np.abs(x) > np.abs(fx))       # exact value beyond the midpoint
+    toward = mid & (np.abs(x) < np.abs(fx))     # exact value short of it
+    lo = (bits & np.uint32(0xFFFF0000)).view(np.float32).astype(np.float64)   # smaller magnitude
+    hi = ((bits & np.uint32(0xFFFF0000)) + np.uint32(0x10000)).view(np.float32).astype(np.float64)
+    out = np.where(away, hi, np.where(toward, lo, out))
+    return out
+
+
+def kv_quant_i8_ref(x):
+    """int8 KV code of one (token, KV head) vector, written from the reading of the int8-KV
+    rule: s = fp16(max|x| / 127) rounded once to nearest even (NumPy's float64 -> float16
+    conversion, pinned in test_fp16_round_and_decode_vs_numpy), q = rint(x / s) (NumPy rint:
+    ties to even) clamped to [-127, 127], and s = 0 gives q = 0.  Returns (q int8, s16 bits)."""
+    x = np.asarray(x, dtype=np.float64)
+    s16 = np.float16(np.abs(x).max() / 127.0)
+    s = float(s16)
+    if s == 0.0:
+        return np.zeros(x.shape, dtype=np.int8), 0
+    q = np.clip(np.rint(x / s), -127, 127).astype(np.int8)
+    return q, int(np.array([s16]).view(np.uint16)[0])
+
+
+def test_bf16_rne_helper_and_oracle_at_float64_midpoints():
+    # closed forms: 1 + 2^-8 is the midpoint between 1 and 1 + 2^-7 (the bf16 spacing at 1)
+    cases = [
+        (1 + 2.0 ** -8, 1.0),                          # exact tie -> even (1.0)
+        (1 + 2.0 ** -8 + 2.0 ** -30, 1 + 2.0 ** -7),   # just above the midpoint
+        (1 + 2.0 ** -8 - 2.0 ** -30, 1.0),             # just below it
+        (1 + 3 * 2.0 ** -8, 1 + 2.0 ** -6),            # tie between odd 1+2^-7 and even 1+2^-6
+        (-(1 + 2.0 ** -8 + 2.0 ** -40), -(1 + 2.0 ** -7)),
+        (3 * 2.0 ** -9 + 2.0 ** -40, 3 * 2.0 ** -9),   # a grid point plus far less than half a step
+    ]
+    xs = np.array([c[0] for c in cases])
+    want = np.array([c[1] for c in cases])
+    assert np.array_equal(bf16_rne(xs), want)
+    got = np.array([oracle.bf16_to_double(oracle.double_to_bf16(float(v))) for v in xs])
+    assert np.array_equal(got, want)
+    # and on random float64 values, where float32 double rounding would disagree only rarely
+    rng = np.random.default_rng(21)
+    v = rng.standard_normal(20000) * np.exp(rng.uniform(-20, 20, 20000))
+    got = np.array([oracle.bf16_to_double(oracle.double_to_bf16(float(a))) for a in v])
+    assert np.array_equal(got, bf16_rne(v))
+
+
+def test_kv_int8_codes_exact_with_constructed_midpoints():
+    """The oracle's int8-KV quantiser equals the reference bit for bit, including scales
+    that sit exactly on an fp16 rounding midpoint and codes exactly on a half integer."""
+    vecs = []
+    # scale tie: amax / 127 = 1 + 2^-11, the midpoint between 1 and 1 + 2^-10 -> even (1.0)
+    m = 1 + 2.0 ** -11
+    vecs.append(np.array([127 * m, 0.3, -0.7, 5.0]))
+    # just above / below that midpoint (one float32 step of amax)
+    up = np.nextafter(np.float32(127 * m), np.float32(200))
+    dn = np.nextafter(np.float32(127 * m), np.float32(0))
+    vecs.append(np.array([float(up), 1.0]))
+    vecs.append(np.array([float(dn), 1.0]))
+    # the odd-to-even case: amax / 127 = 1 + 3 * 2^-11 (between odd 1+2^-10 and even 1+2^-9)
+    vecs.append(np.array([127 * (1 + 3 * 2.0 ** -11), -2.0]))
+    # a float64 amax just above that midpoint, closer than float32 resolves: the exact
+    # quotient rounds up; a float32 quotient would land on the midpoint and round to even
+    vecs.append(np.array([127 * m * (1 + 2.0 ** -40), 1.0]))
+    # codes on half integers: s = 2^-6 exactly, x = (k + 1/2) s -> even k
+    s = 2.0 ** -6
+    vecs.append(np.array([127 * s, 2.5 * s, 3.5 * s, -2.5 * s, -3.5 * s, 0.5 * s, -0.5 * s, 126.5 * s]))
+    # a scale in the fp16 subnormal range that rounds down, so max|x| / s > 127.5: clamp
+    vecs.append(np.array([127 * 1.4 * 2.0 ** -24, -127 * 1.4 * 2.0 ** -24, 1e-9]))
+    # a scale that rounds to zero
+    vecs.append(np.array([1e-9, -3e-10]))
+    # random vectors of float32 values (what the cache is fed) at several magnitudes
+    rng = np.random.default_rng(22)
+    for sc in (1e-4, 1e-2, 1.0, 30.0):
+        for _ in range(50):
+            vecs.append(rng.standard_normal(128).astype(np.float32).astype(np.float64) * sc)
+    for x in vecs:
+        qo, so = oracle.kv_quant_i8(x)
+        qr, sr = kv_quant_i8_ref(x)
+        assert so == sr, (x, so, sr)
+        assert np.array_equal(qo, qr), (x, qo, qr)
+    # the constructed cases land where intended
+    assert kv_quant_i8_ref(vecs[0])[1] == 0x3C00                 # 1.0: tie to even
+    assert kv_quant_i8_ref(vecs[1])[1] == 0x3C01                 # above: 1 + 2^-10
+    assert kv_quant_i8_ref(vecs[2])[1] == 0x3C00                 # below: 1.0
+    assert kv_quant_i8_ref(vecs[3])[1] == 0x3C02                 # odd -> even neighbour
+    assert kv_quant_i8_ref(vecs[4])[1] == 0x3C01                 # float64 above the midpoint
+    assert kv_quant_i8_ref(vecs[5])[0].tolist() == [127, 2, 4, -2, -4, 0, 0, 126]
+    assert kv_quant_i8_ref(vecs[6])[0].tolist()[:2] == [127, -127]
+    assert kv_quant_i8_ref(vecs[7])[1] == 0 and not kv_quant_i8_ref(vecs[7])[0].any()
+
+
+def test_kv_int8_fp32_arithmetic_rounds_once():
+    """The cache quantises float32 vectors with float32 arithmetic: s16 = fp16(RN32(amax /
+    127)) and q = rint(RN32(x / s)).  For float32 operands both equal the single roundings
+    of the exact quotients (the int8-KV reading): a float32 amax is never close enough to
+    127 x an fp16 midpoint for the float32 quotient to land on that midpoint, and x / s
+    (24-bit by 11-bit) is never within half a float32 step of a half integer it does not
+    equal.  Checked here on every float32 amax of four binades and on the codes of every
+    float32 x of one binade for a spread of scales; an exhaustive run over every float32
+    amax in [2^-40, 65504 x 127] (5.3e8 values) found no difference either."""
+    for e in (-12, -7, 0, 6):   # amax in [2^e, 2^(e+1)): scales from subnormal fp16 to ~1
+        lo = np.float32(2.0 ** e).view(np.uint32)
+        a = np.arange(lo, lo + (1 << 23), dtype=np.uint32).view(np.float32)
+        via32 = (a / np.float32(127.0)).astype(np.float16).view(np.uint16)
+        exact = (a.astype(np.float64) / 127.0).astype(np.float16).view(np.uint16)
+        assert np.array_equal(via32, exact), e
+    lo = np.float32(1.0).view(np.uint32)
+    x = np.arange(lo, lo + (1 << 23), dtype=np.uint32).view(np.float32)     # every x in [1, 2)
+    rng = np.random.default_rng(23)
+    for s16 in np.concatenate([[0x2400, 0x2401, 0x2BFF, 0x1C00], rng.integers(0x1000, 0x3C00, 8)]).astype(np.uint16):
+        sc = np.array([s16], dtype=np.uint16).view(np.float16).astype(np.float32)[0]
+        via32 = np.rint(x / sc)
+        exact = np.rint(x.astype(np.float64) / np.float64(sc))
+        assert np.array_equal(via32.astype(np.float64), exact), hex(int(s16))
+
+
 def _torch_forward(shape, weights, tokens):
     """Independent brute-force forward of a whole prefix in float64 torch, built from
     library routines (rms_norm, causal scaled_dot_product_attention with GQA, silu) and
-    complex-number RoPE.  Activation and KV rounding to binary32 at the same points."""
+    complex-number RoPE, with the storage roundings of the configuration written
+    separately from the oracle: the activation type (binary32 via torch, or bf16 via
+    bf16_rne) at each RMSNorm output, the attention output and the SwiGLU output; the KV
+    type (binary32, bf16, or kv_quant_i8_ref per token and KV head) on the stored k and v."""
     D, hd = shape.dim, shape.head_dim
     n = len(tokens)
 
@@ -391,6 +526,24 @@ def _torch_forward(shape, weights, tokens):
     def r32(t):
         return t.float().double()
 
+    def rbf(t):
+        return torch.from_numpy(bf16_rne(t.numpy()).reshape(t.shape))
+
+    ract = rbf if shape.act == synth.ACT_BF16 else r32
+
+    def rkv(t):                        # t [n, kv heads, hd], post-RoPE k or v
+        if shape.kvfmt == synth.KV_F32:
+            return r32(t)
+        if shape.kvfmt == synth.KV_BF16:
+            return rbf(t)
+        a = t.numpy()
+        out = np.empty_like(a)
+        for i in range(a.shape[0]):
+            for j in range(a.shape[1]):
+                q, s16 = kv_quant_i8_ref(a[i, j])
+                out[i, j] = q.astype(np.float64) * float(np.array([s16], np.uint16).view(np.float16)[0])
+        return torch.from_numpy(out)
+
     def rope(t):                       # t [n, heads, hd]
         half = hd // 2
         z = torch.complex(t[..., :half], t[..., half:])
@@ -403,28 +556,47 @@ def _torch_forward(shape, weights, tokens):
     x = r32(emb[torch.as_tensor(tokens, dtype=torch.long)])     # fp32 dequant of the rows
     for i in range(shape.n_layers):
         g = lambda nm: torch.from_numpy(weights[f"L{i}.{nm}"]["g"].astype(np.float64))
-        xn = r32(F.rms_norm(x, (D,), weight=g("attn_norm"), eps=shape.rms_eps))
+        xn = ract(F.rms_norm(x, (D,), weight=g("attn_norm"), eps=shape.rms_eps))
         q = (xn @ deq(f"L{i}.wq").T).view(n, shape.n_q_heads, hd)
         k = (xn @ deq(f"L{i}.wk").T).view(n, shape.n_kv_heads, hd)
         v = (xn @ deq(f"L{i}.wv").T).view(n, shape.n_kv_heads, hd)
-        q, k = rope(q), r32(rope(k))
-        v = r32(v)
+        q, k = rope(q), rkv(rope(k))
+        v = rkv(v)
         o = F.scaled_dot_product_attention(q.transpose(0, 1)[None], k.transpose(0, 1)[None].contiguous(),
                                            v.transpose(0, 1)[None].contiguous(),
                                            is_causal=True, enable_gqa=True)[0].transpose(0, 1)
-        o = r32(o.reshape(n, -1))
+        o = ract(o.reshape(n, -1))
         x = x + o @ deq(f"L{i}.wo").T
-        xn = r32(F.rms_norm(x, (D,), weight=g("ffn_norm"), eps=shape.rms_eps))
-        h = r32(F.silu(xn @ deq(f"L{i}.w_gate").T) * (xn @ deq(f"L{i}.w_up").T))
+        xn = ract(F.rms_norm(x, (D,), weight=g("ffn_norm"), eps=shape.rms_eps))
+        h = ract(F.silu(xn @ deq(f"L{i}.w_gate").T) * (xn @ deq(f"L{i}.w_up").T))
         x = x + h @ deq(f"L{i}.w_down").T
     fin = torch.from_numpy(weights["final_norm"]["g"].astype(np.float64))
-    xn = r32(F.rms_norm(x[-1], (D,), weight=fin, eps=shape.rms_eps))
+    xn = ract(F.rms_norm(x[-1], (D,), weight=fin, eps=shape.rms_eps))
     head = emb if shape.tied else deq("lm_head")
     return (xn @ head.T).float().numpy(), x[-1].numpy()
 
 
-@pytest.mark.parametrize("kw", [dict(), dict(wfmt=synth.W_Q8_0, tied=True), dict(wfmt=synth.W_BF16)])
+# the weight, activation and KV formats of every configuration the library is measured on
+_FORWARD_FORMATS = [
+    dict(),                                                                   # tiny
+    dict(act=synth.ACT_BF16, kvfmt=synth.KV_BF16),                            # SmolLM3-3B shape
+    dict(wfmt=synth.W_Q8_0, act=synth.ACT_BF16, kvfmt=synth.KV_BF16, tied=True),   # Llama-3.2-1B
+    dict(wfmt=synth.W_BF16, act=synth.ACT_BF16, kvfmt=synth.KV_BF16),         # Qwen3-8B shape
+    dict(act=synth.ACT_BF16, kvfmt=synth.KV_I8),                              # Llama-3-8B shape
+    dict(wfmt=synth.W_Q8_0, tied=True),
+    dict(wfmt=synth.W_BF16),
+    dict(wfmt=synth.W_Q8_0, act=synth.ACT_BF16, kvfmt=synth.KV_I8, n_kv_heads=1),
+]
+
+
+@pytest.mark.parametrize("kw", _FORWARD_FORMATS,
+                         ids=lambda kw: "-".join(f"{k}={v}" for k, v in kw.items()) or "base")
 def test_oracle_matches_brute_force_torch_forward(kw):
+    """Both sides compute in float64 and round at the same points, so they agree to float64
+    reassociation noise (~1e-16 relative): a rounding point moved, added or dropped on
+    either side shifts the residual stream by at least a binary32 step (~6e-8 relative),
+    or a bf16 step (~4e-3), far above the bound.  (A rounding could only come out
+    differently if an unrounded value fell within ~1e-16 of a rounding midpoint.)"""
     shape = synth.tiny_shape(**kw)
     m, w = _model(shape, max_ctx=12)
     toks = synth.prompt_tokens(shape.vocab, 12, seed=4)
@@ -432,7 +604,9 @@ def test_oracle_matches_brute_force_torch_forward(kw):
         nxt, logits, hid = m.step(0, toks[t], t, want_hidden=True)
     ref_logits, ref_x = _torch_forward(shape, w, toks)
     scale = np.abs(ref_logits).max()
-    assert np.max(np.abs(logits - ref_logits)) <= 1e-5 * scale
-    assert np.allclose(hid[-1], ref_x, rtol=1e-5, atol=1e-6 * np.abs(ref_x).max())
-    if np.sort(ref_logits)[-1] - np.sort(ref_logits)[-2] > 1e-4 * scale:
+    # logits are stored as binary32 on both sides: within a couple of binary32 steps
+    assert np.max(np.abs(logits - ref_logits)) <= 1e-6 * scale
+    # the float64 residual stream after the last layer
+    assert np.max(np.abs(hid[-1] - ref_x)) <= 1e-11 * np.abs(ref_x).max()
+    if np.sort(ref_logits)[-1] - np.sort(ref_logits)[-2] > 1e-5 * scale:
         assert nxt == int(np.argmax(ref_logits))
