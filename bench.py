@@ -73,37 +73,46 @@ def kernel_source_hash() -> str:
     return h.hexdigest()
 
 
-def recorded_traffic(workload: str):
+def recorded_traffic(workload: str, attended: str):
     """HBM bytes per step-kernel launch from the committed FETCH_SIZE / WRITE_SIZE readings of
-    this workload (each scaled by what the counter reads for a plain copy of known size), or
-    None when there are none or the kernel's sources have changed since they were taken."""
+    this workload over the same attended contexts (each counter scaled by what it reads for
+    a plain copy of known size), or None when there are none, they cover other contexts, or
+    the kernel's sources have changed since they were taken."""
     path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", f"k_step_traffic_{workload}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         r = json.load(f)
-    if r.get("kernel_source_sha256") != kernel_source_hash():
+    if r.get("kernel_source_sha256") != kernel_source_hash() or r.get("attended") != attended:
         return None
     return (r["fetch_kib_per_launch"] * r["fetch_scale"] + r["write_kib_per_launch"] * r["write_scale"]) * 1024.0
 
 
-def cpu_baseline(w: synth.Workload, weights, ctx_mid: int, n_steps: int) -> dict:
-    """The oracle, as it stands, on this host: n_steps decode steps at contexts around the
-    middle of the decoded range, from synthetic stored KV."""
+def cpu_baseline(w: synth.Workload, weights, n_steps: int) -> dict:
+    """The oracle, as it stands, on this host: n_steps decode steps ending at the workload's
+    context (synthetic stored KV before them), with every core OpenMP offers, then with one."""
     import oracle
     s = w.shape
-    m = oracle.Model(s, weights, max_ctx=w.context, max_seqs=1)
-    for layer in range(s.n_layers):
-        k, v, ks, vs = synth.synthetic_kv(s, ctx_mid, seed=5, layer=layer)
-        m.kv_write(0, layer, 0, k, v, ks, vs)
-    tok = 17
-    t0 = time.perf_counter()
-    for i in range(n_steps):
-        tok, _, _ = m.step(0, tok, ctx_mid + i)
-    dt = time.perf_counter() - t0
-    return {"value": n_steps / dt, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"{n_steps} batch-1 decode steps at attended context {ctx_mid + 1}..{ctx_mid + n_steps} "
-                      f"(synthetic stored KV), fp64 oracle, {dt:.1f} s"}
+    pos0 = w.context - n_steps
+    out = {}
+    for label, threads in (("all", oracle.num_threads()), ("one", 1)):
+        oracle.set_num_threads(threads)
+        m = oracle.Model(s, weights, max_ctx=w.context, max_seqs=1)
+        for layer in range(s.n_layers):
+            k, v, ks, vs = synth.synthetic_kv(s, pos0, seed=5, layer=layer)
+            m.kv_write(0, layer, 0, k, v, ks, vs)
+        tok = 17
+        t0 = time.perf_counter()
+        for i in range(n_steps):
+            tok, _, _ = m.step(0, tok, pos0 + i)
+        out[label] = (n_steps / (time.perf_counter() - t0), threads)
+        del m
+    oracle.set_num_threads(out["all"][1])
+    return {"value": round(out["all"][0], 4), "unit": "tokens/s", "cores": out["all"][1], "kind": "oracle",
+            "value_1_thread": round(out["one"][0], 4),
+            "sample": f"{n_steps} batch-1 decode steps at attended context {pos0 + 1}..{w.context} "
+                      f"(synthetic stored KV before them), fp64 oracle, with {out['all'][1]} OpenMP threads "
+                      f"and again with 1"}
 
 
 def main():
@@ -112,9 +121,10 @@ def main():
     ap.add_argument("--steps", type=int, default=1536)
     ap.add_argument("--warmup", type=int, default=16)
     ap.add_argument("--workload", default=synth.SMOLLM3_3B.shape.name, choices=sorted(synth.BY_NAME))
-    ap.add_argument("--cpu-steps", type=int, default=40)
+    ap.add_argument("--cpu-steps", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true")
+    ap.add_argument("--no-read-ceiling", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only copy MIB MiB device to device 3 times and exit: the plain copy whose "
                          "FETCH_SIZE / WRITE_SIZE counter readings scale the step kernel's")
@@ -142,9 +152,14 @@ def main():
         print("only the batch-1 workloads are benchmarked here", file=sys.stderr)
         sys.exit(2)
     K, W = args.steps, args.warmup
-    if w.prompt_len + K > w.context:
-        print(f"--steps {K} would run past context {w.context}", file=sys.stderr)
+    # The K timed steps end at the workload's context: the first takes position start.
+    start = w.context - K
+    if K < 1 or start < 1:
+        print(f"--steps {K} does not fit below context {w.context}", file=sys.stderr)
         sys.exit(2)
+    # prefill the workload's prompt and decode up to start, or synthetic KV up to start
+    real_prompt = not w.synthetic_prefix and w.prompt_len <= start
+    attended = f"{start + 1}..{w.context}"
 
     t0 = time.perf_counter()
     weights = synth.gen_weights(s, synth.weights_seed(w))
@@ -160,38 +175,55 @@ def main():
           f"{'persistent step kernel' if persistent else 'one kernel per sub-step'}", file=sys.stderr, flush=True)
 
     prompt = torch.as_tensor(synth.prompt_tokens(s.vocab, w.prompt_len)).to(dev)
-    tok = torch.zeros(1, dtype=torch.int32, device=dev)
+    hist = torch.zeros(K + 1, dtype=torch.int32, device=dev)     # tokens of the timed steps
 
-    def decode(n):
-        for _ in range(n):
-            dtd.dtd_decode_step(eng.h, [0], tok.data_ptr(), tok.data_ptr())
+    def decode_on(seq, buf, n):
+        """n greedy steps of seq: step i reads buf[i] and writes its next token to buf[i + 1]."""
+        base = buf.data_ptr()
+        for i in range(n):
+            dtd.dtd_decode_step(eng.h, [seq], base + 4 * i, base + 4 * (i + 1))
 
-    def fresh_sequence():
-        if eng.seq_len(0) >= 0:
-            eng.reset_seq(0)
-        nxt, _ = eng.prefill(0, prompt)
-        tok.copy_(nxt)
+    def build_sequence(seq, length):
+        """seq at `length` positions, its next token in hist[0]: the workload's prompt then
+        greedy decode steps, or synthetic KV (workloads that decode at a fixed context)."""
+        if eng.seq_len(seq) >= 0:
+            eng.reset_seq(seq)
+        if real_prompt:
+            nxt, _ = eng.prefill(seq, prompt)
+            fill = torch.zeros(length - w.prompt_len + 1, dtype=torch.int32, device=dev)
+            fill[0] = nxt[0]
+            decode_on(seq, fill, length - w.prompt_len)
+            hist[0] = fill[-1]
+        else:
+            dtd.dtd_debug_kv_fill(eng.h, seq, length, 5)
+            hist[0] = 17
         torch.cuda.synchronize()
 
-    # warmup: W steps on a throwaway sequence
-    fresh_sequence()
-    decode(W)
+    # warmup: W steps on another sequence at the same contexts
+    build_sequence(1, start)
+    warm = torch.zeros(W + 1, dtype=torch.int32, device=dev)
+    warm[0] = hist[0]
+    decode_on(1, warm, W)
     torch.cuda.synchronize()
+    dtd.dtd_check_device_errors(eng.h)
+    eng.reset_seq(1)
 
-    # timed region: K greedy steps from position 512, the token fed back on the device
-    fresh_sequence()
+    # timed region: K greedy steps, the token fed back on the device
+    build_sequence(0, start)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    decode(K)
+    decode_on(0, hist, K)
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
-    assert eng.seq_len(0) == w.prompt_len + K
+    dtd.dtd_check_device_errors(eng.h)     # a device-side wait that gave up, or a bad token id
+    assert eng.seq_len(0) == w.context
+    tokens = hist.cpu().numpy().copy()
 
     wb = weight_bytes(s)
     wtot = sum(v for k, v in wb.items() if k != "per_layer")
     kvpp = kv_bytes_per_position(s)
-    attended = np.arange(w.prompt_len + 1, w.prompt_len + K + 1, dtype=np.float64)
-    kv_total = float(kvpp * attended.sum())
+    attended_t = np.arange(start + 1, w.context + 1, dtype=np.float64)
+    kv_total = float(kvpp * attended_t.sum())
     bytes_total = wtot * K + kv_total
     gbs = bytes_total / dt / 1e9
 
@@ -199,32 +231,53 @@ def main():
     if not args.no_kernel_timing:
         # the same workload again with HIP events around every launch of the kernel that
         # moves the most bytes, on the engine's stream: the persistent step kernel (weights
-        # + KV of one step per launch) or, per sub-step, the gate/up projection
-        fresh_sequence()
+        # + KV of one step per launch) or, per sub-step, the gate/up projection; the greedy
+        # tokens must repeat those of the timed run
+        build_sequence(0, start)
         kind = dtd.KERNEL_STEP if persistent else dtd.KERNEL_GATE_UP
         dtd.dtd_debug_kernel_timing(eng.h, kind, True)
-        decode(K)
+        decode_on(0, hist, K)
         ms, cnt = dtd.dtd_debug_kernel_timing(eng.h, kind, False)
+        dtd.dtd_check_device_errors(eng.h)
+        again = hist.cpu().numpy()
+        if not np.array_equal(again, tokens):
+            print(f"[bench] the rerun's greedy tokens differ from the timed run's "
+                  f"(first at step {int(np.flatnonzero(again != tokens)[0])})", file=sys.stderr)
+            sys.exit(1)
         if persistent:
             per_launch = wtot + kv_total / K
-            name = "k_step (persistent batch-1 decode step, int8-row weights, bf16 KV)"
+            name = (f"k_step (persistent batch-1 decode step, {synth.WFMT_NAMES[s.wfmt]} weights, "
+                    f"{synth.KV_NAMES[s.kvfmt]} KV)")
         else:
             per_launch = wb["per_layer"]["gate_up"]
-            name = "k_gemv (gate/up projection, int8-row, SwiGLU epilogue)"
+            name = "k_gemv (gate/up projection, SwiGLU epilogue)"
         avg_s = ms / 1e3 / max(cnt, 1)
         ach = per_launch / avg_s / 1e9 if cnt else 0.0
-        traffic = recorded_traffic(s.name) if persistent else None
+        traffic = recorded_traffic(s.name, attended) if persistent else None
         roofline = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                     "frac": round(ach / PEAK_HBM_GBS, 4),
                     "traffic": None if traffic is None else round(traffic), "kernel": name,
                     "bytes_per_launch": round(per_launch), "avg_launch_us": round(avg_s * 1e6, 2),
                     "launches": cnt}
 
+    ceiling = None
+    if not args.no_read_ceiling:
+        buf = torch.empty(8 << 30, dtype=torch.uint8, device=dev)
+        ceiling = dtd.dtd_debug_stream_read(buf.data_ptr(), buf.numel(), 10, torch.cuda.current_stream().cuda_stream)
+        del buf
+        torch.cuda.empty_cache()
+        if roofline is not None:
+            roofline["measured_read_ceiling_gbs"] = round(ceiling, 1)
+            roofline["frac_of_measured_ceiling"] = round(roofline["achieved"] / ceiling, 4)
+
     cpu = None
     if not args.no_cpu_baseline:
-        ctx_mid = (w.prompt_len + w.context) // 2
-        cpu = cpu_baseline(w, weights, ctx_mid, args.cpu_steps)
+        cpu = cpu_baseline(w, weights, args.cpu_steps)
 
+    if real_prompt:
+        how = f"prefill {w.prompt_len} random tokens, greedy decode to position {start}, then {K} timed steps"
+    else:
+        how = f"synthetic KV for {start} positions, then {K} timed greedy steps"
     rec = {
         "metric": "decode tokens/s and achieved HBM GB/s (% of peak) per decode step, 1 GPU",
         "value": round(K / dt, 2),
@@ -236,17 +289,19 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": f"{synth.WFMT_NAMES[s.wfmt]} weights x {synth.ACT_NAMES[s.act]} activations, "
+                 f"{synth.KV_NAMES[s.kvfmt]} KV, fp32 accumulation",
         "data": "synthetic",
-        "config": {"workload": f"{s.name} batch-1 greedy decode, prefill {w.prompt_len} random tokens "
-                               f"then {K} steps (attended context {w.prompt_len + 1}..{w.prompt_len + K})",
+        "config": {"workload": f"{s.name} batch-1 greedy decode to context {w.context}: {how} "
+                               f"(attended context {attended})",
                    "dim": s.dim, "layers": s.n_layers, "q_heads": s.n_q_heads, "kv_heads": s.n_kv_heads,
                    "head_dim": s.head_dim, "ffn": s.ffn_dim, "vocab": s.vocab,
                    "weights": synth.WFMT_NAMES[s.wfmt], "activations": synth.ACT_NAMES[s.act],
-                   "kv_cache": synth.KV_NAMES[s.kvfmt], "batch": 1},
+                   "kv_cache": synth.KV_NAMES[s.kvfmt], "tied": bool(s.tied), "batch": 1},
         "hbm_gbs": round(gbs, 1),
         "hbm_frac_of_peak": round(gbs / PEAK_HBM_GBS, 4),
         "bytes_per_step": round(bytes_total / K),
+        "greedy_tokens_checked": "timed run == kernel-timing rerun; device error word clear",
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

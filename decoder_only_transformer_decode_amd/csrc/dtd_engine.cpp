@@ -1197,3 +1197,41 @@ extern "C" int32_t dtd_debug_uses_persistent(const dtd_engine* e, int32_t batch)
   if (!e) return DTD_E_ARG;
   return e->persist_ok && batch == 1 && !e->capture && e->path != 1 ? 1 : 0;
 }
+
+extern "C" int32_t dtd_debug_step_kernel_shape(const dtd_engine* e) {
+  if (!e) return DTD_E_ARG;
+  return persistent_fixed_shape(e->d) ? 128 : 0;
+}
+
+extern "C" dtd_status dtd_debug_stream_read(const void* buf_dev, int64_t bytes, int32_t reps, void* hip_stream,
+                                            double* gbs) {
+  if (!buf_dev || bytes < 16 || reps <= 0 || !gbs) {
+    g_create_err = "stream_read: null buffer or output, bytes < 16 or reps <= 0";
+    return DTD_E_ARG;
+  }
+  hipStream_t st = (hipStream_t)hip_stream;
+  int dev = 0, cus = 0;
+  uint32_t* sink = nullptr;
+  hipEvent_t a = nullptr, b = nullptr;
+  hipError_t r = hipGetDevice(&dev);
+  if (r == hipSuccess) r = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (r == hipSuccess) r = hipMalloc((void**)&sink, 256);
+  if (r == hipSuccess) r = hipEventCreate(&a);
+  if (r == hipSuccess) r = hipEventCreate(&b);
+  if (r == hipSuccess) r = launch_stream_read(buf_dev, (size_t)bytes, sink, cus, st);   // untimed first pass
+  if (r == hipSuccess) r = hipEventRecord(a, st);
+  for (int i = 0; i < reps && r == hipSuccess; i++) r = launch_stream_read(buf_dev, (size_t)bytes, sink, cus, st);
+  if (r == hipSuccess) r = hipEventRecord(b, st);
+  if (r == hipSuccess) r = hipEventSynchronize(b);
+  float ms = 0.f;
+  if (r == hipSuccess) r = hipEventElapsedTime(&ms, a, b);
+  if (a) (void)hipEventDestroy(a);
+  if (b) (void)hipEventDestroy(b);
+  if (sink) (void)hipFree(sink);
+  if (r != hipSuccess) {
+    g_create_err = std::string("stream_read: ") + hipGetErrorString(r);
+    return DTD_E_HIP;
+  }
+  *gbs = (double)(bytes / 16 * 16) * reps / (ms * 1e-3) / 1e9;
+  return DTD_OK;
+}

@@ -141,6 +141,7 @@ size_t persistent_smem_bytes(const Dims& d, int nch, int nwg);
 size_t persistent_xs_floats(const Dims& d, int nch);
 int persistent_tags_per_step(const Dims& d);
 bool persistent_supports(const Dims& d);   // shapes the persistent step kernel handles
+bool persistent_fixed_shape(const Dims& d);   // the step kernel with hd 128, G 4, bs 16 fixed
 hipError_t persistent_prepare(const Dims& d, size_t smem, int* blocks_per_cu);
 hipError_t launch_persistent(const PersistArgs& a, int nwg, size_t smem, hipStream_t st);
 hipError_t launch_embed(const Dims& d, const MatDev& emb, const StepDesc* desc, int B,
@@ -158,6 +159,7 @@ hipError_t launch_argmax(const Dims& d, const StepDesc* desc, int B, const float
                          hipStream_t st);
 hipError_t launch_dequant_rows(const Dims& d, const MatDev& m, const int32_t* rows, int nrows,
                                float* out, hipStream_t st);
+hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, int cus, hipStream_t st);
 hipError_t launch_kv_fill(const Dims& d, const KvLayer& kv, const int32_t* blocks, int nblk_used,
                           int len, int layer, uint64_t seed, hipStream_t st);
 

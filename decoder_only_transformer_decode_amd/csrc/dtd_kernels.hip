@@ -315,6 +315,25 @@ __global__ __launch_bounds__(256) void k_dequant_rows(Dims d, MatDev m, const in
     out[(size_t)r * m.cols + c] = deq_elem(m, d.wfmt, sr, c);
 }
 
+// Streaming-read ceiling probe: reads n 16-byte vectors with nontemporal loads, four in
+// flight per thread, grid-stride, and folds them by XOR.  The fold is stored only when it
+// equals `never` (a value the caller picks), so the loads cannot be dropped.
+__global__ __launch_bounds__(256) void k_stream_read(const uint4* p, size_t n, uint32_t never, uint32_t* sink) {
+  uint32_t acc = 0;
+  const size_t stride = (size_t)gridDim.x * 256;
+  size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  for (; i + 3 * stride < n; i += 4 * stride) {
+    const uint4 a = gload_stream<uint4>(p + i), b = gload_stream<uint4>(p + i + stride);
+    const uint4 c = gload_stream<uint4>(p + i + 2 * stride), d = gload_stream<uint4>(p + i + 3 * stride);
+    acc ^= (a.x ^ a.y ^ a.z ^ a.w) ^ (b.x ^ b.y ^ b.z ^ b.w) ^ (c.x ^ c.y ^ c.z ^ c.w) ^ (d.x ^ d.y ^ d.z ^ d.w);
+  }
+  for (; i < n; i += stride) {
+    const uint4 a = gload_stream<uint4>(p + i);
+    acc ^= a.x ^ a.y ^ a.z ^ a.w;
+  }
+  if (acc == never) sink[0] = acc;
+}
+
 // counter-based hash (splitmix64 finaliser) for synthetic KV contents
 __device__ __forceinline__ uint64_t mix64(uint64_t z) {
   z = (z ^ (z >> 30)) * 0xbf58476d1ce4e5b9ull;
@@ -445,6 +464,12 @@ hipError_t launch_argmax(const Dims& d, const StepDesc* desc, int B, const float
 hipError_t launch_dequant_rows(const Dims& d, const MatDev& m, const int32_t* rows, int nrows,
                                float* out, hipStream_t st) {
   hipLaunchKernelGGL(k_dequant_rows, dim3(nrows), dim3(256), 0, st, d, m, rows, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, int cus, hipStream_t st) {
+  hipLaunchKernelGGL(k_stream_read, dim3(cus * 16), dim3(256), 0, st, (const uint4*)buf, bytes / 16,
+                     0xA5C3E1F7u, sink);
   return hipGetLastError();
 }
 

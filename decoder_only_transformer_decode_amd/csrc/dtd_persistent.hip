@@ -1509,12 +1509,19 @@ __global__ __launch_bounds__(PT) void k_step(PersistArgs a) {
   PTRACE(3 + d.L * 11);
 }
 
-// the probe step, and the normal step per activation type, each with the attention shape of
-// the target models (head size 128, 4 query heads per KV head, KV blocks of 16) fixed or read
-// at run time
+// The normal step per activation type, with the attention shape of the target models (head
+// size 128, 4 query heads per KV head, KV blocks of 16) fixed or read at run time; and its
+// probe variant: with that shape, the same instantiation parameters as the normal step (so
+// a probe at that shape checks the code the normal step runs), otherwise one variant that
+// reads the activation type at run time.
 template <int WFMT, int KVFMT>
 const void* step_kernel(bool probe, int act, bool fixed) {
-  if (probe) return (const void*)k_step<WFMT, KVFMT, true, -1, 0>;
+  if (probe) {
+    if (fixed)
+      return act == ACT_BF16 ? (const void*)k_step<WFMT, KVFMT, true, ACT_BF16, 128>
+                             : (const void*)k_step<WFMT, KVFMT, true, ACT_F32, 128>;
+    return (const void*)k_step<WFMT, KVFMT, true, -1, 0>;
+  }
   if (fixed)
     return act == ACT_BF16 ? (const void*)k_step<WFMT, KVFMT, false, ACT_BF16, 128>
                            : (const void*)k_step<WFMT, KVFMT, false, ACT_F32, 128>;
@@ -1524,7 +1531,7 @@ const void* step_kernel(bool probe, int act, bool fixed) {
 
 const void* pick(const Dims& d, bool probe) {
   const int wfmt = d.wfmt, kvfmt = d.kvfmt, act = d.act;
-  const bool fixed = d.hd == 128 && d.G == kFixedG && d.bs == kFixedBs;
+  const bool fixed = persistent_fixed_shape(d);
   if (wfmt == W_INT8_ROW) {
     if (kvfmt == KV_F32) return step_kernel<W_INT8_ROW, KV_F32>(probe, act, fixed);
     if (kvfmt == KV_BF16) return step_kernel<W_INT8_ROW, KV_BF16>(probe, act, fixed);
@@ -1541,6 +1548,8 @@ const void* pick(const Dims& d, bool probe) {
 }
 
 }  // namespace
+
+bool persistent_fixed_shape(const Dims& d) { return d.hd == 128 && d.G == kFixedG && d.bs == kFixedBs; }
 
 size_t persistent_xs_floats(const Dims& d, int nch) {
   const int vec = d.wfmt == W_BF16 ? 8 : 16, kstep = 64 * vec;

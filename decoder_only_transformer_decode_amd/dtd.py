@@ -78,6 +78,8 @@ _SIGS = {
     "dtd_debug_probe_record_bytes": ([C.POINTER(dtd_config), _I32], _I64),
     "dtd_debug_set_path": ([_P, _I32], _I32),
     "dtd_debug_uses_persistent": ([_P, _I32], _I32),
+    "dtd_debug_step_kernel_shape": ([_P], _I32),
+    "dtd_debug_stream_read": ([_P, _I64, _I32, _P, C.POINTER(C.c_double)], _I32),
 }
 
 
@@ -256,6 +258,10 @@ def dtd_debug_uses_persistent(eng, batch: int) -> bool:
     return bool(load().dtd_debug_uses_persistent(eng, batch))
 
 
+def dtd_debug_step_kernel_shape(eng) -> int:
+    return int(load().dtd_debug_step_kernel_shape(eng))
+
+
 def dtd_debug_kv_fill(eng, seq_id: int, length: int, seed: int):
     _check(eng, load().dtd_debug_kv_fill(eng, seq_id, length, seed))
 
@@ -326,3 +332,12 @@ class Engine:
 
     def seq_len(self, seq_id: int) -> int:
         return dtd_seq_len(self.h, seq_id)
+
+
+def dtd_debug_stream_read(buf_ptr: int, nbytes: int, reps: int, stream: int) -> float:
+    """Streaming-read bandwidth (GB/s) over a device buffer."""
+    out = C.c_double()
+    st = load().dtd_debug_stream_read(C.c_void_p(buf_ptr), nbytes, reps, C.c_void_p(stream), C.byref(out))
+    if st != DTD_OK:
+        raise DtdError(st, load().dtd_last_error(None).decode())
+    return out.value

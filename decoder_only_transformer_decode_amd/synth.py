@@ -74,6 +74,9 @@ class Workload:
     block_size: int = 16     # KV block size (tokens per block)
     seed_index: int = 0      # weights use seed 1234 + seed_index
     note: str = ""
+    # the context before the decoded steps is synthetic stored KV (the workload names a
+    # context to decode at, not a prompt to prefill)
+    synthetic_prefix: bool = False
 
 
 # The five model shapes and workloads this library is measured and checked on.
@@ -90,7 +93,7 @@ LLAMA32_1B = Workload(
     ModelShape("llama-3.2-1b-shaped", 2048, 16, 32, 8, 64, 8192, 128256,
                W_Q8_0, ACT_BF16, KV_BF16, tied=True),
     batch=1, prompt_len=4032, context=4096, seed_index=2,
-    note="decode at context 4096 (tied embeddings)")
+    note="decode at context 4096 (tied embeddings)", synthetic_prefix=True)
 QWEN3_8B = Workload(
     ModelShape("qwen3-8b-shaped", 4096, 36, 32, 8, 128, 12288, 151936,
                W_BF16, ACT_BF16, KV_BF16),
@@ -100,7 +103,7 @@ LLAMA3_8B = Workload(
     ModelShape("llama-3-8b-shaped", 4096, 32, 32, 8, 128, 14336, 128256,
                W_INT8_ROW, ACT_BF16, KV_I8),
     batch=32, prompt_len=16384 - 16, context=16384, seed_index=4,
-    note="batch 32 at context 16384, int8 KV with an fp16 scale per token and head")
+    note="batch 32 at context 16384, int8 KV with an fp16 scale per token and head", synthetic_prefix=True)
 
 WORKLOADS = [TINY, SMOLLM3_3B, LLAMA32_1B, QWEN3_8B, LLAMA3_8B]
 BY_NAME = {w.shape.name: w for w in WORKLOADS}

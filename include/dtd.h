@@ -224,6 +224,12 @@ dtd_status dtd_debug_kv_fill(dtd_engine* e, int64_t seq_id, int32_t len, uint64_
 dtd_status dtd_debug_kernel_timing(dtd_engine* e, int32_t kind, int32_t enable,
                                    double* total_ms, int64_t* count);
 
+/* Streaming-read ceiling of the device: reads `bytes` (rounded down to 16) of device memory
+ * buf_dev once untimed, then `reps` times, with 16-byte nontemporal loads spread over every
+ * compute unit, on hip_stream; *gbs gets the timed passes' bytes per second / 1e9.  Needs no
+ * engine; on error the message is what dtd_last_error(NULL) returns.  Synchronous. */
+dtd_status dtd_debug_stream_read(const void* buf_dev, int64_t bytes, int32_t reps, void* hip_stream, double* gbs);
+
 /* Schedule selection.  path 0 (default): batch-1 steps run as one persistent kernel per
  * step (every phase in one cooperative launch) when the device allows it, other batches
  * and hidden-state capture as one kernel per sub-step; 1: always one kernel per sub-step;
@@ -232,6 +238,13 @@ dtd_status dtd_debug_set_path(dtd_engine* e, int32_t path);
 
 /* 1 if a decode step of this batch size would run the persistent kernel now, else 0. */
 int32_t dtd_debug_uses_persistent(const dtd_engine* e, int32_t batch);
+
+/* The head size the batch-1 step kernel of this engine has fixed at compile time: 128 when
+ * the model has head size 128, 4 query heads per KV head and KV blocks of 16 positions (the
+ * instantiation built for that shape, whose probe variant dtd_debug_decode_probe then runs
+ * too), or 0 when the kernel reads the shape at run time.  A dtd_status < 0 for a null
+ * engine. */
+int32_t dtd_debug_step_kernel_shape(const dtd_engine* e);
 
 #ifdef __cplusplus
 }

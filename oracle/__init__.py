@@ -75,6 +75,7 @@ def lib():
         L.orc_kv_read_raw.argtypes, L.orc_kv_read_raw.restype = [P, I32, I32, I32, I32, P, P, P, P], I32
         L.orc_full_forward.argtypes, L.orc_full_forward.restype = [P, P, I32, P, P], I32
         L.orc_num_threads.argtypes, L.orc_num_threads.restype = [], I32
+        L.orc_set_num_threads.argtypes, L.orc_set_num_threads.restype = [I32], None
         _lib = L
     return _lib
 
@@ -175,6 +176,10 @@ def kv_quant_i8(x):
 
 def num_threads() -> int:
     return int(lib().orc_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    lib().orc_set_num_threads(int(n))
 
 
 # ---- whole model ---------------------------------------------------------------------

@@ -637,6 +637,14 @@ int32_t orc_full_forward(orc_model* m, const int32_t* tokens, int32_t n, float* 
   return next;
 }
 
+void orc_set_num_threads(int32_t n) {
+#ifdef _OPENMP
+  if (n > 0) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
+
 int32_t orc_num_threads(void) {
 #ifdef _OPENMP
   return omp_get_max_threads();

@@ -118,6 +118,8 @@ int32_t    orc_kv_read_raw(const orc_model* m, int32_t seq, int32_t layer, int32
 int32_t    orc_full_forward(orc_model* m, const int32_t* tokens, int32_t n,
                             float* logits, double* hidden);
 int32_t    orc_num_threads(void);
+/* Sets the OpenMP thread count of later calls (n > 0). */
+void       orc_set_num_threads(int32_t n);
 
 #ifdef __cplusplus
 }

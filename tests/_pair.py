@@ -154,10 +154,12 @@ def _from_act(raw, act):
     return raw.view(np.float32).astype(np.float64)
 
 
-def probe_step(P, gpu_ids, orc_ids, toks, poss, tag, check=True):
+def probe_step(P, gpu_ids, orc_ids, toks, poss, tag, check=True, kv_inject=None):
     """Oracle step (with its per-layer trace) for each sequence, then one GPU probe step in
     which every kernel reads the oracle's own inputs; every kernel's output is compared
-    with the oracle's.  Returns the oracle outputs [(next, logits, hidden, trace)]."""
+    with the oracle's.  Returns the oracle outputs [(next, logits, hidden, trace)].
+    kv_inject (layer -> (k, v), float32 [B][kv_dim]) replaces the new position's injected
+    k and v, which the GPU then rounds to the KV type as it appends them."""
     t = P.torch
     s = P.shape
     B = len(gpu_ids)
@@ -174,7 +176,9 @@ def probe_step(P, gpu_ids, orc_ids, toks, poss, tag, check=True):
     for l in range(s.n_layers):
         for name, off, n, is_act in layout:
             o0, _ = fields[name]
-            if name in ("k", "v"):
+            if name in ("k", "v") and kv_inject is not None:
+                vals = np.asarray(kv_inject[l][0 if name == "k" else 1], dtype=np.float64).reshape(B, n)
+            elif name in ("k", "v"):
                 vals = np.stack([stored[b][l][0 if name == "k" else 1].reshape(-1) for b in range(B)])
             else:
                 vals = np.stack([outs[b][3][l, o0:o0 + n] for b in range(B)])   # [B][n] float64
@@ -238,3 +242,20 @@ def probe_step(P, gpu_ids, orc_ids, toks, poss, tag, check=True):
     P.probe_stats[0] += flips
     P.probe_stats[1] = max(P.probe_stats[1], worst)
     return outs
+
+
+def stored_kv_reference(shape, x32):
+    """The cache entry the KV rounding of the int8-KV, bf16 and fp32 readings makes of
+    float32 vectors x32 [..., n_kv_heads * head_dim], from the oracle's own rounding
+    functions: (codes or bits [..., Hkv, hd], fp16 scale bits [..., Hkv] or None)."""
+    x = np.asarray(x32, dtype=np.float32).astype(np.float64)
+    x = x.reshape(x.shape[:-1] + (shape.n_kv_heads, shape.head_dim))
+    if shape.kvfmt == synth.KV_F32:
+        return x.astype(np.float32), None
+    if shape.kvfmt == synth.KV_BF16:
+        return np.vectorize(oracle.double_to_bf16, otypes=[np.uint16])(x), None
+    q = np.empty(x.shape, dtype=np.int8)
+    sc = np.empty(x.shape[:-1], dtype=np.uint16)
+    for idx in np.ndindex(*x.shape[:-1]):
+        q[idx], sc[idx] = oracle.kv_quant_i8(x[idx])
+    return q, sc

@@ -45,6 +45,7 @@ def _run(P, O2, seq_ids, n_pos, steps=2, tok0=17):
     toks = {sid: tok0 + 3 * i for i, sid in enumerate(seq_ids)}
     pos = dict(n_pos)
     worst_free, worst_env = 0.0, 0.0
+    tokens_checked = 0
     for step in range(steps):
         ng, lg, _ = P.gpu_step(seq_ids, [toks[i] for i in seq_ids])
         outs = probe_step(P, [i + 100 for i in seq_ids], seq_ids, [toks[i] for i in seq_ids],
@@ -53,14 +54,24 @@ def _run(P, O2, seq_ids, n_pos, steps=2, tok0=17):
             no, lo = outs[b][0], outs[b][1]
             fe = normwise(lg[b], lo)
             pe = normwise(O2.step(P.oslot(sid), toks[sid], pos[sid])[1], lo)
+            delta = float(np.abs(lg[b].astype(np.float64) - lo).max())
+            margin = top2_margin(lo)
             print(f"{s.name} step {step} seq {sid} T={pos[sid] + 1}: probe ok (bf16 flips so far "
                   f"{P.probe_stats[0]}, worst fp32 field err {P.probe_stats[1]:.2e}), margin "
-                  f"{top2_margin(lo):.3e}; free-running {fe:.2e} (token {int(ng[b])}/{no}), "
+                  f"{margin:.3e}; free-running {fe:.2e} (max abs {delta:.3e}, token {int(ng[b])}/{no}), "
                   f"oracle sensitivity {pe:.2e}", flush=True)
+            # the free-running greedy token, wherever no error of the size seen can reorder
+            # the oracle's top two
+            if margin > 2 * delta:
+                assert int(ng[b]) == no, f"{s.name} step {step} seq {sid}: token {int(ng[b])} vs {no}"
+                tokens_checked += 1
             worst_free, worst_env = max(worst_free, fe), max(worst_env, pe)
             toks[sid] = no
             pos[sid] += 1
-    assert worst_free <= max(TOL, ENV_FACTOR * worst_env), (worst_free, worst_env)
+    bound = max(TOL, ENV_FACTOR * worst_env)
+    print(f"{s.name}: free-running max err {worst_free:.2e}, bound {bound:.2e} (oracle sensitivity "
+          f"{worst_env:.2e}); {tokens_checked} free-running tokens asserted", flush=True)
+    assert worst_free <= bound, (worst_free, worst_env)
 
 
 def _pair(w, shape, **kw):
@@ -72,6 +83,9 @@ def _pair(w, shape, **kw):
 def test_smollm3_shape_full_size_at_context_2048():
     w = synth.SMOLLM3_3B
     P, O2 = _pair(w, w.shape, max_seqs=2)
+    # the instantiation the benchmark times (hd 128, G 4, KV blocks of 16 fixed); the probe
+    # steps below run its probe variant, built with the same parameters
+    assert dtd.dtd_debug_step_kernel_shape(P.eng.h) == 128 and dtd.dtd_debug_uses_persistent(P.eng.h, 1)
     _write_kv(P, O2, 0, [0, 100], w.context - 2, seed=5)
     _run(P, O2, [0], {0: w.context - 2})
     P.close()

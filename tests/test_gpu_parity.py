@@ -10,7 +10,7 @@ import numpy as np
 import pytest
 
 from decoder_only_transformer_decode_amd import dtd, synth
-from _pair import ENV_FACTOR, TOL, Pair, need_gpu, normwise, probe_step, top2_margin
+from _pair import ENV_FACTOR, TOL, Pair, need_gpu, normwise, probe_step, stored_kv_reference, top2_margin
 
 pytestmark = pytest.mark.gpu
 
@@ -119,6 +119,9 @@ _FORMATS = [
     dict(n_q_heads=8, n_kv_heads=2, head_dim=128),
     dict(n_q_heads=8, n_kv_heads=2, head_dim=128, wfmt=synth.W_Q8_0, act=synth.ACT_BF16, kvfmt=synth.KV_I8),
     dict(n_q_heads=8, n_kv_heads=2, head_dim=128, wfmt=synth.W_BF16, act=synth.ACT_BF16, kvfmt=synth.KV_BF16),
+    # int8-row weights, bf16 activations and bf16 KV at that shape: the instantiation the
+    # benchmark times on the SmolLM3-3B shape (its probe variant has the same parameters)
+    dict(n_q_heads=8, n_kv_heads=2, head_dim=128, act=synth.ACT_BF16, kvfmt=synth.KV_BF16),
 ]
 
 
@@ -149,6 +152,10 @@ def teacher_forced(P, gpu_ids, orc_ids, toks, poss, tag):
 def test_formats(kw, path):
     s = _GRID.replace(**kw)
     P = Pair(s, max_ctx=96, max_seqs=2, seed=21, path=path)
+    fixed = s.head_dim == 128 and s.n_q_heads == 4 * s.n_kv_heads
+    assert dtd.dtd_debug_step_kernel_shape(P.eng.h) == (128 if fixed else 0)
+    _say(f"formats {kw}: step kernel shape {'fixed hd 128, G 4, bs 16' if fixed else 'run time'}, "
+         f"{PATH_IDS[PATHS.index(path)]} schedule")
     O2 = P.perturbed_oracle(1, max_ctx=96)
     prompt = synth.prompt_tokens(s.vocab, 70, seed=3)
     tr = Tracker()
@@ -224,6 +231,80 @@ def test_batched_decode_mixed_lengths(kw):
     for sid in ids:
         assert P.eng.seq_len(sid) == pos[sid] == P.eng.seq_len(sid + 100)
     tr.check("batched " + s.name)
+    P.close()
+
+
+# ---------------------------------------------------------------------------------------
+# the KV append's rounding to the cache type, on fresh float32 vectors with constructed ties
+# ---------------------------------------------------------------------------------------
+
+def _kv_cases(hd, rng):
+    """float32 head vectors that put the KV rounding on its edge cases."""
+    m = 1 + 2.0 ** -11                       # fp16 midpoint between 1 and 1 + 2^-10
+    c = []
+    v = rng.standard_normal(hd) * 0.3
+    v[3] = 127 * m                           # int8 scale exactly on an fp16 midpoint (ties even)
+    c.append(v)
+    v = rng.standard_normal(hd) * 0.3
+    v[0] = 127 * (1 + 3 * 2.0 ** -11)        # midpoint between odd and even fp16 neighbours
+    c.append(v)
+    s = 2.0 ** -6                            # int8 codes exactly on half integers
+    v = (rng.integers(-126, 126, hd) + 0.5) * s
+    v[0] = 127 * s
+    c.append(v)
+    v = rng.standard_normal(hd)              # bf16 ties and their float32 neighbours
+    v[:6] = [1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8, -(1 + 2.0 ** -8), 1 + 2.0 ** -8 + 2.0 ** -23,
+             1 + 2.0 ** -8 - 2.0 ** -23, 2.0 ** -130]
+    c.append(v)
+    v = rng.standard_normal(hd) * 1e-6       # a subnormal fp16 scale that rounds down: clamps
+    v[1] = 127 * 1.4 * 2.0 ** -24
+    v[2] = -127 * 1.4 * 2.0 ** -24
+    c.append(v)
+    c.append(np.zeros(hd))                   # zero scale
+    c.append(rng.standard_normal(hd) * 40.0)
+    return [np.asarray(x, dtype=np.float32) for x in c]
+
+
+@pytest.mark.parametrize("path", PATHS, ids=PATH_IDS)
+@pytest.mark.parametrize("kvfmt", [synth.KV_F32, synth.KV_BF16, synth.KV_I8], ids=["f32", "bf16", "i8"])
+@pytest.mark.parametrize("hd", [32, 128], ids=["hd32", "hd128"])
+def test_kv_append_rounding_bit_exact(kvfmt, path, hd):
+    """Probe steps inject fresh float32 k/v (not already rounded) for the new position; the
+    entry the GPU appends must equal the oracle's KV rounding of those same values, bit for
+    bit: scale and codes for int8, bits for bf16 and fp32."""
+    kw = dict(kvfmt=kvfmt, act=synth.ACT_BF16)
+    if hd == 128:
+        kw.update(n_q_heads=8, n_kv_heads=2, head_dim=128)
+    s = _GRID.replace(**kw)
+    P = Pair(s, max_ctx=32, max_seqs=1, seed=3, path=path)
+    rng = np.random.default_rng(5 + hd + kvfmt)
+    cases = _kv_cases(s.head_dim, rng)
+    n_steps = (len(cases) + s.n_kv_heads - 1) // s.n_kv_heads * 2
+    for step in range(n_steps):
+        inj = {}
+        for layer in range(s.n_layers):
+            vec = []
+            for which in range(2):          # k, v
+                heads = [cases[(step * s.n_kv_heads + j + which + layer) % len(cases)]
+                         for j in range(s.n_kv_heads)]
+                vec.append(np.concatenate(heads)[None, :])
+            inj[layer] = tuple(vec)
+        probe_step(P, [0], [0], [3 + step], [step], f"kv rounding step {step}", check=False, kv_inject=inj)
+        for layer in range(s.n_layers):
+            kr, ksr = stored_kv_reference(s, inj[layer][0])
+            vr, vsr = stored_kv_reference(s, inj[layer][1])
+            kg, vg = np.empty_like(kr), np.empty_like(vr)
+            ksg = vsg = None
+            if ksr is not None:
+                ksg, vsg = np.empty_like(ksr), np.empty_like(vsr)
+            dtd.dtd_debug_kv_read(P.eng.h, 0, layer, step, 1, kg, vg, ksg, vsg)
+            where = f"step {step} layer {layer}"
+            assert np.array_equal(kg.view(np.uint8), kr.view(np.uint8)), f"{where}: stored k"
+            assert np.array_equal(vg.view(np.uint8), vr.view(np.uint8)), f"{where}: stored v"
+            if ksr is not None:
+                assert np.array_equal(ksg, ksr) and np.array_equal(vsg, vsr), f"{where}: scales"
+    _say(f"kv rounding {synth.KV_NAMES[kvfmt]} hd {hd} ({PATH_IDS[PATHS.index(path)]}): "
+         f"{n_steps} positions x {s.n_layers} layers bit-exact")
     P.close()
 
 
