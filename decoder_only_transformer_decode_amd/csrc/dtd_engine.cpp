@@ -10,6 +10,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <unordered_map>
 #include <vector>
@@ -103,12 +104,38 @@ struct dtd_engine {
   uint32_t epoch = 1;            // tag of the next launch's first phase (0 never used)
   int path = 0;                  // 0 auto, 1 per-kernel, 2 persistent
 
+  void* scratch_dev = nullptr;   // this device's copy of the allocation-free entry point's scratch
   int timing_kind = -1;
   std::vector<TimerPair> timers;
   size_t timers_used = 0;
 };
 
 static thread_local std::string g_create_err;   // message of this thread's last failed dtd_create
+
+// Work memory of dtd_decode_step_noalloc: a file-scope device array, one copy on every GPU
+// the library runs on, held until the process ends.  Host code never uses the array's
+// name as an address (on the host it names a stand-in, not device memory): each device's
+// copy is looked up once with hipGetSymbolAddress, when the first engine is created on
+// that device, and kept in g_scratch_dev.
+constexpr size_t kNoAllocScratchBytes = (size_t)16 << 20;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_dev[kMaxDevices];
+
+// The address of this device's scratch copy (the device is current); nullptr on failure.
+static void* scratch_on_current_device(int device, hipError_t* err) {
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  *err = hipSuccess;
+  if (device < 0 || device >= kMaxDevices) { *err = hipErrorInvalidDevice; return nullptr; }
+  if (!g_scratch_dev[device]) {
+    void* p = nullptr;
+    *err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (*err != hipSuccess) return nullptr;
+    g_scratch_dev[device] = p;
+  }
+  return g_scratch_dev[device];
+}
 
 // ---------------------------------------------------------------------------------------
 // helpers
@@ -318,6 +345,14 @@ extern "C" dtd_status dtd_create(const dtd_config* cfg, void* hip_stream, dtd_en
     return st;
   };
   if (hipGetDevice(&e->device) != hipSuccess) { e->err = "hipGetDevice failed"; return cleanup(DTD_E_HIP); }
+  {
+    hipError_t r;
+    e->scratch_dev = scratch_on_current_device(e->device, &r);
+    if (!e->scratch_dev) {
+      e->err = std::string("hipGetSymbolAddress(scratch) failed: ") + hipGetErrorString(r);
+      return cleanup(DTD_E_HIP);
+    }
+  }
 
   // RoPE tables: angle pos * theta^(-2i/d) in double, cos/sin stored as fp32
   const int half = d.hd / 2;
@@ -643,10 +678,18 @@ static ProbeLayout probe_layout(const Dims& d, int B, size_t ab) {
 // With inject/capture (debug probe): every kernel of every layer reads its input from the
 // inject record and its output is copied to the capture record, so each kernel can be
 // compared with the reference operation on identical inputs.
+static dtd_status run_sub_steps(dtd_engine* e, int B, bool do_head, const uint8_t* inject, uint8_t* capture,
+                                float* partials);
+
+// partials: the split-K attention partials of the per-sub-step schedule (the engine's buffer,
+// or the allocation-free entry point's static scratch).  force_per_kernel: run that schedule
+// even at batch 1; no_timing: leave the kernel-timing hooks (which may create events) out.
 static dtd_status run_step(dtd_engine* e, int B, const int* slots, const int* poss, const int* pblks,
                            const int32_t* tokens, int32_t* next, float* logits_out, bool do_head,
-                           const std::vector<Update>& upd, const uint8_t* inject = nullptr,
-                           uint8_t* capture = nullptr) {
+                           const Update* upd, int n_upd, const uint8_t* inject = nullptr,
+                           uint8_t* capture = nullptr, float* partials = nullptr, bool force_per_kernel = false,
+                           bool no_timing = false) {
+  if (!partials) partials = e->partials;
   const Dims& d = e->d;
   hipStream_t st = e->stream;
   // descriptor into the next pinned ring slot, then one host->device copy
@@ -655,12 +698,12 @@ static dtd_status run_step(dtd_engine* e, int B, const int* slots, const int* po
   memset(hd, 0, sizeof(StepDesc));
   hd->batch = B;
   hd->do_head = do_head ? 1 : 0;
-  hd->n_updates = (int32_t)upd.size();
+  hd->n_updates = (int32_t)n_upd;
   hd->tokens = tokens;
   hd->next_tokens = next;
   hd->logits_out = logits_out;
   for (int b = 0; b < B; b++) { hd->pos[b] = poss[b]; hd->slot[b] = slots[b]; hd->pos_block[b] = pblks[b]; }
-  for (size_t u = 0; u < upd.size(); u++) {
+  for (int u = 0; u < n_upd; u++) {
     hd->upd[u][0] = upd[u].slot; hd->upd[u][1] = upd[u].lblock; hd->upd[u][2] = upd[u].pblock;
   }
   HIP_OK(e, hipMemcpyAsync(e->desc_dev, hd, sizeof(StepDesc), hipMemcpyHostToDevice, st));
@@ -668,7 +711,7 @@ static dtd_status run_step(dtd_engine* e, int B, const int* slots, const int* po
   e->desc_ev_used[e->ring] = true;
   e->ring = (e->ring + 1) % kRing;
 
-  if (e->persist_ok && B == 1 && !e->capture && e->path != 1) {
+  if (e->persist_ok && B == 1 && !e->capture && e->path != 1 && !force_per_kernel) {
     PersistArgs a{};
     a.d = d;
     a.layers = e->players;
@@ -714,7 +757,20 @@ static dtd_status run_step(dtd_engine* e, int B, const int* slots, const int* po
     e->epoch += ntag;
       return DTD_OK;
   }
-  if (e->path == 2) return fail(e, DTD_E_UNSUPPORTED, "persistent step kernel unavailable for this call");
+  if (e->path == 2 && !force_per_kernel)
+    return fail(e, DTD_E_UNSUPPORTED, "persistent step kernel unavailable for this call");
+  const int timing_saved = e->timing_kind;
+  if (no_timing) e->timing_kind = -1;
+  const dtd_status rs = run_sub_steps(e, B, do_head, inject, capture, partials);
+  e->timing_kind = timing_saved;
+  return rs;
+}
+
+// The per-sub-step schedule of one step (the descriptor is already on the device).
+static dtd_status run_sub_steps(dtd_engine* e, int B, bool do_head, const uint8_t* inject, uint8_t* capture,
+                                float* partials) {
+  const Dims& d = e->d;
+  hipStream_t st = e->stream;
 
   HIP_OK(e, launch_embed(d, e->emb, e->desc_dev, B, e->bt_dev, e->x, e->err_dev, st));
   const size_t ab = act_bytes(e->cfg.act);
@@ -760,8 +816,8 @@ static dtd_status run_step(dtd_engine* e, int B, const int* slots, const int* po
       HIP_OK(e, cp(e->knew, in + pl.k, fkv));
       HIP_OK(e, cp(e->vnew, in + pl.v, fkv));
     }
-    TIMED(4, launch_attention(d, e->desc_dev, B, e->q, e->knew, e->vnew, kv, e->bt_dev, e->partials, st));
-    HIP_OK(e, launch_combine(d, e->desc_dev, B, e->partials, e->o, st));
+    TIMED(4, launch_attention(d, e->desc_dev, B, e->q, e->knew, e->vnew, kv, e->bt_dev, partials, st));
+    HIP_OK(e, launch_combine(d, e->desc_dev, B, partials, e->o, st));
     if (probe) {
       HIP_OK(e, cp(out + pl.o, e->o, fo));
       HIP_OK(e, cp(e->o, in + pl.o, fo));
@@ -824,6 +880,7 @@ extern "C" dtd_status dtd_prefill(dtd_engine* e, int64_t seq_id, const int32_t* 
     return fail(e, DTD_E_KVFULL, "prefill: needs %d KV blocks, %zu free", need, e->free_blocks.size());
   if (is_new) {
     Seq s;
+    s.blocks.reserve((size_t)e->d.max_blocks);
     s.slot = e->free_slots.back();
     e->free_slots.pop_back();
     it = e->seqs.emplace(seq_id, s).first;
@@ -831,33 +888,38 @@ extern "C" dtd_status dtd_prefill(dtd_engine* e, int64_t seq_id, const int32_t* 
   Seq& s = it->second;
   for (int i = 0; i < n; i++) {
     const int pos = s.len;
-    std::vector<Update> upd;
+    Update upd[1];
+    int n_upd = 0;
     if (pos / e->d.bs >= (int)s.blocks.size()) {
       const int32_t b = e->free_blocks.back();
       e->free_blocks.pop_back();
       s.blocks.push_back(b);
-      upd.push_back({s.slot, (int)s.blocks.size() - 1, b});
+      upd[n_upd++] = {s.slot, (int)s.blocks.size() - 1, b};
     }
     const bool last = i == n - 1;
     const int pblk = s.blocks[(size_t)(pos / e->d.bs)];
     st = run_step(e, 1, &s.slot, &pos, &pblk, tokens_dev + i, next_token_dev, last ? logits_dev : nullptr, last,
-                  upd);
+                  upd, n_upd);
     if (st) return st;
     s.len++;
   }
   return DTD_OK;
 }
 
+// Sequence lookups, block allocation and the step launch of a decode call.  Uses fixed-size
+// arrays only (no heap allocation): a sequence's block list has its full capacity reserved
+// when the sequence is created.
 static dtd_status decode_impl(dtd_engine* e, int32_t batch, const int64_t* seq_ids_host,
                               const int32_t* tokens_dev, int32_t* next_tokens_dev, float* logits_dev,
-                              const uint8_t* inject, uint8_t* capture, bool create_missing) {
+                              const uint8_t* inject, uint8_t* capture, bool create_missing,
+                              float* partials = nullptr, bool no_alloc = false) {
   dtd_status st = ready(e);
   if (st) return st;
   if (batch <= 0 || batch > e->cfg.max_batch)
     return fail(e, DTD_E_ARG, "decode_step: batch %d outside [1, %d]", batch, e->cfg.max_batch);
   if (!seq_ids_host || !tokens_dev || !next_tokens_dev) return fail(e, DTD_E_ARG, "decode_step: null pointer");
   int need = 0;
-  std::vector<Seq*> ss((size_t)batch);
+  Seq* ss[kMaxBatch];
   int missing = 0;
   for (int b = 0; b < batch; b++) {
     for (int c = 0; c < b; c++)
@@ -867,42 +929,50 @@ static dtd_status decode_impl(dtd_engine* e, int32_t batch, const int64_t* seq_i
   }
   if (missing > (int)e->free_slots.size()) return fail(e, DTD_E_KVFULL, "decode_step: no free sequence slot");
   if (missing > (int)e->free_blocks.size()) return fail(e, DTD_E_KVFULL, "decode_step: no free KV block");
+  for (int b = 0; b < batch; b++) {
+    auto it = e->seqs.find(seq_ids_host[b]);
+    if (it == e->seqs.end() && !create_missing)
+      return fail(e, DTD_E_NOSEQ, "decode_step: unknown seq_id %lld", (long long)seq_ids_host[b]);
+    if (it != e->seqs.end()) {
+      const Seq& s = it->second;
+      if (s.len + 1 > e->cfg.max_ctx)
+        return fail(e, DTD_E_CTX, "decode_step: seq_id %lld is at max_ctx %d", (long long)seq_ids_host[b], e->cfg.max_ctx);
+      if (s.len / e->d.bs >= (int)s.blocks.size()) need++;
+    } else {
+      need++;
+    }
+  }
+  if (need > (int)e->free_blocks.size())
+    return fail(e, DTD_E_KVFULL, "decode_step: needs %d KV blocks, %zu free", need, e->free_blocks.size());
+  // validated: only now change engine state
   for (int b = 0; b < batch && missing; b++)
     if (e->seqs.find(seq_ids_host[b]) == e->seqs.end()) {
       Seq s;
       s.slot = e->free_slots.back();
+      s.blocks.reserve((size_t)e->d.max_blocks);
       e->free_slots.pop_back();
-      e->seqs.emplace(seq_ids_host[b], s);
+      e->seqs.emplace(seq_ids_host[b], std::move(s));
     }
+  for (int b = 0; b < batch; b++) ss[b] = &e->seqs.find(seq_ids_host[b])->second;
+  int slots[kMaxBatch], poss[kMaxBatch], pblks[kMaxBatch];
+  Update upd[kMaxBatch];
+  int n_upd = 0;
   for (int b = 0; b < batch; b++) {
-    auto it = e->seqs.find(seq_ids_host[b]);
-    if (it == e->seqs.end()) return fail(e, DTD_E_NOSEQ, "decode_step: unknown seq_id %lld", (long long)seq_ids_host[b]);
-    Seq& s = it->second;
-    if (s.len + 1 > e->cfg.max_ctx)
-      return fail(e, DTD_E_CTX, "decode_step: seq_id %lld is at max_ctx %d", (long long)seq_ids_host[b], e->cfg.max_ctx);
-    if (s.len / e->d.bs >= (int)s.blocks.size()) need++;
-    ss[(size_t)b] = &s;
-  }
-  if (need > (int)e->free_blocks.size())
-    return fail(e, DTD_E_KVFULL, "decode_step: needs %d KV blocks, %zu free", need, e->free_blocks.size());
-  std::vector<int> slots((size_t)batch), poss((size_t)batch), pblks((size_t)batch);
-  std::vector<Update> upd;
-  for (int b = 0; b < batch; b++) {
-    Seq& s = *ss[(size_t)b];
+    Seq& s = *ss[b];
     if (s.len / e->d.bs >= (int)s.blocks.size()) {
       const int32_t blk = e->free_blocks.back();
       e->free_blocks.pop_back();
       s.blocks.push_back(blk);
-      upd.push_back({s.slot, (int)s.blocks.size() - 1, blk});
+      upd[n_upd++] = {s.slot, (int)s.blocks.size() - 1, blk};
     }
-    slots[(size_t)b] = s.slot;
-    poss[(size_t)b] = s.len;
-    pblks[(size_t)b] = s.blocks[(size_t)(s.len / e->d.bs)];
+    slots[b] = s.slot;
+    poss[b] = s.len;
+    pblks[b] = s.blocks[(size_t)(s.len / e->d.bs)];
   }
-  st = run_step(e, batch, slots.data(), poss.data(), pblks.data(), tokens_dev, next_tokens_dev, logits_dev, true, upd,
-                inject, capture);
+  st = run_step(e, batch, slots, poss, pblks, tokens_dev, next_tokens_dev, logits_dev, true, upd, n_upd,
+                inject, capture, partials, no_alloc, no_alloc);
   if (st) return st;
-  for (int b = 0; b < batch; b++) ss[(size_t)b]->len++;
+  for (int b = 0; b < batch; b++) ss[b]->len++;
   return DTD_OK;
 }
 
@@ -910,6 +980,24 @@ extern "C" dtd_status dtd_decode_step(dtd_engine* e, int32_t batch, const int64_
                                       const int32_t* tokens_dev, int32_t* next_tokens_dev,
                                       float* logits_dev) {
   return decode_impl(e, batch, seq_ids_host, tokens_dev, next_tokens_dev, logits_dev, nullptr, nullptr, false);
+}
+
+extern "C" dtd_status dtd_decode_step_noalloc(dtd_engine* e, int32_t batch, const int64_t* seq_ids_host,
+                                              const int32_t* tokens_dev, int32_t* next_tokens_dev,
+                                              float* logits_dev) {
+  if (!e) return DTD_E_ARG;
+  if (batch <= 0 || batch > e->cfg.max_batch)
+    return fail(e, DTD_E_ARG, "decode_step_noalloc: batch %d outside [1, %d]", batch, e->cfg.max_batch);
+  // the split-K attention partials [batch][Hq][nch][hd + 2] fp32 live in the static scratch
+  const Dims& d = e->d;
+  const size_t need = (size_t)batch * d.Hq * d.nch * (d.hd + 2) * sizeof(float);
+  if (need > kNoAllocScratchBytes)
+    return fail(e, DTD_E_UNSUPPORTED,
+                "decode_step_noalloc: %zu bytes of attention partials for batch %d exceed the %zu-byte "
+                "static scratch (fewer sequences per call, or a shorter max_ctx, fit)",
+                need, batch, kNoAllocScratchBytes);
+  return decode_impl(e, batch, seq_ids_host, tokens_dev, next_tokens_dev, logits_dev, nullptr, nullptr, false,
+                     (float*)e->scratch_dev, true);
 }
 
 extern "C" dtd_status dtd_debug_decode_probe(dtd_engine* e, int32_t batch, const int64_t* seq_ids_host,
@@ -1034,6 +1122,7 @@ static dtd_status ensure_seq_blocks(dtd_engine* e, int64_t seq_id, int len, Seq*
   if (it == e->seqs.end()) {
     if (e->free_slots.empty()) return fail(e, DTD_E_KVFULL, "no free sequence slot");
     Seq s;
+    s.blocks.reserve((size_t)e->d.max_blocks);
     s.slot = e->free_slots.back();
     e->free_slots.pop_back();
     it = e->seqs.emplace(seq_id, s).first;

@@ -63,6 +63,7 @@ _SIGS = {
     "dtd_load_weights": ([_P, C.POINTER(dtd_tensor), _I32], _I32),
     "dtd_prefill": ([_P, _I64, _P, _I32, _P, _P], _I32),
     "dtd_decode_step": ([_P, _I32, C.POINTER(_I64), _P, _P, _P], _I32),
+    "dtd_decode_step_noalloc": ([_P, _I32, C.POINTER(_I64), _P, _P, _P], _I32),
     "dtd_reset_seq": ([_P, _I64], _I32),
     "dtd_seq_len": ([_P, _I64], _I32),
     "dtd_check_device_errors": ([_P], _I32),
@@ -182,6 +183,13 @@ def dtd_reset_seq(eng, seq_id: int):
 
 def dtd_seq_len(eng, seq_id: int) -> int:
     return int(load().dtd_seq_len(eng, seq_id))
+
+
+def dtd_decode_step_noalloc(eng, seq_ids: Sequence[int], tokens_dev: int, next_tokens_dev: int,
+                            logits_dev: int = 0):
+    ids = (C.c_int64 * len(seq_ids))(*seq_ids)
+    _check(eng, load().dtd_decode_step_noalloc(eng, len(seq_ids), ids, C.c_void_p(tokens_dev),
+                                               C.c_void_p(next_tokens_dev), C.c_void_p(logits_dev or None)))
 
 
 def dtd_check_device_errors(eng):
