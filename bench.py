@@ -149,8 +149,8 @@ def main():
     w = synth.BY_NAME[args.workload]
     s = w.shape
     if w.batch != 1:
-        print("only the batch-1 workloads are benchmarked here", file=sys.stderr)
-        sys.exit(2)
+        bench_batched(args, w)
+        return
     K, W = args.steps, args.warmup
     # The K timed steps end at the workload's context: the first takes position start.
     start = w.context - K
@@ -302,6 +302,153 @@ def main():
         "hbm_frac_of_peak": round(gbs / PEAK_HBM_GBS, 4),
         "bytes_per_step": round(bytes_total / K),
         "greedy_tokens_checked": "timed run == kernel-timing rerun; device error word clear",
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    eng.close()
+    print(json.dumps(rec), flush=True)
+
+
+def cpu_baseline_batched(w: synth.Workload, weights, ctxs, n_seqs: int) -> dict:
+    """The oracle on this host: one decode step for each of the first n_seqs sequences of the
+    batch at its context (synthetic stored KV before it), every OpenMP thread.  The oracle
+    steps sequences one at a time, so its tokens/s over the sample is its batch rate."""
+    import oracle
+    s = w.shape
+    m = oracle.Model(s, weights, max_ctx=w.context, max_seqs=n_seqs)
+    for b in range(n_seqs):
+        for layer in range(s.n_layers):
+            k, v, ks, vs = synth.synthetic_kv(s, int(ctxs[b]) - 1, seed=5 + b, layer=layer)
+            m.kv_write(b, layer, 0, k, v, ks, vs)
+    t0 = time.perf_counter()
+    for b in range(n_seqs):
+        m.step(b, 17 + b, int(ctxs[b]) - 1)
+    dt = time.perf_counter() - t0
+    return {"value": round(n_seqs / dt, 4), "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"one decode step of {n_seqs} of the batch's sequences (attended contexts "
+                      f"{', '.join(str(int(c)) for c in ctxs[:n_seqs])}), synthetic stored KV, fp64 oracle, "
+                      f"{dt:.1f} s"}
+
+
+def bench_batched(args, w: synth.Workload):
+    """Batched decode: every step advances all B sequences by one token (continuous-batch
+    decode at the workload's contexts); the K timed steps end at each sequence's context."""
+    import torch
+    s = w.shape
+    B, K, W = w.batch, args.steps, args.warmup
+    ctxs = synth.context_lengths(B) if w.mixed_contexts else np.full(B, w.context, dtype=np.int32)
+    if int(ctxs.min()) - K - W < 1:
+        print(f"--steps {K} + --warmup {W} do not fit below the shortest context {int(ctxs.min())}", file=sys.stderr)
+        sys.exit(2)
+    t0 = time.perf_counter()
+    print(f"[bench] generating {s.name} weights", file=sys.stderr, flush=True)
+    weights = synth.gen_weights(s, synth.weights_seed(w))
+    t_gen = time.perf_counter() - t0
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda", 0)
+    eng = dtd.Engine(s, max_ctx=w.context, max_seqs=B, max_batch=B, kv_block_size=w.block_size)
+    eng.load_weights(synth.flat_tensors(weights))
+    print(f"[bench] weights generated in {t_gen:.1f} s and loaded; batch {B}", file=sys.stderr, flush=True)
+    ids = list(range(B))
+    hist = torch.zeros((K + 1, B), dtype=torch.int32, device=dev)
+    row = B * 4
+
+    def prepare():
+        """every sequence at context - K - W positions of synthetic KV, then W warmup steps"""
+        for b in ids:
+            if eng.seq_len(b) >= 0:
+                eng.reset_seq(b)
+            dtd.dtd_debug_kv_fill(eng.h, b, int(ctxs[b]) - K - W, 7 + b)
+        warm = torch.zeros((W + 1, B), dtype=torch.int32, device=dev)
+        warm[0] = torch.as_tensor(synth.prompt_tokens(s.vocab, B, seed=3)).to(dev)
+        for i in range(W):
+            dtd.dtd_decode_step(eng.h, ids, warm.data_ptr() + i * row, warm.data_ptr() + (i + 1) * row)
+        hist[0] = warm[W]
+        torch.cuda.synchronize()
+        dtd.dtd_check_device_errors(eng.h)
+
+    def run():
+        for i in range(K):
+            dtd.dtd_decode_step(eng.h, ids, hist.data_ptr() + i * row, hist.data_ptr() + (i + 1) * row)
+
+    prepare()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    run()
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    dtd.dtd_check_device_errors(eng.h)
+    tokens = hist.cpu().numpy().copy()
+
+    wb = weight_bytes(s)
+    wtot = sum(v for k, v in wb.items() if k != "per_layer")
+    kvpp = kv_bytes_per_position(s)
+    # attended contexts of the timed steps: step i attends ctx_b - K + 1 + i positions
+    att = sum(float(c - K + 1 + i) for c in ctxs for i in range(K))
+    kv_total = kvpp * att
+    bytes_total = wtot * K + kv_total
+    gbs = bytes_total / dt / 1e9
+
+    def timed(kind):
+        prepare()
+        dtd.dtd_debug_kernel_timing(eng.h, kind, True)
+        run()
+        ms, cnt = dtd.dtd_debug_kernel_timing(eng.h, kind, False)
+        dtd.dtd_check_device_errors(eng.h)
+        again = hist.cpu().numpy()
+        if not np.array_equal(again, tokens):
+            print("[bench] a rerun's greedy tokens differ from the timed run's", file=sys.stderr)
+            sys.exit(1)
+        return ms / 1e3 / max(cnt, 1), cnt
+
+    roofline = None
+    if not args.no_kernel_timing:
+        a_s, a_n = timed(dtd.KERNEL_ATTN)
+        per_attn = kv_total / K / s.n_layers            # one layer's KV read, all sequences
+        g_s, g_n = timed(dtd.KERNEL_GATE_UP)
+        per_gu = wb["per_layer"]["gate_up"]
+        roofline = {"bound": "hbm", "achieved": round(per_attn / a_s / 1e9, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                    "frac": round(per_attn / a_s / 1e9 / PEAK_HBM_GBS, 4), "traffic": None,
+                    "kernel": f"k_attn (split-K GQA decode attention over paged {synth.KV_NAMES[s.kvfmt]} KV, "
+                              f"{B} sequences, one layer)",
+                    "bytes_per_launch": round(per_attn), "avg_launch_us": round(a_s * 1e6, 2), "launches": a_n,
+                    "gemm_gate_up": {"kernel": f"k_gemm (gate/up projection on the matrix cores, "
+                                               f"{synth.WFMT_NAMES[s.wfmt]} weights, batch {B})",
+                                     "achieved": round(per_gu / g_s / 1e9, 1),
+                                     "frac": round(per_gu / g_s / 1e9 / PEAK_HBM_GBS, 4),
+                                     "bytes_per_launch": per_gu, "avg_launch_us": round(g_s * 1e6, 2),
+                                     "launches": g_n,
+                                     "mfma_tflops": round(2.0 * s.dim * 2 * s.ffn_dim * B / g_s / 1e12, 2)}}
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline_batched(w, weights, ctxs, 2)
+    ctx_desc = (f"per-sequence contexts uniform in [512, 4096] (seed 7; mean {float(ctxs.mean()):.0f})"
+                if w.mixed_contexts else f"every sequence at context {w.context}")
+    rec = {
+        "metric": "decode tokens/s and achieved HBM GB/s (% of peak) per decode step, 1 GPU",
+        "value": round(B * K / dt, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(dt / K * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": f"{synth.WFMT_NAMES[s.wfmt]} weights x {synth.ACT_NAMES[s.act]} activations, "
+                 f"{synth.KV_NAMES[s.kvfmt]} KV, fp32 accumulation",
+        "data": "synthetic",
+        "config": {"workload": f"{s.name} batched greedy decode, batch {B}, paged KV blocks of {w.block_size}, "
+                               f"{ctx_desc}; synthetic KV, then {W} warmup and {K} timed steps ending at each "
+                               f"sequence's context",
+                   "dim": s.dim, "layers": s.n_layers, "q_heads": s.n_q_heads, "kv_heads": s.n_kv_heads,
+                   "head_dim": s.head_dim, "ffn": s.ffn_dim, "vocab": s.vocab,
+                   "weights": synth.WFMT_NAMES[s.wfmt], "activations": synth.ACT_NAMES[s.act],
+                   "kv_cache": synth.KV_NAMES[s.kvfmt], "batch": B},
+        "hbm_gbs": round(gbs, 1),
+        "hbm_frac_of_peak": round(gbs / PEAK_HBM_GBS, 4),
+        "bytes_per_step": round(bytes_total / K),
+        "greedy_tokens_checked": "timed run == kernel-timing reruns; device error word clear",
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

@@ -73,6 +73,8 @@ struct dtd_engine {
   float* knew = nullptr;
   float* vnew = nullptr;
   float* partials = nullptr;
+  float* gemm_partials = nullptr;   // split-K sums of the batched matrix-core projections
+  int cus = 0;                      // compute units of the device
   void* o = nullptr;
   void* h = nullptr;
   float* logits = nullptr;
@@ -309,7 +311,7 @@ static dtd_status dev_alloc(dtd_engine* e, T** p, size_t bytes) {
 static void free_all(dtd_engine* e) {
   release_weights(e);
   void* ps[] = {e->rope_cos, e->rope_sin, e->kpool, e->vpool, e->kspool, e->vspool, e->bt_dev,
-                e->x, e->xn, e->q, e->knew, e->vnew, e->partials, e->o, e->h, e->logits,
+                e->x, e->xn, e->q, e->knew, e->vnew, e->partials, e->gemm_partials, e->o, e->h, e->logits,
                 e->err_dev, e->desc_dev, e->rows_dev, e->players, e->tags};
   for (void* p : ps)
     if (p) (void)hipFree(p);
@@ -407,6 +409,11 @@ extern "C" dtd_status dtd_create(const dtd_config* cfg, void* hip_stream, dtd_en
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, e->device) != hipSuccess ||
         hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, e->device) != hipSuccess)
       return cleanup(DTD_E_HIP);
+    e->cus = cus > 0 ? cus : 1;
+    // split-K sums of the matrix-core projections (batched steps)
+    if (MB >= 2 && gemm_eligible(d, MB)) {
+      if ((st = dev_alloc(e, &e->gemm_partials, gemm_partial_bytes(d, MB, e->cus)))) return cleanup(st);
+    }
     e->p_nch = (cfg->max_ctx + kAttnTile - 1) / kAttnTile;
     e->p_smem = persistent_smem_bytes(d, e->p_nch, cus > 0 ? cus : 1);
     if (coop && cus > 0 && persistent_supports(d) && persistent_prepare(d, e->p_smem, &per_cu) == hipSuccess &&
@@ -679,7 +686,7 @@ static ProbeLayout probe_layout(const Dims& d, int B, size_t ab) {
 // inject record and its output is copied to the capture record, so each kernel can be
 // compared with the reference operation on identical inputs.
 static dtd_status run_sub_steps(dtd_engine* e, int B, bool do_head, const uint8_t* inject, uint8_t* capture,
-                                float* partials);
+                                float* partials, float* gemm_partials);
 
 // partials: the split-K attention partials of the per-sub-step schedule (the engine's buffer,
 // or the allocation-free entry point's static scratch).  force_per_kernel: run that schedule
@@ -687,9 +694,10 @@ static dtd_status run_sub_steps(dtd_engine* e, int B, bool do_head, const uint8_
 static dtd_status run_step(dtd_engine* e, int B, const int* slots, const int* poss, const int* pblks,
                            const int32_t* tokens, int32_t* next, float* logits_out, bool do_head,
                            const Update* upd, int n_upd, const uint8_t* inject = nullptr,
-                           uint8_t* capture = nullptr, float* partials = nullptr, bool force_per_kernel = false,
-                           bool no_timing = false) {
+                           uint8_t* capture = nullptr, float* partials = nullptr, float* gemm_partials = nullptr,
+                           bool force_per_kernel = false, bool no_timing = false) {
   if (!partials) partials = e->partials;
+  if (!gemm_partials) gemm_partials = e->gemm_partials;
   const Dims& d = e->d;
   hipStream_t st = e->stream;
   // descriptor into the next pinned ring slot, then one host->device copy
@@ -761,16 +769,22 @@ static dtd_status run_step(dtd_engine* e, int B, const int* slots, const int* po
     return fail(e, DTD_E_UNSUPPORTED, "persistent step kernel unavailable for this call");
   const int timing_saved = e->timing_kind;
   if (no_timing) e->timing_kind = -1;
-  const dtd_status rs = run_sub_steps(e, B, do_head, inject, capture, partials);
+  const dtd_status rs = run_sub_steps(e, B, do_head, inject, capture, partials, gemm_partials);
   e->timing_kind = timing_saved;
   return rs;
 }
 
 // The per-sub-step schedule of one step (the descriptor is already on the device).
 static dtd_status run_sub_steps(dtd_engine* e, int B, bool do_head, const uint8_t* inject, uint8_t* capture,
-                                float* partials) {
+                                float* partials, float* gemm_partials) {
   const Dims& d = e->d;
   hipStream_t st = e->stream;
+  // a projection: on the matrix cores when the batch makes it a real GEMM, else the
+  // weight-streaming GEMV
+  const bool mfma = gemm_eligible(d, B);
+  auto proj = [&](const MatDev& m, const void* xin, int epi, const EpiArgs& ea) {
+    return mfma ? launch_gemm(d, m, xin, B, epi, ea, gemm_partials, e->cus, st) : launch_gemv(d, m, xin, B, epi, ea, st);
+  };
 
   HIP_OK(e, launch_embed(d, e->emb, e->desc_dev, B, e->bt_dev, e->x, e->err_dev, st));
   const size_t ab = act_bytes(e->cfg.act);
@@ -807,7 +821,7 @@ static dtd_status run_sub_steps(dtd_engine* e, int B, bool do_head, const uint8_
       HIP_OK(e, cp(out + pl.xn, e->xn, fxn));
       HIP_OK(e, cp(e->xn, in + pl.xn, fxn));
     }
-    TIMED(2, launch_gemv(d, W.qkv, e->xn, B, EPI_QKV, ea, st));
+    TIMED(2, proj(W.qkv, e->xn, EPI_QKV, ea));
     if (probe) {
       HIP_OK(e, cp(out + pl.q, e->q, fq));
       HIP_OK(e, cp(out + pl.k, e->knew, fkv));
@@ -823,7 +837,7 @@ static dtd_status run_sub_steps(dtd_engine* e, int B, bool do_head, const uint8_
       HIP_OK(e, cp(e->o, in + pl.o, fo));
       HIP_OK(e, cp(e->x, in + pl.x_in, fx));
     }
-    TIMED(3, launch_gemv(d, W.o, e->o, B, EPI_RESID, ea, st));
+    TIMED(3, proj(W.o, e->o, EPI_RESID, ea));
     if (probe) {
       HIP_OK(e, cp(out + pl.x_mid, e->x, fx));
       HIP_OK(e, cp(e->x, in + pl.x_mid, fx));
@@ -833,12 +847,12 @@ static dtd_status run_sub_steps(dtd_engine* e, int B, bool do_head, const uint8_
       HIP_OK(e, cp(out + pl.xn2, e->xn, fxn));
       HIP_OK(e, cp(e->xn, in + pl.xn2, fxn));
     }
-    TIMED(0, launch_gemv(d, W.gu, e->xn, B, EPI_SWIGLU, ea, st));
+    TIMED(0, proj(W.gu, e->xn, EPI_SWIGLU, ea));
     if (probe) {
       HIP_OK(e, cp(out + pl.h, e->h, fh));
       HIP_OK(e, cp(e->h, in + pl.h, fh));
     }
-    TIMED(1, launch_gemv(d, W.down, e->h, B, EPI_RESID, ea, st));
+    TIMED(1, proj(W.down, e->h, EPI_RESID, ea));
     if (probe) HIP_OK(e, cp(out + pl.x_out, e->x, fx));
     if (e->capture)
       HIP_OK(e, hipMemcpyAsync(e->capture + (size_t)(l + 1) * B * d.D, e->x, (size_t)B * d.D * 4,
@@ -847,7 +861,7 @@ static dtd_status run_sub_steps(dtd_engine* e, int B, bool do_head, const uint8_
   if (probe) HIP_OK(e, cp(e->x, inject + (size_t)(d.L - 1) * pl.record + pl.x_out, fx));
   if (do_head) {
     HIP_OK(e, launch_rmsnorm(d, e->x, e->final_norm, e->xn, B, st));
-    TIMED(5, launch_gemv(d, e->head, e->xn, B, EPI_LOGITS, ea, st));
+    TIMED(5, proj(e->head, e->xn, EPI_LOGITS, ea));
     HIP_OK(e, launch_argmax(d, e->desc_dev, B, e->logits, st));
   }
   return DTD_OK;
@@ -912,7 +926,7 @@ extern "C" dtd_status dtd_prefill(dtd_engine* e, int64_t seq_id, const int32_t* 
 static dtd_status decode_impl(dtd_engine* e, int32_t batch, const int64_t* seq_ids_host,
                               const int32_t* tokens_dev, int32_t* next_tokens_dev, float* logits_dev,
                               const uint8_t* inject, uint8_t* capture, bool create_missing,
-                              float* partials = nullptr, bool no_alloc = false) {
+                              float* partials = nullptr, float* gemm_partials = nullptr, bool no_alloc = false) {
   dtd_status st = ready(e);
   if (st) return st;
   if (batch <= 0 || batch > e->cfg.max_batch)
@@ -970,7 +984,7 @@ static dtd_status decode_impl(dtd_engine* e, int32_t batch, const int64_t* seq_i
     pblks[b] = s.blocks[(size_t)(s.len / e->d.bs)];
   }
   st = run_step(e, batch, slots, poss, pblks, tokens_dev, next_tokens_dev, logits_dev, true, upd, n_upd,
-                inject, capture, partials, no_alloc, no_alloc);
+                inject, capture, partials, gemm_partials, no_alloc, no_alloc);
   if (st) return st;
   for (int b = 0; b < batch; b++) ss[b]->len++;
   return DTD_OK;
@@ -988,16 +1002,19 @@ extern "C" dtd_status dtd_decode_step_noalloc(dtd_engine* e, int32_t batch, cons
   if (!e) return DTD_E_ARG;
   if (batch <= 0 || batch > e->cfg.max_batch)
     return fail(e, DTD_E_ARG, "decode_step_noalloc: batch %d outside [1, %d]", batch, e->cfg.max_batch);
-  // the split-K attention partials [batch][Hq][nch][hd + 2] fp32 live in the static scratch
+  // The static scratch holds the split-K attention partials [batch][Hq][nch][hd + 2] fp32,
+  // then (batched matrix-core projections) the split-K sums of the projections.
   const Dims& d = e->d;
-  const size_t need = (size_t)batch * d.Hq * d.nch * (d.hd + 2) * sizeof(float);
-  if (need > kNoAllocScratchBytes)
+  const size_t attn = ((size_t)batch * d.Hq * d.nch * (d.hd + 2) * sizeof(float) + 255) / 256 * 256;
+  const size_t gemm = gemm_eligible(d, batch) ? gemm_partial_bytes(d, batch, e->cus) : 0;
+  if (attn + gemm > kNoAllocScratchBytes)
     return fail(e, DTD_E_UNSUPPORTED,
-                "decode_step_noalloc: %zu bytes of attention partials for batch %d exceed the %zu-byte "
-                "static scratch (fewer sequences per call, or a shorter max_ctx, fit)",
-                need, batch, kNoAllocScratchBytes);
+                "decode_step_noalloc: %zu bytes of attention partials and %zu of projection partial sums for "
+                "batch %d exceed the %zu-byte static scratch (fewer sequences per call, or a shorter max_ctx, fit)",
+                attn, gemm, batch, kNoAllocScratchBytes);
+  float* base = (float*)e->scratch_dev;
   return decode_impl(e, batch, seq_ids_host, tokens_dev, next_tokens_dev, logits_dev, nullptr, nullptr, false,
-                     (float*)e->scratch_dev, true);
+                     base, (float*)((uint8_t*)base + attn), true);
 }
 
 extern "C" dtd_status dtd_debug_decode_probe(dtd_engine* e, int32_t batch, const int64_t* seq_ids_host,

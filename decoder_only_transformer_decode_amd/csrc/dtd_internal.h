@@ -150,6 +150,12 @@ hipError_t launch_rmsnorm(const Dims& d, const float* x, const float* g, void* x
                           hipStream_t st);
 hipError_t launch_gemv(const Dims& d, const MatDev& m, const void* xin, int B, int epi,
                        const EpiArgs& ea, hipStream_t st);
+// batch > 1 projections on the matrix cores (bf16 activations; int8-row or bf16 weights)
+bool gemm_eligible(const Dims& d, int B);
+int gemm_splits(int N, int K, int cus);                 // K splits of an N x K matrix
+size_t gemm_partial_bytes(const Dims& d, int B, int cus);   // work buffer of the split-K sums
+hipError_t launch_gemm(const Dims& d, const MatDev& m, const void* xin, int B, int epi, const EpiArgs& ea,
+                       float* partials, int cus, hipStream_t st);
 hipError_t launch_attention(const Dims& d, const StepDesc* desc, int B, const float* q,
                             const float* knew, const float* vnew, const KvLayer& kv,
                             const int32_t* block_table, float* partials, hipStream_t st);

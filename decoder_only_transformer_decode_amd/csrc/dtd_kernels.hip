@@ -8,6 +8,7 @@
 // wavefront with cross-lane shuffles.  Everything that does not move weight or KV bytes
 // (RMSNorm scaling, RoPE, KV append, SwiGLU, residual adds, argmax) rides in the
 // prologues and epilogues of those kernels.
+#include <algorithm>
 #include <math.h>
 #include <stdint.h>
 #include <limits.h>
@@ -19,6 +20,7 @@ namespace dtd {
 namespace {
 
 using namespace dev;
+using std::max;
 
 // ---------------------------------------------------------------------------------------
 // S0 embedding (+ block-table updates of this step)
@@ -254,6 +256,211 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
 }
 
 // ---------------------------------------------------------------------------------------
+// S2 / S6 / S8 / S9 / S10 at batch > 1: weight-streaming GEMM on the matrix cores
+//
+// With several sequences a projection is a real (small-M) GEMM: every weight element is
+// used once per sequence, and streaming the weights at HBM speed takes more multiply-adds
+// than the vector units deliver.  C[n][b] = sum_k W[n][k] X[b][k] runs as
+// v_mfma_f32_16x16x32_bf16 tiles: A = 16 weight rows x 32 k (int8-row codes are exact in
+// bf16, their row scale is applied to the fp32 sum, after the dot, as in the int8
+// weight-only scheme of "从 smollm3.go 看 LLM inference"), B = 32 k x 16 sequences of the
+// bf16 activations, fp32 accumulation.
+//
+// A workgroup (4 waves) owns 64 weight rows, each wave 16; each lane streams its row's 16-byte
+// pieces straight from HBM into MFMA operand registers (nontemporal loads), one K chunk of
+// 256 columns ahead of use.  The activation chunk [16*NBB sequences][256] is staged in LDS,
+// double buffered, and read as the B operands by all four waves.  When a matrix has fewer
+// row tiles than compute units, its K range is split over S workgroups (blockIdx.y); their
+// fp32 partial sums go to a work buffer and k_gemm_reduce adds them in a fixed order and
+// runs the epilogue, so the result does not depend on scheduling.
+// ---------------------------------------------------------------------------------------
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kGemmRows = 64;                 // weight rows per workgroup (4 waves x 16)
+constexpr int kGemmKC = 256;                  // K columns per staged activation chunk
+constexpr int kGemmLd = kGemmKC * 2 + 16;     // LDS bytes per staged sequence row (16 B pad)
+
+struct GemmArgs {
+  GemvArgs g;        // dims, matrix, bf16 input [B][K], batch, epilogue destinations
+  float* partials;   // [S][B][N] fp32 when S > 1
+  int S;             // K splits
+  int nchunk;        // K chunks of kGemmKC columns
+};
+
+// k covered by one 16-byte piece per lane: 8 bf16 or 16 int8 per lane, 4 lanes per row
+template <int WFMT> struct GemmW {
+  static constexpr int EB = WFMT == W_BF16 ? 2 : 1;
+  static constexpr int KSTEP = 64 / EB;            // k per load step of a 16-row tile
+  static constexpr int LPC = kGemmKC / KSTEP;       // load steps per chunk: bf16 8, int8 4
+};
+
+// two int8 codes (bytes b, b + 1 of u) as a packed pair of bf16 (exact: |q| <= 127)
+__device__ __forceinline__ uint32_t i8x2_to_bf16x2(uint32_t u, int b) {
+  const uint32_t lo = __float_as_uint(sext8(u, b)), hi = __float_as_uint(sext8(u, b + 1));
+  return __builtin_amdgcn_perm(hi, lo, 0x07060302u);   // upper halves: lo's, then hi's
+}
+
+template <int WFMT, int EPI, int NBB>
+__global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t xl[];   // [2][16*NBB][kGemmLd]
+  constexpr int EB = GemmW<WFMT>::EB, KSTEP = GemmW<WFMT>::KSTEP, LPC = GemmW<WFMT>::LPC;
+  constexpr int XROWS = 16 * NBB, XV = XROWS * kGemmKC / 8 / 256;   // 16-byte X pieces per thread
+  constexpr int BUF = XROWS * kGemmLd;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int N = a.g.m.rows, K = a.g.m.cols, B = a.g.B;
+  const int n0 = blockIdx.x * kGemmRows;
+  const int sp = blockIdx.y, S = a.S;
+  const int c_lo = sp * a.nchunk / S, c_hi = (sp + 1) * a.nchunk / S;
+  // this lane's weight row, and the k offset of its 16 bytes within a load step
+  const int row = n0 + 16 * wave + (lane & 15);
+  const bool row_ok = row < N;
+  const uint8_t* wbase = (const uint8_t*)a.g.m.w;
+  const uint8_t* wrow = wbase + (size_t)(row_ok ? row : 0) * (size_t)K * EB;
+  const int kl = (lane >> 4) * (16 / EB);
+  const uint8_t* xg = (const uint8_t*)a.g.xin;
+
+  // Loads outside the matrix (past K, or chunks past this split) read the matrix's first 16
+  // bytes: every such lane of a wave hits one line, and each buffer keeps one issue site.
+  auto issue_w = [&](int c, u32x4 (&w)[LPC]) {
+#pragma unroll
+    for (int i = 0; i < LPC; i++) {
+      const int k = c * kGemmKC + i * KSTEP + kl;
+      const bool ok = row_ok && c < c_hi && k < K;
+      w[i] = gload_stream<u32x4>(ok ? wrow + (size_t)k * EB : wbase);
+    }
+  };
+  auto x_piece = [&](int c, int v, int& r, int& k) {
+    const int idx = tid + 256 * v;
+    r = idx >> 5;                                   // kGemmKC / 8 = 32 pieces per row
+    k = c * kGemmKC + (idx & 31) * 8;
+  };
+  auto issue_x = [&](int c, uint4 (&x)[XV]) {
+#pragma unroll
+    for (int v = 0; v < XV; v++) {
+      int r, k;
+      x_piece(c, v, r, k);
+      const bool ok = r < B && k < K && c < c_hi;
+      x[v] = gload<uint4>(ok ? xg + ((size_t)r * K + k) * 2 : xg);
+    }
+  };
+  auto store_x = [&](int c, const uint4 (&x)[XV], int buf) {
+#pragma unroll
+    for (int v = 0; v < XV; v++) {
+      int r, k;
+      x_piece(c, v, r, k);
+      const bool ok = r < B && k < K;
+      *(uint4*)(xl + buf * BUF + r * kGemmLd + (k - c * kGemmKC) * 2) = ok ? x[v] : make_uint4(0u, 0u, 0u, 0u);
+    }
+  };
+  f32x4 acc[NBB];
+#pragma unroll
+  for (int j = 0; j < NBB; j++) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto consume = [&](const u32x4 (&w)[LPC], int buf) {
+    const uint8_t* xb = xl + buf * BUF + (lane & 15) * kGemmLd;
+#pragma unroll
+    for (int i = 0; i < LPC; i++) {
+      const int kc = (i * KSTEP + kl) * 2;         // byte column of the lane's first k in the chunk
+      if constexpr (WFMT == W_BF16) {
+        const bf16x8 A = __builtin_bit_cast(bf16x8, w[i]);
+#pragma unroll
+        for (int j = 0; j < NBB; j++) {
+          const bf16x8 Bv = *(const bf16x8*)(xb + j * 16 * kGemmLd + kc);
+          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Bv, acc[j], 0, 0, 0);
+        }
+      } else {
+        // the lane's 16 codes are k .. k+15: the first 8 feed one product, the last 8 the next
+        const u32x4 lo = {i8x2_to_bf16x2(w[i].x, 0), i8x2_to_bf16x2(w[i].x, 2), i8x2_to_bf16x2(w[i].y, 0),
+                          i8x2_to_bf16x2(w[i].y, 2)};
+        const u32x4 hi = {i8x2_to_bf16x2(w[i].z, 0), i8x2_to_bf16x2(w[i].z, 2), i8x2_to_bf16x2(w[i].w, 0),
+                          i8x2_to_bf16x2(w[i].w, 2)};
+        const bf16x8 A0 = __builtin_bit_cast(bf16x8, lo), A1 = __builtin_bit_cast(bf16x8, hi);
+#pragma unroll
+        for (int j = 0; j < NBB; j++) {
+          const bf16x8 B0 = *(const bf16x8*)(xb + j * 16 * kGemmLd + kc);
+          const bf16x8 B1 = *(const bf16x8*)(xb + j * 16 * kGemmLd + kc + 16);
+          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, B0, acc[j], 0, 0, 0);
+          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, B1, acc[j], 0, 0, 0);
+        }
+      }
+    }
+  };
+
+  // Chunk c is multiplied from LDS buffer c & 1 with weight registers WA (even steps) or WB
+  // (odd steps) while chunk c + 1's activations and chunk c + 2's weights are on their way.
+  u32x4 WA[LPC], WB[LPC];
+  uint4 xr[XV];
+  issue_x(c_lo, xr);
+  issue_w(c_lo, WA);
+  issue_w(c_lo + 1, WB);
+  store_x(c_lo, xr, 0);
+  __syncthreads();
+  for (int c = c_lo; c < c_hi; c += 2) {
+    issue_x(c + 1, xr);
+    consume(WA, 0);
+    issue_w(c + 2, WA);
+    store_x(c + 1, xr, 1);
+    __syncthreads();
+    if (c + 1 >= c_hi) break;                     // (uniform)
+    issue_x(c + 2, xr);
+    consume(WB, 1);
+    issue_w(c + 3, WB);
+    store_x(c + 2, xr, 0);
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < LPC; i++) { (void)WA[i]; (void)WB[i]; }
+
+  // lane l holds rows 4(l/16) .. +3 of the wave's 16, for sequence 16 j + l % 16
+  const int r0 = n0 + 16 * wave + 4 * (lane >> 4);
+#pragma unroll
+  for (int j = 0; j < NBB; j++) {
+    const int b = 16 * j + (lane & 15);
+    if (b >= B) continue;
+    if (S == 1) {
+      float v[4] = {acc[j][0], acc[j][1], acc[j][2], acc[j][3]};
+      if constexpr (WFMT == W_INT8_ROW) {
+#pragma unroll
+        for (int r = 0; r < 4; r++)
+          if (r0 + r < N) v[r] *= ((const float*)a.g.m.s)[r0 + r];   // row scale after the dot
+      }
+      gemv_epilogue<EPI, 4>(a.g, b, r0, v);
+    } else {
+      float* P = a.partials + ((size_t)sp * B + b) * N;
+#pragma unroll
+      for (int r = 0; r < 4; r++)
+        if (r0 + r < N) P[r0 + r] = acc[j][r];
+    }
+  }
+}
+
+// the S partial sums of 4 consecutive rows of one sequence, added in split order, then the
+// epilogue
+template <int WFMT, int EPI>
+__global__ __launch_bounds__(256) void k_gemm_reduce(GemmArgs a) {
+  const int N = a.g.m.rows, B = a.g.B;
+  const int nq = (N + 3) / 4;
+  const int idx = blockIdx.x * 256 + threadIdx.x;
+  if (idx >= nq * B) return;
+  const int b = idx / nq, r0 = (idx - b * nq) * 4;
+  float v[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int sp = 0; sp < a.S; sp++) {
+    const float* P = a.partials + ((size_t)sp * B + b) * N;
+#pragma unroll
+    for (int r = 0; r < 4; r++)
+      if (r0 + r < N) v[r] += P[r0 + r];
+  }
+  if constexpr (WFMT == W_INT8_ROW) {
+#pragma unroll
+    for (int r = 0; r < 4; r++)
+      if (r0 + r < N) v[r] *= ((const float*)a.g.m.s)[r0 + r];
+  }
+  gemv_epilogue<EPI, 4>(a.g, b, r0, v);
+}
+
+// ---------------------------------------------------------------------------------------
 // S4 + S5 split-K GQA decode attention (work item in dtd_device.h) and the chunk merge
 // ---------------------------------------------------------------------------------------
 
@@ -389,7 +596,86 @@ hipError_t gemv_epi(const GemvArgs& a, int epi, int NB, int ROWS, dim3 grid, siz
 }
 
 
+// Lets an instantiation use more than the default 64 KB of dynamic LDS (once per kernel).
+template <int WFMT, int EPI, int NBB>
+hipError_t gemm_lds_limit(size_t smem) {
+  static const hipError_t r = hipFuncSetAttribute((const void*)k_gemm<WFMT, EPI, NBB>,
+                                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+  return r;
+}
+
+template <int WFMT, int EPI>
+hipError_t gemm_dispatch(const GemmArgs& a, int nbb, dim3 grid, size_t smem, hipStream_t st) {
+  hipError_t r = hipSuccess;
+  switch (nbb) {
+    case 1: hipLaunchKernelGGL((k_gemm<WFMT, EPI, 1>), grid, dim3(256), smem, st, a); break;
+    case 2: hipLaunchKernelGGL((k_gemm<WFMT, EPI, 2>), grid, dim3(256), smem, st, a); break;
+    case 3: hipLaunchKernelGGL((k_gemm<WFMT, EPI, 3>), grid, dim3(256), smem, st, a); break;
+    default:
+      if ((r = gemm_lds_limit<WFMT, EPI, 4>(smem)) != hipSuccess) return r;
+      hipLaunchKernelGGL((k_gemm<WFMT, EPI, 4>), grid, dim3(256), smem, st, a);
+      break;
+  }
+  r = hipGetLastError();
+  if (r != hipSuccess || a.S == 1) return r;
+  const int threads = (a.g.m.rows + 3) / 4 * a.g.B;
+  hipLaunchKernelGGL((k_gemm_reduce<WFMT, EPI>), dim3((threads + 255) / 256), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+template <int WFMT>
+hipError_t gemm_epi(const GemmArgs& a, int epi, int nbb, dim3 grid, size_t smem, hipStream_t st) {
+  switch (epi) {
+    case EPI_QKV: return gemm_dispatch<WFMT, EPI_QKV>(a, nbb, grid, smem, st);
+    case EPI_RESID: return gemm_dispatch<WFMT, EPI_RESID>(a, nbb, grid, smem, st);
+    case EPI_SWIGLU: return gemm_dispatch<WFMT, EPI_SWIGLU>(a, nbb, grid, smem, st);
+    default: return gemm_dispatch<WFMT, EPI_LOGITS>(a, nbb, grid, smem, st);
+  }
+}
+
 }  // namespace
+
+bool gemm_eligible(const Dims& d, int B) {
+  return B >= 2 && B <= kMaxBatch && d.act == ACT_BF16 && (d.wfmt == W_INT8_ROW || d.wfmt == W_BF16);
+}
+
+int gemm_splits(int N, int K, int cus) {
+  const int tiles = (N + kGemmRows - 1) / kGemmRows;
+  const int nchunk = (K + kGemmKC - 1) / kGemmKC;
+  if (tiles >= cus) return 1;
+  const int S = (cus + tiles - 1) / tiles;
+  return S < nchunk ? S : nchunk;
+}
+
+size_t gemm_partial_bytes(const Dims& d, int B, int cus) {
+  size_t m = 0;
+  const int shapes[5][2] = {{d.qkv_rows, d.D}, {d.D, d.q_dim}, {2 * d.F, d.D}, {d.D, d.F}, {d.V, d.D}};
+  for (const auto& sh : shapes) {
+    const int S = gemm_splits(sh[0], sh[1], cus);
+    if (S > 1) m = std::max(m, (size_t)S * B * sh[0] * sizeof(float));
+  }
+  return m;
+}
+
+hipError_t launch_gemm(const Dims& d, const MatDev& m, const void* xin, int B, int epi, const EpiArgs& ea,
+                       float* partials, int cus, hipStream_t st) {
+  GemmArgs a;
+  a.g.d = d;
+  a.g.m = m;
+  a.g.xin = xin;
+  a.g.B = B;
+  a.g.act_in = d.act;
+  a.g.kc = 0;
+  a.g.ea = ea;
+  a.partials = partials;
+  a.S = gemm_splits(m.rows, m.cols, cus);
+  a.nchunk = (m.cols + kGemmKC - 1) / kGemmKC;
+  const int nbb = (B + 15) / 16;
+  const dim3 grid((m.rows + kGemmRows - 1) / kGemmRows, a.S);
+  const size_t smem = 2 * (size_t)16 * nbb * kGemmLd;
+  if (d.wfmt == W_INT8_ROW) return gemm_epi<W_INT8_ROW>(a, epi, nbb, grid, smem, st);
+  return gemm_epi<W_BF16>(a, epi, nbb, grid, smem, st);
+}
 
 hipError_t launch_embed(const Dims& d, const MatDev& emb, const StepDesc* desc, int B,
                         int32_t* block_table, float* x, int32_t* err, hipStream_t st) {

@@ -77,6 +77,8 @@ class Workload:
     # the context before the decoded steps is synthetic stored KV (the workload names a
     # context to decode at, not a prompt to prefill)
     synthetic_prefix: bool = False
+    # batched: each sequence's context drawn by context_lengths() (else all at `context`)
+    mixed_contexts: bool = False
 
 
 # The five model shapes and workloads this library is measured and checked on.
@@ -98,7 +100,8 @@ QWEN3_8B = Workload(
     ModelShape("qwen3-8b-shaped", 4096, 36, 32, 8, 128, 12288, 151936,
                W_BF16, ACT_BF16, KV_BF16),
     batch=64, prompt_len=0, context=4096, block_size=16, seed_index=3,
-    note="batch 64, paged KV block 16, per-sequence context uniform in [512, 4096]")
+    note="batch 64, paged KV block 16, per-sequence context uniform in [512, 4096]",
+    synthetic_prefix=True, mixed_contexts=True)
 LLAMA3_8B = Workload(
     ModelShape("llama-3-8b-shaped", 4096, 32, 32, 8, 128, 14336, 128256,
                W_INT8_ROW, ACT_BF16, KV_I8),

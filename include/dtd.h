@@ -149,13 +149,14 @@ dtd_status dtd_decode_step(dtd_engine* e, int32_t batch, const int64_t* seq_ids_
 /* dtd_decode_step for callers that cannot allocate (code under HIP graph capture, tight
  * serving loops, harnesses that forbid allocation): same arguments, semantics and errors,
  * but the call allocates nothing, on the device or the host.  It runs the one-kernel-per-
- * sub-step schedule at every batch size, with the split-K attention partials (batch x Hq x
- * nch x (head_dim + 2) fp32, nch = ceil(max_ctx / chunk)) in a static device array of
- * 16 MiB that the library holds on each GPU until the process ends; a call that would need
- * more returns DTD_E_UNSUPPORTED before anything is enqueued.  Every call on one GPU shares
- * that array, and each call writes every partial before reading it: calls that overlap on
- * one GPU (other streams, other engines, other threads) race and must be serialised by the
- * caller.  Kernel-timing hooks are not applied to it. */
+ * sub-step schedule at every batch size, with its work memory -- the split-K attention
+ * partials (batch x Hq x nch x (head_dim + 2) fp32, nch = ceil(max_ctx / chunk)) and, for
+ * batched matrix-core projections, their split-K sums (splits x batch x rows fp32) -- in a
+ * static device array of 16 MiB that the library holds on each GPU until the process ends;
+ * a call that would need more returns DTD_E_UNSUPPORTED before anything is enqueued.  Every
+ * call on one GPU shares that array, and each call writes every value it reads there before
+ * reading it: calls that overlap on one GPU (other streams, other engines, other threads)
+ * race and must be serialised by the caller.  Kernel-timing hooks are not applied to it. */
 dtd_status dtd_decode_step_noalloc(dtd_engine* e, int32_t batch, const int64_t* seq_ids_host,
                                    const int32_t* tokens_dev, int32_t* next_tokens_dev,
                                    float* logits_dev);

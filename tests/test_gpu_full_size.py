@@ -99,21 +99,23 @@ def test_llama32_1b_shape_full_width_q8_0_tied_at_context_4096():
     P.close()
 
 
-def test_qwen3_8b_shape_full_width_bf16_paged_batch():
+def test_qwen3_8b_shape_full_width_bf16_paged_batch_64():
+    # the real batch: 64 sequences, contexts uniform in [512, 4096], paged KV blocks of 16
     w = synth.QWEN3_8B
-    ctx = [int(c) for c in synth.context_lengths(w.batch)[:3]]
-    P, O2 = _pair(w, w.shape.replace(n_layers=2), max_seqs=6, max_batch=3)
+    ctx = [int(c) for c in synth.context_lengths(w.batch)]
+    P, O2 = _pair(w, w.shape.replace(n_layers=2), max_seqs=2 * w.batch, max_batch=w.batch)
     for sid, n in enumerate(ctx):
         _write_kv(P, O2, sid, [sid, sid + 100], n, seed=30 + sid)
-    _run(P, O2, [0, 1, 2], dict(enumerate(ctx)))
+    _run(P, O2, list(range(w.batch)), dict(enumerate(ctx)))
     P.close()
 
 
-def test_llama3_8b_shape_full_width_int8_kv_at_context_16384():
+def test_llama3_8b_shape_full_width_int8_kv_batch_32_at_context_16384():
+    # the real batch: 32 sequences at context 16384, int8 KV with fp16 scales
     w = synth.LLAMA3_8B
     n = w.context - 2
-    P, O2 = _pair(w, w.shape.replace(n_layers=2), max_seqs=4, max_batch=2)
-    for sid in (0, 1):
+    P, O2 = _pair(w, w.shape.replace(n_layers=2), max_seqs=2 * w.batch, max_batch=w.batch)
+    for sid in range(w.batch):
         _write_kv(P, O2, sid, [sid, sid + 100], n, seed=40 + sid)
-    _run(P, O2, [1, 0], {0: n, 1: n})
+    _run(P, O2, list(range(w.batch))[::-1], {sid: n for sid in range(w.batch)})
     P.close()

@@ -235,6 +235,57 @@ def test_batched_decode_mixed_lengths(kw):
 
 
 # ---------------------------------------------------------------------------------------
+# batched steps: projections on the matrix cores (bf16 activations, int8-row or bf16 weights)
+# ---------------------------------------------------------------------------------------
+
+def _write_kv_ids(P, sid, gpu_ids, n, seed):
+    s = P.shape
+    for layer in range(s.n_layers):
+        k, v, ks, vs = synth.synthetic_kv(s, n, seed=seed, layer=layer)
+        ks16 = None if ks is None else ks.view(np.uint16)
+        vs16 = None if vs is None else vs.view(np.uint16)
+        for g in gpu_ids:
+            dtd.dtd_debug_kv_write(P.eng.h, g, layer, 0, k, v, ks16, vs16)
+        P.orc.kv_write(P.oslot(sid), layer, 0, k, v, ks, vs)
+
+
+@pytest.mark.parametrize("kw", [dict(act=synth.ACT_BF16, kvfmt=synth.KV_BF16),
+                                dict(wfmt=synth.W_BF16, act=synth.ACT_BF16, kvfmt=synth.KV_BF16),
+                                dict(act=synth.ACT_BF16, kvfmt=synth.KV_I8)],
+                         ids=["int8row", "bf16w", "int8row-i8kv"])
+def test_batched_steps_matrix_core_projections(kw):
+    """64 sequences of mixed lengths, stepped in batches of 64, 40, 17 and 2 (one to four
+    16-sequence column blocks, ragged ones included); the grid shape's matrices have fewer
+    row tiles than compute units, so every projection also takes the split-K path.  Each
+    batch is checked kernel by kernel (probe) and free-running against the oracle."""
+    s = _GRID.replace(**kw)
+    P = Pair(s, max_ctx=64, max_seqs=160, max_batch=64, seed=31)
+    O2 = P.perturbed_oracle(5, max_ctx=64, max_seqs=64)
+    rng = np.random.default_rng(44)
+    ids = list(range(64))
+    lens = [int(n) for n in rng.integers(1, 48, size=64)]
+    for sid, n in zip(ids, lens):
+        _write_kv_ids(P, sid, [sid, sid + 100], n, seed=200 + sid)
+        for layer in range(s.n_layers):
+            k, v, ks, vs = synth.synthetic_kv(s, n, seed=200 + sid, layer=layer)
+            O2.kv_write(P.oslot(sid), layer, 0, k, v, ks, vs)
+    toks = {sid: int(t) for sid, t in zip(ids, rng.integers(0, s.vocab, size=64))}
+    pos = dict(zip(ids, lens))
+    tr = Tracker()
+    for sub in (ids, ids[5:45], ids[30:47], [63, 0]):
+        ng, lg, _ = P.gpu_step(sub, [toks[i] for i in sub])
+        outs = teacher_forced(P, [i + 100 for i in sub], sub, [toks[i] for i in sub], [pos[i] for i in sub],
+                              f"batch {len(sub)}")
+        for b, sid in enumerate(sub):
+            tr.add(lg[b], outs[b][1], O2.step(P.oslot(sid), toks[sid], pos[sid])[1])
+            toks[sid] = outs[b][0]
+            pos[sid] += 1
+        _say(f"batch {len(sub)}: probe ok (bf16 flips so far {P.probe_stats[0]})")
+    tr.check("matrix-core batched " + s.name)
+    P.close()
+
+
+# ---------------------------------------------------------------------------------------
 # the KV append's rounding to the cache type, on fresh float32 vectors with constructed ties
 # ---------------------------------------------------------------------------------------
 
