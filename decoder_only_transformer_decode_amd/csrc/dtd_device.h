@@ -50,7 +50,13 @@ __device__ __forceinline__ T gload_stream(const void* p) {
 
 template <typename T>
 __device__ __forceinline__ void gstore(void* p, T v) {
-  *(__attribute__((address_space(1))) T*)p = v;
+  if constexpr (sizeof(T) == 16) {
+    *(__attribute__((address_space(1))) gv4u*)p = __builtin_bit_cast(gv4u, v);
+  } else if constexpr (sizeof(T) == 8) {
+    *(__attribute__((address_space(1))) gv2u*)p = __builtin_bit_cast(gv2u, v);
+  } else {
+    *(__attribute__((address_space(1))) T*)p = v;
+  }
 }
 
 // ---------------------------------------------------------------------------------------

@@ -245,10 +245,11 @@ static Dims make_dims(const dtd_config* c) {
   d.bs = c->kv_block_size;
   d.max_blocks = (c->max_ctx + d.bs - 1) / d.bs;
   d.max_ctx = c->max_ctx;
-  // Split the context so that a full batch at full context gives ~2048 work items.
+  // Split the context so that a full batch at full context gives ~4096 work items (one
+  // wave each in the common-shape attention kernel: several per compute unit).
   const int64_t work = (int64_t)c->max_batch * d.Hkv * c->max_ctx;
   int ct = kAttnTile;
-  while (ct < 2048 && (int64_t)ct * 2048 < work) ct <<= 1;
+  while (ct < 2048 && (int64_t)ct * 4096 < work) ct <<= 1;
   d.ct = ct;
   d.nch = (c->max_ctx + ct - 1) / ct;
   d.eps = c->rms_eps;

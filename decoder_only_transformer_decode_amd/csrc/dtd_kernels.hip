@@ -478,6 +478,347 @@ __global__ __launch_bounds__(256) void k_attn(AttnCtx a, const StepDesc* desc, f
                    [partials](size_t i, float v) { partials[i] = v; });
 }
 
+// ---------------------------------------------------------------------------------------
+// S4 + S5 for the common shapes (KV blocks of 16 positions; head size 128 or 64 with 4 query
+// heads per KV head, or 32 with 5): one wave per (sequence b, KV head j, chunk c)
+//
+// The wave walks its chunk one paged block at a time.  A block's K (and V) rows of head j
+// are contiguous in the pool, so one wave-wide load of 16 bytes per lane reads 1 KB of it,
+// fully coalesced; lane l then holds elements [e0, e0 + 16/EB) of one position, e0 set by
+// l mod LPP (LPP lanes per position).  The block ids of the chunk sit in two registers and
+// are broadcast with readlane, and the loads of the next two blocks are in flight while one
+// is being used.  Scores, the online softmax and P V for the whole query group run in
+// registers: per-lane partial dot products reduced over the LPP lanes of a position with DPP,
+// softmax statistics across positions with cross-group shuffles, so K and V are read once
+// for the G heads (the GQA decode rule of the Qwen3-8B engine article, 4.4.2) without
+// staging through LDS or any workgroup barrier.  The wave leaves an unnormalised partial
+// (acc, m, l) per head in the same layout as k_attn; k_combine merges the chunks.
+// ---------------------------------------------------------------------------------------
+
+template <int CTRL>
+__device__ __forceinline__ float dppf(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+
+// sum / max over aligned groups of L consecutive lanes; every lane of a group gets its result
+template <int L>
+__device__ __forceinline__ float grp_sum(float v) {
+  if constexpr (L >= 2) v += dppf<0xb1>(v);    // quad_perm [1,0,3,2]
+  if constexpr (L >= 4) v += dppf<0x4e>(v);    // quad_perm [2,3,0,1]
+  if constexpr (L >= 8) v += dppf<0x141>(v);   // row_half_mirror
+  if constexpr (L >= 16) v += dppf<0x140>(v);  // row_mirror
+  if constexpr (L >= 32) v += __shfl_xor(v, 16, 64);
+  if constexpr (L >= 64) v += __shfl_xor(v, 32, 64);
+  return v;
+}
+
+template <int L>
+__device__ __forceinline__ float grp_max(float v) {
+  if constexpr (L >= 2) v = fmaxf(v, dppf<0xb1>(v));
+  if constexpr (L >= 4) v = fmaxf(v, dppf<0x4e>(v));
+  if constexpr (L >= 8) v = fmaxf(v, dppf<0x141>(v));
+  if constexpr (L >= 16) v = fmaxf(v, dppf<0x140>(v));
+  if constexpr (L >= 32) v = fmaxf(v, __shfl_xor(v, 16, 64));
+  if constexpr (L >= 64) v = fmaxf(v, __shfl_xor(v, 32, 64));
+  return v;
+}
+
+// sum / max over the lanes l, l ^ S, l ^ 2S, ... (one lane of every group of S)
+template <int S>
+__device__ __forceinline__ float xgrp_sum(float v) {
+#pragma unroll
+  for (int m = S; m < 64; m <<= 1) v += __shfl_xor(v, m, 64);
+  return v;
+}
+
+template <int S>
+__device__ __forceinline__ float xgrp_max(float v) {
+#pragma unroll
+  for (int m = S; m < 64; m <<= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
+  return v;
+}
+
+// Layout of one wave-wide load of a block's rows: PB bytes per lane (16; 8 for int8, so that
+// a lane holds 8 elements in every format and the registers stay within two waves per SIMD).
+template <int KVFMT, int HD>
+struct WaveKv {
+  static constexpr int EB = KVFMT == KV_F32 ? 4 : (KVFMT == KV_BF16 ? 2 : 1);
+  static constexpr int PB = KVFMT == KV_I8 ? 8 : 16;
+  static constexpr int RB = HD * EB;         // bytes of one position's row (one KV head)
+  static constexpr int LPP = RB / PB;        // lanes per position in one wave-wide load
+  static constexpr int PPI = 64 / LPP;       // positions per wave-wide load
+  static constexpr int ELEM = PB / EB;       // elements per lane per load
+  static constexpr int NI = 16 / PPI;        // loads per 16-position block
+  static constexpr int LOADB = 64 * PB;      // bytes per wave-wide load
+  static_assert(16 * RB >= LOADB && PPI <= 16, "a block must fill at least one wave-wide load");
+};
+
+template <int PB> struct Piece;
+template <> struct Piece<16> { typedef uint4 T; };
+template <> struct Piece<8> { typedef uint2 T; };
+
+// the floats of one piece of a stored row (int8: the codes, unscaled)
+template <int KVFMT, int ELEM>
+__device__ __forceinline__ void decode_piece(const uint2& u, float (&f)[ELEM]) {
+  static_assert(KVFMT == KV_I8 && ELEM == 8, "8-byte pieces: int8");
+  const uint32_t w[2] = {u.x, u.y};
+#pragma unroll
+  for (int q = 0; q < 2; q++)
+#pragma unroll
+    for (int b = 0; b < 4; b++) f[4 * q + b] = sext8(w[q], b);
+}
+
+template <int KVFMT, int ELEM>
+__device__ __forceinline__ void decode_piece(const uint4& u, float (&f)[ELEM]) {
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int q = 0; q < 4; q++) {
+    if constexpr (KVFMT == KV_F32) {
+      f[q] = __uint_as_float(w[q]);
+    } else if constexpr (KVFMT == KV_BF16) {
+      f[2 * q] = __uint_as_float(w[q] << 16);
+      f[2 * q + 1] = __uint_as_float(w[q] & 0xffff0000u);
+    } else {
+#pragma unroll
+      for (int b = 0; b < 4; b++) f[4 * q + b] = sext8(w[q], b);
+    }
+  }
+}
+
+template <int KVFMT, int HD, int G>
+__global__ __launch_bounds__(256) void k_attn_w(AttnCtx a, const StepDesc* desc, float* partials) {
+  using W = WaveKv<KVFMT, HD>;
+  constexpr int RB = W::RB, LPP = W::LPP, PPI = W::PPI, ELEM = W::ELEM, NI = W::NI, PB = W::PB;
+  typedef typename Piece<PB>::T PieceT;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int c = blockIdx.x * 4 + wave, j = blockIdx.y, b = blockIdx.z;
+  const Dims& d = a.d;
+  const int pos = desc->pos[b];
+  const int t_begin = c * a.ct;
+  if (c >= a.nch || t_begin > pos) return;              // (wave-uniform) chunk past the sequence
+  const int t_end = min(pos + 1, t_begin + a.ct);
+  const int pg = lane / LPP, e0 = (lane % LPP) * ELEM;
+  const int Hkv = d.Hkv;
+
+  // the group's queries at this lane's elements, scaled by 1/sqrt(hd)
+  float q[G][ELEM];
+  {
+    const float sc = 1.0f / sqrtf((float)HD);
+    const float* qb = a.q + (size_t)b * d.q_dim + (size_t)j * G * HD + e0;
+#pragma unroll
+    for (int h = 0; h < G; h++)
+#pragma unroll
+      for (int e = 0; e < ELEM; e += 4) {
+        const float4 v = gload<float4>(qb + h * HD + e);
+        q[h][e] = v.x * sc; q[h][e + 1] = v.y * sc; q[h][e + 2] = v.z * sc; q[h][e + 3] = v.w * sc;
+      }
+  }
+  // block ids of the chunk's blocks (at most 128)
+  const int lb0 = t_begin >> 4, nb = (t_end - t_begin + 15) >> 4;
+  const int32_t* btrow = a.bt + (size_t)desc->slot[b] * d.max_blocks;
+  const int bt_lo = lane < nb ? gload<int32_t>(btrow + lb0 + lane) : 0;
+  const int bt_hi = lane + 64 < nb ? gload<int32_t>(btrow + lb0 + lane + 64) : 0;
+
+  // The new position: rounded to the KV encoding and appended through the block table by the
+  // wave whose chunk holds it; its stored (decoded) values replace the block's row there.
+  const bool has_new = pos >= t_begin && pos < t_end;
+  float nk[ELEM], nv[ELEM];
+#pragma unroll
+  for (int e = 0; e < ELEM; e++) nk[e] = nv[e] = 0.f;
+  if (has_new) {
+    const size_t row = ((size_t)desc->pos_block[b] * Hkv + j) * 16 + (pos & 15);
+#pragma unroll
+    for (int which = 0; which < 2; which++) {
+      const float* src = (which ? a.vnew : a.knew) + (size_t)b * d.kv_dim + (size_t)j * HD + e0;
+      float x[ELEM];
+#pragma unroll
+      for (int e = 0; e < ELEM; e += 4) {
+        const float4 v = gload<float4>(src + e);
+        x[e] = v.x; x[e + 1] = v.y; x[e + 2] = v.z; x[e + 3] = v.w;
+      }
+      float dec[ELEM];
+      uint32_t w[4] = {0u, 0u, 0u, 0u};
+      if constexpr (KVFMT == KV_F32) {
+#pragma unroll
+        for (int e = 0; e < ELEM; e++) dec[e] = x[e];
+#pragma unroll
+        for (int qd = 0; qd < 4; qd++) w[qd] = __float_as_uint(x[qd]);
+      } else if constexpr (KVFMT == KV_BF16) {
+#pragma unroll
+        for (int qd = 0; qd < 4; qd++) {
+          const uint32_t lo = f32_to_bf16(x[2 * qd]), hi = f32_to_bf16(x[2 * qd + 1]);
+          w[qd] = lo | hi << 16;
+          dec[2 * qd] = bf16_to_f32(lo);
+          dec[2 * qd + 1] = bf16_to_f32(hi);
+        }
+      } else {
+        // s = fp16(max|x| / 127) over the head's hd values (the LPP lanes of a position hold
+        // them all), q = clamp(rint(x / s), -127, 127), s = 0 gives q = 0
+        float mx = 0.f;
+#pragma unroll
+        for (int e = 0; e < ELEM; e++) mx = fmaxf(mx, fabsf(x[e]));
+        mx = grp_max<LPP>(mx);
+        const uint16_t s16 = f32_to_f16(mx / 127.0f);
+        const float sc = f16_to_f32(s16);
+#pragma unroll
+        for (int qd = 0; qd < ELEM / 4; qd++) {
+          uint32_t packed = 0;
+#pragma unroll
+          for (int bb = 0; bb < 4; bb++) {
+            const int e = 4 * qd + bb;
+            const float code = sc != 0.f ? fminf(fmaxf(rintf(x[e] / sc), -127.f), 127.f) : 0.f;
+            dec[e] = code * sc;
+            packed |= ((uint32_t)(int32_t)code & 0xffu) << (8 * bb);
+          }
+          w[qd] = packed;
+        }
+        if (lane == 0) gstore<uint16_t>((which ? a.kv.vs : a.kv.ks) + row, s16);
+      }
+      uint8_t* dst = (uint8_t*)(which ? a.kv.v : a.kv.k) + row * RB + (size_t)e0 * W::EB;
+      if (pg == 0) {
+        if constexpr (PB == 16) gstore<uint4>(dst, make_uint4(w[0], w[1], w[2], w[3]));
+        else gstore<uint64_t>(dst, (uint64_t)w[1] << 32 | w[0]);
+      }
+#pragma unroll
+      for (int e = 0; e < ELEM; e++) (which ? nv : nk)[e] = dec[e];
+    }
+  }
+
+  struct Tile {
+    PieceT k[NI], v[NI];
+    float ks[NI], vs[NI];   // int8: the rows' scales
+  };
+  // Issues block t of the chunk (past the last block: one line at the pool's start, unused).
+  auto issue = [&](int t, Tile& T) {
+    const bool real = t < nb;
+    const int blk = t < 64 ? __builtin_amdgcn_readlane(bt_lo, t & 63) : __builtin_amdgcn_readlane(bt_hi, t & 63);
+    const size_t rowbase = ((size_t)(real ? blk : 0) * Hkv + j) * 16;
+    const uint8_t* kb = (const uint8_t*)a.kv.k + (real ? rowbase * RB + lane * PB : 0);
+    const uint8_t* vb = (const uint8_t*)a.kv.v + (real ? rowbase * RB + lane * PB : 0);
+#pragma unroll
+    for (int i = 0; i < NI; i++) {
+      T.k[i] = gload<PieceT>(kb + (real ? i * W::LOADB : 0));
+      T.v[i] = gload<PieceT>(vb + (real ? i * W::LOADB : 0));
+    }
+    if constexpr (KVFMT == KV_I8) {
+#pragma unroll
+      for (int i = 0; i < NI; i++) {
+        const size_t r = real ? rowbase + PPI * i + pg : 0;
+        T.ks[i] = f16_to_f32(gload<uint16_t>(a.kv.ks + r));
+        T.vs[i] = f16_to_f32(gload<uint16_t>(a.kv.vs + r));
+      }
+    }
+  };
+
+  float m[G], l[G], acc[G][ELEM];
+#pragma unroll
+  for (int h = 0; h < G; h++) {
+    m[h] = -INFINITY;
+    l[h] = 0.f;
+#pragma unroll
+    for (int e = 0; e < ELEM; e++) acc[h][e] = 0.f;
+  }
+  auto consume = [&](int t, const Tile& T) {
+    const int p0 = t_begin + 16 * t;
+    float s[NI][G];
+    bool isnew[NI], valid[NI];
+#pragma unroll
+    for (int i = 0; i < NI; i++) {
+      const int p = p0 + PPI * i + pg;
+      isnew[i] = has_new && p == pos;
+      valid[i] = p < t_end;   // rows past the chunk's end (last block) are never attended
+      float kf[ELEM];
+      decode_piece<KVFMT, ELEM>(T.k[i], kf);
+#pragma unroll
+      for (int e = 0; e < ELEM; e++) kf[e] = isnew[i] ? nk[e] : kf[e];
+#pragma unroll
+      for (int h = 0; h < G; h++) {
+        float sacc = 0.f;
+#pragma unroll
+        for (int e = 0; e < ELEM; e++) sacc = fmaf(q[h][e], kf[e], sacc);
+        s[i][h] = sacc;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NI; i++) {
+#pragma unroll
+      for (int h = 0; h < G; h++) {
+        float v = grp_sum<LPP>(s[i][h]);
+        if constexpr (KVFMT == KV_I8) v *= isnew[i] ? 1.f : T.ks[i];
+        s[i][h] = valid[i] ? v : -INFINITY;   // a select: whatever a stale row holds is dropped
+      }
+    }
+    float alpha[G], p_[NI][G];
+#pragma unroll
+    for (int h = 0; h < G; h++) {
+      float mx = s[0][h];
+#pragma unroll
+      for (int i = 1; i < NI; i++) mx = fmaxf(mx, s[i][h]);
+      mx = xgrp_max<LPP>(mx);
+      const float mn = fmaxf(m[h], mx);
+      alpha[h] = expf(m[h] - mn);
+      float ps = 0.f;
+#pragma unroll
+      for (int i = 0; i < NI; i++) {
+        p_[i][h] = expf(s[i][h] - mn);
+        ps += p_[i][h];
+      }
+      ps = xgrp_sum<LPP>(ps);
+      l[h] = l[h] * alpha[h] + ps;
+      m[h] = mn;
+    }
+#pragma unroll
+    for (int h = 0; h < G; h++)
+#pragma unroll
+      for (int e = 0; e < ELEM; e++) acc[h][e] *= alpha[h];
+#pragma unroll
+    for (int i = 0; i < NI; i++) {
+      float vf[ELEM];
+      decode_piece<KVFMT, ELEM>(T.v[i], vf);
+      // a stale row past the end holds anything, and 0 times a non-finite value is not 0
+#pragma unroll
+      for (int e = 0; e < ELEM; e++) vf[e] = isnew[i] ? nv[e] : (valid[i] ? vf[e] : 0.f);
+#pragma unroll
+      for (int h = 0; h < G; h++) {
+        float pv = p_[i][h];
+        if constexpr (KVFMT == KV_I8) pv = valid[i] ? pv * (isnew[i] ? 1.f : T.vs[i]) : 0.f;   // V's row scale into p
+#pragma unroll
+        for (int e = 0; e < ELEM; e++) acc[h][e] = fmaf(pv, vf[e], acc[h][e]);
+      }
+    }
+  };
+
+  Tile TA, TB;
+  issue(0, TA);
+  issue(1, TB);
+  for (int t = 0; t < nb; t += 2) {
+    consume(t, TA);
+    issue(t + 2, TA);
+    if (t + 1 >= nb) break;
+    consume(t + 1, TB);
+    issue(t + 3, TB);
+  }
+
+  // the position groups' accumulators, then the partial in k_attn's layout
+#pragma unroll
+  for (int h = 0; h < G; h++)
+#pragma unroll
+    for (int e = 0; e < ELEM; e++) acc[h][e] = xgrp_sum<LPP>(acc[h][e]);
+  const int cs = HD + 2;
+  if (pg == 0) {
+#pragma unroll
+    for (int h = 0; h < G; h++) {
+      float* P = partials + (((size_t)b * d.Hq + (size_t)j * G + h) * a.nch + c) * cs;
+#pragma unroll
+      for (int e = 0; e < ELEM; e++) gstore<float>(P + e0 + e, acc[h][e]);   // (rows of hd + 2: no 16-B alignment)
+      if (lane == 0) {
+        P[HD] = m[h];
+        P[HD + 1] = l[h];
+      }
+    }
+  }
+}
+
 // one (head, sequence): o = merge of its chunk partials, rounded to the activation type
 __global__ __launch_bounds__(256) void k_combine(Dims d, const StepDesc* desc, const float* partials,
                                                  void* o) {
@@ -727,6 +1068,23 @@ hipError_t launch_attention(const Dims& d, const StepDesc* desc, int B, const fl
   a.bt = block_table;
   a.ct = d.ct;
   a.nch = d.nch;
+  if (d.bs == 16) {
+    const dim3 gw((d.nch + 3) / 4, d.Hkv, B);
+#define DTD_ATTN_W(KV, HDv, Gv)                                                                   \
+  if (d.kvfmt == KV && d.hd == HDv && d.G == Gv) {                                                \
+    hipLaunchKernelGGL((k_attn_w<KV, HDv, Gv>), gw, dim3(256), 0, st, a, desc, partials);         \
+    return hipGetLastError();                                                                     \
+  }
+    DTD_ATTN_W(KV_BF16, 128, 4)
+    DTD_ATTN_W(KV_I8, 128, 4)
+    DTD_ATTN_W(KV_F32, 128, 4)
+    DTD_ATTN_W(KV_BF16, 64, 4)
+    DTD_ATTN_W(KV_I8, 64, 4)
+    DTD_ATTN_W(KV_F32, 64, 4)
+    DTD_ATTN_W(KV_BF16, 32, 5)
+    DTD_ATTN_W(KV_F32, 32, 5)
+#undef DTD_ATTN_W
+  }
   const dim3 grid(d.nch, d.Hkv, B);
   const size_t smem = sizeof(float) * attn_smem_floats(d.G, d.hd);
   if (d.kvfmt == KV_F32) hipLaunchKernelGGL(k_attn<KV_F32>, grid, dim3(256), smem, st, a, desc, partials);

@@ -120,14 +120,22 @@ int32_t dtd_expected_tensors(const dtd_config* cfg, dtd_tensor_spec* out, int32_
 
 /* ---- lifecycle ---------------------------------------------------------------------- */
 
-/* Creates an engine on the current HIP device.  hip_stream is a hipStream_t (NULL = the
- * null stream); all work is enqueued on it.  Allocates the KV pool and work buffers. */
+/* Creates an engine on the current HIP device: the KV block pool (fixed-size blocks shared
+ * by all sequences, handed out from a free list: the paged KV cache of the Qwen3-8B engine
+ * article, 4.3.1), per-sequence block tables, the RoPE tables and work buffers.  hip_stream
+ * is a hipStream_t (NULL = the null stream); all work is enqueued on it.  The engine keeps
+ * its own copy of *cfg.  Errors: DTD_E_ARG / DTD_E_UNSUPPORTED for a configuration
+ * dtd_validate_config rejects, DTD_E_OOM when device memory runs out, DTD_E_HIP for another
+ * HIP failure; *out is then NULL and dtd_last_error(NULL) has the reason. */
 dtd_status dtd_create(const dtd_config* cfg, void* hip_stream, dtd_engine** out);
 
 /* Copies every weight part into engine-owned device memory (repacked for the kernels).
- * All parts must be given in one call; fail-closed: a missing, unknown, duplicate or
- * wrongly sized part is rejected before anything is copied.  Synchronous: the caller may
- * free its buffers when it returns. */
+ * All parts must be given in one call.  Loading fails closed, like the hardened model
+ * loader of the nxmr.cn C17 engine article (4.1): a missing, unknown, duplicate or wrongly
+ * sized part is rejected (DTD_E_ARG) before anything is copied, and the engine then holds
+ * no weights (later steps fail with DTD_E_STATE).  t[i].data is host memory or, with
+ * on_device = 1, device memory; nbytes is the part's exact size (dtd_expected_tensors).
+ * Synchronous: the caller may free its buffers when it returns. */
 dtd_status dtd_load_weights(dtd_engine* e, const dtd_tensor* t, int32_t n);
 
 /* Appends n tokens (device int32 [n], each in [0, V)) to sequence seq_id, creating the
@@ -161,15 +169,22 @@ dtd_status dtd_decode_step_noalloc(dtd_engine* e, int32_t batch, const int64_t* 
                                    const int32_t* tokens_dev, int32_t* next_tokens_dev,
                                    float* logits_dev);
 
-/* Forgets a sequence: its KV blocks and slot return to the free lists.  Host only. */
+/* Forgets a sequence, as the Qwen3-8B engine article's ResetSeq call does (4.1.2): its KV
+ * blocks and its slot return to the free lists, and the seq_id may be used again for a new
+ * sequence.  Host only (nothing is enqueued; the blocks' contents are not cleared).
+ * DTD_E_NOSEQ for an unknown seq_id. */
 dtd_status dtd_reset_seq(dtd_engine* e, int64_t seq_id);
 
 /* Current length (positions written) of a sequence, or a dtd_status < 0. */
 int32_t dtd_seq_len(const dtd_engine* e, int64_t seq_id);
 
-/* Reports a token id outside [0, V) seen on the device by an earlier prefill or decode
- * step (such tokens are read as id 0).  Synchronises the stream.  DTD_E_ARG if one was
- * seen since the last check, else DTD_OK. */
+/* Reports what the device flagged since the last check, and synchronises the stream:
+ *   - DTD_E_ARG: an earlier prefill or decode step read a token id outside [0, V) (it used
+ *     id 0 instead); the flag is cleared, the engine stays usable;
+ *   - DTD_E_HIP: a wait of the batch-1 step kernel for another workgroup timed out (every
+ *     workgroup then gave up, so the outputs of that step and of any later one are not
+ *     valid); the engine is unusable from then on, destroy it;
+ *   - DTD_OK otherwise. */
 dtd_status dtd_check_device_errors(dtd_engine* e);
 
 void        dtd_destroy(dtd_engine* e);
