@@ -9,6 +9,7 @@
 // (RMSNorm scaling, RoPE, KV append, SwiGLU, residual adds, argmax) rides in the
 // prologues and epilogues of those kernels.
 #include <algorithm>
+#include <type_traits>
 #include <math.h>
 #include <stdint.h>
 #include <limits.h>
@@ -600,10 +601,12 @@ __global__ __launch_bounds__(256) void k_attn_w(AttnCtx a, const StepDesc* desc,
   const int pg = lane / LPP, e0 = (lane % LPP) * ELEM;
   const int Hkv = d.Hkv;
 
-  // the group's queries at this lane's elements, scaled by 1/sqrt(hd)
+  // the group's queries at this lane's elements, scaled by log2(e)/sqrt(hd): scores are kept
+  // in base-2 units, so that every exponential is one v_exp_f32 (2^x); the partial's running
+  // max goes out in natural units
   float q[G][ELEM];
   {
-    const float sc = 1.0f / sqrtf((float)HD);
+    const float sc = 1.4426950408889634f / sqrtf((float)HD);
     const float* qb = a.q + (size_t)b * d.q_dim + (size_t)j * G * HD + e0;
 #pragma unroll
     for (int h = 0; h < G; h++)
@@ -718,15 +721,18 @@ __global__ __launch_bounds__(256) void k_attn_w(AttnCtx a, const StepDesc* desc,
 #pragma unroll
     for (int e = 0; e < ELEM; e++) acc[h][e] = 0.f;
   }
-  auto consume = [&](int t, const Tile& T) {
+  // EDGE: the chunk's last block, the only one that can end inside the block or hold the new
+  // position (the selects for those cases are left out of every other block)
+  auto consume = [&](int t, const Tile& T, auto edge) {
+    constexpr bool EDGE = decltype(edge)::value;
     const int p0 = t_begin + 16 * t;
     float s[NI][G];
     bool isnew[NI], valid[NI];
 #pragma unroll
     for (int i = 0; i < NI; i++) {
       const int p = p0 + PPI * i + pg;
-      isnew[i] = has_new && p == pos;
-      valid[i] = p < t_end;   // rows past the chunk's end (last block) are never attended
+      isnew[i] = EDGE && has_new && p == pos;
+      valid[i] = !EDGE || p < t_end;   // rows past the chunk's end (last block) are never attended
       float kf[ELEM];
       decode_piece<KVFMT, ELEM>(T.k[i], kf);
 #pragma unroll
@@ -756,11 +762,11 @@ __global__ __launch_bounds__(256) void k_attn_w(AttnCtx a, const StepDesc* desc,
       for (int i = 1; i < NI; i++) mx = fmaxf(mx, s[i][h]);
       mx = xgrp_max<LPP>(mx);
       const float mn = fmaxf(m[h], mx);
-      alpha[h] = expf(m[h] - mn);
+      alpha[h] = __builtin_amdgcn_exp2f(m[h] - mn);   // 2^(-inf) = 0 on the first block
       float ps = 0.f;
 #pragma unroll
       for (int i = 0; i < NI; i++) {
-        p_[i][h] = expf(s[i][h] - mn);
+        p_[i][h] = __builtin_amdgcn_exp2f(s[i][h] - mn);
         ps += p_[i][h];
       }
       ps = xgrp_sum<LPP>(ps);
@@ -791,11 +797,15 @@ __global__ __launch_bounds__(256) void k_attn_w(AttnCtx a, const StepDesc* desc,
   Tile TA, TB;
   issue(0, TA);
   issue(1, TB);
+  using Mid = std::integral_constant<bool, false>;
+  using Last = std::integral_constant<bool, true>;
   for (int t = 0; t < nb; t += 2) {
-    consume(t, TA);
+    if (t == nb - 1) consume(t, TA, Last{});
+    else consume(t, TA, Mid{});
     issue(t + 2, TA);
     if (t + 1 >= nb) break;
-    consume(t + 1, TB);
+    if (t + 1 == nb - 1) consume(t + 1, TB, Last{});
+    else consume(t + 1, TB, Mid{});
     issue(t + 3, TB);
   }
 
@@ -812,7 +822,7 @@ __global__ __launch_bounds__(256) void k_attn_w(AttnCtx a, const StepDesc* desc,
 #pragma unroll
       for (int e = 0; e < ELEM; e++) gstore<float>(P + e0 + e, acc[h][e]);   // (rows of hd + 2: no 16-B alignment)
       if (lane == 0) {
-        P[HD] = m[h];
+        P[HD] = m[h] * 0.6931471805599453f;   // base-2 running max back to natural units
         P[HD + 1] = l[h];
       }
     }
@@ -980,6 +990,8 @@ bool gemm_eligible(const Dims& d, int B) {
   return B >= 2 && B <= kMaxBatch && d.act == ACT_BF16 && (d.wfmt == W_INT8_ROW || d.wfmt == W_BF16);
 }
 
+// K splits: about one workgroup per compute unit.  (Two per compute unit, which keeps more
+// weights in flight, measured slower: the larger partial sums cost more than they gained.)
 int gemm_splits(int N, int K, int cus) {
   const int tiles = (N + kGemmRows - 1) / kGemmRows;
   const int nchunk = (K + kGemmKC - 1) / kGemmKC;
