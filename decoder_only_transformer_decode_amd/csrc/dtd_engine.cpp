@@ -74,6 +74,8 @@ struct dtd_engine {
   float* vnew = nullptr;
   float* partials = nullptr;
   float* gemm_partials = nullptr;   // split-K sums of the batched matrix-core projections
+  int32_t* tok_scratch = nullptr;   // greedy tokens of a prefill chunk [mb]
+  int mb = 0;                       // rows of the work buffers (max batch or prefill chunk)
   int cus = 0;                      // compute units of the device
   void* o = nullptr;
   void* h = nullptr;
@@ -313,7 +315,7 @@ static void free_all(dtd_engine* e) {
   release_weights(e);
   void* ps[] = {e->rope_cos, e->rope_sin, e->kpool, e->vpool, e->kspool, e->vspool, e->bt_dev,
                 e->x, e->xn, e->q, e->knew, e->vnew, e->partials, e->gemm_partials, e->o, e->h, e->logits,
-                e->err_dev, e->desc_dev, e->rows_dev, e->players, e->tags};
+                e->err_dev, e->desc_dev, e->rows_dev, e->players, e->tags, e->tok_scratch};
   for (void* p : ps)
     if (p) (void)hipFree(p);
   if (e->desc_host) (void)hipHostFree(e->desc_host);
@@ -388,7 +390,9 @@ extern "C" dtd_status dtd_create(const dtd_config* cfg, void* hip_stream, dtd_en
   if ((st = dev_alloc(e, &e->bt_dev, bt_bytes))) return cleanup(st);
   if (hipMemset(e->bt_dev, 0, bt_bytes) != hipSuccess) return cleanup(DTD_E_HIP);
 
-  const int MB = cfg->max_batch;
+  // work buffers hold a decode batch or a prefill chunk, whichever is larger
+  const int MB = std::max(cfg->max_batch, kPrefillChunk);
+  e->mb = MB;
   const size_t ab = act_bytes(cfg->act);
   if ((st = dev_alloc(e, &e->x, (size_t)MB * d.D * 4)) ||
       (st = dev_alloc(e, &e->xn, (size_t)MB * d.D * ab)) ||
@@ -400,7 +404,8 @@ extern "C" dtd_status dtd_create(const dtd_config* cfg, void* hip_stream, dtd_en
       (st = dev_alloc(e, &e->o, (size_t)MB * d.q_dim * ab)) ||
       (st = dev_alloc(e, &e->h, (size_t)MB * d.F * ab)) ||
       (st = dev_alloc(e, &e->logits, (size_t)MB * d.V * 4)) ||
-      (st = dev_alloc(e, &e->err_dev, 16)) || (st = dev_alloc(e, &e->desc_dev, sizeof(StepDesc))))
+      (st = dev_alloc(e, &e->err_dev, 16)) || (st = dev_alloc(e, &e->desc_dev, sizeof(StepDesc))) ||
+      (st = dev_alloc(e, &e->tok_scratch, (size_t)MB * 4)))
     return cleanup(st);
   if (hipMemset(e->err_dev, 0, 16) != hipSuccess) return cleanup(DTD_E_HIP);
 
@@ -687,7 +692,7 @@ static ProbeLayout probe_layout(const Dims& d, int B, size_t ab) {
 // inject record and its output is copied to the capture record, so each kernel can be
 // compared with the reference operation on identical inputs.
 static dtd_status run_sub_steps(dtd_engine* e, int B, bool do_head, const uint8_t* inject, uint8_t* capture,
-                                float* partials, float* gemm_partials);
+                                float* partials, float* gemm_partials, bool append_first);
 
 // partials: the split-K attention partials of the per-sub-step schedule (the engine's buffer,
 // or the allocation-free entry point's static scratch).  force_per_kernel: run that schedule
@@ -696,7 +701,7 @@ static dtd_status run_step(dtd_engine* e, int B, const int* slots, const int* po
                            const int32_t* tokens, int32_t* next, float* logits_out, bool do_head,
                            const Update* upd, int n_upd, const uint8_t* inject = nullptr,
                            uint8_t* capture = nullptr, float* partials = nullptr, float* gemm_partials = nullptr,
-                           bool force_per_kernel = false, bool no_timing = false) {
+                           bool force_per_kernel = false, bool no_timing = false, bool append_first = false) {
   if (!partials) partials = e->partials;
   if (!gemm_partials) gemm_partials = e->gemm_partials;
   const Dims& d = e->d;
@@ -770,14 +775,14 @@ static dtd_status run_step(dtd_engine* e, int B, const int* slots, const int* po
     return fail(e, DTD_E_UNSUPPORTED, "persistent step kernel unavailable for this call");
   const int timing_saved = e->timing_kind;
   if (no_timing) e->timing_kind = -1;
-  const dtd_status rs = run_sub_steps(e, B, do_head, inject, capture, partials, gemm_partials);
+  const dtd_status rs = run_sub_steps(e, B, do_head, inject, capture, partials, gemm_partials, append_first);
   e->timing_kind = timing_saved;
   return rs;
 }
 
 // The per-sub-step schedule of one step (the descriptor is already on the device).
 static dtd_status run_sub_steps(dtd_engine* e, int B, bool do_head, const uint8_t* inject, uint8_t* capture,
-                                float* partials, float* gemm_partials) {
+                                float* partials, float* gemm_partials, bool append_first) {
   const Dims& d = e->d;
   hipStream_t st = e->stream;
   // a projection: on the matrix cores when the batch makes it a real GEMM, else the
@@ -831,6 +836,7 @@ static dtd_status run_sub_steps(dtd_engine* e, int B, bool do_head, const uint8_
       HIP_OK(e, cp(e->knew, in + pl.k, fkv));
       HIP_OK(e, cp(e->vnew, in + pl.v, fkv));
     }
+    if (append_first) HIP_OK(e, launch_kv_append(d, e->desc_dev, B, e->knew, e->vnew, kv, st));
     TIMED(4, launch_attention(d, e->desc_dev, B, e->q, e->knew, e->vnew, kv, e->bt_dev, partials, st));
     HIP_OK(e, launch_combine(d, e->desc_dev, B, partials, e->o, st));
     if (probe) {
@@ -901,6 +907,44 @@ extern "C" dtd_status dtd_prefill(dtd_engine* e, int64_t seq_id, const int32_t* 
     it = e->seqs.emplace(seq_id, s).first;
   }
   Seq& s = it->second;
+  // Batched prefill: the prompt in chunks of up to kPrefillChunk positions, each chunk one
+  // step of the per-sub-step schedule with the chunk's positions as its batch (projections on
+  // the matrix cores where the formats allow); every position's K/V is appended before the
+  // chunk's attention, so that each position attends to the ones before it.  With the
+  // persistent-only schedule selected, or hidden-state capture on (its buffer holds one
+  // step's batch), positions go one per step.
+  if (n >= 2 && e->path != 2 && !e->capture) {
+    for (int c0 = 0; c0 < n; c0 += kPrefillChunk) {
+      const int B = std::min(kPrefillChunk, n - c0);
+      const bool last = c0 + B == n;
+      int slots[kPrefillChunk], poss[kPrefillChunk], pblks[kPrefillChunk];
+      Update upd[kPrefillChunk];
+      int n_upd = 0;
+      for (int b = 0; b < B; b++) {
+        const int pos = s.len + b;
+        if (pos / e->d.bs >= (int)s.blocks.size()) {
+          const int32_t blk = e->free_blocks.back();
+          e->free_blocks.pop_back();
+          s.blocks.push_back(blk);
+          upd[n_upd++] = {s.slot, (int)s.blocks.size() - 1, blk};
+        }
+        slots[b] = s.slot;
+        poss[b] = pos;
+        pblks[b] = s.blocks[(size_t)(pos / e->d.bs)];
+      }
+      st = run_step(e, B, slots, poss, pblks, tokens_dev + c0, e->tok_scratch, nullptr, last, upd, n_upd,
+                    nullptr, nullptr, nullptr, nullptr, true, false, true);
+      if (st) return st;
+      s.len += B;
+      if (last) {
+        HIP_OK(e, hipMemcpyAsync(next_token_dev, e->tok_scratch + (B - 1), 4, hipMemcpyDeviceToDevice, e->stream));
+        if (logits_dev)
+          HIP_OK(e, hipMemcpyAsync(logits_dev, e->logits + (size_t)(B - 1) * e->d.V, (size_t)e->d.V * 4,
+                                   hipMemcpyDeviceToDevice, e->stream));
+      }
+    }
+    return DTD_OK;
+  }
   for (int i = 0; i < n; i++) {
     const int pos = s.len;
     Update upd[1];

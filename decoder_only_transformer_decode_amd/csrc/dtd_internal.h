@@ -9,6 +9,7 @@ namespace dtd {
 
 constexpr int kMaxBatch = 64;
 constexpr int kMaxUpdates = 64;
+constexpr int kPrefillChunk = 64;   // prompt positions per batched prefill step
 constexpr int kAttnTile = 64;      // positions per LDS tile in decode attention (one per lane)
 constexpr int kPersistWaves = 8;   // waves per workgroup of the persistent step kernel
 constexpr int kErrToken = 1;       // device error bits: token id out of range
@@ -136,6 +137,29 @@ inline size_t h_buffer_words(int F, int nwg) {
   return packed > (size_t)F ? packed : (size_t)F;
 }
 
+// Sampler settings of one row (dtd_sample.hip): temperature 0 = greedy; top_k 0, top_p 1
+// and min_p 0 turn those filters off.  counter picks the draw (the position whose logits
+// the row holds).
+struct SampleRow {
+  float temperature;
+  int32_t top_k;
+  float top_p;
+  float min_p;
+  uint64_t seed;
+  int64_t counter;
+};
+
+// Arguments of the sampling kernel, passed by value: rows b < B of logits (row stride
+// `stride` floats, V columns) -> out[b].
+struct SampleArgs {
+  const float* logits;
+  int64_t stride;
+  int32_t V;
+  int32_t B;
+  int32_t* out;
+  SampleRow row[kMaxBatch];
+};
+
 // ---- launchers (dtd_kernels.hip, dtd_persistent.hip) ----
 size_t persistent_smem_bytes(const Dims& d, int nch, int nwg);
 size_t persistent_xs_floats(const Dims& d, int nch);
@@ -159,12 +183,15 @@ hipError_t launch_gemm(const Dims& d, const MatDev& m, const void* xin, int B, i
 hipError_t launch_attention(const Dims& d, const StepDesc* desc, int B, const float* q,
                             const float* knew, const float* vnew, const KvLayer& kv,
                             const int32_t* block_table, float* partials, hipStream_t st);
+hipError_t launch_kv_append(const Dims& d, const StepDesc* desc, int B, const float* knew, const float* vnew,
+                            const KvLayer& kv, hipStream_t st);
 hipError_t launch_combine(const Dims& d, const StepDesc* desc, int B, const float* partials,
                           void* o, hipStream_t st);
 hipError_t launch_argmax(const Dims& d, const StepDesc* desc, int B, const float* logits,
                          hipStream_t st);
 hipError_t launch_dequant_rows(const Dims& d, const MatDev& m, const int32_t* rows, int nrows,
                                float* out, hipStream_t st);
+hipError_t launch_sample(const SampleArgs& a, hipStream_t st);
 hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, int cus, hipStream_t st);
 hipError_t launch_kv_fill(const Dims& d, const KvLayer& kv, const int32_t* blocks, int nblk_used,
                           int len, int layer, uint64_t seed, hipStream_t st);

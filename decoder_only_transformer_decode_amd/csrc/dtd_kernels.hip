@@ -829,6 +829,22 @@ __global__ __launch_bounds__(256) void k_attn_w(AttnCtx a, const StepDesc* desc,
   }
 }
 
+// KV append of every new position of a step, before its attention: one workgroup per
+// (position b, KV head j).  A prefill chunk puts several positions of one sequence in one
+// step, and each attends to the ones before it, which must then be in the cache already.
+// The attention kernels append their own new position again, with identical bytes.
+template <int KVFMT>
+__global__ __launch_bounds__(128) void k_kv_append(Dims d, KvLayer kv, const StepDesc* desc, const float* knew,
+                                                   const float* vnew) {
+  __shared__ float new_s[256];
+  __shared__ float red[4];
+  const int b = blockIdx.x, j = blockIdx.y;
+  const int pos = desc->pos[b];
+  const size_t row = ((size_t)desc->pos_block[b] * d.Hkv + j) * d.bs + (pos % d.bs);
+  kv_append<KVFMT>(kv, row, d.hd, knew + (size_t)b * d.kv_dim + (size_t)j * d.hd,
+                   vnew + (size_t)b * d.kv_dim + (size_t)j * d.hd, new_s, red);
+}
+
 // one (head, sequence): o = merge of its chunk partials, rounded to the activation type
 __global__ __launch_bounds__(256) void k_combine(Dims d, const StepDesc* desc, const float* partials,
                                                  void* o) {
@@ -1102,6 +1118,15 @@ hipError_t launch_attention(const Dims& d, const StepDesc* desc, int B, const fl
   if (d.kvfmt == KV_F32) hipLaunchKernelGGL(k_attn<KV_F32>, grid, dim3(256), smem, st, a, desc, partials);
   else if (d.kvfmt == KV_BF16) hipLaunchKernelGGL(k_attn<KV_BF16>, grid, dim3(256), smem, st, a, desc, partials);
   else hipLaunchKernelGGL(k_attn<KV_I8>, grid, dim3(256), smem, st, a, desc, partials);
+  return hipGetLastError();
+}
+
+hipError_t launch_kv_append(const Dims& d, const StepDesc* desc, int B, const float* knew, const float* vnew,
+                            const KvLayer& kv, hipStream_t st) {
+  const dim3 grid(B, d.Hkv);
+  if (d.kvfmt == KV_F32) hipLaunchKernelGGL(k_kv_append<KV_F32>, grid, dim3(128), 0, st, d, kv, desc, knew, vnew);
+  else if (d.kvfmt == KV_BF16) hipLaunchKernelGGL(k_kv_append<KV_BF16>, grid, dim3(128), 0, st, d, kv, desc, knew, vnew);
+  else hipLaunchKernelGGL(k_kv_append<KV_I8>, grid, dim3(128), 0, st, d, kv, desc, knew, vnew);
   return hipGetLastError();
 }
 

@@ -139,9 +139,16 @@ dtd_status dtd_create(const dtd_config* cfg, void* hip_stream, dtd_engine** out)
 dtd_status dtd_load_weights(dtd_engine* e, const dtd_tensor* t, int32_t n);
 
 /* Appends n tokens (device int32 [n], each in [0, V)) to sequence seq_id, creating the
- * sequence if it is new, by running them through the decode step one position after
- * the other.  Writes the greedy next token after the last one to next_token_dev
- * (int32 [1]) and, if logits_dev is not NULL, its fp32 logits [V]. */
+ * sequence if it is new, and writes the greedy next token after the last one to
+ * next_token_dev (int32 [1]) and, if logits_dev is not NULL, its fp32 logits [V].  The
+ * result is that of running the tokens through the decode step one position after the
+ * other (smollm3.go's Prefill(tokens, startPos); the C17 engine article, 4.3).  It runs as
+ * batched steps over chunks of up to 64 positions: the projections of a chunk as one GEMM
+ * (matrix cores with bf16 activations and int8-row or bf16 weights), every position's K/V
+ * appended to the cache before the chunk's attention, each position attending causally to
+ * [0, its position] (the Qwen3-8B engine article's batched prefill, 4.4.1).  One position
+ * per step instead when n = 1, when hidden-state capture is on, or with the persistent-
+ * only schedule (dtd_debug_set_path 2). */
 dtd_status dtd_prefill(dtd_engine* e, int64_t seq_id, const int32_t* tokens_dev, int32_t n,
                        int32_t* next_token_dev, float* logits_dev);
 

@@ -259,3 +259,61 @@ def stored_kv_reference(shape, x32):
     for idx in np.ndindex(*x.shape[:-1]):
         q[idx], sc[idx] = oracle.kv_quant_i8(x[idx])
     return q, sc
+
+
+def kv_encoding_step(shape, ref, ref_scales):
+    """One step of the stored KV encoding at each of the oracle's decoded values `ref`
+    (fp32 or bf16: one unit in the last place; int8: one code at the row's fp16 scale, plus
+    the scale itself landing one fp16 step the other way)."""
+    mag = np.abs(np.asarray(ref, np.float64))
+    if shape.kvfmt == synth.KV_F32:
+        return np.ldexp(1.0, np.frexp(np.maximum(mag, 1e-30))[1] - 24)
+    if shape.kvfmt == synth.KV_BF16:
+        return np.ldexp(1.0, np.frexp(np.maximum(mag, 1e-30))[1] - 8)
+    return ref_scales.view(np.float16).astype(np.float64)[..., None] + mag * 2.0 ** -10
+
+
+def kv_excess(g, ref, step):
+    """(largest |g - ref| beyond one encoding step, relative to max |ref|; the fraction of
+    elements more than half a step apart)"""
+    ref = np.asarray(ref, np.float64)
+    diff = np.abs(np.asarray(g, np.float64) - ref)
+    den = np.abs(ref).max()
+    den = den if den > 0 else 1.0
+    return float(np.maximum(diff - step, 0.0).max() / den), float(np.mean(diff > 0.5 * step))
+
+
+def stored_kv_error(P, seq_id, layer, start, n, other=None):
+    """The GPU's stored K/V of positions [start, start + n) against the oracle's.
+
+    Each side rounds its own fp32 k/v to the KV encoding, and the two unrounded values differ
+    by accumulation-order error, so a stored element may sit one encoding step away from the
+    oracle's (a rounding boundary fell between them).  Returns (excess, flipped): the largest
+    difference beyond that one step, relative to max |oracle|, and the fraction of elements
+    that differ by more than half a step.  With `other` (a second oracle model that ran the
+    same tokens in slot 0) also returns that model's excess over the oracle, measured the
+    same way.
+    """
+    s = P.shape
+    k0, v0, ks0, vs0 = P.orc.kv_read_raw(P.oslot(seq_id), layer, start, n)
+    ko, vo = np.empty_like(k0), np.empty_like(v0)
+    kso = vso = None
+    if ks0 is not None:
+        kso, vso = np.empty_like(ks0), np.empty_like(vs0)
+    dtd.dtd_debug_kv_read(P.eng.h, seq_id, layer, start, n, ko, vo, kso, vso)
+    kd, vd = P.orc.kv_read(P.oslot(seq_id), layer, start, n)
+    o2 = other.kv_read(0, layer, start, n) if other is not None else (None, None)
+    worst, flip, env = 0.0, 0.0, 0.0
+    for raw, sc, ref, osc, alt in ((ko, kso, kd, ks0, o2[0]), (vo, vso, vd, vs0, o2[1])):
+        if s.kvfmt == synth.KV_F32:
+            g = raw.astype(np.float64)
+        elif s.kvfmt == synth.KV_BF16:
+            g = synth.bf16_bits_to_f32(raw).astype(np.float64)
+        else:
+            g = raw.astype(np.float64) * sc.view(np.float16).astype(np.float64)[..., None]
+        step = kv_encoding_step(s, ref, osc)
+        e, f = kv_excess(g, ref, step)
+        worst, flip = max(worst, e), max(flip, f)
+        if alt is not None:
+            env = max(env, kv_excess(alt, ref, step)[0])
+    return (worst, flip, env) if other is not None else (worst, flip)

@@ -10,7 +10,8 @@ import numpy as np
 import pytest
 
 from decoder_only_transformer_decode_amd import dtd, synth
-from _pair import ENV_FACTOR, TOL, Pair, need_gpu, normwise, probe_step, stored_kv_reference, top2_margin
+from _pair import (ENV_FACTOR, TOL, Pair, need_gpu, normwise, probe_step, stored_kv_error, stored_kv_reference,
+                   top2_margin)
 
 pytestmark = pytest.mark.gpu
 
@@ -419,21 +420,8 @@ def test_long_context_from_identical_stored_kv(kw, n_pos):
     tr.check(f"long context {n_pos}")
     # the KV the GPU appended (teacher-forced copy) matches the oracle's stored KV
     for layer in range(s.n_layers):
-        kr, vr, ksr, vsr = P.orc.kv_read_raw(0, layer, n_pos, 3)
-        ko, vo = np.empty_like(kr), np.empty_like(vr)
-        kso = vso = None
-        if ksr is not None:
-            kso, vso = np.empty_like(ksr), np.empty_like(vsr)
-        dtd.dtd_debug_kv_read(P.eng.h, 0, layer, n_pos, 3, ko, vo, kso, vso)
-        kd, vd = P.orc.kv_read(0, layer, n_pos, 3)
-        if s.kvfmt == synth.KV_F32:
-            gk, gv = ko.astype(np.float64), vo.astype(np.float64)
-        elif s.kvfmt == synth.KV_BF16:
-            gk, gv = synth.bf16_bits_to_f32(ko).astype(np.float64), synth.bf16_bits_to_f32(vo).astype(np.float64)
-        else:
-            gk = ko.astype(np.float64) * kso.view(np.float16).astype(np.float64)[..., None]
-            gv = vo.astype(np.float64) * vso.view(np.float16).astype(np.float64)[..., None]
-        assert normwise(gk, kd) <= TOL and normwise(gv, vd) <= TOL
+        excess, flipped = stored_kv_error(P, 0, layer, n_pos, 3)
+        assert excess <= TOL, f"layer {layer} stored KV beyond one encoding step: {excess:.3e}"
     P.close()
 
 
@@ -442,17 +430,68 @@ def test_long_context_from_identical_stored_kv(kw, n_pos):
 # ---------------------------------------------------------------------------------------
 
 def test_prefill_equals_sequential_steps_and_is_deterministic():
+    # batched prefill (chunks of positions as one step) against the same tokens stepped one
+    # at a time: the same method, different kernels, so equal within the tolerance; and
+    # repeatable bit for bit
     s = _GRID.replace(act=synth.ACT_BF16, kvfmt=synth.KV_BF16)
-    P = Pair(s, max_ctx=64, max_seqs=3, seed=4)
-    prompt = synth.prompt_tokens(s.vocab, 20, seed=9)
-    _, lp = P.gpu_prefill(1, prompt)
+    P = Pair(s, max_ctx=160, max_seqs=3, seed=4)
+    prompt = synth.prompt_tokens(s.vocab, 90, seed=9)
+    gp, lp = P.gpu_prefill(1, prompt)
     P.gpu_prefill(2, prompt[:1])
     for t in prompt[1:]:
-        _, ls, _ = P.gpu_step([2], [t])
-    assert np.array_equal(lp, ls[0])
+        ns, ls, _ = P.gpu_step([2], [t])
+    err = normwise(lp, ls[0])
+    _say(f"batched prefill vs sequential steps: logits err {err:.2e}")
+    assert err <= TOL
+    delta = float(np.abs(lp.astype(np.float64) - ls[0]).max())
+    if top2_margin(ls[0]) > 2 * delta:
+        assert gp == int(ns[0])
     P.eng.reset_seq(1)
     _, lp2 = P.gpu_prefill(1, prompt)
     assert np.array_equal(lp, lp2)
+    P.close()
+
+
+@pytest.mark.parametrize("kw", [dict(act=synth.ACT_BF16, kvfmt=synth.KV_BF16),
+                                dict(act=synth.ACT_BF16, kvfmt=synth.KV_I8),
+                                dict(wfmt=synth.W_BF16, act=synth.ACT_BF16, kvfmt=synth.KV_BF16),
+                                dict(n_q_heads=8, n_kv_heads=2, head_dim=128, act=synth.ACT_BF16, kvfmt=synth.KV_BF16),
+                                dict(wfmt=synth.W_Q8_0, kvfmt=synth.KV_F32)],
+                         ids=["int8row-bf16kv", "int8kv", "bf16w", "hd128", "q8_0-f32"])
+def test_batched_prefill_matches_oracle(kw):
+    """A 100-token prompt prefilled as chunks of 64 and 36 positions (NEXT-1): logits of the
+    last position and every stored K/V against the oracle's position-by-position run, then
+    free-running decode steps."""
+    s = _GRID.replace(**kw)
+    P = Pair(s, max_ctx=128, max_seqs=2, seed=17)
+    O2 = P.perturbed_oracle(6, max_ctx=128)
+    prompt = synth.prompt_tokens(s.vocab, 100, seed=12)
+    tr = Tracker()
+    g_tok, g_log = P.gpu_prefill(0, prompt)
+    o_tok, o_log = P.orc_prefill(0, prompt)
+    for i, t in enumerate(prompt):
+        o2 = O2.step(0, int(t), i)
+    tr.add(g_log, o_log, o2[1])
+    # every stored position: each side rounded its own k/v to the KV encoding, so an
+    # element may sit one encoding step from the oracle's where a rounding boundary fell
+    # between the two unrounded values.  Beyond that step, layer 0 is within the tolerance;
+    # deeper layers carry the rounding of the activations before them, so they are held to
+    # the free-running bound, from the perturbed oracle's KV measured the same way
+    for layer in range(s.n_layers):
+        excess, flipped, env = stored_kv_error(P, 0, layer, 0, 100, other=O2)
+        bound = TOL if layer == 0 else max(TOL, ENV_FACTOR * env)
+        _say(f"layer {layer} stored KV: excess {excess:.2e} (bound {bound:.2e}, oracle sensitivity {env:.2e}), "
+             f"elements one step apart {flipped:.2%}")
+        assert excess <= bound, f"layer {layer} stored KV beyond one encoding step: {excess:.3e} > {bound:.3e}"
+    toks_g, toks_o = [g_tok], [o_tok]
+    for step in range(4):
+        ng, lg, _ = P.gpu_step([0], [toks_g[-1]])
+        no, lo, _ = P.orc_step(0, toks_o[-1], 100 + step)
+        tr.add(lg[0], lo, O2.step(0, toks_o[-1], 100 + step)[1])
+        toks_g.append(int(ng[0]))
+        toks_o.append(no)
+    _say(f"batched prefill {kw}: tokens {toks_g} / oracle {toks_o}")
+    tr.check("batched prefill " + s.name)
     P.close()
 
 
