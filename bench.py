@@ -88,6 +88,35 @@ def recorded_traffic(workload: str, attended: str):
     return (r["fetch_kib_per_launch"] * r["fetch_scale"] + r["write_kib_per_launch"] * r["write_scale"]) * 1024.0
 
 
+def sampler_timing(vocab: int, batch: int, step_ms: float) -> dict:
+    """Average duration of one k_sample launch (dtd_sample) over `batch` rows of the
+    workload's vocabulary, HIP events on the launch stream: temperature only, and every
+    filter on.  The logits are Gaussian with spread 3 (synth.bench_logits)."""
+    import torch
+    st = torch.cuda.current_stream()
+    logits = torch.from_numpy(synth.bench_logits(batch, vocab, seed=3)).cuda()
+    out = torch.zeros(batch, dtype=torch.int32, device="cuda")
+    res = {"kernel": "k_sample (one workgroup per row)", "vocab": vocab, "batch": batch}
+    for name, kw in (("temperature_only", dict(temperature=0.8)),
+                     ("all_filters", dict(temperature=0.8, top_k=40, top_p=0.95, min_p=0.05))):
+        samp = [dtd.sampler(seed=b, **kw) for b in range(batch)]
+        ctr = list(range(batch))
+        for _ in range(3):
+            dtd.dtd_sample(logits.data_ptr(), vocab, batch, vocab, samp, ctr, out.data_ptr(), st.cuda_stream)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        n = 20
+        a.record(st)
+        for _ in range(n):
+            dtd.dtd_sample(logits.data_ptr(), vocab, batch, vocab, samp, ctr, out.data_ptr(), st.cuda_stream)
+        b.record(st)
+        b.synchronize()
+        us = a.elapsed_time(b) / n * 1e3
+        res[f"{name}_us"] = round(us, 1)
+        res[f"{name}_share_of_step"] = round(us / (step_ms * 1e3), 4)
+    res["all_filters_settings"] = "temperature 0.8, top_k 40, top_p 0.95, min_p 0.05"
+    return res
+
+
 def cpu_baseline(w: synth.Workload, weights, n_steps: int) -> dict:
     """The oracle, as it stands, on this host: n_steps decode steps ending at the workload's
     context (synthetic stored KV before them), with every core OpenMP offers, then with one."""
@@ -273,6 +302,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, weights, args.cpu_steps)
+    sampling = sampler_timing(s.vocab, 1, dt / K * 1e3)
 
     if real_prompt:
         how = f"prefill {w.prompt_len} random tokens, greedy decode to position {start}, then {K} timed steps"
@@ -304,6 +334,7 @@ def main():
         "greedy_tokens_checked": "timed run == kernel-timing rerun; device error word clear",
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "sampling": sampling,
     }
     eng.close()
     print(json.dumps(rec), flush=True)
@@ -422,6 +453,7 @@ def bench_batched(args, w: synth.Workload):
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline_batched(w, weights, ctxs, 2)
+    sampling = sampler_timing(s.vocab, B, dt / K * 1e3)
     ctx_desc = (f"per-sequence contexts uniform in [512, 4096] (seed 7; mean {float(ctxs.mean()):.0f})"
                 if w.mixed_contexts else f"every sequence at context {w.context}")
     rec = {
@@ -451,6 +483,8 @@ def bench_batched(args, w: synth.Workload):
         "greedy_tokens_checked": "timed run == kernel-timing reruns; device error word clear",
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "sampling": sampling,
+        "sampling": sampling,
     }
     eng.close()
     print(json.dumps(rec), flush=True)

@@ -92,6 +92,7 @@ struct dtd_engine {
   int32_t* err_host = nullptr;    // pinned
 
   std::unordered_map<int64_t, Seq> seqs;
+  std::unordered_map<int64_t, dtd_sampler> samplers;   // sequences that do not decode greedily
   std::vector<int> free_slots;
   std::vector<int32_t> free_blocks;
 
@@ -882,6 +883,39 @@ static dtd_status ready(dtd_engine* e) {
   return DTD_OK;
 }
 
+static bool sampler_valid(const dtd_sampler& s) {
+  return std::isfinite(s.temperature) && s.temperature >= 0.f && s.top_k >= 0 && s.top_p > 0.f && s.top_p <= 1.f &&
+         s.min_p >= 0.f && s.min_p <= 1.f;
+}
+
+static SampleRow sample_row(const dtd_sampler& s, int64_t counter) {
+  return SampleRow{s.temperature, s.top_k, s.top_p, s.min_p, s.seed, counter};
+}
+
+// Replaces the greedy tokens of a step's rows whose sequences have a sampler with a
+// temperature above 0: rows b < B of `logits` (V floats apart), drawing with counter =
+// the position whose logits the row holds.
+static dtd_status sample_rows(dtd_engine* e, int B, const int64_t* seq_ids, const int* poss, const float* logits,
+                              int32_t* out) {
+  if (e->samplers.empty()) return DTD_OK;
+  SampleArgs a;
+  bool any = false;
+  for (int b = 0; b < B; b++) {
+    auto it = e->samplers.find(seq_ids[b]);
+    const dtd_sampler g{0.f, 0, 1.f, 0.f, 0};
+    a.row[b] = sample_row(it == e->samplers.end() ? g : it->second, poss[b]);
+    any = any || a.row[b].temperature > 0.f;
+  }
+  if (!any) return DTD_OK;
+  a.logits = logits;
+  a.stride = e->d.V;
+  a.V = e->d.V;
+  a.B = B;
+  a.out = out;
+  HIP_OK(e, launch_sample(a, e->stream));
+  return DTD_OK;
+}
+
 static int blocks_needed(const dtd_engine* e, int len) { return (len + e->d.bs - 1) / e->d.bs; }
 
 extern "C" dtd_status dtd_prefill(dtd_engine* e, int64_t seq_id, const int32_t* tokens_dev, int32_t n,
@@ -941,6 +975,8 @@ extern "C" dtd_status dtd_prefill(dtd_engine* e, int64_t seq_id, const int32_t* 
         if (logits_dev)
           HIP_OK(e, hipMemcpyAsync(logits_dev, e->logits + (size_t)(B - 1) * e->d.V, (size_t)e->d.V * 4,
                                    hipMemcpyDeviceToDevice, e->stream));
+        const int lastpos = s.len - 1;
+        return sample_rows(e, 1, &seq_id, &lastpos, e->logits + (size_t)(B - 1) * e->d.V, next_token_dev);
       }
     }
     return DTD_OK;
@@ -962,7 +998,8 @@ extern "C" dtd_status dtd_prefill(dtd_engine* e, int64_t seq_id, const int32_t* 
     if (st) return st;
     s.len++;
   }
-  return DTD_OK;
+  const int lastpos = s.len - 1;
+  return sample_rows(e, 1, &seq_id, &lastpos, e->logits, next_token_dev);
 }
 
 // Sequence lookups, block allocation and the step launch of a decode call.  Uses fixed-size
@@ -1031,6 +1068,8 @@ static dtd_status decode_impl(dtd_engine* e, int32_t batch, const int64_t* seq_i
   st = run_step(e, batch, slots, poss, pblks, tokens_dev, next_tokens_dev, logits_dev, true, upd, n_upd,
                 inject, capture, partials, gemm_partials, no_alloc, no_alloc);
   if (st) return st;
+  st = sample_rows(e, batch, seq_ids_host, poss, e->logits, next_tokens_dev);
+  if (st) return st;
   for (int b = 0; b < batch; b++) ss[b]->len++;
   return DTD_OK;
 }
@@ -1086,6 +1125,52 @@ extern "C" dtd_status dtd_reset_seq(dtd_engine* e, int64_t seq_id) {
   for (auto b = it->second.blocks.rbegin(); b != it->second.blocks.rend(); ++b) e->free_blocks.push_back(*b);
   e->free_slots.push_back(it->second.slot);
   e->seqs.erase(it);
+  e->samplers.erase(seq_id);
+  return DTD_OK;
+}
+
+extern "C" dtd_status dtd_set_sampler(dtd_engine* e, int64_t seq_id, const dtd_sampler* s) {
+  if (!e) return DTD_E_ARG;
+  if (!s || s->temperature == 0.f) {
+    if (s && !sampler_valid(*s)) return fail(e, DTD_E_ARG, "set_sampler: invalid settings");
+    e->samplers.erase(seq_id);
+    return DTD_OK;
+  }
+  if (e->d.V > kMaxSampleVocab)
+    return fail(e, DTD_E_UNSUPPORTED, "set_sampler: vocabulary %d above %d", e->d.V, kMaxSampleVocab);
+  if (!sampler_valid(*s))
+    return fail(e, DTD_E_ARG, "set_sampler: temperature %g, top_k %d, top_p %g, min_p %g outside their ranges",
+                (double)s->temperature, s->top_k, (double)s->top_p, (double)s->min_p);
+  e->samplers[seq_id] = *s;
+  return DTD_OK;
+}
+
+extern "C" dtd_status dtd_sample(const float* logits_dev, int64_t row_stride, int32_t batch, int32_t vocab,
+                                 const dtd_sampler* samplers_host, const int64_t* counters_host, int32_t* tokens_dev,
+                                 void* hip_stream) {
+  if (!logits_dev || !samplers_host || !counters_host || !tokens_dev || batch < 1 || batch > kMaxBatch ||
+      vocab < 1 || vocab > kMaxSampleVocab || row_stride < vocab) {
+    g_create_err = "sample: null pointer, batch outside [1, 64], vocab outside [1, 2^19] or row_stride < vocab";
+    return DTD_E_ARG;
+  }
+  SampleArgs a;
+  for (int b = 0; b < batch; b++) {
+    if (!sampler_valid(samplers_host[b])) {
+      g_create_err = "sample: sampler settings outside their ranges";
+      return DTD_E_ARG;
+    }
+    a.row[b] = sample_row(samplers_host[b], counters_host[b]);
+  }
+  a.logits = logits_dev;
+  a.stride = row_stride;
+  a.V = vocab;
+  a.B = batch;
+  a.out = tokens_dev;
+  const hipError_t r = launch_sample(a, (hipStream_t)hip_stream);
+  if (r != hipSuccess) {
+    g_create_err = std::string("sample: ") + hipGetErrorString(r);
+    return DTD_E_HIP;
+  }
   return DTD_OK;
 }
 

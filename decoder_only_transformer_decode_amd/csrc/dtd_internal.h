@@ -10,6 +10,7 @@ namespace dtd {
 constexpr int kMaxBatch = 64;
 constexpr int kMaxUpdates = 64;
 constexpr int kPrefillChunk = 64;   // prompt positions per batched prefill step
+constexpr int kMaxSampleVocab = 1 << 19;   // fixed-point token weights: V * 2^44 < 2^64
 constexpr int kAttnTile = 64;      // positions per LDS tile in decode attention (one per lane)
 constexpr int kPersistWaves = 8;   // waves per workgroup of the persistent step kernel
 constexpr int kErrToken = 1;       // device error bits: token id out of range

@@ -47,6 +47,11 @@ class dtd_tensor_spec(C.Structure):
                 ("cols", C.c_int32), ("elem", C.c_int32)]
 
 
+class dtd_sampler(C.Structure):
+    _fields_ = [("temperature", C.c_float), ("top_k", C.c_int32), ("top_p", C.c_float),
+                ("min_p", C.c_float), ("seed", C.c_uint64)]
+
+
 class DtdError(RuntimeError):
     def __init__(self, status: int, msg: str):
         super().__init__(f"{STATUS_NAMES.get(status, status)}: {msg}")
@@ -65,6 +70,8 @@ _SIGS = {
     "dtd_decode_step": ([_P, _I32, C.POINTER(_I64), _P, _P, _P], _I32),
     "dtd_decode_step_noalloc": ([_P, _I32, C.POINTER(_I64), _P, _P, _P], _I32),
     "dtd_reset_seq": ([_P, _I64], _I32),
+    "dtd_sample": ([_P, _I64, _I32, _I32, C.POINTER(dtd_sampler), C.POINTER(_I64), _P, _P], _I32),
+    "dtd_set_sampler": ([_P, _I64, C.POINTER(dtd_sampler)], _I32),
     "dtd_seq_len": ([_P, _I64], _I32),
     "dtd_check_device_errors": ([_P], _I32),
     "dtd_destroy": ([_P], None),
@@ -338,6 +345,9 @@ class Engine:
     def reset_seq(self, seq_id: int):
         dtd_reset_seq(self.h, seq_id)
 
+    def set_sampler(self, seq_id: int, s: Optional["dtd_sampler"]):
+        dtd_set_sampler(self.h, seq_id, s)
+
     def seq_len(self, seq_id: int) -> int:
         return dtd_seq_len(self.h, seq_id)
 
@@ -349,3 +359,23 @@ def dtd_debug_stream_read(buf_ptr: int, nbytes: int, reps: int, stream: int) -> 
     if st != DTD_OK:
         raise DtdError(st, load().dtd_last_error(None).decode())
     return out.value
+
+
+def sampler(temperature: float = 0.0, top_k: int = 0, top_p: float = 1.0, min_p: float = 0.0,
+            seed: int = 0) -> dtd_sampler:
+    return dtd_sampler(temperature, top_k, top_p, min_p, seed)
+
+
+def dtd_sample(logits_ptr: int, row_stride: int, batch: int, vocab: int, samplers: Sequence[dtd_sampler],
+               counters: Sequence[int], tokens_ptr: int, stream: int = 0):
+    """One sampled token per row into tokens_ptr (device int32 [batch]); asynchronous."""
+    arr = (dtd_sampler * batch)(*samplers)
+    ctr = (C.c_int64 * batch)(*[int(c) for c in counters])
+    st = load().dtd_sample(C.c_void_p(logits_ptr), row_stride, batch, vocab, arr, ctr, C.c_void_p(tokens_ptr),
+                           C.c_void_p(stream))
+    if st != DTD_OK:
+        raise DtdError(st, load().dtd_last_error(None).decode())
+
+
+def dtd_set_sampler(h, seq_id: int, s: Optional[dtd_sampler]):
+    _check(h, load().dtd_set_sampler(h, seq_id, C.byref(s) if s is not None else None))

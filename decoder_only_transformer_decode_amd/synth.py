@@ -326,3 +326,31 @@ def tiny_shape(**kw) -> ModelShape:
     """A very small shape for brute-force oracle checks."""
     base = ModelShape("micro", 64, 2, 4, 2, 16, 96, 97, W_INT8_ROW, ACT_F32, KV_F32)
     return base.replace(**kw)
+
+
+def sampling_logits(rows: int, vocab: int, seed: int = 0) -> np.ndarray:
+    """fp32 logit rows [rows][vocab] for sampler tests: Gaussian with a spread that varies by
+    row (0.5 to 8), plus rows with many exact ties (multiples of 0.25), rows with a few -inf
+    and NaN entries, a row with one dominant logit and a row of equal logits."""
+    rng = np.random.default_rng(seed)
+    spreads = [0.5, 1.0, 2.0, 4.0, 8.0]
+    out = np.empty((rows, vocab), np.float32)
+    for r in range(rows):
+        x = rng.standard_normal(vocab) * spreads[r % len(spreads)]
+        if r % 7 == 3:
+            x = np.round(x * 4) / 4
+        if r % 11 == 5 and vocab > 8:
+            bad = rng.choice(vocab, size=max(2, vocab // 100), replace=False)
+            x[bad[: len(bad) // 2]] = -np.inf
+            x[bad[len(bad) // 2:]] = np.nan
+        if r % 13 == 8:
+            x[rng.integers(vocab)] = x.max() + 20.0
+        if r % 17 == 9:
+            x[:] = 1.5
+        out[r] = x.astype(np.float32)
+    return out
+
+
+def bench_logits(rows: int, vocab: int, seed: int = 0) -> np.ndarray:
+    """fp32 logit rows [rows][vocab], N(0, 3^2): the sampler's timing input."""
+    return (_stream(seed, 1).standard_normal((rows, vocab)) * 3.0).astype(np.float32)

@@ -176,10 +176,58 @@ dtd_status dtd_decode_step_noalloc(dtd_engine* e, int32_t batch, const int64_t* 
                                    const int32_t* tokens_dev, int32_t* next_tokens_dev,
                                    float* logits_dev);
 
+/* ---- sampling ----------------------------------------------------------------------- */
+
+/* Sampler settings: the sampler of the nxmr.cn C17 engine article (4.6) and of smollm3.go's
+ * walkthrough ("sampling: from logits to the next token").
+ *   temperature  0 = greedy: the largest logit, the lowest index among equal ones.  Above 0
+ *                the logits are divided by it and soft-maxed.
+ *   top_k        > 0 keeps the top_k most probable tokens (0 = off).
+ *   top_p        < 1 keeps the shortest run of most probable tokens whose probability
+ *                reaches top_p (1 = off); range (0, 1].
+ *   min_p        > 0 keeps the tokens whose probability is at least min_p (0 = off); the
+ *                most probable token always stays; range [0, 1].
+ *   seed         key of the draws.
+ * The filters apply in that order, each to the renormalised distribution the one before it
+ * left; "most probable" orders by logit, then by index.  One token is then drawn by inverse
+ * transform sampling in vocabulary order: the first kept token whose cumulative
+ * probability exceeds u, with u = the top 53 bits of the first word of the Philox4x64-10
+ * block (Salmon et al., SC 2011) at counter (c, 0, 0, 0) and key (seed, 0), times 2^-53.
+ * The same (seed, c) always gives the same u.  Probabilities are computed as exact integer
+ * sums of weights exp((l - max) / T) in 2^-44 fixed point: tokens with a weight below
+ * 2^-44 of the largest are never drawn.  NaN logits are never drawn. */
+typedef struct {
+  float temperature;
+  int32_t top_k;
+  float top_p;
+  float min_p;
+  uint64_t seed;
+} dtd_sampler;
+
+/* Samples one token per row: rows b < batch of logits_dev (fp32, row b at
+ * logits_dev + b * row_stride, vocab columns) with samplers_host[b] and draw counter
+ * counters_host[b] (host arrays [batch]) -> tokens_dev[b] (device int32 [batch]).  Needs no
+ * engine and allocates nothing; enqueued on hip_stream (a hipStream_t, NULL = the null
+ * stream), asynchronous.  DTD_E_ARG for a null pointer, batch outside [1, 64], vocab
+ * outside [1, 2^19], row_stride < vocab or settings outside their ranges (the message is
+ * then what dtd_last_error(NULL) returns); DTD_E_HIP if the launch fails. */
+dtd_status dtd_sample(const float* logits_dev, int64_t row_stride, int32_t batch, int32_t vocab,
+                      const dtd_sampler* samplers_host, const int64_t* counters_host, int32_t* tokens_dev,
+                      void* hip_stream);
+
+/* Sets how sequence seq_id picks its next tokens from then on: every later dtd_prefill and
+ * decode step of it draws with *s instead of taking the greedy token, with counter = the
+ * position whose logits are sampled (the last prompt position for a prefill), so a
+ * sequence's draws do not depend on the batch it shares.  s = NULL or temperature 0
+ * restores greedy.  The sequence need not exist yet; dtd_reset_seq forgets the setting.
+ * Host only.  DTD_E_ARG for settings outside their ranges, DTD_E_UNSUPPORTED when the
+ * model's vocabulary exceeds 2^19. */
+dtd_status dtd_set_sampler(dtd_engine* e, int64_t seq_id, const dtd_sampler* s);
+
 /* Forgets a sequence, as the Qwen3-8B engine article's ResetSeq call does (4.1.2): its KV
- * blocks and its slot return to the free lists, and the seq_id may be used again for a new
- * sequence.  Host only (nothing is enqueued; the blocks' contents are not cleared).
- * DTD_E_NOSEQ for an unknown seq_id. */
+ * blocks and its slot return to the free lists, its sampler setting is dropped, and the
+ * seq_id may be used again for a new sequence.  Host only (nothing is enqueued; the
+ * blocks' contents are not cleared).  DTD_E_NOSEQ for an unknown seq_id. */
 dtd_status dtd_reset_seq(dtd_engine* e, int64_t seq_id);
 
 /* Current length (positions written) of a sequence, or a dtd_status < 0. */

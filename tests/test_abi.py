@@ -87,6 +87,7 @@ def test_null_engine_calls_are_errors_not_crashes():
     assert lib.dtd_reset_seq(None, 1) == dtd.DTD_E_ARG
     assert lib.dtd_seq_len(None, 1) == dtd.DTD_E_ARG
     assert lib.dtd_decode_step(None, 1, None, None, None, None) == dtd.DTD_E_ARG
+    assert lib.dtd_set_sampler(None, 1, None) == dtd.DTD_E_ARG
     assert lib.dtd_last_error(None) == b"null engine"
     lib.dtd_destroy(None)
 
@@ -101,3 +102,14 @@ def test_rejected_create_leaves_its_reason_for_last_error():
     assert b"n_kv_heads 3" in lib.dtd_last_error(None)
     with pytest.raises(dtd.DtdError, match="n_kv_heads 3"):
         dtd.dtd_create(bad, 0)
+
+
+def test_sample_checks_its_arguments_before_any_device_call():
+    # null pointers and out-of-range sizes are rejected on the host (no GPU needed)
+    lib = dtd.load()
+    s = (dtd.dtd_sampler * 1)(dtd.sampler(temperature=1.0))
+    c = (C.c_int64 * 1)(0)
+    assert lib.dtd_sample(None, 10, 1, 10, s, c, None, None) == dtd.DTD_E_ARG
+    assert b"sample:" in lib.dtd_last_error(None)
+    assert lib.dtd_sample(None, 10, 0, 10, None, None, None, None) == dtd.DTD_E_ARG
+    assert lib.dtd_sample(None, 10, 65, 10, None, None, None, None) == dtd.DTD_E_ARG
