@@ -63,13 +63,17 @@ KERNEL_SOURCES = ["decoder_only_transformer_decode_amd/csrc/dtd_persistent.hip",
 
 
 def kernel_source_hash() -> str:
-    """sha256 over the step kernel's sources, to tell whether recorded counters still apply"""
+    """sha256 over the step kernel's sources (of the shared internal header, the part before
+    its launcher declarations), to tell whether recorded counters still apply"""
     import hashlib
     h = hashlib.sha256()
     root = os.path.dirname(os.path.abspath(__file__))
     for rel in KERNEL_SOURCES:
         with open(os.path.join(root, rel), "rb") as f:
-            h.update(f.read())
+            data = f.read()
+        if rel.endswith("dtd_internal.h"):
+            data = data.split(b"// ---- launchers")[0]
+        h.update(data)
     return h.hexdigest()
 
 
@@ -82,10 +86,11 @@ def recorded_traffic(workload: str, attended: str):
     if not os.path.exists(path):
         return None
     with open(path) as f:
-        r = json.load(f)
-    if r.get("kernel_source_sha256") != kernel_source_hash() or r.get("attended") != attended:
-        return None
-    return (r["fetch_kib_per_launch"] * r["fetch_scale"] + r["write_kib_per_launch"] * r["write_scale"]) * 1024.0
+        doc = json.load(f)
+    for r in doc.get("records", []):
+        if r.get("kernel_source_sha256") == kernel_source_hash() and r.get("attended") == attended:
+            return (r["fetch_kib_per_launch"] * r["fetch_scale"] + r["write_kib_per_launch"] * r["write_scale"]) * 1024.0
+    return None
 
 
 def sampler_timing(vocab: int, batch: int, step_ms: float) -> dict:
