@@ -11,7 +11,7 @@ ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libdtd.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["dtd_kernels.hip", "dtd_persistent.hip", "dtd_sample.hip", "dtd_engine.cpp"]
+SOURCES = ["dtd_kernels.hip", "dtd_persistent.hip", "dtd_sample.hip", "dtd_engine.cpp", "dtd_sched.cpp"]
 
 # -packed-fp32-ops: keep the compiler from emitting packed fp32 VALU ops (v_pk_*_f32).
 FLAGS = ["-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC", "-shared",

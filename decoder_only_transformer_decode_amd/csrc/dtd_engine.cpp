@@ -34,6 +34,19 @@ struct Seq {
   int slot = -1;
   int len = 0;
   std::vector<int32_t> blocks;
+  // token ids of positions [0, len) when the host knows them all (prefill inputs with the
+  // prefix cache on); decode steps append ids only the device holds
+  std::vector<int32_t> tokens;
+  bool tokens_known = true;
+  int reused = 0;   // positions the last prefill took from the prefix cache
+};
+
+// A prefix-cache entry: the KV of a token sequence's positions [0, tokens.size()), held as
+// references to the blocks that store it.
+struct PrefixEntry {
+  std::vector<int32_t> tokens;
+  std::vector<int32_t> blocks;
+  uint64_t used = 0;   // LRU clock of the last hit or insert
 };
 
 struct TimerPair {
@@ -95,6 +108,14 @@ struct dtd_engine {
   std::unordered_map<int64_t, dtd_sampler> samplers;   // sequences that do not decode greedily
   std::vector<int> free_slots;
   std::vector<int32_t> free_blocks;
+  std::vector<int32_t> blk_ref;   // holders of each KV block: sequences and prefix-cache entries
+
+  // prefix cache: entries by id, and every prefix of every entry by its hash
+  int pcache_cap = 0;             // 0: off
+  int64_t pcache_next = 0;
+  uint64_t pcache_clock = 0;
+  std::unordered_map<int64_t, PrefixEntry> pcache;
+  std::unordered_multimap<uint64_t, std::pair<int64_t, int32_t>> pindex;   // hash -> (entry, length)
 
   float* capture = nullptr;
 
@@ -450,6 +471,7 @@ extern "C" dtd_status dtd_create(const dtd_config* cfg, void* hip_stream, dtd_en
   for (int s = cfg->max_seqs - 1; s >= 0; s--) e->free_slots.push_back(s);
   e->free_blocks.resize((size_t)cfg->kv_num_blocks);
   for (int i = 0; i < cfg->kv_num_blocks; i++) e->free_blocks[(size_t)i] = i;
+  e->blk_ref.assign((size_t)cfg->kv_num_blocks, 0);
   uint64_t lcg = 0x9E3779B97F4A7C15ull;
   for (int i = cfg->kv_num_blocks - 1; i > 0; i--) {
     lcg = lcg * 6364136223846793005ull + 1442695040888963407ull;
@@ -918,6 +940,126 @@ static dtd_status sample_rows(dtd_engine* e, int B, const int64_t* seq_ids, cons
 
 static int blocks_needed(const dtd_engine* e, int len) { return (len + e->d.bs - 1) / e->d.bs; }
 
+// ---- KV blocks: a free list plus a holder count per block, so that sequences and prefix-cache
+// entries can share blocks (the Qwen3-8B engine article's paged KV block manager, 4.3.1: fixed
+// blocks, O(1) allocation and release, free blocks reused)
+static int32_t take_block(dtd_engine* e) {
+  const int32_t b = e->free_blocks.back();
+  e->free_blocks.pop_back();
+  e->blk_ref[(size_t)b] = 1;
+  return b;
+}
+
+static void drop_block(dtd_engine* e, int32_t b) {
+  if (--e->blk_ref[(size_t)b] == 0) e->free_blocks.push_back(b);
+}
+
+// ---- prefix cache (the Qwen3-8B engine article's automatic prefix cache, 4.4.4): KV of token
+// sequences already run, found by a hash of the token prefix, the whole sequence first and then
+// ever shorter prefixes; a hit skips prefilling the matched positions.
+
+// FNV-1a over the token ids, one hash per prefix length: h[L] covers tokens [0, L)
+static void prefix_hashes(const int32_t* t, int n, std::vector<uint64_t>& h) {
+  h.resize((size_t)n + 1);
+  uint64_t x = 0xcbf29ce484222325ull;
+  h[0] = x;
+  for (int i = 0; i < n; i++) {
+    const uint32_t v = (uint32_t)t[i];
+    for (int k = 0; k < 4; k++) {
+      x ^= (v >> (8 * k)) & 0xffu;
+      x *= 0x100000001b3ull;
+    }
+    h[(size_t)i + 1] = x;
+  }
+}
+
+static void pcache_drop(dtd_engine* e, int64_t id) {
+  auto it = e->pcache.find(id);
+  if (it == e->pcache.end()) return;
+  const PrefixEntry& pe = it->second;
+  std::vector<uint64_t> h;
+  prefix_hashes(pe.tokens.data(), (int)pe.tokens.size(), h);
+  for (size_t L = 1; L < h.size(); L++) {
+    auto r = e->pindex.equal_range(h[L]);
+    for (auto j = r.first; j != r.second;) {
+      if (j->second.first == id) j = e->pindex.erase(j);
+      else ++j;
+    }
+  }
+  for (int32_t b : pe.blocks) drop_block(e, b);
+  e->pcache.erase(it);
+}
+
+// evicts least recently used entries (never `keep`) until `need` blocks are free or no other
+// entry is left
+static bool make_room(dtd_engine* e, int need, int64_t keep = -1) {
+  while ((int)e->free_blocks.size() < need) {
+    auto lru = e->pcache.end();
+    for (auto it = e->pcache.begin(); it != e->pcache.end(); ++it)
+      if (it->first != keep && (lru == e->pcache.end() || it->second.used < lru->second.used)) lru = it;
+    if (lru == e->pcache.end()) break;
+    pcache_drop(e, lru->first);
+  }
+  return (int)e->free_blocks.size() >= need;
+}
+
+// the longest cached prefix of t[0, n) shorter than n (the last position is always run, for
+// its logits); 0 if none.  *entry gets the entry holding it.
+static int pcache_lookup(dtd_engine* e, const int32_t* t, int n, int64_t* entry) {
+  if (e->pcache.empty() || n < 2) return 0;
+  std::vector<uint64_t> h;
+  prefix_hashes(t, n, h);
+  for (int L = n - 1; L >= 1; L--) {
+    auto r = e->pindex.equal_range(h[(size_t)L]);
+    for (auto j = r.first; j != r.second; ++j) {
+      const PrefixEntry& pe = e->pcache.at(j->second.first);
+      if (j->second.second == L && (int)pe.tokens.size() >= L && std::equal(t, t + L, pe.tokens.begin())) {
+        *entry = j->second.first;
+        return L;
+      }
+    }
+  }
+  return 0;
+}
+
+// records positions [0, n) of sequence s, holding tokens t, as an entry
+static void pcache_insert(dtd_engine* e, const Seq& s, const int32_t* t, int n) {
+  if (e->pcache_cap <= 0 || n < 1 || n > s.len) return;
+  std::vector<uint64_t> h;
+  prefix_hashes(t, n, h);
+  auto r = e->pindex.equal_range(h[(size_t)n]);
+  for (auto j = r.first; j != r.second; ++j) {
+    PrefixEntry& pe = e->pcache.at(j->second.first);
+    if (j->second.second == n && (int)pe.tokens.size() == n && std::equal(t, t + n, pe.tokens.begin())) {
+      pe.used = ++e->pcache_clock;             // already cached
+      return;
+    }
+  }
+  while ((int)e->pcache.size() >= e->pcache_cap) {
+    auto lru = e->pcache.begin();
+    for (auto it = e->pcache.begin(); it != e->pcache.end(); ++it)
+      if (it->second.used < lru->second.used) lru = it;
+    pcache_drop(e, lru->first);
+  }
+  const int64_t id = e->pcache_next++;
+  PrefixEntry pe;
+  pe.tokens.assign(t, t + n);
+  pe.blocks.assign(s.blocks.begin(), s.blocks.begin() + blocks_needed(e, n));
+  for (int32_t b : pe.blocks) e->blk_ref[(size_t)b]++;
+  pe.used = ++e->pcache_clock;
+  e->pcache.emplace(id, std::move(pe));
+  for (int L = 1; L <= n; L++) e->pindex.emplace(h[(size_t)L], std::make_pair(id, L));
+}
+
+// copies every layer's K and V (and int8 scales) of block src to block dst, on the stream
+static dtd_status copy_block(dtd_engine* e, int32_t src, int32_t dst) {
+  HIP_OK(e, launch_kv_copy_block(e->d, e->players, src, dst, e->stream));
+  return DTD_OK;
+}
+
+static dtd_status prefill_run(dtd_engine* e, int64_t seq_id, Seq& s, const int32_t* tokens_dev, int n,
+                              int32_t* next_token_dev, float* logits_dev);
+
 extern "C" dtd_status dtd_prefill(dtd_engine* e, int64_t seq_id, const int32_t* tokens_dev, int32_t n,
                                   int32_t* next_token_dev, float* logits_dev) {
   dtd_status st = ready(e);
@@ -929,9 +1071,21 @@ extern "C" dtd_status dtd_prefill(dtd_engine* e, int64_t seq_id, const int32_t* 
   if ((int64_t)len0 + n > e->cfg.max_ctx)
     return fail(e, DTD_E_CTX, "prefill: %d + %d positions exceed max_ctx %d", len0, n, e->cfg.max_ctx);
   if (is_new && e->free_slots.empty()) return fail(e, DTD_E_KVFULL, "prefill: no free sequence slot");
+  // with the prefix cache on, the host reads the tokens: to look up a new sequence's longest
+  // cached prefix, and to record the prompt afterwards
+  const bool pc = e->pcache_cap > 0;
+  std::vector<int32_t> host;
+  if (pc) {
+    host.resize((size_t)n);
+    HIP_OK(e, hipStreamSynchronize(e->stream));
+    HIP_OK(e, hipMemcpy(host.data(), tokens_dev, (size_t)n * 4, hipMemcpyDeviceToHost));
+  }
+  int64_t hit = -1;
+  const int reuse = (pc && is_new) ? pcache_lookup(e, host.data(), n, &hit) : 0;
+  const int shared = reuse / e->d.bs;       // whole blocks taken over from the entry
   const int have = is_new ? 0 : (int)it->second.blocks.size();
-  const int need = blocks_needed(e, len0 + n) - have;
-  if (need > (int)e->free_blocks.size())
+  const int need = blocks_needed(e, len0 + n) - have - shared;
+  if (!make_room(e, need, hit))
     return fail(e, DTD_E_KVFULL, "prefill: needs %d KV blocks, %zu free", need, e->free_blocks.size());
   if (is_new) {
     Seq s;
@@ -941,6 +1095,40 @@ extern "C" dtd_status dtd_prefill(dtd_engine* e, int64_t seq_id, const int32_t* 
     it = e->seqs.emplace(seq_id, s).first;
   }
   Seq& s = it->second;
+  if (!pc) s.tokens_known = false;
+  s.reused = reuse;
+  if (reuse > 0) {
+    // positions [0, reuse) from the entry: its whole blocks shared, a partial last one copied
+    PrefixEntry& pe = e->pcache.at(hit);
+    pe.used = ++e->pcache_clock;
+    for (int j = 0; j < shared; j++) {
+      s.blocks.push_back(pe.blocks[(size_t)j]);
+      e->blk_ref[(size_t)pe.blocks[(size_t)j]]++;
+    }
+    if (reuse % e->d.bs) {
+      const int32_t nb = take_block(e);
+      if ((st = copy_block(e, pe.blocks[(size_t)shared], nb))) return st;
+      s.blocks.push_back(nb);
+    }
+    HIP_OK(e, hipStreamSynchronize(e->stream));
+    HIP_OK(e, hipMemcpy(e->bt_dev + (size_t)s.slot * e->d.max_blocks, s.blocks.data(), s.blocks.size() * 4,
+                        hipMemcpyHostToDevice));
+    s.len = reuse;
+    s.tokens.assign(host.begin(), host.begin() + reuse);
+    tokens_dev += reuse;
+    n -= reuse;
+  }
+  if (pc && s.tokens_known) s.tokens.insert(s.tokens.end(), host.begin() + reuse, host.end());
+  st = prefill_run(e, seq_id, s, tokens_dev, n, next_token_dev, logits_dev);
+  if (st) return st;
+  if (pc && s.tokens_known && (int)s.tokens.size() == s.len) pcache_insert(e, s, s.tokens.data(), s.len);
+  return DTD_OK;
+}
+
+// Runs n tokens of an existing sequence (its blocks for the positions before are in place).
+static dtd_status prefill_run(dtd_engine* e, int64_t seq_id, Seq& s, const int32_t* tokens_dev, int n,
+                              int32_t* next_token_dev, float* logits_dev) {
+  dtd_status st = DTD_OK;
   // Batched prefill: the prompt in chunks of up to kPrefillChunk positions, each chunk one
   // step of the per-sub-step schedule with the chunk's positions as its batch (projections on
   // the matrix cores where the formats allow); every position's K/V is appended before the
@@ -957,8 +1145,7 @@ extern "C" dtd_status dtd_prefill(dtd_engine* e, int64_t seq_id, const int32_t* 
       for (int b = 0; b < B; b++) {
         const int pos = s.len + b;
         if (pos / e->d.bs >= (int)s.blocks.size()) {
-          const int32_t blk = e->free_blocks.back();
-          e->free_blocks.pop_back();
+          const int32_t blk = take_block(e);
           s.blocks.push_back(blk);
           upd[n_upd++] = {s.slot, (int)s.blocks.size() - 1, blk};
         }
@@ -986,8 +1173,7 @@ extern "C" dtd_status dtd_prefill(dtd_engine* e, int64_t seq_id, const int32_t* 
     Update upd[1];
     int n_upd = 0;
     if (pos / e->d.bs >= (int)s.blocks.size()) {
-      const int32_t b = e->free_blocks.back();
-      e->free_blocks.pop_back();
+      const int32_t b = take_block(e);
       s.blocks.push_back(b);
       upd[n_upd++] = {s.slot, (int)s.blocks.size() - 1, b};
     }
@@ -1024,7 +1210,7 @@ static dtd_status decode_impl(dtd_engine* e, int32_t batch, const int64_t* seq_i
     if (create_missing && e->seqs.find(seq_ids_host[b]) == e->seqs.end()) missing++;
   }
   if (missing > (int)e->free_slots.size()) return fail(e, DTD_E_KVFULL, "decode_step: no free sequence slot");
-  if (missing > (int)e->free_blocks.size()) return fail(e, DTD_E_KVFULL, "decode_step: no free KV block");
+  if (!make_room(e, missing)) return fail(e, DTD_E_KVFULL, "decode_step: no free KV block");
   for (int b = 0; b < batch; b++) {
     auto it = e->seqs.find(seq_ids_host[b]);
     if (it == e->seqs.end() && !create_missing)
@@ -1038,7 +1224,7 @@ static dtd_status decode_impl(dtd_engine* e, int32_t batch, const int64_t* seq_i
       need++;
     }
   }
-  if (need > (int)e->free_blocks.size())
+  if (!make_room(e, need))
     return fail(e, DTD_E_KVFULL, "decode_step: needs %d KV blocks, %zu free", need, e->free_blocks.size());
   // validated: only now change engine state
   for (int b = 0; b < batch && missing; b++)
@@ -1056,8 +1242,7 @@ static dtd_status decode_impl(dtd_engine* e, int32_t batch, const int64_t* seq_i
   for (int b = 0; b < batch; b++) {
     Seq& s = *ss[b];
     if (s.len / e->d.bs >= (int)s.blocks.size()) {
-      const int32_t blk = e->free_blocks.back();
-      e->free_blocks.pop_back();
+      const int32_t blk = take_block(e);
       s.blocks.push_back(blk);
       upd[n_upd++] = {s.slot, (int)s.blocks.size() - 1, blk};
     }
@@ -1070,7 +1255,10 @@ static dtd_status decode_impl(dtd_engine* e, int32_t batch, const int64_t* seq_i
   if (st) return st;
   st = sample_rows(e, batch, seq_ids_host, poss, e->logits, next_tokens_dev);
   if (st) return st;
-  for (int b = 0; b < batch; b++) ss[b]->len++;
+  for (int b = 0; b < batch; b++) {
+    ss[b]->len++;
+    ss[b]->tokens_known = false;   // the token ids of a decode step stay on the device
+  }
   return DTD_OK;
 }
 
@@ -1122,7 +1310,7 @@ extern "C" dtd_status dtd_reset_seq(dtd_engine* e, int64_t seq_id) {
   if (!e) return DTD_E_ARG;
   auto it = e->seqs.find(seq_id);
   if (it == e->seqs.end()) return fail(e, DTD_E_NOSEQ, "reset_seq: unknown seq_id %lld", (long long)seq_id);
-  for (auto b = it->second.blocks.rbegin(); b != it->second.blocks.rend(); ++b) e->free_blocks.push_back(*b);
+  for (auto b = it->second.blocks.rbegin(); b != it->second.blocks.rend(); ++b) drop_block(e, *b);
   e->free_slots.push_back(it->second.slot);
   e->seqs.erase(it);
   e->samplers.erase(seq_id);
@@ -1143,6 +1331,54 @@ extern "C" dtd_status dtd_set_sampler(dtd_engine* e, int64_t seq_id, const dtd_s
                 (double)s->temperature, s->top_k, (double)s->top_p, (double)s->min_p);
   e->samplers[seq_id] = *s;
   return DTD_OK;
+}
+
+extern "C" dtd_status dtd_set_prefix_cache(dtd_engine* e, int32_t max_entries) {
+  if (!e) return DTD_E_ARG;
+  if (max_entries < 0) return fail(e, DTD_E_ARG, "set_prefix_cache: max_entries %d < 0", max_entries);
+  e->pcache_cap = max_entries;
+  while ((int)e->pcache.size() > max_entries) {
+    auto lru = e->pcache.begin();
+    for (auto it = e->pcache.begin(); it != e->pcache.end(); ++it)
+      if (it->second.used < lru->second.used) lru = it;
+    pcache_drop(e, lru->first);
+  }
+  return DTD_OK;
+}
+
+extern "C" dtd_status dtd_prefix_cache_add(dtd_engine* e, int64_t seq_id, const int32_t* tokens_host, int32_t n) {
+  if (!e) return DTD_E_ARG;
+  auto it = e->seqs.find(seq_id);
+  if (it == e->seqs.end()) return fail(e, DTD_E_NOSEQ, "prefix_cache_add: unknown seq_id %lld", (long long)seq_id);
+  if (!tokens_host || n < 1 || n > it->second.len)
+    return fail(e, DTD_E_ARG, "prefix_cache_add: n %d outside [1, %d] or null tokens", n, it->second.len);
+  if (e->pcache_cap <= 0) return fail(e, DTD_E_STATE, "prefix_cache_add: the prefix cache is off");
+  pcache_insert(e, it->second, tokens_host, n);
+  return DTD_OK;
+}
+
+extern "C" dtd_status dtd_get_config(const dtd_engine* e, dtd_config* out) {
+  if (!e || !out) return DTD_E_ARG;
+  *out = e->cfg;
+  return DTD_OK;
+}
+
+extern "C" void* dtd_get_stream(const dtd_engine* e) { return e ? (void*)e->stream : nullptr; }
+
+extern "C" int32_t dtd_debug_prefix_reused(const dtd_engine* e, int64_t seq_id) {
+  if (!e) return DTD_E_ARG;
+  auto it = e->seqs.find(seq_id);
+  return it == e->seqs.end() ? DTD_E_NOSEQ : it->second.reused;
+}
+
+extern "C" int32_t dtd_debug_kv_blocks_free(const dtd_engine* e) {
+  if (!e) return DTD_E_ARG;
+  return (int32_t)e->free_blocks.size();
+}
+
+extern "C" int32_t dtd_debug_prefix_entries(const dtd_engine* e) {
+  if (!e) return DTD_E_ARG;
+  return (int32_t)e->pcache.size();
 }
 
 extern "C" dtd_status dtd_sample(const float* logits_dev, int64_t row_stride, int32_t batch, int32_t vocab,
@@ -1276,12 +1512,10 @@ static dtd_status ensure_seq_blocks(dtd_engine* e, int64_t seq_id, int len, Seq*
   }
   Seq& s = it->second;
   const int need = blocks_needed(e, len) - (int)s.blocks.size();
-  if (need > (int)e->free_blocks.size()) return fail(e, DTD_E_KVFULL, "needs %d KV blocks, %zu free", need, e->free_blocks.size());
+  if (!make_room(e, need)) return fail(e, DTD_E_KVFULL, "needs %d KV blocks, %zu free", need, e->free_blocks.size());
+  s.tokens_known = false;
   if (need > 0) {
-    for (int i = 0; i < need; i++) {
-      s.blocks.push_back(e->free_blocks.back());
-      e->free_blocks.pop_back();
-    }
+    for (int i = 0; i < need; i++) s.blocks.push_back(take_block(e));
     HIP_OK(e, hipStreamSynchronize(e->stream));
     HIP_OK(e, hipMemcpy(e->bt_dev + (size_t)s.slot * e->d.max_blocks, s.blocks.data(), s.blocks.size() * 4,
                         hipMemcpyHostToDevice));

@@ -186,6 +186,7 @@ hipError_t launch_attention(const Dims& d, const StepDesc* desc, int B, const fl
                             const int32_t* block_table, float* partials, hipStream_t st);
 hipError_t launch_kv_append(const Dims& d, const StepDesc* desc, int B, const float* knew, const float* vnew,
                             const KvLayer& kv, hipStream_t st);
+hipError_t launch_kv_copy_block(const Dims& d, const PLayer* layers, int src, int dst, hipStream_t st);
 hipError_t launch_combine(const Dims& d, const StepDesc* desc, int B, const float* partials,
                           void* o, hipStream_t st);
 hipError_t launch_argmax(const Dims& d, const StepDesc* desc, int B, const float* logits,

@@ -845,6 +845,23 @@ __global__ __launch_bounds__(128) void k_kv_append(Dims d, KvLayer kv, const Ste
                    vnew + (size_t)b * d.kv_dim + (size_t)j * d.hd, new_s, red);
 }
 
+// Prefix reuse: copies KV block src to block dst in every layer (grid: layer x {K, V, K
+// scales, V scales}); `elem` = bytes of one stored element, 16-byte pieces, tail bytes alone.
+__global__ __launch_bounds__(256) void k_kv_copy_block(const PLayer* layers, int Hkv, int bs, int hd, int elem,
+                                                       int src, int dst) {
+  const KvLayer kv = layers[blockIdx.x].kv;
+  const int which = blockIdx.y;
+  const bool scales = which >= 2;
+  uint8_t* pool = (uint8_t*)(which == 0 ? kv.k : which == 1 ? kv.v : which == 2 ? (void*)kv.ks : (void*)kv.vs);
+  if (!pool) return;
+  const size_t n = scales ? (size_t)Hkv * bs * 2 : (size_t)Hkv * bs * hd * elem;
+  const uint8_t* a = pool + (size_t)src * n;
+  uint8_t* b = pool + (size_t)dst * n;
+  const size_t n16 = n % 16 == 0 ? n / 16 : 0;    // 16-byte pieces only when every block starts aligned
+  for (size_t i = threadIdx.x; i < n16; i += 256) ((uint4*)b)[i] = ((const uint4*)a)[i];
+  for (size_t i = n16 * 16 + threadIdx.x; i < n; i += 256) b[i] = a[i];
+}
+
 // one (head, sequence): o = merge of its chunk partials, rounded to the activation type
 __global__ __launch_bounds__(256) void k_combine(Dims d, const StepDesc* desc, const float* partials,
                                                  void* o) {
@@ -1127,6 +1144,12 @@ hipError_t launch_kv_append(const Dims& d, const StepDesc* desc, int B, const fl
   if (d.kvfmt == KV_F32) hipLaunchKernelGGL(k_kv_append<KV_F32>, grid, dim3(128), 0, st, d, kv, desc, knew, vnew);
   else if (d.kvfmt == KV_BF16) hipLaunchKernelGGL(k_kv_append<KV_BF16>, grid, dim3(128), 0, st, d, kv, desc, knew, vnew);
   else hipLaunchKernelGGL(k_kv_append<KV_I8>, grid, dim3(128), 0, st, d, kv, desc, knew, vnew);
+  return hipGetLastError();
+}
+
+hipError_t launch_kv_copy_block(const Dims& d, const PLayer* layers, int src, int dst, hipStream_t st) {
+  const int elem = d.kvfmt == KV_F32 ? 4 : (d.kvfmt == KV_BF16 ? 2 : 1);
+  hipLaunchKernelGGL(k_kv_copy_block, dim3(d.L, 4), dim3(256), 0, st, layers, d.Hkv, d.bs, d.hd, elem, src, dst);
   return hipGetLastError();
 }
 

@@ -72,6 +72,23 @@ _SIGS = {
     "dtd_reset_seq": ([_P, _I64], _I32),
     "dtd_sample": ([_P, _I64, _I32, _I32, C.POINTER(dtd_sampler), C.POINTER(_I64), _P, _P], _I32),
     "dtd_set_sampler": ([_P, _I64, C.POINTER(dtd_sampler)], _I32),
+    "dtd_set_prefix_cache": ([_P, _I32], _I32),
+    "dtd_prefix_cache_add": ([_P, _I64, C.POINTER(_I32), _I32], _I32),
+    "dtd_get_config": ([_P, C.POINTER(dtd_config)], _I32),
+    "dtd_get_stream": ([_P], _P),
+    "dtd_debug_prefix_reused": ([_P, _I64], _I32),
+    "dtd_debug_kv_blocks_free": ([_P], _I32),
+    "dtd_debug_prefix_entries": ([_P], _I32),
+    "dtd_sched_create": ([_P, _I32, C.POINTER(_P)], _I32),
+    "dtd_sched_destroy": ([_P], None),
+    "dtd_sched_submit": ([_P, C.POINTER(_I32), _I32, _I32, _I32, C.POINTER(dtd_sampler), C.POINTER(_I64)], _I32),
+    "dtd_sched_step": ([_P, C.POINTER(_I32)], _I32),
+    "dtd_sched_start": ([_P], _I32),
+    "dtd_sched_stop": ([_P], _I32),
+    "dtd_sched_wait": ([_P, _I64, _I32], _I32),
+    "dtd_sched_result": ([_P, _I64, C.POINTER(_I32), _I32, C.POINTER(_I32)], _I32),
+    "dtd_sched_release": ([_P, _I64], _I32),
+    "dtd_sched_last_error": ([_P], C.c_char_p),
     "dtd_seq_len": ([_P, _I64], _I32),
     "dtd_check_device_errors": ([_P], _I32),
     "dtd_destroy": ([_P], None),
@@ -348,6 +365,23 @@ class Engine:
     def set_sampler(self, seq_id: int, s: Optional["dtd_sampler"]):
         dtd_set_sampler(self.h, seq_id, s)
 
+    def set_prefix_cache(self, max_entries: int):
+        _check(self.h, load().dtd_set_prefix_cache(self.h, max_entries))
+
+    def prefix_cache_add(self, seq_id: int, tokens):
+        arr = np.ascontiguousarray(tokens, dtype=np.int32)
+        _check(self.h, load().dtd_prefix_cache_add(self.h, seq_id, arr.ctypes.data_as(C.POINTER(C.c_int32)),
+                                                   arr.size))
+
+    def prefix_reused(self, seq_id: int) -> int:
+        return load().dtd_debug_prefix_reused(self.h, seq_id)
+
+    def kv_blocks_free(self) -> int:
+        return load().dtd_debug_kv_blocks_free(self.h)
+
+    def prefix_entries(self) -> int:
+        return load().dtd_debug_prefix_entries(self.h)
+
     def seq_len(self, seq_id: int) -> int:
         return dtd_seq_len(self.h, seq_id)
 
@@ -379,3 +413,74 @@ def dtd_sample(logits_ptr: int, row_stride: int, batch: int, vocab: int, sampler
 
 def dtd_set_sampler(h, seq_id: int, s: Optional[dtd_sampler]):
     _check(h, load().dtd_set_sampler(h, seq_id, C.byref(s) if s is not None else None))
+
+
+class Scheduler:
+    """Continuous batching over an Engine (dtd_sched_*): submit requests, then step, or run
+    the scheduler's own loop with start() and wait()."""
+
+    def __init__(self, eng: "Engine", prompt_budget: int = 0):
+        self.eng = eng
+        h = C.c_void_p()
+        st = load().dtd_sched_create(eng.h, prompt_budget, C.byref(h))
+        if st != DTD_OK:
+            raise DtdError(st, "dtd_sched_create")
+        self.h = h
+
+    def _check(self, st):
+        if st != DTD_OK:
+            raise DtdError(st, load().dtd_sched_last_error(self.h).decode())
+
+    def submit(self, prompt, max_new_tokens: int, stop_token: int = -1,
+               sampler: Optional[dtd_sampler] = None) -> int:
+        arr = np.ascontiguousarray(prompt, dtype=np.int32)
+        rid = C.c_int64()
+        st = load().dtd_sched_submit(self.h, arr.ctypes.data_as(C.POINTER(C.c_int32)), arr.size, max_new_tokens,
+                                     stop_token, C.byref(sampler) if sampler is not None else None, C.byref(rid))
+        if st != DTD_OK:
+            raise DtdError(st, "dtd_sched_submit")
+        return rid.value
+
+    def step(self) -> int:
+        pending = C.c_int32()
+        self._check(load().dtd_sched_step(self.h, C.byref(pending)))
+        return pending.value
+
+    def run(self, max_steps: int = 1 << 20) -> int:
+        """Steps until nothing is queued or running; returns the number of steps."""
+        for i in range(max_steps):
+            if self.step() == 0:
+                return i + 1
+        raise RuntimeError("scheduler did not drain")
+
+    def start(self):
+        self._check(load().dtd_sched_start(self.h))
+
+    def stop(self):
+        self._check(load().dtd_sched_stop(self.h))
+
+    def wait(self, rid: int, timeout_ms: int = -1) -> int:
+        return load().dtd_sched_wait(self.h, rid, timeout_ms)
+
+    def result(self, rid: int):
+        done = C.c_int32()
+        cap = 1 << 16
+        buf = (C.c_int32 * cap)()
+        n = load().dtd_sched_result(self.h, rid, buf, cap, C.byref(done))
+        if n < 0:
+            raise DtdError(n, load().dtd_sched_last_error(self.h).decode())
+        return [int(buf[i]) for i in range(min(n, cap))], bool(done.value)
+
+    def release(self, rid: int):
+        self._check(load().dtd_sched_release(self.h, rid))
+
+    def close(self):
+        if getattr(self, "h", None):
+            load().dtd_sched_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -224,6 +224,76 @@ dtd_status dtd_sample(const float* logits_dev, int64_t row_stride, int32_t batch
  * model's vocabulary exceeds 2^19. */
 dtd_status dtd_set_sampler(dtd_engine* e, int64_t seq_id, const dtd_sampler* s);
 
+/* ---- prefix cache --------------------------------------------------------------------- */
+
+/* The automatic prefix cache of the Qwen3-8B engine article (4.4.4).  With max_entries > 0,
+ * every dtd_prefill that starts a new sequence first looks for the longest cached prefix of
+ * its tokens (the whole token list first, then ever shorter prefixes, matched by a hash of
+ * the prefix and then token by token) and takes those positions' KV instead of computing
+ * them: whole KV blocks are shared, a partly filled last block is copied.  The last prompt
+ * position always runs, for its logits.  After the prefill, the sequence's prompt is recorded
+ * as an entry (when the host knows all of its tokens: prefills only, no decode steps before).
+ * Entries hold references to their KV blocks; the least recently used entries are dropped
+ * when more than max_entries exist or when a call needs free blocks.  With the cache on,
+ * dtd_prefill reads its tokens to the host first (it synchronises the stream).  max_entries
+ * 0 turns the cache off and drops every entry.  Host only.  DTD_E_ARG if max_entries < 0. */
+dtd_status dtd_set_prefix_cache(dtd_engine* e, int32_t max_entries);
+
+/* Records positions [0, n) of sequence seq_id as a prefix-cache entry whose tokens are
+ * tokens_host[0, n) (the caller vouches that those are the tokens the positions hold, e.g. a
+ * prompt and the tokens decoded after it).  Host only.  DTD_E_NOSEQ for an unknown seq_id,
+ * DTD_E_ARG for n outside [1, its length], DTD_E_STATE when the cache is off. */
+dtd_status dtd_prefix_cache_add(dtd_engine* e, int64_t seq_id, const int32_t* tokens_host, int32_t n);
+
+/* ---- continuous batching ----------------------------------------------------------------- */
+
+/* A scheduler runs requests through one engine as continuous batches: the scheduling loop of
+ * the Qwen3-8B engine article (4.3.2).  A request is a prompt (host int32 tokens) and a token
+ * budget.  It is admitted, in arrival order, when the KV pool can hold its whole run and the
+ * batch (at most max_batch) has room; its prompt is then prefilled.  Every scheduling step
+ * runs one decode step for all admitted requests together, each at its own position; a
+ * request that has max_new_tokens tokens, or produced stop_token (>= 0), leaves and frees its
+ * KV (recorded in the prefix cache first when that is on), and the next ones join.  Requests
+ * use engine sequence ids below 0; the scheduler assumes it has the engine's sequences and KV
+ * pool to itself.  prompt_budget caps the prompt tokens admitted per step (0 = 4096; at least
+ * one request is admitted).  dtd_sched_destroy first stops the loop and drops unfinished
+ * requests. */
+typedef struct dtd_sched dtd_sched;
+dtd_status dtd_sched_create(dtd_engine* e, int32_t prompt_budget, dtd_sched** out);
+void       dtd_sched_destroy(dtd_sched* s);
+
+/* Queues a request; *id_out gets its id.  sampler NULL = greedy.  Thread-safe.  DTD_E_ARG for
+ * a bad argument or token id, DTD_E_CTX when n + max_new_tokens - 1 positions exceed max_ctx,
+ * DTD_E_KVFULL when the whole pool could not hold the run. */
+dtd_status dtd_sched_submit(dtd_sched* s, const int32_t* prompt_host, int32_t n, int32_t max_new_tokens,
+                            int32_t stop_token, const dtd_sampler* sampler, int64_t* id_out);
+
+/* One scheduling step on the calling thread (admissions, one batched decode step,
+ * departures); *pending (may be NULL) gets the number of queued and running requests after
+ * it.  Returns the first engine error of the step (the requests it hit fail; the others go on;
+ * dtd_sched_last_error has the message).  DTD_E_STATE while the background loop runs. */
+dtd_status dtd_sched_step(dtd_sched* s, int32_t* pending);
+
+/* Runs scheduling steps on a thread of the scheduler's own whenever requests are queued or
+ * running, until dtd_sched_stop.  While it runs, make no other calls on the engine. */
+dtd_status dtd_sched_start(dtd_sched* s);
+dtd_status dtd_sched_stop(dtd_sched* s);
+
+/* Blocks until request id is done or timeout_ms passes (< 0: no limit).  Returns the
+ * request's status (DTD_OK, or the engine error it failed with), DTD_E_STATE on time-out,
+ * DTD_E_NOSEQ for an unknown id.  Thread-safe. */
+dtd_status dtd_sched_wait(dtd_sched* s, int64_t id, int32_t timeout_ms);
+
+/* Copies up to cap of request id's generated tokens to tokens_host; returns how many it has
+ * (or the status it failed with, < 0); *done (may be NULL) = 1 once it has left.  Thread-safe. */
+int32_t dtd_sched_result(dtd_sched* s, int64_t id, int32_t* tokens_host, int32_t cap, int32_t* done);
+
+/* Forgets a finished request.  DTD_E_STATE if it has not finished. */
+dtd_status dtd_sched_release(dtd_sched* s, int64_t id);
+
+/* Message of the scheduler's first failed step (empty if none). */
+const char* dtd_sched_last_error(const dtd_sched* s);
+
 /* Forgets a sequence, as the Qwen3-8B engine article's ResetSeq call does (4.1.2): its KV
  * blocks and its slot return to the free lists, its sampler setting is dropped, and the
  * seq_id may be used again for a new sequence.  Host only (nothing is enqueued; the
@@ -232,6 +302,10 @@ dtd_status dtd_reset_seq(dtd_engine* e, int64_t seq_id);
 
 /* Current length (positions written) of a sequence, or a dtd_status < 0. */
 int32_t dtd_seq_len(const dtd_engine* e, int64_t seq_id);
+
+/* The engine's configuration (its copy of what dtd_create got) and its HIP stream. */
+dtd_status dtd_get_config(const dtd_engine* e, dtd_config* out);
+void*      dtd_get_stream(const dtd_engine* e);
 
 /* Reports what the device flagged since the last check, and synchronises the stream:
  *   - DTD_E_ARG: an earlier prefill or decode step read a token id outside [0, V) (it used
@@ -314,6 +388,12 @@ dtd_status dtd_debug_kernel_timing(dtd_engine* e, int32_t kind, int32_t enable,
  * compute unit, on hip_stream; *gbs gets the timed passes' bytes per second / 1e9.  Needs no
  * engine; on error the message is what dtd_last_error(NULL) returns.  Synchronous. */
 dtd_status dtd_debug_stream_read(const void* buf_dev, int64_t bytes, int32_t reps, void* hip_stream, double* gbs);
+
+/* Positions the last dtd_prefill of seq_id took from the prefix cache (0 for none), free KV
+ * blocks, and prefix-cache entries; or a dtd_status < 0. */
+int32_t dtd_debug_prefix_reused(const dtd_engine* e, int64_t seq_id);
+int32_t dtd_debug_kv_blocks_free(const dtd_engine* e);
+int32_t dtd_debug_prefix_entries(const dtd_engine* e);
 
 /* Schedule selection.  path 0 (default): batch-1 steps run as one persistent kernel per
  * step (every phase in one cooperative launch) when the device allows it, other batches

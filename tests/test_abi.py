@@ -113,3 +113,21 @@ def test_sample_checks_its_arguments_before_any_device_call():
     assert b"sample:" in lib.dtd_last_error(None)
     assert lib.dtd_sample(None, 10, 0, 10, None, None, None, None) == dtd.DTD_E_ARG
     assert lib.dtd_sample(None, 10, 65, 10, None, None, None, None) == dtd.DTD_E_ARG
+
+
+def test_prefix_cache_and_scheduler_calls_check_their_arguments():
+    lib = dtd.load()
+    assert lib.dtd_set_prefix_cache(None, 4) == dtd.DTD_E_ARG
+    assert lib.dtd_prefix_cache_add(None, 1, None, 1) == dtd.DTD_E_ARG
+    cfg = dtd.dtd_config()
+    assert lib.dtd_get_config(None, C.byref(cfg)) == dtd.DTD_E_ARG
+    assert lib.dtd_get_stream(None) is None
+    h = C.c_void_p(1)
+    assert lib.dtd_sched_create(None, 0, C.byref(h)) == dtd.DTD_E_ARG and not h.value
+    rid = C.c_int64()
+    assert lib.dtd_sched_submit(None, None, 1, 1, -1, None, C.byref(rid)) == dtd.DTD_E_ARG
+    assert lib.dtd_sched_step(None, None) == dtd.DTD_E_ARG
+    assert lib.dtd_sched_result(None, 0, None, 0, None) == dtd.DTD_E_ARG
+    assert lib.dtd_sched_wait(None, 0, 0) == dtd.DTD_E_ARG
+    assert lib.dtd_sched_last_error(None) == b"null scheduler"
+    lib.dtd_sched_destroy(None)
