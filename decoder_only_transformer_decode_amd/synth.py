@@ -23,11 +23,11 @@ from typing import Dict, List, Optional
 
 import numpy as np
 
-W_INT8_ROW, W_Q8_0, W_BF16 = 0, 1, 2
+W_INT8_ROW, W_Q8_0, W_BF16, W_Q4_0 = 0, 1, 2, 3
 ACT_F32, ACT_BF16 = 0, 1
 KV_F32, KV_BF16, KV_I8 = 0, 1, 2
 
-WFMT_NAMES = {W_INT8_ROW: "int8-row", W_Q8_0: "q8_0", W_BF16: "bf16"}
+WFMT_NAMES = {W_INT8_ROW: "int8-row", W_Q8_0: "q8_0", W_BF16: "bf16", W_Q4_0: "q4_0"}
 ACT_NAMES = {ACT_F32: "f32", ACT_BF16: "bf16"}
 KV_NAMES = {KV_F32: "f32", KV_BF16: "bf16", KV_I8: "int8+fp16 scale per token and head"}
 
@@ -224,13 +224,47 @@ def encode_q8_0(w: np.ndarray):
     return q, d
 
 
+def encode_q4_0(w: np.ndarray):
+    """Q4_0 ("Go 语言原本" 20.2.4): blocks of 32 columns; d = fp16(m / -8) where m is the
+    block's element of largest magnitude (the first one on ties); q = roundf(w / float(d))
+    + 8 clamped to [0, 15] (d == 0 gives q == 8); byte j of a block's 16 holds q[j] in its
+    low 4 bits and q[j + 16] in its high 4 bits.  Returns codes [rows][cols/2] uint8 and
+    scales [rows][cols/32] fp16."""
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    r, c = w.shape
+    assert c % Q8_BLOCK == 0
+    nb = c // Q8_BLOCK
+    codes = np.empty((r, c // 2), dtype=np.uint8)
+    d = np.empty((r, nb), dtype=np.float16)
+    for r0 in range(0, r, _CHUNK_ROWS):
+        wb = w[r0:r0 + _CHUNK_ROWS].reshape(-1, nb, Q8_BLOCK)
+        m = np.take_along_axis(wb, np.abs(wb).argmax(axis=2)[:, :, None], axis=2)[:, :, 0]
+        d16 = (m / np.float32(-8.0)).astype(np.float32).astype(np.float16)
+        d32 = d16.astype(np.float32)
+        safe = np.where(d32 != 0, d32, np.float32(1.0)).astype(np.float32)
+        y = wb / safe[:, :, None]
+        _round_half_away(y)
+        y += np.float32(8.0)
+        np.clip(y, 0, 15, out=y)
+        y[d32 == 0] = 8
+        q = y.astype(np.uint8)
+        packed = q[:, :, :16] | (q[:, :, 16:] << np.uint8(4))
+        codes[r0:r0 + _CHUNK_ROWS] = packed.reshape(-1, c // 2)
+        d[r0:r0 + _CHUNK_ROWS] = d16
+    return codes, d
+
+
 def encode_matrix(w: np.ndarray, wfmt: int) -> Dict[str, np.ndarray]:
-    """Planar parts as handed to load_weights: '.q' + '.s' (int8-row / Q8_0) or '.w' (bf16)."""
+    """Planar parts as handed to load_weights: '.q' + '.s' (int8-row / Q8_0 / Q4_0) or '.w'
+    (bf16)."""
     if wfmt == W_INT8_ROW:
         q, s = encode_int8_row(w)
         return {"q": q, "s": s}
     if wfmt == W_Q8_0:
         q, d = encode_q8_0(w)
+        return {"q": q, "s": d}
+    if wfmt == W_Q4_0:
+        q, d = encode_q4_0(w)
         return {"q": q, "s": d}
     if wfmt == W_BF16:
         return {"w": f32_to_bf16_bits(w)}

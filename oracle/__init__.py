@@ -15,7 +15,7 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "liboracle.so")
 
-W_INT8_ROW, W_Q8_0, W_BF16 = 0, 1, 2
+W_INT8_ROW, W_Q8_0, W_BF16, W_Q4_0 = 0, 1, 2, 3
 ACT_F32, ACT_BF16 = 0, 1
 KV_F32, KV_BF16, KV_I8 = 0, 1, 2
 
@@ -124,11 +124,16 @@ def rmsnorm(x, g, eps):
     return out
 
 
+def _cols(wfmt, w):
+    """matrix width: Q4_0 codes pack two columns per byte"""
+    return w.shape[1] * 2 if wfmt == W_Q4_0 else w.shape[1]
+
+
 def dequant_row(wfmt, w, s, r):
     w = np.ascontiguousarray(w)
     s = None if s is None else np.ascontiguousarray(s)
-    out = np.empty(w.shape[1], dtype=np.float32)
-    lib().orc_dequant_row(wfmt, _p(w), _p(s), w.shape[1], int(r), _p(out))
+    out = np.empty(_cols(wfmt, w), dtype=np.float32)
+    lib().orc_dequant_row(wfmt, _p(w), _p(s), _cols(wfmt, w), int(r), _p(out))
     return out
 
 
@@ -137,7 +142,7 @@ def gemv(wfmt, w, s, x):
     s = None if s is None else np.ascontiguousarray(s)
     x = _c(x, np.float64)
     out = np.empty(w.shape[0], dtype=np.float64)
-    lib().orc_gemv(wfmt, _p(w), _p(s), w.shape[0], w.shape[1], _p(x), _p(out))
+    lib().orc_gemv(wfmt, _p(w), _p(s), w.shape[0], _cols(wfmt, w), _p(x), _p(out))
     return out
 
 

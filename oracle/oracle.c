@@ -96,6 +96,21 @@ void orc_rmsnorm(const double* x, const float* g, int32_t n, double eps, double*
   for (int32_t i = 0; i < n; i++) out[i] = x[i] * r * (double)g[i];
 }
 
+/* Q4_0 ("Go 语言原本" 20.2.4, quantization: tensors back to bytes): blocks of 32 columns,
+ * 16 bytes of 4-bit codes and one fp16 scale d per block; the low 4 bits of a block's byte j
+ * belong to column j of the block, the high 4 bits to column j + 16; a code q stands for
+ * (q - 8) * d.  Codes are stored [rows][cols/2] bytes, scales [rows][cols/32]. */
+static int32_t q4_0_code(const void* w, int32_t cols, int32_t r, int32_t c) {
+  const uint8_t* row = (const uint8_t*)w + (size_t)r * (cols / 2);
+  const int32_t blk = c / 32, j = c % 32;
+  const uint8_t byte = row[blk * 16 + (j % 16)];
+  return (int32_t)(j < 16 ? (byte & 15) : (byte >> 4)) - 8;
+}
+
+static double q4_0_scale(const void* s, int32_t cols, int32_t r, int32_t c) {
+  return orc_fp16_to_double(((const uint16_t*)s)[(size_t)r * (cols / 32) + c / 32]);
+}
+
 void orc_dequant_row(int32_t wfmt, const void* w, const void* s, int32_t cols, int32_t r,
                      float* out) {
   if (wfmt == ORC_W_INT8_ROW) {
@@ -106,6 +121,8 @@ void orc_dequant_row(int32_t wfmt, const void* w, const void* s, int32_t cols, i
     const int8_t* q = (const int8_t*)w + (size_t)r * cols;
     const uint16_t* d = (const uint16_t*)s + (size_t)r * (cols / 32);
     for (int32_t c = 0; c < cols; c++) out[c] = (float)q[c] * (float)orc_fp16_to_double(d[c / 32]);
+  } else if (wfmt == ORC_W_Q4_0) {
+    for (int32_t c = 0; c < cols; c++) out[c] = (float)q4_0_code(w, cols, r, c) * (float)q4_0_scale(s, cols, r, c);
   } else {
     const uint16_t* b = (const uint16_t*)w + (size_t)r * cols;
     for (int32_t c = 0; c < cols; c++) out[c] = (float)orc_bf16_to_double(b[c]);
@@ -128,6 +145,15 @@ static double row_dot(int32_t wfmt, const void* w, const void* s, int32_t cols, 
       double part = 0.0;
       for (int32_t c = b * 32; c < b * 32 + 32; c++) part += (double)q[c] * x[c];
       acc += orc_fp16_to_double(d[b]) * part;
+    }
+    return acc;
+  }
+  if (wfmt == ORC_W_Q4_0) {
+    double acc = 0.0;
+    for (int32_t b = 0; b < cols / 32; b++) {
+      double part = 0.0;
+      for (int32_t c = b * 32; c < b * 32 + 32; c++) part += (double)q4_0_code(w, cols, r, c) * x[c];
+      acc += q4_0_scale(s, cols, r, b * 32) * part;
     }
     return acc;
   }
@@ -248,7 +274,7 @@ orc_model* orc_create(const orc_cfg* cfg) {
       c->head_dim <= 0 || c->head_dim > 1024 || (c->head_dim % 2) || c->ffn_dim <= 0 || c->vocab <= 0 ||
       (c->n_q_heads % c->n_kv_heads) || c->max_ctx <= 0 || c->max_seqs <= 0)
     return NULL;
-  if (c->wfmt == ORC_W_Q8_0 && ((c->dim % 32) || (c->ffn_dim % 32) ||
+  if ((c->wfmt == ORC_W_Q8_0 || c->wfmt == ORC_W_Q4_0) && ((c->dim % 32) || (c->ffn_dim % 32) ||
                                 ((c->n_q_heads * c->head_dim) % 32)))
     return NULL;
   orc_model* m = (orc_model*)calloc(1, sizeof(orc_model));

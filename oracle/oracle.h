@@ -38,6 +38,7 @@ extern "C" {
 #define ORC_W_INT8_ROW 0
 #define ORC_W_Q8_0     1
 #define ORC_W_BF16     2
+#define ORC_W_Q4_0     3
 #define ORC_ACT_F32    0
 #define ORC_ACT_BF16   1
 #define ORC_KV_F32     0

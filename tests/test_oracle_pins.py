@@ -130,6 +130,54 @@ def test_q8_0_dequant_exact_and_blockwise():
     assert np.all(q[2, 32:64] == 0) and d[2, 1] == 0
 
 
+def _q4_unpack(codes):
+    """Q4_0 codes [rows][cols/2] -> q - 8 [rows][cols], from the page's layout: the low 4
+    bits of a block's byte j are column j of the block, the high 4 bits column j + 16."""
+    r, half = codes.shape
+    blocks = codes.reshape(r, half // 16, 16).astype(np.int64)
+    return np.concatenate([blocks & 15, blocks >> 4], axis=2).reshape(r, half * 2) - 8
+
+
+def test_q4_0_nibble_layout_and_dequant_closed_form():
+    # two blocks; byte j = j | (15 - j) << 4: column j holds code j, column 16 + j code 15 - j
+    byte = np.array([j | ((15 - j) << 4) for j in range(16)], dtype=np.uint8)
+    codes = np.concatenate([byte, byte[::-1]])[None, :]
+    d = np.array([[0.5, -0.25]], dtype=np.float16)
+    got = oracle.dequant_row(oracle.W_Q4_0, codes, d, 0).astype(np.float64)
+    want = [(j - 8) * 0.5 for j in range(16)] + [(7 - j) * 0.5 for j in range(16)]
+    # the second block's bytes run backwards: byte j holds (15 - j) | j << 4
+    want += [(7 - j) * -0.25 for j in range(16)] + [(j - 8) * -0.25 for j in range(16)]
+    assert np.array_equal(got, np.array(want))
+
+
+def test_q4_0_encoder_follows_the_page_rule():
+    w = np.zeros((1, 64), dtype=np.float32)
+    w[0, :32] = np.linspace(-0.5, 0.6, 32)
+    w[0, 7] = 0.75                      # largest magnitude, positive: d = 0.75 / -8 (exact)
+    w[0, 32:] = np.linspace(1.2, -1.0, 32)
+    w[0, 40] = -1.5                     # largest magnitude, negative: d = 0.1875
+    w[0, 41] = 1.5                      # the same magnitude after it: +8 steps clamps to +7
+    codes, d = synth.encode_q4_0(w)
+    assert codes.shape == (1, 32) and d.shape == (1, 2) and d.dtype == np.float16
+    assert float(d[0, 0]) == -0.09375 and float(d[0, 1]) == 0.1875
+    got = oracle.dequant_row(oracle.W_Q4_0, codes, d, 0)
+    assert got[7] == np.float32(0.75) and got[40] == np.float32(-1.5)
+    assert got[41] == np.float32(7 * 0.1875)
+    err = np.abs(got.astype(np.float64) - w[0])
+    step = np.repeat(np.abs(d[0].astype(np.float64)), 32)
+    ok = np.ones(64, bool)
+    ok[41] = False
+    assert np.all(err[ok] <= step[ok] / 2 + 1e-12)
+    # an all-zero block: scale 0, every code 8
+    z = np.zeros((2, 32), dtype=np.float32)
+    cz, dz = synth.encode_q4_0(z)
+    assert np.all(cz == 0x88) and np.all(dz == 0)
+    # bytes on the device: 16 of codes + 2 of scale per 32 weights
+    big = np.random.default_rng(0).standard_normal((3, 96)).astype(np.float32)
+    c3, d3 = synth.encode_q4_0(big)
+    assert c3.nbytes + d3.nbytes == 3 * (96 // 32) * 18
+
+
 def test_quant_bytes_page_figures():
     g = _gold("page_figures.json")
     qb = g["quant_bytes"]
@@ -148,9 +196,12 @@ def test_gemv_matches_float64_matmul_all_formats():
     rng = np.random.default_rng(5)
     w = (rng.standard_normal((33, 160)) * 0.02).astype(np.float32)
     x = rng.standard_normal(160)
-    for fmt in (oracle.W_INT8_ROW, oracle.W_Q8_0, oracle.W_BF16):
+    for fmt in (oracle.W_INT8_ROW, oracle.W_Q8_0, oracle.W_BF16, oracle.W_Q4_0):
         parts = synth.encode_matrix(w, fmt)
-        if fmt == oracle.W_INT8_ROW:
+        if fmt == oracle.W_Q4_0:
+            W = _q4_unpack(parts["q"]).astype(np.float64) * np.repeat(parts["s"].astype(np.float64), 32, axis=1)
+            got = oracle.gemv(fmt, parts["q"], parts["s"], x)
+        elif fmt == oracle.W_INT8_ROW:
             W = parts["q"].astype(np.float64) * parts["s"].astype(np.float64)[:, None]
             got = oracle.gemv(fmt, parts["q"], parts["s"], x)
         elif fmt == oracle.W_Q8_0:
@@ -516,6 +567,9 @@ def _torch_forward(shape, weights, tokens):
 
     def deq(name):
         p = weights[name]
+        if "s" in p and p["q"].dtype == np.uint8:      # Q4_0
+            return torch.from_numpy(_q4_unpack(p["q"]).astype(np.float64) *
+                                    np.repeat(p["s"].astype(np.float64), 32, axis=1))
         if "s" in p and p["s"].dtype == np.float32:
             return torch.from_numpy(p["q"].astype(np.float64) * p["s"].astype(np.float64)[:, None])
         if "s" in p:
@@ -586,6 +640,8 @@ _FORWARD_FORMATS = [
     dict(wfmt=synth.W_Q8_0, tied=True),
     dict(wfmt=synth.W_BF16),
     dict(wfmt=synth.W_Q8_0, act=synth.ACT_BF16, kvfmt=synth.KV_I8, n_kv_heads=1),
+    dict(wfmt=synth.W_Q4_0),                                                  # 4-bit weights
+    dict(wfmt=synth.W_Q4_0, act=synth.ACT_BF16, kvfmt=synth.KV_BF16, tied=True),
 ]
 
 
