@@ -12,6 +12,7 @@ Prints one JSON line (rank 0).  Runs on one GPU only.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import json
 import os
 import sys
@@ -35,6 +36,8 @@ def weight_bytes(s: synth.ModelShape) -> dict:
             return r * c * 2
         if s.wfmt == synth.W_INT8_ROW:
             return r * c + r * 4
+        if s.wfmt == synth.W_Q4_0:
+            return r * c // 2 + r * (c // 32) * 2
         return r * c + r * (c // 32) * 2
     per_layer = {
         "qkv": mat(s.q_dim + 2 * s.kv_dim, s.dim),
@@ -162,8 +165,14 @@ def main():
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only copy MIB MiB device to device 3 times and exit: the plain copy whose "
                          "FETCH_SIZE / WRITE_SIZE counter readings scale the step kernel's")
+    ap.add_argument("--weights", choices=sorted(synth.WFMT_NAMES.values()), default=None,
+                    help="store the workload's matrices in this format instead of its own")
     ap.add_argument("--path", choices=["auto", "per-kernel", "persistent"], default="auto",
                     help="schedule: auto (persistent step kernel at batch 1), or force one")
+    ap.add_argument("--serve", type=int, default=0, metavar="N",
+                    help="instead of the decode step: N requests through the continuous-batching "
+                         "scheduler (qwen3-8b-shaped unless --workload names another batched shape), "
+                         "with the prefix cache off and then on; prints one JSON line")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this decode step runs on a single MI355X and has no "
@@ -181,7 +190,13 @@ def main():
         print(json.dumps({"copy_probe_bytes": n, "copies": 3}), flush=True)
         return
     w = synth.BY_NAME[args.workload]
+    if args.weights:
+        fmt = {v: k for k, v in synth.WFMT_NAMES.items()}[args.weights]
+        w = dataclasses.replace(w, shape=w.shape.replace(wfmt=fmt))
     s = w.shape
+    if args.serve:
+        bench_serve(args, w if w.batch != 1 else synth.QWEN3_8B)
+        return
     if w.batch != 1:
         bench_batched(args, w)
         return
@@ -340,6 +355,78 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "sampling": sampling,
+    }
+    eng.close()
+    print(json.dumps(rec), flush=True)
+
+
+def bench_serve(args, w: synth.Workload):
+    """Continuous batching: N requests, all sharing a 256-token system prefix, each with its
+    own user part (32..480 tokens) and answer budget (32..256 tokens), submitted at once to
+    the scheduler (batches of up to 64); greedy decoding.  Runs twice, prefix cache off and
+    on; value = generated tokens/s with the cache on.  Both runs must produce the same tokens
+    wherever no near tie parts them (counted, reported)."""
+    import torch
+    s = w.shape
+    N, B, ctx = args.serve, 64, 2048
+    rng = np.random.default_rng(11)
+    system = synth.prompt_tokens(s.vocab, 256, seed=500)
+    reqs = []
+    for i in range(N):
+        user = synth.prompt_tokens(s.vocab, int(rng.integers(32, 481)), seed=1000 + i)
+        reqs.append((np.concatenate([system, user]).astype(np.int32), int(rng.integers(32, 257))))
+    t0 = time.perf_counter()
+    weights = synth.gen_weights(s, synth.weights_seed(w))
+    print(f"[bench] weights generated in {time.perf_counter() - t0:.1f} s", file=sys.stderr, flush=True)
+    torch.cuda.set_device(0)
+    eng = dtd.Engine(s, max_ctx=ctx, max_seqs=B, max_batch=B, kv_block_size=16,
+                     kv_num_blocks=B * (ctx // 16))
+    eng.load_weights(synth.flat_tensors(weights))
+    runs = {}
+    outs = {}
+    for cache in (0, B):
+        eng.set_prefix_cache(cache)
+        sch = dtd.Scheduler(eng)
+        # warmup: a few requests through the same paths, then a clean cache
+        for p, m in reqs[:4]:
+            sch.submit(p[:300], 8)
+        sch.run()
+        eng.set_prefix_cache(0)
+        eng.set_prefix_cache(cache)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        ids = [sch.submit(p, m) for p, m in reqs]
+        steps = sch.run()
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
+        toks = [sch.result(r)[0] for r in ids]
+        gen = sum(len(t) for t in toks)
+        runs[cache] = {"seconds": round(dt, 3), "generated_tokens": gen,
+                       "generated_tokens_per_s": round(gen / dt, 1),
+                       "prompt_tokens": int(sum(len(p) for p, _ in reqs)), "scheduling_steps": steps,
+                       "mean_decode_batch": round((gen - N) / max(steps, 1), 2)}
+        outs[cache] = toks
+        sch.close()
+        print(f"[bench] prefix cache {'on' if cache else 'off'}: {runs[cache]}", file=sys.stderr, flush=True)
+    same = sum(int(a == b) for a, b in zip(outs[0], outs[B]))
+    on, off = runs[B], runs[0]
+    rec = {
+        "metric": "continuous-batching serving throughput (generated tokens/s), 1 GPU",
+        "value": on["generated_tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "higher_is_better": True,
+        "vs_baseline": None,
+        "dtype": f"{synth.WFMT_NAMES[s.wfmt]} weights x {synth.ACT_NAMES[s.act]} activations, "
+                 f"{synth.KV_NAMES[s.kvfmt]} KV, fp32 accumulation",
+        "data": "synthetic",
+        "config": {"workload": f"{s.name} serving: {N} requests submitted at once, a shared 256-token system "
+                               f"prefix + a 32..480-token user part each, 32..256 greedy tokens each, "
+                               f"batches of up to {B}, max context {ctx}",
+                   "requests": N, "max_batch": B},
+        "prefix_cache_on": on,
+        "prefix_cache_off": off,
+        "requests_with_identical_tokens_both_runs": same,
     }
     eng.close()
     print(json.dumps(rec), flush=True)

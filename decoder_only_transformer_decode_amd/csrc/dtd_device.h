@@ -140,9 +140,16 @@ __device__ __forceinline__ float block_max(float v, float* red) {
   return s;
 }
 
-// one stored weight element as fp32: int8-row q*s, Q8_0 q*d (one fp32 product), bf16 widen
+// one stored weight element as fp32: int8-row q*s, Q8_0 q*d, Q4_0 (q-8)*d (one fp32 product;
+// a Q4_0 block's byte j holds column j in its low 4 bits and column j+16 in its high 4 bits),
+// bf16 widen
 __device__ __forceinline__ float deq_elem(const MatDev& m, int wfmt, int r, int c) {
   const size_t e = (size_t)r * m.cols + c;
+  if (wfmt == W_Q4_0) {
+    const uint8_t byte = ((const uint8_t*)m.w)[(size_t)r * (m.cols / 2) + (c / 32) * 16 + (c % 16)];
+    const int q = (c % 32) < 16 ? (byte & 15) : (byte >> 4);
+    return (float)(q - 8) * f16_to_f32(((const uint16_t*)m.s)[(size_t)r * (m.cols / 32) + c / 32]);
+  }
   if (wfmt == W_INT8_ROW) return (float)((const int8_t*)m.w)[e] * ((const float*)m.s)[r];
   if (wfmt == W_Q8_0)
     return (float)((const int8_t*)m.w)[e] *

@@ -186,7 +186,7 @@ static dtd_status fail(dtd_engine* e, dtd_status st, const char* fmt, ...) {
     }                                                                                 \
   } while (0)
 
-static int vec_elems(int wfmt) { return wfmt == DTD_W_BF16 ? 8 : 16; }
+static int vec_elems(int wfmt) { return wfmt == DTD_W_BF16 ? 8 : (wfmt == DTD_W_Q4_0 ? 32 : 16); }
 
 static dtd_status check_config(const dtd_config* c, char* msg, int32_t msg_len) {
   auto bad = [&](dtd_status st, const char* fmt, auto... args) {
@@ -199,7 +199,7 @@ static dtd_status check_config(const dtd_config* c, char* msg, int32_t msg_len) 
       c->head_dim <= 0 || c->ffn_dim <= 0 || c->vocab <= 0)
     return bad(DTD_E_ARG, "%s", "dimensions must be positive");
   if (c->n_q_heads % c->n_kv_heads) return bad(DTD_E_ARG, "n_kv_heads %d does not divide n_q_heads %d", c->n_kv_heads, c->n_q_heads);
-  if (c->wfmt < 0 || c->wfmt > 2 || c->act < 0 || c->act > 1 || c->kvfmt < 0 || c->kvfmt > 2)
+  if (c->wfmt < 0 || c->wfmt > 3 || c->act < 0 || c->act > 1 || c->kvfmt < 0 || c->kvfmt > 2)
     return bad(DTD_E_ARG, "%s", "unknown weight, activation or KV format");
   if (!(c->rms_eps >= 0.f) || !(c->rope_theta > 0.f)) return bad(DTD_E_ARG, "%s", "rms_eps must be >= 0 and rope_theta > 0");
   if (c->kv_block_size <= 0 || c->kv_block_size > 4096 || c->kv_num_blocks <= 0 || c->max_seqs <= 0 ||
@@ -214,8 +214,8 @@ static dtd_status check_config(const dtd_config* c, char* msg, int32_t msg_len) 
   const int v = vec_elems(c->wfmt);
   if (c->dim % v || c->ffn_dim % v || qd % v)
     return bad(DTD_E_UNSUPPORTED, "dim, ffn_dim and n_q_heads*head_dim must be multiples of %d", v);
-  if (c->wfmt == DTD_W_Q8_0 && (c->dim % 32 || c->ffn_dim % 32 || qd % 32))
-    return bad(DTD_E_ARG, "%s", "Q8_0 needs every matrix width to be a multiple of 32");
+  if ((c->wfmt == DTD_W_Q8_0 || c->wfmt == DTD_W_Q4_0) && (c->dim % 32 || c->ffn_dim % 32 || qd % 32))
+    return bad(DTD_E_ARG, "%s", "Q8_0 and Q4_0 need every matrix width to be a multiple of 32");
   if ((int64_t)c->max_ctx * c->kv_block_size > (int64_t)1 << 40) return bad(DTD_E_ARG, "%s", "max_ctx too large");
   if (msg && msg_len > 0) msg[0] = 0;
   return DTD_OK;
@@ -236,7 +236,7 @@ static std::vector<dtd_tensor_spec> expected_parts(const dtd_config* c) {
     if (c->wfmt == DTD_W_BF16) {
       add(base + ".w", rows, cols, 2, (int64_t)rows * cols * 2);
     } else {
-      add(base + ".q", rows, cols, 1, (int64_t)rows * cols);
+      add(base + ".q", rows, cols, 1, (int64_t)rows * cols / (c->wfmt == DTD_W_Q4_0 ? 2 : 1));
       if (c->wfmt == DTD_W_INT8_ROW) add(base + ".s", rows, 1, 4, (int64_t)rows * 4);
       else add(base + ".s", rows, cols / 32, 2, (int64_t)rows * (cols / 32) * 2);
     }
@@ -444,7 +444,9 @@ extern "C" dtd_status dtd_create(const dtd_config* cfg, void* hip_stream, dtd_en
     }
     e->p_nch = (cfg->max_ctx + kAttnTile - 1) / kAttnTile;
     e->p_smem = persistent_smem_bytes(d, e->p_nch, cus > 0 ? cus : 1);
-    if (coop && cus > 0 && persistent_supports(d) && persistent_prepare(d, e->p_smem, &per_cu) == hipSuccess &&
+    // the batch-1 step kernel is built for int8-row, Q8_0 and bf16 weights; Q4_0 runs the
+    // per-sub-step kernels at every batch size
+    if (coop && cus > 0 && d.wfmt != W_Q4_0 && persistent_supports(d) && persistent_prepare(d, e->p_smem, &per_cu) == hipSuccess &&
         per_cu >= 1) {
       e->persist_ok = true;
       e->nwg = cus;
@@ -523,8 +525,8 @@ static dtd_status upload_packed(dtd_engine* e, const std::vector<SrcMat>& mats,
   const int wfmt = e->cfg.wfmt;
   const int rows = (int)rowmap.size();
   const size_t eb = wfmt == DTD_W_BF16 ? 2 : 1;
-  const size_t wrow = (size_t)cols * eb;
-  const size_t srow = wfmt == DTD_W_INT8_ROW ? 4 : (wfmt == DTD_W_Q8_0 ? (size_t)(cols / 32) * 2 : 0);
+  const size_t wrow = wfmt == DTD_W_Q4_0 ? (size_t)cols / 2 : (size_t)cols * eb;
+  const size_t srow = wfmt == DTD_W_INT8_ROW ? 4 : (wfmt == DTD_W_BF16 ? 0 : (size_t)(cols / 32) * 2);
   std::vector<uint8_t> wbuf((size_t)rows * wrow), sbuf((size_t)rows * srow);
   for (int r = 0; r < rows; r++) {
     const SrcMat& m = mats[(size_t)rowmap[(size_t)r].first];
@@ -1670,7 +1672,7 @@ extern "C" int32_t dtd_debug_uses_persistent(const dtd_engine* e, int32_t batch)
 
 extern "C" int32_t dtd_debug_step_kernel_shape(const dtd_engine* e) {
   if (!e) return DTD_E_ARG;
-  return persistent_fixed_shape(e->d) ? 128 : 0;
+  return e->persist_ok && persistent_fixed_shape(e->d) ? 128 : 0;
 }
 
 extern "C" dtd_status dtd_debug_stream_read(const void* buf_dev, int64_t bytes, int32_t reps, void* hip_stream,

@@ -16,7 +16,7 @@ constexpr int kPersistWaves = 8;   // waves per workgroup of the persistent step
 constexpr int kErrToken = 1;       // device error bits: token id out of range
 constexpr int kErrBarrier = 2;     //                    a cross-workgroup wait timed out
 
-enum WFmt { W_INT8_ROW = 0, W_Q8_0 = 1, W_BF16 = 2 };
+enum WFmt { W_INT8_ROW = 0, W_Q8_0 = 1, W_BF16 = 2, W_Q4_0 = 3 };
 enum Act { ACT_F32 = 0, ACT_BF16 = 1 };
 enum KvFmt { KV_F32 = 0, KV_BF16 = 1, KV_I8 = 2 };
 enum Epi { EPI_QKV = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_LOGITS = 3 };

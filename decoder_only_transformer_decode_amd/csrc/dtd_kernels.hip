@@ -88,6 +88,8 @@ struct GemvArgs {
 
 template <int WFMT> struct WVec { static constexpr int VEC = 16; static constexpr int EB = 1; };
 template <> struct WVec<W_BF16> { static constexpr int VEC = 8; static constexpr int EB = 2; };
+// Q4_0: one 16-byte piece is one whole 32-column block (addressed in bytes as k / 2)
+template <> struct WVec<W_Q4_0> { static constexpr int VEC = 32; static constexpr int EB = 1; };
 
 template <int EPI, int ROWS>
 __device__ __forceinline__ void gemv_epilogue(const GemvArgs& a, int b, int row0, const float* v) {
@@ -163,7 +165,7 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
   const int nb = min(NB, a.B - b0);
   const int KCP = a.kc;
   const uint8_t* wbase = (const uint8_t*)a.m.w;
-  const size_t row_bytes = (size_t)K * EB;
+  const size_t row_bytes = WFMT == W_Q4_0 ? (size_t)K / 2 : (size_t)K * EB;
 
   float acc[ROWS][NB];
 #pragma unroll
@@ -171,10 +173,76 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
 #pragma unroll
     for (int bb = 0; bb < NB; bb++) acc[i][bb] = 0.f;
 
+  // one k-step's weights: ROWS 16-byte pieces per lane (and their Q8_0 / Q4_0 block scales)
+  auto load_w = [&](uint4 (&wv)[ROWS], float (&qs)[ROWS], int kc0, int kcn, int ks) {
+    const int kl = ks + lane * VEC;
+    const bool kvalid = kl < kcn;
+    const int k = kc0 + kl;
+#pragma unroll
+    for (int i = 0; i < ROWS; i++) {
+      const int r = row0 + i;
+      const bool ok = kvalid && r < N;
+      wv[i] = ok ? *(const uint4*)(wbase + (size_t)r * row_bytes + (WFMT == W_Q4_0 ? (size_t)k / 2 : (size_t)k * EB))
+                 : make_uint4(0u, 0u, 0u, 0u);
+      qs[i] = 0.f;
+      if constexpr (WFMT == W_Q8_0 || WFMT == W_Q4_0)
+        qs[i] = ok ? f16_to_f32(((const uint16_t*)a.m.s)[(size_t)r * (K / 32) + (k >> 5)]) : 0.f;
+    }
+  };
+  // one k-step's multiply-adds against the staged activations
+  auto dot_w = [&](const uint4 (&wv)[ROWS], const float (&qs)[ROWS], int ks) {
+#pragma unroll
+    for (int bb = 0; bb < NB; bb++) {
+      float xv[VEC];
+      const float4* xp = (const float4*)(xs + bb * KCP + ks) + lane;
+#pragma unroll
+      for (int jj = 0; jj < VEC / 4; jj++) {
+        const float4 t = xp[jj * 64];
+        xv[4 * jj + 0] = t.x; xv[4 * jj + 1] = t.y; xv[4 * jj + 2] = t.z; xv[4 * jj + 3] = t.w;
+      }
+#pragma unroll
+      for (int i = 0; i < ROWS; i++) {
+        const uint32_t u[4] = {wv[i].x, wv[i].y, wv[i].z, wv[i].w};
+        if constexpr (WFMT == W_BF16) {
+          float s = acc[i][bb];
+#pragma unroll
+          for (int q = 0; q < 4; q++) {
+            s += __uint_as_float(u[q] << 16) * xv[2 * q];
+            s += __uint_as_float(u[q] & 0xffff0000u) * xv[2 * q + 1];
+          }
+          acc[i][bb] = s;
+        } else if constexpr (WFMT == W_Q4_0) {
+          // byte b of the block: column b in the low 4 bits, column b + 16 in the high 4
+          float s = 0.f;
+#pragma unroll
+          for (int q = 0; q < 4; q++)
+#pragma unroll
+            for (int by = 0; by < 4; by++) {
+              const uint32_t byte = (u[q] >> (8 * by)) & 0xffu;
+              s += (float)((int)(byte & 15u) - 8) * xv[4 * q + by];
+              s += (float)((int)(byte >> 4) - 8) * xv[16 + 4 * q + by];
+            }
+          acc[i][bb] += qs[i] * s;
+        } else {
+          float s = 0.f;
+#pragma unroll
+          for (int q = 0; q < 4; q++)
+#pragma unroll
+            for (int by = 0; by < 4; by++) s += sext8(u[q], by) * xv[4 * q + by];
+          if constexpr (WFMT == W_Q8_0) acc[i][bb] += qs[i] * s;
+          else acc[i][bb] += s;
+        }
+      }
+    }
+  };
+
+  uint4 wa[ROWS], wb[ROWS];
+  float qa[ROWS], qb[ROWS];
   for (int kc0 = 0; kc0 < K; kc0 += KCP) {
     const int kcn = min(KCP, K - kc0);
     const int kcpad = (kcn + KSTEP - 1) / KSTEP * KSTEP;
     if (kc0) __syncthreads();
+    load_w(wa, qa, kc0, kcn, 0);     // the chunk's first weights are in flight while x is staged
     for (int idx = threadIdx.x; idx < NB * kcpad; idx += 256) {
       const int bb = idx / kcpad, kk = idx - bb * kcpad;
       float v = 0.f;
@@ -188,52 +256,13 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
     }
     __syncthreads();
 
-    for (int ks = 0; ks < kcn; ks += KSTEP) {
-      const int kl = ks + lane * VEC;
-      const bool kvalid = kl < kcn;
-      const int k = kc0 + kl;
-      uint4 wv[ROWS];
-      float qs[ROWS];
-#pragma unroll
-      for (int i = 0; i < ROWS; i++) {
-        const int r = row0 + i;
-        const bool ok = kvalid && r < N;
-        wv[i] = ok ? *(const uint4*)(wbase + (size_t)r * row_bytes + (size_t)k * EB)
-                   : make_uint4(0u, 0u, 0u, 0u);
-        if constexpr (WFMT == W_Q8_0)
-          qs[i] = ok ? f16_to_f32(((const uint16_t*)a.m.s)[(size_t)r * (K / 32) + (k >> 5)]) : 0.f;
-      }
-#pragma unroll
-      for (int bb = 0; bb < NB; bb++) {
-        float xv[VEC];
-        const float4* xp = (const float4*)(xs + bb * KCP + ks) + lane;
-#pragma unroll
-        for (int jj = 0; jj < VEC / 4; jj++) {
-          const float4 t = xp[jj * 64];
-          xv[4 * jj + 0] = t.x; xv[4 * jj + 1] = t.y; xv[4 * jj + 2] = t.z; xv[4 * jj + 3] = t.w;
-        }
-#pragma unroll
-        for (int i = 0; i < ROWS; i++) {
-          const uint32_t u[4] = {wv[i].x, wv[i].y, wv[i].z, wv[i].w};
-          if constexpr (WFMT == W_BF16) {
-            float s = acc[i][bb];
-#pragma unroll
-            for (int q = 0; q < 4; q++) {
-              s += __uint_as_float(u[q] << 16) * xv[2 * q];
-              s += __uint_as_float(u[q] & 0xffff0000u) * xv[2 * q + 1];
-            }
-            acc[i][bb] = s;
-          } else {
-            float s = 0.f;
-#pragma unroll
-            for (int q = 0; q < 4; q++)
-#pragma unroll
-              for (int by = 0; by < 4; by++) s += sext8(u[q], by) * xv[4 * q + by];
-            if constexpr (WFMT == W_Q8_0) acc[i][bb] += qs[i] * s;
-            else acc[i][bb] += s;
-          }
-        }
-      }
+    // two k-steps per trip, the next step's weights always one step ahead
+    for (int ks = 0; ks < kcn; ks += 2 * KSTEP) {
+      if (ks + KSTEP < kcn) load_w(wb, qb, kc0, kcn, ks + KSTEP);
+      dot_w(wa, qa, ks);
+      if (ks + KSTEP >= kcn) break;
+      if (ks + 2 * KSTEP < kcn) load_w(wa, qa, kc0, kcn, ks + 2 * KSTEP);
+      dot_w(wb, qb, ks + KSTEP);
     }
   }
 
@@ -962,6 +991,13 @@ __global__ __launch_bounds__(256) void k_kv_fill(Dims d, KvLayer kv, const int32
 
 template <int WFMT, int EPI>
 hipError_t gemv_dispatch(const GemvArgs& a, int NB, int ROWS, dim3 grid, size_t smem, hipStream_t st) {
+  if constexpr (WFMT == W_Q4_0) {
+    // one 16-byte load covers 32 columns: eight rows per wave keep enough bytes in flight
+    if (NB == 1 && ROWS == 8) {
+      hipLaunchKernelGGL((k_gemv<WFMT, EPI, 1, 8>), grid, dim3(256), smem, st, a);
+      return hipGetLastError();
+    }
+  }
   if (NB == 1 && ROWS == 2) hipLaunchKernelGGL((k_gemv<WFMT, EPI, 1, 2>), grid, dim3(256), smem, st, a);
   else if (NB == 1 && ROWS == 4) hipLaunchKernelGGL((k_gemv<WFMT, EPI, 1, 4>), grid, dim3(256), smem, st, a);
   else if (NB == 4 && ROWS == 2) hipLaunchKernelGGL((k_gemv<WFMT, EPI, 4, 2>), grid, dim3(256), smem, st, a);
@@ -1085,8 +1121,8 @@ hipError_t launch_gemv(const Dims& d, const MatDev& m, const void* xin, int B, i
   a.act_in = d.act;
   a.ea = ea;
   const int NB = B == 1 ? 1 : 4;
-  const int ROWS = m.rows >= 4 * 16 * 256 ? 4 : 2;
-  const int VEC = d.wfmt == W_BF16 ? 8 : 16, KSTEP = 64 * VEC;
+  const int ROWS = (d.wfmt == W_Q4_0 && B == 1 && m.rows >= 8 * 4 * 256) ? 8 : (m.rows >= 4 * 16 * 256 ? 4 : 2);
+  const int VEC = d.wfmt == W_BF16 ? 8 : (d.wfmt == W_Q4_0 ? 32 : 16), KSTEP = 64 * VEC;
   const int budget_floats = 16384;  // 64 KiB of LDS
   int kc = (budget_floats / NB) / KSTEP * KSTEP;
   const int kpad = (m.cols + KSTEP - 1) / KSTEP * KSTEP;
@@ -1097,6 +1133,7 @@ hipError_t launch_gemv(const Dims& d, const MatDev& m, const void* xin, int B, i
   switch (d.wfmt) {
     case W_INT8_ROW: return gemv_epi<W_INT8_ROW>(a, epi, NB, ROWS, grid, smem, st);
     case W_Q8_0: return gemv_epi<W_Q8_0>(a, epi, NB, ROWS, grid, smem, st);
+    case W_Q4_0: return gemv_epi<W_Q4_0>(a, epi, NB, ROWS, grid, smem, st);
     default: return gemv_epi<W_BF16>(a, epi, NB, ROWS, grid, smem, st);
   }
 }

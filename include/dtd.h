@@ -52,8 +52,12 @@ typedef enum {
  *             ("从 smollm3.go 看 LLM inference", int8 weight-only quantization);
  *   Q8_0:     int8 codes [rows][cols] + one fp16 scale per run of 32 columns
  *             [rows][cols/32] ("Go 语言原本" 20.2.4);
- *   BF16:     bf16 bit patterns [rows][cols]. */
-enum { DTD_W_INT8_ROW = 0, DTD_W_Q8_0 = 1, DTD_W_BF16 = 2 };
+ *   BF16:     bf16 bit patterns [rows][cols];
+ *   Q4_0:     4-bit codes in blocks of 32 columns, 16 bytes per block [rows][cols/2] (byte j
+ *             of a block: column j in the low 4 bits, column j+16 in the high 4 bits), plus
+ *             one fp16 scale per block [rows][cols/32]; W = (q - 8) * d ("Go 语言原本" 20.2.4).
+ *             The batch-1 step kernel does not take it: Q4_0 runs the per-sub-step kernels. */
+enum { DTD_W_INT8_ROW = 0, DTD_W_Q8_0 = 1, DTD_W_BF16 = 2, DTD_W_Q4_0 = 3 };
 /* activation storage type at the rounding points: each RMSNorm output, the attention
  * output and the SwiGLU output.  The residual stream, queries, scores, softmax,
  * accumulators and logits are fp32 in every configuration. */
@@ -407,7 +411,8 @@ int32_t dtd_debug_uses_persistent(const dtd_engine* e, int32_t batch);
 /* The head size the batch-1 step kernel of this engine has fixed at compile time: 128 when
  * the model has head size 128, 4 query heads per KV head and KV blocks of 16 positions (the
  * instantiation built for that shape, whose probe variant dtd_debug_decode_probe then runs
- * too), or 0 when the kernel reads the shape at run time.  A dtd_status < 0 for a null
+ * too), or 0 when the kernel reads the shape at run time or the engine has no step kernel
+ * (Q4_0 weights, or a device without cooperative launches).  A dtd_status < 0 for a null
  * engine. */
 int32_t dtd_debug_step_kernel_shape(const dtd_engine* e);
 
