@@ -69,6 +69,8 @@ def lib():
         L.orc_set_tensor.argtypes, L.orc_set_tensor.restype = [P, C.c_char_p, P, P], I32
         L.orc_ready.argtypes, L.orc_ready.restype = [P], I32
         L.orc_step.argtypes, L.orc_step.restype = [P, I32, I32, I32, P, P, P], I32
+        L.orc_step_kept.argtypes, L.orc_step_kept.restype = [P, I32, I32, I32, P, I32, P, P], I32
+        L.orc_attention_kept.argtypes, L.orc_attention_kept.restype = [P, I32, I32, I32, I32, P, P, P, P, P], None
         L.orc_trace_len.argtypes, L.orc_trace_len.restype = [P], I32
         L.orc_kv_write.argtypes, L.orc_kv_write.restype = [P, I32, I32, I32, I32, P, P, P, P], I32
         L.orc_kv_read.argtypes, L.orc_kv_read.restype = [P, I32, I32, I32, I32, P, P], I32
@@ -134,6 +136,17 @@ def dequant_row(wfmt, w, s, r):
     s = None if s is None else np.ascontiguousarray(s)
     out = np.empty(_cols(wfmt, w), dtype=np.float32)
     lib().orc_dequant_row(wfmt, _p(w), _p(s), _cols(wfmt, w), int(r), _p(out))
+    return out
+
+
+def attention_kept(q, hkv, K, V, keep, prob=None):
+    """q [hq][d]; K, V [n][hkv][d]; keep [n] -> out [hq][d] (prob [n] accumulated in place)"""
+    q = _c(q, np.float64); K = _c(K, np.float64); V = _c(V, np.float64)
+    keep = np.ascontiguousarray(keep, dtype=np.uint8)
+    hq, d = q.shape
+    out = np.empty((hq, d), dtype=np.float64)
+    lib().orc_attention_kept(_p(q), hq, hkv, d, K.shape[0], _p(K), _p(V), _p(keep), _p(out),
+                             _p(prob) if prob is not None else None)
     return out
 
 
@@ -240,6 +253,19 @@ class Model:
         if want_trace:
             return nxt, logits, hidden, trace
         return nxt, logits, hidden
+
+    def step_kept(self, seq: int, token: int, pos: int, keep, score_layers: int, scores):
+        """orc_step over the kept positions (keep: bool/uint8 [pos + 1]); adds the attention
+        probabilities of the last score_layers layers to scores (float64 [pos + 1], in place).
+        Returns (next token, logits)."""
+        keep = np.ascontiguousarray(keep, dtype=np.uint8)
+        assert keep.size == pos + 1 and scores.dtype == np.float64 and scores.size >= pos + 1
+        logits = np.empty(self.shape.vocab, dtype=np.float32)
+        nxt = lib().orc_step_kept(self._h, int(seq), int(token), int(pos), _p(keep), int(score_layers),
+                                  _p(scores), _p(logits))
+        if nxt < 0:
+            raise RuntimeError(f"orc_step_kept failed: {nxt}")
+        return nxt, logits
 
     def trace_fields(self):
         """(name, offset, length) of each field of a trace record."""

@@ -211,6 +211,46 @@ void orc_attention(const double* q, int32_t hq, int32_t hkv, int32_t d, int32_t 
   }
 }
 
+/* attention over the positions t < n_pos with keep[t] != 0; prob (may be NULL) gets each
+ * attended position's softmax probability added, summed over the query heads */
+void orc_attention_kept(const double* q, int32_t hq, int32_t hkv, int32_t d, int32_t n_pos,
+                        const double* K, const double* V, const uint8_t* keep, double* out,
+                        double* prob) {
+  int32_t G = hq / hkv;
+  double scale = 1.0 / sqrt((double)d);
+  double* p = (double*)malloc(sizeof(double) * (size_t)hq * (size_t)(n_pos > 0 ? n_pos : 1));
+#pragma omp parallel for schedule(static)
+  for (int32_t h = 0; h < hq; h++) {
+    int32_t j = h / G;
+    double* sc = p + (size_t)h * n_pos;
+    double m = -INFINITY;
+    for (int32_t t = 0; t < n_pos; t++) {
+      if (!keep[t]) continue;
+      const double* k = K + ((size_t)t * hkv + j) * d;
+      double dot = 0.0;
+      for (int32_t i = 0; i < d; i++) dot += q[(size_t)h * d + i] * k[i];
+      sc[t] = dot * scale;
+      if (sc[t] > m) m = sc[t];
+    }
+    double sum = 0.0;
+    for (int32_t t = 0; t < n_pos; t++) {
+      sc[t] = keep[t] ? exp(sc[t] - m) : 0.0;
+      sum += sc[t];
+    }
+    for (int32_t t = 0; t < n_pos; t++) sc[t] /= sum;
+    for (int32_t i = 0; i < d; i++) {
+      double o = 0.0;
+      for (int32_t t = 0; t < n_pos; t++)
+        if (keep[t]) o += sc[t] * V[((size_t)t * hkv + j) * d + i];
+      out[(size_t)h * d + i] = o;
+    }
+  }
+  if (prob)
+    for (int32_t h = 0; h < hq; h++)
+      for (int32_t t = 0; t < n_pos; t++) prob[t] += p[(size_t)h * n_pos + t];
+  free(p);
+}
+
 double orc_silu(double z) { return z / (1.0 + exp(-z)); }
 
 int32_t orc_argmax_f32(const float* v, int32_t n) {
@@ -482,8 +522,24 @@ static void qkv_rope(const orc_model* m, const layer_t* L, int32_t pos, scratch_
   for (int32_t h = 0; h < c->n_kv_heads; h++) orc_rope(s->k + (size_t)h * c->head_dim, c->head_dim, pos, c->rope_theta);
 }
 
+static int32_t step_impl(orc_model* m, int32_t seq, int32_t token, int32_t pos, float* logits,
+                         double* hidden, double* trace, const uint8_t* keep, int32_t score_layers,
+                         double* scores);
+
 int32_t orc_step(orc_model* m, int32_t seq, int32_t token, int32_t pos, float* logits,
                  double* hidden, double* trace) {
+  return step_impl(m, seq, token, pos, logits, hidden, trace, NULL, 0, NULL);
+}
+
+int32_t orc_step_kept(orc_model* m, int32_t seq, int32_t token, int32_t pos, const uint8_t* keep,
+                      int32_t score_layers, double* scores, float* logits) {
+  if (!keep || pos < 0 || !keep[pos]) return -15;
+  return step_impl(m, seq, token, pos, logits, NULL, NULL, keep, score_layers, scores);
+}
+
+static int32_t step_impl(orc_model* m, int32_t seq, int32_t token, int32_t pos, float* logits,
+                         double* hidden, double* trace, const uint8_t* keep, int32_t score_layers,
+                         double* scores) {
   const orc_cfg* c = &m->c;
   if (!orc_ready(m)) return -10;
   if (seq < 0 || seq >= c->max_seqs) return -11;
@@ -529,7 +585,11 @@ int32_t orc_step(orc_model* m, int32_t seq, int32_t token, int32_t pos, float* l
     kv_store(c, kv->v, kv->vs, l, pos, s.v);
     kv_load(c, kv->k, kv->ks, l, 0, pos + 1, Kd);
     kv_load(c, kv->v, kv->vs, l, 0, pos + 1, Vd);
-    orc_attention(s.q, c->n_q_heads, c->n_kv_heads, c->head_dim, pos + 1, Kd, Vd, s.o);
+    if (keep)
+      orc_attention_kept(s.q, c->n_q_heads, c->n_kv_heads, c->head_dim, pos + 1, Kd, Vd, keep, s.o,
+                     l >= c->n_layers - score_layers ? scores : NULL);
+    else
+      orc_attention(s.q, c->n_q_heads, c->n_kv_heads, c->head_dim, pos + 1, Kd, Vd, s.o);
     if (trace) memcpy(t_o, s.o, dsz * qd);
     round_vec(s.o, qd, c->act);
     gemv_mat(m, &L->wo, s.o, s.tmp);

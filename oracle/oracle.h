@@ -77,6 +77,12 @@ void    orc_rope(double* v, int32_t d, int32_t pos, double theta);
 /* q [hq][d]; K, V [n_pos][hkv][d]; out [hq][d]; q head h reads kv head h / (hq/hkv) */
 void    orc_attention(const double* q, int32_t hq, int32_t hkv, int32_t d, int32_t n_pos,
                       const double* K, const double* V, double* out);
+/* orc_attention over the positions t < n_pos with keep[t] != 0 only; prob (may be NULL,
+ * double [n_pos]) gets each attended position's softmax probability added, summed over the
+ * query heads */
+void    orc_attention_kept(const double* q, int32_t hq, int32_t hkv, int32_t d, int32_t n_pos,
+                           const double* K, const double* V, const uint8_t* keep, double* out,
+                           double* prob);
 double  orc_silu(double z);
 /* first index of the maximum; -1 if n <= 0, -2 if any value is NaN */
 int32_t orc_argmax_f32(const float* v, int32_t n);
@@ -104,6 +110,13 @@ int32_t    orc_ready(const orc_model* m);
 int32_t    orc_step(orc_model* m, int32_t seq, int32_t token, int32_t pos,
                     float* logits, double* hidden, double* trace);
 int32_t    orc_trace_len(const orc_model* m);
+/* orc_step with a kept set (the Initial-Key KV cache of the C17 engine article, 5.3): the
+ * token at `pos` attends only to the positions t <= pos with keep[t] != 0 (keep [pos + 1];
+ * the new position is always attended).  In each of the last score_layers layers, the
+ * softmax probability every attended position receives is added, summed over the query
+ * heads, to scores[t] (double [pos + 1]; may be NULL).  Returns as orc_step. */
+int32_t    orc_step_kept(orc_model* m, int32_t seq, int32_t token, int32_t pos, const uint8_t* keep,
+                         int32_t score_layers, double* scores, float* logits);
 /* Writes n positions of stored K/V (native encoding, [n][hkv][d]; scales [n][hkv] fp16
  * for int8) at pos0..pos0+n-1 of (seq, layer). */
 int32_t    orc_kv_write(orc_model* m, int32_t seq, int32_t layer, int32_t pos0, int32_t n,
