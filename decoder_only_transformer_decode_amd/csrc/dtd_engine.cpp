@@ -39,6 +39,21 @@ struct Seq {
   std::vector<int32_t> tokens;
   bool tokens_known = true;
   int reused = 0;   // positions the last prefill took from the prefix cache
+  // KV budget: tokens run so far (the next token's RoPE position) and the true position of
+  // each cache entry (kept in step only while a budget is set)
+  int rpos = 0;
+  std::vector<int32_t> kv_pos;
+};
+
+// Initial-Key KV budget of one sequence (the C17 engine article, 5.3)
+struct KvBudget {
+  int budget = 0, n_initial = 0, n_recent = 0, score_layers = 0;
+};
+
+// Per-row extras of a step: RoPE positions and the first scored layer (null: none)
+struct StepExtra {
+  const int* rpos = nullptr;
+  const int* score_from = nullptr;
 };
 
 // A prefix-cache entry: the KV of a token sequence's positions [0, tokens.size()), held as
@@ -109,6 +124,12 @@ struct dtd_engine {
   std::vector<int> free_slots;
   std::vector<int32_t> free_blocks;
   std::vector<int32_t> blk_ref;   // holders of each KV block: sequences and prefix-cache entries
+  std::unordered_map<int64_t, KvBudget> budgets;   // sequences under a KV budget
+  float* scores_dev = nullptr;    // [max_seqs][max_ctx] attention-score sums of budgeted sequences
+  float* attn_stat = nullptr;     // [mb][Hq][2] merged softmax max and normaliser of a scored layer
+  int32_t* evict_dev = nullptr;   // [3][max_ctx] eviction lists (old blocks, new blocks, kept entries)
+  int step_score_min = 1 << 30;   // first scored layer of the step being run
+  int step_max_pos = 0;
 
   // prefix cache: entries by id, and every prefix of every entry by its hash
   int pcache_cap = 0;             // 0: off
@@ -337,7 +358,8 @@ static void free_all(dtd_engine* e) {
   release_weights(e);
   void* ps[] = {e->rope_cos, e->rope_sin, e->kpool, e->vpool, e->kspool, e->vspool, e->bt_dev,
                 e->x, e->xn, e->q, e->knew, e->vnew, e->partials, e->gemm_partials, e->o, e->h, e->logits,
-                e->err_dev, e->desc_dev, e->rows_dev, e->players, e->tags, e->tok_scratch};
+                e->err_dev, e->desc_dev, e->rows_dev, e->players, e->tags, e->tok_scratch,
+                e->scores_dev, e->attn_stat, e->evict_dev};
   for (void* p : ps)
     if (p) (void)hipFree(p);
   if (e->desc_host) (void)hipHostFree(e->desc_host);
@@ -427,7 +449,10 @@ extern "C" dtd_status dtd_create(const dtd_config* cfg, void* hip_stream, dtd_en
       (st = dev_alloc(e, &e->h, (size_t)MB * d.F * ab)) ||
       (st = dev_alloc(e, &e->logits, (size_t)MB * d.V * 4)) ||
       (st = dev_alloc(e, &e->err_dev, 16)) || (st = dev_alloc(e, &e->desc_dev, sizeof(StepDesc))) ||
-      (st = dev_alloc(e, &e->tok_scratch, (size_t)MB * 4)))
+      (st = dev_alloc(e, &e->tok_scratch, (size_t)MB * 4)) ||
+      (st = dev_alloc(e, &e->scores_dev, (size_t)cfg->max_seqs * cfg->max_ctx * 4)) ||
+      (st = dev_alloc(e, &e->attn_stat, (size_t)MB * d.Hq * 2 * 4)) ||
+      (st = dev_alloc(e, &e->evict_dev, (size_t)3 * cfg->max_ctx * 4)))
     return cleanup(st);
   if (hipMemset(e->err_dev, 0, 16) != hipSuccess) return cleanup(DTD_E_HIP);
 
@@ -726,7 +751,8 @@ static dtd_status run_step(dtd_engine* e, int B, const int* slots, const int* po
                            const int32_t* tokens, int32_t* next, float* logits_out, bool do_head,
                            const Update* upd, int n_upd, const uint8_t* inject = nullptr,
                            uint8_t* capture = nullptr, float* partials = nullptr, float* gemm_partials = nullptr,
-                           bool force_per_kernel = false, bool no_timing = false, bool append_first = false) {
+                           bool force_per_kernel = false, bool no_timing = false, bool append_first = false,
+                           const StepExtra* extra = nullptr) {
   if (!partials) partials = e->partials;
   if (!gemm_partials) gemm_partials = e->gemm_partials;
   const Dims& d = e->d;
@@ -741,7 +767,17 @@ static dtd_status run_step(dtd_engine* e, int B, const int* slots, const int* po
   hd->tokens = tokens;
   hd->next_tokens = next;
   hd->logits_out = logits_out;
-  for (int b = 0; b < B; b++) { hd->pos[b] = poss[b]; hd->slot[b] = slots[b]; hd->pos_block[b] = pblks[b]; }
+  e->step_score_min = 1 << 30;
+  e->step_max_pos = 0;
+  for (int b = 0; b < B; b++) {
+    hd->pos[b] = poss[b]; hd->slot[b] = slots[b]; hd->pos_block[b] = pblks[b];
+    hd->rpos[b] = extra && extra->rpos ? extra->rpos[b] : poss[b];
+    hd->score_from[b] = extra && extra->score_from ? extra->score_from[b] : d.L;
+    e->step_score_min = std::min(e->step_score_min, hd->score_from[b]);
+    e->step_max_pos = std::max(e->step_max_pos, poss[b]);
+  }
+  // RoPE positions and score sums are only in the per-sub-step kernels
+  if (extra) force_per_kernel = true;
   for (int u = 0; u < n_upd; u++) {
     hd->upd[u][0] = upd[u].slot; hd->upd[u][1] = upd[u].lblock; hd->upd[u][2] = upd[u].pblock;
   }
@@ -863,7 +899,10 @@ static dtd_status run_sub_steps(dtd_engine* e, int B, bool do_head, const uint8_
     }
     if (append_first) HIP_OK(e, launch_kv_append(d, e->desc_dev, B, e->knew, e->vnew, kv, st));
     TIMED(4, launch_attention(d, e->desc_dev, B, e->q, e->knew, e->vnew, kv, e->bt_dev, partials, st));
-    HIP_OK(e, launch_combine(d, e->desc_dev, B, partials, e->o, st));
+    const bool scored = l >= e->step_score_min;
+    HIP_OK(e, launch_combine(d, e->desc_dev, B, partials, e->o, st, scored ? e->attn_stat : nullptr));
+    if (scored)
+      HIP_OK(e, launch_score(d, e->desc_dev, B, e->step_max_pos, l, e->q, kv, e->bt_dev, e->attn_stat, e->scores_dev, st));
     if (probe) {
       HIP_OK(e, cp(out + pl.o, e->o, fo));
       HIP_OK(e, cp(e->o, in + pl.o, fo));
@@ -1059,6 +1098,74 @@ static dtd_status copy_block(dtd_engine* e, int32_t src, int32_t dst) {
   return DTD_OK;
 }
 
+// ---- KV budget (the Initial-Key cache of the C17 engine article, 5.3) ----------------------
+
+static const KvBudget* budget_of(const dtd_engine* e, int64_t seq_id) {
+  auto it = e->budgets.find(seq_id);
+  return it == e->budgets.end() ? nullptr : &it->second;
+}
+
+// a new sequence under a budget starts with a clear score row
+static dtd_status budget_seq_created(dtd_engine* e, int64_t seq_id, Seq& s) {
+  if (!budget_of(e, seq_id)) return DTD_OK;
+  s.kv_pos.reserve((size_t)e->cfg.max_ctx);
+  HIP_OK(e, hipMemsetAsync(e->scores_dev + (size_t)s.slot * e->cfg.max_ctx, 0, (size_t)e->cfg.max_ctx * 4, e->stream));
+  return DTD_OK;
+}
+
+// Brings a sequence back to its budget when it holds more entries: the entries of its first
+// n_initial positions, its last n_recent entries, and the highest attention-score sums of the
+// others (the earlier entry on equal sums) stay, in order, copied into fresh blocks; the rest
+// are dropped with their scores.  Synchronous (the host reads the scores).
+static dtd_status kv_evict(dtd_engine* e, Seq& s, const KvBudget& kb) {
+  const int n = s.len;
+  if (n <= kb.budget) return DTD_OK;
+  const int mc = e->cfg.max_ctx;
+  std::vector<float> sc((size_t)n);
+  HIP_OK(e, hipStreamSynchronize(e->stream));
+  HIP_OK(e, hipMemcpy(sc.data(), e->scores_dev + (size_t)s.slot * mc, (size_t)n * 4, hipMemcpyDeviceToHost));
+  int n_init = 0;
+  while (n_init < n && s.kv_pos[(size_t)n_init] < kb.n_initial) n_init++;
+  const int rec0 = std::max(n_init, n - kb.n_recent);
+  std::vector<int32_t> middle;
+  for (int i = n_init; i < rec0; i++) middle.push_back(i);
+  std::stable_sort(middle.begin(), middle.end(), [&](int a, int b) { return sc[(size_t)a] > sc[(size_t)b]; });
+  const int take = std::max(0, kb.budget - n_init - (n - rec0));
+  if ((int)middle.size() > take) middle.resize((size_t)take);
+  std::vector<int32_t> keep;
+  for (int i = 0; i < n_init; i++) keep.push_back(i);
+  keep.insert(keep.end(), middle.begin(), middle.end());
+  for (int i = rec0; i < n; i++) keep.push_back(i);
+  std::sort(keep.begin(), keep.end());
+  const int m = (int)keep.size();
+  const int nb = blocks_needed(e, m);
+  if (!make_room(e, nb))
+    return fail(e, DTD_E_KVFULL, "KV budget: %d blocks for the kept entries, %zu free", nb, e->free_blocks.size());
+  std::vector<int32_t> fresh;
+  for (int i = 0; i < nb; i++) fresh.push_back(take_block(e));
+  HIP_OK(e, hipMemcpy(e->evict_dev, s.blocks.data(), s.blocks.size() * 4, hipMemcpyHostToDevice));
+  HIP_OK(e, hipMemcpy(e->evict_dev + mc, fresh.data(), fresh.size() * 4, hipMemcpyHostToDevice));
+  HIP_OK(e, hipMemcpy(e->evict_dev + 2 * (size_t)mc, keep.data(), keep.size() * 4, hipMemcpyHostToDevice));
+  HIP_OK(e, launch_kv_gather(e->d, e->players, e->evict_dev, e->evict_dev + mc, e->evict_dev + 2 * (size_t)mc, m,
+                             e->stream));
+  std::vector<float> nsc((size_t)mc, 0.f);
+  std::vector<int32_t> npos((size_t)m);
+  for (int i = 0; i < m; i++) {
+    nsc[(size_t)i] = sc[(size_t)keep[(size_t)i]];
+    npos[(size_t)i] = s.kv_pos[(size_t)keep[(size_t)i]];
+  }
+  HIP_OK(e, hipStreamSynchronize(e->stream));
+  HIP_OK(e, hipMemcpy(e->scores_dev + (size_t)s.slot * mc, nsc.data(), (size_t)mc * 4, hipMemcpyHostToDevice));
+  for (int32_t b : s.blocks) drop_block(e, b);
+  s.blocks.assign(fresh.begin(), fresh.end());
+  HIP_OK(e, hipMemcpy(e->bt_dev + (size_t)s.slot * e->d.max_blocks, s.blocks.data(), s.blocks.size() * 4,
+                      hipMemcpyHostToDevice));
+  s.kv_pos.assign(npos.begin(), npos.end());
+  s.len = m;
+  s.tokens_known = false;
+  return DTD_OK;
+}
+
 static dtd_status prefill_run(dtd_engine* e, int64_t seq_id, Seq& s, const int32_t* tokens_dev, int n,
                               int32_t* next_token_dev, float* logits_dev);
 
@@ -1083,7 +1190,8 @@ extern "C" dtd_status dtd_prefill(dtd_engine* e, int64_t seq_id, const int32_t* 
     HIP_OK(e, hipMemcpy(host.data(), tokens_dev, (size_t)n * 4, hipMemcpyDeviceToHost));
   }
   int64_t hit = -1;
-  const int reuse = (pc && is_new) ? pcache_lookup(e, host.data(), n, &hit) : 0;
+  const KvBudget* kb = budget_of(e, seq_id);
+  const int reuse = (pc && is_new && !kb) ? pcache_lookup(e, host.data(), n, &hit) : 0;
   const int shared = reuse / e->d.bs;       // whole blocks taken over from the entry
   const int have = is_new ? 0 : (int)it->second.blocks.size();
   const int need = blocks_needed(e, len0 + n) - have - shared;
@@ -1095,6 +1203,7 @@ extern "C" dtd_status dtd_prefill(dtd_engine* e, int64_t seq_id, const int32_t* 
     s.slot = e->free_slots.back();
     e->free_slots.pop_back();
     it = e->seqs.emplace(seq_id, s).first;
+    if ((st = budget_seq_created(e, seq_id, it->second))) return st;
   }
   Seq& s = it->second;
   if (!pc) s.tokens_known = false;
@@ -1116,6 +1225,7 @@ extern "C" dtd_status dtd_prefill(dtd_engine* e, int64_t seq_id, const int32_t* 
     HIP_OK(e, hipMemcpy(e->bt_dev + (size_t)s.slot * e->d.max_blocks, s.blocks.data(), s.blocks.size() * 4,
                         hipMemcpyHostToDevice));
     s.len = reuse;
+    s.rpos = reuse;
     s.tokens.assign(host.begin(), host.begin() + reuse);
     tokens_dev += reuse;
     n -= reuse;
@@ -1123,6 +1233,7 @@ extern "C" dtd_status dtd_prefill(dtd_engine* e, int64_t seq_id, const int32_t* 
   if (pc && s.tokens_known) s.tokens.insert(s.tokens.end(), host.begin() + reuse, host.end());
   st = prefill_run(e, seq_id, s, tokens_dev, n, next_token_dev, logits_dev);
   if (st) return st;
+  if (kb) return kv_evict(e, s, *kb);
   if (pc && s.tokens_known && (int)s.tokens.size() == s.len) pcache_insert(e, s, s.tokens.data(), s.len);
   return DTD_OK;
 }
@@ -1131,6 +1242,11 @@ extern "C" dtd_status dtd_prefill(dtd_engine* e, int64_t seq_id, const int32_t* 
 static dtd_status prefill_run(dtd_engine* e, int64_t seq_id, Seq& s, const int32_t* tokens_dev, int n,
                               int32_t* next_token_dev, float* logits_dev) {
   dtd_status st = DTD_OK;
+  // under a KV budget (or after one evicted entries) the steps carry RoPE positions, and the
+  // last prompt position's attention adds to the scores
+  const KvBudget* kb = budget_of(e, seq_id);
+  const bool extra_on = kb || s.rpos != s.len;
+  const int sfrom = kb ? e->d.L - kb->score_layers : e->d.L;
   // Batched prefill: the prompt in chunks of up to kPrefillChunk positions, each chunk one
   // step of the per-sub-step schedule with the chunk's positions as its batch (projections on
   // the matrix cores where the formats allow); every position's K/V is appended before the
@@ -1155,16 +1271,25 @@ static dtd_status prefill_run(dtd_engine* e, int64_t seq_id, Seq& s, const int32
         poss[b] = pos;
         pblks[b] = s.blocks[(size_t)(pos / e->d.bs)];
       }
+      int rps[kPrefillChunk], sfs[kPrefillChunk];
+      for (int b = 0; b < B; b++) {
+        rps[b] = s.rpos + b;
+        sfs[b] = (last && b == B - 1) ? sfrom : e->d.L;
+      }
+      const StepExtra ex{rps, sfs};
       st = run_step(e, B, slots, poss, pblks, tokens_dev + c0, e->tok_scratch, nullptr, last, upd, n_upd,
-                    nullptr, nullptr, nullptr, nullptr, true, false, true);
+                    nullptr, nullptr, nullptr, nullptr, true, false, true, extra_on ? &ex : nullptr);
       if (st) return st;
+      if (kb)
+        for (int b = 0; b < B; b++) s.kv_pos.push_back(s.rpos + b);
       s.len += B;
+      s.rpos += B;
       if (last) {
         HIP_OK(e, hipMemcpyAsync(next_token_dev, e->tok_scratch + (B - 1), 4, hipMemcpyDeviceToDevice, e->stream));
         if (logits_dev)
           HIP_OK(e, hipMemcpyAsync(logits_dev, e->logits + (size_t)(B - 1) * e->d.V, (size_t)e->d.V * 4,
                                    hipMemcpyDeviceToDevice, e->stream));
-        const int lastpos = s.len - 1;
+        const int lastpos = s.rpos - 1;
         return sample_rows(e, 1, &seq_id, &lastpos, e->logits + (size_t)(B - 1) * e->d.V, next_token_dev);
       }
     }
@@ -1181,12 +1306,16 @@ static dtd_status prefill_run(dtd_engine* e, int64_t seq_id, Seq& s, const int32
     }
     const bool last = i == n - 1;
     const int pblk = s.blocks[(size_t)(pos / e->d.bs)];
+    const int rp = s.rpos, sf = last ? sfrom : e->d.L;
+    const StepExtra ex{&rp, &sf};
     st = run_step(e, 1, &s.slot, &pos, &pblk, tokens_dev + i, next_token_dev, last ? logits_dev : nullptr, last,
-                  upd, n_upd);
+                  upd, n_upd, nullptr, nullptr, nullptr, nullptr, false, false, false, extra_on ? &ex : nullptr);
     if (st) return st;
+    if (kb) s.kv_pos.push_back(s.rpos);
     s.len++;
+    s.rpos++;
   }
-  const int lastpos = s.len - 1;
+  const int lastpos = s.rpos - 1;
   return sample_rows(e, 1, &seq_id, &lastpos, e->logits, next_token_dev);
 }
 
@@ -1219,7 +1348,7 @@ static dtd_status decode_impl(dtd_engine* e, int32_t batch, const int64_t* seq_i
       return fail(e, DTD_E_NOSEQ, "decode_step: unknown seq_id %lld", (long long)seq_ids_host[b]);
     if (it != e->seqs.end()) {
       const Seq& s = it->second;
-      if (s.len + 1 > e->cfg.max_ctx)
+      if (s.len + 1 > e->cfg.max_ctx || s.rpos + 1 > e->cfg.max_ctx)
         return fail(e, DTD_E_CTX, "decode_step: seq_id %lld is at max_ctx %d", (long long)seq_ids_host[b], e->cfg.max_ctx);
       if (s.len / e->d.bs >= (int)s.blocks.size()) need++;
     } else {
@@ -1235,7 +1364,8 @@ static dtd_status decode_impl(dtd_engine* e, int32_t batch, const int64_t* seq_i
       s.slot = e->free_slots.back();
       s.blocks.reserve((size_t)e->d.max_blocks);
       e->free_slots.pop_back();
-      e->seqs.emplace(seq_ids_host[b], std::move(s));
+      auto nit = e->seqs.emplace(seq_ids_host[b], std::move(s)).first;
+      if ((st = budget_seq_created(e, seq_ids_host[b], nit->second))) return st;
     }
   for (int b = 0; b < batch; b++) ss[b] = &e->seqs.find(seq_ids_host[b])->second;
   int slots[kMaxBatch], poss[kMaxBatch], pblks[kMaxBatch];
@@ -1252,15 +1382,30 @@ static dtd_status decode_impl(dtd_engine* e, int32_t batch, const int64_t* seq_i
     poss[b] = s.len;
     pblks[b] = s.blocks[(size_t)(s.len / e->d.bs)];
   }
+  // KV budgets (and sequences whose entries were evicted): RoPE positions and score sums
+  int rps[kMaxBatch], sfs[kMaxBatch];
+  bool extra_on = false;
+  const KvBudget* kbs[kMaxBatch];
+  for (int b = 0; b < batch; b++) {
+    kbs[b] = budget_of(e, seq_ids_host[b]);
+    rps[b] = ss[b]->rpos;
+    sfs[b] = kbs[b] ? e->d.L - kbs[b]->score_layers : e->d.L;
+    extra_on = extra_on || kbs[b] || ss[b]->rpos != ss[b]->len;
+  }
+  const StepExtra ex{rps, sfs};
   st = run_step(e, batch, slots, poss, pblks, tokens_dev, next_tokens_dev, logits_dev, true, upd, n_upd,
-                inject, capture, partials, gemm_partials, no_alloc, no_alloc);
+                inject, capture, partials, gemm_partials, no_alloc, no_alloc, false, extra_on ? &ex : nullptr);
   if (st) return st;
-  st = sample_rows(e, batch, seq_ids_host, poss, e->logits, next_tokens_dev);
+  st = sample_rows(e, batch, seq_ids_host, rps, e->logits, next_tokens_dev);
   if (st) return st;
   for (int b = 0; b < batch; b++) {
+    if (kbs[b]) ss[b]->kv_pos.push_back(ss[b]->rpos);
     ss[b]->len++;
+    ss[b]->rpos++;
     ss[b]->tokens_known = false;   // the token ids of a decode step stay on the device
   }
+  for (int b = 0; b < batch; b++)
+    if (kbs[b] && (st = kv_evict(e, *ss[b], *kbs[b]))) return st;
   return DTD_OK;
 }
 
@@ -1286,6 +1431,12 @@ extern "C" dtd_status dtd_decode_step_noalloc(dtd_engine* e, int32_t batch, cons
                 "decode_step_noalloc: %zu bytes of attention partials and %zu of projection partial sums for "
                 "batch %d exceed the %zu-byte static scratch (fewer sequences per call, or a shorter max_ctx, fit)",
                 attn, gemm, batch, kNoAllocScratchBytes);
+  for (int b = 0; b < batch && seq_ids_host; b++) {
+    auto it = e->seqs.find(seq_ids_host[b]);
+    if (budget_of(e, seq_ids_host[b]) || (it != e->seqs.end() && it->second.rpos != it->second.len))
+      return fail(e, DTD_E_UNSUPPORTED, "decode_step_noalloc: seq_id %lld is under a KV budget",
+                  (long long)seq_ids_host[b]);
+  }
   float* base = (float*)e->scratch_dev;
   return decode_impl(e, batch, seq_ids_host, tokens_dev, next_tokens_dev, logits_dev, nullptr, nullptr, false,
                      base, (float*)((uint8_t*)base + attn), true);
@@ -1316,6 +1467,7 @@ extern "C" dtd_status dtd_reset_seq(dtd_engine* e, int64_t seq_id) {
   e->free_slots.push_back(it->second.slot);
   e->seqs.erase(it);
   e->samplers.erase(seq_id);
+  e->budgets.erase(seq_id);
   return DTD_OK;
 }
 
@@ -1357,6 +1509,54 @@ extern "C" dtd_status dtd_prefix_cache_add(dtd_engine* e, int64_t seq_id, const 
   if (e->pcache_cap <= 0) return fail(e, DTD_E_STATE, "prefix_cache_add: the prefix cache is off");
   pcache_insert(e, it->second, tokens_host, n);
   return DTD_OK;
+}
+
+extern "C" dtd_status dtd_set_kv_budget(dtd_engine* e, int64_t seq_id, int32_t budget, int32_t n_initial,
+                                        int32_t n_recent, int32_t score_layers) {
+  if (!e) return DTD_E_ARG;
+  if (budget == 0) {
+    e->budgets.erase(seq_id);
+    return DTD_OK;
+  }
+  if (budget < 0 || n_initial < 0 || n_recent < 1 || budget < n_initial + n_recent + 1 || budget > e->cfg.max_ctx ||
+      score_layers < 1 || score_layers > e->d.L)
+    return fail(e, DTD_E_ARG, "set_kv_budget: budget %d, n_initial %d, n_recent %d, score_layers %d out of range",
+                budget, n_initial, n_recent, score_layers);
+  auto it = e->seqs.find(seq_id);
+  const bool had = budget_of(e, seq_id) != nullptr;
+  e->budgets[seq_id] = KvBudget{budget, n_initial, n_recent, score_layers};
+  if (it != e->seqs.end() && !had) {
+    Seq& s = it->second;
+    if (s.rpos != s.len) return fail(e, DTD_E_STATE, "set_kv_budget: the sequence has evicted entries");
+    dtd_status st = budget_seq_created(e, seq_id, s);
+    if (st) return st;
+    s.kv_pos.clear();
+    for (int p = 0; p < s.len; p++) s.kv_pos.push_back(p);
+  }
+  return DTD_OK;
+}
+
+extern "C" int32_t dtd_debug_kv_positions(const dtd_engine* e, int64_t seq_id, int32_t* out_host, int32_t cap) {
+  if (!e || (cap > 0 && !out_host)) return DTD_E_ARG;
+  auto it = e->seqs.find(seq_id);
+  if (it == e->seqs.end()) return DTD_E_NOSEQ;
+  const Seq& s = it->second;
+  for (int i = 0; i < std::min(s.len, cap); i++)
+    out_host[i] = budget_of(e, seq_id) ? s.kv_pos[(size_t)i] : (s.rpos == s.len ? i : -1);
+  return s.len;
+}
+
+extern "C" int32_t dtd_debug_kv_scores(dtd_engine* e, int64_t seq_id, float* out_host, int32_t cap) {
+  if (!e || (cap > 0 && !out_host)) return DTD_E_ARG;
+  auto it = e->seqs.find(seq_id);
+  if (it == e->seqs.end()) return DTD_E_NOSEQ;
+  const int n = std::min(it->second.len, cap);
+  if (n > 0) {
+    HIP_OK(e, hipStreamSynchronize(e->stream));
+    HIP_OK(e, hipMemcpy(out_host, e->scores_dev + (size_t)it->second.slot * e->cfg.max_ctx, (size_t)n * 4,
+                        hipMemcpyDeviceToHost));
+  }
+  return it->second.len;
 }
 
 extern "C" dtd_status dtd_get_config(const dtd_engine* e, dtd_config* out) {
@@ -1500,6 +1700,17 @@ extern "C" dtd_status dtd_debug_capture_hidden(dtd_engine* e, int32_t enable, fl
   return DTD_OK;
 }
 
+// a debug write that extends a sequence to `len` positions: they are its token positions too
+// (unless entries were evicted before)
+static void grow_debug_len(dtd_engine* e, int64_t seq_id, Seq& s, int len) {
+  if (s.rpos == s.len) {
+    if (budget_of(e, seq_id))
+      for (int p = s.len; p < len; p++) s.kv_pos.push_back(p);
+    s.rpos = len;
+  }
+  s.len = len;
+}
+
 // make sure a sequence exists with blocks for [0, len); new block-table entries are written
 // synchronously (the debug entry points are synchronous)
 static dtd_status ensure_seq_blocks(dtd_engine* e, int64_t seq_id, int len, Seq** out) {
@@ -1511,6 +1722,8 @@ static dtd_status ensure_seq_blocks(dtd_engine* e, int64_t seq_id, int len, Seq*
     s.slot = e->free_slots.back();
     e->free_slots.pop_back();
     it = e->seqs.emplace(seq_id, s).first;
+    dtd_status st = budget_seq_created(e, seq_id, it->second);
+    if (st) return st;
   }
   Seq& s = it->second;
   const int need = blocks_needed(e, len) - (int)s.blocks.size();
@@ -1589,7 +1802,7 @@ static dtd_status kv_copy(dtd_engine* e, int64_t seq_id, int32_t layer, int32_t 
       }
     }
   }
-  if (write && pos0 + n > s->len) s->len = pos0 + n;
+  if (write && pos0 + n > s->len) grow_debug_len(e, seq_id, *s, pos0 + n);
   return DTD_OK;
 }
 
@@ -1630,7 +1843,7 @@ extern "C" dtd_status dtd_debug_kv_fill(dtd_engine* e, int64_t seq_id, int32_t l
     e->broken = true;
     return fail(e, DTD_E_HIP, "kv_fill: %s", hipGetErrorString(r));
   }
-  if (len > s->len) s->len = len;
+  if (len > s->len) grow_debug_len(e, seq_id, *s, len);
   return DTD_OK;
 }
 

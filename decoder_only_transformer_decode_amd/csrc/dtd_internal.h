@@ -35,6 +35,11 @@ struct StepDesc {
   int32_t slot[kMaxBatch];           // sequence slot (block-table row)
   int32_t pos_block[kMaxBatch];      // physical KV block of the new position
   int32_t upd[kMaxUpdates][3];       // (slot, logical block, physical block)
+  // KV budget: a sequence's token position (for RoPE) can run ahead of its cache index `pos`
+  // once entries have been evicted; attention-score sums are added, from layer score_from[b]
+  // on (L: none), to the sequence slot's row of the score buffer
+  int32_t rpos[kMaxBatch];
+  int32_t score_from[kMaxBatch];
 };
 
 struct Dims {
@@ -188,7 +193,11 @@ hipError_t launch_kv_append(const Dims& d, const StepDesc* desc, int B, const fl
                             const KvLayer& kv, hipStream_t st);
 hipError_t launch_kv_copy_block(const Dims& d, const PLayer* layers, int src, int dst, hipStream_t st);
 hipError_t launch_combine(const Dims& d, const StepDesc* desc, int B, const float* partials,
-                          void* o, hipStream_t st);
+                          void* o, hipStream_t st, float* stat = nullptr);
+hipError_t launch_score(const Dims& d, const StepDesc* desc, int B, int max_pos, int layer, const float* q,
+                        const KvLayer& kv, const int32_t* bt, const float* stat, float* scores, hipStream_t st);
+hipError_t launch_kv_gather(const Dims& d, const PLayer* layers, const int32_t* old_blocks, const int32_t* new_blocks,
+                            const int32_t* keep, int n, hipStream_t st);
 hipError_t launch_argmax(const Dims& d, const StepDesc* desc, int B, const float* logits,
                          hipStream_t st);
 hipError_t launch_dequant_rows(const Dims& d, const MatDev& m, const int32_t* rows, int nrows,

@@ -97,8 +97,9 @@ __device__ __forceinline__ void gemv_epilogue(const GemvArgs& a, int b, int row0
   const Dims& d = a.d;
   if constexpr (EPI == EPI_QKV) {
     // Stored QKV rows: q and k heads hold the RoPE pairs (i, i + hd/2) as adjacent rows
-    // (2i, 2i+1); v rows are in natural order.
-    const int pos = a.ea.desc->pos[b];
+    // (2i, 2i+1); v rows are in natural order.  The rotation is by the token's position,
+    // which runs ahead of its cache index once a KV budget has evicted entries.
+    const int pos = a.ea.desc->rpos[b];
     const int half = d.hd >> 1;
 #pragma unroll
     for (int i = 0; i < ROWS; i += 2) {
@@ -891,13 +892,83 @@ __global__ __launch_bounds__(256) void k_kv_copy_block(const PLayer* layers, int
   for (size_t i = n16 * 16 + threadIdx.x; i < n; i += 256) b[i] = a[i];
 }
 
-// one (head, sequence): o = merge of its chunk partials, rounded to the activation type
+// one (head, sequence): o = merge of its chunk partials, rounded to the activation type;
+// with stat, also the softmax's max M and normaliser L (natural-log units) per (sequence, head)
 __global__ __launch_bounds__(256) void k_combine(Dims d, const StepDesc* desc, const float* partials,
-                                                 void* o) {
+                                                 void* o, float* stat) {
   const int h = blockIdx.x, b = blockIdx.y, i = threadIdx.x;
   const int nv = (desc->pos[b] + d.ct) / d.ct;
   const float* P = partials + ((size_t)b * d.Hq + h) * d.nch * (d.hd + 2);
   if (i < d.hd) store_act(o, (size_t)b * d.q_dim + (size_t)h * d.hd + i, combine_one(P, nv, d.hd, i), d.act);
+  if (stat && i == 0) {
+    const int cs = d.hd + 2;
+    float M = -INFINITY, L = 0.f;
+    for (int c = 0; c < nv; c++) M = fmaxf(M, P[c * cs + d.hd]);
+    for (int c = 0; c < nv; c++) L += expf(P[c * cs + d.hd] - M) * P[c * cs + d.hd + 1];
+    stat[((size_t)b * d.Hq + h) * 2] = M;
+    stat[((size_t)b * d.Hq + h) * 2 + 1] = L;
+  }
+}
+
+// KV budget scores (the Initial-Key cache of the C17 engine article, 5.3): the softmax
+// probability each cache entry t <= pos of sequence b gets from this step's queries, summed
+// over the query heads, added to scores[slot][t].  Grid (B, entry tiles of 256); a thread
+// owns one entry (so the sum over heads has one fixed order), recomputes q_h . k_t / sqrt(d)
+// from the stored key and divides exp(s - M_h) by L_h from the merged attention statistics.
+template <int KVFMT>
+__global__ __launch_bounds__(256) void k_score(Dims d, const StepDesc* desc, int layer, const float* q,
+                                               KvLayer kv, const int32_t* bt, const float* stat, float* scores) {
+  const int b = blockIdx.x;
+  if (layer < desc->score_from[b]) return;
+  const int t = blockIdx.y * 256 + threadIdx.x;
+  const int pos = desc->pos[b], slot = desc->slot[b];
+  if (t > pos) return;
+  const int blk = bt[(size_t)slot * d.max_blocks + t / d.bs];
+  const float scale = 1.f / sqrtf((float)d.hd);
+  float sum = 0.f;
+  for (int j = 0; j < d.Hkv; j++) {
+    const size_t row = ((size_t)blk * d.Hkv + j) * d.bs + (t % d.bs);
+    float ks = 1.f;
+    if constexpr (KVFMT == KV_I8) ks = f16_to_f32(kv.ks[row]);
+    for (int g = 0; g < d.G; g++) {
+      const int h = j * d.G + g;
+      const float* qh = q + (size_t)b * d.q_dim + (size_t)h * d.hd;
+      float dot = 0.f;
+      for (int i = 0; i < d.hd; i++) {
+        float kval;
+        if constexpr (KVFMT == KV_F32) kval = ((const float*)kv.k)[row * d.hd + i];
+        else if constexpr (KVFMT == KV_BF16) kval = bf16_to_f32(((const uint16_t*)kv.k)[row * d.hd + i]);
+        else kval = (float)((const int8_t*)kv.k)[row * d.hd + i] * ks;
+        dot += qh[i] * kval;
+      }
+      const float M = stat[((size_t)b * d.Hq + h) * 2], L = stat[((size_t)b * d.Hq + h) * 2 + 1];
+      sum += expf(dot * scale - M) / L;
+    }
+  }
+  scores[(size_t)slot * d.max_ctx + t] += sum;
+}
+
+// KV budget eviction: copies cache entries keep[i] (i < n, through the old block list) to
+// entry i (through the new block list) in every layer: K and V rows and int8 scales.  Grid
+// (layers, n); one block per (layer, entry).
+__global__ __launch_bounds__(128) void k_kv_gather(const PLayer* layers, int Hkv, int bs, int hd, int elem,
+                                                   const int32_t* old_blocks, const int32_t* new_blocks,
+                                                   const int32_t* keep) {
+  const KvLayer kv = layers[blockIdx.x].kv;
+  const int i = blockIdx.y, t = keep[i];
+  const int ob = old_blocks[t / bs], nb = new_blocks[i / bs];
+  const size_t rowb = (size_t)hd * elem;
+  for (int j = 0; j < Hkv; j++) {
+    const size_t src = ((size_t)ob * Hkv + j) * bs + (t % bs), dst = ((size_t)nb * Hkv + j) * bs + (i % bs);
+    for (size_t x = threadIdx.x; x < rowb; x += 128) {
+      ((uint8_t*)kv.k)[dst * rowb + x] = ((const uint8_t*)kv.k)[src * rowb + x];
+      ((uint8_t*)kv.v)[dst * rowb + x] = ((const uint8_t*)kv.v)[src * rowb + x];
+    }
+    if (kv.ks && threadIdx.x == 0) {
+      kv.ks[dst] = kv.ks[src];
+      kv.vs[dst] = kv.vs[src];
+    }
+  }
 }
 
 // S11 greedy argmax over the fp32 logits, lowest index among equal maxima
@@ -1191,8 +1262,25 @@ hipError_t launch_kv_copy_block(const Dims& d, const PLayer* layers, int src, in
 }
 
 hipError_t launch_combine(const Dims& d, const StepDesc* desc, int B, const float* partials,
-                          void* o, hipStream_t st) {
-  hipLaunchKernelGGL(k_combine, dim3(d.Hq, B), dim3(d.hd), 0, st, d, desc, partials, o);
+                          void* o, hipStream_t st, float* stat) {
+  hipLaunchKernelGGL(k_combine, dim3(d.Hq, B), dim3(d.hd), 0, st, d, desc, partials, o, stat);
+  return hipGetLastError();
+}
+
+hipError_t launch_score(const Dims& d, const StepDesc* desc, int B, int max_pos, int layer, const float* q,
+                        const KvLayer& kv, const int32_t* bt, const float* stat, float* scores, hipStream_t st) {
+  const dim3 grid(B, (max_pos + 1 + 255) / 256);
+  if (d.kvfmt == KV_F32) hipLaunchKernelGGL(k_score<KV_F32>, grid, dim3(256), 0, st, d, desc, layer, q, kv, bt, stat, scores);
+  else if (d.kvfmt == KV_BF16) hipLaunchKernelGGL(k_score<KV_BF16>, grid, dim3(256), 0, st, d, desc, layer, q, kv, bt, stat, scores);
+  else hipLaunchKernelGGL(k_score<KV_I8>, grid, dim3(256), 0, st, d, desc, layer, q, kv, bt, stat, scores);
+  return hipGetLastError();
+}
+
+hipError_t launch_kv_gather(const Dims& d, const PLayer* layers, const int32_t* old_blocks, const int32_t* new_blocks,
+                            const int32_t* keep, int n, hipStream_t st) {
+  const int elem = d.kvfmt == KV_F32 ? 4 : (d.kvfmt == KV_BF16 ? 2 : 1);
+  hipLaunchKernelGGL(k_kv_gather, dim3(d.L, n), dim3(128), 0, st, layers, d.Hkv, d.bs, d.hd, elem, old_blocks,
+                     new_blocks, keep);
   return hipGetLastError();
 }
 

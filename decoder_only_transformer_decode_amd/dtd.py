@@ -79,6 +79,9 @@ _SIGS = {
     "dtd_debug_prefix_reused": ([_P, _I64], _I32),
     "dtd_debug_kv_blocks_free": ([_P], _I32),
     "dtd_debug_prefix_entries": ([_P], _I32),
+    "dtd_set_kv_budget": ([_P, _I64, _I32, _I32, _I32, _I32], _I32),
+    "dtd_debug_kv_positions": ([_P, _I64, C.POINTER(_I32), _I32], _I32),
+    "dtd_debug_kv_scores": ([_P, _I64, C.POINTER(C.c_float), _I32], _I32),
     "dtd_sched_create": ([_P, _I32, C.POINTER(_P)], _I32),
     "dtd_sched_destroy": ([_P], None),
     "dtd_sched_submit": ([_P, C.POINTER(_I32), _I32, _I32, _I32, C.POINTER(dtd_sampler), C.POINTER(_I64)], _I32),
@@ -381,6 +384,26 @@ class Engine:
 
     def prefix_entries(self) -> int:
         return load().dtd_debug_prefix_entries(self.h)
+
+    def set_kv_budget(self, seq_id: int, budget: int, n_initial: int = 4, n_recent: int = 16,
+                      score_layers: int = 1):
+        _check(self.h, load().dtd_set_kv_budget(self.h, seq_id, budget, n_initial, n_recent, score_layers))
+
+    def kv_positions(self, seq_id: int):
+        cap = self.cfg.max_ctx
+        buf = (C.c_int32 * cap)()
+        n = load().dtd_debug_kv_positions(self.h, seq_id, buf, cap)
+        if n < 0:
+            raise DtdError(n, "dtd_debug_kv_positions")
+        return [int(buf[i]) for i in range(n)]
+
+    def kv_scores(self, seq_id: int):
+        cap = self.cfg.max_ctx
+        buf = (C.c_float * cap)()
+        n = load().dtd_debug_kv_scores(self.h, seq_id, buf, cap)
+        if n < 0:
+            raise DtdError(n, load().dtd_last_error(self.h).decode())
+        return np.array(buf[:n], dtype=np.float32)
 
     def seq_len(self, seq_id: int) -> int:
         return dtd_seq_len(self.h, seq_id)

@@ -249,6 +249,28 @@ dtd_status dtd_set_prefix_cache(dtd_engine* e, int32_t max_entries);
  * DTD_E_ARG for n outside [1, its length], DTD_E_STATE when the cache is off. */
 dtd_status dtd_prefix_cache_add(dtd_engine* e, int64_t seq_id, const int32_t* tokens_host, int32_t n);
 
+/* ---- KV budget ------------------------------------------------------------------------- */
+
+/* The Initial-Key cache of the nxmr.cn C17 engine article (5.3): from now on, whenever
+ * sequence seq_id holds more than `budget` KV entries after a prefill or decode step, its
+ * cache keeps only the entries of its first n_initial positions (where attention pools), its
+ * last n_recent entries, and, of the others, those with the largest sums of the attention
+ * they received (softmax probability, summed over the query heads and over the last
+ * score_layers layers, added at every decode step and, for a prefill, by its last position's
+ * query; the earlier entry wins equal sums); the rest are evicted and the kept entries are
+ * compacted, in order, into fresh KV blocks (synchronous: the host reads the sums).  Kept
+ * keys keep their RoPE rotation and new tokens are rotated by their true position, so a
+ * sequence's positions still end at max_ctx (the RoPE table); the budget bounds the KV blocks
+ * it holds.  With budget >= its length nothing is evicted and the outputs are the full
+ * cache's.  Budgeted sequences run the per-sub-step kernels, are never reused from or
+ * recorded in the prefix cache, and are refused by dtd_decode_step_noalloc.  budget 0 turns
+ * the budget off (entries already evicted stay evicted).  The sequence need not exist yet;
+ * dtd_reset_seq drops the setting.  DTD_E_ARG for budget < n_initial + n_recent + 1,
+ * n_recent < 1, budget > max_ctx or score_layers outside [1, n_layers]; DTD_E_STATE when
+ * setting a budget on a sequence whose entries were evicted before. */
+dtd_status dtd_set_kv_budget(dtd_engine* e, int64_t seq_id, int32_t budget, int32_t n_initial, int32_t n_recent,
+                             int32_t score_layers);
+
 /* ---- continuous batching ----------------------------------------------------------------- */
 
 /* A scheduler runs requests through one engine as continuous batches: the scheduling loop of
@@ -398,6 +420,12 @@ dtd_status dtd_debug_stream_read(const void* buf_dev, int64_t bytes, int32_t rep
 int32_t dtd_debug_prefix_reused(const dtd_engine* e, int64_t seq_id);
 int32_t dtd_debug_kv_blocks_free(const dtd_engine* e);
 int32_t dtd_debug_prefix_entries(const dtd_engine* e);
+
+/* A sequence's cache entries in order: their token positions (out_host [cap]; -1 where
+ * unknown) or their attention-score sums (synchronous).  Returns the entry count, or a
+ * dtd_status < 0. */
+int32_t dtd_debug_kv_positions(const dtd_engine* e, int64_t seq_id, int32_t* out_host, int32_t cap);
+int32_t dtd_debug_kv_scores(dtd_engine* e, int64_t seq_id, float* out_host, int32_t cap);
 
 /* Schedule selection.  path 0 (default): batch-1 steps run as one persistent kernel per
  * step (every phase in one cooperative launch) when the device allows it, other batches
