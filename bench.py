@@ -169,6 +169,9 @@ def main():
                     help="store the workload's matrices in this format instead of its own")
     ap.add_argument("--path", choices=["auto", "per-kernel", "persistent"], default="auto",
                     help="schedule: auto (persistent step kernel at batch 1), or force one")
+    ap.add_argument("--kv-budget", type=int, default=0, metavar="B",
+                    help="batch-1 workloads: decode under an Initial-Key KV budget of B entries "
+                         "(4 initial, 64 recent, the last 2 layers scored)")
     ap.add_argument("--serve", type=int, default=0, metavar="N",
                     help="instead of the decode step: N requests through the continuous-batching "
                          "scheduler (qwen3-8b-shaped unless --workload names another batched shape), "
@@ -237,6 +240,8 @@ def main():
         greedy decode steps, or synthetic KV (workloads that decode at a fixed context)."""
         if eng.seq_len(seq) >= 0:
             eng.reset_seq(seq)
+        if args.kv_budget:
+            eng.set_kv_budget(seq, args.kv_budget, n_initial=4, n_recent=64, score_layers=2)
         if real_prompt:
             nxt, _ = eng.prefill(seq, prompt)
             fill = torch.zeros(length - w.prompt_len + 1, dtype=torch.int32, device=dev)
@@ -265,13 +270,15 @@ def main():
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
     dtd.dtd_check_device_errors(eng.h)     # a device-side wait that gave up, or a bad token id
-    assert eng.seq_len(0) == w.context
+    assert eng.seq_len(0) == (min(w.context, args.kv_budget) if args.kv_budget else w.context)
     tokens = hist.cpu().numpy().copy()
 
     wb = weight_bytes(s)
     wtot = sum(v for k, v in wb.items() if k != "per_layer")
     kvpp = kv_bytes_per_position(s)
     attended_t = np.arange(start + 1, w.context + 1, dtype=np.float64)
+    if args.kv_budget:      # the kept entries and the new one
+        attended_t = np.minimum(attended_t, args.kv_budget + 1)
     kv_total = float(kvpp * attended_t.sum())
     bytes_total = wtot * K + kv_total
     gbs = bytes_total / dt / 1e9
@@ -347,7 +354,9 @@ def main():
                    "dim": s.dim, "layers": s.n_layers, "q_heads": s.n_q_heads, "kv_heads": s.n_kv_heads,
                    "head_dim": s.head_dim, "ffn": s.ffn_dim, "vocab": s.vocab,
                    "weights": synth.WFMT_NAMES[s.wfmt], "activations": synth.ACT_NAMES[s.act],
-                   "kv_cache": synth.KV_NAMES[s.kvfmt], "tied": bool(s.tied), "batch": 1},
+                   "kv_cache": synth.KV_NAMES[s.kvfmt], "tied": bool(s.tied), "batch": 1,
+                   **({"kv_budget": {"entries": args.kv_budget, "initial": 4, "recent": 64, "scored_layers": 2}}
+                      if args.kv_budget else {})},
         "hbm_gbs": round(gbs, 1),
         "hbm_frac_of_peak": round(gbs / PEAK_HBM_GBS, 4),
         "bytes_per_step": round(bytes_total / K),

@@ -244,16 +244,33 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
     const int kcpad = (kcn + KSTEP - 1) / KSTEP * KSTEP;
     if (kc0) __syncthreads();
     load_w(wa, qa, kc0, kcn, 0);     // the chunk's first weights are in flight while x is staged
-    for (int idx = threadIdx.x; idx < NB * kcpad; idx += 256) {
-      const int bb = idx / kcpad, kk = idx - bb * kcpad;
-      float v = 0.f;
-      if (bb < nb && kk < kcn) {
-        const size_t gi = (size_t)(b0 + bb) * K + kc0 + kk;
-        v = a.act_in == ACT_BF16 ? bf16_to_f32(((const uint16_t*)a.xin)[gi])
-                                 : ((const float*)a.xin)[gi];
+    // x staged 4 columns per access (K and every chunk are multiples of 4), four accesses in
+    // flight per thread: the staging is a few load latencies, not one per column
+    const int n4 = NB * kcpad / 4;
+    for (int base = threadIdx.x; base < n4; base += 256 * 4) {
+      float4 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; u++) {
+        const int idx = (base + u * 256) * 4, bb = idx / kcpad, kk = idx - bb * kcpad;
+        v[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (base + u * 256 < n4 && bb < nb && kk < kcn) {
+          const size_t gi = (size_t)(b0 + bb) * K + kc0 + kk;
+          if (a.act_in == ACT_BF16) {
+            const uint2 r = *(const uint2*)((const uint16_t*)a.xin + gi);
+            v[u] = make_float4(bf16_to_f32(r.x & 0xffffu), bf16_to_f32(r.x >> 16), bf16_to_f32(r.y & 0xffffu),
+                               bf16_to_f32(r.y >> 16));
+          } else {
+            v[u] = *(const float4*)((const float*)a.xin + gi);
+          }
+        }
       }
-      const int st = kk / KSTEP, r = kk - st * KSTEP, ln = r / VEC, j = r - ln * VEC;
-      xs[bb * KCP + st * KSTEP + (j >> 2) * 256 + ln * 4 + (j & 3)] = v;
+#pragma unroll
+      for (int u = 0; u < 4; u++) {
+        if (base + u * 256 >= n4) break;
+        const int idx = (base + u * 256) * 4, bb = idx / kcpad, kk = idx - bb * kcpad;
+        const int st = kk / KSTEP, r = kk - st * KSTEP, ln = r / VEC, j = r - ln * VEC;
+        *(float4*)&xs[bb * KCP + st * KSTEP + (j >> 2) * 256 + ln * 4] = v[u];
+      }
     }
     __syncthreads();
 
@@ -912,40 +929,59 @@ __global__ __launch_bounds__(256) void k_combine(Dims d, const StepDesc* desc, c
 
 // KV budget scores (the Initial-Key cache of the C17 engine article, 5.3): the softmax
 // probability each cache entry t <= pos of sequence b gets from this step's queries, summed
-// over the query heads, added to scores[slot][t].  Grid (B, entry tiles of 256); a thread
-// owns one entry (so the sum over heads has one fixed order), recomputes q_h . k_t / sqrt(d)
-// from the stored key and divides exp(s - M_h) by L_h from the merged attention statistics.
+// over the query heads, added to scores[slot][t].  Grid (B, tiles of 64 entries), four
+// waves: lane l of wave w takes entry (tile, l) against KV heads w, w+4, ...; it recomputes
+// q_h . k_t / sqrt(d) for that head's G query heads (q staged in LDS) from the stored key and
+// adds exp(s - M_h) / L_h with the merged attention statistics.  The waves' sums meet in LDS
+// and are added in wave order, so every entry's sum has one fixed order.
 template <int KVFMT>
 __global__ __launch_bounds__(256) void k_score(Dims d, const StepDesc* desc, int layer, const float* q,
                                                KvLayer kv, const int32_t* bt, const float* stat, float* scores) {
+  extern __shared__ float qs[];        // [q_dim] this row's queries, then [4][64] wave sums
   const int b = blockIdx.x;
   if (layer < desc->score_from[b]) return;
-  const int t = blockIdx.y * 256 + threadIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int i = threadIdx.x; i < d.q_dim; i += 256) qs[i] = q[(size_t)b * d.q_dim + i];
+  __syncthreads();
+  const int t = blockIdx.y * 64 + lane;
   const int pos = desc->pos[b], slot = desc->slot[b];
-  if (t > pos) return;
-  const int blk = bt[(size_t)slot * d.max_blocks + t / d.bs];
   const float scale = 1.f / sqrtf((float)d.hd);
   float sum = 0.f;
-  for (int j = 0; j < d.Hkv; j++) {
-    const size_t row = ((size_t)blk * d.Hkv + j) * d.bs + (t % d.bs);
-    float ks = 1.f;
-    if constexpr (KVFMT == KV_I8) ks = f16_to_f32(kv.ks[row]);
-    for (int g = 0; g < d.G; g++) {
-      const int h = j * d.G + g;
-      const float* qh = q + (size_t)b * d.q_dim + (size_t)h * d.hd;
-      float dot = 0.f;
-      for (int i = 0; i < d.hd; i++) {
-        float kval;
-        if constexpr (KVFMT == KV_F32) kval = ((const float*)kv.k)[row * d.hd + i];
-        else if constexpr (KVFMT == KV_BF16) kval = bf16_to_f32(((const uint16_t*)kv.k)[row * d.hd + i]);
-        else kval = (float)((const int8_t*)kv.k)[row * d.hd + i] * ks;
-        dot += qh[i] * kval;
+  if (t <= pos) {
+    const int blk = bt[(size_t)slot * d.max_blocks + t / d.bs];
+    for (int j = wave; j < d.Hkv; j += 4) {
+      const size_t row = ((size_t)blk * d.Hkv + j) * d.bs + (t % d.bs);
+      float ksc = 1.f;
+      if constexpr (KVFMT == KV_I8) ksc = f16_to_f32(kv.ks[row]);
+      for (int g = 0; g < d.G; g++) {
+        const int h = j * d.G + g;
+        const float* qh = qs + (size_t)h * d.hd;
+        float dot = 0.f;
+        for (int i = 0; i < d.hd; i += 4) {
+          float k4[4];
+          if constexpr (KVFMT == KV_F32) {
+            const float4 v = *(const float4*)((const float*)kv.k + row * d.hd + i);
+            k4[0] = v.x; k4[1] = v.y; k4[2] = v.z; k4[3] = v.w;
+          } else if constexpr (KVFMT == KV_BF16) {
+            const uint2 v = *(const uint2*)((const uint16_t*)kv.k + row * d.hd + i);
+            k4[0] = bf16_to_f32(v.x & 0xffffu); k4[1] = bf16_to_f32(v.x >> 16);
+            k4[2] = bf16_to_f32(v.y & 0xffffu); k4[3] = bf16_to_f32(v.y >> 16);
+          } else {
+            const uint32_t v = *(const uint32_t*)((const int8_t*)kv.k + row * d.hd + i);
+            for (int c = 0; c < 4; c++) k4[c] = sext8(v, c) * ksc;
+          }
+          for (int c = 0; c < 4; c++) dot += qh[i + c] * k4[c];
+        }
+        const float M = stat[((size_t)b * d.Hq + h) * 2], L = stat[((size_t)b * d.Hq + h) * 2 + 1];
+        sum += expf(dot * scale - M) / L;
       }
-      const float M = stat[((size_t)b * d.Hq + h) * 2], L = stat[((size_t)b * d.Hq + h) * 2 + 1];
-      sum += expf(dot * scale - M) / L;
     }
   }
-  scores[(size_t)slot * d.max_ctx + t] += sum;
+  float* ws = qs + d.q_dim;
+  ws[wave * 64 + lane] = sum;
+  __syncthreads();
+  if (wave == 0 && t <= pos)
+    scores[(size_t)slot * d.max_ctx + t] += ((ws[lane] + ws[64 + lane]) + ws[128 + lane]) + ws[192 + lane];
 }
 
 // KV budget eviction: copies cache entries keep[i] (i < n, through the old block list) to
@@ -958,13 +994,20 @@ __global__ __launch_bounds__(128) void k_kv_gather(const PLayer* layers, int Hkv
   const int i = blockIdx.y, t = keep[i];
   const int ob = old_blocks[t / bs], nb = new_blocks[i / bs];
   const size_t rowb = (size_t)hd * elem;
-  for (int j = 0; j < Hkv; j++) {
+  const bool wide = rowb % 16 == 0;          // rows of 16-byte pieces (every row starts aligned)
+  const size_t pieces = wide ? rowb / 16 : rowb;
+  for (size_t x = threadIdx.x; x < (size_t)Hkv * pieces; x += 128) {
+    const int j = (int)(x / pieces);
+    const size_t p = x - (size_t)j * pieces;
     const size_t src = ((size_t)ob * Hkv + j) * bs + (t % bs), dst = ((size_t)nb * Hkv + j) * bs + (i % bs);
-    for (size_t x = threadIdx.x; x < rowb; x += 128) {
-      ((uint8_t*)kv.k)[dst * rowb + x] = ((const uint8_t*)kv.k)[src * rowb + x];
-      ((uint8_t*)kv.v)[dst * rowb + x] = ((const uint8_t*)kv.v)[src * rowb + x];
+    if (wide) {
+      ((uint4*)kv.k)[dst * pieces + p] = ((const uint4*)kv.k)[src * pieces + p];
+      ((uint4*)kv.v)[dst * pieces + p] = ((const uint4*)kv.v)[src * pieces + p];
+    } else {
+      ((uint8_t*)kv.k)[dst * rowb + p] = ((const uint8_t*)kv.k)[src * rowb + p];
+      ((uint8_t*)kv.v)[dst * rowb + p] = ((const uint8_t*)kv.v)[src * rowb + p];
     }
-    if (kv.ks && threadIdx.x == 0) {
+    if (kv.ks && p == 0) {
       kv.ks[dst] = kv.ks[src];
       kv.vs[dst] = kv.vs[src];
     }
@@ -1269,10 +1312,11 @@ hipError_t launch_combine(const Dims& d, const StepDesc* desc, int B, const floa
 
 hipError_t launch_score(const Dims& d, const StepDesc* desc, int B, int max_pos, int layer, const float* q,
                         const KvLayer& kv, const int32_t* bt, const float* stat, float* scores, hipStream_t st) {
-  const dim3 grid(B, (max_pos + 1 + 255) / 256);
-  if (d.kvfmt == KV_F32) hipLaunchKernelGGL(k_score<KV_F32>, grid, dim3(256), 0, st, d, desc, layer, q, kv, bt, stat, scores);
-  else if (d.kvfmt == KV_BF16) hipLaunchKernelGGL(k_score<KV_BF16>, grid, dim3(256), 0, st, d, desc, layer, q, kv, bt, stat, scores);
-  else hipLaunchKernelGGL(k_score<KV_I8>, grid, dim3(256), 0, st, d, desc, layer, q, kv, bt, stat, scores);
+  const dim3 grid(B, (max_pos + 1 + 63) / 64);
+  const size_t smem = ((size_t)d.q_dim + 256) * 4;
+  if (d.kvfmt == KV_F32) hipLaunchKernelGGL(k_score<KV_F32>, grid, dim3(256), smem, st, d, desc, layer, q, kv, bt, stat, scores);
+  else if (d.kvfmt == KV_BF16) hipLaunchKernelGGL(k_score<KV_BF16>, grid, dim3(256), smem, st, d, desc, layer, q, kv, bt, stat, scores);
+  else hipLaunchKernelGGL(k_score<KV_I8>, grid, dim3(256), smem, st, d, desc, layer, q, kv, bt, stat, scores);
   return hipGetLastError();
 }
 
