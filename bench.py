@@ -80,18 +80,20 @@ def kernel_source_hash() -> str:
     return h.hexdigest()
 
 
-def recorded_traffic(workload: str, attended: str):
+def recorded_traffic(workload: str, attended: str, weights: str, kv_budget: int):
     """HBM bytes per step-kernel launch from the committed FETCH_SIZE / WRITE_SIZE readings of
-    this workload over the same attended contexts (each counter scaled by what it reads for
-    a plain copy of known size), or None when there are none, they cover other contexts, or
-    the kernel's sources have changed since they were taken."""
+    this workload (same weight format and KV budget) over the same attended contexts (each
+    counter scaled by what it reads for a plain copy of known size), or None when there are
+    none, they cover other contexts or another variant of the workload, or the kernel's
+    sources have changed since they were taken."""
     path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", f"k_step_traffic_{workload}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         doc = json.load(f)
     for r in doc.get("records", []):
-        if r.get("kernel_source_sha256") == kernel_source_hash() and r.get("attended") == attended:
+        if (r.get("kernel_source_sha256") == kernel_source_hash() and r.get("attended") == attended
+                and r.get("weights") == weights and r.get("kv_budget", 0) == kv_budget):
             return (r["fetch_kib_per_launch"] * r["fetch_scale"] + r["write_kib_per_launch"] * r["write_scale"]) * 1024.0
     return None
 
@@ -309,7 +311,8 @@ def main():
             name = "k_gemv (gate/up projection, SwiGLU epilogue)"
         avg_s = ms / 1e3 / max(cnt, 1)
         ach = per_launch / avg_s / 1e9 if cnt else 0.0
-        traffic = recorded_traffic(s.name, attended) if persistent else None
+        traffic = (recorded_traffic(s.name, attended, synth.WFMT_NAMES[s.wfmt], args.kv_budget)
+                   if persistent else None)
         roofline = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                     "frac": round(ach / PEAK_HBM_GBS, 4),
                     "traffic": None if traffic is None else round(traffic), "kernel": name,

@@ -127,6 +127,8 @@ struct dtd_engine {
   std::unordered_map<int64_t, KvBudget> budgets;   // sequences under a KV budget
   float* scores_dev = nullptr;    // [max_seqs][max_ctx] attention-score sums of budgeted sequences
   float* attn_stat = nullptr;     // [mb][Hq][2] merged softmax max and normaliser of a scored layer
+  float* p_score_q = nullptr;     // step kernel: [L][q_dim] queries of the scored layers
+  float* p_score_stat = nullptr;  // step kernel: [L][Hq][2] their softmax max and normaliser
   int32_t* evict_dev = nullptr;   // [3][max_ctx] eviction lists (old blocks, new blocks, kept entries)
   int step_score_min = 1 << 30;   // first scored layer of the step being run
   int step_max_pos = 0;
@@ -359,7 +361,7 @@ static void free_all(dtd_engine* e) {
   void* ps[] = {e->rope_cos, e->rope_sin, e->kpool, e->vpool, e->kspool, e->vspool, e->bt_dev,
                 e->x, e->xn, e->q, e->knew, e->vnew, e->partials, e->gemm_partials, e->o, e->h, e->logits,
                 e->err_dev, e->desc_dev, e->rows_dev, e->players, e->tags, e->tok_scratch,
-                e->scores_dev, e->attn_stat, e->evict_dev};
+                e->scores_dev, e->attn_stat, e->evict_dev, e->p_score_q, e->p_score_stat};
   for (void* p : ps)
     if (p) (void)hipFree(p);
   if (e->desc_host) (void)hipHostFree(e->desc_host);
@@ -452,6 +454,8 @@ extern "C" dtd_status dtd_create(const dtd_config* cfg, void* hip_stream, dtd_en
       (st = dev_alloc(e, &e->tok_scratch, (size_t)MB * 4)) ||
       (st = dev_alloc(e, &e->scores_dev, (size_t)cfg->max_seqs * cfg->max_ctx * 4)) ||
       (st = dev_alloc(e, &e->attn_stat, (size_t)MB * d.Hq * 2 * 4)) ||
+      (st = dev_alloc(e, &e->p_score_q, (size_t)d.L * d.q_dim * 4)) ||
+      (st = dev_alloc(e, &e->p_score_stat, (size_t)d.L * d.Hq * 2 * 4)) ||
       (st = dev_alloc(e, &e->evict_dev, (size_t)3 * cfg->max_ctx * 4)))
     return cleanup(st);
   if (hipMemset(e->err_dev, 0, 16) != hipSuccess) return cleanup(DTD_E_HIP);
@@ -469,9 +473,7 @@ extern "C" dtd_status dtd_create(const dtd_config* cfg, void* hip_stream, dtd_en
     }
     e->p_nch = (cfg->max_ctx + kAttnTile - 1) / kAttnTile;
     e->p_smem = persistent_smem_bytes(d, e->p_nch, cus > 0 ? cus : 1);
-    // the batch-1 step kernel is built for int8-row, Q8_0 and bf16 weights; Q4_0 runs the
-    // per-sub-step kernels at every batch size
-    if (coop && cus > 0 && d.wfmt != W_Q4_0 && persistent_supports(d) && persistent_prepare(d, e->p_smem, &per_cu) == hipSuccess &&
+    if (coop && cus > 0 && persistent_supports(d) && persistent_prepare(d, e->p_smem, &per_cu) == hipSuccess &&
         per_cu >= 1) {
       e->persist_ok = true;
       e->nwg = cus;
@@ -776,8 +778,6 @@ static dtd_status run_step(dtd_engine* e, int B, const int* slots, const int* po
     e->step_score_min = std::min(e->step_score_min, hd->score_from[b]);
     e->step_max_pos = std::max(e->step_max_pos, poss[b]);
   }
-  // RoPE positions and score sums are only in the per-sub-step kernels
-  if (extra) force_per_kernel = true;
   for (int u = 0; u < n_upd; u++) {
     hd->upd[u][0] = upd[u].slot; hd->upd[u][1] = upd[u].lblock; hd->upd[u][2] = upd[u].pblock;
   }
@@ -828,9 +828,23 @@ static dtd_status run_step(dtd_engine* e, int B, const int* slots, const int* po
     a.inject = inject;
     a.capture = capture;
     a.po = probe_layout(d, 1, act_bytes(e->cfg.act));
+    a.score_q = e->p_score_q;
+    a.score_stat = e->p_score_stat;
     TIMED(6, launch_persistent(a, e->nwg, e->p_smem, st));
     e->epoch += ntag;
-      return DTD_OK;
+    // a KV budget's score sums over the scored layers, from the queries and softmax
+    // statistics the step kernel kept (the new entry is in the cache by now)
+    const size_t kvb = kv_elem_bytes(e->cfg.kvfmt);
+    for (int l = std::max(e->step_score_min, 0); l < d.L; l++) {
+      KvLayer kv;
+      kv.k = (uint8_t*)e->kpool + (size_t)l * e->kv_layer_elems * kvb;
+      kv.v = (uint8_t*)e->vpool + (size_t)l * e->kv_layer_elems * kvb;
+      kv.ks = e->kspool ? e->kspool + (size_t)l * e->kv_layer_scales : nullptr;
+      kv.vs = e->vspool ? e->vspool + (size_t)l * e->kv_layer_scales : nullptr;
+      HIP_OK(e, launch_score(d, e->desc_dev, 1, e->step_max_pos, l, e->p_score_q + (size_t)l * d.q_dim, kv,
+                             e->bt_dev, e->p_score_stat + (size_t)l * d.Hq * 2, e->scores_dev, st));
+    }
+    return DTD_OK;
   }
   if (e->path == 2 && !force_per_kernel)
     return fail(e, DTD_E_UNSUPPORTED, "persistent step kernel unavailable for this call");

@@ -132,6 +132,11 @@ struct PersistArgs {
   const uint8_t* inject;    // probe records (null: normal step)
   uint8_t* capture;
   ProbeLayout po;
+  // layers from the descriptor's score_from[0] on (a KV budget's scored layers): each one's
+  // post-RoPE queries [L][q_dim] and per-head softmax (max, sum) [L][Hq][2], for the score
+  // sums computed after the step
+  float* score_q;
+  float* score_stat;
 };
 
 // Packed hand-off of the SwiGLU output with bf16 activations: each workgroup of the step

@@ -51,51 +51,9 @@ constexpr unsigned kSpinLimit = 1u << 20;
 // argmax words take epoch + L * kTagsPerLayer
 enum { TG_QKV = 0, TG_PART = 1, TG_O = 2, TG_XM = 3, TG_H = 4, TG_XO = 5, kTagsPerLayer = 6 };
 
-#ifdef DTD_PHASE_TRACE
-// Phase timeline, in a profiling build only: wave 0 of each workgroup records the 100 MHz
-// real-time counter at every phase boundary (1 + 11 per layer + 3 events).
-constexpr int kTraceWG = 256, kTraceEv = 512;
-__device__ uint64_t g_phase_trace[kTraceWG * kTraceEv];
-#define PTRACE(ev)                                                                          \
-  do {                                                                                      \
-    if (threadIdx.x == 0 && blockIdx.x < kTraceWG && (ev) < kTraceEv)                       \
-      g_phase_trace[blockIdx.x * kTraceEv + (ev)] = __builtin_amdgcn_s_memrealtime();       \
-  } while (0)
-// timestamps inside a streaming loop go to LDS first (a global store there would make the
-// compiler drain all loads in flight at every later wait)
-__shared__ unsigned long long g_trace_lds[16];
-#define PTRACE_LDS(k)                                                                      \
-  do {                                                                                     \
-    if (threadIdx.x == 0 && (k) < 16) g_trace_lds[(k)] = __builtin_amdgcn_s_memrealtime();   \
-  } while (0)
-// a value instead of a time stamp
-#define PTRACE_SET(ev, val)                                                                 \
-  do {                                                                                      \
-    if (threadIdx.x == 0 && blockIdx.x < kTraceWG && (ev) < kTraceEv)                       \
-      g_phase_trace[blockIdx.x * kTraceEv + (ev)] = (val);                                  \
-  } while (0)
-// inside an attention item: only when the caller set the item-trace flag
-#define ITRACE(ev) \
-  do {                 \
-    if (itrace) PTRACE(ev); \
-  } while (0)
-#else
-#define ITRACE(ev) \
-  do {              \
-  } while (0)
-#define PTRACE_SET(ev, val) \
-  do {                      \
-  } while (0)
-#define PTRACE(ev) \
-  do {             \
-  } while (0)
-#define PTRACE_LDS(k) \
-  do {                \
-  } while (0)
-#endif
-
 template <int WFMT> struct PVec { static constexpr int VEC = 16; };   // elements per 16 B
 template <> struct PVec<W_BF16> { static constexpr int VEC = 8; };
+template <> struct PVec<W_Q4_0> { static constexpr int VEC = 32; };   // one Q4_0 block
 
 // ---------------------------------------------------------------------------------------
 // tagged words
@@ -252,7 +210,7 @@ __device__ __forceinline__ PPhase make_phase(const MatDev& m, int g, int nwg) {
   p.s = (const uint8_t*)m.s;
   p.N = m.rows;
   p.K = m.cols;
-  p.Kb = m.cols * (WFMT == W_BF16 ? 2 : 1);
+  p.Kb = WFMT == W_BF16 ? m.cols * 2 : (WFMT == W_Q4_0 ? m.cols >> 1 : m.cols);
   const int cpr = (p.Kb + 1023) >> 10;   // 1 KB lines per row
   // Row pairs are dealt out round-robin (workgroup g owns pairs g, g + nwg, ...), not in one
   // contiguous slice per workgroup: every hand-off lines all workgroups up at the start of a
@@ -309,7 +267,7 @@ template <int WFMT> struct Grp {
 
 struct WBuf {
   v4u w[GRP];
-  uint32_t sc[GRP];   // Q8_0: fp16 block scale bits; int8-row: fp32 row scale bits
+  uint32_t sc[GRP];   // Q8_0, Q4_0: fp16 block scale bits; int8-row: fp32 row scale bits
 };
 
 // A wave's stream in one phase: its row pairs in turn, each pair as 2*cpr lines that
@@ -324,7 +282,8 @@ struct ICur {
 };
 
 // Issues the next GRP lines of this wave's stream in phase p, with their scales (Q8_0: the
-// line's block scale; int8-row: the row scale), and advances the cursor.  Every call issues
+// block scale of the lane's 16 columns; Q4_0: the scale of the lane's whole block of 32;
+// int8-row: the row scale), and advances the cursor.  Every call issues
 // the same loads whatever the phase: a line (or a lane's part of one) outside the matrix reads
 // offset 0 of the matrix instead, and its value is never used (whole lines are skipped by the
 // consumer; a lane's part past the row end meets the input vector's zero padding).  Addresses
@@ -341,6 +300,8 @@ __device__ __forceinline__ void issue_group(const PPhase& p, ICur& ic, WBuf& b) 
     b.w[s] = gload_stream<v4u>(p.w + (ok ? (uint32_t)row * (uint32_t)p.Kb + (uint32_t)cb : 0u));
     if constexpr (WFMT == W_Q8_0)
       b.sc[s] = gload<uint16_t>(p.s + (ok ? ((uint32_t)row * (uint32_t)(p.K >> 5) + (uint32_t)(cb >> 5)) * 2u : 0u));
+    else if constexpr (WFMT == W_Q4_0)
+      b.sc[s] = gload<uint16_t>(p.s + (ok ? ((uint32_t)row * (uint32_t)(p.K >> 5) + (uint32_t)(cb >> 4)) * 2u : 0u));
     else if constexpr (WFMT == W_INT8_ROW)
       b.sc[s] = gload<uint32_t>(p.s + (rok ? (uint32_t)row * 4u : 0u));
     if (s & 1) {
@@ -528,11 +489,47 @@ struct Cursor {
   float rsc0, rsc1;   // int8-row: scales of the pair's rows
 };
 
-// dot product of one line (16 bytes per lane) with this lane's input chunk
+// Q4_0 nibble k (0..7) of v as (q - 8) / 16, where v holds the codes with bit 3 of every
+// nibble flipped: a nibble q ^ 8 read as a signed 4-bit integer is q - 8, and
+// v_cvt_off_f32_i4 converts the low 4 bits of its operand to that integer / 16.  The
+// operand's byte comes straight out of the register (an SDWA byte select), so an even nibble
+// costs one instruction and the odd ones share one shift per dword.
+template <int SEL>
+__device__ __forceinline__ float q4_byte(uint32_t v) {
+  float r;
+  if constexpr (SEL == 0)
+    asm("v_cvt_off_f32_i4_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_0" : "=v"(r) : "v"(v));
+  else if constexpr (SEL == 1)
+    asm("v_cvt_off_f32_i4_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_1" : "=v"(r) : "v"(v));
+  else if constexpr (SEL == 2)
+    asm("v_cvt_off_f32_i4_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_2" : "=v"(r) : "v"(v));
+  else
+    asm("v_cvt_off_f32_i4_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_3" : "=v"(r) : "v"(v));
+  return r;
+}
+
+// dot product of one line (16 bytes per lane) with this lane's input chunk; Q4_0 lines give
+// it / 16 (the scale carries the factor 16)
 template <int WFMT>
-__device__ __forceinline__ float line_dot(const v4u& v, const float4 (&x)[WFMT == W_BF16 ? 2 : 4]) {
+__device__ __forceinline__ float line_dot(const v4u& v, const float4 (&x)[PVec<WFMT>::VEC / 4]) {
   float part = 0.f;
-  if constexpr (WFMT == W_BF16) {
+  if constexpr (WFMT == W_Q4_0) {
+    // the lane's 16 bytes are one block of 32 columns: byte b holds column b in its low 4
+    // bits and column b + 16 in its high 4 bits (the Q4_0 block of "Go 语言原本" 20.2.4)
+    const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+      const uint32_t lo = u[q] ^ 0x88888888u, hi = lo >> 4;
+      part = fmaf(q4_byte<0>(lo), x[q].x, part);
+      part = fmaf(q4_byte<1>(lo), x[q].y, part);
+      part = fmaf(q4_byte<2>(lo), x[q].z, part);
+      part = fmaf(q4_byte<3>(lo), x[q].w, part);
+      part = fmaf(q4_byte<0>(hi), x[4 + q].x, part);
+      part = fmaf(q4_byte<1>(hi), x[4 + q].y, part);
+      part = fmaf(q4_byte<2>(hi), x[4 + q].z, part);
+      part = fmaf(q4_byte<3>(hi), x[4 + q].w, part);
+    }
+  } else if constexpr (WFMT == W_BF16) {
     const uint32_t u[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
     for (int q = 0; q < 4; q++) {
@@ -563,19 +560,19 @@ __device__ __forceinline__ float line_dot(const v4u& v, const float4 (&x)[WFMT =
 template <int WFMT>
 __device__ __forceinline__ void consume_group(const PPhase& p, int c0, int total, const WBuf& b, const float4* x4,
                                               Cursor& cu, float* ores) {
-  const int wave = wave_id(), lane = threadIdx.x & 63;
+  const int lane = threadIdx.x & 63;
   if (c0 >= total) {   // a pad group (wave-uniform): its registers are read, nothing else
     // (the scales in the form the products use, so that no conversion of them is placed
     // next to their loads)
 #pragma unroll
     for (int s = 0; s < GRP; s++) {
       settle(b.w[s]);
-      if constexpr (WFMT == W_Q8_0) settle(f16_to_f32((uint16_t)b.sc[s]));
+      if constexpr (WFMT == W_Q8_0 || WFMT == W_Q4_0) settle(f16_to_f32((uint16_t)b.sc[s]));
       else if constexpr (WFMT == W_INT8_ROW) settle(__uint_as_float(b.sc[s]));
     }
     return;
   }
-  constexpr int XQ = WFMT == W_BF16 ? 2 : 4;   // float4 of input per lane and line
+  constexpr int XQ = PVec<WFMT>::VEC / 4;      // float4 of input per lane and line
   constexpr int NS = GRP / 2;                  // line steps in a group
   // all steps' input chunks first, so their LDS round trips overlap (a pad step reads some
   // chunk below cpr)
@@ -596,6 +593,9 @@ __device__ __forceinline__ void consume_group(const PPhase& p, int c0, int total
   if constexpr (WFMT == W_Q8_0) {
 #pragma unroll
     for (int s = 0; s < GRP; s++) part[s] *= f16_to_f32((uint16_t)b.sc[s]);
+  } else if constexpr (WFMT == W_Q4_0) {   // (q - 8) / 16 above: the factor 16 goes with d
+#pragma unroll
+    for (int s = 0; s < GRP; s++) part[s] *= 16.f * f16_to_f32((uint16_t)b.sc[s]);
   }
 #pragma unroll
   for (int st = 0; st < GRP / 2; st++) {
@@ -913,8 +913,7 @@ __host__ __device__ inline size_t attn_p_floats(int G, int hd) {
 template <int KVFMT, typename Put>
 __device__ __forceinline__ void attn_item_p(const Dims& d, const KvLayer& kv, const int* bt_s, int j, int c,
                                             int ct, int nch, int pos, int pos_blk, const float* qg, const float* kn,
-                                            const float* vn, float* sm, KvRegs<KVFMT>& kr, Put put,
-                                            bool itrace = false) {
+                                            const float* vn, float* sm, KvRegs<KVFMT>& kr, Put put) {
   const int hd = d.hd, G = d.G, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int t_begin = c * ct, t_end = min(pos + 1, t_begin + ct), ldk = kv_ld(hd);
   float* q_s = sm;                          // [G][hd], pre-scaled by 1/sqrt(hd)
@@ -938,7 +937,6 @@ __device__ __forceinline__ void attn_item_p(const Dims& d, const KvLayer& kv, co
   float acc[kAttnOut];
 #pragma unroll
   for (int k = 0; k < kAttnOut; k++) acc[k] = 0.f;
-  ITRACE(403);
 
   for (int t0 = t_begin; t0 < t_end; t0 += kAttnTile) {
     const int n = min(kAttnTile, t_end - t0);
@@ -949,7 +947,6 @@ __device__ __forceinline__ void attn_item_p(const Dims& d, const KvLayer& kv, co
     kv_store<KVFMT>(d, kr, t0, n, pos, new_s, ks_s, vs_s, tk, tv);
     if (t0 + kAttnTile < t_end) kv_issue<KVFMT>(d, kv, bt_s, j, t0 + kAttnTile, min(kAttnTile, t_end - t0 - kAttnTile), kr);
     __syncthreads();
-    ITRACE(404);
     // Scores on the matrix cores, heads in groups of 4: one v_mfma_f32_4x4x1f32 multiplies,
     // for one head dimension d, the 64 tile rows (A: lane t holds k[t][d]) by 4 queries (B:
     // lane t holds q[4 hg + t % 4][d], 0 past the last head); lane t then holds
@@ -1003,7 +1000,6 @@ __device__ __forceinline__ void attn_item_p(const Dims& d, const KvLayer& kv, co
       }
     }
     __syncthreads();
-    ITRACE(405);
     // P V on the matrix cores, per group of 4 heads: one MFMA per tile row t multiplies 64
     // head dimensions (A: lane holds v[t][64 half + lane]) by 4 probabilities (B: lane holds
     // p[4 hg + lane % 4][t]); lane l then holds O[64 half + 4(l/4) + r][4 hg + l % 4].  Wave w
@@ -1048,7 +1044,6 @@ __device__ __forceinline__ void attn_item_p(const Dims& d, const KvLayer& kv, co
     }
   }
   __syncthreads();
-  ITRACE(406);
   const int cs = hd + 2;
 #pragma unroll
   for (int k = 0; k < kAttnOut; k++) {
@@ -1117,7 +1112,7 @@ __global__ __launch_bounds__(PT) void k_step(PersistArgs a) {
   __shared__ int sfail;
   __shared__ float wbest[PW];
   __shared__ int widx[PW];
-  __shared__ float rope_s[128];       // cos | sin of this step's position (hd <= 128)
+  __shared__ float rope_s[128];       // cos | sin of this step's token position (hd <= 128)
   // The common attention shape as constants where the instantiation names it (HD > 0: head
   // size HD, 4 query heads per KV head, KV blocks of 16 positions): the attention item's and
   // the merge's divisions, strides, loop and split counts by them then fold away.
@@ -1143,14 +1138,16 @@ __global__ __launch_bounds__(PT) void k_step(PersistArgs a) {
   auto inj = [&](int l, size_t off) { return (const void*)(a.inject + (size_t)l * a.po.record + off); };
   auto cap = [&](int l, size_t off) { return (void*)(a.capture + (size_t)l * a.po.record + off); };
 
-  PTRACE(0);
   if (tid == 0) sfail = 0;
   int tok = desc->tokens[0];
   if (tok < 0 || tok >= d.V) {
     if (tid == 0) __hip_atomic_fetch_or(err, kErrToken, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     tok = 0;
   }
-  const int pos = desc->pos[0], slot = desc->slot[0], pos_blk = desc->pos_block[0];
+  // pos: the new entry's cache index (attention covers entries 0..pos); rpos: the token's
+  // position in the text, which RoPE rotates by (they differ once a KV budget has evicted)
+  const int pos = desc->pos[0], slot = desc->slot[0], pos_blk = desc->pos_block[0], rpos = desc->rpos[0];
+  const int score_from = desc->score_from[0];
   const bool do_head = desc->do_head != 0;
 
   WBuf pre, preb;   // weight groups in flight (A, B of gemv_phase)
@@ -1176,8 +1173,8 @@ __global__ __launch_bounds__(PT) void k_step(PersistArgs a) {
         a.bt[(size_t)desc->upd[u][0] * d.max_blocks + desc->upd[u][1]] = desc->upd[u][2];
   }
   for (int i = tid; i < (hd >> 1); i += PT) {
-    rope_s[i] = gload<float>(a.rope_cos + (size_t)pos * (hd >> 1) + i);
-    rope_s[(hd >> 1) + i] = gload<float>(a.rope_sin + (size_t)pos * (hd >> 1) + i);
+    rope_s[i] = gload<float>(a.rope_cos + (size_t)rpos * (hd >> 1) + i);
+    rope_s[(hd >> 1) + i] = gload<float>(a.rope_sin + (size_t)rpos * (hd >> 1) + i);
   }
   // layer-0 input: the token's embedding row, dequantised by every workgroup
   if (!probe)
@@ -1198,8 +1195,6 @@ __global__ __launch_bounds__(PT) void k_step(PersistArgs a) {
     const int l = q >> 2;                        // layer (d.L for the head)
     const int k = q == 4 * d.L ? PH_HEAD : (q & 3);
     CPLayer* Ly = layers + (l < d.L ? l : d.L - 1);
-    const int tb = 1 + l * 11;
-    PTRACE(k == PH_HEAD ? tb : tb + (k == PH_QKV ? 0 : 2 * k + 2));
 
     // The phase after this one (its first weight groups are issued at the end of this
     // projection; after QKV none: the O projection's weights are issued after attention,
@@ -1229,9 +1224,7 @@ __global__ __launch_bounds__(PT) void k_step(PersistArgs a) {
         const uint64_t* src = k == PH_GU ? a.t_xm : a.t_xo;
         gather(d.D, k == PH_GU ? T(l, TG_XM) : T(l - 1, TG_XO), err, &sfail, [&](int i) { return src + i; },
                [&](int i, float v) { xf[i] = v; });
-        if (l == 5 && k == PH_GU) PTRACE(452);
         __syncthreads();
-        if (l == 5 && k == PH_GU) PTRACE(453);
         if (sfail) return;
       }
       // Every path reads the gains (gn): a load whose register is never read stays pending
@@ -1250,7 +1243,6 @@ __global__ __launch_bounds__(PT) void k_step(PersistArgs a) {
         }
       } else {
         norm_lds<VEC>(xf, gn, d.D, d.eps, act, xs, nullptr, red);
-        if (l == 5 && k == PH_GU) PTRACE(454);
       }
     } else {
       // the attention output (O) or the SwiGLU output (down), as produced
@@ -1267,7 +1259,6 @@ __global__ __launch_bounds__(PT) void k_step(PersistArgs a) {
           // fq + (gp < fr) SwiGLU outputs: no integer division per word on the way in.
           const uint64_t hs_inv = 0xffffffffull / (uint64_t)hs + 1ull;
           const int fq = d.F / nwg, fr = d.F - fq * nwg;
-          if (l == 5) PTRACE(415);
           zero_tail<VEC>(d.F, xs);
           gather_words<8, 48>(nwg * hs, T(l, TG_H) & 0xffffu, err, &sfail, [&](int w) { return a.t_h + w; },
                               [&](int w, uint64_t word) {
@@ -1280,7 +1271,6 @@ __global__ __launch_bounds__(PT) void k_step(PersistArgs a) {
                                     xs[swz<VEC>(gp + nwg * t)] = __uint_as_float((uint32_t)(word >> (16 * hh)) << 16);
                                 }
                               });
-          if (l == 5) PTRACE(416);
         }
       } else {
         stage_tagged<VEC>(is_o ? a.t_o : a.t_h, T(l, is_o ? TG_O : TG_H), is_o ? d.q_dim : d.F, xs, err, &sfail);
@@ -1292,7 +1282,6 @@ __global__ __launch_bounds__(PT) void k_step(PersistArgs a) {
     __syncthreads();
 
     // ---- the projection; the next one's first weight groups are issued at its end ----
-    PTRACE(k == PH_HEAD ? tb + 1 : tb + (k == PH_QKV ? 1 : 2 * k + 3));
 #pragma unroll
     for (int i = 0; i < kNormV; i++) settle(gn[i]);   // no gain load may reach the stream
     // The loop ends with loads of nothing (pad groups) in A and B; the next phase's first
@@ -1300,13 +1289,7 @@ __global__ __launch_bounds__(PT) void k_step(PersistArgs a) {
     // so issued before the epilogue they would hold up its stores, which publish what every
     // other workgroup waits for, until their own data had come in.
     gemv_phase<WFMT>(ph, pre, preb, xs, ores, ic);
-#ifdef DTD_PHASE_TRACE
-    if (l == 5 && (k == PH_GU || k == PH_DOWN) && lane == 0)
-      g_phase_trace[g * kTraceEv + 430 + (k == PH_GU ? 0 : 10) + wave] = __builtin_amdgcn_s_memrealtime();
-#endif
     __syncthreads();
-    if (l == 5 && k == PH_GU) PTRACE(438);
-    if (l == 5 && k == PH_DOWN) PTRACE(448);
 
     // ---- epilogue ----
     if (k == PH_QKV) {
@@ -1330,7 +1313,6 @@ __global__ __launch_bounds__(PT) void k_step(PersistArgs a) {
       e.hs = h_words_per_wg(d.F, nwg);
       e.ch = probe ? cap(l, a.po.h) : nullptr;
       phase_epilogue<EPI_SWIGLU>(d, ph, ores, e);
-      if (l == 5) PTRACE(439);
     } else {
       phase_epilogue<EPI_LOGITS>(d, ph, ores, e);
     }
@@ -1340,7 +1322,6 @@ __global__ __launch_bounds__(PT) void k_step(PersistArgs a) {
       issue_group<WFMT>(nx, ic, pre);
       issue_group<WFMT>(nx, ic, preb);
     }
-    PTRACE(k == PH_HEAD ? tb + 2 : tb + (k == PH_QKV ? 2 : 2 * k + 4));
 
     if (k == PH_QKV) {
       // ---- KV append + split-K attention ----
@@ -1373,13 +1354,13 @@ __global__ __launch_bounds__(PT) void k_step(PersistArgs a) {
         }
         __syncthreads();
         if (sfail) return;
-        if (l == 5) PTRACE(400);
+        // a scored layer keeps its queries for the score sums (the head group's first chunk)
+        if (l >= score_from && c == 0)
+          for (int t = tid; t < G * hd; t += PT) a.score_q[(size_t)l * d.q_dim + j * G * hd + t] = ain[t];
         uint64_t* tp = a.t_part;
         attn_item_p<KVFMT>(d, lkv, bt_s, j, c, a.ct, a.nch, pos, pos_blk, ain, ain + G * hd, ain + G * hd + hd,
-                           smem, kr, [tp, tpart](size_t i, float v) { put_tag(tp + i, tpart, v); }, l == 5);
-        if (l == 5) PTRACE(401);
+                           smem, kr, [tp, tpart](size_t i, float v) { put_tag(tp + i, tpart, v); });
       }
-      PTRACE(tb + 3);
       // the O projection's first weight groups, on their way during the merge (a merging
       // workgroup would otherwise be the last to start O, and every workgroup waits for its rows)
       nx = make_phase<WFMT>(cmat(&Ly->o), g, nwg);
@@ -1405,7 +1386,6 @@ __global__ __launch_bounds__(PT) void k_step(PersistArgs a) {
                  [&](int t, float v) { ml[t] = v; });
           __syncthreads();
           if (sfail) return;
-          if (l == 5) PTRACE(402);
           if (wave == 0) {   // weights e^(m_c - M) and their l sum
             float M = -INFINITY;
             for (int cc = lane; cc < nv; cc += 64) M = fmaxf(M, ml[cc * 2]);
@@ -1417,10 +1397,15 @@ __global__ __launch_bounds__(PT) void k_step(PersistArgs a) {
               L += wt * ml[cc * 2 + 1];
             }
             L = wave_total(L);
-            if (lane == 0) Lsum[0] = L;
+            if (lane == 0) {
+              Lsum[0] = L;
+              if (l >= score_from) {   // a scored layer: the head's softmax max and sum
+                a.score_stat[((size_t)l * d.Hq + h) * 2] = M;
+                a.score_stat[((size_t)l * d.Hq + h) * 2 + 1] = L;
+              }
+            }
           }
           __syncthreads();
-          if (l == 5) PTRACE(409);
           float acc = 0.f;
           for (int c0 = 0; c0 < nv; c0 += MB * NP) {
             uint64_t w[MB];
@@ -1455,9 +1440,7 @@ __global__ __launch_bounds__(PT) void k_step(PersistArgs a) {
               put_tag(a.t_o + h * hd + tid, T(l, TG_O), o);
             }
           }
-          if (l == 5) PTRACE(410);
           __syncthreads();
-          if (l == 5) PTRACE(411);
         }
       }
       __syncthreads();
@@ -1506,7 +1489,6 @@ __global__ __launch_bounds__(PT) void k_step(PersistArgs a) {
     if (ov > b || (ov == b && oi < bi)) { b = ov; bi = oi; }
   }
   if (lane == 0) desc->next_tokens[0] = bi == INT_MAX ? 0 : bi;
-  PTRACE(3 + d.L * 11);
 }
 
 // The normal step per activation type, with the attention shape of the target models (head
@@ -1542,6 +1524,11 @@ const void* pick(const Dims& d, bool probe) {
     if (kvfmt == KV_BF16) return step_kernel<W_Q8_0, KV_BF16>(probe, act, fixed);
     return step_kernel<W_Q8_0, KV_I8>(probe, act, fixed);
   }
+  if (wfmt == W_Q4_0) {
+    if (kvfmt == KV_F32) return step_kernel<W_Q4_0, KV_F32>(probe, act, fixed);
+    if (kvfmt == KV_BF16) return step_kernel<W_Q4_0, KV_BF16>(probe, act, fixed);
+    return step_kernel<W_Q4_0, KV_I8>(probe, act, fixed);
+  }
   if (kvfmt == KV_F32) return step_kernel<W_BF16, KV_F32>(probe, act, fixed);
   if (kvfmt == KV_BF16) return step_kernel<W_BF16, KV_BF16>(probe, act, fixed);
   return step_kernel<W_BF16, KV_I8>(probe, act, fixed);
@@ -1552,7 +1539,7 @@ const void* pick(const Dims& d, bool probe) {
 bool persistent_fixed_shape(const Dims& d) { return d.hd == 128 && d.G == kFixedG && d.bs == kFixedBs; }
 
 size_t persistent_xs_floats(const Dims& d, int nch) {
-  const int vec = d.wfmt == W_BF16 ? 8 : 16, kstep = 64 * vec;
+  const int vec = d.wfmt == W_BF16 ? 8 : (d.wfmt == W_Q4_0 ? 32 : 16), kstep = 64 * vec;
   int kmax = d.D > d.F ? d.D : d.F;
   if (d.q_dim > kmax) kmax = d.q_dim;
   size_t need = (size_t)(kmax + kstep - 1) / kstep * kstep;                             // projection input
@@ -1604,10 +1591,3 @@ hipError_t launch_persistent(const PersistArgs& a, int nwg, size_t smem, hipStre
 
 }  // namespace dtd
 
-#ifdef DTD_PHASE_TRACE
-// copies the phase timeline of the last launch ([256][512] uint64) to host memory
-extern "C" int dtd_phase_trace_dump(void* host, size_t bytes) {
-  if (bytes > sizeof(dtd::g_phase_trace)) bytes = sizeof(dtd::g_phase_trace);
-  return hipMemcpyFromSymbol(host, HIP_SYMBOL(dtd::g_phase_trace), bytes, 0, hipMemcpyDeviceToHost) == hipSuccess ? 0 : 1;
-}
-#endif

@@ -55,8 +55,7 @@ typedef enum {
  *   BF16:     bf16 bit patterns [rows][cols];
  *   Q4_0:     4-bit codes in blocks of 32 columns, 16 bytes per block [rows][cols/2] (byte j
  *             of a block: column j in the low 4 bits, column j+16 in the high 4 bits), plus
- *             one fp16 scale per block [rows][cols/32]; W = (q - 8) * d ("Go 语言原本" 20.2.4).
- *             The batch-1 step kernel does not take it: Q4_0 runs the per-sub-step kernels. */
+ *             one fp16 scale per block [rows][cols/32]; W = (q - 8) * d ("Go 语言原本" 20.2.4). */
 enum { DTD_W_INT8_ROW = 0, DTD_W_Q8_0 = 1, DTD_W_BF16 = 2, DTD_W_Q4_0 = 3 };
 /* activation storage type at the rounding points: each RMSNorm output, the attention
  * output and the SwiGLU output.  The residual stream, queries, scores, softmax,
@@ -262,8 +261,10 @@ dtd_status dtd_prefix_cache_add(dtd_engine* e, int64_t seq_id, const int32_t* to
  * keys keep their RoPE rotation and new tokens are rotated by their true position, so a
  * sequence's positions still end at max_ctx (the RoPE table); the budget bounds the KV blocks
  * it holds.  With budget >= its length nothing is evicted and the outputs are the full
- * cache's.  Budgeted sequences run the per-sub-step kernels, are never reused from or
- * recorded in the prefix cache, and are refused by dtd_decode_step_noalloc.  budget 0 turns
+ * cache's.  A budgeted sequence decoding alone runs the batch-1 step kernel (which keeps
+ * the scored layers' queries and softmax statistics for the score sums that follow it); in
+ * a batch or a prefill chunk it runs the per-sub-step kernels.  Budgeted sequences are never
+ * reused from or recorded in the prefix cache, and are refused by dtd_decode_step_noalloc.  budget 0 turns
  * the budget off (entries already evicted stay evicted).  The sequence need not exist yet;
  * dtd_reset_seq drops the setting.  DTD_E_ARG for budget < n_initial + n_recent + 1,
  * n_recent < 1, budget > max_ctx or score_layers outside [1, n_layers]; DTD_E_STATE when
@@ -395,9 +396,15 @@ dtd_status dtd_debug_kv_write(dtd_engine* e, int64_t seq_id, int32_t layer, int3
 dtd_status dtd_debug_kv_read(dtd_engine* e, int64_t seq_id, int32_t layer, int32_t pos0,
                              int32_t n, void* k, void* v, void* k_scale, void* v_scale);
 
-/* Sets a sequence's length to len (creating it if new) with synthetic KV in every layer:
- * values from a counter-based hash of (seed, layer, position, head, i), spread like
- * N(0, (0.02*sqrt(D))^2) but not Gaussian.  For timing long contexts only. */
+/* Sets a sequence's length to len (creating it if new) with synthetic KV in every layer;
+ * for timing long contexts only.  Element i of KV head j at position t of layer l, for K
+ * (w = 0) and V (w = 1): h = m(seed ^ m(l<<40 ^ t<<20 ^ j<<12 ^ i<<1 ^ w)) with m the
+ * splitmix64 finaliser, u = (h>>40) * 2^-23 - 1 in [-1, 1), and the value u * a with
+ * a = 0.02 * sqrt(D) * 1.7320508 in fp32 (uniform with the standard deviation
+ * 0.02 * sqrt(D)); bf16 stores it rounded to nearest even; int8 stores rint(127 u) with
+ * the fp16 scale a / 127.  Positions below len of a longer sequence are overwritten and
+ * its length is kept.  Errors: DTD_E_ARG for len outside [1, max_ctx], DTD_E_KVFULL
+ * when the sequence slots or KV blocks run out. */
 dtd_status dtd_debug_kv_fill(dtd_engine* e, int64_t seq_id, int32_t len, uint64_t seed);
 
 /* Kernel timing.  kind: 0 = the gate/up projection, 1 = the down projection, 2 = the
@@ -440,8 +447,8 @@ int32_t dtd_debug_uses_persistent(const dtd_engine* e, int32_t batch);
  * the model has head size 128, 4 query heads per KV head and KV blocks of 16 positions (the
  * instantiation built for that shape, whose probe variant dtd_debug_decode_probe then runs
  * too), or 0 when the kernel reads the shape at run time or the engine has no step kernel
- * (Q4_0 weights, or a device without cooperative launches).  A dtd_status < 0 for a null
- * engine. */
+ * (a device without cooperative launches, or a shape outside the kernel's limits).  A
+ * dtd_status < 0 for a null engine. */
 int32_t dtd_debug_step_kernel_shape(const dtd_engine* e);
 
 #ifdef __cplusplus

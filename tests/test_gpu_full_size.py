@@ -91,6 +91,17 @@ def test_smollm3_shape_full_size_at_context_2048():
     P.close()
 
 
+def test_smollm3_shape_q4_0_full_width_at_context_2048():
+    # Q4_0 weights at the SmolLM3-3B width, in the step-kernel instantiation the benchmark's
+    # Q4_0 workload times (four layers: the oracle's cost)
+    w = synth.SMOLLM3_3B
+    P, O2 = _pair(w, w.shape.replace(wfmt=synth.W_Q4_0, n_layers=4), max_seqs=2)
+    assert dtd.dtd_debug_step_kernel_shape(P.eng.h) == 128 and dtd.dtd_debug_uses_persistent(P.eng.h, 1)
+    _write_kv(P, O2, 0, [0, 100], w.context - 2, seed=7)
+    _run(P, O2, [0], {0: w.context - 2})
+    P.close()
+
+
 def test_llama32_1b_shape_full_width_q8_0_tied_at_context_4096():
     w = synth.LLAMA32_1B
     P, O2 = _pair(w, w.shape.replace(n_layers=2), max_seqs=2)

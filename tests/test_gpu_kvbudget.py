@@ -58,12 +58,14 @@ def _oracle_run(ob, token, score=True):
     return tok, log, pre
 
 
-def _run_budgeted(s, kw_budget, prompt_len, steps, seed, batch_with_plain=False):
+def _run_budgeted(s, kw_budget, prompt_len, steps, seed, batch_with_plain=False, path=dtd.PATH_AUTO):
     """GPU sequence 0 under the budget (free-running greedy), the oracle's BudgetedSeq
     teacher-forced through its tokens.  Returns the number of steps compared before the first
     near tie (or all of them)."""
     budget, n_init, n_rec, layers = kw_budget
-    P = Pair(s, max_ctx=128, max_seqs=3, max_batch=2, seed=seed)
+    P = Pair(s, max_ctx=128, max_seqs=3, max_batch=2, seed=seed, path=path)
+    if path == dtd.PATH_PERSISTENT:
+        assert dtd.dtd_debug_uses_persistent(P.eng.h, 1)
     O = oracle.Model(s, P.w, max_ctx=128, max_seqs=2)
     P.eng.set_kv_budget(0, budget, n_initial=n_init, n_recent=n_rec, score_layers=layers)
     ob = KB.BudgetedSeq(O, 0, budget, n_init, n_rec, layers)
@@ -119,13 +121,16 @@ def _run_budgeted(s, kw_budget, prompt_len, steps, seed, batch_with_plain=False)
     return compared
 
 
+@pytest.mark.parametrize("path", [dtd.PATH_PERSISTENT, dtd.PATH_PER_KERNEL], ids=["step-kernel", "per-kernel"])
 @pytest.mark.parametrize("kw", [dict(), dict(act=synth.ACT_BF16, kvfmt=synth.KV_I8),
                                 dict(n_q_heads=8, n_kv_heads=2, head_dim=128, act=synth.ACT_BF16,
                                      kvfmt=synth.KV_BF16)],
                          ids=["f32", "bf16-int8kv", "hd128"])
-def test_budget_evicts_like_the_oracle(kw):
+def test_budget_evicts_like_the_oracle(kw, path):
+    # batch 1: the step kernel (scores from its kept queries and softmax statistics) or the
+    # per-sub-step kernels
     s = _GRID.replace(**kw)
-    n = _run_budgeted(s, (24, 3, 6, 1), prompt_len=30, steps=40, seed=7)
+    n = _run_budgeted(s, (24, 3, 6, 1), prompt_len=30, steps=40, seed=7, path=path)
     _say(f"{kw}: {n} steps with the same kept entries, scores and outputs as the oracle")
     assert n >= 20
 

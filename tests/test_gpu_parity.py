@@ -123,10 +123,11 @@ _FORMATS = [
     # int8-row weights, bf16 activations and bf16 KV at that shape: the instantiation the
     # benchmark times on the SmolLM3-3B shape (its probe variant has the same parameters)
     dict(n_q_heads=8, n_kv_heads=2, head_dim=128, act=synth.ACT_BF16, kvfmt=synth.KV_BF16),
-    # Q4_0 weights (per-sub-step kernels only)
+    # Q4_0 weights; the last one is the instantiation the benchmark's Q4_0 workload times
     dict(wfmt=synth.W_Q4_0),
     dict(wfmt=synth.W_Q4_0, act=synth.ACT_BF16, kvfmt=synth.KV_BF16, tied=True),
     dict(n_q_heads=8, n_kv_heads=2, head_dim=128, wfmt=synth.W_Q4_0, act=synth.ACT_BF16, kvfmt=synth.KV_I8),
+    dict(n_q_heads=8, n_kv_heads=2, head_dim=128, wfmt=synth.W_Q4_0, act=synth.ACT_BF16, kvfmt=synth.KV_BF16),
 ]
 
 
@@ -156,10 +157,8 @@ def teacher_forced(P, gpu_ids, orc_ids, toks, poss, tag):
 @pytest.mark.parametrize("kw", _FORMATS, ids=lambda kw: "-".join(f"{k}={v}" for k, v in kw.items()) or "base")
 def test_formats(kw, path):
     s = _GRID.replace(**kw)
-    if s.wfmt == synth.W_Q4_0 and path == dtd.PATH_PERSISTENT:
-        pytest.skip("the batch-1 step kernel does not take Q4_0 weights")
     P = Pair(s, max_ctx=96, max_seqs=2, seed=21, path=path)
-    fixed = s.head_dim == 128 and s.n_q_heads == 4 * s.n_kv_heads and s.wfmt != synth.W_Q4_0
+    fixed = s.head_dim == 128 and s.n_q_heads == 4 * s.n_kv_heads
     assert dtd.dtd_debug_step_kernel_shape(P.eng.h) == (128 if fixed else 0)
     _say(f"formats {kw}: step kernel shape {'fixed hd 128, G 4, bs 16' if fixed else 'run time'}, "
          f"{PATH_IDS[PATHS.index(path)]} schedule")
@@ -401,6 +400,76 @@ def test_kv_block_table_roundtrip_bit_exact(kvfmt):
             assert np.array_equal(ko, ek) and np.array_equal(vo, ev)
             if kvfmt == synth.KV_I8:
                 assert np.array_equal(kso, eks) and np.array_equal(vso, evs)
+    P.close()
+
+
+def _splitmix_final(z):
+    z = z.astype(np.uint64)
+    z = (z ^ (z >> np.uint64(30))) * np.uint64(0xbf58476d1ce4e5b9)
+    z = (z ^ (z >> np.uint64(27))) * np.uint64(0x94d049bb133111eb)
+    return z ^ (z >> np.uint64(31))
+
+
+def _kv_fill_values(s, layer, n, seed):
+    """dtd_debug_kv_fill's contents as its declaration defines them: (u, a) with u of shape
+    [2][n][Hkv][hd] (K, V) and the fp32 amplitude a."""
+    t, j, i, w = np.meshgrid(np.arange(n, dtype=np.uint64), np.arange(s.n_kv_heads, dtype=np.uint64),
+                             np.arange(s.head_dim, dtype=np.uint64), np.arange(2, dtype=np.uint64), indexing="ij")
+    key = (np.uint64(layer) << np.uint64(40)) ^ (t << np.uint64(20)) ^ (j << np.uint64(12)) ^ (i << np.uint64(1)) ^ w
+    h = _splitmix_final(np.uint64(seed) ^ _splitmix_final(key))
+    u = (h >> np.uint64(40)).astype(np.float32) * np.float32(2.0 ** -23) - np.float32(1.0)
+    a = np.float32(0.02) * np.float32(np.sqrt(np.float32(s.dim))) * np.float32(1.7320508)
+    return np.moveaxis(u, 3, 0), a
+
+
+@pytest.mark.parametrize("kvfmt", [synth.KV_F32, synth.KV_BF16, synth.KV_I8])
+def test_kv_fill_is_its_definition(kvfmt):
+    # the long-context timing fill: every stored element against the declared hash, through
+    # the block table of two interleaved sequences; the length it sets; a step on top of it
+    s = _GRID.replace(kvfmt=kvfmt)
+    P = Pair(s, max_ctx=160, max_seqs=3, max_batch=2, seed=1)
+    n_a, n_b = 150, 37
+    dtd.dtd_debug_kv_fill(P.eng.h, 2, 20, 11)
+    dtd.dtd_debug_kv_fill(P.eng.h, 1, n_a, 9)
+    dtd.dtd_debug_kv_fill(P.eng.h, 2, n_b, 11)       # grows into a block after sequence 1's
+    assert P.eng.seq_len(1) == n_a and P.eng.seq_len(2) == n_b
+    for sid, n, seed in ((1, n_a, 9), (2, n_b, 11)):
+        for layer in range(s.n_layers):
+            u, a = _kv_fill_values(s, layer, n, seed)
+            dt = {synth.KV_F32: np.float32, synth.KV_BF16: np.uint16, synth.KV_I8: np.int8}[kvfmt]
+            ko = np.empty((n, s.n_kv_heads, s.head_dim), dt)
+            vo = np.empty_like(ko)
+            kso = vso = None
+            if kvfmt == synth.KV_I8:
+                kso, vso = np.empty((n, s.n_kv_heads), np.uint16), np.empty((n, s.n_kv_heads), np.uint16)
+            dtd.dtd_debug_kv_read(P.eng.h, sid, layer, 0, n, ko, vo, kso, vso)
+            for w, got in ((0, ko), (1, vo)):
+                where = f"seq {sid} layer {layer} {'KV'[w]}"
+                if kvfmt == synth.KV_I8:
+                    # the codes depend on u alone: exact
+                    assert np.array_equal(got, np.rint(u[w] * np.float32(127.0)).astype(np.int8)), where
+                    sc = (kso if w == 0 else vso).view(np.float16).astype(np.float64)
+                    assert np.allclose(sc, float(a) / 127.0, rtol=1e-3, atol=0), where
+                    continue
+                ref = u[w] * a                       # fp32 product, as stored for fp32
+                g = got.astype(np.float64) if kvfmt == synth.KV_F32 else synth.bf16_bits_to_f32(got).astype(np.float64)
+                # a comes from the device's sqrtf: allow a few fp32 ulps of it, then bf16's step
+                rel = 2.0 ** -21 if kvfmt == synth.KV_F32 else 2.0 ** -8
+                assert np.all(np.abs(g - ref) <= rel * np.abs(ref) + 1e-30), where
+                if kvfmt == synth.KV_BF16:
+                    exact = np.mean(got == synth.f32_to_bf16_bits(ref.astype(np.float32)))
+                    assert exact > 0.999, f"{where}: {exact:.4f} of elements round like the definition"
+    # a shorter fill of a longer sequence overwrites positions and keeps its length
+    dtd.dtd_debug_kv_fill(P.eng.h, 1, 20, 10)
+    assert P.eng.seq_len(1) == n_a
+    free = P.eng.kv_blocks_free()
+    for bad in (0, -3, 161):
+        with pytest.raises(dtd.DtdError):
+            dtd.dtd_debug_kv_fill(P.eng.h, 2, bad, 1)
+    assert P.eng.seq_len(2) == n_b and P.eng.kv_blocks_free() == free
+    # decoding continues at position len
+    ng, lg, _ = P.gpu_step([1, 2], [3, 4])
+    assert np.isfinite(lg).all() and P.eng.seq_len(1) == n_a + 1 and P.eng.seq_len(2) == n_b + 1
     P.close()
 
 
