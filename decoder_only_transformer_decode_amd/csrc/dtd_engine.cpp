@@ -234,6 +234,7 @@ static dtd_status check_config(const dtd_config* c, char* msg, int32_t msg_len) 
   const int G = c->n_q_heads / c->n_kv_heads;
   if (G * c->head_dim > 2048) return bad(DTD_E_UNSUPPORTED, "query group size x head_dim = %d > 2048", G * c->head_dim);
   const int qd = c->n_q_heads * c->head_dim;
+  if (qd > 16384) return bad(DTD_E_UNSUPPORTED, "n_q_heads x head_dim = %d > 16384", qd);
   const int v = vec_elems(c->wfmt);
   if (c->dim % v || c->ffn_dim % v || qd % v)
     return bad(DTD_E_UNSUPPORTED, "dim, ffn_dim and n_q_heads*head_dim must be multiples of %d", v);
@@ -912,8 +913,14 @@ static dtd_status run_sub_steps(dtd_engine* e, int B, bool do_head, const uint8_
       HIP_OK(e, cp(e->vnew, in + pl.v, fkv));
     }
     if (append_first) HIP_OK(e, launch_kv_append(d, e->desc_dev, B, e->knew, e->vnew, kv, st));
-    TIMED(4, launch_attention(d, e->desc_dev, B, e->q, e->knew, e->vnew, kv, e->bt_dev, partials, st));
     const bool scored = l >= e->step_score_min;
+    if (append_first && B >= 2) {
+      // a prefill chunk (consecutive positions of one sequence, their K/V appended above):
+      // blocked causal attention over the cache
+      TIMED(4, launch_attn_prefill(d, e->desc_dev, B, e->step_max_pos, e->q, kv, e->bt_dev, partials, st));
+    } else {
+      TIMED(4, launch_attention(d, e->desc_dev, B, e->q, e->knew, e->vnew, kv, e->bt_dev, partials, st));
+    }
     HIP_OK(e, launch_combine(d, e->desc_dev, B, partials, e->o, st, scored ? e->attn_stat : nullptr));
     if (scored)
       HIP_OK(e, launch_score(d, e->desc_dev, B, e->step_max_pos, l, e->q, kv, e->bt_dev, e->attn_stat, e->scores_dev, st));
@@ -1899,7 +1906,7 @@ extern "C" int32_t dtd_debug_uses_persistent(const dtd_engine* e, int32_t batch)
 
 extern "C" int32_t dtd_debug_step_kernel_shape(const dtd_engine* e) {
   if (!e) return DTD_E_ARG;
-  return e->persist_ok && persistent_fixed_shape(e->d) ? 128 : 0;
+  return e->persist_ok ? persistent_fixed_hd(e->d) : 0;
 }
 
 extern "C" dtd_status dtd_debug_stream_read(const void* buf_dev, int64_t bytes, int32_t reps, void* hip_stream,

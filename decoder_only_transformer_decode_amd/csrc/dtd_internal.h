@@ -176,7 +176,9 @@ size_t persistent_smem_bytes(const Dims& d, int nch, int nwg);
 size_t persistent_xs_floats(const Dims& d, int nch);
 int persistent_tags_per_step(const Dims& d);
 bool persistent_supports(const Dims& d);   // shapes the persistent step kernel handles
-bool persistent_fixed_shape(const Dims& d);   // the step kernel with hd 128, G 4, bs 16 fixed
+// the head size the step kernel fixes at compile time for this shape (128; 64 with bf16
+// activations; with G 4 and KV blocks of 16), or 0 (the shape read at run time)
+int persistent_fixed_hd(const Dims& d);
 hipError_t persistent_prepare(const Dims& d, size_t smem, int* blocks_per_cu);
 hipError_t launch_persistent(const PersistArgs& a, int nwg, size_t smem, hipStream_t st);
 hipError_t launch_embed(const Dims& d, const MatDev& emb, const StepDesc* desc, int B,
@@ -199,6 +201,11 @@ hipError_t launch_kv_append(const Dims& d, const StepDesc* desc, int B, const fl
 hipError_t launch_kv_copy_block(const Dims& d, const PLayer* layers, int src, int dst, hipStream_t st);
 hipError_t launch_combine(const Dims& d, const StepDesc* desc, int B, const float* partials,
                           void* o, hipStream_t st, float* stat = nullptr);
+// causal attention of a prefill chunk: n consecutive positions from desc->pos[0] (the last
+// one last_pos) of the sequence in desc->slot[0], all appended; leaves launch_attention's
+// partials [n][Hq][nch][hd+2] for launch_combine
+hipError_t launch_attn_prefill(const Dims& d, const StepDesc* desc, int n, int last_pos, const float* q,
+                               const KvLayer& kv, const int32_t* bt, float* partials, hipStream_t st);
 hipError_t launch_score(const Dims& d, const StepDesc* desc, int B, int max_pos, int layer, const float* q,
                         const KvLayer& kv, const int32_t* bt, const float* stat, float* scores, hipStream_t st);
 hipError_t launch_kv_gather(const Dims& d, const PLayer* layers, const int32_t* old_blocks, const int32_t* new_blocks,

@@ -929,59 +929,55 @@ __global__ __launch_bounds__(256) void k_combine(Dims d, const StepDesc* desc, c
 
 // KV budget scores (the Initial-Key cache of the C17 engine article, 5.3): the softmax
 // probability each cache entry t <= pos of sequence b gets from this step's queries, summed
-// over the query heads, added to scores[slot][t].  Grid (B, tiles of 64 entries), four
-// waves: lane l of wave w takes entry (tile, l) against KV heads w, w+4, ...; it recomputes
-// q_h . k_t / sqrt(d) for that head's G query heads (q staged in LDS) from the stored key and
-// adds exp(s - M_h) / L_h with the merged attention statistics.  The waves' sums meet in LDS
-// and are added in wave order, so every entry's sum has one fixed order.
+// over the query heads, added to scores[slot][t].  Grid (B, groups of 4 entries), four
+// waves: wave w takes entry 4 * group + w, its lanes split the head dimension, and the row's
+// queries are staged in LDS.  For each query head h in order it recomputes q_h . k_t / sqrt(d)
+// from the stored key (a wave sum: every lane holds the same total) and adds
+// exp(s - M_h) / L_h with the merged attention statistics, so every entry's sum has one fixed
+// order.
 template <int KVFMT>
 __global__ __launch_bounds__(256) void k_score(Dims d, const StepDesc* desc, int layer, const float* q,
                                                KvLayer kv, const int32_t* bt, const float* stat, float* scores) {
-  extern __shared__ float qs[];        // [q_dim] this row's queries, then [4][64] wave sums
+  extern __shared__ float qb[];        // [q_dim] this row's queries
   const int b = blockIdx.x;
-  if (layer < desc->score_from[b]) return;
+  if (layer < desc->score_from[b]) return;   // block-uniform
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (int i = threadIdx.x; i < d.q_dim; i += 256) qs[i] = q[(size_t)b * d.q_dim + i];
+  for (int i = threadIdx.x; i < d.q_dim; i += 256) qb[i] = q[(size_t)b * d.q_dim + i];
   __syncthreads();
-  const int t = blockIdx.y * 64 + lane;
+  const int t = blockIdx.y * 4 + wave;
   const int pos = desc->pos[b], slot = desc->slot[b];
+  if (t > pos) return;   // wave-uniform; no barrier below
   const float scale = 1.f / sqrtf((float)d.hd);
+  const int blk = bt[(size_t)slot * d.max_blocks + t / d.bs];
   float sum = 0.f;
-  if (t <= pos) {
-    const int blk = bt[(size_t)slot * d.max_blocks + t / d.bs];
-    for (int j = wave; j < d.Hkv; j += 4) {
-      const size_t row = ((size_t)blk * d.Hkv + j) * d.bs + (t % d.bs);
-      float ksc = 1.f;
-      if constexpr (KVFMT == KV_I8) ksc = f16_to_f32(kv.ks[row]);
-      for (int g = 0; g < d.G; g++) {
-        const int h = j * d.G + g;
-        const float* qh = qs + (size_t)h * d.hd;
-        float dot = 0.f;
-        for (int i = 0; i < d.hd; i += 4) {
-          float k4[4];
-          if constexpr (KVFMT == KV_F32) {
-            const float4 v = *(const float4*)((const float*)kv.k + row * d.hd + i);
-            k4[0] = v.x; k4[1] = v.y; k4[2] = v.z; k4[3] = v.w;
-          } else if constexpr (KVFMT == KV_BF16) {
-            const uint2 v = *(const uint2*)((const uint16_t*)kv.k + row * d.hd + i);
-            k4[0] = bf16_to_f32(v.x & 0xffffu); k4[1] = bf16_to_f32(v.x >> 16);
-            k4[2] = bf16_to_f32(v.y & 0xffffu); k4[3] = bf16_to_f32(v.y >> 16);
-          } else {
-            const uint32_t v = *(const uint32_t*)((const int8_t*)kv.k + row * d.hd + i);
-            for (int c = 0; c < 4; c++) k4[c] = sext8(v, c) * ksc;
-          }
-          for (int c = 0; c < 4; c++) dot += qh[i + c] * k4[c];
-        }
-        const float M = stat[((size_t)b * d.Hq + h) * 2], L = stat[((size_t)b * d.Hq + h) * 2 + 1];
-        sum += expf(dot * scale - M) / L;
+  for (int j = 0; j < d.Hkv; j++) {
+    const size_t row = ((size_t)blk * d.Hkv + j) * d.bs + (t % d.bs);
+    float kx[2];   // elements lane and lane + 64 of the key (head size <= 128)
+#pragma unroll
+    for (int u = 0; u < 2; u++) {
+      const int i = lane + 64 * u;
+      float v = 0.f;
+      if (i < d.hd) {
+        if constexpr (KVFMT == KV_F32) v = ((const float*)kv.k)[row * d.hd + i];
+        else if constexpr (KVFMT == KV_BF16) v = bf16_to_f32(((const uint16_t*)kv.k)[row * d.hd + i]);
+        else v = (float)((const int8_t*)kv.k)[row * d.hd + i] * f16_to_f32(kv.ks[row]);
       }
+      kx[u] = v;
+    }
+    for (int g = 0; g < d.G; g++) {
+      const int h = j * d.G + g;
+      float p = 0.f;
+#pragma unroll
+      for (int u = 0; u < 2; u++) {
+        const int i = lane + 64 * u;
+        if (i < d.hd) p += qb[(size_t)h * d.hd + i] * kx[u];
+      }
+      const float dot = wave_sum(p);
+      const float M = stat[((size_t)b * d.Hq + h) * 2], L = stat[((size_t)b * d.Hq + h) * 2 + 1];
+      sum += expf(dot * scale - M) / L;
     }
   }
-  float* ws = qs + d.q_dim;
-  ws[wave * 64 + lane] = sum;
-  __syncthreads();
-  if (wave == 0 && t <= pos)
-    scores[(size_t)slot * d.max_ctx + t] += ((ws[lane] + ws[64 + lane]) + ws[128 + lane]) + ws[192 + lane];
+  if (lane == 0) scores[(size_t)slot * d.max_ctx + t] += sum;
 }
 
 // KV budget eviction: copies cache entries keep[i] (i < n, through the old block list) to
@@ -1095,6 +1091,334 @@ __global__ __launch_bounds__(256) void k_kv_fill(Dims d, KvLayer kv, const int32
         ((int8_t*)pool)[row * d.hd + i] = (int8_t)rintf(u * 127.f);
         if (i == 0) (which ? kv.vs : kv.ks)[row] = f32_to_f16(amp / 127.f);
       }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// Prefill attention: the causal attention of a chunk of n consecutive positions p0 .. p0+n-1
+// of one sequence, every one of whose K/V entries is already in the cache.  Blocked with an
+// online softmax, FlashAttention-2 style (the Qwen3-8B engine article, 4.4.1; lightLLM's
+// context_flashattention_nopad): a workgroup takes 16 query positions, up to 4 query heads
+// of one KV head (one head per wave) and one chunk of the keys (the decode attention's chunk
+// length, a multiple of 64), and walks the chunk's keys up to its last position in tiles of
+// 64 staged once in LDS for all its waves, so each K/V row is read once per 16 positions
+// rather than once per position.  Each (position, head, chunk) leaves an unnormalised partial
+// (O, max, sum) in the decode attention's layout, and k_combine merges a position's chunks
+// exactly as it does after a decode step.
+//
+// Both products run on the matrix cores (v_mfma_f32_16x16x32_bf16, fp32 accumulation) at
+// fp32 accuracy: an fp32 operand x enters as three bf16 terms, hi = bf16(x),
+// mid = bf16(x - hi), lo = bf16(x - hi - mid), which carry x to 2^-24 relative, and every
+// product of terms whose weights add to at least 2^-24 is taken (hi hi, hi mid, mid hi,
+// hi lo, mid mid, lo hi).  bf16 or int8 K/V is exact in bf16 (one term), so S = Q K^T
+// takes three products and O += P V three.  int8 K/V keep their per-entry scales outside
+// the products: the K scale multiplies its score column, the V scale its probability
+// column.  The scores of a tile leave the MFMA with a row's keys spread over 16 lanes; P goes
+// through LDS to reach the operand layout of the second product.
+// ---------------------------------------------------------------------------------------
+
+constexpr int kPfQ = 16;   // query positions per workgroup
+constexpr int kPfT = 64;   // keys per staged tile
+
+struct PfLayout {
+  int hdp, kld, vld, pld;                    // head size padded to 32; LDS row pitches
+  size_t k[3], v[3], ksc, vsc, p, bytes;     // terms of K (hi, mid, lo) and of V
+};
+
+// K tile [64][kld] bf16 and V tile transposed [hdp][vld] bf16, three terms each for fp32
+// K/V and one otherwise; int8 scales [64] each; each wave's P [16][pld] fp32
+__host__ __device__ inline PfLayout pf_layout(int hd, int kvfmt) {
+  PfLayout L;
+  L.hdp = (hd + 31) / 32 * 32;
+  L.kld = L.hdp + 8;
+  L.vld = kPfT + 8;
+  L.pld = kPfT + 4;
+  const int terms = kvfmt == KV_F32 ? 3 : 1;
+  size_t o = 0;
+  for (int u = 0; u < 3; u++) { L.k[u] = o; if (u < terms) o += (size_t)kPfT * L.kld * 2; }
+  for (int u = 0; u < 3; u++) { L.v[u] = o; if (u < terms) o += (size_t)L.hdp * L.vld * 2; }
+  L.ksc = o; o += kPfT * 4;
+  L.vsc = o; o += kPfT * 4;
+  L.p = o; o += (size_t)4 * kPfQ * L.pld * 4;
+  L.bytes = o;
+  return L;
+}
+
+// x = hi + mid + lo as three bf16 bit patterns (each rounded to nearest even; the
+// differences are exact in fp32)
+__device__ __forceinline__ void split3(float x, uint32_t (&t)[3]) {
+  t[0] = f32_to_bf16(x);
+  const float r1 = x - bf16_to_f32(t[0]);
+  t[1] = f32_to_bf16(r1);
+  t[2] = f32_to_bf16(r1 - bf16_to_f32(t[1]));
+}
+
+// 8 fp32 values as the three bf16x8 operand terms
+__device__ __forceinline__ void split8(const float (&x)[8], bf16x8 (&out)[3]) {
+  u32x4 w[3];
+#pragma unroll
+  for (int u = 0; u < 4; u++) {
+    uint32_t a[3], b[3];
+    split3(x[2 * u], a);
+    split3(x[2 * u + 1], b);
+#pragma unroll
+    for (int s = 0; s < 3; s++) w[s][u] = a[s] | (b[s] << 16);
+  }
+#pragma unroll
+  for (int s = 0; s < 3; s++) out[s] = __builtin_bit_cast(bf16x8, w[s]);
+}
+
+// acc += A B for A given as three terms and B as NB terms (1: exact in bf16, 3: fp32), the
+// term products down to 2^-24; smaller terms first
+template <int NB>
+__device__ __forceinline__ f32x4 mfma_split(const bf16x8 (&a)[3], const bf16x8 (&b)[3], f32x4 acc) {
+  if constexpr (NB == 3) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[0], b[2], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[1], b[1], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[0], b[1], acc, 0, 0, 0);
+  }
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[2], b[0], acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[1], b[0], acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[0], b[0], acc, 0, 0, 0);
+  return acc;
+}
+
+// sum or max over the 16 lanes of a lane's row group (lanes l ^ 1, 2, 4, 8): every lane of
+// the group gets the same result
+__device__ __forceinline__ float grp16_sum(float v) {
+#pragma unroll
+  for (int m = 1; m < 16; m <<= 1) v += __shfl_xor(v, m, 64);
+  return v;
+}
+__device__ __forceinline__ float grp16_max(float v) {
+#pragma unroll
+  for (int m = 1; m < 16; m <<= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
+  return v;
+}
+
+// K/V element e of a pool, as fp32 (int8: the code; its scale is applied apart)
+template <int KVFMT>
+__device__ __forceinline__ float kv_raw(const void* pool, size_t e) {
+  if constexpr (KVFMT == KV_F32) return ((const float*)pool)[e];
+  else if constexpr (KVFMT == KV_BF16) return bf16_to_f32(((const uint16_t*)pool)[e]);
+  else return (float)((const int8_t*)pool)[e];
+}
+
+// 8 consecutive elements from e (a multiple-of-8 head size: aligned vector loads)
+template <int KVFMT>
+__device__ __forceinline__ void kv_raw8(const void* pool, size_t e, float (&x)[8]) {
+  if constexpr (KVFMT == KV_F32) {
+    const float4 a = *(const float4*)((const float*)pool + e), b = *(const float4*)((const float*)pool + e + 4);
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w; x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+  } else if constexpr (KVFMT == KV_BF16) {
+    const uint4 a = *(const uint4*)((const uint16_t*)pool + e);
+    const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+    for (int u = 0; u < 4; u++) { x[2 * u] = bf16_to_f32(w[u] & 0xffffu); x[2 * u + 1] = bf16_to_f32(w[u] >> 16); }
+  } else {
+    const uint2 a = *(const uint2*)((const int8_t*)pool + e);
+#pragma unroll
+    for (int u = 0; u < 4; u++) { x[u] = sext8(a.x, u); x[4 + u] = sext8(a.y, u); }
+  }
+}
+
+template <int KVFMT>
+__global__ __launch_bounds__(256) void k_attn_prefill(Dims d, const StepDesc* desc, int n, const float* q,
+                                                      KvLayer kv, const int32_t* bt, float* partials) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t pf_sm[];
+  constexpr int NT = KVFMT == KV_F32 ? 3 : 1;   // bf16 terms of a K/V element
+  const PfLayout Ly = pf_layout(d.hd, KVFMT);
+  uint16_t* kt[3];
+  uint16_t* vt[3];
+#pragma unroll
+  for (int u = 0; u < 3; u++) { kt[u] = (uint16_t*)(pf_sm + Ly.k[u]); vt[u] = (uint16_t*)(pf_sm + Ly.v[u]); }
+  float* ksc = (float*)(pf_sm + Ly.ksc);
+  float* vsc = (float*)(pf_sm + Ly.vsc);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  float* pw = (float*)(pf_sm + Ly.p) + (size_t)wave * kPfQ * Ly.pld;
+  const int hd = d.hd, HDP = Ly.hdp, G = d.G;
+  const int ngz = (G + 3) / 4;
+  const int j = blockIdx.x / ngz, g = (blockIdx.x - j * ngz) * 4 + wave;
+  const bool active = g < G;                 // wave-uniform
+  const int h = j * G + (active ? g : 0);
+  const int c = blockIdx.y, i0 = blockIdx.z * kPfQ;
+  const int p0 = desc->pos[0], slot = desc->slot[0];
+  const int last = p0 + min(n, i0 + kPfQ) - 1;   // the last key any row of this block attends
+  const int k_lo = c * d.ct, k_hi = min(last + 1, k_lo + d.ct);   // this block's keys
+  if (k_lo > last) return;                       // (block-uniform) a chunk past every row
+  const int* btrow = bt + (size_t)slot * d.max_blocks;
+  const int r16 = lane & 15, quad = lane >> 4;
+
+  // this wave's queries / sqrt(d) as A operands: row r16 (position i0 + r16; rows past the
+  // chunk repeat its last query and are never stored), k = 32 s + 8 quad + u
+  bf16x8 qa[4][3];
+  {
+    const float inv = 1.f / sqrtf((float)hd);
+    const float* qr = q + (size_t)min(i0 + r16, n - 1) * d.q_dim + (size_t)h * hd;
+#pragma unroll
+    for (int s = 0; s < 4; s++) {
+      float x[8];
+#pragma unroll
+      for (int u = 0; u < 8; u++) {
+        const int dd = 32 * s + 8 * quad + u;
+        x[u] = dd < hd ? qr[dd] * inv : 0.f;
+      }
+      split8(x, qa[s]);
+    }
+  }
+  f32x4 oacc[8];   // O: d-blocks of 16 (head size <= 128)
+#pragma unroll
+  for (int db = 0; db < 8; db++) oacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m[4], l[4];   // running max and sum of rows 4 quad + i
+#pragma unroll
+  for (int i = 0; i < 4; i++) { m[i] = -INFINITY; l[i] = 0.f; }
+
+  const int pieces = HDP / 8;
+  for (int t0 = k_lo; t0 < k_hi; t0 += kPfT) {
+    __syncthreads();   // every wave is done with the previous tile and its P
+    // ---- stage keys t0 .. t0+63 of KV head j; zeros past `last` and past the head size ----
+    for (int idx = tid; idx < kPfT * pieces; idx += 256) {
+      const int kr = idx / pieces, d0 = (idx - kr * pieces) * 8, t = t0 + kr;
+      float kx[8], vx[8];
+#pragma unroll
+      for (int u = 0; u < 8; u++) { kx[u] = 0.f; vx[u] = 0.f; }
+      float ks = 0.f, vs = 0.f;
+      if (t < k_hi && d0 < hd) {
+        const int blk = btrow[t / d.bs];
+        const size_t row = ((size_t)blk * d.Hkv + j) * d.bs + (t % d.bs);
+        if ((hd & 7) == 0) {
+          kv_raw8<KVFMT>(kv.k, row * hd + d0, kx);
+          kv_raw8<KVFMT>(kv.v, row * hd + d0, vx);
+        } else {
+#pragma unroll
+          for (int u = 0; u < 8; u++)
+            if (d0 + u < hd) {
+              kx[u] = kv_raw<KVFMT>(kv.k, row * hd + d0 + u);
+              vx[u] = kv_raw<KVFMT>(kv.v, row * hd + d0 + u);
+            }
+        }
+        if constexpr (KVFMT == KV_I8) {
+          ks = f16_to_f32(kv.ks[row]);
+          vs = f16_to_f32(kv.vs[row]);
+        }
+      }
+      if constexpr (KVFMT == KV_I8) {
+        if (d0 == 0) { ksc[kr] = ks; vsc[kr] = vs; }
+      }
+      bf16x8 kb8[3];
+      split8(kx, kb8);
+#pragma unroll
+      for (int s = 0; s < NT; s++) *(bf16x8*)(kt[s] + (size_t)kr * Ly.kld + d0) = kb8[s];
+#pragma unroll
+      for (int u = 0; u < 8; u++) {
+        uint32_t vv[3];
+        split3(vx[u], vv);
+#pragma unroll
+        for (int s = 0; s < NT; s++) vt[s][(size_t)(d0 + u) * Ly.vld + kr] = (uint16_t)vv[s];
+      }
+    }
+    __syncthreads();
+    // ---- S = Q K^T, the online softmax, P to LDS ----
+    float al[4];
+    if (active) {
+      f32x4 sacc[4];
+#pragma unroll
+      for (int kb = 0; kb < 4; kb++) sacc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < 4; s++) {
+        if (32 * s >= HDP) break;
+#pragma unroll
+        for (int kb = 0; kb < 4; kb++) {
+          const size_t at = (size_t)(16 * kb + r16) * Ly.kld + 32 * s + 8 * quad;
+          bf16x8 kb8[3];
+#pragma unroll
+          for (int u = 0; u < NT; u++) kb8[u] = *(const bf16x8*)(kt[u] + at);
+          sacc[kb] = mfma_split<NT>(qa[s], kb8, sacc[kb]);
+        }
+      }
+      // lane: rows 4 quad + i, key t0 + 16 kb + r16
+      float mx[4];
+#pragma unroll
+      for (int i = 0; i < 4; i++) mx[i] = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 4; kb++) {
+        const int key = t0 + 16 * kb + r16;
+        const float kscale = KVFMT == KV_I8 ? ksc[16 * kb + r16] : 1.f;
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          const int pos = p0 + i0 + 4 * quad + i;
+          const float s = sacc[kb][i] * kscale;
+          sacc[kb][i] = (key <= pos && key < k_hi) ? s : -INFINITY;
+          mx[i] = fmaxf(mx[i], sacc[kb][i]);
+        }
+      }
+      // a row none of whose keys so far is in range keeps max -inf; its terms use 0 in its
+      // place (every exponential is then of -inf: 0), and its partial is never read
+      float ps[4], base[4];
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        const float mn = fmaxf(m[i], grp16_max(mx[i]));
+        base[i] = mn == -INFINITY ? 0.f : mn;
+        al[i] = expf(m[i] - base[i]);
+        m[i] = mn;
+        ps[i] = 0.f;
+      }
+#pragma unroll
+      for (int kb = 0; kb < 4; kb++) {
+        const float vscale = KVFMT == KV_I8 ? vsc[16 * kb + r16] : 1.f;
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          const float p = expf(sacc[kb][i] - base[i]);
+          ps[i] += p;
+          pw[(4 * quad + i) * Ly.pld + 16 * kb + r16] = p * vscale;
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 4; i++) l[i] = l[i] * al[i] + grp16_sum(ps[i]);
+    }
+    __syncthreads();   // P is in LDS (the barrier also orders the wave's own writes and reads)
+    // ---- O = O * alpha + P V ----
+    if (active) {
+#pragma unroll
+      for (int db = 0; db < 8; db++)
+#pragma unroll
+        for (int i = 0; i < 4; i++) oacc[db][i] *= al[i];
+#pragma unroll
+      for (int ks = 0; ks < 2; ks++) {
+        const float* pr = pw + r16 * Ly.pld + 32 * ks + 8 * quad;
+        const float4 a0 = *(const float4*)pr, a1 = *(const float4*)(pr + 4);
+        const float px[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+        bf16x8 pa[3];
+        split8(px, pa);
+#pragma unroll
+        for (int db = 0; db < 8; db++) {
+          if (16 * db >= HDP) break;
+          const size_t at = (size_t)(16 * db + r16) * Ly.vld + 32 * ks + 8 * quad;
+          bf16x8 vb8[3];
+#pragma unroll
+          for (int u = 0; u < NT; u++) vb8[u] = *(const bf16x8*)(vt[u] + at);
+          oacc[db] = mfma_split<NT>(pa, vb8, oacc[db]);
+        }
+      }
+    }
+  }
+  if (!active) return;
+  // ---- the partial (O, max, sum) of every row whose position reaches this chunk ----
+  const int cs = hd + 2;
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    const int b = i0 + 4 * quad + i;
+    if (b >= n || p0 + b < k_lo) continue;
+    float* P = partials + (((size_t)b * d.Hq + h) * d.nch + c) * cs;
+#pragma unroll
+    for (int db = 0; db < 8; db++) {
+      const int dd = 16 * db + r16;
+      if (dd < hd) P[dd] = oacc[db][i];
+    }
+    if (r16 == 0) {
+      P[hd] = m[i];
+      P[hd + 1] = l[i];
     }
   }
 }
@@ -1310,10 +1634,29 @@ hipError_t launch_combine(const Dims& d, const StepDesc* desc, int B, const floa
   return hipGetLastError();
 }
 
+hipError_t launch_attn_prefill(const Dims& d, const StepDesc* desc, int n, int last_pos, const float* q,
+                               const KvLayer& kv, const int32_t* bt, float* partials, hipStream_t st) {
+  const PfLayout L = pf_layout(d.hd, d.kvfmt);
+  const dim3 grid(d.Hkv * ((d.G + 3) / 4), last_pos / d.ct + 1, (n + kPfQ - 1) / kPfQ);
+  const void* fn = d.kvfmt == KV_F32 ? (const void*)k_attn_prefill<KV_F32>
+                   : d.kvfmt == KV_BF16 ? (const void*)k_attn_prefill<KV_BF16> : (const void*)k_attn_prefill<KV_I8>;
+  // above 64 KB of LDS a kernel needs the attribute (fp32 K/V at head size 128: about 125 KB)
+  static bool raised[3] = {false, false, false};
+  if (L.bytes > 65536 && !raised[d.kvfmt]) {
+    const hipError_t r = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)L.bytes);
+    if (r != hipSuccess) return r;
+    raised[d.kvfmt] = true;
+  }
+  if (d.kvfmt == KV_F32) hipLaunchKernelGGL(k_attn_prefill<KV_F32>, grid, dim3(256), L.bytes, st, d, desc, n, q, kv, bt, partials);
+  else if (d.kvfmt == KV_BF16) hipLaunchKernelGGL(k_attn_prefill<KV_BF16>, grid, dim3(256), L.bytes, st, d, desc, n, q, kv, bt, partials);
+  else hipLaunchKernelGGL(k_attn_prefill<KV_I8>, grid, dim3(256), L.bytes, st, d, desc, n, q, kv, bt, partials);
+  return hipGetLastError();
+}
+
 hipError_t launch_score(const Dims& d, const StepDesc* desc, int B, int max_pos, int layer, const float* q,
                         const KvLayer& kv, const int32_t* bt, const float* stat, float* scores, hipStream_t st) {
-  const dim3 grid(B, (max_pos + 1 + 63) / 64);
-  const size_t smem = ((size_t)d.q_dim + 256) * 4;
+  const dim3 grid(B, (max_pos + 1 + 3) / 4);
+  const size_t smem = (size_t)d.q_dim * 4;
   if (d.kvfmt == KV_F32) hipLaunchKernelGGL(k_score<KV_F32>, grid, dim3(256), smem, st, d, desc, layer, q, kv, bt, stat, scores);
   else if (d.kvfmt == KV_BF16) hipLaunchKernelGGL(k_score<KV_BF16>, grid, dim3(256), smem, st, d, desc, layer, q, kv, bt, stat, scores);
   else hipLaunchKernelGGL(k_score<KV_I8>, grid, dim3(256), smem, st, d, desc, layer, q, kv, bt, stat, scores);

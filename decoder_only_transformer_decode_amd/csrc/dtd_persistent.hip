@@ -1491,13 +1491,18 @@ __global__ __launch_bounds__(PT) void k_step(PersistArgs a) {
   if (lane == 0) desc->next_tokens[0] = bi == INT_MAX ? 0 : bi;
 }
 
-// The normal step per activation type, with the attention shape of the target models (head
-// size 128, 4 query heads per KV head, KV blocks of 16) fixed or read at run time; and its
-// probe variant: with that shape, the same instantiation parameters as the normal step (so
-// a probe at that shape checks the code the normal step runs), otherwise one variant that
-// reads the activation type at run time.
+// The normal step per activation type, with the attention shape of the target models fixed
+// (4 query heads per KV head, KV blocks of 16, and head size 128 with either activation type
+// or head size 64 with bf16 activations) or read at run time; and its probe variant: with a
+// fixed shape, the same instantiation parameters as the normal step (so a probe at that
+// shape checks the code the normal step runs), otherwise one variant that reads the
+// activation type at run time.
 template <int WFMT, int KVFMT>
-const void* step_kernel(bool probe, int act, bool fixed) {
+const void* step_kernel(bool probe, int act, int fixed_hd) {
+  if (fixed_hd == 64)
+    return probe ? (const void*)k_step<WFMT, KVFMT, true, ACT_BF16, 64>
+                 : (const void*)k_step<WFMT, KVFMT, false, ACT_BF16, 64>;
+  const bool fixed = fixed_hd == 128;
   if (probe) {
     if (fixed)
       return act == ACT_BF16 ? (const void*)k_step<WFMT, KVFMT, true, ACT_BF16, 128>
@@ -1513,7 +1518,7 @@ const void* step_kernel(bool probe, int act, bool fixed) {
 
 const void* pick(const Dims& d, bool probe) {
   const int wfmt = d.wfmt, kvfmt = d.kvfmt, act = d.act;
-  const bool fixed = persistent_fixed_shape(d);
+  const int fixed = persistent_fixed_hd(d);
   if (wfmt == W_INT8_ROW) {
     if (kvfmt == KV_F32) return step_kernel<W_INT8_ROW, KV_F32>(probe, act, fixed);
     if (kvfmt == KV_BF16) return step_kernel<W_INT8_ROW, KV_BF16>(probe, act, fixed);
@@ -1536,7 +1541,11 @@ const void* pick(const Dims& d, bool probe) {
 
 }  // namespace
 
-bool persistent_fixed_shape(const Dims& d) { return d.hd == 128 && d.G == kFixedG && d.bs == kFixedBs; }
+int persistent_fixed_hd(const Dims& d) {
+  if (d.G != kFixedG || d.bs != kFixedBs) return 0;
+  if (d.hd == 128) return 128;
+  return d.hd == 64 && d.act == ACT_BF16 ? 64 : 0;
+}
 
 size_t persistent_xs_floats(const Dims& d, int nch) {
   const int vec = d.wfmt == W_BF16 ? 8 : (d.wfmt == W_Q4_0 ? 32 : 16), kstep = 64 * vec;

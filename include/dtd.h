@@ -69,7 +69,7 @@ typedef struct {
   int32_t abi_version;        /* DTD_ABI_VERSION */
   int32_t dim;                /* model width D */
   int32_t n_layers;
-  int32_t n_q_heads;          /* Hq; q_dim = Hq * head_dim */
+  int32_t n_q_heads;          /* Hq; q_dim = Hq * head_dim <= 16384 */
   int32_t n_kv_heads;         /* Hkv, divides Hq; q head h reads kv head h / (Hq/Hkv) */
   int32_t head_dim;           /* d: a multiple of 4 in [8, 128] */
   int32_t ffn_dim;            /* F */
@@ -444,9 +444,10 @@ dtd_status dtd_debug_set_path(dtd_engine* e, int32_t path);
 int32_t dtd_debug_uses_persistent(const dtd_engine* e, int32_t batch);
 
 /* The head size the batch-1 step kernel of this engine has fixed at compile time: 128 when
- * the model has head size 128, 4 query heads per KV head and KV blocks of 16 positions (the
- * instantiation built for that shape, whose probe variant dtd_debug_decode_probe then runs
- * too), or 0 when the kernel reads the shape at run time or the engine has no step kernel
+ * the model has head size 128, 4 query heads per KV head and KV blocks of 16 positions, 64
+ * for head size 64 with the same group and block sizes and bf16 activations (the
+ * instantiations built for those shapes, whose probe variants dtd_debug_decode_probe then
+ * runs too), or 0 when the kernel reads the shape at run time or the engine has no step kernel
  * (a device without cooperative launches, or a shape outside the kernel's limits).  A
  * dtd_status < 0 for a null engine. */
 int32_t dtd_debug_step_kernel_shape(const dtd_engine* e);

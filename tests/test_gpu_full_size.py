@@ -105,6 +105,8 @@ def test_smollm3_shape_q4_0_full_width_at_context_2048():
 def test_llama32_1b_shape_full_width_q8_0_tied_at_context_4096():
     w = synth.LLAMA32_1B
     P, O2 = _pair(w, w.shape.replace(n_layers=2), max_seqs=2)
+    # the head-size-64 instantiation the benchmark's Llama-3.2-1B workload times
+    assert dtd.dtd_debug_step_kernel_shape(P.eng.h) == 64 and dtd.dtd_debug_uses_persistent(P.eng.h, 1)
     _write_kv(P, O2, 0, [0, 100], w.context - 2, seed=6)
     _run(P, O2, [0], {0: w.context - 2})
     P.close()

@@ -128,6 +128,10 @@ _FORMATS = [
     dict(wfmt=synth.W_Q4_0, act=synth.ACT_BF16, kvfmt=synth.KV_BF16, tied=True),
     dict(n_q_heads=8, n_kv_heads=2, head_dim=128, wfmt=synth.W_Q4_0, act=synth.ACT_BF16, kvfmt=synth.KV_I8),
     dict(n_q_heads=8, n_kv_heads=2, head_dim=128, wfmt=synth.W_Q4_0, act=synth.ACT_BF16, kvfmt=synth.KV_BF16),
+    # head size 64 with G 4 and bf16 activations: the fixed-shape instantiation the Llama-3.2-1B
+    # workload runs (Q8_0, bf16 KV, tied head), and one with int8 KV
+    dict(n_q_heads=8, n_kv_heads=2, head_dim=64, wfmt=synth.W_Q8_0, act=synth.ACT_BF16, kvfmt=synth.KV_BF16, tied=True),
+    dict(n_q_heads=8, n_kv_heads=2, head_dim=64, act=synth.ACT_BF16, kvfmt=synth.KV_I8),
 ]
 
 
@@ -158,9 +162,10 @@ def teacher_forced(P, gpu_ids, orc_ids, toks, poss, tag):
 def test_formats(kw, path):
     s = _GRID.replace(**kw)
     P = Pair(s, max_ctx=96, max_seqs=2, seed=21, path=path)
-    fixed = s.head_dim == 128 and s.n_q_heads == 4 * s.n_kv_heads
-    assert dtd.dtd_debug_step_kernel_shape(P.eng.h) == (128 if fixed else 0)
-    _say(f"formats {kw}: step kernel shape {'fixed hd 128, G 4, bs 16' if fixed else 'run time'}, "
+    g4 = s.n_q_heads == 4 * s.n_kv_heads
+    fixed = 128 if g4 and s.head_dim == 128 else (64 if g4 and s.head_dim == 64 and s.act == synth.ACT_BF16 else 0)
+    assert dtd.dtd_debug_step_kernel_shape(P.eng.h) == fixed
+    _say(f"formats {kw}: step kernel shape {f'fixed hd {fixed}, G 4, bs 16' if fixed else 'run time'}, "
          f"{PATH_IDS[PATHS.index(path)]} schedule")
     O2 = P.perturbed_oracle(1, max_ctx=96)
     prompt = synth.prompt_tokens(s.vocab, 70, seed=3)
