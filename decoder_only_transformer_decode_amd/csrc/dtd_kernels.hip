@@ -351,6 +351,43 @@ __device__ __forceinline__ uint32_t i8x2_to_bf16x2(uint32_t u, int b) {
   return __builtin_amdgcn_perm(hi, lo, 0x07060302u);   // upper halves: lo's, then hi's
 }
 
+// x = hi + mid + lo as three bf16 bit patterns (each rounded to nearest even; the
+// differences are exact in fp32)
+__device__ __forceinline__ void split3(float x, uint32_t (&t)[3]) {
+  t[0] = f32_to_bf16(x);
+  const float r1 = x - bf16_to_f32(t[0]);
+  t[1] = f32_to_bf16(r1);
+  t[2] = f32_to_bf16(r1 - bf16_to_f32(t[1]));
+}
+
+// 8 fp32 values as the three bf16x8 operand terms
+__device__ __forceinline__ void split8(const float (&x)[8], bf16x8 (&out)[3]) {
+  u32x4 w[3];
+#pragma unroll
+  for (int u = 0; u < 4; u++) {
+    uint32_t a[3], b[3];
+    split3(x[2 * u], a);
+    split3(x[2 * u + 1], b);
+#pragma unroll
+    for (int s = 0; s < 3; s++) w[s][u] = a[s] | (b[s] << 16);
+  }
+#pragma unroll
+  for (int s = 0; s < 3; s++) out[s] = __builtin_bit_cast(bf16x8, w[s]);
+}
+
+// acc += A B for operands given as NA and NB bf16 terms (1: exact in bf16, 3: an fp32 value
+// split by split3): the term products whose weights add to at least 2^-24, smaller first
+template <int NA, int NB>
+__device__ __forceinline__ f32x4 mfma_terms(const bf16x8 (&a)[3], const bf16x8 (&b)[3], f32x4 acc) {
+  if constexpr (NA == 3) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[2], b[0], acc, 0, 0, 0);
+  if constexpr (NB == 3) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[0], b[2], acc, 0, 0, 0);
+  if constexpr (NA == 3 && NB == 3) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[1], b[1], acc, 0, 0, 0);
+  if constexpr (NA == 3) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[1], b[0], acc, 0, 0, 0);
+  if constexpr (NB == 3) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[0], b[1], acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[0], b[0], acc, 0, 0, 0);
+  return acc;
+}
+
 template <int WFMT, int EPI, int NBB>
 __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t xl[];   // [2][16*NBB][kGemmLd]
@@ -530,17 +567,23 @@ __global__ __launch_bounds__(256) void k_attn(AttnCtx a, const StepDesc* desc, f
 // S4 + S5 for the common shapes (KV blocks of 16 positions; head size 128 or 64 with 4 query
 // heads per KV head, or 32 with 5): one wave per (sequence b, KV head j, chunk c)
 //
-// The wave walks its chunk one paged block at a time.  A block's K (and V) rows of head j
-// are contiguous in the pool, so one wave-wide load of 16 bytes per lane reads 1 KB of it,
-// fully coalesced; lane l then holds elements [e0, e0 + 16/EB) of one position, e0 set by
-// l mod LPP (LPP lanes per position).  The block ids of the chunk sit in two registers and
-// are broadcast with readlane, and the loads of the next two blocks are in flight while one
-// is being used.  Scores, the online softmax and P V for the whole query group run in
-// registers: per-lane partial dot products reduced over the LPP lanes of a position with DPP,
-// softmax statistics across positions with cross-group shuffles, so K and V are read once
-// for the G heads (the GQA decode rule of the Qwen3-8B engine article, 4.4.2) without
-// staging through LDS or any workgroup barrier.  The wave leaves an unnormalised partial
-// (acc, m, l) per head in the same layout as k_attn; k_combine merges the chunks.
+// The wave walks its chunk one paged block (16 positions) at a time; the block ids of the
+// chunk sit in two registers and are broadcast with readlane, and the loads of the next two
+// blocks are in flight while one is being used.  K and V are read once for the G heads (the
+// GQA decode rule of the Qwen3-8B engine article, 4.4.2), with no workgroup barrier.
+//  - Scores on the matrix cores: S^T = K Q^T with v_mfma_f32_16x16x32_bf16, rows the block's
+//    16 positions, columns the group's heads (G <= 16; the other columns are zero).  Lane
+//    (quad, r16) loads its A operand straight from the pool, 8 elements of position r16 per
+//    32-wide slice of the head; bf16 and int8 keys are exact in bf16 (int8 scales multiply
+//    the score rows), fp32 keys and the queries enter as three bf16 terms, so the products
+//    keep fp32 accuracy.
+//  - The online softmax runs on the score layout (a head's 16 scores on 4 lanes), and each
+//    block's P and rescale factors go to the P V layout through 1 KB of the wave's LDS.
+//  - P V on the vector units: one wave-wide load of PB bytes per lane reads whole V rows,
+//    lane l holding elements [e0, e0 + ELEM) of one position (LPP lanes per position), and
+//    the G heads' accumulators stay in registers until the cross-group sum at the end.
+// The wave leaves an unnormalised partial (acc, m, l) per head in the same layout as k_attn;
+// k_combine merges the chunks.
 // ---------------------------------------------------------------------------------------
 
 template <int CTRL>
@@ -637,8 +680,17 @@ template <int KVFMT, int HD, int G>
 __global__ __launch_bounds__(256) void k_attn_w(AttnCtx a, const StepDesc* desc, float* partials) {
   using W = WaveKv<KVFMT, HD>;
   constexpr int RB = W::RB, LPP = W::LPP, PPI = W::PPI, ELEM = W::ELEM, NI = W::NI, PB = W::PB;
+  constexpr int NS = HD / 32;                    // 32-wide slices of the head dimension
+  constexpr int NTK = KVFMT == KV_F32 ? 3 : 1;   // bf16 terms of a stored key element
+  constexpr int KPC = 8 * W::EB / PB;            // pieces of a lane's 8 key elements in one slice
+  static_assert(HD % 32 == 0 && G <= 16, "head size a multiple of 32, at most 16 query heads per KV head");
   typedef typename Piece<PB>::T PieceT;
+  // per wave: this block's P [16 positions][G] and alpha [G] on their way from the score
+  // layout to the P V layout; the new position's key row as stored
+  __shared__ float pl_s[4][17 * G];
+  __shared__ __attribute__((aligned(16))) uint8_t nrow_s[4][RB];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r16 = lane & 15, quad = lane >> 4;
   const int c = blockIdx.x * 4 + wave, j = blockIdx.y, b = blockIdx.z;
   const Dims& d = a.d;
   const int pos = desc->pos[b];
@@ -647,21 +699,26 @@ __global__ __launch_bounds__(256) void k_attn_w(AttnCtx a, const StepDesc* desc,
   const int t_end = min(pos + 1, t_begin + a.ct);
   const int pg = lane / LPP, e0 = (lane % LPP) * ELEM;
   const int Hkv = d.Hkv;
+  float* pl = pl_s[wave];
+  uint8_t* nrow = nrow_s[wave];
 
-  // the group's queries at this lane's elements, scaled by log2(e)/sqrt(hd): scores are kept
-  // in base-2 units, so that every exponential is one v_exp_f32 (2^x); the partial's running
-  // max goes out in natural units
-  float q[G][ELEM];
+  // The query group as the B operand of S^T = K Q^T on the matrix cores: lane (quad, r16)
+  // holds head r16 (zero past G), elements 32 s + 8 quad .. +7 of slice s, scaled by
+  // log2(e)/sqrt(hd) so that scores are in base-2 units (every exponential is one v_exp_f32),
+  // as three bf16 terms (fp32 accuracy)
+  bf16x8 qb[NS][3];
   {
     const float sc = 1.4426950408889634f / sqrtf((float)HD);
-    const float* qb = a.q + (size_t)b * d.q_dim + (size_t)j * G * HD + e0;
+    const float* qh = a.q + (size_t)b * d.q_dim + (size_t)(j * G + (r16 < G ? r16 : 0)) * HD + 8 * quad;
 #pragma unroll
-    for (int h = 0; h < G; h++)
+    for (int s = 0; s < NS; s++) {
+      const float4 u0 = gload<float4>(qh + 32 * s), u1 = gload<float4>(qh + 32 * s + 4);
+      const float x[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+      float y[8];
 #pragma unroll
-      for (int e = 0; e < ELEM; e += 4) {
-        const float4 v = gload<float4>(qb + h * HD + e);
-        q[h][e] = v.x * sc; q[h][e + 1] = v.y * sc; q[h][e + 2] = v.z * sc; q[h][e + 3] = v.w * sc;
-      }
+      for (int u = 0; u < 8; u++) y[u] = r16 < G ? x[u] * sc : 0.f;
+      split8(y, qb[s]);
+    }
   }
   // block ids of the chunk's blocks (at most 128)
   const int lb0 = t_begin >> 4, nb = (t_end - t_begin + 15) >> 4;
@@ -669,6 +726,7 @@ __global__ __launch_bounds__(256) void k_attn_w(AttnCtx a, const StepDesc* desc,
   const int bt_lo = lane < nb ? gload<int32_t>(btrow + lb0 + lane) : 0;
   const int bt_hi = lane + 64 < nb ? gload<int32_t>(btrow + lb0 + lane + 64) : 0;
 
+  float new_ks = 1.f;   // int8: the new position's key scale
   // The new position: rounded to the KV encoding and appended through the block table by the
   // wave whose chunk holds it; its stored (decoded) values replace the block's row there.
   const bool has_new = pos >= t_begin && pos < t_end;
@@ -723,11 +781,18 @@ __global__ __launch_bounds__(256) void k_attn_w(AttnCtx a, const StepDesc* desc,
           w[qd] = packed;
         }
         if (lane == 0) gstore<uint16_t>((which ? a.kv.vs : a.kv.ks) + row, s16);
+        if (which == 0) new_ks = sc;
       }
       uint8_t* dst = (uint8_t*)(which ? a.kv.v : a.kv.k) + row * RB + (size_t)e0 * W::EB;
       if (pg == 0) {
         if constexpr (PB == 16) gstore<uint4>(dst, make_uint4(w[0], w[1], w[2], w[3]));
         else gstore<uint64_t>(dst, (uint64_t)w[1] << 32 | w[0]);
+        // the key row as stored, for the score of the new position (its block's loads may
+        // have been issued before the store)
+        if (which == 0) {
+          if constexpr (PB == 16) *(uint4*)(nrow + e0 * W::EB) = make_uint4(w[0], w[1], w[2], w[3]);
+          else *(uint2*)(nrow + e0 * W::EB) = make_uint2(w[0], w[1]);
+        }
       }
 #pragma unroll
       for (int e = 0; e < ELEM; e++) (which ? nv : nk)[e] = dec[e];
@@ -735,106 +800,134 @@ __global__ __launch_bounds__(256) void k_attn_w(AttnCtx a, const StepDesc* desc,
   }
 
   struct Tile {
-    PieceT k[NI], v[NI];
-    float ks[NI], vs[NI];   // int8: the rows' scales
+    PieceT kq[NS * KPC];   // key r16 of the block, elements 32 s + 8 quad .. +7 of each slice
+    PieceT v[NI];          // V in the P V layout: position PPI i + pg, elements e0 ..
+    uint2 ks4;             // int8: key scales of positions 4 quad .. +3
+    float vs[NI];          // int8: value scales of the P V positions
   };
   // Issues block t of the chunk (past the last block: one line at the pool's start, unused).
   auto issue = [&](int t, Tile& T) {
     const bool real = t < nb;
     const int blk = t < 64 ? __builtin_amdgcn_readlane(bt_lo, t & 63) : __builtin_amdgcn_readlane(bt_hi, t & 63);
     const size_t rowbase = ((size_t)(real ? blk : 0) * Hkv + j) * 16;
-    const uint8_t* kb = (const uint8_t*)a.kv.k + (real ? rowbase * RB + lane * PB : 0);
+    const uint8_t* kb = (const uint8_t*)a.kv.k + (real ? (rowbase + r16) * RB + (size_t)8 * quad * W::EB : 0);
     const uint8_t* vb = (const uint8_t*)a.kv.v + (real ? rowbase * RB + lane * PB : 0);
 #pragma unroll
-    for (int i = 0; i < NI; i++) {
-      T.k[i] = gload<PieceT>(kb + (real ? i * W::LOADB : 0));
-      T.v[i] = gload<PieceT>(vb + (real ? i * W::LOADB : 0));
-    }
-    if constexpr (KVFMT == KV_I8) {
+    for (int s = 0; s < NS; s++)
 #pragma unroll
-      for (int i = 0; i < NI; i++) {
-        const size_t r = real ? rowbase + PPI * i + pg : 0;
-        T.ks[i] = f16_to_f32(gload<uint16_t>(a.kv.ks + r));
-        T.vs[i] = f16_to_f32(gload<uint16_t>(a.kv.vs + r));
-      }
+      for (int u = 0; u < KPC; u++) T.kq[s * KPC + u] = gload<PieceT>(kb + (real ? 32 * s * W::EB + u * PB : 0));
+#pragma unroll
+    for (int i = 0; i < NI; i++) T.v[i] = gload<PieceT>(vb + (real ? i * W::LOADB : 0));
+    if constexpr (KVFMT == KV_I8) {
+      T.ks4 = gload<uint2>(a.kv.ks + (real ? rowbase + 4 * quad : 0));
+#pragma unroll
+      for (int i = 0; i < NI; i++) T.vs[i] = f16_to_f32(gload<uint16_t>(a.kv.vs + (real ? rowbase + PPI * i + pg : 0)));
     }
   };
 
-  float m[G], l[G], acc[G][ELEM];
+  // running max and sum of head r16 (the score layout's column), and the P V accumulators
+  float mc = -INFINITY, lc = 0.f, acc[G][ELEM];
 #pragma unroll
-  for (int h = 0; h < G; h++) {
-    m[h] = -INFINITY;
-    l[h] = 0.f;
+  for (int h = 0; h < G; h++)
 #pragma unroll
     for (int e = 0; e < ELEM; e++) acc[h][e] = 0.f;
-  }
   // EDGE: the chunk's last block, the only one that can end inside the block or hold the new
   // position (the selects for those cases are left out of every other block)
   auto consume = [&](int t, const Tile& T, auto edge) {
     constexpr bool EDGE = decltype(edge)::value;
     const int p0 = t_begin + 16 * t;
-    float s[NI][G];
-    bool isnew[NI], valid[NI];
+    const int kn = pos - p0;                       // the new position's row in this block
+    // ---- S^T = K Q^T: rows the block's 16 positions, columns the group's heads ----
+    f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < NI; i++) {
-      const int p = p0 + PPI * i + pg;
-      isnew[i] = EDGE && has_new && p == pos;
-      valid[i] = !EDGE || p < t_end;   // rows past the chunk's end (last block) are never attended
-      float kf[ELEM];
-      decode_piece<KVFMT, ELEM>(T.k[i], kf);
+    for (int s = 0; s < NS; s++) {
+      PieceT pc[KPC];
 #pragma unroll
-      for (int e = 0; e < ELEM; e++) kf[e] = isnew[i] ? nk[e] : kf[e];
+      for (int u = 0; u < KPC; u++) pc[u] = T.kq[s * KPC + u];
+      if (EDGE && has_new && r16 == kn) {
 #pragma unroll
-      for (int h = 0; h < G; h++) {
-        float sacc = 0.f;
-#pragma unroll
-        for (int e = 0; e < ELEM; e++) sacc = fmaf(q[h][e], kf[e], sacc);
-        s[i][h] = sacc;
+        for (int u = 0; u < KPC; u++) pc[u] = *(const PieceT*)(nrow + (32 * s + 8 * quad) * W::EB + u * PB);
       }
-    }
-#pragma unroll
-    for (int i = 0; i < NI; i++) {
-#pragma unroll
-      for (int h = 0; h < G; h++) {
-        float v = grp_sum<LPP>(s[i][h]);
-        if constexpr (KVFMT == KV_I8) v *= isnew[i] ? 1.f : T.ks[i];
-        s[i][h] = valid[i] ? v : -INFINITY;   // a select: whatever a stale row holds is dropped
+      bf16x8 ka[3];
+      if constexpr (KVFMT == KV_BF16) {
+        ka[0] = __builtin_bit_cast(bf16x8, pc[0]);
+      } else if constexpr (KVFMT == KV_I8) {
+        const u32x4 w4 = {i8x2_to_bf16x2(pc[0].x, 0), i8x2_to_bf16x2(pc[0].x, 2), i8x2_to_bf16x2(pc[0].y, 0),
+                          i8x2_to_bf16x2(pc[0].y, 2)};
+        ka[0] = __builtin_bit_cast(bf16x8, w4);
+      } else {
+        const float x[8] = {__uint_as_float(pc[0].x), __uint_as_float(pc[0].y), __uint_as_float(pc[0].z),
+                            __uint_as_float(pc[0].w), __uint_as_float(pc[1].x), __uint_as_float(pc[1].y),
+                            __uint_as_float(pc[1].z), __uint_as_float(pc[1].w)};
+        split8(x, ka);
       }
+      sacc = mfma_terms<NTK, 3>(ka, qb[s], sacc);
     }
+    // lane (quad, r16): positions p0 + 4 quad + i, head r16
+    float sv[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const int key = 4 * quad + i;
+      float v = sacc[i];
+      if constexpr (KVFMT == KV_I8) {
+        const uint32_t hw = i < 2 ? T.ks4.x : T.ks4.y;
+        float ksc = f16_to_f32((uint16_t)((i & 1) ? hw >> 16 : hw & 0xffffu));
+        if (EDGE && has_new && key == kn) ksc = new_ks;
+        v *= ksc;
+      }
+      sv[i] = (!EDGE || p0 + key < t_end) ? v : -INFINITY;   // a stale row past the end is dropped
+    }
+    // the online softmax of head r16 over the block's 16 positions (4 lanes of the column)
+    float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float mn = fmaxf(mc, mx);                // finite: the chunk's first position is in range
+    const float al = __builtin_amdgcn_exp2f(mc - mn);   // 2^(-inf) = 0 on the first block
+    float pr[4], ps = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      pr[i] = __builtin_amdgcn_exp2f(sv[i] - mn);
+      ps += pr[i];
+    }
+    ps += __shfl_xor(ps, 16, 64);
+    ps += __shfl_xor(ps, 32, 64);
+    lc = lc * al + ps;
+    mc = mn;
+    // P and alpha to the P V layout through this wave's LDS (a wave's LDS accesses complete
+    // in order; the empty asm keeps the compiler from moving them across each other)
+    if (r16 < G) {
+#pragma unroll
+      for (int i = 0; i < 4; i++) pl[(4 * quad + i) * G + r16] = pr[i];
+      if (quad == 0) pl[16 * G + r16] = al;
+    }
+    asm volatile("" ::: "memory");
     float alpha[G], p_[NI][G];
 #pragma unroll
-    for (int h = 0; h < G; h++) {
-      float mx = s[0][h];
+    for (int h = 0; h < G; h++) alpha[h] = pl[16 * G + h];
 #pragma unroll
-      for (int i = 1; i < NI; i++) mx = fmaxf(mx, s[i][h]);
-      mx = xgrp_max<LPP>(mx);
-      const float mn = fmaxf(m[h], mx);
-      alpha[h] = __builtin_amdgcn_exp2f(m[h] - mn);   // 2^(-inf) = 0 on the first block
-      float ps = 0.f;
+    for (int i = 0; i < NI; i++)
 #pragma unroll
-      for (int i = 0; i < NI; i++) {
-        p_[i][h] = __builtin_amdgcn_exp2f(s[i][h] - mn);
-        ps += p_[i][h];
-      }
-      ps = xgrp_sum<LPP>(ps);
-      l[h] = l[h] * alpha[h] + ps;
-      m[h] = mn;
-    }
+      for (int h = 0; h < G; h++) p_[i][h] = pl[(PPI * i + pg) * G + h];
+    asm volatile("" ::: "memory");
+    // ---- O = O * alpha + P V ----
 #pragma unroll
     for (int h = 0; h < G; h++)
 #pragma unroll
       for (int e = 0; e < ELEM; e++) acc[h][e] *= alpha[h];
 #pragma unroll
     for (int i = 0; i < NI; i++) {
+      const int p = p0 + PPI * i + pg;
+      const bool isnew = EDGE && has_new && p == pos;
+      const bool valid = !EDGE || p < t_end;   // rows past the chunk's end (last block) are never attended
       float vf[ELEM];
       decode_piece<KVFMT, ELEM>(T.v[i], vf);
       // a stale row past the end holds anything, and 0 times a non-finite value is not 0
 #pragma unroll
-      for (int e = 0; e < ELEM; e++) vf[e] = isnew[i] ? nv[e] : (valid[i] ? vf[e] : 0.f);
+      for (int e = 0; e < ELEM; e++) vf[e] = isnew ? nv[e] : (valid ? vf[e] : 0.f);
 #pragma unroll
       for (int h = 0; h < G; h++) {
         float pv = p_[i][h];
-        if constexpr (KVFMT == KV_I8) pv = valid[i] ? pv * (isnew[i] ? 1.f : T.vs[i]) : 0.f;   // V's row scale into p
+        if constexpr (KVFMT == KV_I8) pv = valid ? pv * (isnew ? 1.f : T.vs[i]) : 0.f;   // V's row scale into p
 #pragma unroll
         for (int e = 0; e < ELEM; e++) acc[h][e] = fmaf(pv, vf[e], acc[h][e]);
       }
@@ -856,11 +949,18 @@ __global__ __launch_bounds__(256) void k_attn_w(AttnCtx a, const StepDesc* desc,
     issue(t + 3, TB);
   }
 
-  // the position groups' accumulators, then the partial in k_attn's layout
+  // the position groups' accumulators, each head's max and sum (from its column's lanes),
+  // then the partial in k_attn's layout
 #pragma unroll
   for (int h = 0; h < G; h++)
 #pragma unroll
     for (int e = 0; e < ELEM; e++) acc[h][e] = xgrp_sum<LPP>(acc[h][e]);
+  float mh[G], lh[G];
+#pragma unroll
+  for (int h = 0; h < G; h++) {
+    mh[h] = __shfl(mc, h, 64);
+    lh[h] = __shfl(lc, h, 64);
+  }
   const int cs = HD + 2;
   if (pg == 0) {
 #pragma unroll
@@ -869,8 +969,8 @@ __global__ __launch_bounds__(256) void k_attn_w(AttnCtx a, const StepDesc* desc,
 #pragma unroll
       for (int e = 0; e < ELEM; e++) gstore<float>(P + e0 + e, acc[h][e]);   // (rows of hd + 2: no 16-B alignment)
       if (lane == 0) {
-        P[HD] = m[h] * 0.6931471805599453f;   // base-2 running max back to natural units
-        P[HD + 1] = l[h];
+        P[HD] = mh[h] * 0.6931471805599453f;   // base-2 running max back to natural units
+        P[HD + 1] = lh[h];
       }
     }
   }
@@ -1145,45 +1245,6 @@ __host__ __device__ inline PfLayout pf_layout(int hd, int kvfmt) {
   return L;
 }
 
-// x = hi + mid + lo as three bf16 bit patterns (each rounded to nearest even; the
-// differences are exact in fp32)
-__device__ __forceinline__ void split3(float x, uint32_t (&t)[3]) {
-  t[0] = f32_to_bf16(x);
-  const float r1 = x - bf16_to_f32(t[0]);
-  t[1] = f32_to_bf16(r1);
-  t[2] = f32_to_bf16(r1 - bf16_to_f32(t[1]));
-}
-
-// 8 fp32 values as the three bf16x8 operand terms
-__device__ __forceinline__ void split8(const float (&x)[8], bf16x8 (&out)[3]) {
-  u32x4 w[3];
-#pragma unroll
-  for (int u = 0; u < 4; u++) {
-    uint32_t a[3], b[3];
-    split3(x[2 * u], a);
-    split3(x[2 * u + 1], b);
-#pragma unroll
-    for (int s = 0; s < 3; s++) w[s][u] = a[s] | (b[s] << 16);
-  }
-#pragma unroll
-  for (int s = 0; s < 3; s++) out[s] = __builtin_bit_cast(bf16x8, w[s]);
-}
-
-// acc += A B for A given as three terms and B as NB terms (1: exact in bf16, 3: fp32), the
-// term products down to 2^-24; smaller terms first
-template <int NB>
-__device__ __forceinline__ f32x4 mfma_split(const bf16x8 (&a)[3], const bf16x8 (&b)[3], f32x4 acc) {
-  if constexpr (NB == 3) {
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[0], b[2], acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[1], b[1], acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[0], b[1], acc, 0, 0, 0);
-  }
-  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[2], b[0], acc, 0, 0, 0);
-  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[1], b[0], acc, 0, 0, 0);
-  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[0], b[0], acc, 0, 0, 0);
-  return acc;
-}
-
 // sum or max over the 16 lanes of a lane's row group (lanes l ^ 1, 2, 4, 8): every lane of
 // the group gets the same result
 __device__ __forceinline__ float grp16_sum(float v) {
@@ -1334,7 +1395,7 @@ __global__ __launch_bounds__(256) void k_attn_prefill(Dims d, const StepDesc* de
           bf16x8 kb8[3];
 #pragma unroll
           for (int u = 0; u < NT; u++) kb8[u] = *(const bf16x8*)(kt[u] + at);
-          sacc[kb] = mfma_split<NT>(qa[s], kb8, sacc[kb]);
+          sacc[kb] = mfma_terms<3, NT>(qa[s], kb8, sacc[kb]);
         }
       }
       // lane: rows 4 quad + i, key t0 + 16 kb + r16
@@ -1398,7 +1459,7 @@ __global__ __launch_bounds__(256) void k_attn_prefill(Dims d, const StepDesc* de
           bf16x8 vb8[3];
 #pragma unroll
           for (int u = 0; u < NT; u++) vb8[u] = *(const bf16x8*)(vt[u] + at);
-          oacc[db] = mfma_split<NT>(pa, vb8, oacc[db]);
+          oacc[db] = mfma_terms<3, NT>(pa, vb8, oacc[db]);
         }
       }
     }
