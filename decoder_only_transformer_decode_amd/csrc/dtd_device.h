@@ -165,7 +165,7 @@ __device__ __forceinline__ float deq_elem(const MatDev& m, int wfmt, int r, int 
 // so K/V is read once per query group (the GQA decode rule of the Qwen3-8B engine
 // article, 4.4.2).  Softmax is online across tiles (running max, running sum, rescaled
 // accumulators); the item leaves an unnormalised partial (acc, m, l) per head, merged by
-// combine_one.  The item whose chunk holds the new position rounds the new k/v to the KV
+// k_combine.  The item whose chunk holds the new position rounds the new k/v to the KV
 // encoding, writes it through the block table and attends to the stored value.
 // ---------------------------------------------------------------------------------------
 
@@ -357,21 +357,6 @@ __device__ __forceinline__ void attn_item(const AttnCtx& a, int b, int j, int c,
     put(P + hd, st_s[g * 4]);
     put(P + hd + 1, st_s[g * 4 + 1]);
   }
-}
-
-// element i of one head's output from its nv chunk partials P [nv][hd+2]:
-// sum_c e^(m_c - M) acc_c[i] / sum_c e^(m_c - M) l_c
-__device__ __forceinline__ float combine_one(const float* P, int nv, int hd, int i) {
-  const int cs = hd + 2;
-  float M = -INFINITY;
-  for (int c = 0; c < nv; c++) M = fmaxf(M, P[c * cs + hd]);
-  float L = 0.f, acc = 0.f;
-  for (int c = 0; c < nv; c++) {
-    const float w = expf(P[c * cs + hd] - M);
-    L += w * P[c * cs + hd + 1];
-    acc += w * P[c * cs + i];
-  }
-  return acc / L;
 }
 
 }  // namespace dev

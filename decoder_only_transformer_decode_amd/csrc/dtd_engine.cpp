@@ -23,6 +23,7 @@ using namespace dtd;
 namespace {
 
 constexpr int kRing = 64;   // pinned step-descriptor slots in flight
+constexpr int kEvictRing = 8;   // pinned block-list slots of device-side evictions in flight
 
 struct LayerW {
   MatDev qkv, o, gu, down;
@@ -43,6 +44,9 @@ struct Seq {
   // each cache entry (kept in step only while a budget is set)
   int rpos = 0;
   std::vector<int32_t> kv_pos;
+  // the positions live in the device's row (kvpos_dev) instead: after an eviction decided on
+  // the device, until the host needs them again
+  bool pos_on_dev = false;
 };
 
 // Initial-Key KV budget of one sequence (the C17 engine article, 5.3)
@@ -130,6 +134,11 @@ struct dtd_engine {
   float* p_score_q = nullptr;     // step kernel: [L][q_dim] queries of the scored layers
   float* p_score_stat = nullptr;  // step kernel: [L][Hq][2] their softmax max and normaliser
   int32_t* evict_dev = nullptr;   // [3][max_ctx] eviction lists (old blocks, new blocks, kept entries)
+  int32_t* kvpos_dev = nullptr;   // [max_seqs][max_ctx] entry positions of budgeted sequences (device-side evictions)
+  int32_t* evict_host = nullptr;  // pinned [kEvictRing][2][max_blocks] block lists for device-side evictions
+  hipEvent_t evict_ev[kEvictRing];
+  bool evict_ev_used[kEvictRing];
+  int evict_ring = 0;
   int step_score_min = 1 << 30;   // first scored layer of the step being run
   int step_max_pos = 0;
 
@@ -362,10 +371,13 @@ static void free_all(dtd_engine* e) {
   void* ps[] = {e->rope_cos, e->rope_sin, e->kpool, e->vpool, e->kspool, e->vspool, e->bt_dev,
                 e->x, e->xn, e->q, e->knew, e->vnew, e->partials, e->gemm_partials, e->o, e->h, e->logits,
                 e->err_dev, e->desc_dev, e->rows_dev, e->players, e->tags, e->tok_scratch,
-                e->scores_dev, e->attn_stat, e->evict_dev, e->p_score_q, e->p_score_stat};
+                e->scores_dev, e->attn_stat, e->evict_dev, e->p_score_q, e->p_score_stat, e->kvpos_dev};
   for (void* p : ps)
     if (p) (void)hipFree(p);
   if (e->desc_host) (void)hipHostFree(e->desc_host);
+  if (e->evict_host) (void)hipHostFree(e->evict_host);
+  for (int i = 0; i < kEvictRing; i++)
+    if (e->evict_ev[i]) (void)hipEventDestroy(e->evict_ev[i]);
   if (e->err_host) (void)hipHostFree(e->err_host);
   for (int i = 0; i < kRing; i++)
     if (e->desc_ev[i]) (void)hipEventDestroy(e->desc_ev[i]);
@@ -384,6 +396,7 @@ extern "C" dtd_status dtd_create(const dtd_config* cfg, void* hip_stream, dtd_en
   }
   dtd_engine* e = new dtd_engine();
   for (int i = 0; i < kRing; i++) { e->desc_ev[i] = nullptr; e->desc_ev_used[i] = false; }
+  for (int i = 0; i < kEvictRing; i++) { e->evict_ev[i] = nullptr; e->evict_ev_used[i] = false; }
   e->cfg = *cfg;
   e->d = make_dims(cfg);
   e->stream = (hipStream_t)hip_stream;
@@ -457,7 +470,8 @@ extern "C" dtd_status dtd_create(const dtd_config* cfg, void* hip_stream, dtd_en
       (st = dev_alloc(e, &e->attn_stat, (size_t)MB * d.Hq * 2 * 4)) ||
       (st = dev_alloc(e, &e->p_score_q, (size_t)d.L * d.q_dim * 4)) ||
       (st = dev_alloc(e, &e->p_score_stat, (size_t)d.L * d.Hq * 2 * 4)) ||
-      (st = dev_alloc(e, &e->evict_dev, (size_t)3 * cfg->max_ctx * 4)))
+      (st = dev_alloc(e, &e->evict_dev, (size_t)3 * cfg->max_ctx * 4)) ||
+      (st = dev_alloc(e, &e->kvpos_dev, (size_t)cfg->max_seqs * cfg->max_ctx * 4)))
     return cleanup(st);
   if (hipMemset(e->err_dev, 0, 16) != hipSuccess) return cleanup(DTD_E_HIP);
 
@@ -490,11 +504,14 @@ extern "C" dtd_status dtd_create(const dtd_config* cfg, void* hip_stream, dtd_en
     if (hipMemset(e->tags, 0, sizeof(uint64_t) * e->tags_words) != hipSuccess) return cleanup(DTD_E_HIP);
   }
   if (hipHostMalloc((void**)&e->desc_host, sizeof(StepDesc) * kRing, 0) != hipSuccess ||
-      hipHostMalloc((void**)&e->err_host, 16, 0) != hipSuccess)
+      hipHostMalloc((void**)&e->err_host, 16, 0) != hipSuccess ||
+      hipHostMalloc((void**)&e->evict_host, sizeof(int32_t) * kEvictRing * 2 * d.max_blocks, 0) != hipSuccess)
     return cleanup(DTD_E_OOM);
   memset(e->err_host, 0, 16);
   for (int i = 0; i < kRing; i++)
     if (hipEventCreateWithFlags(&e->desc_ev[i], hipEventDisableTiming) != hipSuccess) return cleanup(DTD_E_HIP);
+  for (int i = 0; i < kEvictRing; i++)
+    if (hipEventCreateWithFlags(&e->evict_ev[i], hipEventDisableTiming) != hipSuccess) return cleanup(DTD_E_HIP);
 
   // free lists: slots in order; blocks in a fixed shuffled order so that block tables are
   // never the identity (the paged path is exercised even for one sequence)
@@ -1134,14 +1151,71 @@ static dtd_status budget_seq_created(dtd_engine* e, int64_t seq_id, Seq& s) {
   return DTD_OK;
 }
 
+// Brings the host's entry positions of a budgeted sequence up to date when they live on the
+// device: its first `known` entries from the device row (synchronous).
+static dtd_status pull_kv_pos(dtd_engine* e, Seq& s, int known) {
+  if (!s.pos_on_dev) return DTD_OK;
+  s.kv_pos.resize((size_t)known);
+  HIP_OK(e, hipStreamSynchronize(e->stream));
+  if (known > 0)
+    HIP_OK(e, hipMemcpy(s.kv_pos.data(), e->kvpos_dev + (size_t)s.slot * e->cfg.max_ctx, (size_t)known * 4,
+                        hipMemcpyDeviceToHost));
+  s.pos_on_dev = false;
+  return DTD_OK;
+}
+
 // Brings a sequence back to its budget when it holds more entries: the entries of its first
 // n_initial positions, its last n_recent entries, and the highest attention-score sums of the
 // others (the earlier entry on equal sums) stay, in order, copied into fresh blocks; the rest
-// are dropped with their scores.  Synchronous (the host reads the scores).
-static dtd_status kv_evict(dtd_engine* e, Seq& s, const KvBudget& kb) {
+// are dropped with their scores.  new_pos: the token position of the entry the last step
+// appended (entry n - 1).
+//  - One entry over the budget (a decode step): decided and carried out on the device, with
+//    no host round trip; the positions then live in the device's row.
+//  - Otherwise (a prefill): synchronous, the host reads the scores.
+static dtd_status kv_evict(dtd_engine* e, Seq& s, const KvBudget& kb, int new_pos) {
   const int n = s.len;
-  if (n <= kb.budget) return DTD_OK;
   const int mc = e->cfg.max_ctx;
+  if (n == kb.budget + 1 && n > kb.n_initial + kb.n_recent) {
+    // entries [0, n_initial) hold positions 0 .. n_initial - 1 (never evicted)
+    if (!s.pos_on_dev) {
+      HIP_OK(e, hipMemcpy(e->kvpos_dev + (size_t)s.slot * mc, s.kv_pos.data(), (size_t)(n - 1) * 4,
+                          hipMemcpyHostToDevice));
+      s.pos_on_dev = true;
+    }
+    const int m = n - 1, nb = blocks_needed(e, m);
+    if (!make_room(e, nb))
+      return fail(e, DTD_E_KVFULL, "KV budget: %d blocks for the kept entries, %zu free", nb, e->free_blocks.size());
+    const int ring = e->evict_ring;
+    int32_t* hs = e->evict_host + (size_t)ring * 2 * e->d.max_blocks;
+    if (e->evict_ev_used[ring]) HIP_OK(e, hipEventSynchronize(e->evict_ev[ring]));
+    std::copy(s.blocks.begin(), s.blocks.end(), hs);
+    std::vector<int32_t> fresh;
+    for (int i = 0; i < nb; i++) fresh.push_back(take_block(e));
+    std::copy(fresh.begin(), fresh.end(), hs + e->d.max_blocks);
+    hipStream_t st = e->stream;
+    HIP_OK(e, hipMemcpyAsync(e->evict_dev, hs, s.blocks.size() * 4, hipMemcpyHostToDevice, st));
+    HIP_OK(e, hipMemcpyAsync(e->evict_dev + mc, hs + e->d.max_blocks, (size_t)nb * 4, hipMemcpyHostToDevice, st));
+    HIP_OK(e, launch_evict_one(e->scores_dev + (size_t)s.slot * mc, e->kvpos_dev + (size_t)s.slot * mc, n,
+                               kb.n_initial, n - kb.n_recent, new_pos, e->evict_dev + 2 * (size_t)mc, st));
+    HIP_OK(e, launch_kv_gather(e->d, e->players, e->evict_dev, e->evict_dev + mc, e->evict_dev + 2 * (size_t)mc, m,
+                               st));
+    HIP_OK(e, hipMemcpyAsync(e->bt_dev + (size_t)s.slot * e->d.max_blocks, hs + e->d.max_blocks, (size_t)nb * 4,
+                             hipMemcpyHostToDevice, st));
+    HIP_OK(e, hipEventRecord(e->evict_ev[ring], st));
+    e->evict_ev_used[ring] = true;
+    e->evict_ring = (ring + 1) % kEvictRing;
+    for (int32_t b : s.blocks) drop_block(e, b);   // reused only by work queued after the gather
+    s.blocks.assign(fresh.begin(), fresh.end());
+    s.len = m;
+    s.tokens_known = false;
+    return DTD_OK;
+  }
+  if (s.pos_on_dev) {
+    dtd_status ps = pull_kv_pos(e, s, n - 1);
+    if (ps) return ps;
+    s.kv_pos.push_back(new_pos);
+  }
+  if (n <= kb.budget) return DTD_OK;
   std::vector<float> sc((size_t)n);
   HIP_OK(e, hipStreamSynchronize(e->stream));
   HIP_OK(e, hipMemcpy(sc.data(), e->scores_dev + (size_t)s.slot * mc, (size_t)n * 4, hipMemcpyDeviceToHost));
@@ -1254,7 +1328,7 @@ extern "C" dtd_status dtd_prefill(dtd_engine* e, int64_t seq_id, const int32_t* 
   if (pc && s.tokens_known) s.tokens.insert(s.tokens.end(), host.begin() + reuse, host.end());
   st = prefill_run(e, seq_id, s, tokens_dev, n, next_token_dev, logits_dev);
   if (st) return st;
-  if (kb) return kv_evict(e, s, *kb);
+  if (kb) return kv_evict(e, s, *kb, s.rpos - 1);
   if (pc && s.tokens_known && (int)s.tokens.size() == s.len) pcache_insert(e, s, s.tokens.data(), s.len);
   return DTD_OK;
 }
@@ -1268,6 +1342,7 @@ static dtd_status prefill_run(dtd_engine* e, int64_t seq_id, Seq& s, const int32
   const KvBudget* kb = budget_of(e, seq_id);
   const bool extra_on = kb || s.rpos != s.len;
   const int sfrom = kb ? e->d.L - kb->score_layers : e->d.L;
+  if (kb && (st = pull_kv_pos(e, s, s.len))) return st;   // positions are appended on the host below
   // Batched prefill: the prompt in chunks of up to kPrefillChunk positions, each chunk one
   // step of the per-sub-step schedule with the chunk's positions as its batch (projections on
   // the matrix cores where the formats allow); every position's K/V is appended before the
@@ -1420,13 +1495,13 @@ static dtd_status decode_impl(dtd_engine* e, int32_t batch, const int64_t* seq_i
   st = sample_rows(e, batch, seq_ids_host, rps, e->logits, next_tokens_dev);
   if (st) return st;
   for (int b = 0; b < batch; b++) {
-    if (kbs[b]) ss[b]->kv_pos.push_back(ss[b]->rpos);
+    if (kbs[b] && !ss[b]->pos_on_dev) ss[b]->kv_pos.push_back(ss[b]->rpos);
     ss[b]->len++;
     ss[b]->rpos++;
     ss[b]->tokens_known = false;   // the token ids of a decode step stay on the device
   }
   for (int b = 0; b < batch; b++)
-    if (kbs[b] && (st = kv_evict(e, *ss[b], *kbs[b]))) return st;
+    if (kbs[b] && (st = kv_evict(e, *ss[b], *kbs[b], ss[b]->rpos - 1))) return st;
   return DTD_OK;
 }
 
@@ -1562,7 +1637,15 @@ extern "C" int32_t dtd_debug_kv_positions(const dtd_engine* e, int64_t seq_id, i
   auto it = e->seqs.find(seq_id);
   if (it == e->seqs.end()) return DTD_E_NOSEQ;
   const Seq& s = it->second;
-  for (int i = 0; i < std::min(s.len, cap); i++)
+  const int n = std::min(s.len, cap);
+  if (s.pos_on_dev) {   // after evictions decided on the device
+    if (n > 0 && (hipStreamSynchronize(e->stream) != hipSuccess ||
+                  hipMemcpy(out_host, e->kvpos_dev + (size_t)s.slot * e->cfg.max_ctx, (size_t)n * 4,
+                            hipMemcpyDeviceToHost) != hipSuccess))
+      return DTD_E_HIP;
+    return s.len;
+  }
+  for (int i = 0; i < n; i++)
     out_host[i] = budget_of(e, seq_id) ? s.kv_pos[(size_t)i] : (s.rpos == s.len ? i : -1);
   return s.len;
 }

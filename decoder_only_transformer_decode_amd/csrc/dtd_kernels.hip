@@ -52,6 +52,35 @@ __global__ __launch_bounds__(256) void k_rmsnorm(const float* x, const float* g,
   __shared__ float red[4];
   const int b = blockIdx.x;
   const float* xb = x + (size_t)b * D;
+  if ((D & 3) == 0 && D <= 8 * 4 * 256) {
+    // the row in 16-byte pieces, up to 8 per thread, loaded once and kept in registers
+    constexpr int NP = 8;
+    float4 v[NP];
+    float ss = 0.f;
+#pragma unroll
+    for (int k = 0; k < NP; k++) {
+      const int i = 4 * ((int)threadIdx.x + 256 * k);
+      v[k] = i < D ? *(const float4*)(xb + i) : make_float4(0.f, 0.f, 0.f, 0.f);
+      ss += v[k].x * v[k].x + v[k].y * v[k].y + v[k].z * v[k].z + v[k].w * v[k].w;
+    }
+    ss = block_sum(ss, red);
+    const float r = 1.0f / sqrtf(ss / (float)D + eps);
+#pragma unroll
+    for (int k = 0; k < NP; k++) {
+      const int i = 4 * ((int)threadIdx.x + 256 * k);
+      if (i >= D) continue;
+      const float4 gg = *(const float4*)(g + i);
+      const float y0 = v[k].x * r * gg.x, y1 = v[k].y * r * gg.y, y2 = v[k].z * r * gg.z, y3 = v[k].w * r * gg.w;
+      if (act == ACT_BF16) {
+        const uint32_t lo = f32_to_bf16(y0) | ((uint32_t)f32_to_bf16(y1) << 16);
+        const uint32_t hi = f32_to_bf16(y2) | ((uint32_t)f32_to_bf16(y3) << 16);
+        *(uint2*)((uint16_t*)xn + (size_t)b * D + i) = make_uint2(lo, hi);
+      } else {
+        *(float4*)((float*)xn + (size_t)b * D + i) = make_float4(y0, y1, y2, y3);
+      }
+    }
+    return;
+  }
   float ss = 0.f;
   for (int i = threadIdx.x; i < D; i += 256) ss += xb[i] * xb[i];
   ss = block_sum(ss, red);
@@ -1009,19 +1038,39 @@ __global__ __launch_bounds__(256) void k_kv_copy_block(const PLayer* layers, int
   for (size_t i = n16 * 16 + threadIdx.x; i < n; i += 256) b[i] = a[i];
 }
 
-// one (head, sequence): o = merge of its chunk partials, rounded to the activation type;
-// with stat, also the softmax's max M and normaliser L (natural-log units) per (sequence, head)
+// one (head, sequence), a block of max(hd, 64) threads: o = merge of its chunk partials,
+// rounded to the activation type; with stat, also the softmax's max M and normaliser L
+// (natural-log units) per (sequence, head).  Each chunk's weight e^(m_c - M) is worked out
+// once, into LDS; the sums over chunks have a fixed order.
 __global__ __launch_bounds__(256) void k_combine(Dims d, const StepDesc* desc, const float* partials,
                                                  void* o, float* stat) {
-  const int h = blockIdx.x, b = blockIdx.y, i = threadIdx.x;
+  extern __shared__ float w_s[];         // [nch] chunk weights
+  __shared__ float red[4];
+  const int h = blockIdx.x, b = blockIdx.y, i = threadIdx.x, nt = blockDim.x;
   const int nv = (desc->pos[b] + d.ct) / d.ct;
-  const float* P = partials + ((size_t)b * d.Hq + h) * d.nch * (d.hd + 2);
-  if (i < d.hd) store_act(o, (size_t)b * d.q_dim + (size_t)h * d.hd + i, combine_one(P, nv, d.hd, i), d.act);
+  const int cs = d.hd + 2;
+  const float* P = partials + ((size_t)b * d.Hq + h) * d.nch * cs;
+  float mx = -INFINITY;
+  for (int c = i; c < nv; c += nt) mx = fmaxf(mx, P[c * cs + d.hd]);
+  const float M = block_max(mx, red);
+  float ls = 0.f;
+  for (int c = i; c < nv; c += nt) {
+    const float w = expf(P[c * cs + d.hd] - M);
+    w_s[c] = w;
+    ls += w * P[c * cs + d.hd + 1];
+  }
+  const float L = block_sum(ls, red);   // (its barriers also publish w_s)
+  if (i < d.hd) {
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    int c = 0;
+    for (; c + 4 <= nv; c += 4) {
+#pragma unroll
+      for (int u = 0; u < 4; u++) acc[u] += w_s[c + u] * P[(c + u) * cs + i];
+    }
+    for (; c < nv; c++) acc[0] += w_s[c] * P[c * cs + i];
+    store_act(o, (size_t)b * d.q_dim + (size_t)h * d.hd + i, ((acc[0] + acc[1]) + (acc[2] + acc[3])) / L, d.act);
+  }
   if (stat && i == 0) {
-    const int cs = d.hd + 2;
-    float M = -INFINITY, L = 0.f;
-    for (int c = 0; c < nv; c++) M = fmaxf(M, P[c * cs + d.hd]);
-    for (int c = 0; c < nv; c++) L += expf(P[c * cs + d.hd] - M) * P[c * cs + d.hd + 1];
     stat[((size_t)b * d.Hq + h) * 2] = M;
     stat[((size_t)b * d.Hq + h) * 2 + 1] = L;
   }
@@ -1078,6 +1127,56 @@ __global__ __launch_bounds__(256) void k_score(Dims d, const StepDesc* desc, int
     }
   }
   if (lane == 0) scores[(size_t)slot * d.max_ctx + t] += sum;
+}
+
+// KV budget eviction in the steady state of decoding (the Initial-Key cache of the C17 engine
+// article, 5.3): a step left n = budget + 1 entries, so one goes.  The entry is the middle one
+// (index in [n_init, rec0)) with the lowest score sum, the later one among equal sums (the
+// earlier entry wins ties).  The kernel records new_pos as the position of entry n - 1 (the
+// one the step appended), closes the gap in the score and position rows (entries after it
+// move down one place; the freed last score starts again at 0) and writes the kept indices,
+// in order, for k_kv_gather.  One block of 1024 threads, no host round trip.
+__global__ __launch_bounds__(1024) void k_evict_one(float* scores, int32_t* kvpos, int n, int n_init, int rec0,
+                                                    int new_pos, int32_t* keep) {
+  __shared__ float wbest[16];
+  __shared__ int widx[16];
+  __shared__ int ev;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  if (t == 0) kvpos[n - 1] = new_pos;
+  float best = INFINITY;
+  int bi = -1;
+  for (int i = n_init + t; i < rec0; i += 1024) {
+    const float s = scores[i];
+    if (s < best || (s == best && i > bi)) { best = s; bi = i; }
+  }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    const float ob = __shfl_xor(best, m, 64);
+    const int oi = __shfl_xor(bi, m, 64);
+    if (ob < best || (ob == best && oi > bi)) { best = ob; bi = oi; }
+  }
+  if (lane == 0) { wbest[wave] = best; widx[wave] = bi; }
+  __syncthreads();
+  if (t == 0) {
+    for (int w = 1; w < 16; w++)
+      if (wbest[w] < best || (wbest[w] == best && widx[w] > bi)) { best = wbest[w]; bi = widx[w]; }
+    ev = bi;
+  }
+  __syncthreads();
+  const int e = ev;   // >= n_init: the middle range is never empty at n = budget + 1
+  // entries e+1 .. n-1 move down one place, 1024 at a time: every chunk reads its sources
+  // before any of them is overwritten by the next chunk
+  for (int base = e; base < n - 1; base += 1024) {
+    const int i = base + t;
+    float sv = 0.f;
+    int pv = 0;
+    if (i < n - 1) { sv = scores[i + 1]; pv = kvpos[i + 1]; }
+    __syncthreads();
+    if (i < n - 1) { scores[i] = sv; kvpos[i] = pv; }
+    __syncthreads();
+  }
+  if (t == 0) scores[n - 1] = 0.f;
+  for (int i = t; i < n - 1; i += 1024) keep[i] = i < e ? i : i + 1;
 }
 
 // KV budget eviction: copies cache entries keep[i] (i < n, through the old block list) to
@@ -1691,7 +1790,8 @@ hipError_t launch_kv_copy_block(const Dims& d, const PLayer* layers, int src, in
 
 hipError_t launch_combine(const Dims& d, const StepDesc* desc, int B, const float* partials,
                           void* o, hipStream_t st, float* stat) {
-  hipLaunchKernelGGL(k_combine, dim3(d.Hq, B), dim3(d.hd), 0, st, d, desc, partials, o, stat);
+  const int nt = (d.hd + 63) / 64 * 64;
+  hipLaunchKernelGGL(k_combine, dim3(d.Hq, B), dim3(nt), (size_t)d.nch * 4, st, d, desc, partials, o, stat);
   return hipGetLastError();
 }
 
@@ -1721,6 +1821,12 @@ hipError_t launch_score(const Dims& d, const StepDesc* desc, int B, int max_pos,
   if (d.kvfmt == KV_F32) hipLaunchKernelGGL(k_score<KV_F32>, grid, dim3(256), smem, st, d, desc, layer, q, kv, bt, stat, scores);
   else if (d.kvfmt == KV_BF16) hipLaunchKernelGGL(k_score<KV_BF16>, grid, dim3(256), smem, st, d, desc, layer, q, kv, bt, stat, scores);
   else hipLaunchKernelGGL(k_score<KV_I8>, grid, dim3(256), smem, st, d, desc, layer, q, kv, bt, stat, scores);
+  return hipGetLastError();
+}
+
+hipError_t launch_evict_one(float* scores, int32_t* kvpos, int n, int n_init, int rec0, int new_pos, int32_t* keep,
+                            hipStream_t st) {
+  hipLaunchKernelGGL(k_evict_one, dim3(1), dim3(1024), 0, st, scores, kvpos, n, n_init, rec0, new_pos, keep);
   return hipGetLastError();
 }
 
