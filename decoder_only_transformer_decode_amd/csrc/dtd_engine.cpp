@@ -141,6 +141,7 @@ struct dtd_engine {
   int evict_ring = 0;
   int step_score_min = 1 << 30;   // first scored layer of the step being run
   int step_max_pos = 0;
+  int step_chunks = 0;           // decode attention chunks of the current step (k_attn_w shapes)
 
   // prefix cache: entries by id, and every prefix of every entry by its hash
   int pcache_cap = 0;             // 0: off
@@ -767,6 +768,49 @@ static dtd_status run_sub_steps(dtd_engine* e, int B, bool do_head, const uint8_
 // partials: the split-K attention partials of the per-sub-step schedule (the engine's buffer,
 // or the allocation-free entry point's static scratch).  force_per_kernel: run that schedule
 // even at batch 1; no_timing: leave the kernel-timing hooks (which may create events) out.
+// Split-K of the decode attention.  The one-wave-per-chunk kernel (wplan) gets per-sequence
+// chunks: each context cut into equal chunks (a multiple of 16 positions) of at most T, with
+// T the shortest length (from 64 up, at most 2048) for which the whole batch's chunks, one
+// wave each per KV head, fit in one resident wave per slot (8 per compute unit).  With one
+// fixed chunk length instead, mixed contexts leave short last chunks and more waves than
+// slots, and the last ones run alone.  Other shapes split every context at d.ct.
+static void plan_attention_chunks(dtd_engine* e, StepDesc* hd, int B, const int* poss, bool wplan) {
+  const Dims& d = e->d;
+  e->step_chunks = 0;
+  hd->n_chunks = 0;
+  if (!wplan) {
+    for (int b = 0; b < B; b++) hd->ct[b] = d.ct;
+    return;
+  }
+  auto r16 = [](int64_t x) { return (int)((x + 15) / 16 * 16); };
+  const int64_t slots = (int64_t)e->cus * 8;
+  int64_t tot = 0;
+  int maxlen = 1;
+  for (int b = 0; b < B; b++) {
+    tot += poss[b] + 1;
+    maxlen = std::max(maxlen, poss[b] + 1);
+  }
+  // chunks of the batch at bound T (written to the descriptor when write)
+  auto chunks = [&](int T, bool write) {
+    int n = 0;
+    for (int b = 0; b < B; b++) {
+      const int len = poss[b] + 1, n0 = (len + T - 1) / T;
+      const int ct = r16((len + n0 - 1) / n0);
+      n += (len + ct - 1) / ct;
+      if (write) {
+        hd->ct[b] = ct;
+        hd->cend[b] = n;
+      }
+    }
+    return n;
+  };
+  int T = std::max(64, std::max(r16((tot * d.Hkv + slots - 1) / slots), r16((maxlen + d.nch - 1) / d.nch)));
+  T = std::min(T, 2048);
+  while (T < 2048 && (int64_t)chunks(T, false) * d.Hkv > slots) T += 16;
+  hd->n_chunks = chunks(T, true);
+  e->step_chunks = hd->n_chunks;
+}
+
 static dtd_status run_step(dtd_engine* e, int B, const int* slots, const int* poss, const int* pblks,
                            const int32_t* tokens, int32_t* next, float* logits_out, bool do_head,
                            const Update* upd, int n_upd, const uint8_t* inject = nullptr,
@@ -796,6 +840,7 @@ static dtd_status run_step(dtd_engine* e, int B, const int* slots, const int* po
     e->step_score_min = std::min(e->step_score_min, hd->score_from[b]);
     e->step_max_pos = std::max(e->step_max_pos, poss[b]);
   }
+  plan_attention_chunks(e, hd, B, poss, attn_w_shape(d) && !(append_first && B >= 2));
   for (int u = 0; u < n_upd; u++) {
     hd->upd[u][0] = upd[u].slot; hd->upd[u][1] = upd[u].lblock; hd->upd[u][2] = upd[u].pblock;
   }
@@ -936,7 +981,8 @@ static dtd_status run_sub_steps(dtd_engine* e, int B, bool do_head, const uint8_
       // blocked causal attention over the cache
       TIMED(4, launch_attn_prefill(d, e->desc_dev, B, e->step_max_pos, e->q, kv, e->bt_dev, partials, st));
     } else {
-      TIMED(4, launch_attention(d, e->desc_dev, B, e->q, e->knew, e->vnew, kv, e->bt_dev, partials, st));
+      TIMED(4, launch_attention(d, e->desc_dev, B, e->step_chunks, e->q, e->knew, e->vnew, kv, e->bt_dev, partials,
+                                st));
     }
     HIP_OK(e, launch_combine(d, e->desc_dev, B, partials, e->o, st, scored ? e->attn_stat : nullptr));
     if (scored)

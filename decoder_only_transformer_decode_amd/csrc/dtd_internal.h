@@ -27,7 +27,7 @@ struct StepDesc {
   int32_t batch;
   int32_t do_head;                   // run final norm + LM head + argmax
   int32_t n_updates;                 // block-table entries to set before the step
-  int32_t pad_;
+  int32_t n_chunks;                  // decode attention chunks with work, over the batch
   const int32_t* tokens;             // [batch] token ids (caller memory)
   int32_t* next_tokens;              // [batch] greedy outputs (caller memory)
   float* logits_out;                 // [batch][V] or null (caller memory)
@@ -40,6 +40,11 @@ struct StepDesc {
   // on (L: none), to the sequence slot's row of the score buffer
   int32_t rpos[kMaxBatch];
   int32_t score_from[kMaxBatch];
+  // Split-K of the decode attention: sequence b's context in chunks of ct[b] positions (a
+  // multiple of 16); its chunks are entries cend[b-1] .. cend[b]-1 of one list over the batch
+  // (cend[-1] = 0), which the one-wave-per-chunk kernel walks
+  int32_t ct[kMaxBatch];
+  int32_t cend[kMaxBatch];
 };
 
 struct Dims {
@@ -193,7 +198,11 @@ int gemm_splits(int N, int K, int cus);                 // K splits of an N x K 
 size_t gemm_partial_bytes(const Dims& d, int B, int cus);   // work buffer of the split-K sums
 hipError_t launch_gemm(const Dims& d, const MatDev& m, const void* xin, int B, int epi, const EpiArgs& ea,
                        float* partials, int cus, hipStream_t st);
-hipError_t launch_attention(const Dims& d, const StepDesc* desc, int B, const float* q,
+// whether the decode attention of these dimensions runs one wave per chunk (k_attn_w), which
+// takes the descriptor's per-sequence chunks; the other shapes split at d.ct
+bool attn_w_shape(const Dims& d);
+// n_chunks: the descriptor's chunk count (k_attn_w shapes)
+hipError_t launch_attention(const Dims& d, const StepDesc* desc, int B, int n_chunks, const float* q,
                             const float* knew, const float* vnew, const KvLayer& kv,
                             const int32_t* block_table, float* partials, hipStream_t st);
 hipError_t launch_kv_append(const Dims& d, const StepDesc* desc, int B, const float* knew, const float* vnew,

@@ -720,12 +720,19 @@ __global__ __launch_bounds__(256) void k_attn_w(AttnCtx a, const StepDesc* desc,
   __shared__ __attribute__((aligned(16))) uint8_t nrow_s[4][RB];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r16 = lane & 15, quad = lane >> 4;
-  const int c = blockIdx.x * 4 + wave, j = blockIdx.y, b = blockIdx.z;
+  const int w = blockIdx.x * 4 + wave, j = blockIdx.y;
   const Dims& d = a.d;
+  if (w >= desc->n_chunks) return;                      // (wave-uniform) past the chunk list
+  // chunk w of the list: sequence b = the number of sequences whose chunks end at or before
+  // w, chunk c of its context
+  const int ce = lane < desc->batch ? desc->cend[lane] : INT_MAX;
+  const int b = __popcll(__ballot(ce <= w));
+  const int c = w - (b > 0 ? __builtin_amdgcn_readlane(ce, b - 1) : 0);
+  const int ct = desc->ct[b];
   const int pos = desc->pos[b];
-  const int t_begin = c * a.ct;
+  const int t_begin = c * ct;
   if (c >= a.nch || t_begin > pos) return;              // (wave-uniform) chunk past the sequence
-  const int t_end = min(pos + 1, t_begin + a.ct);
+  const int t_end = min(pos + 1, t_begin + ct);
   const int pg = lane / LPP, e0 = (lane % LPP) * ELEM;
   const int Hkv = d.Hkv;
   float* pl = pl_s[wave];
@@ -1047,7 +1054,8 @@ __global__ __launch_bounds__(256) void k_combine(Dims d, const StepDesc* desc, c
   extern __shared__ float w_s[];         // [nch] chunk weights
   __shared__ float red[4];
   const int h = blockIdx.x, b = blockIdx.y, i = threadIdx.x, nt = blockDim.x;
-  const int nv = (desc->pos[b] + d.ct) / d.ct;
+  const int ct = desc->ct[b];
+  const int nv = (desc->pos[b] + ct) / ct;
   const int cs = d.hd + 2;
   const float* P = partials + ((size_t)b * d.Hq + h) * d.nch * cs;
   float mx = -INFINITY;
@@ -1736,7 +1744,14 @@ hipError_t launch_gemv(const Dims& d, const MatDev& m, const void* xin, int B, i
   }
 }
 
-hipError_t launch_attention(const Dims& d, const StepDesc* desc, int B, const float* q,
+bool attn_w_shape(const Dims& d) {
+  // the instantiations launch_attention dispatches to k_attn_w
+  if (d.bs != 16) return false;
+  if (d.hd == 128 || d.hd == 64) return d.G == 4;
+  return d.hd == 32 && d.G == 5 && d.kvfmt != KV_I8;
+}
+
+hipError_t launch_attention(const Dims& d, const StepDesc* desc, int B, int n_chunks, const float* q,
                             const float* knew, const float* vnew, const KvLayer& kv,
                             const int32_t* block_table, float* partials, hipStream_t st) {
   AttnCtx a;
@@ -1748,8 +1763,9 @@ hipError_t launch_attention(const Dims& d, const StepDesc* desc, int B, const fl
   a.bt = block_table;
   a.ct = d.ct;
   a.nch = d.nch;
-  if (d.bs == 16) {
-    const dim3 gw((d.nch + 3) / 4, d.Hkv, B);
+  if (attn_w_shape(d)) {
+    if (n_chunks <= 0) return hipSuccess;
+    const dim3 gw((n_chunks + 3) / 4, d.Hkv, 1);
 #define DTD_ATTN_W(KV, HDv, Gv)                                                                   \
   if (d.kvfmt == KV && d.hd == HDv && d.G == Gv) {                                                \
     hipLaunchKernelGGL((k_attn_w<KV, HDv, Gv>), gw, dim3(256), 0, st, a, desc, partials);         \
