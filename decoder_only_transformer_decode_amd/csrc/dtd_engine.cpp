@@ -768,12 +768,42 @@ static dtd_status run_sub_steps(dtd_engine* e, int B, bool do_head, const uint8_
 // partials: the split-K attention partials of the per-sub-step schedule (the engine's buffer,
 // or the allocation-free entry point's static scratch).  force_per_kernel: run that schedule
 // even at batch 1; no_timing: leave the kernel-timing hooks (which may create events) out.
-// Split-K of the decode attention.  The one-wave-per-chunk kernel (wplan) gets per-sequence
-// chunks: each context cut into equal chunks (a multiple of 16 positions) of at most T, with
-// T the shortest length (from 64 up, at most 2048) for which the whole batch's chunks, one
-// wave each per KV head, fit in one resident wave per slot (8 per compute unit).  With one
-// fixed chunk length instead, mixed contexts leave short last chunks and more waves than
-// slots, and the last ones run alone.  Other shapes split every context at d.ct.
+// Split-K of the decode attention for the one-wave-per-chunk kernel: each context (len_b =
+// pos_b + 1) cut into equal chunks of ct_b positions (a multiple of 16) of at most T, with T
+// the shortest length (from 64, at most 2048, and at least len_b / nch for every b) for which
+// the whole batch's chunks, one wave each per KV head, fit in `slots` resident waves.  With
+// one fixed chunk length instead, mixed contexts leave short last chunks and more waves than
+// slots, and the last ones run alone.  Writes ct[b] and the running chunk count cend[b];
+// returns the batch's chunk count.
+static int plan_chunks(int B, const int* poss, int Hkv, int nch, int64_t slots, int32_t* ct, int32_t* cend) {
+  auto r16 = [](int64_t x) { return (int)((x + 15) / 16 * 16); };
+  int64_t tot = 0;
+  int maxlen = 1;
+  for (int b = 0; b < B; b++) {
+    tot += poss[b] + 1;
+    maxlen = std::max(maxlen, poss[b] + 1);
+  }
+  auto chunks = [&](int T, bool write) {
+    int n = 0;
+    for (int b = 0; b < B; b++) {
+      const int len = poss[b] + 1, n0 = (len + T - 1) / T;
+      const int c = r16((len + n0 - 1) / n0);
+      n += (len + c - 1) / c;
+      if (write) {
+        ct[b] = c;
+        cend[b] = n;
+      }
+    }
+    return n;
+  };
+  int T = std::max(64, std::max(r16((tot * Hkv + slots - 1) / slots), r16((maxlen + nch - 1) / nch)));
+  T = std::min(T, 2048);
+  while (T < 2048 && (int64_t)chunks(T, false) * Hkv > slots) T += 16;
+  return chunks(T, true);
+}
+
+// The descriptor's attention chunks: planned (8 resident waves per compute unit, two per
+// SIMD) for the one-wave-per-chunk kernel, else every context split at d.ct.
 static void plan_attention_chunks(dtd_engine* e, StepDesc* hd, int B, const int* poss, bool wplan) {
   const Dims& d = e->d;
   e->step_chunks = 0;
@@ -782,32 +812,7 @@ static void plan_attention_chunks(dtd_engine* e, StepDesc* hd, int B, const int*
     for (int b = 0; b < B; b++) hd->ct[b] = d.ct;
     return;
   }
-  auto r16 = [](int64_t x) { return (int)((x + 15) / 16 * 16); };
-  const int64_t slots = (int64_t)e->cus * 8;
-  int64_t tot = 0;
-  int maxlen = 1;
-  for (int b = 0; b < B; b++) {
-    tot += poss[b] + 1;
-    maxlen = std::max(maxlen, poss[b] + 1);
-  }
-  // chunks of the batch at bound T (written to the descriptor when write)
-  auto chunks = [&](int T, bool write) {
-    int n = 0;
-    for (int b = 0; b < B; b++) {
-      const int len = poss[b] + 1, n0 = (len + T - 1) / T;
-      const int ct = r16((len + n0 - 1) / n0);
-      n += (len + ct - 1) / ct;
-      if (write) {
-        hd->ct[b] = ct;
-        hd->cend[b] = n;
-      }
-    }
-    return n;
-  };
-  int T = std::max(64, std::max(r16((tot * d.Hkv + slots - 1) / slots), r16((maxlen + d.nch - 1) / d.nch)));
-  T = std::min(T, 2048);
-  while (T < 2048 && (int64_t)chunks(T, false) * d.Hkv > slots) T += 16;
-  hd->n_chunks = chunks(T, true);
+  hd->n_chunks = plan_chunks(B, poss, d.Hkv, d.nch, (int64_t)e->cus * 8, hd->ct, hd->cend);
   e->step_chunks = hd->n_chunks;
 }
 
@@ -2031,6 +2036,16 @@ extern "C" dtd_status dtd_debug_set_path(dtd_engine* e, int32_t path) {
 extern "C" int32_t dtd_debug_uses_persistent(const dtd_engine* e, int32_t batch) {
   if (!e) return DTD_E_ARG;
   return e->persist_ok && batch == 1 && !e->capture && e->path != 1 ? 1 : 0;
+}
+
+extern "C" int32_t dtd_debug_plan_attention_chunks(int32_t batch, const int32_t* pos, int32_t n_kv_heads, int32_t max_chunks,
+                                        int32_t slots, int32_t* ct, int32_t* cend) {
+  if (batch < 1 || batch > kMaxBatch || !pos || !ct || !cend || n_kv_heads < 1 || max_chunks < 1 || slots < 1)
+    return DTD_E_ARG;
+  for (int b = 0; b < batch; b++)
+    if (pos[b] < 0 || (int64_t)pos[b] + 1 > (int64_t)max_chunks * 2048) return DTD_E_ARG;
+  std::vector<int> p(pos, pos + batch);
+  return plan_chunks(batch, p.data(), n_kv_heads, max_chunks, slots, ct, cend);
 }
 
 extern "C" int32_t dtd_debug_step_kernel_shape(const dtd_engine* e) {

@@ -107,6 +107,8 @@ _SIGS = {
     "dtd_debug_set_path": ([_P, _I32], _I32),
     "dtd_debug_uses_persistent": ([_P, _I32], _I32),
     "dtd_debug_step_kernel_shape": ([_P], _I32),
+    "dtd_debug_plan_attention_chunks": ([_I32, C.POINTER(_I32), _I32, _I32, _I32, C.POINTER(_I32), C.POINTER(_I32)],
+                                        _I32),
     "dtd_debug_stream_read": ([_P, _I64, _I32, _P, C.POINTER(C.c_double)], _I32),
 }
 
@@ -507,3 +509,18 @@ class Scheduler:
             self.close()
         except Exception:
             pass
+
+
+def plan_attention_chunks(pos, n_kv_heads: int, max_chunks: int, slots: int):
+    """the batched decode attention's per-sequence chunk lengths and running chunk counts
+    for contexts pos[b] + 1 (host only); returns (ct, cend)"""
+    import numpy as np
+    p = np.ascontiguousarray(pos, dtype=np.int32)
+    ct = np.zeros(len(p), np.int32)
+    cend = np.zeros(len(p), np.int32)
+    ip = C.POINTER(_I32)
+    n = load().dtd_debug_plan_attention_chunks(len(p), p.ctypes.data_as(ip), n_kv_heads, max_chunks, slots,
+                                               ct.ctypes.data_as(ip), cend.ctypes.data_as(ip))
+    if n < 0:
+        raise DtdError(n, "dtd_debug_plan_attention_chunks")
+    return ct, cend

@@ -452,6 +452,17 @@ int32_t dtd_debug_uses_persistent(const dtd_engine* e, int32_t batch);
  * dtd_status < 0 for a null engine. */
 int32_t dtd_debug_step_kernel_shape(const dtd_engine* e);
 
+/* The batched decode attention's split-K plan (host only, no device call), as the engine
+ * makes it each step for the one-wave-per-chunk kernel: batch contexts pos[b] + 1 (1 <=
+ * batch <= 64), n_kv_heads waves per chunk, at most max_chunks chunks per sequence and
+ * `slots` resident waves.  Sequence b is cut into chunks of ct[b] positions (a multiple of
+ * 16, at most 2048); cend[b] is the number of chunks of sequences 0..b.  Returns the batch's
+ * chunk count, or DTD_E_ARG for out-of-range arguments (a context above max_chunks x 2048
+ * included).  Split-K of attention over the context is the Qwen3-8B engine article's
+ * decode attention (4.4.2); the chunk sizing is this library's. */
+int32_t dtd_debug_plan_attention_chunks(int32_t batch, const int32_t* pos, int32_t n_kv_heads, int32_t max_chunks,
+                                        int32_t slots, int32_t* ct, int32_t* cend);
+
 #ifdef __cplusplus
 }
 #endif

@@ -131,3 +131,42 @@ def test_prefix_cache_and_scheduler_calls_check_their_arguments():
     assert lib.dtd_sched_wait(None, 0, 0) == dtd.DTD_E_ARG
     assert lib.dtd_sched_last_error(None) == b"null scheduler"
     lib.dtd_sched_destroy(None)
+
+
+def test_attention_chunk_plan_worked_example():
+    # contexts 600, 1000 and 4096, 8 KV heads, 8 chunks at most, 64 resident waves: the
+    # shortest bound T (multiples of 16 from max(64, 5696 * 8 / 64 = 712 -> 720, 4096 / 8 =
+    # 512)) whose chunks fit 64 waves is 832: 4096 -> 5 chunks of 832 (T = 720 .. 816 still
+    # needs 6), 1000 -> 2 of 512, 600 -> 1 of 608; 8 chunks x 8 heads = 64 waves
+    ct, cend = dtd.plan_attention_chunks([599, 999, 4095], 8, 8, 64)
+    assert list(ct) == [608, 512, 832] and list(cend) == [1, 3, 8]
+    # equal contexts 16384 at batch 32, 2048 slots: chunks of 2048, 8 per sequence, one wave
+    # per slot
+    ct, cend = dtd.plan_attention_chunks([16383] * 32, 8, 16, 2048)
+    assert set(ct) == {2048} and cend[-1] * 8 == 2048
+    # a short context alone: at least 64 positions per chunk
+    ct, cend = dtd.plan_attention_chunks([99], 8, 64, 2048)
+    assert list(ct) == [64] and list(cend) == [2]
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_attention_chunk_plan_invariants(seed):
+    rng = np.random.default_rng(seed)
+    B = int(rng.integers(1, 65))
+    max_ctx = int(rng.choice([256, 4096, 16384, 32768]))
+    hkv = int(rng.choice([1, 2, 8]))
+    nch = -(-max_ctx // int(rng.choice([64, 512, 1024, 2048])))
+    slots = int(rng.choice([64, 1024, 2048]))
+    pos = rng.integers(0, max_ctx, B).astype(np.int32)
+    ct, cend = dtd.plan_attention_chunks(pos, hkv, nch, slots)
+    ln = pos.astype(np.int64) + 1
+    n = -(-ln // ct)
+    assert np.all(ct % 16 == 0) and np.all(ct >= 16) and np.all(ct <= 2048)
+    assert np.all(n <= nch) and np.array_equal(np.cumsum(n), cend)
+    # the chunks of a sequence are equal but for the last, which is never empty
+    assert np.all((n - 1) * ct < ln) and np.all(ln <= n * ct)
+    # they fit the slots whenever chunks of 2048 would
+    if int(np.sum(-(-ln // 2048))) * hkv <= slots:
+        assert int(cend[-1]) * hkv <= slots
+    with pytest.raises(dtd.DtdError):
+        dtd.plan_attention_chunks(np.array([max_ctx], np.int32) * 0 + nch * 2048, hkv, nch, slots)
