@@ -952,6 +952,11 @@ static dtd_status run_sub_steps(dtd_engine* e, int B, bool do_head, const uint8_
   ea.x = e->x; ea.h = e->h; ea.logits = e->logits;
   const size_t fx = (size_t)B * d.D * 4, fxn = (size_t)B * d.D * ab, fq = (size_t)B * d.q_dim * 4;
   const size_t fkv = (size_t)B * d.kv_dim * 4, fo = (size_t)B * d.q_dim * ab, fh = (size_t)B * d.F * ab;
+  // On the matrix-core path (no probe records), a residual projection's split-K sums, the
+  // residual add and the RMSNorm after it run as one launch: xn_ready says the norm of the
+  // next block's input is already in xn.
+  const bool fuse_norm = mfma && !probe;
+  bool xn_ready = false;
   for (int l = 0; l < d.L; l++) {
     const LayerW& W = e->layers[(size_t)l];
     KvLayer kv;
@@ -965,7 +970,8 @@ static dtd_status run_sub_steps(dtd_engine* e, int B, bool do_head, const uint8_
       HIP_OK(e, cp(e->x, in + pl.x_in, fx));
       HIP_OK(e, cp(out + pl.x_in, in + pl.x_in, fx));
     }
-    HIP_OK(e, launch_rmsnorm(d, e->x, W.attn_norm, e->xn, B, st));
+    if (!xn_ready) HIP_OK(e, launch_rmsnorm(d, e->x, W.attn_norm, e->xn, B, st));
+    xn_ready = false;
     if (probe) {
       HIP_OK(e, cp(out + pl.xn, e->xn, fxn));
       HIP_OK(e, cp(e->xn, in + pl.xn, fxn));
@@ -997,12 +1003,16 @@ static dtd_status run_sub_steps(dtd_engine* e, int B, bool do_head, const uint8_
       HIP_OK(e, cp(e->o, in + pl.o, fo));
       HIP_OK(e, cp(e->x, in + pl.x_in, fx));
     }
-    TIMED(3, proj(W.o, e->o, EPI_RESID, ea));
-    if (probe) {
-      HIP_OK(e, cp(out + pl.x_mid, e->x, fx));
-      HIP_OK(e, cp(e->x, in + pl.x_mid, fx));
+    if (fuse_norm) {
+      TIMED(3, launch_gemm_resid_norm(d, W.o, e->o, B, ea, gemm_partials, e->cus, W.ffn_norm, e->xn, st));
+    } else {
+      TIMED(3, proj(W.o, e->o, EPI_RESID, ea));
+      if (probe) {
+        HIP_OK(e, cp(out + pl.x_mid, e->x, fx));
+        HIP_OK(e, cp(e->x, in + pl.x_mid, fx));
+      }
+      HIP_OK(e, launch_rmsnorm(d, e->x, W.ffn_norm, e->xn, B, st));
     }
-    HIP_OK(e, launch_rmsnorm(d, e->x, W.ffn_norm, e->xn, B, st));
     if (probe) {
       HIP_OK(e, cp(out + pl.xn2, e->xn, fxn));
       HIP_OK(e, cp(e->xn, in + pl.xn2, fxn));
@@ -1012,7 +1022,14 @@ static dtd_status run_sub_steps(dtd_engine* e, int B, bool do_head, const uint8_
       HIP_OK(e, cp(out + pl.h, e->h, fh));
       HIP_OK(e, cp(e->h, in + pl.h, fh));
     }
-    TIMED(1, proj(W.down, e->h, EPI_RESID, ea));
+    // the next norm: the next layer's attention norm, or the final norm before the head
+    const float* next_g = l + 1 < d.L ? e->layers[(size_t)l + 1].attn_norm : (do_head ? e->final_norm : nullptr);
+    if (fuse_norm && next_g) {
+      TIMED(1, launch_gemm_resid_norm(d, W.down, e->h, B, ea, gemm_partials, e->cus, next_g, e->xn, st));
+      xn_ready = true;
+    } else {
+      TIMED(1, proj(W.down, e->h, EPI_RESID, ea));
+    }
     if (probe) HIP_OK(e, cp(out + pl.x_out, e->x, fx));
     if (e->capture)
       HIP_OK(e, hipMemcpyAsync(e->capture + (size_t)(l + 1) * B * d.D, e->x, (size_t)B * d.D * 4,
@@ -1020,7 +1037,7 @@ static dtd_status run_sub_steps(dtd_engine* e, int B, bool do_head, const uint8_
   }
   if (probe) HIP_OK(e, cp(e->x, inject + (size_t)(d.L - 1) * pl.record + pl.x_out, fx));
   if (do_head) {
-    HIP_OK(e, launch_rmsnorm(d, e->x, e->final_norm, e->xn, B, st));
+    if (!xn_ready) HIP_OK(e, launch_rmsnorm(d, e->x, e->final_norm, e->xn, B, st));
     TIMED(5, proj(e->head, e->xn, EPI_LOGITS, ea));
     HIP_OK(e, launch_argmax(d, e->desc_dev, B, e->logits, st));
   }

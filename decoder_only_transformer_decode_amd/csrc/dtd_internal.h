@@ -196,6 +196,11 @@ hipError_t launch_gemv(const Dims& d, const MatDev& m, const void* xin, int B, i
 bool gemm_eligible(const Dims& d, int B);
 int gemm_splits(int N, int K, int cus);                 // K splits of an N x K matrix
 size_t gemm_partial_bytes(const Dims& d, int B, int cus);   // work buffer of the split-K sums
+// a residual projection (O or down) on the matrix cores, its residual add into ea.x and the
+// RMSNorm of the result with gain g into xn (one launch for the split-K sums, the add and
+// the norm when K is split)
+hipError_t launch_gemm_resid_norm(const Dims& d, const MatDev& m, const void* xin, int B, const EpiArgs& ea,
+                                  float* partials, int cus, const float* g, void* xn, hipStream_t st);
 hipError_t launch_gemm(const Dims& d, const MatDev& m, const void* xin, int B, int epi, const EpiArgs& ea,
                        float* partials, int cus, hipStream_t st);
 // whether the decode attention of these dimensions runs one wave per chunk (k_attn_w), which

@@ -574,6 +574,58 @@ __global__ __launch_bounds__(256) void k_gemm_reduce(GemmArgs a) {
   gemv_epilogue<EPI, 4>(a.g, b, r0, v);
 }
 
+// The split-K sums of a residual projection (O or down: N = D rows), the residual add, and
+// the RMSNorm that follows it (of the next block), in one launch: one workgroup per
+// sequence.  Thread t takes rows 4 (t + 256 k), the rows k_gemm_reduce and k_rmsnorm's
+// vector path give it, and adds in their order, so x and xn are the bits those two
+// kernels produce.  D a multiple of 4, at most 8192.
+template <int WFMT>
+__global__ __launch_bounds__(256) void k_gemm_reduce_norm(GemmArgs a, const float* g, void* xn) {
+  __shared__ float red[4];
+  constexpr int NP = 8;
+  const int D = a.g.m.rows, B = a.g.B, b = blockIdx.x;
+  float* xb = a.g.ea.x + (size_t)b * D;
+  float4 v[NP];
+  float ss = 0.f;
+#pragma unroll
+  for (int k = 0; k < NP; k++) {
+    const int i = 4 * ((int)threadIdx.x + 256 * k);
+    v[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (i >= D) continue;
+    float s[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int sp = 0; sp < a.S; sp++) {
+      const float4 p = *(const float4*)(a.partials + ((size_t)sp * B + b) * D + i);
+      s[0] += p.x; s[1] += p.y; s[2] += p.z; s[3] += p.w;
+    }
+    if constexpr (WFMT == W_INT8_ROW) {
+      const float4 sc = *(const float4*)((const float*)a.g.m.s + i);
+      s[0] *= sc.x; s[1] *= sc.y; s[2] *= sc.z; s[3] *= sc.w;
+    }
+    float4 x = *(const float4*)(xb + i);
+    x.x += s[0]; x.y += s[1]; x.z += s[2]; x.w += s[3];
+    *(float4*)(xb + i) = x;
+    v[k] = x;
+    ss += x.x * x.x + x.y * x.y + x.z * x.z + x.w * x.w;
+  }
+  ss = block_sum(ss, red);
+  const float r = 1.0f / sqrtf(ss / (float)D + a.g.d.eps);
+  const int act = a.g.d.act;
+#pragma unroll
+  for (int k = 0; k < NP; k++) {
+    const int i = 4 * ((int)threadIdx.x + 256 * k);
+    if (i >= D) continue;
+    const float4 gg = *(const float4*)(g + i);
+    const float y0 = v[k].x * r * gg.x, y1 = v[k].y * r * gg.y, y2 = v[k].z * r * gg.z, y3 = v[k].w * r * gg.w;
+    if (act == ACT_BF16) {
+      const uint32_t lo = f32_to_bf16(y0) | ((uint32_t)f32_to_bf16(y1) << 16);
+      const uint32_t hi = f32_to_bf16(y2) | ((uint32_t)f32_to_bf16(y3) << 16);
+      *(uint2*)((uint16_t*)xn + (size_t)b * D + i) = make_uint2(lo, hi);
+    } else {
+      *(float4*)((float*)xn + (size_t)b * D + i) = make_float4(y0, y1, y2, y3);
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------------------
 // S4 + S5 split-K GQA decode attention (work item in dtd_device.h) and the chunk merge
 // ---------------------------------------------------------------------------------------
@@ -1631,7 +1683,7 @@ hipError_t gemm_lds_limit(size_t smem) {
 }
 
 template <int WFMT, int EPI>
-hipError_t gemm_dispatch(const GemmArgs& a, int nbb, dim3 grid, size_t smem, hipStream_t st) {
+hipError_t gemm_dispatch(const GemmArgs& a, int nbb, dim3 grid, size_t smem, hipStream_t st, bool reduce = true) {
   hipError_t r = hipSuccess;
   switch (nbb) {
     case 1: hipLaunchKernelGGL((k_gemm<WFMT, EPI, 1>), grid, dim3(256), smem, st, a); break;
@@ -1643,7 +1695,7 @@ hipError_t gemm_dispatch(const GemmArgs& a, int nbb, dim3 grid, size_t smem, hip
       break;
   }
   r = hipGetLastError();
-  if (r != hipSuccess || a.S == 1) return r;
+  if (r != hipSuccess || a.S == 1 || !reduce) return r;
   const int threads = (a.g.m.rows + 3) / 4 * a.g.B;
   hipLaunchKernelGGL((k_gemm_reduce<WFMT, EPI>), dim3((threads + 255) / 256), dim3(256), 0, st, a);
   return hipGetLastError();
@@ -1703,6 +1755,39 @@ hipError_t launch_gemm(const Dims& d, const MatDev& m, const void* xin, int B, i
   const size_t smem = 2 * (size_t)16 * nbb * kGemmLd;
   if (d.wfmt == W_INT8_ROW) return gemm_epi<W_INT8_ROW>(a, epi, nbb, grid, smem, st);
   return gemm_epi<W_BF16>(a, epi, nbb, grid, smem, st);
+}
+
+hipError_t launch_gemm_resid_norm(const Dims& d, const MatDev& m, const void* xin, int B, const EpiArgs& ea,
+                                  float* partials, int cus, const float* g, void* xn, hipStream_t st) {
+  const int S = gemm_splits(m.rows, m.cols, cus);
+  if (S == 1 || m.rows != d.D || d.D % 4 || d.D > 8 * 4 * 256) {
+    const hipError_t r = launch_gemm(d, m, xin, B, EPI_RESID, ea, partials, cus, st);
+    return r != hipSuccess ? r : launch_rmsnorm(d, ea.x, g, xn, B, st);
+  }
+  GemmArgs a;
+  a.g.d = d;
+  a.g.m = m;
+  a.g.xin = xin;
+  a.g.B = B;
+  a.g.act_in = d.act;
+  a.g.kc = 0;
+  a.g.ea = ea;
+  a.partials = partials;
+  a.S = S;
+  a.nchunk = (m.cols + kGemmKC - 1) / kGemmKC;
+  const int nbb = (B + 15) / 16;
+  const dim3 grid((m.rows + kGemmRows - 1) / kGemmRows, a.S);
+  const size_t smem = 2 * (size_t)16 * nbb * kGemmLd;
+  // the GEMM with its split-K partial sums only (the reduce below runs the epilogue)
+  hipError_t r;
+  if (d.wfmt == W_INT8_ROW) {
+    r = gemm_dispatch<W_INT8_ROW, EPI_RESID>(a, nbb, grid, smem, st, false);
+    if (r == hipSuccess) hipLaunchKernelGGL(k_gemm_reduce_norm<W_INT8_ROW>, dim3(B), dim3(256), 0, st, a, g, xn);
+  } else {
+    r = gemm_dispatch<W_BF16, EPI_RESID>(a, nbb, grid, smem, st, false);
+    if (r == hipSuccess) hipLaunchKernelGGL(k_gemm_reduce_norm<W_BF16>, dim3(B), dim3(256), 0, st, a, g, xn);
+  }
+  return r != hipSuccess ? r : hipGetLastError();
 }
 
 hipError_t launch_embed(const Dims& d, const MatDev& emb, const StepDesc* desc, int B,
