@@ -448,8 +448,9 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
   };
   auto x_piece = [&](int c, int v, int& r, int& k) {
     const int idx = tid + 256 * v;
-    r = idx >> 5;                                   // kGemmKC / 8 = 32 pieces per row
-    k = c * kGemmKC + (idx & 31) * 8;
+    constexpr int PPR = kGemmKC / 8;                // 16-byte pieces per row
+    r = idx / PPR;
+    k = c * kGemmKC + (idx % PPR) * 8;
   };
   auto issue_x = [&](int c, uint4 (&x)[XV]) {
 #pragma unroll
