@@ -1278,10 +1278,31 @@ __global__ __launch_bounds__(1024) void k_argmax(const float* logits, int V, con
   const float* L = logits + (size_t)b * V;
   float best = -INFINITY;
   int idx = INT_MAX;
-  for (int v = threadIdx.x; v < V; v += 1024) {
-    const float x = L[v];
+  auto take = [&](float x, int v) {
     if (x > best || (idx == INT_MAX && !isnan(x))) { best = x; idx = v; }
+  };
+  // a thread's entries in ascending order: 16-byte pieces t, t + 1024, ... (four loads in
+  // flight), then the tail past the last whole piece
+  const int nq = (V & 3) == 0 ? V >> 2 : 0;
+  for (int q0 = threadIdx.x; q0 < nq; q0 += 4 * 1024) {
+    float4 x[4];
+#pragma unroll
+    for (int u = 0; u < 4; u++) {
+      const int q = q0 + u * 1024;
+      x[u] = q < nq ? *(const float4*)(L + 4 * (size_t)q) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; u++) {
+      const int q = q0 + u * 1024;
+      if (q < nq) {
+        take(x[u].x, 4 * q);
+        take(x[u].y, 4 * q + 1);
+        take(x[u].z, 4 * q + 2);
+        take(x[u].w, 4 * q + 3);
+      }
+    }
   }
+  for (int v = 4 * nq + (int)threadIdx.x; v < V; v += 1024) take(L[v], v);
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) {
     const float ob = __shfl_xor(best, m, 64);
