@@ -578,8 +578,8 @@ __global__ __launch_bounds__(256) void k_gemm_reduce(GemmArgs a) {
 // The split-K sums of a residual projection (O or down: N = D rows), the residual add, and
 // the RMSNorm that follows it (of the next block), in one launch: one workgroup per
 // sequence.  Thread t takes rows 4 (t + 256 k), the rows k_gemm_reduce and k_rmsnorm's
-// vector path give it, and adds in their order, so x and xn are the bits those two
-// kernels produce.  D a multiple of 4, at most 8192.
+// vector path give it, and runs their operations in their order.  D a multiple of 4, at
+// most 8192.
 template <int WFMT>
 __global__ __launch_bounds__(256) void k_gemm_reduce_norm(GemmArgs a, const float* g, void* xn) {
   __shared__ float red[4];
