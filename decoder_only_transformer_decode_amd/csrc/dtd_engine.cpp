@@ -902,15 +902,18 @@ static dtd_status run_step(dtd_engine* e, int B, const int* slots, const int* po
     e->epoch += ntag;
     // a KV budget's score sums over the scored layers, from the queries and softmax
     // statistics the step kernel kept (the new entry is in the cache by now)
+    // (one launch for all of them)
     const size_t kvb = kv_elem_bytes(e->cfg.kvfmt);
-    for (int l = std::max(e->step_score_min, 0); l < d.L; l++) {
+    const int l0 = std::max(e->step_score_min, 0);
+    if (l0 < d.L) {
       KvLayer kv;
-      kv.k = (uint8_t*)e->kpool + (size_t)l * e->kv_layer_elems * kvb;
-      kv.v = (uint8_t*)e->vpool + (size_t)l * e->kv_layer_elems * kvb;
-      kv.ks = e->kspool ? e->kspool + (size_t)l * e->kv_layer_scales : nullptr;
-      kv.vs = e->vspool ? e->vspool + (size_t)l * e->kv_layer_scales : nullptr;
-      HIP_OK(e, launch_score(d, e->desc_dev, 1, e->step_max_pos, l, e->p_score_q + (size_t)l * d.q_dim, kv,
-                             e->bt_dev, e->p_score_stat + (size_t)l * d.Hq * 2, e->scores_dev, st));
+      kv.k = (uint8_t*)e->kpool + (size_t)l0 * e->kv_layer_elems * kvb;
+      kv.v = (uint8_t*)e->vpool + (size_t)l0 * e->kv_layer_elems * kvb;
+      kv.ks = e->kspool ? e->kspool + (size_t)l0 * e->kv_layer_scales : nullptr;
+      kv.vs = e->vspool ? e->vspool + (size_t)l0 * e->kv_layer_scales : nullptr;
+      HIP_OK(e, launch_score(d, e->desc_dev, 1, e->step_max_pos, l0, d.L - l0, e->p_score_q + (size_t)l0 * d.q_dim,
+                             d.q_dim, kv, e->kv_layer_elems * kvb, e->kv_layer_scales * 2, e->bt_dev,
+                             e->p_score_stat + (size_t)l0 * d.Hq * 2, (size_t)d.Hq * 2, e->scores_dev, st));
     }
     return DTD_OK;
   }
@@ -997,7 +1000,8 @@ static dtd_status run_sub_steps(dtd_engine* e, int B, bool do_head, const uint8_
     }
     HIP_OK(e, launch_combine(d, e->desc_dev, B, partials, e->o, st, scored ? e->attn_stat : nullptr));
     if (scored)
-      HIP_OK(e, launch_score(d, e->desc_dev, B, e->step_max_pos, l, e->q, kv, e->bt_dev, e->attn_stat, e->scores_dev, st));
+      HIP_OK(e, launch_score(d, e->desc_dev, B, e->step_max_pos, l, 1, e->q, 0, kv, 0, 0, e->bt_dev, e->attn_stat, 0,
+                             e->scores_dev, st));
     if (probe) {
       HIP_OK(e, cp(out + pl.o, e->o, fo));
       HIP_OK(e, cp(e->o, in + pl.o, fo));

@@ -220,8 +220,11 @@ hipError_t launch_combine(const Dims& d, const StepDesc* desc, int B, const floa
 // partials [n][Hq][nch][hd+2] for launch_combine
 hipError_t launch_attn_prefill(const Dims& d, const StepDesc* desc, int n, int last_pos, const float* q,
                                const KvLayer& kv, const int32_t* bt, float* partials, hipStream_t st);
-hipError_t launch_score(const Dims& d, const StepDesc* desc, int B, int max_pos, int layer, const float* q,
-                        const KvLayer& kv, const int32_t* bt, const float* stat, float* scores, hipStream_t st);
+// KV budget score sums of layers layer0 .. layer0 + nl - 1 (their queries, K pools and
+// statistics q_ls floats, k_ls / s_ls bytes and st_ls floats apart), added in layer order
+hipError_t launch_score(const Dims& d, const StepDesc* desc, int B, int max_pos, int layer0, int nl, const float* q,
+                        size_t q_ls, const KvLayer& kv, size_t k_ls, size_t s_ls, const int32_t* bt, const float* stat,
+                        size_t st_ls, float* scores, hipStream_t st);
 // KV budget, one eviction on the device (n = budget + 1 entries): picks the entry, closes
 // the gap in the score and position rows, writes the n - 1 kept indices to keep
 hipError_t launch_evict_one(float* scores, int32_t* kvpos, int n, int n_init, int rec0, int new_pos, int32_t* keep,

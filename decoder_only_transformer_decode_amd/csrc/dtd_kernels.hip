@@ -1144,50 +1144,69 @@ __global__ __launch_bounds__(256) void k_combine(Dims d, const StepDesc* desc, c
 // queries are staged in LDS.  For each query head h in order it recomputes q_h . k_t / sqrt(d)
 // from the stored key (a wave sum: every lane holds the same total) and adds
 // exp(s - M_h) / L_h with the merged attention statistics, so every entry's sum has one fixed
-// order.
+// order.  Layers layer0 .. layer0 + nl - 1 in one launch (those from the row's score_from on):
+// layer l's queries, keys, scales and statistics sit l strides past layer0's, and each
+// layer's sum is added to the entry in layer order by the wave that owns the entry.
+struct ScoreLayers {
+  int layer0, nl;
+  const float* q;      // layer0's [B][q_dim]
+  size_t q_ls;         // floats between layers
+  KvLayer kv;          // layer0's pools
+  size_t k_ls, s_ls;   // bytes of K, fp16 scales between layers
+  const float* stat;   // layer0's [B][Hq][2]
+  size_t st_ls;        // floats between layers
+};
 template <int KVFMT>
-__global__ __launch_bounds__(256) void k_score(Dims d, const StepDesc* desc, int layer, const float* q,
-                                               KvLayer kv, const int32_t* bt, const float* stat, float* scores) {
-  extern __shared__ float qb[];        // [q_dim] this row's queries
+__global__ __launch_bounds__(256) void k_score(Dims d, const StepDesc* desc, ScoreLayers a, const int32_t* bt,
+                                               float* scores) {
+  extern __shared__ float qb[];        // [q_dim] this row's queries of one layer
   const int b = blockIdx.x;
-  if (layer < desc->score_from[b]) return;   // block-uniform
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (int i = threadIdx.x; i < d.q_dim; i += 256) qb[i] = q[(size_t)b * d.q_dim + i];
-  __syncthreads();
   const int t = blockIdx.y * 4 + wave;
   const int pos = desc->pos[b], slot = desc->slot[b];
-  if (t > pos) return;   // wave-uniform; no barrier below
+  const bool mine = t <= pos;          // (wave-uniform; waves past the row still take the barriers)
   const float scale = 1.f / sqrtf((float)d.hd);
-  const int blk = bt[(size_t)slot * d.max_blocks + t / d.bs];
-  float sum = 0.f;
-  for (int j = 0; j < d.Hkv; j++) {
-    const size_t row = ((size_t)blk * d.Hkv + j) * d.bs + (t % d.bs);
-    float kx[2];   // elements lane and lane + 64 of the key (head size <= 128)
-#pragma unroll
-    for (int u = 0; u < 2; u++) {
-      const int i = lane + 64 * u;
-      float v = 0.f;
-      if (i < d.hd) {
-        if constexpr (KVFMT == KV_F32) v = ((const float*)kv.k)[row * d.hd + i];
-        else if constexpr (KVFMT == KV_BF16) v = bf16_to_f32(((const uint16_t*)kv.k)[row * d.hd + i]);
-        else v = (float)((const int8_t*)kv.k)[row * d.hd + i] * f16_to_f32(kv.ks[row]);
-      }
-      kx[u] = v;
-    }
-    for (int g = 0; g < d.G; g++) {
-      const int h = j * d.G + g;
-      float p = 0.f;
+  const int blk = mine ? bt[(size_t)slot * d.max_blocks + t / d.bs] : 0;
+  for (int l = 0; l < a.nl; l++) {
+    if (a.layer0 + l < desc->score_from[b]) continue;   // block-uniform
+    __syncthreads();                                     // the previous layer's readers are done
+    const float* q = a.q + (size_t)l * a.q_ls;
+    for (int i = threadIdx.x; i < d.q_dim; i += 256) qb[i] = q[(size_t)b * d.q_dim + i];
+    __syncthreads();
+    if (!mine) continue;
+    const uint8_t* kl = (const uint8_t*)a.kv.k + (size_t)l * a.k_ls;
+    const uint16_t* ksl = KVFMT == KV_I8 ? (const uint16_t*)((const uint8_t*)a.kv.ks + (size_t)l * a.s_ls) : nullptr;
+    const float* stat = a.stat + (size_t)l * a.st_ls;
+    float sum = 0.f;
+    for (int j = 0; j < d.Hkv; j++) {
+      const size_t row = ((size_t)blk * d.Hkv + j) * d.bs + (t % d.bs);
+      float kx[2];   // elements lane and lane + 64 of the key (head size <= 128)
 #pragma unroll
       for (int u = 0; u < 2; u++) {
         const int i = lane + 64 * u;
-        if (i < d.hd) p += qb[(size_t)h * d.hd + i] * kx[u];
+        float v = 0.f;
+        if (i < d.hd) {
+          if constexpr (KVFMT == KV_F32) v = ((const float*)kl)[row * d.hd + i];
+          else if constexpr (KVFMT == KV_BF16) v = bf16_to_f32(((const uint16_t*)kl)[row * d.hd + i]);
+          else v = (float)((const int8_t*)kl)[row * d.hd + i] * f16_to_f32(ksl[row]);
+        }
+        kx[u] = v;
       }
-      const float dot = wave_sum(p);
-      const float M = stat[((size_t)b * d.Hq + h) * 2], L = stat[((size_t)b * d.Hq + h) * 2 + 1];
-      sum += expf(dot * scale - M) / L;
+      for (int g = 0; g < d.G; g++) {
+        const int h = j * d.G + g;
+        float p = 0.f;
+#pragma unroll
+        for (int u = 0; u < 2; u++) {
+          const int i = lane + 64 * u;
+          if (i < d.hd) p += qb[(size_t)h * d.hd + i] * kx[u];
+        }
+        const float dot = wave_sum(p);
+        const float M = stat[((size_t)b * d.Hq + h) * 2], L = stat[((size_t)b * d.Hq + h) * 2 + 1];
+        sum += expf(dot * scale - M) / L;
+      }
     }
+    if (lane == 0) scores[(size_t)slot * d.max_ctx + t] += sum;
   }
-  if (lane == 0) scores[(size_t)slot * d.max_ctx + t] += sum;
 }
 
 // KV budget eviction in the steady state of decoding (the Initial-Key cache of the C17 engine
@@ -1937,13 +1956,16 @@ hipError_t launch_attn_prefill(const Dims& d, const StepDesc* desc, int n, int l
   return hipGetLastError();
 }
 
-hipError_t launch_score(const Dims& d, const StepDesc* desc, int B, int max_pos, int layer, const float* q,
-                        const KvLayer& kv, const int32_t* bt, const float* stat, float* scores, hipStream_t st) {
+hipError_t launch_score(const Dims& d, const StepDesc* desc, int B, int max_pos, int layer0, int nl, const float* q,
+                        size_t q_ls, const KvLayer& kv, size_t k_ls, size_t s_ls, const int32_t* bt, const float* stat,
+                        size_t st_ls, float* scores, hipStream_t st) {
+  if (nl <= 0) return hipSuccess;
+  ScoreLayers a{layer0, nl, q, q_ls, kv, k_ls, s_ls, stat, st_ls};
   const dim3 grid(B, (max_pos + 1 + 3) / 4);
   const size_t smem = (size_t)d.q_dim * 4;
-  if (d.kvfmt == KV_F32) hipLaunchKernelGGL(k_score<KV_F32>, grid, dim3(256), smem, st, d, desc, layer, q, kv, bt, stat, scores);
-  else if (d.kvfmt == KV_BF16) hipLaunchKernelGGL(k_score<KV_BF16>, grid, dim3(256), smem, st, d, desc, layer, q, kv, bt, stat, scores);
-  else hipLaunchKernelGGL(k_score<KV_I8>, grid, dim3(256), smem, st, d, desc, layer, q, kv, bt, stat, scores);
+  if (d.kvfmt == KV_F32) hipLaunchKernelGGL(k_score<KV_F32>, grid, dim3(256), smem, st, d, desc, a, bt, scores);
+  else if (d.kvfmt == KV_BF16) hipLaunchKernelGGL(k_score<KV_BF16>, grid, dim3(256), smem, st, d, desc, a, bt, scores);
+  else hipLaunchKernelGGL(k_score<KV_I8>, grid, dim3(256), smem, st, d, desc, a, bt, scores);
   return hipGetLastError();
 }
 

@@ -135,6 +135,16 @@ def test_budget_evicts_like_the_oracle(kw, path):
     assert n >= 20
 
 
+@pytest.mark.parametrize("kw", [dict(), dict(act=synth.ACT_BF16, kvfmt=synth.KV_I8)], ids=["f32", "bf16-int8kv"])
+def test_budget_scores_every_scored_layer_in_one_launch(kw):
+    # batch 1 on the step kernel with both layers scored: the score sums of the two layers
+    # come from one launch, layer by layer
+    s = _GRID.replace(**kw)
+    n = _run_budgeted(s, (24, 3, 6, 2), prompt_len=30, steps=30, seed=11, path=dtd.PATH_PERSISTENT)
+    _say(f"{kw}, 2 scored layers: {n} steps with the same kept entries, scores and outputs as the oracle")
+    assert n >= 15
+
+
 def test_budgeted_and_plain_sequences_share_a_batch():
     n = _run_budgeted(_GRID, (32, 4, 8, 2), prompt_len=20, steps=40, seed=9, batch_with_plain=True)
     _say(f"batch of a budgeted and a plain sequence: {n} steps compared")
