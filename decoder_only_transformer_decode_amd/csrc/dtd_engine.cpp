@@ -1264,15 +1264,15 @@ static dtd_status kv_evict(dtd_engine* e, Seq& s, const KvBudget& kb, int new_po
     std::vector<int32_t> fresh;
     for (int i = 0; i < nb; i++) fresh.push_back(take_block(e));
     std::copy(fresh.begin(), fresh.end(), hs + e->d.max_blocks);
+    // one copy of both lists (old blocks at 0, new ones at max_blocks, the kept entries after
+    // them); the eviction kernel also writes the new blocks into the block table
     hipStream_t st = e->stream;
-    HIP_OK(e, hipMemcpyAsync(e->evict_dev, hs, s.blocks.size() * 4, hipMemcpyHostToDevice, st));
-    HIP_OK(e, hipMemcpyAsync(e->evict_dev + mc, hs + e->d.max_blocks, (size_t)nb * 4, hipMemcpyHostToDevice, st));
+    const size_t mb = (size_t)e->d.max_blocks;
+    HIP_OK(e, hipMemcpyAsync(e->evict_dev, hs, (mb + (size_t)nb) * 4, hipMemcpyHostToDevice, st));
     HIP_OK(e, launch_evict_one(e->scores_dev + (size_t)s.slot * mc, e->kvpos_dev + (size_t)s.slot * mc, n,
-                               kb.n_initial, n - kb.n_recent, new_pos, e->evict_dev + 2 * (size_t)mc, st));
-    HIP_OK(e, launch_kv_gather(e->d, e->players, e->evict_dev, e->evict_dev + mc, e->evict_dev + 2 * (size_t)mc, m,
-                               st));
-    HIP_OK(e, hipMemcpyAsync(e->bt_dev + (size_t)s.slot * e->d.max_blocks, hs + e->d.max_blocks, (size_t)nb * 4,
-                             hipMemcpyHostToDevice, st));
+                               kb.n_initial, n - kb.n_recent, new_pos, e->evict_dev + 2 * mb, e->evict_dev + mb, nb,
+                               e->bt_dev + (size_t)s.slot * mb, st));
+    HIP_OK(e, launch_kv_gather(e->d, e->players, e->evict_dev, e->evict_dev + mb, e->evict_dev + 2 * mb, m, st));
     HIP_OK(e, hipEventRecord(e->evict_ev[ring], st));
     e->evict_ev_used[ring] = true;
     e->evict_ring = (ring + 1) % kEvictRing;

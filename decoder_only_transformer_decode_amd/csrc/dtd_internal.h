@@ -226,9 +226,10 @@ hipError_t launch_score(const Dims& d, const StepDesc* desc, int B, int max_pos,
                         size_t q_ls, const KvLayer& kv, size_t k_ls, size_t s_ls, const int32_t* bt, const float* stat,
                         size_t st_ls, float* scores, hipStream_t st);
 // KV budget, one eviction on the device (n = budget + 1 entries): picks the entry, closes
-// the gap in the score and position rows, writes the n - 1 kept indices to keep
+// the gap in the score and position rows, writes the n - 1 kept indices to keep, and puts
+// the nb new blocks (fresh) in the sequence's block-table row
 hipError_t launch_evict_one(float* scores, int32_t* kvpos, int n, int n_init, int rec0, int new_pos, int32_t* keep,
-                            hipStream_t st);
+                            const int32_t* fresh, int nb, int32_t* bt_row, hipStream_t st);
 hipError_t launch_kv_gather(const Dims& d, const PLayer* layers, const int32_t* old_blocks, const int32_t* new_blocks,
                             const int32_t* keep, int n, hipStream_t st);
 hipError_t launch_argmax(const Dims& d, const StepDesc* desc, int B, const float* logits,

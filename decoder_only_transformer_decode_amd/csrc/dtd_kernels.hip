@@ -1217,12 +1217,14 @@ __global__ __launch_bounds__(256) void k_score(Dims d, const StepDesc* desc, Sco
 // move down one place; the freed last score starts again at 0) and writes the kept indices,
 // in order, for k_kv_gather.  One block of 1024 threads, no host round trip.
 __global__ __launch_bounds__(1024) void k_evict_one(float* scores, int32_t* kvpos, int n, int n_init, int rec0,
-                                                    int new_pos, int32_t* keep) {
+                                                    int new_pos, int32_t* keep, const int32_t* fresh, int nb,
+                                                    int32_t* bt_row) {
   __shared__ float wbest[16];
   __shared__ int widx[16];
   __shared__ int ev;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   if (t == 0) kvpos[n - 1] = new_pos;
+  for (int i = t; i < nb; i += 1024) bt_row[i] = fresh[i];   // the sequence's new blocks
   float best = INFINITY;
   int bi = -1;
   for (int i = n_init + t; i < rec0; i += 1024) {
@@ -1970,8 +1972,9 @@ hipError_t launch_score(const Dims& d, const StepDesc* desc, int B, int max_pos,
 }
 
 hipError_t launch_evict_one(float* scores, int32_t* kvpos, int n, int n_init, int rec0, int new_pos, int32_t* keep,
-                            hipStream_t st) {
-  hipLaunchKernelGGL(k_evict_one, dim3(1), dim3(1024), 0, st, scores, kvpos, n, n_init, rec0, new_pos, keep);
+                            const int32_t* fresh, int nb, int32_t* bt_row, hipStream_t st) {
+  hipLaunchKernelGGL(k_evict_one, dim3(1), dim3(1024), 0, st, scores, kvpos, n, n_init, rec0, new_pos, keep, fresh,
+                     nb, bt_row);
   return hipGetLastError();
 }
 
