@@ -1140,11 +1140,11 @@ __global__ __launch_bounds__(256) void k_combine(Dims d, const StepDesc* desc, c
 // KV budget scores (the Initial-Key cache of the C17 engine article, 5.3): the softmax
 // probability each cache entry t <= pos of sequence b gets from this step's queries, summed
 // over the query heads, added to scores[slot][t].  Grid (B, groups of 4 entries), four
-// waves: wave w takes entry 4 * group + w, its lanes split the head dimension, and the row's
-// queries are staged in LDS.  For each query head h in order it recomputes q_h . k_t / sqrt(d)
-// from the stored key (a wave sum: every lane holds the same total) and adds
-// exp(s - M_h) / L_h with the merged attention statistics, so every entry's sum has one fixed
-// order.  Layers layer0 .. layer0 + nl - 1 in one launch (those from the row's score_from on):
+// waves: wave w takes entry 4 * group + w, and the row's queries are staged in LDS.  The
+// wave recomputes every q_h . k_t / sqrt(d) from the stored key, the heads side by side
+// (P lanes per head, each with a slice of the head dimension), and adds
+// exp(s - M_h) / L_h with the merged attention statistics in head order, so every entry's
+// sum has one fixed order.  Layers layer0 .. layer0 + nl - 1 in one launch (those from the row's score_from on):
 // layer l's queries, keys, scales and statistics sit l strides past layer0's, and each
 // layer's sum is added to the entry in layer order by the wave that owns the entry.
 struct ScoreLayers {
@@ -1159,13 +1159,15 @@ struct ScoreLayers {
 template <int KVFMT>
 __global__ __launch_bounds__(256) void k_score(Dims d, const StepDesc* desc, ScoreLayers a, const int32_t* bt,
                                                float* scores) {
-  extern __shared__ float qb[];        // [q_dim] this row's queries of one layer
+  extern __shared__ __attribute__((aligned(16))) float qb[];   // [q_dim] this row's queries of one layer (read as float4)
   const int b = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int t = blockIdx.y * 4 + wave;
   const int pos = desc->pos[b], slot = desc->slot[b];
   const bool mine = t <= pos;          // (wave-uniform; waves past the row still take the barriers)
   const float scale = 1.f / sqrtf((float)d.hd);
+  int P = 1;                           // lanes per head: a power of 2, P heads' worth fit 64 lanes
+  while (2 * P * d.Hq <= 64 && d.hd % (8 * P) == 0) P *= 2;
   const int blk = mine ? bt[(size_t)slot * d.max_blocks + t / d.bs] : 0;
   for (int l = 0; l < a.nl; l++) {
     if (a.layer0 + l < desc->score_from[b]) continue;   // block-uniform
@@ -1177,33 +1179,43 @@ __global__ __launch_bounds__(256) void k_score(Dims d, const StepDesc* desc, Sco
     const uint8_t* kl = (const uint8_t*)a.kv.k + (size_t)l * a.k_ls;
     const uint16_t* ksl = KVFMT == KV_I8 ? (const uint16_t*)((const uint8_t*)a.kv.ks + (size_t)l * a.s_ls) : nullptr;
     const float* stat = a.stat + (size_t)l * a.st_ls;
+    // lane (head h, part) takes dims [part dl, (part + 1) dl) of q_h . k_{h / G}, the P lanes
+    // of a head add their parts, and the heads' terms are added in head order
+    const int dl = d.hd / P;
     float sum = 0.f;
-    for (int j = 0; j < d.Hkv; j++) {
-      const size_t row = ((size_t)blk * d.Hkv + j) * d.bs + (t % d.bs);
-      float kx[2];   // elements lane and lane + 64 of the key (head size <= 128)
+    for (int h0 = 0; h0 < d.Hq; h0 += 64 / P) {
+      const int h = h0 + lane / P, part = lane & (P - 1);
+      float p = 0.f;
+      if (h < d.Hq) {
+        const size_t row = ((size_t)blk * d.Hkv + h / d.G) * d.bs + (t % d.bs);
+        const float* qh = qb + (size_t)h * d.hd + part * dl;
+        const size_t e0 = row * d.hd + (size_t)part * dl;
+        for (int i = 0; i < dl; i += 4) {
+          float k4[4];
+          if constexpr (KVFMT == KV_F32) {
+            const float4 v = *(const float4*)((const float*)kl + e0 + i);
+            k4[0] = v.x; k4[1] = v.y; k4[2] = v.z; k4[3] = v.w;
+          } else if constexpr (KVFMT == KV_BF16) {
+            const uint2 v = *(const uint2*)((const uint16_t*)kl + e0 + i);
+            k4[0] = __uint_as_float(v.x << 16); k4[1] = __uint_as_float(v.x & 0xffff0000u);
+            k4[2] = __uint_as_float(v.y << 16); k4[3] = __uint_as_float(v.y & 0xffff0000u);
+          } else {
+            const uint32_t v = *(const uint32_t*)((const int8_t*)kl + e0 + i);
+            const float ks = f16_to_f32(ksl[row]);
 #pragma unroll
-      for (int u = 0; u < 2; u++) {
-        const int i = lane + 64 * u;
-        float v = 0.f;
-        if (i < d.hd) {
-          if constexpr (KVFMT == KV_F32) v = ((const float*)kl)[row * d.hd + i];
-          else if constexpr (KVFMT == KV_BF16) v = bf16_to_f32(((const uint16_t*)kl)[row * d.hd + i]);
-          else v = (float)((const int8_t*)kl)[row * d.hd + i] * f16_to_f32(ksl[row]);
+            for (int u = 0; u < 4; u++) k4[u] = sext8(v, u) * ks;
+          }
+          const float4 q4 = *(const float4*)(qh + i);
+          p += q4.x * k4[0] + q4.y * k4[1] + q4.z * k4[2] + q4.w * k4[3];
         }
-        kx[u] = v;
       }
-      for (int g = 0; g < d.G; g++) {
-        const int h = j * d.G + g;
-        float p = 0.f;
-#pragma unroll
-        for (int u = 0; u < 2; u++) {
-          const int i = lane + 64 * u;
-          if (i < d.hd) p += qb[(size_t)h * d.hd + i] * kx[u];
-        }
-        const float dot = wave_sum(p);
+      for (int m = 1; m < P; m <<= 1) p += __shfl_xor(p, m, 64);
+      float e = 0.f;
+      if (h < d.Hq) {
         const float M = stat[((size_t)b * d.Hq + h) * 2], L = stat[((size_t)b * d.Hq + h) * 2 + 1];
-        sum += expf(dot * scale - M) / L;
+        e = expf(p * scale - M) / L;
       }
+      for (int u = 0; u < 64 / P && h0 + u < d.Hq; u++) sum += __shfl(e, u * P, 64);
     }
     if (lane == 0) scores[(size_t)slot * d.max_ctx + t] += sum;
   }
