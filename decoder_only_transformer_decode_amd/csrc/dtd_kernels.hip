@@ -47,19 +47,23 @@ __global__ __launch_bounds__(256) void k_embed(Dims d, MatDev emb, const StepDes
 // S1 / S7 / S10 RMSNorm: xn = round_act(x / sqrt(mean(x^2) + eps) * g)
 // ---------------------------------------------------------------------------------------
 
-__global__ __launch_bounds__(256) void k_rmsnorm(const float* x, const float* g, void* xn, int D,
-                                                 float eps, int act) {
-  __shared__ float red[4];
+// One workgroup of kNormThreads per row (many loads in flight: a row is a few KB and the
+// batch is a few dozen rows).
+constexpr int kNormThreads = 1024;
+constexpr int kNormPieces = 2;            // 16-byte pieces per thread: rows up to 8192
+__global__ __launch_bounds__(kNormThreads) void k_rmsnorm(const float* x, const float* g, void* xn, int D,
+                                                          float eps, int act) {
+  __shared__ float red[kNormThreads / 64];
   const int b = blockIdx.x;
   const float* xb = x + (size_t)b * D;
-  if ((D & 3) == 0 && D <= 8 * 4 * 256) {
-    // the row in 16-byte pieces, up to 8 per thread, loaded once and kept in registers
-    constexpr int NP = 8;
+  if ((D & 3) == 0 && D <= kNormPieces * 4 * kNormThreads) {
+    // the row in 16-byte pieces, kept in registers
+    constexpr int NP = kNormPieces;
     float4 v[NP];
     float ss = 0.f;
 #pragma unroll
     for (int k = 0; k < NP; k++) {
-      const int i = 4 * ((int)threadIdx.x + 256 * k);
+      const int i = 4 * ((int)threadIdx.x + kNormThreads * k);
       v[k] = i < D ? *(const float4*)(xb + i) : make_float4(0.f, 0.f, 0.f, 0.f);
       ss += v[k].x * v[k].x + v[k].y * v[k].y + v[k].z * v[k].z + v[k].w * v[k].w;
     }
@@ -67,7 +71,7 @@ __global__ __launch_bounds__(256) void k_rmsnorm(const float* x, const float* g,
     const float r = 1.0f / sqrtf(ss / (float)D + eps);
 #pragma unroll
     for (int k = 0; k < NP; k++) {
-      const int i = 4 * ((int)threadIdx.x + 256 * k);
+      const int i = 4 * ((int)threadIdx.x + kNormThreads * k);
       if (i >= D) continue;
       const float4 gg = *(const float4*)(g + i);
       const float y0 = v[k].x * r * gg.x, y1 = v[k].y * r * gg.y, y2 = v[k].z * r * gg.z, y3 = v[k].w * r * gg.w;
@@ -82,15 +86,15 @@ __global__ __launch_bounds__(256) void k_rmsnorm(const float* x, const float* g,
     return;
   }
   float ss = 0.f;
-  for (int i = threadIdx.x; i < D; i += 256) ss += xb[i] * xb[i];
+  for (int i = threadIdx.x; i < D; i += kNormThreads) ss += xb[i] * xb[i];
   ss = block_sum(ss, red);
   const float r = 1.0f / sqrtf(ss / (float)D + eps);
   if (act == ACT_BF16) {
     uint16_t* o = (uint16_t*)xn + (size_t)b * D;
-    for (int i = threadIdx.x; i < D; i += 256) o[i] = f32_to_bf16(xb[i] * r * g[i]);
+    for (int i = threadIdx.x; i < D; i += kNormThreads) o[i] = f32_to_bf16(xb[i] * r * g[i]);
   } else {
     float* o = (float*)xn + (size_t)b * D;
-    for (int i = threadIdx.x; i < D; i += 256) o[i] = xb[i] * r * g[i];
+    for (int i = threadIdx.x; i < D; i += kNormThreads) o[i] = xb[i] * r * g[i];
   }
 }
 
@@ -577,20 +581,20 @@ __global__ __launch_bounds__(256) void k_gemm_reduce(GemmArgs a) {
 
 // The split-K sums of a residual projection (O or down: N = D rows), the residual add, and
 // the RMSNorm that follows it (of the next block), in one launch: one workgroup per
-// sequence.  Thread t takes rows 4 (t + 256 k), the rows k_gemm_reduce and k_rmsnorm's
-// vector path give it, and runs their operations in their order.  D a multiple of 4, at
-// most 8192.
+// sequence.  Thread t takes rows 4 (t + kNormThreads k), the rows k_rmsnorm's vector path
+// gives it, and runs k_gemm_reduce's and k_rmsnorm's operations in their order.  D a
+// multiple of 4, at most 8192.
 template <int WFMT>
-__global__ __launch_bounds__(256) void k_gemm_reduce_norm(GemmArgs a, const float* g, void* xn) {
-  __shared__ float red[4];
-  constexpr int NP = 8;
+__global__ __launch_bounds__(kNormThreads) void k_gemm_reduce_norm(GemmArgs a, const float* g, void* xn) {
+  __shared__ float red[kNormThreads / 64];
+  constexpr int NP = kNormPieces;
   const int D = a.g.m.rows, B = a.g.B, b = blockIdx.x;
   float* xb = a.g.ea.x + (size_t)b * D;
   float4 v[NP];
   float ss = 0.f;
 #pragma unroll
   for (int k = 0; k < NP; k++) {
-    const int i = 4 * ((int)threadIdx.x + 256 * k);
+    const int i = 4 * ((int)threadIdx.x + kNormThreads * k);
     v[k] = make_float4(0.f, 0.f, 0.f, 0.f);
     if (i >= D) continue;
     float s[4] = {0.f, 0.f, 0.f, 0.f};
@@ -613,7 +617,7 @@ __global__ __launch_bounds__(256) void k_gemm_reduce_norm(GemmArgs a, const floa
   const int act = a.g.d.act;
 #pragma unroll
   for (int k = 0; k < NP; k++) {
-    const int i = 4 * ((int)threadIdx.x + 256 * k);
+    const int i = 4 * ((int)threadIdx.x + kNormThreads * k);
     if (i >= D) continue;
     const float4 gg = *(const float4*)(g + i);
     const float y0 = v[k].x * r * gg.x, y1 = v[k].y * r * gg.y, y2 = v[k].z * r * gg.z, y3 = v[k].w * r * gg.w;
@@ -1815,7 +1819,7 @@ hipError_t launch_gemm(const Dims& d, const MatDev& m, const void* xin, int B, i
 hipError_t launch_gemm_resid_norm(const Dims& d, const MatDev& m, const void* xin, int B, const EpiArgs& ea,
                                   float* partials, int cus, const float* g, void* xn, hipStream_t st) {
   const int S = gemm_splits(m.rows, m.cols, cus);
-  if (S == 1 || m.rows != d.D || d.D % 4 || d.D > 8 * 4 * 256) {
+  if (S == 1 || m.rows != d.D || d.D % 4 || d.D > kNormPieces * 4 * kNormThreads) {
     const hipError_t r = launch_gemm(d, m, xin, B, EPI_RESID, ea, partials, cus, st);
     return r != hipSuccess ? r : launch_rmsnorm(d, ea.x, g, xn, B, st);
   }
@@ -1837,10 +1841,10 @@ hipError_t launch_gemm_resid_norm(const Dims& d, const MatDev& m, const void* xi
   hipError_t r;
   if (d.wfmt == W_INT8_ROW) {
     r = gemm_dispatch<W_INT8_ROW, EPI_RESID>(a, nbb, grid, smem, st, false);
-    if (r == hipSuccess) hipLaunchKernelGGL(k_gemm_reduce_norm<W_INT8_ROW>, dim3(B), dim3(256), 0, st, a, g, xn);
+    if (r == hipSuccess) hipLaunchKernelGGL(k_gemm_reduce_norm<W_INT8_ROW>, dim3(B), dim3(kNormThreads), 0, st, a, g, xn);
   } else {
     r = gemm_dispatch<W_BF16, EPI_RESID>(a, nbb, grid, smem, st, false);
-    if (r == hipSuccess) hipLaunchKernelGGL(k_gemm_reduce_norm<W_BF16>, dim3(B), dim3(256), 0, st, a, g, xn);
+    if (r == hipSuccess) hipLaunchKernelGGL(k_gemm_reduce_norm<W_BF16>, dim3(B), dim3(kNormThreads), 0, st, a, g, xn);
   }
   return r != hipSuccess ? r : hipGetLastError();
 }
@@ -1853,7 +1857,7 @@ hipError_t launch_embed(const Dims& d, const MatDev& emb, const StepDesc* desc, 
 
 hipError_t launch_rmsnorm(const Dims& d, const float* x, const float* g, void* xn, int B,
                           hipStream_t st) {
-  hipLaunchKernelGGL(k_rmsnorm, dim3(B), dim3(256), 0, st, x, g, xn, d.D, d.eps, d.act);
+  hipLaunchKernelGGL(k_rmsnorm, dim3(B), dim3(kNormThreads), 0, st, x, g, xn, d.D, d.eps, d.act);
   return hipGetLastError();
 }
 
