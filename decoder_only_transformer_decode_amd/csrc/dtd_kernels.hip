@@ -27,8 +27,9 @@ using std::max;
 // S0 embedding (+ block-table updates of this step)
 // ---------------------------------------------------------------------------------------
 
-__global__ __launch_bounds__(256) void k_embed(Dims d, MatDev emb, const StepDesc* desc,
-                                               int32_t* bt, float* x, int32_t* err) {
+// one workgroup of 1024 threads per sequence (a few elements per thread in flight)
+__global__ __launch_bounds__(1024) void k_embed(Dims d, MatDev emb, const StepDesc* desc,
+                                                int32_t* bt, float* x, int32_t* err) {
   const int b = blockIdx.x;
   if (b == 0) {
     for (int u = threadIdx.x; u < desc->n_updates; u += blockDim.x)
@@ -1851,7 +1852,7 @@ hipError_t launch_gemm_resid_norm(const Dims& d, const MatDev& m, const void* xi
 
 hipError_t launch_embed(const Dims& d, const MatDev& emb, const StepDesc* desc, int B,
                         int32_t* block_table, float* x, int32_t* err, hipStream_t st) {
-  hipLaunchKernelGGL(k_embed, dim3(B), dim3(256), 0, st, d, emb, desc, block_table, x, err);
+  hipLaunchKernelGGL(k_embed, dim3(B), dim3(1024), 0, st, d, emb, desc, block_table, x, err);
   return hipGetLastError();
 }
 
