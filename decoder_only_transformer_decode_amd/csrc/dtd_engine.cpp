@@ -176,7 +176,7 @@ static thread_local std::string g_create_err;   // message of this thread's last
 // name as an address (on the host it names a stand-in, not device memory): each device's
 // copy is looked up once with hipGetSymbolAddress, when the first engine is created on
 // that device, and kept in g_scratch_dev.
-constexpr size_t kNoAllocScratchBytes = (size_t)16 << 20;
+constexpr size_t kNoAllocScratchBytes = (size_t)32 << 20;
 static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
 constexpr int kMaxDevices = 64;
 static std::mutex g_scratch_mu;

@@ -170,7 +170,7 @@ dtd_status dtd_decode_step(dtd_engine* e, int32_t batch, const int64_t* seq_ids_
  * sub-step schedule at every batch size, with its work memory -- the split-K attention
  * partials (batch x Hq x nch x (head_dim + 2) fp32, nch = ceil(max_ctx / chunk)) and, for
  * batched matrix-core projections, their split-K sums (splits x batch x rows fp32) -- in a
- * static device array of 16 MiB that the library holds on each GPU until the process ends;
+ * static device array of 32 MiB that the library holds on each GPU until the process ends;
  * a call that would need more returns DTD_E_UNSUPPORTED before anything is enqueued.  Every
  * call on one GPU shares that array, and each call writes every value it reads there before
  * reading it: calls that overlap on one GPU (other streams, other engines, other threads)
